@@ -1,0 +1,140 @@
+"""fp64 CPU oracle for decode-phase paged attention: TEST INFRASTRUCTURE ONLY.
+
+Only tests/, the package smoke check and bench.py's CPU-baseline leg may import this
+package.  The GPU product path must never call it.  The arithmetic lives in
+oracle.c; this module only marshals numpy arrays into it.
+
+Array conventions (numpy, host memory, C-contiguous):
+  dtype "f32": np.float32 arrays; "f16": np.float16; "bf16": np.uint16 bit patterns.
+  q [B][Hq][d], k_pool [N][Hkv][16][d], v_pool [N][Hkv][d][16],
+  block_tables [B][max_blocks] int32, context_lens [B] int32.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from .build import LIB, build_oracle
+
+DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2}
+NUMPY_STORAGE = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16}
+
+_lib = None
+
+
+def load(path=None):
+    """Load (building first if absent) the oracle shared library."""
+    global _lib
+    if path is not None:
+        return _bind(ctypes.CDLL(path))
+    if _lib is None:
+        if not os.path.exists(LIB):
+            build_oracle()
+        _lib = _bind(ctypes.CDLL(LIB))
+    return _lib
+
+
+def _bind(lib):
+    P = ctypes.c_void_p
+    I = ctypes.c_int
+    lib.oracle_widen.argtypes = [P, I, ctypes.c_size_t, P]
+    lib.oracle_widen.restype = I
+    lib.oracle_kv_cache_bytes.argtypes = [ctypes.c_uint64] * 6
+    lib.oracle_kv_cache_bytes.restype = ctypes.c_uint64
+    lib.oracle_decode_paged.argtypes = [P, P, P, I, I, I, I, I, I, P, I, P, ctypes.c_float,
+                                        P, P, I]
+    lib.oracle_decode_paged.restype = I
+    lib.oracle_decode_contig.argtypes = [P, P, P, I, I, I, I, I, I, P, ctypes.c_float, P, P, I]
+    lib.oracle_decode_contig.restype = I
+    lib.oracle_cache_append.argtypes = [P, P, I, I, I, I, P, P, P, I]
+    lib.oracle_cache_append.restype = I
+    return lib
+
+
+def default_threads():
+    return max(1, len(os.sched_getaffinity(0)))
+
+
+def _ptr(a):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _check(arr, dtype):
+    want = NUMPY_STORAGE[dtype]
+    if arr.dtype != want or not arr.flags.c_contiguous:
+        raise TypeError(f"expected C-contiguous {np.dtype(want).name} for {dtype}, got {arr.dtype}")
+
+
+def widen(bits, dtype, lib=None):
+    """Exact widening of stored elements to fp64 (oracle's own conversion)."""
+    lib = lib or load()
+    _check(bits, dtype)
+    out = np.empty(bits.size, np.float64)
+    rc = lib.oracle_widen(_ptr(bits), DTYPE_CODES[dtype], bits.size, _ptr(out))
+    if rc:
+        raise ValueError("oracle_widen failed")
+    return out.reshape(bits.shape)
+
+
+def kv_cache_bytes(layers, kv_heads, head_dim, seq_len, batch, dtype_size, lib=None):
+    lib = lib or load()
+    return int(lib.oracle_kv_cache_bytes(layers, kv_heads, head_dim, seq_len, batch, dtype_size))
+
+
+def decode_paged(q, k_pool, v_pool, dtype, block_tables, context_lens, scale,
+                 threads=None, lib=None):
+    """Returns (out [B][Hq][d] fp64, wsum [B][Hq] fp64)."""
+    lib = lib or load()
+    for a in (q, k_pool, v_pool):
+        _check(a, dtype)
+    B, hq, d = q.shape
+    nblk, hkv, bs, d2 = k_pool.shape
+    assert bs == 16 and d2 == d and v_pool.shape == (nblk, hkv, d, 16)
+    bt = np.ascontiguousarray(block_tables, np.int32)
+    cl = np.ascontiguousarray(context_lens, np.int32)
+    assert bt.shape[0] == B and cl.shape == (B,)
+    out = np.zeros((B, hq, d), np.float64)
+    wsum = np.zeros((B, hq), np.float64)
+    rc = lib.oracle_decode_paged(_ptr(q), _ptr(k_pool), _ptr(v_pool), DTYPE_CODES[dtype], B,
+                                 hq, hkv, d, nblk, _ptr(bt), bt.shape[1], _ptr(cl),
+                                 ctypes.c_float(np.float32(scale)), _ptr(out), _ptr(wsum),
+                                 threads or default_threads())
+    if rc:
+        raise ValueError(f"oracle_decode_paged returned {rc}")
+    return out, wsum
+
+
+def decode_contig(q, k, v, dtype, context_lens, scale, threads=None, lib=None):
+    """k, v: [B][Hkv][S_max][d] contiguous caches.  Returns (out, wsum) in fp64."""
+    lib = lib or load()
+    for a in (q, k, v):
+        _check(a, dtype)
+    B, hq, d = q.shape
+    B2, hkv, s_max, d2 = k.shape
+    assert B2 == B and d2 == d and v.shape == k.shape
+    cl = np.ascontiguousarray(context_lens, np.int32)
+    out = np.zeros((B, hq, d), np.float64)
+    wsum = np.zeros((B, hq), np.float64)
+    rc = lib.oracle_decode_contig(_ptr(q), _ptr(k), _ptr(v), DTYPE_CODES[dtype], B, hq, hkv,
+                                  d, s_max, _ptr(cl), ctypes.c_float(np.float32(scale)),
+                                  _ptr(out), _ptr(wsum), threads or default_threads())
+    if rc:
+        raise ValueError(f"oracle_decode_contig returned {rc}")
+    return out, wsum
+
+
+def cache_append(k_pool, v_pool, k_new, v_new, slot_mapping, dtype, lib=None):
+    """Returns appended copies of (k_pool, v_pool); the inputs are not modified."""
+    lib = lib or load()
+    for a in (k_pool, v_pool, k_new, v_new):
+        _check(a, dtype)
+    k_out = k_pool.copy()
+    v_out = v_pool.copy()
+    nblk, hkv, _, d = k_pool.shape
+    sm = np.ascontiguousarray(slot_mapping, np.int32)
+    assert k_new.shape == (sm.size, hkv, d) and v_new.shape == k_new.shape
+    rc = lib.oracle_cache_append(_ptr(k_out), _ptr(v_out), DTYPE_CODES[dtype], nblk, hkv, d,
+                                 _ptr(k_new), _ptr(v_new), _ptr(sm), sm.size)
+    if rc:
+        raise ValueError(f"oracle_cache_append returned {rc}")
+    return k_out, v_out

@@ -1,0 +1,294 @@
+"""Seeded synthetic workloads for decode-phase paged attention.
+
+This module only builds inputs: random values, a physical block pool, block tables,
+context lengths, the rows a decode step appends and their slots.  It computes no
+attention arithmetic, so both the GPU path and the fp64 CPU oracle can consume what
+it builds without sharing any of the method's code.
+
+Recipe (every workload is synthetic; the pages use no dataset for this path):
+  * values: numpy PCG64(seed) float32 normals times sigma, rounded to the storage
+    type by round-to-nearest-even (bf16 by bit arithmetic, f16 by numpy's cast);
+  * pool: K is [N][Hkv][16][d], V is [N][Hkv][d][16]; every element starts as a NaN
+    ("poison").  Only rows of live tokens get values, so any read of a free block,
+    of another request's block, of a tail row past the context or of a table entry
+    past ceil(ctx/16) turns into NaN in the output;
+  * the decode step's own token (position ctx-1) is left poisoned in the pool and
+    delivered through k_new/v_new + slot_mapping, i.e. append then attend;
+  * block tables hold physical ids drawn from a seeded shuffle of the pool (or of a
+    fragmented free list); entries past a sequence's last block point at a poisoned
+    spare block, so a stray read stays in bounds but poisons the result.
+
+Storage in numpy: f32 -> float32, f16 -> float16, bf16 -> uint16 bit patterns.
+"""
+from __future__ import annotations
+
+import dataclasses
+import hashlib
+import math
+from typing import List, Optional, Sequence, Tuple
+
+import numpy as np
+
+BLOCK = 16
+STORAGE = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16}
+ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
+NAN_BITS = {"f32": np.uint32(0x7FC00000), "f16": np.uint16(0x7E00), "bf16": np.uint16(0x7FC0)}
+_CHUNK = 1 << 22  # values drawn per generator call
+
+
+def round_to_storage(x: np.ndarray, dtype: str) -> np.ndarray:
+    """float32 -> storage representation, round-to-nearest-even."""
+    x = np.ascontiguousarray(x, np.float32)
+    if dtype == "f32":
+        return x
+    if dtype == "f16":
+        return x.astype(np.float16)
+    u = x.view(np.uint32)
+    rounded = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
+    return rounded.astype(np.uint16)
+
+
+def _normals(rng: np.random.Generator, n: int, sigma: float) -> np.ndarray:
+    out = np.empty(n, np.float32)
+    for s in range(0, n, _CHUNK):
+        e = min(n, s + _CHUNK)
+        out[s:e] = rng.standard_normal(e - s, dtype=np.float32)
+    if sigma != 1.0:
+        out *= np.float32(sigma)
+    return out
+
+
+@dataclasses.dataclass
+class Spec:
+    """Shape and pool recipe of one workload."""
+    name: str
+    dtype: str
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    context_lens: Sequence[int]
+    sigma: float = 0.5
+    seed: int = 0
+    spare_blocks: int = 0           # poisoned blocks beyond the live ones
+    free_fraction: float = 0.0      # >0: fragmented pool, only this fraction is free
+    exact_pool: Optional[int] = None  # force the pool size (must fit live + spare)
+    max_blocks_per_seq: Optional[int] = None
+    # groups of sequences sharing their first n blocks: [(seq ids, n_shared_blocks)]
+    prefix_groups: Sequence[Tuple[Sequence[int], int]] = ()
+    append: bool = True             # deliver token ctx-1 through cache_append
+
+
+@dataclasses.dataclass
+class Workload:
+    spec: Spec
+    dtype: str
+    q: np.ndarray                   # [B][Hq][d]
+    k_pool: np.ndarray              # [N][Hkv][16][d], before the append
+    v_pool: np.ndarray              # [N][Hkv][d][16], before the append
+    k_new: np.ndarray               # [T][Hkv][d]
+    v_new: np.ndarray
+    slot_mapping: np.ndarray        # [T] int32
+    block_tables: np.ndarray        # [B][max_blocks] int32
+    context_lens: np.ndarray        # [B] int32
+    scale: np.float32
+    live_blocks: np.ndarray         # distinct physical ids holding live tokens
+    poison_block: int               # id of a block that is entirely poisoned
+
+    @property
+    def num_seqs(self):
+        return self.q.shape[0]
+
+    @property
+    def num_q_heads(self):
+        return self.q.shape[1]
+
+    @property
+    def num_kv_heads(self):
+        return self.k_pool.shape[1]
+
+    @property
+    def head_dim(self):
+        return self.q.shape[2]
+
+    @property
+    def num_blocks(self):
+        return self.k_pool.shape[0]
+
+    @property
+    def max_context_len(self):
+        return int(self.context_lens.max()) if self.context_lens.size else 0
+
+    def logical_kv_bytes(self) -> int:
+        """K+V bytes of every (token, kv-head) the step attends to, per sequence."""
+        return int(self.context_lens.astype(np.int64).sum()) * self.num_kv_heads * 2 * \
+            self.head_dim * ELEM_BYTES[self.dtype]
+
+    def unique_kv_bytes(self) -> int:
+        """K+V bytes of distinct physical token rows attended to (shared blocks once)."""
+        seen = {}
+        for b in range(self.num_seqs):
+            n = int(self.context_lens[b])
+            for lb in range((n + BLOCK - 1) // BLOCK):
+                p = int(self.block_tables[b, lb])
+                seen[p] = max(seen.get(p, 0), min(BLOCK, n - lb * BLOCK))
+        rows = sum(seen.values())
+        return rows * self.num_kv_heads * 2 * self.head_dim * ELEM_BYTES[self.dtype]
+
+    def digest(self) -> str:
+        h = hashlib.sha256()
+        for a in (self.q, self.k_pool, self.v_pool, self.k_new, self.v_new, self.slot_mapping,
+                  self.block_tables, self.context_lens):
+            h.update(np.ascontiguousarray(a).view(np.uint8).tobytes())
+        return h.hexdigest()
+
+
+def _poison(shape, dtype):
+    if dtype == "f32":
+        return np.full(shape, NAN_BITS["f32"], np.uint32).view(np.float32)
+    if dtype == "f16":
+        return np.full(shape, NAN_BITS["f16"], np.uint16).view(np.float16)
+    return np.full(shape, NAN_BITS["bf16"], np.uint16)
+
+
+def build(spec: Spec, seed: Optional[int] = None) -> Workload:
+    seed = spec.seed if seed is None else seed
+    rng = np.random.Generator(np.random.PCG64(seed))
+    dt = spec.dtype
+    B = len(spec.context_lens)
+    hq, hkv, d = spec.num_q_heads, spec.num_kv_heads, spec.head_dim
+    assert hq % hkv == 0
+    ctx = np.asarray(spec.context_lens, np.int64)
+    nblk = (ctx + BLOCK - 1) // BLOCK
+    maxb = spec.max_blocks_per_seq or max(1, int(nblk.max()) if B else 1)
+    assert (nblk <= maxb).all()
+
+    # ---- block ownership: shared prefixes first, then every sequence's own blocks
+    shared_of = {}
+    n_shared_total = 0
+    for seqs, n_sh in spec.prefix_groups:
+        for s in seqs:
+            assert n_sh * BLOCK <= ctx[s], "a shared prefix must be whole blocks of context"
+            shared_of[s] = (tuple(seqs), n_sh)
+        n_shared_total += n_sh
+    own = [int(nblk[b]) - (shared_of[b][1] if b in shared_of else 0) for b in range(B)]
+    n_live = n_shared_total + sum(own)
+
+    if spec.free_fraction > 0:
+        n_pool = max(math.ceil(n_live / spec.free_fraction), n_live + 1)
+        n_free = math.ceil(spec.free_fraction * n_pool)
+        perm = rng.permutation(n_pool)
+        free_list = perm[:n_free]           # a random 30% (say) in random order
+    else:
+        n_pool = spec.exact_pool or (n_live + spec.spare_blocks)
+        assert n_pool >= n_live
+        free_list = rng.permutation(n_pool)
+    cursor = 0
+
+    def take(n):
+        nonlocal cursor
+        ids = free_list[cursor:cursor + n]
+        assert ids.size == n, "pool too small"
+        cursor += n
+        return ids
+
+    group_blocks = {}
+    for seqs, n_sh in spec.prefix_groups:
+        group_blocks[tuple(seqs)] = take(n_sh)
+    unused = set(range(n_pool))
+    tables = np.zeros((B, maxb), np.int32)
+    for b in range(B):
+        row = []
+        if b in shared_of:
+            row.extend(group_blocks[shared_of[b][0]].tolist())
+        row.extend(take(own[b]).tolist())
+        tables[b, :len(row)] = row
+    live = np.unique(np.concatenate([tables[b, :nblk[b]] for b in range(B)])) if n_live else \
+        np.zeros(0, np.int64)
+    unused.difference_update(int(x) for x in live)
+    poison_block = min(unused) if unused else -1
+    for b in range(B):
+        if nblk[b] < maxb:
+            assert poison_block >= 0, "table padding needs a poisoned spare block"
+            tables[b, nblk[b]:] = poison_block
+
+    # ---- values: q, then K and V of every live block (ascending id), then new rows
+    q = round_to_storage(_normals(rng, B * hq * d, spec.sigma), dt).reshape(B, hq, d)
+    k_pool = _poison((n_pool, hkv, BLOCK, d), dt)
+    v_pool = _poison((n_pool, hkv, d, BLOCK), dt)
+    per_block = hkv * BLOCK * d
+    step = max(1, _CHUNK // per_block)
+    for which in ("k", "v"):
+        for s in range(0, live.size, step):
+            ids = live[s:s + step]
+            vals = round_to_storage(_normals(rng, ids.size * per_block, spec.sigma), dt)
+            vals = vals.reshape(ids.size, hkv, BLOCK, d)
+            if which == "k":
+                k_pool[ids] = vals
+            else:
+                v_pool[ids] = vals.transpose(0, 1, 3, 2)
+
+    # tail rows past each context stay poisoned
+    for b in range(B):
+        n = int(ctx[b])
+        if n % BLOCK:
+            p = tables[b, n // BLOCK]
+            k_pool[p, :, n % BLOCK:, :] = _poison((hkv, BLOCK - n % BLOCK, d), dt)
+            v_pool[p, :, :, n % BLOCK:] = _poison((hkv, d, BLOCK - n % BLOCK), dt)
+
+    # the step's own token (ctx-1): poisoned in the pool, delivered by the append
+    appending = [b for b in range(B) if spec.append and ctx[b] > 0]
+    T = len(appending)
+    k_new = round_to_storage(_normals(rng, T * hkv * d, spec.sigma), dt).reshape(T, hkv, d)
+    v_new = round_to_storage(_normals(rng, T * hkv * d, spec.sigma), dt).reshape(T, hkv, d)
+    slots = np.full(T, -1, np.int32)
+    for i, b in enumerate(appending):
+        pos = int(ctx[b]) - 1
+        p = int(tables[b, pos // BLOCK])
+        k_pool[p, :, pos % BLOCK, :] = _poison((hkv, d), dt)
+        v_pool[p, :, :, pos % BLOCK] = _poison((hkv, d), dt)
+        slots[i] = p * BLOCK + pos % BLOCK
+
+    scale = np.float32(1.0 / math.sqrt(d))
+    return Workload(spec, dt, q, k_pool, v_pool, k_new, v_new, slots, tables,
+                    ctx.astype(np.int32), scale, live, poison_block)
+
+
+# ----------------------------------------------------------------- named configs
+
+def _ragged_lens(seed: int, n: int, lo: int, hi: int) -> List[int]:
+    r = np.random.Generator(np.random.PCG64(seed ^ 0x5EED))
+    return r.integers(lo, hi + 1, size=n).tolist()
+
+
+def config_spec(i: int) -> Spec:
+    """The five decode workloads.
+
+    1 tiny fp32: 1 seq, 4 q / 1 kv heads, d 64, 37 tokens, 8-block pool.
+    2 Llama-7B-shaped MHA fp16: 8 seqs x 4096, 32/32 heads, d 128, exactly 2048 blocks.
+    3 Llama-70B-shaped GQA bf16: 32 seqs x 4096, 64/8 heads, d 128, 8192 live + 32 spare.
+    4 continuous-batching ragged bf16: 64 seqs, ctx ~ U[1, 8192], 32/8 heads, d 128,
+      pool where a random 30% of blocks is free and the rest belongs to other requests.
+    5 long + shared prefix bf16: 4 seqs x 32768 and 8 beams x 2304 that share their first
+      2048 tokens (128 physical blocks), 64/8 heads, d 128.
+    """
+    if i == 1:
+        return Spec("tiny_fp32", "f32", 4, 1, 64, [37], sigma=1.0, seed=1, exact_pool=8)
+    if i == 2:
+        return Spec("llama7b_mha_fp16", "f16", 32, 32, 128, [4096] * 8, seed=2,
+                    exact_pool=2048)
+    if i == 3:
+        return Spec("llama70b_gqa_bf16", "bf16", 64, 8, 128, [4096] * 32, seed=3,
+                    spare_blocks=32)
+    if i == 4:
+        return Spec("ragged_gqa_bf16", "bf16", 32, 8, 128, _ragged_lens(4, 64, 1, 8192),
+                    seed=4, free_fraction=0.30, max_blocks_per_seq=512)
+    if i == 5:
+        return Spec("long_shared_prefix_bf16", "bf16", 64, 8, 128,
+                    [32768] * 4 + [2304] * 8, seed=5, spare_blocks=12,
+                    max_blocks_per_seq=2048,
+                    prefix_groups=[(list(range(4, 12)), 128)])
+    raise ValueError(f"no config {i}")
+
+
+def make_config(i: int, seed: Optional[int] = None) -> Workload:
+    return build(config_spec(i), seed)

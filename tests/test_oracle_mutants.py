@@ -1,0 +1,58 @@
+"""Planted mistakes in copies of the oracle must each fail at least one pin (CPU only).
+
+Each mutant is oracle.c with one plausible slip (a dropped term, a wrong sign or index,
+a transposed operand), compiled to a temporary library and run through every check in
+tests/_pins.py.  A mutant that passes them all would mean the pins cannot see that
+class of mistake.
+"""
+import os
+
+import pytest
+
+import oracle as O
+from oracle.build import SRC, build_oracle
+from tests import _pins
+
+MUTANTS = {
+    "gqa_interleaved_heads": ("int kvh = h / group;", "int kvh = h % A->hkv;"),
+    "scale_dropped": ("J->scores[t] = J->scale * dot;", "J->scores[t] = dot;"),
+    "v_read_token_major": (
+        "size_t idx = ((phys * P->hkv + P->kv_head) * P->d + e) * ORACLE_BLOCK + off;",
+        "size_t idx = ((phys * P->hkv + P->kv_head) * ORACLE_BLOCK + off) * P->d + e;"),
+    "k_row_off_by_one": (
+        "size_t off = (size_t)(t % ORACLE_BLOCK);\n    size_t idx = ((phys * P->hkv + P->kv_head) * ORACLE_BLOCK",
+        "size_t off = (size_t)((t + 1) % ORACLE_BLOCK);\n    size_t idx = ((phys * P->hkv + P->kv_head) * ORACLE_BLOCK"),
+    "exp_sign_flipped": ("J->scores[t] = exp(J->scores[t] - m);",
+                         "J->scores[t] = exp(m - J->scores[t]);"),
+    "final_divide_dropped": ("out[e] = acc / z;", "out[e] = acc;"),
+    "block_index_uses_offset": (
+        "size_t phys = (size_t)P->table_row[t / ORACLE_BLOCK];\n    size_t off = (size_t)(t % ORACLE_BLOCK);\n    size_t idx = ((phys * P->hkv + P->kv_head) * P->d",
+        "size_t phys = (size_t)P->table_row[t % P->hkv];\n    size_t off = (size_t)(t % ORACLE_BLOCK);\n    size_t idx = ((phys * P->hkv + P->kv_head) * P->d"),
+    "f16_exponent_bias": ("v = ldexp((double)(frac | 0x400), expo - 25);",
+                          "v = ldexp((double)(frac | 0x400), expo - 24);"),
+    "bf16_shift": ("uint32_t u = (uint32_t)b << 16;", "uint32_t u = (uint32_t)b << 15;"),
+    "append_row_col_swapped": (
+        "size_t vdst = ((blk * num_kv_heads + h) * head_dim + e) * ORACLE_BLOCK + off;",
+        "size_t vdst = ((blk * num_kv_heads + h) * ORACLE_BLOCK + off) * head_dim + e;"),
+    "kv_size_factor_dropped": ("return 2ull * layers * kv_heads", "return layers * kv_heads"),
+    "max_over_first_token_only": ("if (J->scores[t] > m)", "if (t == 0)"),
+    "weight_sum_unnormalised": ("s += J->scores[t] / z;", "s += J->scores[t];"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation anchor for {name} not unique in oracle.c"
+    mutated = tmp_path / "oracle_mut.c"
+    mutated.write_text(src.replace(old, new))
+    lib_path = build_oracle(str(mutated), str(tmp_path / f"lib_{name}.so"))
+    lib = O.load(lib_path)
+    failures = []
+    for check in _pins.ALL_CHECKS:
+        try:
+            check(lib)
+        except (AssertionError, ValueError) as exc:
+            failures.append(check.__name__)
+    assert failures, f"mutant {name} passed every pin"
