@@ -1,0 +1,214 @@
+#!/usr/bin/env python3
+"""Decode-phase PagedAttention benchmark on one MI355X.
+
+A step is one layer of one decode step over one batch: pa_cache_append of the step's
+new K/V rows, then pa_decode (partition kernel + reduce when split) over the whole
+batch.  The headline workload is the Llama-70B-shaped GQA decode: 32 sequences x 4096
+tokens, 64 q-heads / 8 kv-heads, head_dim 128, bf16 KV, 16-token blocks in a shuffled
+pool.  Inputs are seeded and synthetic and already resident in HBM when timing starts.
+The step cycles over four copies of the layer's pools at distinct addresses, as the
+layers of a real step do, so K/V is not reused from the 256 MB last-level cache.
+
+Printed: ONE JSON line on stdout.
+  value      KV GB/s over the whole step (algorithmic K+V bytes / wall time per step)
+  roofline   the decode call (partition + reduce kernels), timed per launch with HIP
+             events on the launching stream after a 1 GiB cache-flush write, against
+             the 8 TB/s HBM peak
+  cpu_baseline  the fp64 oracle on the host cores, on the same workload
+Progress goes to stderr.
+"""
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+import torch
+
+HBM_PEAK_GBS = 8000.0
+LAYERS = 4
+FLUSH_BYTES = 1 << 30
+HEADLINE = 3
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=HEADLINE,
+                    help="workload id 1..5 (default: the Llama-70B GQA headline)")
+    ap.add_argument("--partition-tokens", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--roofline-launches", type=int, default=50)
+    return ap.parse_args()
+
+
+def cpu_baseline(w):
+    """The fp64 oracle as it is, on the host cores, on the same workload (append then
+    decode of the whole batch); median of 3 runs."""
+    import oracle as O
+    threads = O.default_threads()
+    kp, vp, bt, sl = w.oracle_view()
+    kp, vp = O.cache_append(kp, vp, w.k_new, w.v_new, sl, w.dtype)
+    times = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        O.decode_paged(w.q, kp, vp, w.dtype, bt, w.context_lens, w.scale, threads=threads)
+        times.append(time.perf_counter() - t0)
+    t = statistics.median(times)
+    return {"value": round(w.logical_kv_bytes() / t / 1e9, 4), "unit": "GB/s",
+            "cores": threads, "kind": "oracle",
+            "sample": f"whole workload ({w.spec.name}, {w.num_seqs} seqs), decode only, "
+                      f"median of 3 runs: {t:.3f} s/step, "
+                      f"{w.num_seqs / t:.1f} tokens/s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: every GPU box here has one MI355X and this "
+              "decode path is not sharded across GPUs; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        sys.exit(2)
+
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    from paged_kv_cache_161_amd import binding as PA
+    from paged_kv_cache_161_amd import workloads as W
+    from tests import devutil as U
+
+    PA.load()
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    w = W.make_config(args.config)
+    log(f"[bench] built {w.spec.name} in {time.time() - t0:.1f}s: B={w.num_seqs} "
+        f"Hq={w.num_q_heads} Hkv={w.num_kv_heads} d={w.head_dim} "
+        f"max_ctx={w.max_context_len} pool={w.num_blocks} blocks")
+
+    pools = [U.device_pools(w, dev) for _ in range(LAYERS)]
+    d = U.device_inputs(w, dev)
+    out = torch.empty_like(d["q"])
+    ptok = args.partition_tokens
+    ws_bytes = PA.workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                                  w.max_context_len, ptok)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    kv_bytes = w.logical_kv_bytes()
+    uniq_bytes = w.unique_kv_bytes()
+    scale = float(w.scale)
+    max_ctx = w.max_context_len
+
+    def step(i):
+        kp, vp = pools[i % LAYERS]
+        PA.cache_append(kp, vp, d["k_new"], d["v_new"], d["slot_mapping"])
+        PA.decode(d["q"], kp, vp, d["block_tables"], d["context_lens"], scale, max_ctx, ptok,
+                  out=out, workspace=ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {args.warmup} steps done")
+
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms_per_step = wall * 1e3 / args.steps
+    log(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.1f} us/step")
+
+    # roofline: event-timed decode calls, each after a cache-flushing write
+    stream = torch.cuda.current_stream(dev)
+    durs = []
+    for i in range(args.roofline_launches):
+        kp, vp = pools[i % LAYERS]
+        flush.fill_(i & 0xFF)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        PA.decode(d["q"], kp, vp, d["block_tables"], d["context_lens"], scale, max_ctx, ptok,
+                  out=out, workspace=ws)
+        e1.record(stream)
+        e1.synchronize()
+        durs.append(e0.elapsed_time(e1) * 1e-3)
+    dur = statistics.mean(durs)
+    achieved = kv_bytes / dur / 1e9
+    log(f"[bench] decode call: mean {dur * 1e6:.1f} us (min {min(durs) * 1e6:.1f}, "
+        f"max {max(durs) * 1e6:.1f}) over {len(durs)} flushed launches -> {achieved:.0f} GB/s")
+
+    # parity on the timed inputs (sampled rows against the oracle)
+    parity = None
+    try:
+        import oracle as O
+        rows = np.random.Generator(np.random.PCG64(0)).choice(
+            w.num_seqs, size=min(4, w.num_seqs), replace=False)
+        sub = {k: v for k, v in zip(("k", "v", "bt", "sl"), w.oracle_view())}
+        kpo, vpo = O.cache_append(sub["k"], sub["v"], w.k_new, w.v_new, sub["sl"], w.dtype)
+        ref, _ = O.decode_paged(np.ascontiguousarray(w.q[rows]), kpo, vpo, w.dtype,
+                                np.ascontiguousarray(sub["bt"][rows]), w.context_lens[rows],
+                                w.scale)
+        got = U.widen(U.from_dev(out, w.dtype), w.dtype)[rows]
+        ok, mx, mean = U.tolerance_ok(got, ref, w.dtype)
+        parity = {"rows_checked": int(rows.size), "max_abs_err": mx, "mean_abs_err": mean,
+                  "pass": bool(ok and np.isfinite(got).all())}
+        log(f"[bench] parity on timed inputs: {parity}")
+    except Exception as exc:  # parity is reported, never silently assumed
+        parity = {"error": repr(exc)}
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w)
+    if cpu:
+        log(f"[bench] cpu baseline: {cpu}")
+
+    value = kv_bytes / (ms_per_step * 1e-3) / 1e9
+    tokens_per_s = w.num_seqs / (ms_per_step * 1e-3)
+    result = {
+        "metric": "decode-attention KV GB/s (% of HBM peak) and tokens/s, 1 MI355X",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded PCG64 normals x0.5, NaN-poisoned paged pool)",
+        "config": {"workload": f"{w.spec.name}: {w.num_seqs} seqs x ctx {max_ctx}, "
+                               f"{w.num_q_heads} q / {w.num_kv_heads} kv heads, d "
+                               f"{w.head_dim}, 16-token blocks, {w.num_blocks}-block shuffled pool; "
+                               f"step = append + decode of one layer",
+                   "num_seqs": w.num_seqs, "context_len": max_ctx,
+                   "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
+                   "head_dim": w.head_dim, "block_size": 16,
+                   "partition_tokens": ptok or PA.partition_tokens(
+                       w.num_seqs, w.num_q_heads, w.num_kv_heads, max_ctx),
+                   "parallelism": "none (1 GPU)"},
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "tokens_per_s": round(tokens_per_s, 1),
+        "context_tokens_per_s": round(float(w.context_lens.sum()) / (ms_per_step * 1e-3), 1),
+        "kv_bytes_per_step": kv_bytes,
+        "unique_kv_bytes_per_step": uniq_bytes,
+        "roofline": {"bound": "hbm", "kernel": "pa_decode call (partition + reduce)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "launch_us_mean": round(dur * 1e6, 2),
+                     "bytes_per_launch": kv_bytes},
+        "cpu_baseline": cpu,
+        "parity": parity,
+        "context_figures": {"A100_ridge_flop_per_byte": 156, "H100_hbm_TBps": 3.35},
+    }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

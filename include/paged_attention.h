@@ -1,0 +1,147 @@
+/*
+ * paged_attention.h -- C ABI of the MI355X (gfx950) decode-phase PagedAttention library.
+ *
+ * Two operations, as the web pages on paged KV caches state the problem:
+ *
+ *   pa_cache_append  writes the K/V rows a decode step produces into a pool of fixed
+ *                    16-token physical blocks, through a slot mapping.
+ *                    (LLM-101-CN "推理优化", section "vLLM 架构深度解析",
+ *                    KVCachePool.write_tokens: new rows go to a page and an offset
+ *                    inside it; "LLM应用 12 推理优化", PagedKVCache.update: page =
+ *                    position // page_size, offset = position % page_size.)
+ *
+ *   pa_decode        for every sequence and q-head, softmax(q . K^T * scale) . V over
+ *                    the sequence's context, reading K/V through the sequence's block
+ *                    table (logical block -> physical block), with GQA head groups.
+ *                    (LLM-101-CN "推理优化", sections "物理块与逻辑块" and
+ *                    "PagedAttention 内核实现" (decode: per-page local attention merged
+ *                    with the max/normaliser combine); "大模型推理的三维本质原理解析与
+ *                    工程实践", section 6 GQA; "Deep dive into vLLM 06", section on
+ *                    Flash-Decoding: split the KV axis and merge partials with the same
+ *                    m, l rescaling rule.)
+ *
+ * Conventions shared by every entry point
+ *   - Pointers named *_pool, q, out, k_new, v_new, slot_mapping, block_tables,
+ *     context_lens and workspace are DEVICE pointers (hipMalloc'd or torch CUDA
+ *     tensors).  pa_kv_pool itself lives in host memory and is read during the call.
+ *   - The caller owns every buffer.  The library allocates nothing, keeps no state
+ *     across calls other than cached device attributes, and never frees caller memory.
+ *   - Calls are asynchronous on `stream` (a hipStream_t passed as void*, NULL = the
+ *     default stream): they return once the kernels are enqueued.
+ *   - Argument errors are detected on the host before anything is enqueued; nothing is
+ *     written then.  A launch failure returns PA_ERR_HIP.  Nothing throws across the ABI.
+ *   - Element types: PA_F32 (4 bytes), PA_F16 (IEEE half), PA_BF16 (bfloat16).  q, the
+ *     pools, the new rows and out all use the pool's element type; arithmetic is fp32.
+ *   - Calls on different streams touching disjoint buffers may run concurrently.
+ *
+ * Pool layout (one layer; K and V are two separate buffers of equal size):
+ *   k_pool [num_blocks][num_kv_heads][16][head_dim]   token-major inside a block
+ *   v_pool [num_blocks][num_kv_heads][head_dim][16]   token-minor inside a block
+ * so one (block, kv-head) tile of K or of V is a single contiguous run of
+ * 16 * head_dim elements (4 KiB for head_dim 128 in 16-bit types).  Token t of a
+ * sequence is row t % 16 of physical block block_tables[seq][t / 16]; its slot number
+ * is physical_block * 16 + t % 16.
+ */
+#ifndef PAGED_ATTENTION_H
+#define PAGED_ATTENTION_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_BLOCK_SIZE 16
+
+typedef enum pa_status {
+    PA_OK = 0,
+    PA_ERR_INVALID_ARG = 1,   /* null pointer, negative size, inconsistent shapes      */
+    PA_ERR_UNSUPPORTED = 2,   /* valid but not built: dtype, head_dim, block size     */
+    PA_ERR_WORKSPACE = 3,     /* workspace pointer null or smaller than required      */
+    PA_ERR_HIP = 4            /* the HIP runtime reported an error at launch          */
+} pa_status;
+
+typedef enum pa_dtype {
+    PA_F32 = 0,
+    PA_F16 = 1,
+    PA_BF16 = 2
+} pa_dtype;
+
+/* One layer's paged KV pool.  block_size must be PA_BLOCK_SIZE; head_dim must be one
+ * of 64, 128, 256; dtype one of pa_dtype. */
+typedef struct pa_kv_pool {
+    void *k_pool;
+    void *v_pool;
+    int32_t num_blocks;
+    int32_t block_size;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    int32_t dtype;
+} pa_kv_pool;
+
+/* Bytes of ONE of the two pools (K or V) for these dimensions; 0 if any argument is
+ * invalid or unsupported.  Host-only, no device access. */
+size_t pa_pool_bytes(int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                     int32_t dtype);
+
+/* Scatter num_tokens new rows into the pool (LLM-101-CN "推理优化",
+ * KVCachePool.write_tokens; "LLM应用 12 推理优化", PagedKVCache.update).
+ *   k_new, v_new   [num_tokens][num_kv_heads][head_dim], pool dtype, device
+ *   slot_mapping   [num_tokens] int32, device: row i goes to physical block
+ *                  slot_mapping[i] / 16, row slot_mapping[i] % 16, for every kv-head.
+ * Bytes are copied unchanged.  A negative slot means "no row" (padding) and is
+ * skipped.  A slot >= num_blocks * 16 is also skipped (never written), so a bad slot
+ * cannot corrupt memory outside the pool.  Two rows with the same slot race (caller
+ * error).  num_tokens == 0 is a valid no-op. */
+pa_status pa_cache_append(const pa_kv_pool *pool, const void *k_new, const void *v_new,
+                          const int32_t *slot_mapping, int32_t num_tokens, void *stream);
+
+/* The partition length, in tokens, pa_decode uses when partition_tokens == 0 (auto).
+ * A return value >= max_context_len means a single pass (no partials, no workspace).
+ * Host-only; the same inputs always give the same answer.  Returns -1 on bad input. */
+int32_t pa_decode_partition_tokens(int32_t num_seqs, int32_t num_q_heads,
+                                   int32_t num_kv_heads, int32_t max_context_len);
+
+/* Workspace bytes pa_decode needs for these arguments (partition_tokens as passed to
+ * pa_decode, 0 = auto).  0 when the call runs in a single pass.  Returns SIZE_MAX on
+ * invalid arguments.  Host-only. */
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t max_context_len,
+                                 int32_t partition_tokens);
+
+/* Decode attention for one layer (definitions as cited at the top of this file).
+ *   q              [num_seqs][num_q_heads][head_dim], pool dtype, device
+ *   out            [num_seqs][num_q_heads][head_dim], pool dtype, device; each element
+ *                  is the fp32 result rounded to nearest-even
+ *   scale          multiplies q . k (normally 1/sqrt(head_dim)), applied in fp32
+ *   block_tables   [num_seqs][max_blocks_per_seq] int32, device; entries at index
+ *                  >= ceil(context_lens[s] / 16) are never read
+ *   context_lens   [num_seqs] int32, device; token count attended by each sequence
+ *                  (the step's own token included: append first, then decode)
+ *   max_context_len  host-side upper bound of context_lens, sizes the launch grid
+ *   partition_tokens 0 = automatic; otherwise a positive multiple of 16: the KV axis
+ *                  of each sequence is cut into partitions of this many tokens,
+ *                  computed independently and merged by the max/normaliser rule
+ *   workspace      device scratch of at least pa_decode_workspace_bytes(...) bytes
+ *                  (may be NULL when that is 0); contents need no initialisation
+ * num_q_heads must be a multiple of the pool's num_kv_heads; q-head h reads kv-head
+ * h / (num_q_heads / num_kv_heads).
+ * A sequence with context length 0 gets an all-zero output.  Device-side inconsistency
+ * the host cannot see -- a context length < 0, > max_context_len or
+ * > max_blocks_per_seq * 16, or a needed table entry outside [0, num_blocks) -- makes
+ * that sequence's output NaN; no out-of-bounds memory is ever read. */
+pa_status pa_decode(const pa_kv_pool *pool, const void *q, void *out, int32_t num_seqs,
+                    int32_t num_q_heads, float scale, const int32_t *block_tables,
+                    int32_t max_blocks_per_seq, const int32_t *context_lens,
+                    int32_t max_context_len, int32_t partition_tokens, void *workspace,
+                    size_t workspace_bytes, void *stream);
+
+/* Static, human-readable text for a status code. */
+const char *pa_status_string(int32_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_ATTENTION_H */

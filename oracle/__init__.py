@@ -123,13 +123,13 @@ def decode_contig(q, k, v, dtype, context_lens, scale, threads=None, lib=None):
     return out, wsum
 
 
-def cache_append(k_pool, v_pool, k_new, v_new, slot_mapping, dtype, lib=None):
-    """Returns appended copies of (k_pool, v_pool); the inputs are not modified."""
+def cache_append(k_pool, v_pool, k_new, v_new, slot_mapping, dtype, inplace=False, lib=None):
+    """Returns appended (k_pool, v_pool): copies, or the inputs themselves if inplace."""
     lib = lib or load()
     for a in (k_pool, v_pool, k_new, v_new):
         _check(a, dtype)
-    k_out = k_pool.copy()
-    v_out = v_pool.copy()
+    k_out = k_pool if inplace else k_pool.copy()
+    v_out = v_pool if inplace else v_pool.copy()
     nblk, hkv, _, d = k_pool.shape
     sm = np.ascontiguousarray(slot_mapping, np.int32)
     assert k_new.shape == (sm.size, hkv, d) and v_new.shape == k_new.shape

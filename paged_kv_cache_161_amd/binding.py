@@ -1,0 +1,164 @@
+"""ctypes binding of libpa_mi355x.so (the C ABI in include/paged_attention.h).
+
+Argument marshalling only: torch CUDA tensors become device pointers, the current
+torch stream becomes the hipStream_t.  Every step of the computation runs in the
+library's HIP kernels; there is no fallback.  If the library is not built, loading
+raises instead of computing anything another way.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libpa_mi355x.so")
+HEADER_PATH = os.path.join(os.path.dirname(HERE), "include", "paged_attention.h")
+
+BLOCK_SIZE = 16
+PA_F32, PA_F16, PA_BF16 = 0, 1, 2
+DTYPE_CODE = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}
+STATUS = {0: "PA_OK", 1: "PA_ERR_INVALID_ARG", 2: "PA_ERR_UNSUPPORTED", 3: "PA_ERR_WORKSPACE",
+          4: "PA_ERR_HIP"}
+
+
+class PaError(RuntimeError):
+    def __init__(self, status: int, text: str):
+        super().__init__(f"{STATUS.get(status, status)}: {text}")
+        self.status = status
+
+
+class PaKvPool(ctypes.Structure):
+    _fields_ = [("k_pool", ctypes.c_void_p), ("v_pool", ctypes.c_void_p),
+                ("num_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load the HIP library; raises if it has not been built."""
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -c 'import __graft_entry__ as g; "
+                           "g.build()'` (hipcc, gfx950) first")
+    lib = ctypes.CDLL(path)
+    P, I32 = ctypes.c_void_p, ctypes.c_int32
+    lib.pa_pool_bytes.argtypes = [I32, I32, I32, I32]
+    lib.pa_pool_bytes.restype = ctypes.c_size_t
+    lib.pa_cache_append.argtypes = [ctypes.POINTER(PaKvPool), P, P, P, I32, P]
+    lib.pa_cache_append.restype = ctypes.c_int
+    lib.pa_decode_partition_tokens.argtypes = [I32, I32, I32, I32]
+    lib.pa_decode_partition_tokens.restype = I32
+    lib.pa_decode_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32]
+    lib.pa_decode_workspace_bytes.restype = ctypes.c_size_t
+    lib.pa_decode.argtypes = [ctypes.POINTER(PaKvPool), P, P, I32, I32, ctypes.c_float, P, I32,
+                              P, I32, I32, P, ctypes.c_size_t, P]
+    lib.pa_decode.restype = ctypes.c_int
+    lib.pa_status_string.argtypes = [I32]
+    lib.pa_status_string.restype = ctypes.c_char_p
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def _raise(status: int):
+    if status != 0:
+        raise PaError(status, load().pa_status_string(status).decode())
+
+
+def _stream_handle(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _dev_ptr(t: Optional[torch.Tensor], name: str, dtype=None) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def make_pool(k_pool: torch.Tensor, v_pool: torch.Tensor) -> PaKvPool:
+    """k_pool [N][Hkv][16][d] and v_pool [N][Hkv][d][16], same dtype."""
+    if k_pool.dim() != 4 or v_pool.dim() != 4:
+        raise ValueError("pools are 4-D: k [N][Hkv][16][d], v [N][Hkv][d][16]")
+    n, hkv, bs, d = k_pool.shape
+    if tuple(v_pool.shape) != (n, hkv, d, bs) or v_pool.dtype != k_pool.dtype:
+        raise ValueError("v_pool must be [N][Hkv][d][16] with k_pool's dtype")
+    if k_pool.dtype not in DTYPE_CODE:
+        raise ValueError(f"unsupported dtype {k_pool.dtype}")
+    return PaKvPool(_dev_ptr(k_pool, "k_pool"), _dev_ptr(v_pool, "v_pool"), n, bs, hkv, d,
+                    DTYPE_CODE[k_pool.dtype])
+
+
+def pool_bytes(num_blocks: int, num_kv_heads: int, head_dim: int, dtype: torch.dtype) -> int:
+    return int(load().pa_pool_bytes(num_blocks, num_kv_heads, head_dim, DTYPE_CODE[dtype]))
+
+
+def cache_append(k_pool, v_pool, k_new, v_new, slot_mapping) -> None:
+    """Write k_new/v_new [T][Hkv][d] rows into the pools at slot_mapping [T] (int32)."""
+    pool = make_pool(k_pool, v_pool)
+    T = int(slot_mapping.numel())
+    if tuple(k_new.shape) != (T, pool.num_kv_heads, pool.head_dim) or k_new.shape != v_new.shape:
+        raise ValueError("k_new/v_new must be [T][Hkv][d]")
+    st = load().pa_cache_append(ctypes.byref(pool), _dev_ptr(k_new, "k_new", k_pool.dtype),
+                                _dev_ptr(v_new, "v_new", k_pool.dtype),
+                                _dev_ptr(slot_mapping, "slot_mapping", torch.int32), T,
+                                _stream_handle(k_pool.device))
+    _raise(st)
+
+
+def partition_tokens(num_seqs: int, num_q_heads: int, num_kv_heads: int,
+                     max_context_len: int) -> int:
+    return int(load().pa_decode_partition_tokens(num_seqs, num_q_heads, num_kv_heads,
+                                                 max_context_len))
+
+
+def workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                    max_context_len: int, partition_tokens: int = 0) -> int:
+    n = int(load().pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                             max_context_len, partition_tokens))
+    if n == ctypes.c_size_t(-1).value:
+        raise PaError(1, "invalid arguments for pa_decode_workspace_bytes")
+    return n
+
+
+def decode(q, k_pool, v_pool, block_tables, context_lens, scale: float, max_context_len: int,
+           partition_tokens: int = 0, out: Optional[torch.Tensor] = None,
+           workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """softmax(q K^T scale) V per sequence and q-head through the block tables.
+
+    q [B][Hq][d]; block_tables [B][max_blocks] int32; context_lens [B] int32;
+    max_context_len: host-side bound of context_lens.  Returns out [B][Hq][d].
+    """
+    pool = make_pool(k_pool, v_pool)
+    B, hq, d = q.shape
+    if d != pool.head_dim:
+        raise ValueError("q head_dim differs from the pool's")
+    if out is None:
+        out = torch.empty_like(q)
+    need = workspace_bytes(B, hq, pool.num_kv_heads, d, max_context_len, partition_tokens)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = _dev_ptr(workspace, "workspace") if need else None
+    ws_len = workspace.numel() * workspace.element_size() if need else 0
+    st = load().pa_decode(ctypes.byref(pool), _dev_ptr(q, "q", k_pool.dtype),
+                          _dev_ptr(out, "out", k_pool.dtype), B, hq, ctypes.c_float(scale),
+                          _dev_ptr(block_tables, "block_tables", torch.int32),
+                          block_tables.shape[1], _dev_ptr(context_lens, "context_lens",
+                                                          torch.int32),
+                          max_context_len, partition_tokens, ws_ptr, ws_len,
+                          _stream_handle(q.device))
+    _raise(st)
+    return out

@@ -1,0 +1,235 @@
+// pa_api.cpp -- the library's C ABI: argument checks, partition choice, launches.
+// Every check here runs on the host before anything is enqueued, so an error return
+// means nothing was written.
+#include <limits.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/paged_attention.h"
+#include "pa_common.h"
+
+namespace {
+
+using pa::kBlock;
+
+bool dtype_ok(int32_t dtype) { return dtype == PA_F32 || dtype == PA_F16 || dtype == PA_BF16; }
+
+bool head_dim_ok(int32_t dtype, int32_t head_dim)
+{
+    if (head_dim == 64 || head_dim == 128)
+        return true;
+    return head_dim == 256 && dtype != PA_F32;
+}
+
+size_t elem_bytes(int32_t dtype) { return dtype == PA_F32 ? 4 : 2; }
+
+// Most blocks one wave may walk in one partition: the kernel keeps a wave's block ids
+// one per lane of a single register.
+int32_t max_part_blocks(int32_t head_dim) { return pa::waves_per_group(head_dim) * pa::kWave; }
+
+pa_status check_pool(const pa_kv_pool *pool)
+{
+    if (!pool || !pool->k_pool || !pool->v_pool)
+        return PA_ERR_INVALID_ARG;
+    if (pool->num_blocks <= 0 || pool->num_kv_heads <= 0 || pool->head_dim <= 0)
+        return PA_ERR_INVALID_ARG;
+    if (!dtype_ok(pool->dtype))
+        return PA_ERR_UNSUPPORTED;
+    if (pool->block_size != PA_BLOCK_SIZE || !head_dim_ok(pool->dtype, pool->head_dim))
+        return PA_ERR_UNSUPPORTED;
+    if ((int64_t)pool->num_blocks * kBlock > INT32_MAX)   // slots are int32
+        return PA_ERR_UNSUPPORTED;
+    return PA_OK;
+}
+
+// Partition length in blocks for a (validated) decode call; 0 on invalid input.
+int32_t choose_part_blocks(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                           int32_t head_dim, int32_t max_context_len, int32_t partition_tokens)
+{
+    const int32_t max_blocks = (max_context_len + kBlock - 1) / kBlock;
+    if (max_blocks == 0)
+        return 1;
+    if (partition_tokens > 0)
+        return partition_tokens / kBlock;
+    // Auto: about 16 blocks per wave (64 per 4-wave workgroup, 512 KiB of K+V at
+    // d = 128 16-bit) keeps ragged batches balanced; when that leaves fewer workgroups
+    // than the GPU keeps resident, cut finer so every resident slot streams, but not
+    // below ~2 blocks per wave.
+    const int32_t nw = pa::waves_per_group(head_dim);
+    const int64_t chunks = (num_q_heads / num_kv_heads + 15) / 16;
+    const int64_t units = (int64_t)num_seqs * num_kv_heads * chunks;
+    const int64_t target_blocks = 16LL * nw;
+    int64_t parts = (max_blocks + target_blocks - 1) / target_blocks;
+    const int64_t fill = (pa::kResidentGroups + units - 1) / units;
+    const int64_t cap = (max_blocks + 2 * nw - 1) / (2 * nw);
+    const int64_t want = fill < cap ? fill : cap;
+    if (want > parts)
+        parts = want;
+    if (parts < 1)
+        parts = 1;
+    int32_t pb = (int32_t)((max_blocks + parts - 1) / parts);
+    if (pb > max_part_blocks(head_dim))
+        pb = max_part_blocks(head_dim);
+    return pb;
+}
+
+// Host-side validation of pa_decode's scalar arguments.
+pa_status check_decode_scalars(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t max_context_len,
+                               int32_t partition_tokens)
+{
+    if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_context_len < 0)
+        return PA_ERR_INVALID_ARG;
+    if (num_q_heads % num_kv_heads != 0)
+        return PA_ERR_INVALID_ARG;
+    if (partition_tokens < 0 || partition_tokens % kBlock != 0)
+        return PA_ERR_INVALID_ARG;
+    if (partition_tokens > 0 && partition_tokens / kBlock > max_part_blocks(head_dim))
+        return PA_ERR_UNSUPPORTED;
+    if (num_seqs > 65535)
+        return PA_ERR_UNSUPPORTED;
+    const int64_t chunks = (num_q_heads / num_kv_heads + 15) / 16;
+    if ((int64_t)num_kv_heads * chunks > 65535)
+        return PA_ERR_UNSUPPORTED;
+    return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t pa_pool_bytes(int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim, int32_t dtype)
+{
+    if (num_blocks <= 0 || num_kv_heads <= 0 || !dtype_ok(dtype) || !head_dim_ok(dtype, head_dim))
+        return 0;
+    return (size_t)num_blocks * num_kv_heads * kBlock * head_dim * elem_bytes(dtype);
+}
+
+const char *pa_status_string(int32_t status)
+{
+    switch (status) {
+    case PA_OK: return "ok";
+    case PA_ERR_INVALID_ARG: return "invalid argument";
+    case PA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case PA_ERR_WORKSPACE: return "workspace missing or too small";
+    case PA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+    }
+}
+
+pa_status pa_cache_append(const pa_kv_pool *pool, const void *k_new, const void *v_new,
+                          const int32_t *slot_mapping, int32_t num_tokens, void *stream)
+{
+    pa_status st = check_pool(pool);
+    if (st != PA_OK)
+        return st;
+    if (num_tokens < 0)
+        return PA_ERR_INVALID_ARG;
+    if (num_tokens == 0)
+        return PA_OK;
+    if (!k_new || !v_new || !slot_mapping)
+        return PA_ERR_INVALID_ARG;
+    pa::AppendArgs a;
+    a.k_pool = pool->k_pool;
+    a.v_pool = pool->v_pool;
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.slot_mapping = slot_mapping;
+    a.num_tokens = num_tokens;
+    a.num_blocks = pool->num_blocks;
+    a.num_kv_heads = pool->num_kv_heads;
+    hipError_t e = pa::launch_append(pool->dtype, pool->head_dim, a,
+                                     static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+int32_t pa_decode_partition_tokens(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                   int32_t max_context_len)
+{
+    if (check_decode_scalars(num_seqs, num_q_heads, num_kv_heads, 128, max_context_len, 0) !=
+        PA_OK)
+        return -1;
+    return choose_part_blocks(num_seqs, num_q_heads, num_kv_heads, 128, max_context_len, 0) *
+           kBlock;
+}
+
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t max_context_len,
+                                 int32_t partition_tokens)
+{
+    if (head_dim <= 0 || check_decode_scalars(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                              max_context_len, partition_tokens) != PA_OK)
+        return SIZE_MAX;
+    const int32_t pb = choose_part_blocks(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                          max_context_len, partition_tokens);
+    const int32_t max_blocks = (max_context_len + kBlock - 1) / kBlock;
+    const int64_t parts = max_blocks == 0 ? 1 : (max_blocks + pb - 1) / pb;
+    if (parts <= 1)
+        return 0;
+    const size_t rows = (size_t)num_seqs * num_q_heads * (size_t)parts;
+    return rows * (size_t)head_dim * sizeof(float) + 2 * rows * sizeof(float);
+}
+
+pa_status pa_decode(const pa_kv_pool *pool, const void *q, void *out, int32_t num_seqs,
+                    int32_t num_q_heads, float scale, const int32_t *block_tables,
+                    int32_t max_blocks_per_seq, const int32_t *context_lens,
+                    int32_t max_context_len, int32_t partition_tokens, void *workspace,
+                    size_t workspace_bytes, void *stream)
+{
+    pa_status st = check_pool(pool);
+    if (st != PA_OK)
+        return st;
+    st = check_decode_scalars(num_seqs, num_q_heads, pool->num_kv_heads, pool->head_dim,
+                              max_context_len, partition_tokens);
+    if (st != PA_OK)
+        return st;
+    if (max_blocks_per_seq < 0 || !isfinite(scale))
+        return PA_ERR_INVALID_ARG;
+    if (num_seqs == 0)
+        return PA_OK;
+    if (!q || !out || !block_tables || !context_lens || max_blocks_per_seq == 0)
+        return PA_ERR_INVALID_ARG;
+
+    const int32_t pb = choose_part_blocks(num_seqs, num_q_heads, pool->num_kv_heads,
+                                          pool->head_dim, max_context_len, partition_tokens);
+    const int32_t max_blocks = (max_context_len + kBlock - 1) / kBlock;
+    const int32_t parts = max_blocks == 0 ? 1 : (max_blocks + pb - 1) / pb;
+    const size_t need = pa_decode_workspace_bytes(num_seqs, num_q_heads, pool->num_kv_heads,
+                                                  pool->head_dim, max_context_len,
+                                                  partition_tokens);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return PA_ERR_WORKSPACE;
+    if (pb > max_part_blocks(pool->head_dim))
+        return PA_ERR_UNSUPPORTED;
+
+    pa::DecodeArgs a;
+    a.k_pool = pool->k_pool;
+    a.v_pool = pool->v_pool;
+    a.q = q;
+    a.out = out;
+    const size_t rows = (size_t)num_seqs * num_q_heads * (size_t)parts;
+    a.ws_o = parts > 1 ? static_cast<float *>(workspace) : nullptr;
+    a.ws_m = parts > 1 ? a.ws_o + rows * pool->head_dim : nullptr;
+    a.ws_l = parts > 1 ? a.ws_m + rows : nullptr;
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.num_blocks = pool->num_blocks;
+    a.num_kv_heads = pool->num_kv_heads;
+    a.num_q_heads = num_q_heads;
+    a.group = num_q_heads / pool->num_kv_heads;
+    a.head_chunks = (a.group + 15) / 16;
+    a.max_blocks = max_blocks_per_seq;
+    a.max_context_len = max_context_len;
+    a.part_blocks = pb;
+    a.num_parts = parts;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.split = parts > 1 ? 1 : 0;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = pa::launch_decode(pool->dtype, pool->head_dim, a, num_seqs, s);
+    if (e == hipSuccess && parts > 1)
+        e = pa::launch_reduce(pool->dtype, pool->head_dim, a, num_seqs, s);
+    return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+}  // extern "C"

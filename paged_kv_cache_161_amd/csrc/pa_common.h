@@ -1,0 +1,63 @@
+// pa_common.h -- types and launch declarations shared by the library's HIP sources.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+enum Dt : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
+
+constexpr int kBlock = 16;            // tokens per physical block
+constexpr int kWave = 64;             // CDNA4 wavefront width
+
+// Arguments of the decode partition kernel (by value, host -> kernel).
+struct DecodeArgs {
+    const void *k_pool;               // [num_blocks][hkv][16][D]
+    const void *v_pool;               // [num_blocks][hkv][D][16]
+    const void *q;                    // [B][hq][D]
+    void *out;                        // [B][hq][D]           (single-pass mode)
+    float *ws_o;                      // [B][hq][P][D]         (split mode)
+    float *ws_m;                      // [B][hq][P]   running max, log2 domain
+    float *ws_l;                      // [B][hq][P]   normaliser
+    const int32_t *block_tables;      // [B][max_blocks]
+    const int32_t *context_lens;      // [B]
+    int32_t num_blocks;
+    int32_t num_kv_heads;
+    int32_t num_q_heads;
+    int32_t group;                    // hq / hkv
+    int32_t head_chunks;              // ceil(group / 16)
+    int32_t max_blocks;
+    int32_t max_context_len;
+    int32_t part_blocks;              // blocks per partition
+    int32_t num_parts;                // P (grid x)
+    float scale_log2;                 // scale * log2(e)
+    int32_t split;                    // 1: write partials, 0: write out
+};
+
+struct AppendArgs {
+    void *k_pool;
+    void *v_pool;
+    const void *k_new;                // [T][hkv][D]
+    const void *v_new;
+    const int32_t *slot_mapping;      // [T]
+    int32_t num_tokens;
+    int32_t num_blocks;
+    int32_t num_kv_heads;
+};
+
+// Launchers (return hipSuccess or the launch error).
+hipError_t launch_decode(int dtype, int head_dim, const DecodeArgs &a, int num_seqs,
+                         hipStream_t stream);
+hipError_t launch_reduce(int dtype, int head_dim, const DecodeArgs &a, int num_seqs,
+                         hipStream_t stream);
+hipError_t launch_append(int dtype, int head_dim, const AppendArgs &a, hipStream_t stream);
+
+// Waves per decode workgroup.  At ~146 VGPRs per lane (d = 128, 16-bit) a SIMD holds 3
+// waves, so a CU holds three 4-wave workgroups.
+constexpr int waves_per_group(int /*head_dim*/) { return 4; }
+
+// Decode workgroups the whole GPU keeps resident at once (256 CUs x 3).
+constexpr int kResidentGroups = 768;
+
+}  // namespace pa

@@ -1,0 +1,511 @@
+// pa_decode.hip -- decode-phase paged attention for CDNA4 (gfx950).
+//
+// What is computed: for each sequence b and q-head h, softmax(q . K^T * scale) . V over
+// the sequence's context, with K/V rows found through the block table (token t is row
+// t % 16 of physical block table[t / 16]) and q-head h reading kv-head h / group.
+// Sources: LLM-101-CN "推理优化", sections "物理块与逻辑块" (logical -> physical blocks
+// of 16 tokens) and "PagedAttention 内核实现" (decode: local attention per page, then
+// the max / normaliser combine, exact rather than approximate); "Deep dive into vLLM
+// 06", Online Softmax section (running max m, sum l, deferred divide) and the
+// Flash-Decoding section (split the KV axis, merge the partials with the same rule);
+// "大模型推理的三维本质原理解析与工程实践", section 6 GQA (q-head groups share a KV head).
+//
+// Work decomposition
+//   grid  (P partitions, kv-heads x head-chunks, sequences); a workgroup of NW waves
+//   owns one (sequence, kv-head, <=16 q-heads of its group, partition).  Wave w walks
+//   the partition's blocks w, w+NW, ...; at the end the NW waves merge their running
+//   (m, l, O) in LDS.  With P == 1 the workgroup writes the normalised output; with
+//   P > 1 it writes unnormalised partials that pa_decode_reduce merges.
+//
+// Per 16-token block a wave does two MFMA contractions, no LDS:
+//   S[t][h]  = sum_e K[t][e] * Q[h][e]      A = K tile rows (token t = lane % 16),
+//                                           B = Q rows of the group (head h = lane % 16)
+//   O^T[e][h] += sum_t V^T[e][t] * P[t][h]  A = V^T tile (e = lane % 16),
+//                                           B = P, which is exactly S's accumulator
+//                                           layout (lane: head lane % 16, tokens
+//                                           4*(lane/16) .. +3) rounded to 16 bits.
+//   Because the V pool stores each block token-minor ([d][16]), the PV A operand
+//   (4 consecutive tokens of one e) is a plain 8-byte load, and the K operand (8
+//   consecutive e of one token) a 16-byte load; both come straight from HBM into
+//   registers, and every q-head of the group shares them inside the MFMA.
+//   The softmax statistics of head h live in the 4 lanes {h, h+16, h+32, h+48}; the
+//   tile max needs two cross-row exchanges, the O rescale none (O^T's head is lane % 16).
+#include <math.h>
+
+#include "pa_common.h"
+
+namespace pa {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float wave_max_rows(float v)
+{
+    // max over the 4 lanes that share lane % 16 (one per 16-lane row)
+    v = fmaxf(v, __shfl_xor(v, 16));
+    v = fmaxf(v, __shfl_xor(v, 32));
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum_rows(float v)
+{
+    v += __shfl_xor(v, 16);
+    v += __shfl_xor(v, 32);
+    return v;
+}
+
+// fp32 -> storage element, round to nearest even.
+template <int DT>
+__device__ __forceinline__ void store_elem(void *base, size_t idx, float v)
+{
+    if constexpr (DT == DT_F32) {
+        static_cast<float *>(base)[idx] = v;
+    } else if constexpr (DT == DT_F16) {
+        static_cast<_Float16 *>(base)[idx] = static_cast<_Float16>(v);
+    } else {
+        static_cast<__bf16 *>(base)[idx] = static_cast<__bf16>(v);
+    }
+}
+
+// ------------------------------------------------------------------ tile fragments
+
+// 16-bit K/V (f16, bf16).  Lane (r = lane % 16, g = lane / 16).
+template <int DT, int D>
+struct Tile16 {
+    static constexpr int NQK = D / 32;   // 16x16x32 MFMAs per block for S
+    static constexpr int NPV = D / 16;   // 16x16x16 MFMAs per block for O (one per e-tile)
+    u32x4 k[NQK];                        // K[r][32i + 8g .. +7]
+    u32x2 v[NPV];                        // V^T[16n + r][4g .. 4g+3]
+
+    __device__ __forceinline__ void load(const uint16_t *kt, const uint16_t *vt, int r, int g)
+    {
+#pragma unroll
+        for (int i = 0; i < NQK; ++i)
+            k[i] = *reinterpret_cast<const u32x4 *>(kt + r * D + 32 * i + 8 * g);
+#pragma unroll
+        for (int n = 0; n < NPV; ++n)
+            v[n] = *reinterpret_cast<const u32x2 *>(vt + (16 * n + r) * kBlock + 4 * g);
+    }
+};
+
+template <int DT, int D>
+struct Q16 {
+    u32x4 f[D / 32];                     // Q[h = r][32i + 8g .. +7]
+    __device__ __forceinline__ void load(const uint16_t *qrow, bool valid, int g)
+    {
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i)
+            f[i] = valid ? *reinterpret_cast<const u32x4 *>(qrow + 32 * i + 8 * g)
+                         : u32x4{0u, 0u, 0u, 0u};
+    }
+};
+
+// fp32 K/V.  QK uses 16x16x4 MFMAs: lane (r, g) covers e in [g*D/4, (g+1)*D/4).
+template <int D>
+struct Tile32 {
+    static constexpr int NC = D / 16;    // float4 chunks
+    f32x4 k[NC];                         // K[r][(D/4)g + 4c .. +3]
+    f32x4 v[NC];                         // V^T[16n + r][4g .. 4g+3]
+
+    __device__ __forceinline__ void load(const float *kt, const float *vt, int r, int g)
+    {
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+            k[c] = *reinterpret_cast<const f32x4 *>(kt + r * D + (D / 4) * g + 4 * c);
+#pragma unroll
+        for (int n = 0; n < NC; ++n)
+            v[n] = *reinterpret_cast<const f32x4 *>(vt + (16 * n + r) * kBlock + 4 * g);
+    }
+};
+
+template <int D>
+struct Q32 {
+    f32x4 f[D / 16];                     // Q[h = r][(D/4)g + 4c .. +3]
+    __device__ __forceinline__ void load(const float *qrow, bool valid, int g)
+    {
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c)
+            f[c] = valid ? *reinterpret_cast<const f32x4 *>(qrow + (D / 4) * g + 4 * c)
+                         : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+};
+
+template <int DT, int D> struct Frags {
+    using Tile = Tile16<DT, D>;
+    using Q = Q16<DT, D>;
+    using Elem = uint16_t;
+};
+template <int D> struct Frags<DT_F32, D> {
+    using Tile = Tile32<D>;
+    using Q = Q32<D>;
+    using Elem = float;
+};
+
+// S[t][h] for the 16 tokens of a block (lane holds tokens 4g..4g+3 of head r).
+template <int DT, int D>
+__device__ __forceinline__ f32x4 scores(const typename Frags<DT, D>::Tile &t,
+                                        const typename Frags<DT, D>::Q &q)
+{
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (DT == DT_BF16) {
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i)
+            s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, t.k[i]),
+                                                        __builtin_bit_cast(bf16x8, q.f[i]), s,
+                                                        0, 0, 0);
+    } else if constexpr (DT == DT_F16) {
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i)
+            s = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, t.k[i]),
+                                                       __builtin_bit_cast(f16x8, q.f[i]), s,
+                                                       0, 0, 0);
+    } else {
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                s = __builtin_amdgcn_mfma_f32_16x16x4f32(t.k[c][j], q.f[c][j], s, 0, 0, 0);
+    }
+    return s;
+}
+
+// O^T[e][h] += V^T[e][t] P[t][h].  p holds this lane's 4 weights (tokens 4g..4g+3 of
+// head r).  Returns the weights as the MFMA consumed them (16-bit rounded for
+// 16-bit K/V), so the caller's normaliser sums exactly what was multiplied into V.
+template <int DT, int D>
+__device__ __forceinline__ f32x4 accumulate_pv(typename Frags<DT, D>::Tile &t, f32x4 p,
+                                               f32x4 (&o)[D / 16])
+{
+    if constexpr (DT == DT_BF16) {
+        bf16x4 pb = __builtin_convertvector(p, bf16x4);
+        i16x4 pk = __builtin_bit_cast(i16x4, pb);
+#pragma unroll
+        for (int n = 0; n < D / 16; ++n)
+            o[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, t.v[n]),
+                                                             pk, o[n], 0, 0, 0);
+        return __builtin_convertvector(pb, f32x4);
+    } else if constexpr (DT == DT_F16) {
+        f16x4 ph = __builtin_convertvector(p, f16x4);
+#pragma unroll
+        for (int n = 0; n < D / 16; ++n)
+            o[n] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, t.v[n]), ph,
+                                                         o[n], 0, 0, 0);
+        return __builtin_convertvector(ph, f32x4);
+    } else {
+#pragma unroll
+        for (int n = 0; n < D / 16; ++n)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                o[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(t.v[n][j], p[j], o[n], 0, 0, 0);
+        return p;
+    }
+}
+
+// Zero the V^T entries of tokens >= valid in a partial block.  Rows past the context
+// may hold anything (NaN included); a zero weight alone would not cancel them.
+template <int DT, int D>
+__device__ __forceinline__ void mask_tail_v(typename Frags<DT, D>::Tile &t, int valid, int g)
+{
+    const int t0 = 4 * g;
+    if constexpr (DT == DT_F32) {
+#pragma unroll
+        for (int n = 0; n < D / 16; ++n)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                t.v[n][j] = (t0 + j < valid) ? t.v[n][j] : 0.f;
+    } else {
+        const uint32_t m0 = (t0 < valid ? 0x0000FFFFu : 0u) | (t0 + 1 < valid ? 0xFFFF0000u : 0u);
+        const uint32_t m1 = (t0 + 2 < valid ? 0x0000FFFFu : 0u) | (t0 + 3 < valid ? 0xFFFF0000u : 0u);
+#pragma unroll
+        for (int n = 0; n < D / 16; ++n) {
+            t.v[n][0] &= m0;
+            t.v[n][1] &= m1;
+        }
+    }
+}
+
+// ------------------------------------------------------------------ partition kernel
+
+template <int DT, int D, int NW>
+__global__ __launch_bounds__(NW *kWave) void pa_decode_partition(DecodeArgs a)
+{
+    using F = Frags<DT, D>;
+    using Elem = typename F::Elem;
+    constexpr int DP = D + 4;                       // padded LDS row (floats)
+
+    extern __shared__ float smem[];
+    float *s_m = smem;                              // [NW][16]
+    float *s_l = smem + NW * 16;                    // [NW][16]
+    int *s_bad = reinterpret_cast<int *>(smem + NW * 32);   // [NW]
+    float *s_o = smem + NW * 32 + 16;               // [NW][GS][DP]
+
+    const int p = blockIdx.x;
+    const int kvh = blockIdx.y / a.head_chunks;
+    const int chunk = blockIdx.y - kvh * a.head_chunks;
+    const int b = blockIdx.z;
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r = lane & 15;
+    const int g = lane >> 4;
+
+    const int gs = min(16, a.group - chunk * 16);   // q-heads handled here
+    const int hq0 = kvh * a.group + chunk * 16;     // first q-head of this workgroup
+
+    const int ctx = a.context_lens[b];
+    const int nblk_seq = (ctx + kBlock - 1) / kBlock;
+    const bool bad_ctx = ctx < 0 || ctx > a.max_context_len || nblk_seq > a.max_blocks;
+    const int lb_begin = p * a.part_blocks;
+    const int lb_end = min(lb_begin + a.part_blocks, nblk_seq);
+
+    if (bad_ctx || lb_begin >= lb_end) {
+        // Nothing to stream.  In split mode the reduce kernel handles empty and invalid
+        // sequences itself; in single-pass mode partition 0 writes zeros (empty
+        // context) or NaN (inconsistent context length).
+        if (!a.split && p == 0) {
+            const float fill = bad_ctx ? __builtin_nanf("") : 0.f;
+            for (int idx = tid; idx < gs * D; idx += NW * kWave)
+                store_elem<DT>(a.out, ((size_t)b * a.num_q_heads + hq0) * D + idx, fill);
+        }
+        return;
+    }
+
+    // q fragment of this lane's head (zero for padding heads beyond the group)
+    typename F::Q qf;
+    {
+        const bool hvalid = r < gs;
+        const Elem *qrow = static_cast<const Elem *>(a.q) +
+                           ((size_t)b * a.num_q_heads + hq0 + (hvalid ? r : 0)) * D;
+        qf.load(qrow, hvalid, g);
+    }
+
+    const int nb = lb_end - lb_begin;
+    const int my_n = nb > wave ? (nb - wave + NW - 1) / NW : 0;   // <= 64 (host-checked)
+    const int32_t *bt = a.block_tables + (size_t)b * a.max_blocks + lb_begin + wave;
+    // lane i holds the physical id of this wave's i-th block
+    int bt_lane = lane < my_n ? bt[(size_t)lane * NW] : 0;
+
+    const Elem *kbase = static_cast<const Elem *>(a.k_pool) + (size_t)kvh * kBlock * D;
+    const Elem *vbase = static_cast<const Elem *>(a.v_pool) + (size_t)kvh * kBlock * D;
+    const size_t blk_stride = (size_t)a.num_kv_heads * kBlock * D;
+
+    float m_run = -INFINITY;
+    float l_run = 0.f;
+    f32x4 o[D / 16];
+#pragma unroll
+    for (int n = 0; n < D / 16; ++n)
+        o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    bool tbl_bad = false;
+
+    auto phys_of = [&](int i) -> size_t {
+        int ph = __builtin_amdgcn_readlane(bt_lane, i);
+        if ((unsigned)ph >= (unsigned)a.num_blocks) {   // never read outside the pool
+            tbl_bad = true;
+            ph = 0;
+        }
+        return (size_t)ph * blk_stride;
+    };
+
+    auto process = [&](typename F::Tile &t, int i) {
+        const int lb = lb_begin + wave + i * NW;
+        const int valid = ctx - lb * kBlock;            // >= 1
+        f32x4 s = scores<DT, D>(t, qf);
+        f32x4 x = s * a.scale_log2;
+        if (valid < kBlock) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                x[j] = (4 * g + j < valid) ? x[j] : -INFINITY;
+            mask_tail_v<DT, D>(t, valid, g);
+        }
+        const float mx = wave_max_rows(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = fast_exp2(m_run - m_new);
+        f32x4 pw;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            pw[j] = fast_exp2(x[j] - m_new);
+#pragma unroll
+        for (int n = 0; n < D / 16; ++n)
+            o[n] *= alpha;
+        const f32x4 pu = accumulate_pv<DT, D>(t, pw, o);
+        l_run = l_run * alpha + ((pu[0] + pu[1]) + (pu[2] + pu[3]));
+        m_run = m_new;
+    };
+
+    if (my_n > 0) {
+        typename F::Tile t0, t1;
+        size_t off = phys_of(0);
+        t0.load(kbase + off, vbase + off, r, g);
+        for (int i = 0; i < my_n; i += 2) {
+            if (i + 1 < my_n) {
+                off = phys_of(i + 1);
+                t1.load(kbase + off, vbase + off, r, g);
+            }
+            process(t0, i);
+            if (i + 1 >= my_n)
+                break;
+            if (i + 2 < my_n) {
+                off = phys_of(i + 2);
+                t0.load(kbase + off, vbase + off, r, g);
+            }
+            process(t1, i + 1);
+        }
+    }
+    l_run = wave_sum_rows(l_run);
+
+    // ---- merge the NW waves' (m, l, O) in LDS
+    if (lane == 0)
+        s_bad[wave] = tbl_bad ? 1 : 0;
+    if (g == 0) {
+        s_m[wave * 16 + r] = m_run;
+        s_l[wave * 16 + r] = l_run;
+    }
+    if (r < gs) {
+#pragma unroll
+        for (int n = 0; n < D / 16; ++n)
+            *reinterpret_cast<f32x4 *>(s_o + (wave * gs + r) * DP + 16 * n + 4 * g) = o[n];
+    }
+    __syncthreads();
+
+    bool any_bad = false;
+#pragma unroll
+    for (int w = 0; w < NW; ++w)
+        any_bad |= s_bad[w] != 0;
+    const float qnan = __builtin_nanf("");
+    for (int idx = tid; idx < gs * D; idx += NW * kWave) {
+        const int h = idx / D;
+        const int e = idx - h * D;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < NW; ++w)
+            M = fmaxf(M, s_m[w * 16 + h]);
+        float num = 0.f, den = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            const float mw = s_m[w * 16 + h];
+            const float f = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
+            num += f * s_o[(w * gs + h) * DP + e];
+            den += f * s_l[w * 16 + h];
+        }
+        const size_t row = (size_t)b * a.num_q_heads + hq0 + h;
+        if (!a.split) {
+            const float val = any_bad ? qnan : (den > 0.f ? num / den : 0.f);
+            store_elem<DT>(a.out, row * D + e, val);
+        } else {
+            const size_t slot = row * a.num_parts + p;
+            a.ws_o[slot * D + e] = any_bad ? qnan : num;
+            if (e == 0) {
+                a.ws_m[slot] = any_bad ? qnan : M;
+                a.ws_l[slot] = any_bad ? qnan : den;
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------ reduce kernel
+
+// Merges the P partials of one (sequence, q-head):
+//   M = max_p m_p,  out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p
+// (the pages' combine rule, in the log2 domain the partition kernel uses).
+template <int DT, int D>
+__global__ __launch_bounds__(kWave) void pa_decode_reduce(DecodeArgs a)
+{
+    const int hq = blockIdx.x;
+    const int b = blockIdx.y;
+    const int ctx = a.context_lens[b];
+    const int nblk = (ctx + kBlock - 1) / kBlock;
+    const bool bad_ctx = ctx < 0 || ctx > a.max_context_len || nblk > a.max_blocks;
+    const int np = bad_ctx ? 0 : (nblk + a.part_blocks - 1) / a.part_blocks;
+    const size_t base = ((size_t)b * a.num_q_heads + hq) * a.num_parts;
+
+    float M = -INFINITY;
+    bool nan_seen = false;
+    for (int p = 0; p < np; ++p) {
+        const float m = a.ws_m[base + p];
+        nan_seen |= (m != m);
+        M = fmaxf(M, m);
+    }
+    float den = 0.f;
+    for (int p = 0; p < np; ++p) {
+        const float m = a.ws_m[base + p];
+        const float f = (m == -INFINITY) ? 0.f : fast_exp2(m - M);
+        den += f * a.ws_l[base + p];
+    }
+    const bool poison = bad_ctx || nan_seen;
+    for (int e = threadIdx.x; e < D; e += kWave) {
+        float num = 0.f;
+        for (int p = 0; p < np; ++p) {
+            const float m = a.ws_m[base + p];
+            const float f = (m == -INFINITY) ? 0.f : fast_exp2(m - M);
+            num += f * a.ws_o[(base + p) * D + e];
+        }
+        const float val = poison ? __builtin_nanf("") : (den > 0.f ? num / den : 0.f);
+        store_elem<DT>(a.out, ((size_t)b * a.num_q_heads + hq) * D + e, val);
+    }
+}
+
+template <int DT, int D>
+hipError_t launch_decode_t(const DecodeArgs &a, int num_seqs, hipStream_t stream)
+{
+    constexpr int NW = waves_per_group(D);
+    const int gs_max = min(16, a.group);
+    const size_t lds = sizeof(float) * (NW * 32 + 16 + (size_t)NW * gs_max * (D + 4));
+    auto kern = pa_decode_partition<DT, D, NW>;
+    if (lds > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess)
+            return e;
+    }
+    dim3 grid(a.num_parts, a.num_kv_heads * a.head_chunks, num_seqs);
+    hipLaunchKernelGGL(kern, grid, dim3(NW * kWave), lds, stream, a);
+    return hipGetLastError();
+}
+
+template <int DT, int D>
+hipError_t launch_reduce_t(const DecodeArgs &a, int num_seqs, hipStream_t stream)
+{
+    dim3 grid(a.num_q_heads, num_seqs);
+    hipLaunchKernelGGL((pa_decode_reduce<DT, D>), grid, dim3(kWave), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+#define PA_DISPATCH(FN, ...)                                                              \
+    switch (dtype * 1000 + head_dim) {                                                    \
+    case DT_F32 * 1000 + 64: return FN<DT_F32, 64>(__VA_ARGS__);                          \
+    case DT_F32 * 1000 + 128: return FN<DT_F32, 128>(__VA_ARGS__);                        \
+    case DT_F16 * 1000 + 64: return FN<DT_F16, 64>(__VA_ARGS__);                          \
+    case DT_F16 * 1000 + 128: return FN<DT_F16, 128>(__VA_ARGS__);                        \
+    case DT_F16 * 1000 + 256: return FN<DT_F16, 256>(__VA_ARGS__);                        \
+    case DT_BF16 * 1000 + 64: return FN<DT_BF16, 64>(__VA_ARGS__);                        \
+    case DT_BF16 * 1000 + 128: return FN<DT_BF16, 128>(__VA_ARGS__);                      \
+    case DT_BF16 * 1000 + 256: return FN<DT_BF16, 256>(__VA_ARGS__);                      \
+    default: return hipErrorInvalidValue;                                                 \
+    }
+
+hipError_t launch_decode(int dtype, int head_dim, const DecodeArgs &a, int num_seqs,
+                         hipStream_t stream)
+{
+    PA_DISPATCH(launch_decode_t, a, num_seqs, stream)
+}
+
+hipError_t launch_reduce(int dtype, int head_dim, const DecodeArgs &a, int num_seqs,
+                         hipStream_t stream)
+{
+    PA_DISPATCH(launch_reduce_t, a, num_seqs, stream)
+}
+
+}  // namespace pa

@@ -6,8 +6,10 @@ attention arithmetic, so both the GPU path and the fp64 CPU oracle can consume w
 it builds without sharing any of the method's code.
 
 Recipe (every workload is synthetic; the pages use no dataset for this path):
-  * values: numpy PCG64(seed) float32 normals times sigma, rounded to the storage
-    type by round-to-nearest-even (bf16 by bit arithmetic, f16 by numpy's cast);
+  * values: float32 normals times sigma from numpy PCG64 streams keyed by (seed, array,
+    chunk of ~4M values), rounded to the storage type by round-to-nearest-even (bf16 by
+    bit arithmetic, f16 by numpy's cast); the pool layout (block shuffle, fragmented
+    free list) comes from PCG64(seed);
   * pool: K is [N][Hkv][16][d], V is [N][Hkv][d][16]; every element starts as a NaN
     ("poison").  Only rows of live tokens get values, so any read of a free block,
     of another request's block, of a tail row past the context or of a table entry
@@ -22,9 +24,11 @@ Storage in numpy: f32 -> float32, f16 -> float16, bf16 -> uint16 bit patterns.
 """
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
 import hashlib
 import math
+import os
 from typing import List, Optional, Sequence, Tuple
 
 import numpy as np
@@ -46,16 +50,6 @@ def round_to_storage(x: np.ndarray, dtype: str) -> np.ndarray:
     u = x.view(np.uint32)
     rounded = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
     return rounded.astype(np.uint16)
-
-
-def _normals(rng: np.random.Generator, n: int, sigma: float) -> np.ndarray:
-    out = np.empty(n, np.float32)
-    for s in range(0, n, _CHUNK):
-        e = min(n, s + _CHUNK)
-        out[s:e] = rng.standard_normal(e - s, dtype=np.float32)
-    if sigma != 1.0:
-        out *= np.float32(sigma)
-    return out
 
 
 @dataclasses.dataclass
@@ -80,19 +74,28 @@ class Spec:
 
 @dataclasses.dataclass
 class Workload:
+    """Inputs of one decode step (one layer).
+
+    Only live blocks are held on the host: k_live / v_live hold the blocks listed in
+    live_blocks (ascending physical id) followed by one entirely poisoned block.  The
+    full pool of num_blocks blocks is every other block poisoned; host_pools() and
+    device_pools() materialise it.  oracle_view() relabels the live blocks to
+    0..n-1 (and the poisoned block to n), which leaves every logical K/V row unchanged.
+    """
     spec: Spec
     dtype: str
     q: np.ndarray                   # [B][Hq][d]
-    k_pool: np.ndarray              # [N][Hkv][16][d], before the append
-    v_pool: np.ndarray              # [N][Hkv][d][16], before the append
+    num_blocks: int                 # size of the physical pool
+    live_blocks: np.ndarray         # [n] distinct physical ids holding live tokens
+    k_live: np.ndarray              # [n+1][Hkv][16][d]: live blocks, then a poison block
+    v_live: np.ndarray              # [n+1][Hkv][d][16]
     k_new: np.ndarray               # [T][Hkv][d]
     v_new: np.ndarray
-    slot_mapping: np.ndarray        # [T] int32
-    block_tables: np.ndarray        # [B][max_blocks] int32
+    slot_mapping: np.ndarray        # [T] int32, physical slots
+    block_tables: np.ndarray        # [B][max_blocks] int32, physical ids
     context_lens: np.ndarray        # [B] int32
     scale: np.float32
-    live_blocks: np.ndarray         # distinct physical ids holding live tokens
-    poison_block: int               # id of a block that is entirely poisoned
+    poison_block: int               # physical id of a block that is entirely poisoned
 
     @property
     def num_seqs(self):
@@ -104,19 +107,19 @@ class Workload:
 
     @property
     def num_kv_heads(self):
-        return self.k_pool.shape[1]
+        return self.k_live.shape[1]
 
     @property
     def head_dim(self):
         return self.q.shape[2]
 
     @property
-    def num_blocks(self):
-        return self.k_pool.shape[0]
-
-    @property
     def max_context_len(self):
         return int(self.context_lens.max()) if self.context_lens.size else 0
+
+    @property
+    def elem_bytes(self):
+        return ELEM_BYTES[self.dtype]
 
     def logical_kv_bytes(self) -> int:
         """K+V bytes of every (token, kv-head) the step attends to, per sequence."""
@@ -134,11 +137,42 @@ class Workload:
         rows = sum(seen.values())
         return rows * self.num_kv_heads * 2 * self.head_dim * ELEM_BYTES[self.dtype]
 
+    def pool_shapes(self):
+        hkv, d = self.num_kv_heads, self.head_dim
+        return (self.num_blocks, hkv, BLOCK, d), (self.num_blocks, hkv, d, BLOCK)
+
+    def host_pools(self):
+        """Full poisoned pools with the live blocks in place (before the append)."""
+        ks, vs = self.pool_shapes()
+        k = _poison(ks, self.dtype)
+        v = _poison(vs, self.dtype)
+        k[self.live_blocks] = self.k_live[:-1]
+        v[self.live_blocks] = self.v_live[:-1]
+        return k, v
+
+    def compact_index(self, phys: np.ndarray) -> np.ndarray:
+        """Physical id -> index in k_live/v_live (the poisoned block maps to n)."""
+        phys = np.asarray(phys)
+        pos = np.searchsorted(self.live_blocks, phys)
+        pos = np.minimum(pos, self.live_blocks.size)
+        hit = (pos < self.live_blocks.size) & \
+            (self.live_blocks[np.minimum(pos, self.live_blocks.size - 1)] == phys)
+        return np.where(hit, pos, self.live_blocks.size).astype(np.int32)
+
+    def oracle_view(self):
+        """(k_pool, v_pool, block_tables, slot_mapping) over the relabelled live blocks."""
+        tables = self.compact_index(self.block_tables)
+        slots = self.slot_mapping.copy()
+        ok = slots >= 0
+        slots[ok] = self.compact_index(slots[ok] // BLOCK) * BLOCK + slots[ok] % BLOCK
+        return self.k_live, self.v_live, tables, slots
+
     def digest(self) -> str:
         h = hashlib.sha256()
-        for a in (self.q, self.k_pool, self.v_pool, self.k_new, self.v_new, self.slot_mapping,
-                  self.block_tables, self.context_lens):
+        for a in (self.q, self.live_blocks, self.k_live, self.v_live, self.k_new, self.v_new,
+                  self.slot_mapping, self.block_tables, self.context_lens):
             h.update(np.ascontiguousarray(a).view(np.uint8).tobytes())
+        h.update(str(self.num_blocks).encode())
         return h.hexdigest()
 
 
@@ -148,6 +182,50 @@ def _poison(shape, dtype):
     if dtype == "f16":
         return np.full(shape, NAN_BITS["f16"], np.uint16).view(np.float16)
     return np.full(shape, NAN_BITS["bf16"], np.uint16)
+
+
+def _threads() -> int:
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def _chunk_rng(seed: int, tag: int, chunk: int) -> np.random.Generator:
+    """Independent PCG64 stream per (seed, array tag, chunk): fixed chunking makes the
+    values independent of how many threads fill them."""
+    return np.random.Generator(np.random.PCG64([seed, tag, chunk]))
+
+
+def _fill_normals(seed: int, tag: int, dst: np.ndarray, sigma: float, dtype: str,
+                  transpose_blocks: bool = False):
+    """Fill dst (storage dtype) with sigma * N(0, 1) rounded to the storage type.
+
+    transpose_blocks: dst is [n][Hkv][d][16] and values are drawn in [n][Hkv][16][d]
+    order (a V pool block drawn token-major, stored token-minor).
+    """
+    if dst.size == 0:
+        return
+    lead = dst.shape[0]
+    per = dst.size // lead
+    rows = max(1, _CHUNK // per)              # leading-index rows per chunk
+    n_chunks = (lead + rows - 1) // rows
+
+    def work(c):
+        a, b = c * rows, min(lead, (c + 1) * rows)
+        shape = (b - a,) + (dst.shape[1:] if not transpose_blocks else
+                            (dst.shape[1], dst.shape[3], dst.shape[2]))
+        vals = _chunk_rng(seed, tag, c).standard_normal(size=(b - a) * per, dtype=np.float32)
+        if sigma != 1.0:
+            vals *= np.float32(sigma)
+        vals = round_to_storage(vals, dtype).reshape(shape)
+        if transpose_blocks:
+            dst[a:b] = vals.transpose(0, 1, 3, 2)
+        else:
+            dst[a:b] = vals
+
+    if n_chunks == 1:
+        work(0)
+    else:
+        with concurrent.futures.ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(work, range(n_chunks)))
 
 
 def build(spec: Spec, seed: Optional[int] = None) -> Workload:
@@ -177,7 +255,7 @@ def build(spec: Spec, seed: Optional[int] = None) -> Workload:
         n_pool = max(math.ceil(n_live / spec.free_fraction), n_live + 1)
         n_free = math.ceil(spec.free_fraction * n_pool)
         perm = rng.permutation(n_pool)
-        free_list = perm[:n_free]           # a random 30% (say) in random order
+        free_list = perm[:n_free]           # a random fraction of the ids, in random order
     else:
         n_pool = spec.exact_pool or (n_live + spec.spare_blocks)
         assert n_pool >= n_live
@@ -194,7 +272,6 @@ def build(spec: Spec, seed: Optional[int] = None) -> Workload:
     group_blocks = {}
     for seqs, n_sh in spec.prefix_groups:
         group_blocks[tuple(seqs)] = take(n_sh)
-    unused = set(range(n_pool))
     tables = np.zeros((B, maxb), np.int32)
     for b in range(B):
         row = []
@@ -204,53 +281,53 @@ def build(spec: Spec, seed: Optional[int] = None) -> Workload:
         tables[b, :len(row)] = row
     live = np.unique(np.concatenate([tables[b, :nblk[b]] for b in range(B)])) if n_live else \
         np.zeros(0, np.int64)
-    unused.difference_update(int(x) for x in live)
-    poison_block = min(unused) if unused else -1
+    used = np.zeros(n_pool, bool)
+    used[live] = True
+    unused = np.flatnonzero(~used)
+    poison_block = int(unused[0]) if unused.size else -1
     for b in range(B):
         if nblk[b] < maxb:
             assert poison_block >= 0, "table padding needs a poisoned spare block"
             tables[b, nblk[b]:] = poison_block
 
-    # ---- values: q, then K and V of every live block (ascending id), then new rows
-    q = round_to_storage(_normals(rng, B * hq * d, spec.sigma), dt).reshape(B, hq, d)
-    k_pool = _poison((n_pool, hkv, BLOCK, d), dt)
-    v_pool = _poison((n_pool, hkv, d, BLOCK), dt)
-    per_block = hkv * BLOCK * d
-    step = max(1, _CHUNK // per_block)
-    for which in ("k", "v"):
-        for s in range(0, live.size, step):
-            ids = live[s:s + step]
-            vals = round_to_storage(_normals(rng, ids.size * per_block, spec.sigma), dt)
-            vals = vals.reshape(ids.size, hkv, BLOCK, d)
-            if which == "k":
-                k_pool[ids] = vals
-            else:
-                v_pool[ids] = vals.transpose(0, 1, 3, 2)
+    # ---- values: each array from its own seeded streams (tags 1..5)
+    q = np.empty((B, hq, d), STORAGE[dt])
+    _fill_normals(seed, 1, q, spec.sigma, dt)
+    k_live = np.empty((live.size + 1, hkv, BLOCK, d), STORAGE[dt])
+    v_live = np.empty((live.size + 1, hkv, d, BLOCK), STORAGE[dt])
+    _fill_normals(seed, 2, k_live[:-1], spec.sigma, dt)
+    _fill_normals(seed, 3, v_live[:-1], spec.sigma, dt, transpose_blocks=True)
+    k_live[-1] = _poison((hkv, BLOCK, d), dt)
+    v_live[-1] = _poison((hkv, d, BLOCK), dt)
+    pos_of = {int(p): i for i, p in enumerate(live)}
 
     # tail rows past each context stay poisoned
     for b in range(B):
         n = int(ctx[b])
         if n % BLOCK:
-            p = tables[b, n // BLOCK]
-            k_pool[p, :, n % BLOCK:, :] = _poison((hkv, BLOCK - n % BLOCK, d), dt)
-            v_pool[p, :, :, n % BLOCK:] = _poison((hkv, d, BLOCK - n % BLOCK), dt)
+            i = pos_of[int(tables[b, n // BLOCK])]
+            k_live[i, :, n % BLOCK:, :] = _poison((hkv, BLOCK - n % BLOCK, d), dt)
+            v_live[i, :, :, n % BLOCK:] = _poison((hkv, d, BLOCK - n % BLOCK), dt)
 
     # the step's own token (ctx-1): poisoned in the pool, delivered by the append
     appending = [b for b in range(B) if spec.append and ctx[b] > 0]
     T = len(appending)
-    k_new = round_to_storage(_normals(rng, T * hkv * d, spec.sigma), dt).reshape(T, hkv, d)
-    v_new = round_to_storage(_normals(rng, T * hkv * d, spec.sigma), dt).reshape(T, hkv, d)
+    k_new = np.empty((T, hkv, d), STORAGE[dt])
+    v_new = np.empty((T, hkv, d), STORAGE[dt])
+    _fill_normals(seed, 4, k_new, spec.sigma, dt)
+    _fill_normals(seed, 5, v_new, spec.sigma, dt)
     slots = np.full(T, -1, np.int32)
-    for i, b in enumerate(appending):
+    for j, b in enumerate(appending):
         pos = int(ctx[b]) - 1
         p = int(tables[b, pos // BLOCK])
-        k_pool[p, :, pos % BLOCK, :] = _poison((hkv, d), dt)
-        v_pool[p, :, :, pos % BLOCK] = _poison((hkv, d), dt)
-        slots[i] = p * BLOCK + pos % BLOCK
+        i = pos_of[p]
+        k_live[i, :, pos % BLOCK, :] = _poison((hkv, d), dt)
+        v_live[i, :, :, pos % BLOCK] = _poison((hkv, d), dt)
+        slots[j] = p * BLOCK + pos % BLOCK
 
     scale = np.float32(1.0 / math.sqrt(d))
-    return Workload(spec, dt, q, k_pool, v_pool, k_new, v_new, slots, tables,
-                    ctx.astype(np.int32), scale, live, poison_block)
+    return Workload(spec, dt, q, n_pool, live.astype(np.int64), k_live, v_live, k_new, v_new,
+                    slots, tables, ctx.astype(np.int32), scale, poison_block)
 
 
 # ----------------------------------------------------------------- named configs

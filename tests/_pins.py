@@ -38,7 +38,9 @@ def small_specs():
 
 
 def appended(w, lib):
-    return O.cache_append(w.k_pool, w.v_pool, w.k_new, w.v_new, w.slot_mapping, w.dtype, lib=lib)
+    """Full host pools after the oracle's append of the step's rows."""
+    kp, vp = w.host_pools()
+    return O.cache_append(kp, vp, w.k_new, w.v_new, w.slot_mapping, w.dtype, lib=lib)
 
 
 def gather_contig(w, k_pool, v_pool):
@@ -124,7 +126,7 @@ def check_append(lib):
     for spec in small_specs():
         w = W.build(spec)
         k2, v2 = appended(w, lib)
-        kref, vref = w.k_pool.copy(), w.v_pool.copy()
+        kref, vref = w.host_pools()
         for i, s in enumerate(w.slot_mapping.tolist()):
             if s >= 0:
                 kref[s // BLOCK, :, s % BLOCK, :] = w.k_new[i]
@@ -134,9 +136,10 @@ def check_append(lib):
     # negative slots write nothing
     w = W.build(small_specs()[1])
     skip = np.full_like(w.slot_mapping, -1)
-    k2, v2 = O.cache_append(w.k_pool, w.v_pool, w.k_new, w.v_new, skip, w.dtype, lib=lib)
-    assert k2.view(np.uint8).tobytes() == w.k_pool.view(np.uint8).tobytes()
-    assert v2.view(np.uint8).tobytes() == w.v_pool.view(np.uint8).tobytes()
+    kp, vp = w.host_pools()
+    k2, v2 = O.cache_append(kp, vp, w.k_new, w.v_new, skip, w.dtype, lib=lib)
+    assert k2.view(np.uint8).tobytes() == kp.view(np.uint8).tobytes()
+    assert v2.view(np.uint8).tobytes() == vp.view(np.uint8).tobytes()
 
 
 def check_bruteforce(lib):
@@ -186,9 +189,11 @@ def check_weight_sum(lib):
 
 
 def _hand_workload(dtype, d, n, hq=2, hkv=1):
-    """An unpoisoned single-sequence workload whose arrays the caller overwrites."""
+    """An unpoisoned single-sequence workload; returns it with its full host pools."""
     spec = W.Spec("hand", dtype, hq, hkv, d, [n], seed=5, spare_blocks=1, append=False)
-    return W.build(spec)
+    w = W.build(spec)
+    kp, vp = w.host_pools()
+    return w, kp, vp
 
 
 def check_closed_forms(lib):
@@ -196,38 +201,38 @@ def check_closed_forms(lib):
         st = W.STORAGE[dtype]
         half = W.round_to_storage(np.array([0.5], np.float32), dtype)[0]
         # one key: the output is that key's value row, exactly
-        w = _hand_workload(dtype, 16, 1)
-        out, _ = O.decode_paged(w.q, w.k_pool, w.v_pool, dtype, w.block_tables, w.context_lens,
-                                w.scale, lib=lib)
-        v0 = to_f64(w.v_pool[w.block_tables[0, 0], 0, :, 0], dtype)
+        w, kp, vp = _hand_workload(dtype, 16, 1)
+        out, _ = O.decode_paged(w.q, kp, vp, dtype, w.block_tables, w.context_lens, w.scale,
+                                lib=lib)
+        v0 = to_f64(vp[w.block_tables[0, 0], 0, :, 0], dtype)
         assert np.array_equal(out[0, 0], v0) and np.array_equal(out[0, 1], v0)
         # q = 0: uniform weights, output is the mean of the value rows
-        w = _hand_workload(dtype, 16, 40)
+        w, kp, vp = _hand_workload(dtype, 16, 40)
         w.q[...] = np.zeros(1, st)[0]
-        out, _ = O.decode_paged(w.q, w.k_pool, w.v_pool, dtype, w.block_tables, w.context_lens,
-                                w.scale, lib=lib)
-        K, V = gather_contig(w, w.k_pool, w.v_pool)
+        out, _ = O.decode_paged(w.q, kp, vp, dtype, w.block_tables, w.context_lens, w.scale,
+                                lib=lib)
+        K, V = gather_contig(w, kp, vp)
         Vf = to_f64(V, dtype)[0, 0, :40]
         mean = np.array([math.fsum(Vf[:, e]) / 40 for e in range(16)])
         assert np.max(np.abs(out[0, 0] - mean)) <= 1e-14
         # every value row equal to 0.5: the output is exactly 0.5 (power-of-two scaling)
-        w = _hand_workload(dtype, 16, 40)
-        w.v_pool[...] = half
-        out, _ = O.decode_paged(w.q, w.k_pool, w.v_pool, dtype, w.block_tables, w.context_lens,
-                                w.scale, lib=lib)
+        w, kp, vp = _hand_workload(dtype, 16, 40)
+        vp[...] = half
+        out, _ = O.decode_paged(w.q, kp, vp, dtype, w.block_tables, w.context_lens, w.scale,
+                                lib=lib)
         assert (out == 0.5).all()
         # one key dominating by a score gap of 1024: its weight is 1, the rest underflow to 0
-        w = _hand_workload(dtype, 16, 40)
+        w, kp, vp = _hand_workload(dtype, 16, 40)
         sixteen = W.round_to_storage(np.array([16.0], np.float32), dtype)[0]
         zero = np.zeros(1, st)[0]
         w.q[...] = sixteen
-        w.k_pool[...] = zero
+        kp[...] = zero
         j = 23
         p = w.block_tables[0, j // BLOCK]
-        w.k_pool[p, 0, j % BLOCK, :] = sixteen
-        out, _ = O.decode_paged(w.q, w.k_pool, w.v_pool, dtype, w.block_tables, w.context_lens,
-                                w.scale, lib=lib)
-        vj = to_f64(w.v_pool[p, 0, :, j % BLOCK], dtype)
+        kp[p, 0, j % BLOCK, :] = sixteen
+        out, _ = O.decode_paged(w.q, kp, vp, dtype, w.block_tables, w.context_lens, w.scale,
+                                lib=lib)
+        vj = to_f64(vp[p, 0, :, j % BLOCK], dtype)
         assert np.array_equal(out[0, 0], vj)
 
 

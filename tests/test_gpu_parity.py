@@ -1,0 +1,236 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 CPU oracle.
+
+Bars: append and block-table indexing bit-exact; attention outputs within max |err|
+<= 1e-5 for fp32 and max <= 2e-2, mean <= 5e-3 for f16/bf16 (fp32 accumulation).
+Every workload is seeded and synthetic; pools are NaN-poisoned outside live rows, so
+a stray read shows up as NaN.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from paged_kv_cache_161_amd import binding as PA
+from paged_kv_cache_161_amd import workloads as W
+from tests import devutil as U
+
+pytestmark = pytest.mark.gpu
+
+BLOCK = 16
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def hip_library():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    PA.load()   # raises if the HIP library is not built
+
+
+_CACHE = {}
+
+
+def config(i):
+    if i not in _CACHE:
+        _CACHE.clear()
+        _CACHE[i] = W.make_config(i)
+    return _CACHE[i]
+
+
+def oracle_decode(w):
+    """Oracle result for the workload: append then attend, over the relabelled pool."""
+    kp, vp, bt, sl = w.oracle_view()
+    kp, vp = O.cache_append(kp, vp, w.k_new, w.v_new, sl, w.dtype)
+    out, _ = O.decode_paged(w.q, kp, vp, w.dtype, bt, w.context_lens, w.scale)
+    return out
+
+
+def gpu_step(w, partition_tokens=0, pools=None):
+    """Append then decode on the GPU; returns (out fp64, k_pool, v_pool)."""
+    kp, vp = pools if pools is not None else U.device_pools(w)
+    d = U.device_inputs(w)
+    PA.cache_append(kp, vp, d["k_new"], d["v_new"], d["slot_mapping"])
+    out = PA.decode(d["q"], kp, vp, d["block_tables"], d["context_lens"], float(w.scale),
+                    w.max_context_len, partition_tokens)
+    torch.cuda.synchronize()
+    return U.widen(U.from_dev(out, w.dtype), w.dtype), kp, vp
+
+
+def check(w, got, ref, label):
+    ok, mx, mean = U.tolerance_ok(got, ref, w.dtype)
+    say(f"{label}: max|err| {mx:.3e} mean|err| {mean:.3e}")
+    assert np.isfinite(got).all(), f"{label}: non-finite output"
+    assert ok, f"{label}: max {mx:.3e} mean {mean:.3e} beyond the {w.dtype} bar"
+
+
+SMALL = [
+    W.Spec("bf16_g8_d128", "bf16", 16, 2, 128, [1, 15, 16, 17, 100, 257], seed=101,
+           spare_blocks=3),
+    W.Spec("f16_g1_d128", "f16", 4, 4, 128, [33, 64, 5], seed=102, spare_blocks=2),
+    W.Spec("bf16_g4_d64", "bf16", 8, 2, 64, [40, 1, 96], seed=103, spare_blocks=1),
+    W.Spec("f16_g16_d256", "f16", 32, 2, 256, [300, 7], seed=104, spare_blocks=1),
+    W.Spec("bf16_g32_d128", "bf16", 64, 2, 128, [129, 31], seed=105, spare_blocks=1),
+    W.Spec("f32_g4_d64", "f32", 8, 2, 64, [37, 200, 0], seed=106, spare_blocks=1),
+    W.Spec("f32_g2_d128", "f32", 4, 2, 128, [65, 16], seed=107, spare_blocks=1),
+    W.Spec("bf16_g5_d128", "bf16", 10, 2, 128, [190, 3, 0, 512], seed=108, spare_blocks=1),
+    W.Spec("bf16_empty_batch_rows", "bf16", 8, 8, 128, [0, 0, 5], seed=109, spare_blocks=1),
+]
+
+
+@pytest.mark.parametrize("spec", SMALL, ids=lambda s: s.name)
+@pytest.mark.parametrize("ptok", [0, 16, 48, 256])
+def test_decode_small(spec, ptok):
+    w = W.build(spec)
+    say(f"[small] {spec.name} partition_tokens={ptok}")
+    ref = oracle_decode(w)
+    got, _, _ = gpu_step(w, ptok)
+    check(w, got, ref, f"{spec.name} p{ptok}")
+    zero = w.context_lens == 0
+    assert (got[zero] == 0).all()
+
+
+@pytest.mark.parametrize("i", [1, 2, 3, 4, 5])
+def test_append_bit_exact(i):
+    """The whole pool after the GPU append equals the oracle's append, byte for byte."""
+    w = config(i)
+    say(f"[append] config {i} T={w.slot_mapping.size}")
+    kp, vp = U.device_pools(w)
+    k0, v0 = kp.clone(), vp.clone()
+    d = U.device_inputs(w)
+    PA.cache_append(kp, vp, d["k_new"], d["v_new"], d["slot_mapping"])
+    torch.cuda.synchronize()
+    touched = np.unique(w.slot_mapping[w.slot_mapping >= 0] // BLOCK)
+    # expected touched blocks: the oracle's append on just those blocks
+    idx = w.compact_index(touched)
+    ke, ve = w.k_live[idx].copy(), w.v_live[idx].copy()
+    local = {int(p): j for j, p in enumerate(touched)}
+    slots = np.array([local[int(s) // BLOCK] * BLOCK + int(s) % BLOCK if s >= 0 else -1
+                      for s in w.slot_mapping], np.int32)
+    ke, ve = O.cache_append(ke, ve, w.k_new, w.v_new, slots, w.dtype, inplace=True)
+    tdev = torch.from_numpy(touched).cuda()
+    assert U.from_dev(kp[tdev], w.dtype).tobytes() == ke.tobytes()
+    assert U.from_dev(vp[tdev], w.dtype).tobytes() == ve.tobytes()
+    # every other byte of both pools is unchanged
+    kp[tdev] = k0[tdev]
+    vp[tdev] = v0[tdev]
+    assert torch.equal(U.int_view(kp), U.int_view(k0))
+    assert torch.equal(U.int_view(vp), U.int_view(v0))
+
+
+def test_append_skips_padding_and_out_of_pool_slots():
+    w = W.build(SMALL[0])
+    kp, vp = U.device_pools(w)
+    k0, v0 = kp.clone(), vp.clone()
+    d = U.device_inputs(w)
+    bad = torch.tensor([-1, w.num_blocks * BLOCK, 2 ** 31 - 1, -7] * 2, dtype=torch.int32,
+                       device="cuda")[: d["slot_mapping"].numel()]
+    PA.cache_append(kp, vp, d["k_new"], d["v_new"], bad)
+    torch.cuda.synchronize()
+    assert torch.equal(U.int_view(kp), U.int_view(k0))
+    assert torch.equal(U.int_view(vp), U.int_view(v0))
+
+
+@pytest.mark.parametrize("i", [1, 2, 3, 4, 5])
+def test_decode_config(i):
+    w = config(i)
+    say(f"[decode] config {i} {w.spec.name} B={w.num_seqs} Hq={w.num_q_heads} "
+        f"Hkv={w.num_kv_heads} d={w.head_dim} max_ctx={w.max_context_len} "
+        f"auto partition={PA.partition_tokens(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.max_context_len)}")
+    ref = oracle_decode(w)
+    got, _, _ = gpu_step(w)
+    check(w, got, ref, f"config {i}")
+
+
+@pytest.mark.parametrize("ptok", [16, 512, 4096])
+def test_decode_config3_forced_partitions(ptok):
+    """Split-context with other partition lengths meets the same bar."""
+    w = config(3)
+    say(f"[split] config 3 partition_tokens={ptok}")
+    ref = oracle_decode(w)
+    got, _, _ = gpu_step(w, ptok)
+    check(w, got, ref, f"config 3 p{ptok}")
+
+
+def _probe_workload(dtype, d, ctx, hkv=2, group=4):
+    """One sequence per target position j: q = 1, keys 0 except key j = 16, and value
+    rows holding small integers that name (physical block mod 256, row, kv-head)."""
+    B = ctx
+    spec = W.Spec(f"probe_{dtype}_{d}", dtype, hkv * group, hkv, d, [ctx] * B, seed=7,
+                  spare_blocks=1, append=False)
+    w = W.build(spec)
+    one = W.round_to_storage(np.array([1.0], np.float32), dtype)[0]
+    sixteen = W.round_to_storage(np.array([16.0], np.float32), dtype)[0]
+    zero = np.zeros(1, W.STORAGE[dtype])[0]
+    w.q[...] = one
+    live = w.k_live[:-1]
+    vl = w.v_live[:-1]
+    live[...] = zero
+    codes = np.zeros(vl.shape, np.float32)                 # [n][hkv][d][16]
+    codes[:, :, 0, :] = (w.live_blocks % 256)[:, None, None]
+    codes[:, :, 1, :] = np.arange(BLOCK)[None, None, :]
+    codes[:, :, 2, :] = np.arange(hkv)[None, :, None]
+    vl[...] = W.round_to_storage(codes.reshape(-1), dtype).reshape(vl.shape)
+    for b in range(B):
+        j = b
+        p = int(w.block_tables[b, j // BLOCK])
+        i = int(np.searchsorted(w.live_blocks, p))
+        live[i, :, j % BLOCK, :] = sixteen
+    # poison rows past the context again (the generator's tail rows were overwritten)
+    if ctx % BLOCK:
+        for b in range(B):
+            p = int(w.block_tables[b, ctx // BLOCK])
+            i = int(np.searchsorted(w.live_blocks, p))
+            nanv = W._poison((hkv, BLOCK - ctx % BLOCK, d), dtype)
+            live[i, :, ctx % BLOCK:, :] = nanv
+            vl[i, :, :, ctx % BLOCK:] = nanv.transpose(0, 2, 1)
+    return w
+
+
+@pytest.mark.parametrize("dtype,d,ctx,ptok", [("bf16", 128, 45, 0), ("f16", 128, 45, 0),
+                                              ("f32", 64, 45, 0), ("bf16", 128, 300, 32),
+                                              ("bf16", 64, 33, 16)])
+def test_gather_probe(dtype, d, ctx, ptok):
+    """Each output must be exactly the value row of the one selected token: proves which
+    physical (block, row, kv-head) the kernel read for every logical position."""
+    w = _probe_workload(dtype, d, ctx)
+    say(f"[probe] {dtype} d={d} ctx={ctx} partition_tokens={ptok}")
+    got, _, _ = gpu_step(w, ptok)
+    G = w.num_q_heads // w.num_kv_heads
+    for b in range(w.num_seqs):
+        j = b
+        p = int(w.block_tables[b, j // BLOCK])
+        for h in range(w.num_q_heads):
+            want = np.zeros(d)
+            want[:3] = [p % 256, j % BLOCK, h // G]
+            assert np.array_equal(got[b, h], want), (b, h, got[b, h, :4], want[:4])
+
+
+def test_bad_table_entry_and_context_give_nan_not_fault():
+    w = W.build(SMALL[0])
+    kp, vp = U.device_pools(w)
+    d = U.device_inputs(w)
+    bt = d["block_tables"].clone()
+    bt[4, 1] = w.num_blocks + 5           # sequence 4 (100 tokens) reads block 1
+    cl = d["context_lens"].clone()
+    cl[5] = w.max_context_len + 1         # beyond the host bound
+    cl[0] = -3
+    PA.cache_append(kp, vp, d["k_new"], d["v_new"], d["slot_mapping"])
+    out = PA.decode(d["q"], kp, vp, bt, cl, float(w.scale), w.max_context_len)
+    torch.cuda.synchronize()
+    got = U.widen(U.from_dev(out, w.dtype), w.dtype)
+    assert np.isnan(got[[0, 4, 5]]).all()
+    assert np.isfinite(got[[1, 2, 3]]).all()
+
+
+def test_rejects_unsupported_partition():
+    w = W.build(SMALL[0])
+    kp, vp = U.device_pools(w)
+    d = U.device_inputs(w)
+    with pytest.raises(PA.PaError):
+        PA.decode(d["q"], kp, vp, d["block_tables"], d["context_lens"], float(w.scale),
+                  w.max_context_len, partition_tokens=8)
