@@ -12,8 +12,7 @@ layers of a real step do, so K/V is not reused from the 256 MB last-level cache.
 Printed: ONE JSON line on stdout.
   value      KV GB/s over the whole step (algorithmic K+V bytes / wall time per step)
   roofline   the decode call (partition + reduce kernels), timed per launch with HIP
-             events on the launching stream after a 1 GiB cache-flush write, against
-             the 8 TB/s HBM peak
+             events on the launching stream, against the 8 TB/s HBM peak
   cpu_baseline  the fp64 oracle on the host cores, on the same workload
 Progress goes to stderr.
 """
@@ -29,7 +28,7 @@ import torch
 
 HBM_PEAK_GBS = 8000.0
 LAYERS = 4
-FLUSH_BYTES = 1 << 30
+CALIBRATION_BYTES = 256 << 20
 HEADLINE = 3
 
 
@@ -46,7 +45,10 @@ def parse():
                     help="workload id 1..5 (default: the Llama-70B GQA headline)")
     ap.add_argument("--partition-tokens", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--roofline-launches", type=int, default=50)
+    ap.add_argument("--roofline-launches", type=int, default=100)
+    ap.add_argument("--calibrate", action="store_true",
+                    help="also run one 256 MiB device copy (a kernel of known traffic for "
+                         "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
 
 
@@ -100,7 +102,6 @@ def main():
     ws_bytes = PA.workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim,
                                   w.max_context_len, ptok)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
-    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
     kv_bytes = w.logical_kv_bytes()
     uniq_bytes = w.unique_kv_bytes()
     scale = float(w.scale)
@@ -111,6 +112,16 @@ def main():
         PA.cache_append(kp, vp, d["k_new"], d["v_new"], d["slot_mapping"])
         PA.decode(d["q"], kp, vp, d["block_tables"], d["context_lens"], scale, max_ctx, ptok,
                   out=out, workspace=ws)
+
+    if args.calibrate:
+        src = torch.ones(CALIBRATION_BYTES // 2, dtype=torch.int16, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy: {CALIBRATION_BYTES} bytes read, {CALIBRATION_BYTES} "
+            "written")
+        del src, dst
 
     for i in range(args.warmup):
         step(i)
@@ -126,24 +137,26 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     log(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.1f} us/step")
 
-    # roofline: event-timed decode calls, each after a cache-flushing write
+    # roofline: the decode call timed per launch with HIP events on its stream; the
+    # append between launches is outside the events, and the layer rotation keeps
+    # each launch's K/V out of the caches (1.5 GiB of other pools in between)
     stream = torch.cuda.current_stream(dev)
-    durs = []
-    for i in range(args.roofline_launches):
+    n_l = args.roofline_launches
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n_l)]
+    for i in range(n_l):
         kp, vp = pools[i % LAYERS]
-        flush.fill_(i & 0xFF)
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
+        PA.cache_append(kp, vp, d["k_new"], d["v_new"], d["slot_mapping"])
+        ev[i][0].record(stream)
         PA.decode(d["q"], kp, vp, d["block_tables"], d["context_lens"], scale, max_ctx, ptok,
                   out=out, workspace=ws)
-        e1.record(stream)
-        e1.synchronize()
-        durs.append(e0.elapsed_time(e1) * 1e-3)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    durs = [a.elapsed_time(b) * 1e-3 for a, b in ev]
     dur = statistics.mean(durs)
     achieved = kv_bytes / dur / 1e9
     log(f"[bench] decode call: mean {dur * 1e6:.1f} us (min {min(durs) * 1e6:.1f}, "
-        f"max {max(durs) * 1e6:.1f}) over {len(durs)} flushed launches -> {achieved:.0f} GB/s")
+        f"max {max(durs) * 1e6:.1f}) over {n_l} launches -> {achieved:.0f} GB/s")
 
     # parity on the timed inputs (sampled rows against the oracle)
     parity = None

@@ -5,6 +5,7 @@
 #include <math.h>
 #include <stdint.h>
 
+
 #include "../../include/paged_attention.h"
 #include "pa_common.h"
 
@@ -51,20 +52,22 @@ int32_t choose_part_blocks(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv
         return 1;
     if (partition_tokens > 0)
         return partition_tokens / kBlock;
-    // Auto: about 16 blocks per wave (64 per 4-wave workgroup, 512 KiB of K+V at
-    // d = 128 16-bit) keeps ragged batches balanced; when that leaves fewer workgroups
-    // than the GPU keeps resident, cut finer so every resident slot streams, but not
-    // below ~2 blocks per wave.
+    // Auto: as few partitions as fit (a partition is at most 64 blocks per wave), so
+    // each workgroup streams long runs and no merge pass is needed when a sequence fits
+    // one; cut finer only when that leaves fewer workgroups than the GPU has CUs, but
+    // not below ~2 blocks per wave.
     const int32_t nw = pa::waves_per_group(head_dim);
     const int64_t chunks = (num_q_heads / num_kv_heads + 15) / 16;
     const int64_t units = (int64_t)num_seqs * num_kv_heads * chunks;
-    const int64_t target_blocks = 16LL * nw;
-    int64_t parts = (max_blocks + target_blocks - 1) / target_blocks;
-    const int64_t fill = (pa::kResidentGroups + units - 1) / units;
-    const int64_t cap = (max_blocks + 2 * nw - 1) / (2 * nw);
-    const int64_t want = fill < cap ? fill : cap;
-    if (want > parts)
-        parts = want;
+    const int64_t max_pb = max_part_blocks(head_dim);
+    int64_t parts = (max_blocks + max_pb - 1) / max_pb;
+    if (units * parts < pa::kTargetGroups) {
+        const int64_t fill = (pa::kTargetGroups + units - 1) / units;
+        const int64_t cap = (max_blocks + 2 * nw - 1) / (2 * nw);
+        const int64_t want = fill < cap ? fill : cap;
+        if (want > parts)
+            parts = want;
+    }
     if (parts < 1)
         parts = 1;
     int32_t pb = (int32_t)((max_blocks + parts - 1) / parts);
@@ -227,8 +230,6 @@ pa_status pa_decode(const pa_kv_pool *pool, const void *q, void *out, int32_t nu
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = pa::launch_decode(pool->dtype, pool->head_dim, a, num_seqs, s);
-    if (e == hipSuccess && parts > 1)
-        e = pa::launch_reduce(pool->dtype, pool->head_dim, a, num_seqs, s);
     return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 

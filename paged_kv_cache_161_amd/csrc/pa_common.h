@@ -49,15 +49,26 @@ struct AppendArgs {
 // Launchers (return hipSuccess or the launch error).
 hipError_t launch_decode(int dtype, int head_dim, const DecodeArgs &a, int num_seqs,
                          hipStream_t stream);
-hipError_t launch_reduce(int dtype, int head_dim, const DecodeArgs &a, int num_seqs,
-                         hipStream_t stream);
 hipError_t launch_append(int dtype, int head_dim, const AppendArgs &a, hipStream_t stream);
 
-// Waves per decode workgroup.  At ~146 VGPRs per lane (d = 128, 16-bit) a SIMD holds 3
-// waves, so a CU holds three 4-wave workgroups.
-constexpr int waves_per_group(int /*head_dim*/) { return 4; }
+// Decode launch shape for 16-bit K/V with head_dim <= 128: waves per workgroup and
+// blocks each wave keeps in flight ahead of the one it is computing.
+#ifndef PA_WAVES
+#define PA_WAVES 8
+#endif
+#ifndef PA_PREFETCH
+#define PA_PREFETCH 1
+#endif
+constexpr int kWavesMain = PA_WAVES;
+constexpr int kPrefetchMain = PA_PREFETCH;
 
-// Decode workgroups the whole GPU keeps resident at once (256 CUs x 3).
-constexpr int kResidentGroups = 768;
+// Waves per decode workgroup for a head dimension (the other shapes use 4).
+constexpr int waves_per_group(int head_dim) { return head_dim <= 128 ? kWavesMain : 4; }
+
+// Fewest decode workgroups the partition choice aims for: one per CU of the MI355X.
+#ifndef PA_TARGET_GROUPS
+#define PA_TARGET_GROUPS 256
+#endif
+constexpr int kTargetGroups = PA_TARGET_GROUPS;
 
 }  // namespace pa

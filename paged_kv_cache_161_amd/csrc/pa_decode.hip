@@ -14,8 +14,10 @@
 //   grid  (P partitions, kv-heads x head-chunks, sequences); a workgroup of NW waves
 //   owns one (sequence, kv-head, <=16 q-heads of its group, partition).  Wave w walks
 //   the partition's blocks w, w+NW, ...; at the end the NW waves merge their running
-//   (m, l, O) in LDS.  With P == 1 the workgroup writes the normalised output; with
-//   P > 1 it writes unnormalised partials that pa_decode_reduce merges.
+//   (m, l, O) in LDS.  A sequence whose context fits one partition is finished by
+//   that workgroup; longer ones leave unnormalised partials (o, m, l) that
+//   pa_decode_reduce merges in a second launch (the kernel boundary makes every
+//   partition's partial visible to it).
 //
 // Per 16-token block a wave does two MFMA contractions, no LDS:
 //   S[t][h]  = sum_e K[t][e] * Q[h][e]      A = K tile rows (token t = lane % 16),
@@ -237,8 +239,14 @@ __device__ __forceinline__ void mask_tail_v(typename Frags<DT, D>::Tile &t, int 
 
 // ------------------------------------------------------------------ partition kernel
 
-template <int DT, int D, int NW>
-__global__ __launch_bounds__(NW *kWave) void pa_decode_partition(DecodeArgs a)
+// Waves per SIMD the register budget must allow for a prefetch depth.
+constexpr int min_waves_per_simd(int dt, int d, int pf)
+{
+    return (d > 128 || dt == DT_F32) ? 1 : (pf <= 1 ? 3 : (pf == 2 ? 2 : 1));
+}
+
+template <int DT, int D, int NW, int PF>
+__global__ __launch_bounds__(NW *kWave, min_waves_per_simd(DT, D, PF)) void pa_decode_partition(DecodeArgs a)
 {
     using F = Frags<DT, D>;
     using Elem = typename F::Elem;
@@ -247,7 +255,7 @@ __global__ __launch_bounds__(NW *kWave) void pa_decode_partition(DecodeArgs a)
     extern __shared__ float smem[];
     float *s_m = smem;                              // [NW][16]
     float *s_l = smem + NW * 16;                    // [NW][16]
-    int *s_bad = reinterpret_cast<int *>(smem + NW * 32);   // [NW]
+    int *s_bad = reinterpret_cast<int *>(smem + NW * 32);   // [NW], then a flag at [8]
     float *s_o = smem + NW * 32 + 16;               // [NW][GS][DP]
 
     const int p = blockIdx.x;
@@ -263,17 +271,29 @@ __global__ __launch_bounds__(NW *kWave) void pa_decode_partition(DecodeArgs a)
     const int gs = min(16, a.group - chunk * 16);   // q-heads handled here
     const int hq0 = kvh * a.group + chunk * 16;     // first q-head of this workgroup
 
+    // Issued before the context length is known, so the three loads overlap: the
+    // table row has max_blocks entries, so every index below that bound is readable.
+    const int lb_begin = p * a.part_blocks;
+    const int lb_cap = min(lb_begin + a.part_blocks, a.max_blocks);
+    const int lb_lane = lb_begin + wave + lane * NW;   // this wave's (lane)-th block
+    const int bt_lane = lb_lane < lb_cap ? a.block_tables[(size_t)b * a.max_blocks + lb_lane] : 0;
+    typename F::Q qf;                                // q rows of the group (0 past gs)
+    {
+        const bool hvalid = r < gs;
+        const Elem *qrow = static_cast<const Elem *>(a.q) +
+                           ((size_t)b * a.num_q_heads + hq0 + (hvalid ? r : 0)) * D;
+        qf.load(qrow, hvalid, g);
+    }
     const int ctx = a.context_lens[b];
     const int nblk_seq = (ctx + kBlock - 1) / kBlock;
     const bool bad_ctx = ctx < 0 || ctx > a.max_context_len || nblk_seq > a.max_blocks;
-    const int lb_begin = p * a.part_blocks;
     const int lb_end = min(lb_begin + a.part_blocks, nblk_seq);
 
     if (bad_ctx || lb_begin >= lb_end) {
-        // Nothing to stream.  In split mode the reduce kernel handles empty and invalid
-        // sequences itself; in single-pass mode partition 0 writes zeros (empty
-        // context) or NaN (inconsistent context length).
-        if (!a.split && p == 0) {
+        // Nothing to stream.  When no workgroup of this sequence streams at all,
+        // partition 0 writes its answer: zeros for an empty context, NaN for an
+        // inconsistent length.
+        if (p == 0 && (bad_ctx || nblk_seq == 0)) {
             const float fill = bad_ctx ? __builtin_nanf("") : 0.f;
             for (int idx = tid; idx < gs * D; idx += NW * kWave)
                 store_elem<DT>(a.out, ((size_t)b * a.num_q_heads + hq0) * D + idx, fill);
@@ -281,20 +301,8 @@ __global__ __launch_bounds__(NW *kWave) void pa_decode_partition(DecodeArgs a)
         return;
     }
 
-    // q fragment of this lane's head (zero for padding heads beyond the group)
-    typename F::Q qf;
-    {
-        const bool hvalid = r < gs;
-        const Elem *qrow = static_cast<const Elem *>(a.q) +
-                           ((size_t)b * a.num_q_heads + hq0 + (hvalid ? r : 0)) * D;
-        qf.load(qrow, hvalid, g);
-    }
-
     const int nb = lb_end - lb_begin;
     const int my_n = nb > wave ? (nb - wave + NW - 1) / NW : 0;   // <= 64 (host-checked)
-    const int32_t *bt = a.block_tables + (size_t)b * a.max_blocks + lb_begin + wave;
-    // lane i holds the physical id of this wave's i-th block
-    int bt_lane = lane < my_n ? bt[(size_t)lane * NW] : 0;
 
     const Elem *kbase = static_cast<const Elem *>(a.k_pool) + (size_t)kvh * kBlock * D;
     const Elem *vbase = static_cast<const Elem *>(a.v_pool) + (size_t)kvh * kBlock * D;
@@ -343,23 +351,29 @@ __global__ __launch_bounds__(NW *kWave) void pa_decode_partition(DecodeArgs a)
         m_run = m_new;
     };
 
+    // Ring of PF + 1 tiles: block i + PF is loaded while block i is computed.  The
+    // inner loop is fully unrolled so every ring slot stays a fixed register range.
     if (my_n > 0) {
-        typename F::Tile t0, t1;
-        size_t off = phys_of(0);
-        t0.load(kbase + off, vbase + off, r, g);
-        for (int i = 0; i < my_n; i += 2) {
-            if (i + 1 < my_n) {
-                off = phys_of(i + 1);
-                t1.load(kbase + off, vbase + off, r, g);
+        typename F::Tile ring[PF + 1];
+#pragma unroll
+        for (int k = 0; k < PF; ++k) {
+            if (k < my_n) {
+                const size_t off = phys_of(k);
+                ring[k].load(kbase + off, vbase + off, r, g);
             }
-            process(t0, i);
-            if (i + 1 >= my_n)
-                break;
-            if (i + 2 < my_n) {
-                off = phys_of(i + 2);
-                t0.load(kbase + off, vbase + off, r, g);
+        }
+        for (int i = 0; i < my_n; i += PF + 1) {
+#pragma unroll
+            for (int u = 0; u <= PF; ++u) {
+                const int it = i + u;
+                if (it < my_n) {
+                    if (it + PF < my_n) {
+                        const size_t off = phys_of(it + PF);
+                        ring[(u + PF) % (PF + 1)].load(kbase + off, vbase + off, r, g);
+                    }
+                    process(ring[u], it);
+                }
             }
-            process(t1, i + 1);
         }
     }
     l_run = wave_sum_rows(l_run);
@@ -382,6 +396,9 @@ __global__ __launch_bounds__(NW *kWave) void pa_decode_partition(DecodeArgs a)
 #pragma unroll
     for (int w = 0; w < NW; ++w)
         any_bad |= s_bad[w] != 0;
+    // A sequence that fits one partition is finished here; longer ones leave
+    // unnormalised partials for pa_decode_reduce.
+    const bool partial = a.split && nblk_seq > a.part_blocks;
     const float qnan = __builtin_nanf("");
     for (int idx = tid; idx < gs * D; idx += NW * kWave) {
         const int h = idx / D;
@@ -399,7 +416,7 @@ __global__ __launch_bounds__(NW *kWave) void pa_decode_partition(DecodeArgs a)
             den += f * s_l[w * 16 + h];
         }
         const size_t row = (size_t)b * a.num_q_heads + hq0 + h;
-        if (!a.split) {
+        if (!partial) {
             const float val = any_bad ? qnan : (den > 0.f ? num / den : 0.f);
             store_elem<DT>(a.out, row * D + e, val);
         } else {
@@ -415,43 +432,71 @@ __global__ __launch_bounds__(NW *kWave) void pa_decode_partition(DecodeArgs a)
 
 // ------------------------------------------------------------------ reduce kernel
 
-// Merges the P partials of one (sequence, q-head):
-//   M = max_p m_p,  out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p
-// (the pages' combine rule, in the log2 domain the partition kernel uses).
+// Merges the partials of every sequence that spans more than one partition:
+//   M = max_p m_p,   out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p
+// (the pages' combine rule, in the log2 domain the partition kernel uses).  One
+// workgroup per (sequence, kv-head, head chunk); a thread owns 4 consecutive elements
+// of one q-head and walks the partials 8 at a time, issuing all 8 partitions' loads
+// before using any of them.
 template <int DT, int D>
-__global__ __launch_bounds__(kWave) void pa_decode_reduce(DecodeArgs a)
+__global__ __launch_bounds__(256) void pa_decode_reduce(DecodeArgs a)
 {
-    const int hq = blockIdx.x;
+    constexpr int QB = 8;
+    const int kvh = blockIdx.x / a.head_chunks;
+    const int chunk = blockIdx.x - kvh * a.head_chunks;
     const int b = blockIdx.y;
+    const int gs = min(16, a.group - chunk * 16);
+    const int hq0 = kvh * a.group + chunk * 16;
     const int ctx = a.context_lens[b];
     const int nblk = (ctx + kBlock - 1) / kBlock;
     const bool bad_ctx = ctx < 0 || ctx > a.max_context_len || nblk > a.max_blocks;
-    const int np = bad_ctx ? 0 : (nblk + a.part_blocks - 1) / a.part_blocks;
-    const size_t base = ((size_t)b * a.num_q_heads + hq) * a.num_parts;
+    if (bad_ctx || nblk <= a.part_blocks)
+        return;                                  // finished by the partition kernel
+    const int np = (nblk + a.part_blocks - 1) / a.part_blocks;
+    const float qnan = __builtin_nanf("");
 
-    float M = -INFINITY;
-    bool nan_seen = false;
-    for (int p = 0; p < np; ++p) {
-        const float m = a.ws_m[base + p];
-        nan_seen |= (m != m);
-        M = fmaxf(M, m);
-    }
-    float den = 0.f;
-    for (int p = 0; p < np; ++p) {
-        const float m = a.ws_m[base + p];
-        const float f = (m == -INFINITY) ? 0.f : fast_exp2(m - M);
-        den += f * a.ws_l[base + p];
-    }
-    const bool poison = bad_ctx || nan_seen;
-    for (int e = threadIdx.x; e < D; e += kWave) {
-        float num = 0.f;
-        for (int p = 0; p < np; ++p) {
-            const float m = a.ws_m[base + p];
-            const float f = (m == -INFINITY) ? 0.f : fast_exp2(m - M);
-            num += f * a.ws_o[(base + p) * D + e];
+    for (int idx = threadIdx.x; idx < gs * (D / 4); idx += blockDim.x) {
+        const int h = idx / (D / 4);
+        const int c4 = idx - h * (D / 4);
+        const size_t row = (size_t)b * a.num_q_heads + hq0 + h;
+        const float *mrow = a.ws_m + row * a.num_parts;
+        const float *lrow = a.ws_l + row * a.num_parts;
+        const f32x4 *orow = reinterpret_cast<const f32x4 *>(a.ws_o + row * a.num_parts * D) + c4;
+        float M = -INFINITY, den = 0.f;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        bool nan_seen = false;
+        for (int q0 = 0; q0 < np; q0 += QB) {
+            float mq[QB], lq[QB];
+            f32x4 oq[QB];
+#pragma unroll
+            for (int j = 0; j < QB; ++j) {
+                const bool in = q0 + j < np;
+                mq[j] = in ? mrow[q0 + j] : -INFINITY;
+                lq[j] = in ? lrow[q0 + j] : 0.f;
+                oq[j] = in ? orow[(size_t)(q0 + j) * (D / 4)] : f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+            float mc = M;
+#pragma unroll
+            for (int j = 0; j < QB; ++j) {
+                nan_seen |= (mq[j] != mq[j]);
+                mc = fmaxf(mc, mq[j]);
+            }
+            const float sa = (M == -INFINITY) ? 0.f : fast_exp2(M - mc);
+            den *= sa;
+            acc *= sa;
+#pragma unroll
+            for (int j = 0; j < QB; ++j) {
+                const float f = (mq[j] == -INFINITY) ? 0.f : fast_exp2(mq[j] - mc);
+                den += f * lq[j];
+                acc += f * oq[j];
+            }
+            M = mc;
         }
-        const float val = poison ? __builtin_nanf("") : (den > 0.f ? num / den : 0.f);
-        store_elem<DT>(a.out, ((size_t)b * a.num_q_heads + hq) * D + e, val);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float val = nan_seen ? qnan : (den > 0.f ? acc[j] / den : 0.f);
+            store_elem<DT>(a.out, row * D + 4 * c4 + j, val);
+        }
     }
 }
 
@@ -459,9 +504,10 @@ template <int DT, int D>
 hipError_t launch_decode_t(const DecodeArgs &a, int num_seqs, hipStream_t stream)
 {
     constexpr int NW = waves_per_group(D);
+    constexpr int PF = (D <= 128 && DT != DT_F32) ? kPrefetchMain : 1;
     const int gs_max = min(16, a.group);
     const size_t lds = sizeof(float) * (NW * 32 + 16 + (size_t)NW * gs_max * (D + 4));
-    auto kern = pa_decode_partition<DT, D, NW>;
+    auto kern = pa_decode_partition<DT, D, NW, PF>;
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -470,14 +516,11 @@ hipError_t launch_decode_t(const DecodeArgs &a, int num_seqs, hipStream_t stream
     }
     dim3 grid(a.num_parts, a.num_kv_heads * a.head_chunks, num_seqs);
     hipLaunchKernelGGL(kern, grid, dim3(NW * kWave), lds, stream, a);
-    return hipGetLastError();
-}
-
-template <int DT, int D>
-hipError_t launch_reduce_t(const DecodeArgs &a, int num_seqs, hipStream_t stream)
-{
-    dim3 grid(a.num_q_heads, num_seqs);
-    hipLaunchKernelGGL((pa_decode_reduce<DT, D>), grid, dim3(kWave), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !a.split)
+        return e;
+    dim3 rgrid(a.num_kv_heads * a.head_chunks, num_seqs);
+    hipLaunchKernelGGL((pa_decode_reduce<DT, D>), rgrid, dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -502,10 +545,5 @@ hipError_t launch_decode(int dtype, int head_dim, const DecodeArgs &a, int num_s
     PA_DISPATCH(launch_decode_t, a, num_seqs, stream)
 }
 
-hipError_t launch_reduce(int dtype, int head_dim, const DecodeArgs &a, int num_seqs,
-                         hipStream_t stream)
-{
-    PA_DISPATCH(launch_reduce_t, a, num_seqs, stream)
-}
 
 }  // namespace pa

@@ -103,10 +103,14 @@ def test_partition_choice_is_deterministic_and_sane(lib):
     f = lib.pa_decode_partition_tokens
     # one sequence of 37 tokens: single pass
     assert f(1, 4, 1, 37) >= 37
-    # 32 x 4096 GQA-8 (256 kv units): split so >= 768 resident workgroups stream
-    pt = f(32, 64, 8, 4096)
-    assert pt % 16 == 0 and 4096 / pt >= 3
-    assert f(32, 64, 8, 4096) == pt
+    # 32 x 4096 GQA-8: 256 (sequence, kv-head) units already give one workgroup per CU,
+    # so each fits one partition and no merge pass runs
+    assert f(32, 64, 8, 4096) >= 4096
+    assert f(32, 64, 8, 4096) == f(32, 64, 8, 4096)
+    # the same batch with one kv-head (one GPU's share under 8-way head sharding) is cut
+    # into partitions until >= 256 workgroups stream
+    pt = f(32, 8, 1, 4096)
+    assert pt % 16 == 0 and 32 * (-(-4096 // pt)) >= 256
     # long context at small batch is always split
     assert f(12, 64, 8, 32768) < 32768
     assert f(0, 64, 8, 0) >= 0
@@ -116,8 +120,11 @@ def test_partition_choice_is_deterministic_and_sane(lib):
 def test_workspace_matches_partitions(lib):
     ws = lib.pa_decode_workspace_bytes
     assert ws(1, 4, 1, 64, 37, 0) == 0
-    pt = lib.pa_decode_partition_tokens(32, 64, 8, 4096)
+    pt = lib.pa_decode_partition_tokens(32, 8, 1, 4096)
     parts = -(-4096 // pt)
-    assert ws(32, 64, 8, 128, 4096, 0) == 32 * 64 * parts * (128 + 2) * 4
+    assert parts > 1
+    assert ws(32, 8, 1, 128, 4096, 0) == 32 * 8 * parts * (128 + 2) * 4
+    assert ws(32, 64, 8, 128, 4096, 0) == 0        # single pass
     assert ws(32, 64, 8, 128, 4096, 512) == 32 * 64 * 8 * (128 + 2) * 4
+    assert ws(2, 64, 2, 128, 4096, 512) == 2 * 64 * 8 * (128 + 2) * 4
     assert ws(2, 3, 2, 128, 10, 0) == ctypes.c_size_t(-1).value

@@ -234,3 +234,30 @@ def test_rejects_unsupported_partition():
     with pytest.raises(PA.PaError):
         PA.decode(d["q"], kp, vp, d["block_tables"], d["context_lens"], float(w.scale),
                   w.max_context_len, partition_tokens=8)
+
+
+def test_split_workspace_reuse_and_garbage():
+    """The split-mode arrival counters need no initialisation: a garbage-filled
+    workspace, reused across calls whose partition counts differ, gives the same
+    results as fresh calls."""
+    specs = [SMALL[0], SMALL[7], SMALL[4]]
+    ws = torch.full((1 << 22,), 0xA5, dtype=torch.uint8, device="cuda")
+    for rep in range(3):
+        for spec in specs:
+            for ptok in (16, 32, 64):
+                w = W.build(spec)
+                need = PA.workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads,
+                                          w.head_dim, w.max_context_len, ptok)
+                assert 0 < need <= ws.numel()
+                kp, vp = U.device_pools(w)
+                d = U.device_inputs(w)
+                PA.cache_append(kp, vp, d["k_new"], d["v_new"], d["slot_mapping"])
+                out = PA.decode(d["q"], kp, vp, d["block_tables"], d["context_lens"],
+                                float(w.scale), w.max_context_len, ptok, workspace=ws)
+                ref_out = PA.decode(d["q"], kp, vp, d["block_tables"], d["context_lens"],
+                                    float(w.scale), w.max_context_len, 0)
+                torch.cuda.synchronize()
+                got = U.widen(U.from_dev(out, w.dtype), w.dtype)
+                ref = oracle_decode(w)
+                check(w, got, ref, f"reuse {rep} {spec.name} p{ptok}")
+                assert np.isfinite(U.widen(U.from_dev(ref_out, w.dtype), w.dtype)).all()
