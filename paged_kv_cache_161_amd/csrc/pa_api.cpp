@@ -227,6 +227,7 @@ pa_status pa_decode(const pa_kv_pool *pool, const void *q, void *out, int32_t nu
     a.num_parts = parts;
     a.scale_log2 = scale * 1.4426950408889634f;
     a.split = parts > 1 ? 1 : 0;
+    a.longest_first = (num_seqs > 1 && num_seqs <= pa::kLongestFirstMax) ? 1 : 0;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = pa::launch_decode(pool->dtype, pool->head_dim, a, num_seqs, s);

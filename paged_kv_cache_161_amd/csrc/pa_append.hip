@@ -29,6 +29,12 @@ __global__ __launch_bounds__(256) void pa_cache_append_kernel(AppendArgs a)
     const size_t row = idx / CPR;              // token * hkv + head
     const int h = (int)(row % a.num_kv_heads);
     const int i = (int)(row / a.num_kv_heads);
+    // The row data and the slot are independent loads: issue all three before the
+    // slot decides whether (and where) to store.
+    const u32x4 kv = *reinterpret_cast<const u32x4 *>(
+        static_cast<const char *>(a.k_new) + (row * D + (size_t)c * EPC) * EB);
+    const u32x4 vv = *reinterpret_cast<const u32x4 *>(
+        static_cast<const char *>(a.v_new) + (row * D + (size_t)c * EPC) * EB);
     const int32_t slot = a.slot_mapping[i];
     if (slot < 0 || (int64_t)slot >= (int64_t)a.num_blocks * kBlock)
         return;
@@ -36,12 +42,8 @@ __global__ __launch_bounds__(256) void pa_cache_append_kernel(AppendArgs a)
     const int off = slot % kBlock;
     const size_t tile = (blk * a.num_kv_heads + h) * (size_t)kBlock * D;   // element offset
 
-    const char *ksrc = static_cast<const char *>(a.k_new) + (row * D + (size_t)c * EPC) * EB;
-    const char *vsrc = static_cast<const char *>(a.v_new) + (row * D + (size_t)c * EPC) * EB;
     char *kdst = static_cast<char *>(a.k_pool) + (tile + (size_t)off * D + (size_t)c * EPC) * EB;
-    *reinterpret_cast<u32x4 *>(kdst) = *reinterpret_cast<const u32x4 *>(ksrc);
-
-    const u32x4 vv = *reinterpret_cast<const u32x4 *>(vsrc);
+    *reinterpret_cast<u32x4 *>(kdst) = kv;
     char *vdst = static_cast<char *>(a.v_pool) + (tile + (size_t)c * EPC * kBlock + off) * EB;
     if constexpr (EB == 4) {
 #pragma unroll

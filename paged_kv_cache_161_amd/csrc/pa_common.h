@@ -33,7 +33,11 @@ struct DecodeArgs {
     int32_t num_parts;                // P (grid x)
     float scale_log2;                 // scale * log2(e)
     int32_t split;                    // 1: write partials, 0: write out
+    int32_t longest_first;            // 1: workgroup z takes the z-th longest sequence
 };
+
+// Batches up to this size are dispatched longest sequence first.
+constexpr int kLongestFirstMax = 256;
 
 struct AppendArgs {
     void *k_pool;

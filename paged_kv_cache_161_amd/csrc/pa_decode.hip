@@ -261,8 +261,30 @@ __global__ __launch_bounds__(NW *kWave, min_waves_per_simd(DT, D, PF)) void pa_d
     const int p = blockIdx.x;
     const int kvh = blockIdx.y / a.head_chunks;
     const int chunk = blockIdx.y - kvh * a.head_chunks;
-    const int b = blockIdx.z;
     const int tid = threadIdx.x;
+    // Workgroups are dispatched in z order, so with longest_first workgroup z takes
+    // the sequence whose context length ranks z-th (longest first, ties by index): a
+    // ragged batch then starts its longest streams first instead of last.
+    int b = blockIdx.z;
+    if (a.longest_first) {
+        int *s_ctx = reinterpret_cast<int *>(smem + NW * 32 + 16 + NW * min(16, a.group) * DP);
+        const int nseq = gridDim.z;
+        for (int t = tid; t < nseq; t += NW * kWave)
+            s_ctx[t] = a.context_lens[t];
+        __syncthreads();
+        for (int t = tid; t < nseq; t += NW * kWave) {
+            const int c = s_ctx[t];
+            int rank = 0;
+            for (int u = 0; u < nseq; ++u) {
+                const int cu = s_ctx[u];
+                rank += (cu > c || (cu == c && u < t)) ? 1 : 0;
+            }
+            if (rank == (int)blockIdx.z)
+                s_ctx[nseq] = t;
+        }
+        __syncthreads();
+        b = __builtin_amdgcn_readfirstlane(s_ctx[nseq]);
+    }
     const int lane = tid & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = lane & 15;
@@ -506,7 +528,8 @@ hipError_t launch_decode_t(const DecodeArgs &a, int num_seqs, hipStream_t stream
     constexpr int NW = waves_per_group(D);
     constexpr int PF = (D <= 128 && DT != DT_F32) ? kPrefetchMain : 1;
     const int gs_max = min(16, a.group);
-    const size_t lds = sizeof(float) * (NW * 32 + 16 + (size_t)NW * gs_max * (D + 4));
+    const size_t lds = sizeof(float) * (NW * 32 + 16 + (size_t)NW * gs_max * (D + 4)) +
+                       (a.longest_first ? sizeof(int) * (num_seqs + 1) : 0);
     auto kern = pa_decode_partition<DT, D, NW, PF>;
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),

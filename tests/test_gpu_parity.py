@@ -79,6 +79,10 @@ SMALL = [
     W.Spec("f32_g2_d128", "f32", 4, 2, 128, [65, 16], seed=107, spare_blocks=1),
     W.Spec("bf16_g5_d128", "bf16", 10, 2, 128, [190, 3, 0, 512], seed=108, spare_blocks=1),
     W.Spec("bf16_empty_batch_rows", "bf16", 8, 8, 128, [0, 0, 5], seed=109, spare_blocks=1),
+    # more sequences than the longest-first ordering handles (it covers <= 256)
+    W.Spec("bf16_300_ragged_seqs", "bf16", 8, 2, 128,
+           [int(x) for x in np.random.Generator(np.random.PCG64(110)).integers(0, 70, 300)],
+           seed=110, spare_blocks=1),
 ]
 
 
