@@ -262,10 +262,38 @@ __global__ __launch_bounds__(NW *kWave, min_waves_per_simd(DT, D, PF)) void pa_d
     const int kvh = blockIdx.y / a.head_chunks;
     const int chunk = blockIdx.y - kvh * a.head_chunks;
     const int tid = threadIdx.x;
-    // Workgroups are dispatched in z order, so with longest_first workgroup z takes
-    // the sequence whose context length ranks z-th (longest first, ties by index): a
-    // ragged batch then starts its longest streams first instead of last.
+    const int lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r = lane & 15;
+    const int g = lane >> 4;
+
+    const int gs = min(16, a.group - chunk * 16);   // q-heads handled here
+    const int hq0 = kvh * a.group + chunk * 16;     // first q-head of this workgroup
+
+    // This wave's block ids (one per lane) and the group's q rows, issued before the
+    // context length is known so the loads overlap: the table row has max_blocks
+    // entries, so every index below that bound is readable.
+    const int lb_begin = p * a.part_blocks;
+    const int lb_cap = min(lb_begin + a.part_blocks, a.max_blocks);
+    const int lb_lane = lb_begin + wave + lane * NW;   // this wave's (lane)-th block
+    typename F::Q qf;                                // q rows of the group (0 past gs)
+    int bt_lane;
+    auto load_seq = [&](int seq) {
+        bt_lane = lb_lane < lb_cap ? a.block_tables[(size_t)seq * a.max_blocks + lb_lane] : 0;
+        const bool hvalid = r < gs;
+        const Elem *qrow = static_cast<const Elem *>(a.q) +
+                           ((size_t)seq * a.num_q_heads + hq0 + (hvalid ? r : 0)) * D;
+        qf.load(qrow, hvalid, g);
+    };
+
+    // Workgroups are dispatched in z order, so with longest_first workgroup z takes the
+    // sequence whose context length ranks z-th (longest first, ties by index): a ragged
+    // batch then starts its longest streams first instead of last.  The loads for
+    // sequence z go out first; they are kept when the rank maps z to itself (always,
+    // in a batch of equal lengths) and reissued otherwise.
     int b = blockIdx.z;
+    load_seq(b);
+    int ctx = -1;
     if (a.longest_first) {
         int *s_ctx = reinterpret_cast<int *>(smem + NW * 32 + 16 + NW * min(16, a.group) * DP);
         const int nseq = gridDim.z;
@@ -284,29 +312,12 @@ __global__ __launch_bounds__(NW *kWave, min_waves_per_simd(DT, D, PF)) void pa_d
         }
         __syncthreads();
         b = __builtin_amdgcn_readfirstlane(s_ctx[nseq]);
+        ctx = s_ctx[b];
+        if (b != (int)blockIdx.z)
+            load_seq(b);
+    } else {
+        ctx = a.context_lens[b];
     }
-    const int lane = tid & (kWave - 1);
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int r = lane & 15;
-    const int g = lane >> 4;
-
-    const int gs = min(16, a.group - chunk * 16);   // q-heads handled here
-    const int hq0 = kvh * a.group + chunk * 16;     // first q-head of this workgroup
-
-    // Issued before the context length is known, so the three loads overlap: the
-    // table row has max_blocks entries, so every index below that bound is readable.
-    const int lb_begin = p * a.part_blocks;
-    const int lb_cap = min(lb_begin + a.part_blocks, a.max_blocks);
-    const int lb_lane = lb_begin + wave + lane * NW;   // this wave's (lane)-th block
-    const int bt_lane = lb_lane < lb_cap ? a.block_tables[(size_t)b * a.max_blocks + lb_lane] : 0;
-    typename F::Q qf;                                // q rows of the group (0 past gs)
-    {
-        const bool hvalid = r < gs;
-        const Elem *qrow = static_cast<const Elem *>(a.q) +
-                           ((size_t)b * a.num_q_heads + hq0 + (hvalid ? r : 0)) * D;
-        qf.load(qrow, hvalid, g);
-    }
-    const int ctx = a.context_lens[b];
     const int nblk_seq = (ctx + kBlock - 1) / kBlock;
     const bool bad_ctx = ctx < 0 || ctx > a.max_context_len || nblk_seq > a.max_blocks;
     const int lb_end = min(lb_begin + a.part_blocks, nblk_seq);
