@@ -44,7 +44,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=HEADLINE,
-                    help="workload id 1..5 (default: the Llama-70B GQA headline)")
+                    help="workload id 1..6 (default: the Llama-70B GQA headline; 6 is the "
+                         "same shape with an FP8 E4M3 KV cache)")
     ap.add_argument("--partition-tokens", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--roofline-launches", type=int, default=100)
@@ -86,11 +87,13 @@ def cpu_baseline(w):
     import oracle as O
     threads = O.default_threads()
     kp, vp, bt, sl = w.oracle_view()
-    kp, vp = O.cache_append(kp, vp, w.k_new, w.v_new, sl, w.dtype)
+    kp, vp = O.cache_append(kp, vp, w.k_new, w.v_new, sl, w.kv_dtype, act_dtype=w.dtype,
+                            k_scale=w.k_scale, v_scale=w.v_scale)
     times = []
     for _ in range(3):
         t0 = time.perf_counter()
-        O.decode_paged(w.q, kp, vp, w.dtype, bt, w.context_lens, w.scale, threads=threads)
+        O.decode_paged(w.q, kp, vp, w.kv_dtype, bt, w.context_lens, w.scale, threads=threads,
+                       q_dtype=w.dtype, k_scale=w.k_scale, v_scale=w.v_scale)
         times.append(time.perf_counter() - t0)
     t = statistics.median(times)
     return {"value": round(w.logical_kv_bytes() / t / 1e9, 4), "unit": "GB/s",
@@ -135,11 +138,13 @@ def main():
     scale = float(w.scale)
     max_ctx = w.max_context_len
 
+    sc = U.scales(w)
+
     def step(i):
         kp, vp = pools[i % LAYERS]
-        PA.cache_append(kp, vp, d["k_new"], d["v_new"], d["slot_mapping"])
+        PA.cache_append(kp, vp, d["k_new"], d["v_new"], d["slot_mapping"], **sc)
         PA.decode(d["q"], kp, vp, d["block_tables"], d["context_lens"], scale, max_ctx, ptok,
-                  out=out, workspace=ws)
+                  out=out, workspace=ws, **sc)
 
     if args.calibrate:
         src = torch.ones(CALIBRATION_BYTES // 2, dtype=torch.int16, device=dev)
@@ -178,7 +183,7 @@ def main():
     for i in range(n_l):
         kp, vp = pools[i % LAYERS]
         PA.decode(d["q"], kp, vp, d["block_tables"], d["context_lens"], scale, max_ctx, ptok,
-                  out=out, workspace=ws)
+                  out=out, workspace=ws, **sc)
     e1.record(stream)
     torch.cuda.synchronize()
     dur = e0.elapsed_time(e1) * 1e-3 / n_l
@@ -194,10 +199,11 @@ def main():
         rows = np.random.Generator(np.random.PCG64(0)).choice(
             w.num_seqs, size=min(4, w.num_seqs), replace=False)
         sub = {k: v for k, v in zip(("k", "v", "bt", "sl"), w.oracle_view())}
-        kpo, vpo = O.cache_append(sub["k"], sub["v"], w.k_new, w.v_new, sub["sl"], w.dtype)
-        ref, _ = O.decode_paged(np.ascontiguousarray(w.q[rows]), kpo, vpo, w.dtype,
+        kpo, vpo = O.cache_append(sub["k"], sub["v"], w.k_new, w.v_new, sub["sl"], w.kv_dtype,
+                                  act_dtype=w.dtype, k_scale=w.k_scale, v_scale=w.v_scale)
+        ref, _ = O.decode_paged(np.ascontiguousarray(w.q[rows]), kpo, vpo, w.kv_dtype,
                                 np.ascontiguousarray(sub["bt"][rows]), w.context_lens[rows],
-                                w.scale)
+                                w.scale, q_dtype=w.dtype, k_scale=w.k_scale, v_scale=w.v_scale)
         got = U.widen(U.from_dev(out, w.dtype), w.dtype)[rows]
         ok, mx, mean = U.tolerance_ok(got, ref, w.dtype)
         parity = {"rows_checked": int(rows.size), "max_abs_err": mx, "mean_abs_err": mean,
@@ -223,7 +229,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": w.dtype,
+        "dtype": w.dtype if w.kv_dtype == w.dtype else f"{w.kv_dtype} KV, {w.dtype} q/out",
         "data": "synthetic (seeded PCG64 normals x0.5, NaN-poisoned paged pool)",
         "config": {"workload": f"{w.spec.name}: {w.num_seqs} seqs x ctx {max_ctx}, "
                                f"{w.num_q_heads} q / {w.num_kv_heads} kv heads, d "

@@ -30,17 +30,22 @@
  *     default stream): they return once the kernels are enqueued.
  *   - Argument errors are detected on the host before anything is enqueued; nothing is
  *     written then.  A launch failure returns PA_ERR_HIP.  Nothing throws across the ABI.
- *   - Element types: PA_F32 (4 bytes), PA_F16 (IEEE half), PA_BF16 (bfloat16).  q, the
- *     pools, the new rows and out all use the pool's element type; arithmetic is fp32.
+ *   - Element types: PA_F32 (4 bytes), PA_F16 (IEEE half), PA_BF16 (bfloat16),
+ *     PA_FP8_E4M3 (OCP 8-bit float, 4 exponent bits, 3 fraction bits, max 448, no
+ *     infinities).  q, out and the new rows use the pool's act_dtype; for f32/f16/bf16
+ *     pools that is the pool's own type.  An fp8 pool holds codes c with K = c * k_scale
+ *     and V = c * v_scale (per-tensor scales), q/out/new rows being f16 or bf16 (the
+ *     pages' FP8 E4M3 inference format with per-tensor scaling, "Deep dive into vLLM
+ *     06", FP8 section).  Arithmetic is fp32.
  *   - Calls on different streams touching disjoint buffers may run concurrently.
  *
  * Pool layout (one layer; K and V are two separate buffers of equal size):
  *   k_pool [num_blocks][num_kv_heads][16][head_dim]   token-major inside a block
  *   v_pool [num_blocks][num_kv_heads][head_dim][16]   token-minor inside a block
  * so one (block, kv-head) tile of K or of V is a single contiguous run of
- * 16 * head_dim elements (4 KiB for head_dim 128 in 16-bit types).  Token t of a
- * sequence is row t % 16 of physical block block_tables[seq][t / 16]; its slot number
- * is physical_block * 16 + t % 16.
+ * 16 * head_dim elements (4 KiB for head_dim 128 in 16-bit types, 2 KiB in fp8).
+ * Token t of a sequence is row t % 16 of physical block block_tables[seq][t / 16]; its
+ * slot number is physical_block * 16 + t % 16.
  */
 #ifndef PAGED_ATTENTION_H
 #define PAGED_ATTENTION_H
@@ -65,11 +70,16 @@ typedef enum pa_status {
 typedef enum pa_dtype {
     PA_F32 = 0,
     PA_F16 = 1,
-    PA_BF16 = 2
+    PA_BF16 = 2,
+    PA_FP8_E4M3 = 3
 } pa_dtype;
 
 /* One layer's paged KV pool.  block_size must be PA_BLOCK_SIZE; head_dim must be one
- * of 64, 128, 256; dtype one of pa_dtype. */
+ * of 64, 128, 256 (64 or 128 for PA_F32).  dtype is the pools' element type;
+ * act_dtype the type of q, out and the new rows: equal to dtype for f32/f16/bf16
+ * pools, PA_F16 or PA_BF16 for fp8 pools.  k_scale, v_scale (fp8 pools only; finite,
+ * > 0) turn stored codes into values: K = code * k_scale, V = code * v_scale; they are
+ * ignored for other pools. */
 typedef struct pa_kv_pool {
     void *k_pool;
     void *v_pool;
@@ -78,21 +88,29 @@ typedef struct pa_kv_pool {
     int32_t num_kv_heads;
     int32_t head_dim;
     int32_t dtype;
+    int32_t act_dtype;
+    float k_scale;
+    float v_scale;
 } pa_kv_pool;
 
 /* Bytes of ONE of the two pools (K or V) for these dimensions; 0 if any argument is
  * invalid or unsupported.  Host-only, no device access. */
 size_t pa_pool_bytes(int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
                      int32_t dtype);
+/* (dtype is the pools' element type: 4, 2, 2 or 1 bytes per element.) */
 
 /* Scatter num_tokens new rows into the pool (LLM-101-CN "推理优化",
  * KVCachePool.write_tokens; "LLM应用 12 推理优化", PagedKVCache.update).
- *   k_new, v_new   [num_tokens][num_kv_heads][head_dim], pool dtype, device
+ *   k_new, v_new   [num_tokens][num_kv_heads][head_dim], the pool's act_dtype, device
  *   slot_mapping   [num_tokens] int32, device: row i goes to physical block
  *                  slot_mapping[i] / 16, row slot_mapping[i] % 16, for every kv-head.
- * Bytes are copied unchanged.  A negative slot means "no row" (padding) and is
- * skipped.  A slot >= num_blocks * 16 is also skipped (never written), so a bad slot
- * cannot corrupt memory outside the pool.  Two rows with the same slot race (caller
+ * Bytes are copied unchanged; an fp8 pool instead stores the E4M3 code of
+ * x / k_scale (x / v_scale), the quotient taken in IEEE fp32 and rounded to the
+ * nearest code (ties to even), magnitudes >= 448 saturating to +-448 and NaN kept
+ * NaN ("Deep dive into vLLM 06", kernel fusion: KV-cache write fused with
+ * quantisation).  A negative slot means "no row" (padding) and is skipped.  A slot
+ * >= num_blocks * 16 is also skipped (never written), so a bad slot cannot corrupt
+ * memory outside the pool.  Two rows with the same slot race (caller
  * error).  num_tokens == 0 is a valid no-op. */
 pa_status pa_cache_append(const pa_kv_pool *pool, const void *k_new, const void *v_new,
                           const int32_t *slot_mapping, int32_t num_tokens, void *stream);
@@ -111,8 +129,8 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
                                  int32_t partition_tokens);
 
 /* Decode attention for one layer (definitions as cited at the top of this file).
- *   q              [num_seqs][num_q_heads][head_dim], pool dtype, device
- *   out            [num_seqs][num_q_heads][head_dim], pool dtype, device; each element
+ *   q              [num_seqs][num_q_heads][head_dim], the pool's act_dtype, device
+ *   out            [num_seqs][num_q_heads][head_dim], act_dtype, device; each element
  *                  is the fp32 result rounded to nearest-even
  *   scale          multiplies q . k (normally 1/sqrt(head_dim)), applied in fp32
  *   block_tables   [num_seqs][max_blocks_per_seq] int32, device; entries at index

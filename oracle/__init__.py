@@ -5,7 +5,9 @@ package.  The GPU product path must never call it.  The arithmetic lives in
 oracle.c; this module only marshals numpy arrays into it.
 
 Array conventions (numpy, host memory, C-contiguous):
-  dtype "f32": np.float32 arrays; "f16": np.float16; "bf16": np.uint16 bit patterns.
+  dtype "f32": np.float32 arrays; "f16": np.float16; "bf16": np.uint16 bit patterns;
+  "fp8": np.uint8 OCP E4M3 codes (pools only; q and new rows are then f16 or bf16,
+  and the pool holds code value x k_scale / v_scale).
   q [B][Hq][d], k_pool [N][Hkv][16][d], v_pool [N][Hkv][d][16],
   block_tables [B][max_blocks] int32, context_lens [B] int32.
 """
@@ -16,8 +18,8 @@ import numpy as np
 
 from .build import LIB, build_oracle
 
-DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2}
-NUMPY_STORAGE = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16}
+DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2, "fp8": 3}
+NUMPY_STORAGE = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16, "fp8": np.uint8}
 
 _lib = None
 
@@ -44,8 +46,20 @@ def _bind(lib):
     lib.oracle_decode_paged.argtypes = [P, P, P, I, I, I, I, I, I, P, I, P, ctypes.c_float,
                                         P, P, I]
     lib.oracle_decode_paged.restype = I
+    D = ctypes.c_double
+    lib.oracle_decode_paged_ex.argtypes = [P, I, P, P, I, D, D, I, I, I, I, I, P, I, P,
+                                           ctypes.c_float, P, P, I]
+    lib.oracle_decode_paged_ex.restype = I
+    lib.oracle_cache_append_ex.argtypes = [P, P, I, I, ctypes.c_float, ctypes.c_float, I, I, I,
+                                           P, P, P, I]
+    lib.oracle_cache_append_ex.restype = I
+    lib.oracle_encode_e4m3.argtypes = [P, ctypes.c_size_t, P]
+    lib.oracle_encode_e4m3.restype = None
     lib.oracle_decode_contig.argtypes = [P, P, P, I, I, I, I, I, I, P, ctypes.c_float, P, P, I]
     lib.oracle_decode_contig.restype = I
+    lib.oracle_decode_contig_ex.argtypes = [P, I, P, P, I, ctypes.c_double, ctypes.c_double, I,
+                                            I, I, I, I, P, ctypes.c_float, P, P, I]
+    lib.oracle_decode_contig_ex.restype = I
     lib.oracle_cache_append.argtypes = [P, P, I, I, I, I, P, P, P, I]
     lib.oracle_cache_append.restype = I
     return lib
@@ -81,11 +95,23 @@ def kv_cache_bytes(layers, kv_heads, head_dim, seq_len, batch, dtype_size, lib=N
     return int(lib.oracle_kv_cache_bytes(layers, kv_heads, head_dim, seq_len, batch, dtype_size))
 
 
-def decode_paged(q, k_pool, v_pool, dtype, block_tables, context_lens, scale,
-                 threads=None, lib=None):
-    """Returns (out [B][Hq][d] fp64, wsum [B][Hq] fp64)."""
+def encode_e4m3(x, lib=None):
+    """float32 array -> OCP E4M3 codes (RNE, saturating at 448), the oracle's quantiser."""
     lib = lib or load()
-    for a in (q, k_pool, v_pool):
+    x = np.ascontiguousarray(x, np.float32)
+    out = np.empty(x.shape, np.uint8)
+    lib.oracle_encode_e4m3(_ptr(x), x.size, _ptr(out))
+    return out
+
+
+def decode_paged(q, k_pool, v_pool, dtype, block_tables, context_lens, scale,
+                 threads=None, lib=None, q_dtype=None, k_scale=1.0, v_scale=1.0):
+    """Returns (out [B][Hq][d] fp64, wsum [B][Hq] fp64).  dtype is the pools' type;
+    q_dtype (default: dtype) the type of q; fp8 pools read code x k_scale / v_scale."""
+    lib = lib or load()
+    q_dtype = q_dtype or dtype
+    _check(q, q_dtype)
+    for a in (k_pool, v_pool):
         _check(a, dtype)
     B, hq, d = q.shape
     nblk, hkv, bs, d2 = k_pool.shape
@@ -95,19 +121,23 @@ def decode_paged(q, k_pool, v_pool, dtype, block_tables, context_lens, scale,
     assert bt.shape[0] == B and cl.shape == (B,)
     out = np.zeros((B, hq, d), np.float64)
     wsum = np.zeros((B, hq), np.float64)
-    rc = lib.oracle_decode_paged(_ptr(q), _ptr(k_pool), _ptr(v_pool), DTYPE_CODES[dtype], B,
-                                 hq, hkv, d, nblk, _ptr(bt), bt.shape[1], _ptr(cl),
-                                 ctypes.c_float(np.float32(scale)), _ptr(out), _ptr(wsum),
-                                 threads or default_threads())
+    rc = lib.oracle_decode_paged_ex(_ptr(q), DTYPE_CODES[q_dtype], _ptr(k_pool), _ptr(v_pool),
+                                    DTYPE_CODES[dtype], float(np.float32(k_scale)),
+                                    float(np.float32(v_scale)), B, hq, hkv, d, nblk, _ptr(bt),
+                                    bt.shape[1], _ptr(cl), ctypes.c_float(np.float32(scale)),
+                                    _ptr(out), _ptr(wsum), threads or default_threads())
     if rc:
         raise ValueError(f"oracle_decode_paged returned {rc}")
     return out, wsum
 
 
-def decode_contig(q, k, v, dtype, context_lens, scale, threads=None, lib=None):
-    """k, v: [B][Hkv][S_max][d] contiguous caches.  Returns (out, wsum) in fp64."""
+def decode_contig(q, k, v, dtype, context_lens, scale, threads=None, lib=None, q_dtype=None,
+                  k_scale=1.0, v_scale=1.0):
+    """k, v: [B][Hkv][S_max][d] contiguous caches of dtype.  Returns (out, wsum) in fp64."""
     lib = lib or load()
-    for a in (q, k, v):
+    q_dtype = q_dtype or dtype
+    _check(q, q_dtype)
+    for a in (k, v):
         _check(a, dtype)
     B, hq, d = q.shape
     B2, hkv, s_max, d2 = k.shape
@@ -115,26 +145,36 @@ def decode_contig(q, k, v, dtype, context_lens, scale, threads=None, lib=None):
     cl = np.ascontiguousarray(context_lens, np.int32)
     out = np.zeros((B, hq, d), np.float64)
     wsum = np.zeros((B, hq), np.float64)
-    rc = lib.oracle_decode_contig(_ptr(q), _ptr(k), _ptr(v), DTYPE_CODES[dtype], B, hq, hkv,
-                                  d, s_max, _ptr(cl), ctypes.c_float(np.float32(scale)),
-                                  _ptr(out), _ptr(wsum), threads or default_threads())
+    rc = lib.oracle_decode_contig_ex(_ptr(q), DTYPE_CODES[q_dtype], _ptr(k), _ptr(v),
+                                     DTYPE_CODES[dtype], float(np.float32(k_scale)),
+                                     float(np.float32(v_scale)), B, hq, hkv, d, s_max, _ptr(cl),
+                                     ctypes.c_float(np.float32(scale)), _ptr(out), _ptr(wsum),
+                                     threads or default_threads())
     if rc:
         raise ValueError(f"oracle_decode_contig returned {rc}")
     return out, wsum
 
 
-def cache_append(k_pool, v_pool, k_new, v_new, slot_mapping, dtype, inplace=False, lib=None):
-    """Returns appended (k_pool, v_pool): copies, or the inputs themselves if inplace."""
+def cache_append(k_pool, v_pool, k_new, v_new, slot_mapping, dtype, inplace=False, lib=None,
+                 act_dtype=None, k_scale=1.0, v_scale=1.0):
+    """Returns appended (k_pool, v_pool): copies, or the inputs themselves if inplace.
+    dtype is the pools' type, act_dtype (default: dtype) the new rows' type; an fp8
+    pool stores E4M3(x / scale)."""
     lib = lib or load()
-    for a in (k_pool, v_pool, k_new, v_new):
+    act_dtype = act_dtype or dtype
+    for a in (k_pool, v_pool):
         _check(a, dtype)
+    for a in (k_new, v_new):
+        _check(a, act_dtype)
     k_out = k_pool if inplace else k_pool.copy()
     v_out = v_pool if inplace else v_pool.copy()
     nblk, hkv, _, d = k_pool.shape
     sm = np.ascontiguousarray(slot_mapping, np.int32)
     assert k_new.shape == (sm.size, hkv, d) and v_new.shape == k_new.shape
-    rc = lib.oracle_cache_append(_ptr(k_out), _ptr(v_out), DTYPE_CODES[dtype], nblk, hkv, d,
-                                 _ptr(k_new), _ptr(v_new), _ptr(sm), sm.size)
+    rc = lib.oracle_cache_append_ex(_ptr(k_out), _ptr(v_out), DTYPE_CODES[dtype],
+                                    DTYPE_CODES[act_dtype], ctypes.c_float(np.float32(k_scale)),
+                                    ctypes.c_float(np.float32(v_scale)), nblk, hkv, d,
+                                    _ptr(k_new), _ptr(v_new), _ptr(sm), sm.size)
     if rc:
         raise ValueError(f"oracle_cache_append returned {rc}")
     return k_out, v_out

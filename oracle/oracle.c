@@ -29,7 +29,7 @@
  * against this one.  Every (sequence, q-head) is summed in logical token order, so
  * the result does not depend on the thread count or on where blocks sit in the pool.
  *
- * Storage layouts read here (element = 4 bytes for f32, 2 for f16/bf16):
+ * Storage layouts read here (element = 4 bytes for f32, 2 for f16/bf16, 1 for fp8):
  *   q        [B][Hq][d]
  *   k_pool   [num_blocks][Hkv][16][d]   (token-major inside a block)
  *   v_pool   [num_blocks][Hkv][d][16]   (token-minor inside a block)
@@ -43,7 +43,7 @@
 
 #define ORACLE_BLOCK 16
 
-enum { ORACLE_F32 = 0, ORACLE_F16 = 1, ORACLE_BF16 = 2 };
+enum { ORACLE_F32 = 0, ORACLE_F16 = 1, ORACLE_BF16 = 2, ORACLE_FP8_E4M3 = 3 };
 
 /* IEEE binary16 -> double, written from the format's definition:
  * sign | 5-bit exponent (bias 15) | 10-bit fraction.                                */
@@ -71,13 +71,58 @@ static double widen_bf16_bits(uint16_t b)
     return (double)f;
 }
 
+/* OCP FP8 E4M3 ("E4M3FN") -> double: sign | 4-bit exponent (bias 7) | 3-bit fraction;
+ * no infinities, S.1111.111 is NaN; largest finite magnitude 448.                   */
+static double widen_e4m3_bits(uint8_t c)
+{
+    int sign = (c >> 7) & 1;
+    int expo = (c >> 3) & 0xf;
+    int frac = c & 0x7;
+    double v;
+    if (expo == 15 && frac == 7)
+        v = NAN;
+    else if (expo == 0)
+        v = ldexp((double)frac, -9);                     /* subnormal: frac * 2^-9 */
+    else
+        v = ldexp((double)(frac | 0x8), expo - 10);      /* 1.frac * 2^(expo-7)   */
+    return sign ? -v : v;
+}
+
+/* float -> E4M3 code: round to nearest, ties to even, magnitudes >= 448 saturate to
+ * 448, NaN stays NaN.  Written from the format's value set: subnormals are integer
+ * multiples of 2^-9 below 2^-6; a normal value in [2^k, 2^(k+1)) has 8 steps.         */
+static uint8_t encode_e4m3(float x)
+{
+    uint8_t sign = signbit(x) ? 0x80 : 0x00;
+    if (isnan(x))
+        return sign | 0x7f;
+    float a = fabsf(x);
+    if (a >= 448.0f)
+        return sign | 0x7e;
+    if (a < 0.015625f) {                            /* below 2^-6 */
+        float steps = rintf(a * 512.0f);            /* exact scaling, then RNE */
+        return sign | (uint8_t)steps;               /* 8 steps = smallest normal */
+    }
+    int e;
+    (void)frexpf(a, &e);                            /* a in [2^(e-1), 2^e) */
+    int k = e - 1;
+    float steps = rintf(ldexpf(a, 3 - k));          /* in [8, 16] */
+    if (steps == 16.0f) {
+        k += 1;
+        steps = 8.0f;
+    }
+    return sign | (uint8_t)(((k + 7) << 3) | ((int)steps - 8));
+}
+
 static size_t elem_bytes(int dtype)
 {
-    return dtype == ORACLE_F32 ? 4 : 2;
+    return dtype == ORACLE_F32 ? 4 : (dtype == ORACLE_FP8_E4M3 ? 1 : 2);
 }
 
 static double widen_at(const void *base, size_t idx, int dtype)
 {
+    if (dtype == ORACLE_FP8_E4M3)
+        return widen_e4m3_bits(((const uint8_t *)base)[idx]);
     if (dtype == ORACLE_F32) {
         float f;
         memcpy(&f, (const char *)base + 4 * idx, 4);
@@ -90,11 +135,18 @@ static double widen_at(const void *base, size_t idx, int dtype)
 
 int oracle_widen(const void *src, int dtype, size_t n, double *dst)
 {
-    if (dtype < ORACLE_F32 || dtype > ORACLE_BF16)
+    if (dtype < ORACLE_F32 || dtype > ORACLE_FP8_E4M3)
         return -1;
     for (size_t i = 0; i < n; ++i)
         dst[i] = widen_at(src, i, dtype);
     return 0;
+}
+
+/* E4M3 codes of n floats (the quantiser the fp8 append uses).                        */
+void oracle_encode_e4m3(const float *src, size_t n, uint8_t *dst)
+{
+    for (size_t i = 0; i < n; ++i)
+        dst[i] = encode_e4m3(src[i]);
 }
 
 /* KV cache size 2 * L * H * d_h * S * B * dtype_size
@@ -110,8 +162,8 @@ uint64_t oracle_kv_cache_bytes(uint64_t layers, uint64_t kv_heads, uint64_t head
 /* Attention of one query row over n keys given by two accessor callbacks.
  * Plain two-pass form: scores, max, exp, sum, weighted V, one final divide.       */
 typedef struct {
-    const void *q_row;        /* d elements of dtype */
-    int dtype, d;
+    const void *q_row;        /* d elements of q_dtype */
+    int q_dtype, d;
     double scale;
     int n;                    /* number of keys */
     double *scores;           /* scratch, n entries */
@@ -134,7 +186,7 @@ static void attend(const attn_job *J, double *out, double *wsum)
     for (int t = 0; t < n; ++t) {
         double dot = 0.0;
         for (int e = 0; e < d; ++e)
-            dot += widen_at(J->q_row, (size_t)e, J->dtype) * J->key(J->ctx, t, e);
+            dot += widen_at(J->q_row, (size_t)e, J->q_dtype) * J->key(J->ctx, t, e);
         J->scores[t] = J->scale * dot;
         if (J->scores[t] > m)
             m = J->scores[t];
@@ -161,6 +213,7 @@ static void attend(const attn_job *J, double *out, double *wsum)
 typedef struct {
     const void *k_pool, *v_pool;
     int dtype, hkv, d, kv_head;
+    double k_scale, v_scale;   /* stored value x scale = K, V (1 unless fp8) */
     const int32_t *table_row;  /* logical block -> physical block */
 } paged_ctx;
 
@@ -170,7 +223,7 @@ static double paged_key(const void *c, int t, int e)
     size_t phys = (size_t)P->table_row[t / ORACLE_BLOCK];
     size_t off = (size_t)(t % ORACLE_BLOCK);
     size_t idx = ((phys * P->hkv + P->kv_head) * ORACLE_BLOCK + off) * P->d + e;
-    return widen_at(P->k_pool, idx, P->dtype);
+    return widen_at(P->k_pool, idx, P->dtype) * P->k_scale;
 }
 
 static double paged_val(const void *c, int t, int e)
@@ -179,7 +232,7 @@ static double paged_val(const void *c, int t, int e)
     size_t phys = (size_t)P->table_row[t / ORACLE_BLOCK];
     size_t off = (size_t)(t % ORACLE_BLOCK);
     size_t idx = ((phys * P->hkv + P->kv_head) * P->d + e) * ORACLE_BLOCK + off;
-    return widen_at(P->v_pool, idx, P->dtype);
+    return widen_at(P->v_pool, idx, P->dtype) * P->v_scale;
 }
 
 /* ------------------------------------------------------- contiguous accessors */
@@ -187,20 +240,21 @@ static double paged_val(const void *c, int t, int e)
 typedef struct {
     const void *k, *v;        /* [B][Hkv][S][d] each, dtype elements */
     int dtype, hkv, d, s_max, seq, kv_head;
+    double k_scale, v_scale;
 } contig_ctx;
 
 static double contig_key(const void *c, int t, int e)
 {
     const contig_ctx *C = (const contig_ctx *)c;
     size_t idx = (((size_t)C->seq * C->hkv + C->kv_head) * C->s_max + t) * C->d + e;
-    return widen_at(C->k, idx, C->dtype);
+    return widen_at(C->k, idx, C->dtype) * C->k_scale;
 }
 
 static double contig_val(const void *c, int t, int e)
 {
     const contig_ctx *C = (const contig_ctx *)c;
     size_t idx = (((size_t)C->seq * C->hkv + C->kv_head) * C->s_max + t) * C->d + e;
-    return widen_at(C->v, idx, C->dtype);
+    return widen_at(C->v, idx, C->dtype) * C->v_scale;
 }
 
 /* ---------------------------------------------------------------- threading */
@@ -209,7 +263,9 @@ typedef struct {
     int paged;                 /* 1: paged pool, 0: contiguous cache */
     const void *q;
     const void *k, *v;
-    int dtype, B, hq, hkv, d, num_blocks, max_blocks, s_max;
+    int dtype, q_dtype;        /* K/V storage type, q type */
+    double k_scale, v_scale;
+    int B, hq, hkv, d, num_blocks, max_blocks, s_max;
     const int32_t *tables, *ctx_lens;
     double scale;
     double *out, *wsum;
@@ -235,8 +291,8 @@ static void *decode_worker(void *p)
         int b = u / A->hq, h = u % A->hq;
         int kvh = h / group;
         attn_job J;
-        J.q_row = (const char *)A->q + ((size_t)b * A->hq + h) * A->d * elem_bytes(A->dtype);
-        J.dtype = A->dtype;
+        J.q_row = (const char *)A->q + ((size_t)b * A->hq + h) * A->d * elem_bytes(A->q_dtype);
+        J.q_dtype = A->q_dtype;
         J.d = A->d;
         J.scale = A->scale;
         J.n = A->ctx_lens[b];
@@ -245,12 +301,13 @@ static void *decode_worker(void *p)
         contig_ctx cc;
         if (A->paged) {
             pc.k_pool = A->k; pc.v_pool = A->v; pc.dtype = A->dtype; pc.hkv = A->hkv;
-            pc.d = A->d; pc.kv_head = kvh;
+            pc.d = A->d; pc.kv_head = kvh; pc.k_scale = A->k_scale; pc.v_scale = A->v_scale;
             pc.table_row = A->tables + (size_t)b * A->max_blocks;
             J.key = paged_key; J.val = paged_val; J.ctx = &pc;
         } else {
             cc.k = A->k; cc.v = A->v; cc.dtype = A->dtype; cc.hkv = A->hkv; cc.d = A->d;
             cc.s_max = A->s_max; cc.seq = b; cc.kv_head = kvh;
+            cc.k_scale = A->k_scale; cc.v_scale = A->v_scale;
             J.key = contig_key; J.val = contig_val; J.ctx = &cc;
         }
         attend(&J, A->out + (size_t)u * A->d, A->wsum + u);
@@ -292,23 +349,29 @@ static int run_decode(decode_args *A)
 
 static int check_common(int dtype, int B, int hq, int hkv, int d)
 {
-    if (dtype < ORACLE_F32 || dtype > ORACLE_BF16)
+    if (dtype < ORACLE_F32 || dtype > ORACLE_FP8_E4M3)
         return -1;
     if (B < 0 || hq <= 0 || hkv <= 0 || d <= 0 || hq % hkv != 0)
         return -1;
     return 0;
 }
 
-/* Paged decode attention.  out [B][Hq][d] and wsum [B][Hq] (sum of the normalised
- * softmax weights of each row) are fp64.  Returns 0, or -1 on bad shapes, -2 when a
- * context length or a block-table entry it would read is out of range.            */
-int oracle_decode_paged(const void *q, const void *k_pool, const void *v_pool, int dtype,
-                        int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
-                        int num_blocks, const int32_t *block_tables, int max_blocks_per_seq,
-                        const int32_t *context_lens, float scale, double *out, double *wsum,
-                        int num_threads)
+/* Paged decode attention.  q has type q_dtype; K/V are stored as kv_dtype and read
+ * as stored value x k_scale (x v_scale); for fp8 pools q_dtype is f16 or bf16, for the
+ * others it equals kv_dtype and the scales are 1.  out [B][Hq][d] and wsum [B][Hq]
+ * (sum of the normalised softmax weights of each row) are fp64.  Returns 0, or -1 on
+ * bad shapes, -2 when a context length or a block-table entry it would read is out
+ * of range.                                                                          */
+int oracle_decode_paged_ex(const void *q, int q_dtype, const void *k_pool, const void *v_pool,
+                           int kv_dtype, double k_scale, double v_scale, int num_seqs,
+                           int num_q_heads, int num_kv_heads, int head_dim, int num_blocks,
+                           const int32_t *block_tables, int max_blocks_per_seq,
+                           const int32_t *context_lens, float scale, double *out, double *wsum,
+                           int num_threads)
 {
-    if (check_common(dtype, num_seqs, num_q_heads, num_kv_heads, head_dim))
+    if (check_common(kv_dtype, num_seqs, num_q_heads, num_kv_heads, head_dim) ||
+        check_common(q_dtype, num_seqs, num_q_heads, num_kv_heads, head_dim) ||
+        q_dtype == ORACLE_FP8_E4M3)
         return -1;
     for (int b = 0; b < num_seqs; ++b) {
         int n = context_lens[b];
@@ -320,40 +383,78 @@ int oracle_decode_paged(const void *q, const void *k_pool, const void *v_pool, i
                 return -2;
         }
     }
-    decode_args A = {1, q, k_pool, v_pool, dtype, num_seqs, num_q_heads, num_kv_heads,
-                     head_dim, num_blocks, max_blocks_per_seq, 0, block_tables, context_lens,
-                     (double)scale, out, wsum, num_threads};
+    decode_args A = {1, q, k_pool, v_pool, kv_dtype, q_dtype, k_scale, v_scale, num_seqs,
+                     num_q_heads, num_kv_heads, head_dim, num_blocks, max_blocks_per_seq, 0,
+                     block_tables, context_lens, (double)scale, out, wsum, num_threads};
     return run_decode(&A);
 }
 
-/* The same attention over an ordinary contiguous cache k, v [B][Hkv][S_max][d].    */
+/* Same with q and K/V all of one type and unit scales.                             */
+int oracle_decode_paged(const void *q, const void *k_pool, const void *v_pool, int dtype,
+                        int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                        int num_blocks, const int32_t *block_tables, int max_blocks_per_seq,
+                        const int32_t *context_lens, float scale, double *out, double *wsum,
+                        int num_threads)
+{
+    return oracle_decode_paged_ex(q, dtype, k_pool, v_pool, dtype, 1.0, 1.0, num_seqs,
+                                  num_q_heads, num_kv_heads, head_dim, num_blocks, block_tables,
+                                  max_blocks_per_seq, context_lens, scale, out, wsum,
+                                  num_threads);
+}
+
+/* The same attention over an ordinary contiguous cache k, v [B][Hkv][S_max][d] of
+ * kv_dtype (read as value x scale), q of q_dtype.                                     */
+int oracle_decode_contig_ex(const void *q, int q_dtype, const void *k, const void *v,
+                            int kv_dtype, double k_scale, double v_scale, int num_seqs,
+                            int num_q_heads, int num_kv_heads, int head_dim, int s_max,
+                            const int32_t *context_lens, float scale, double *out,
+                            double *wsum, int num_threads)
+{
+    if (check_common(kv_dtype, num_seqs, num_q_heads, num_kv_heads, head_dim) ||
+        check_common(q_dtype, num_seqs, num_q_heads, num_kv_heads, head_dim) ||
+        q_dtype == ORACLE_FP8_E4M3)
+        return -1;
+    for (int b = 0; b < num_seqs; ++b)
+        if (context_lens[b] < 0 || context_lens[b] > s_max)
+            return -2;
+    decode_args A = {0, q, k, v, kv_dtype, q_dtype, k_scale, v_scale, num_seqs, num_q_heads,
+                     num_kv_heads, head_dim, 0, 0, s_max, NULL, context_lens, (double)scale,
+                     out, wsum, num_threads};
+    return run_decode(&A);
+}
+
 int oracle_decode_contig(const void *q, const void *k, const void *v, int dtype, int num_seqs,
                          int num_q_heads, int num_kv_heads, int head_dim, int s_max,
                          const int32_t *context_lens, float scale, double *out, double *wsum,
                          int num_threads)
 {
-    if (check_common(dtype, num_seqs, num_q_heads, num_kv_heads, head_dim))
-        return -1;
-    for (int b = 0; b < num_seqs; ++b)
-        if (context_lens[b] < 0 || context_lens[b] > s_max)
-            return -2;
-    decode_args A = {0, q, k, v, dtype, num_seqs, num_q_heads, num_kv_heads, head_dim, 0, 0,
-                     s_max, NULL, context_lens, (double)scale, out, wsum, num_threads};
-    return run_decode(&A);
+    return oracle_decode_contig_ex(q, dtype, k, v, dtype, 1.0, 1.0, num_seqs, num_q_heads,
+                                   num_kv_heads, head_dim, s_max, context_lens, scale, out,
+                                   wsum, num_threads);
 }
 
 /* Cache append: new row i goes to slot s = slot_mapping[i], i.e. physical block
  * s / 16, row s % 16 (the page/offset split of "LLM应用 12 推理优化",
  * PagedKVCache.update, and the write-into-the-last-page rule of LLM-101-CN
- * "推理优化", KVCachePool.write_tokens).  A negative slot means "no row".  Bytes are
- * copied unchanged.  k_new, v_new: [T][Hkv][d].  Returns -2 on a slot past the pool. */
-int oracle_cache_append(void *k_pool, void *v_pool, int dtype, int num_blocks,
-                        int num_kv_heads, int head_dim, const void *k_new, const void *v_new,
-                        const int32_t *slot_mapping, int num_tokens)
+ * "推理优化", KVCachePool.write_tokens).  A negative slot means "no row".
+ * k_new, v_new: [T][Hkv][d] of act_dtype.  When the pool has the new rows' type the
+ * bytes are copied unchanged.  An fp8 pool stores encode_e4m3(x / scale), the
+ * division done in fp32 (the KV-cache write fused with quantisation that "Deep dive
+ * into vLLM 06" lists among vLLM's fused kernels).  Returns -2 on a slot past the pool. */
+int oracle_cache_append_ex(void *k_pool, void *v_pool, int kv_dtype, int act_dtype,
+                           float k_scale, float v_scale, int num_blocks, int num_kv_heads,
+                           int head_dim, const void *k_new, const void *v_new,
+                           const int32_t *slot_mapping, int num_tokens)
 {
-    if (check_common(dtype, 1, num_kv_heads, num_kv_heads, head_dim) || num_tokens < 0)
+    if (check_common(kv_dtype, 1, num_kv_heads, num_kv_heads, head_dim) || num_tokens < 0 ||
+        check_common(act_dtype, 1, num_kv_heads, num_kv_heads, head_dim))
         return -1;
-    const size_t eb = elem_bytes(dtype);
+    const int quantise = kv_dtype == ORACLE_FP8_E4M3;
+    if (!quantise && act_dtype != kv_dtype)
+        return -1;
+    if (quantise && act_dtype != ORACLE_F16 && act_dtype != ORACLE_BF16)
+        return -1;
+    const size_t eb = elem_bytes(kv_dtype);
     for (int i = 0; i < num_tokens; ++i) {
         int32_t s = slot_mapping[i];
         if (s < 0)
@@ -366,10 +467,26 @@ int oracle_cache_append(void *k_pool, void *v_pool, int dtype, int num_blocks,
                 size_t src = ((size_t)i * num_kv_heads + h) * head_dim + e;
                 size_t kdst = ((blk * num_kv_heads + h) * ORACLE_BLOCK + off) * head_dim + e;
                 size_t vdst = ((blk * num_kv_heads + h) * head_dim + e) * ORACLE_BLOCK + off;
-                memcpy((char *)k_pool + kdst * eb, (const char *)k_new + src * eb, eb);
-                memcpy((char *)v_pool + vdst * eb, (const char *)v_new + src * eb, eb);
+                if (quantise) {
+                    float kx = (float)widen_at(k_new, src, act_dtype);
+                    float vx = (float)widen_at(v_new, src, act_dtype);
+                    ((uint8_t *)k_pool)[kdst] = encode_e4m3(kx / k_scale);
+                    ((uint8_t *)v_pool)[vdst] = encode_e4m3(vx / v_scale);
+                } else {
+                    memcpy((char *)k_pool + kdst * eb, (const char *)k_new + src * eb, eb);
+                    memcpy((char *)v_pool + vdst * eb, (const char *)v_new + src * eb, eb);
+                }
             }
         }
     }
     return 0;
+}
+
+int oracle_cache_append(void *k_pool, void *v_pool, int dtype, int num_blocks,
+                        int num_kv_heads, int head_dim, const void *k_new, const void *v_new,
+                        const int32_t *slot_mapping, int num_tokens)
+{
+    return oracle_cache_append_ex(k_pool, v_pool, dtype, dtype, 1.0f, 1.0f, num_blocks,
+                                  num_kv_heads, head_dim, k_new, v_new, slot_mapping,
+                                  num_tokens);
 }

@@ -18,8 +18,9 @@ LIB_PATH = os.path.join(HERE, "libpa_mi355x.so")
 HEADER_PATH = os.path.join(os.path.dirname(HERE), "include", "paged_attention.h")
 
 BLOCK_SIZE = 16
-PA_F32, PA_F16, PA_BF16 = 0, 1, 2
+PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3 = 0, 1, 2, 3
 DTYPE_CODE = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}
+FP8_STORAGE = (torch.uint8, torch.float8_e4m3fn)   # tensors holding OCP E4M3 codes
 STATUS = {0: "PA_OK", 1: "PA_ERR_INVALID_ARG", 2: "PA_ERR_UNSUPPORTED", 3: "PA_ERR_WORKSPACE",
           4: "PA_ERR_HIP"}
 
@@ -34,7 +35,8 @@ class PaKvPool(ctypes.Structure):
     _fields_ = [("k_pool", ctypes.c_void_p), ("v_pool", ctypes.c_void_p),
                 ("num_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32),
                 ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
-                ("dtype", ctypes.c_int32)]
+                ("dtype", ctypes.c_int32), ("act_dtype", ctypes.c_int32),
+                ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float)]
 
 
 _lib = None
@@ -89,31 +91,52 @@ def _dev_ptr(t: Optional[torch.Tensor], name: str, dtype=None) -> Optional[int]:
     return t.data_ptr()
 
 
-def make_pool(k_pool: torch.Tensor, v_pool: torch.Tensor) -> PaKvPool:
-    """k_pool [N][Hkv][16][d] and v_pool [N][Hkv][d][16], same dtype."""
+def make_pool(k_pool, v_pool, act_dtype: Optional[torch.dtype] = None, k_scale: float = 1.0,
+              v_scale: float = 1.0) -> PaKvPool:
+    """k_pool [N][Hkv][16][d] and v_pool [N][Hkv][d][16], same dtype.  FP8 pools are
+    uint8 (or float8_e4m3fn) tensors of E4M3 codes; act_dtype (f16/bf16) is then the
+    type of q, out and the new rows, and K = code * k_scale, V = code * v_scale."""
     if k_pool.dim() != 4 or v_pool.dim() != 4:
         raise ValueError("pools are 4-D: k [N][Hkv][16][d], v [N][Hkv][d][16]")
     n, hkv, bs, d = k_pool.shape
     if tuple(v_pool.shape) != (n, hkv, d, bs) or v_pool.dtype != k_pool.dtype:
         raise ValueError("v_pool must be [N][Hkv][d][16] with k_pool's dtype")
-    if k_pool.dtype not in DTYPE_CODE:
+    if k_pool.dtype in FP8_STORAGE:
+        if act_dtype not in (torch.float16, torch.bfloat16):
+            raise ValueError("an fp8 pool needs act_dtype float16 or bfloat16")
+        code, act = PA_FP8_E4M3, DTYPE_CODE[act_dtype]
+    elif k_pool.dtype in DTYPE_CODE:
+        if act_dtype not in (None, k_pool.dtype):
+            raise ValueError("act_dtype must equal the pool dtype for f32/f16/bf16 pools")
+        code = act = DTYPE_CODE[k_pool.dtype]
+        k_scale = v_scale = 1.0
+    else:
         raise ValueError(f"unsupported dtype {k_pool.dtype}")
     return PaKvPool(_dev_ptr(k_pool, "k_pool"), _dev_ptr(v_pool, "v_pool"), n, bs, hkv, d,
-                    DTYPE_CODE[k_pool.dtype])
+                    code, act, float(k_scale), float(v_scale))
+
+
+def _act_dtype(pool: PaKvPool) -> torch.dtype:
+    return {v: k for k, v in DTYPE_CODE.items()}[pool.act_dtype]
 
 
 def pool_bytes(num_blocks: int, num_kv_heads: int, head_dim: int, dtype: torch.dtype) -> int:
-    return int(load().pa_pool_bytes(num_blocks, num_kv_heads, head_dim, DTYPE_CODE[dtype]))
+    code = PA_FP8_E4M3 if dtype in FP8_STORAGE else DTYPE_CODE[dtype]
+    return int(load().pa_pool_bytes(num_blocks, num_kv_heads, head_dim, code))
 
 
-def cache_append(k_pool, v_pool, k_new, v_new, slot_mapping) -> None:
-    """Write k_new/v_new [T][Hkv][d] rows into the pools at slot_mapping [T] (int32)."""
-    pool = make_pool(k_pool, v_pool)
+def cache_append(k_pool, v_pool, k_new, v_new, slot_mapping, k_scale: float = 1.0,
+                 v_scale: float = 1.0) -> None:
+    """Write k_new/v_new [T][Hkv][d] rows into the pools at slot_mapping [T] (int32);
+    an fp8 pool stores the E4M3 codes of k_new / k_scale and v_new / v_scale."""
+    act = k_new.dtype if k_pool.dtype in FP8_STORAGE else None
+    pool = make_pool(k_pool, v_pool, act, k_scale, v_scale)
     T = int(slot_mapping.numel())
     if tuple(k_new.shape) != (T, pool.num_kv_heads, pool.head_dim) or k_new.shape != v_new.shape:
         raise ValueError("k_new/v_new must be [T][Hkv][d]")
-    st = load().pa_cache_append(ctypes.byref(pool), _dev_ptr(k_new, "k_new", k_pool.dtype),
-                                _dev_ptr(v_new, "v_new", k_pool.dtype),
+    act = _act_dtype(pool)
+    st = load().pa_cache_append(ctypes.byref(pool), _dev_ptr(k_new, "k_new", act),
+                                _dev_ptr(v_new, "v_new", act),
                                 _dev_ptr(slot_mapping, "slot_mapping", torch.int32), T,
                                 _stream_handle(k_pool.device))
     _raise(st)
@@ -136,13 +159,16 @@ def workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim
 
 def decode(q, k_pool, v_pool, block_tables, context_lens, scale: float, max_context_len: int,
            partition_tokens: int = 0, out: Optional[torch.Tensor] = None,
-           workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+           workspace: Optional[torch.Tensor] = None, k_scale: float = 1.0,
+           v_scale: float = 1.0) -> torch.Tensor:
     """softmax(q K^T scale) V per sequence and q-head through the block tables.
 
     q [B][Hq][d]; block_tables [B][max_blocks] int32; context_lens [B] int32;
-    max_context_len: host-side bound of context_lens.  Returns out [B][Hq][d].
+    max_context_len: host-side bound of context_lens.  Returns out [B][Hq][d] in q's
+    dtype.  For an fp8 pool, K = code * k_scale and V = code * v_scale.
     """
-    pool = make_pool(k_pool, v_pool)
+    act = q.dtype if k_pool.dtype in FP8_STORAGE else None
+    pool = make_pool(k_pool, v_pool, act, k_scale, v_scale)
     B, hq, d = q.shape
     if d != pool.head_dim:
         raise ValueError("q head_dim differs from the pool's")
@@ -153,8 +179,9 @@ def decode(q, k_pool, v_pool, block_tables, context_lens, scale: float, max_cont
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = _dev_ptr(workspace, "workspace") if need else None
     ws_len = workspace.numel() * workspace.element_size() if need else 0
-    st = load().pa_decode(ctypes.byref(pool), _dev_ptr(q, "q", k_pool.dtype),
-                          _dev_ptr(out, "out", k_pool.dtype), B, hq, ctypes.c_float(scale),
+    act = _act_dtype(pool)
+    st = load().pa_decode(ctypes.byref(pool), _dev_ptr(q, "q", act), _dev_ptr(out, "out", act),
+                          B, hq, ctypes.c_float(scale),
                           _dev_ptr(block_tables, "block_tables", torch.int32),
                           block_tables.shape[1], _dev_ptr(context_lens, "context_lens",
                                                           torch.int32),

@@ -13,7 +13,10 @@ namespace {
 
 using pa::kBlock;
 
-bool dtype_ok(int32_t dtype) { return dtype == PA_F32 || dtype == PA_F16 || dtype == PA_BF16; }
+bool dtype_ok(int32_t dtype)
+{
+    return dtype == PA_F32 || dtype == PA_F16 || dtype == PA_BF16 || dtype == PA_FP8_E4M3;
+}
 
 bool head_dim_ok(int32_t dtype, int32_t head_dim)
 {
@@ -22,7 +25,7 @@ bool head_dim_ok(int32_t dtype, int32_t head_dim)
     return head_dim == 256 && dtype != PA_F32;
 }
 
-size_t elem_bytes(int32_t dtype) { return dtype == PA_F32 ? 4 : 2; }
+size_t elem_bytes(int32_t dtype) { return dtype == PA_F32 ? 4 : (dtype == PA_FP8_E4M3 ? 1 : 2); }
 
 // Most blocks one wave may walk in one partition: the kernel keeps a wave's block ids
 // one per lane of a single register.
@@ -40,6 +43,15 @@ pa_status check_pool(const pa_kv_pool *pool)
         return PA_ERR_UNSUPPORTED;
     if ((int64_t)pool->num_blocks * kBlock > INT32_MAX)   // slots are int32
         return PA_ERR_UNSUPPORTED;
+    if (pool->dtype == PA_FP8_E4M3) {
+        if (pool->act_dtype != PA_F16 && pool->act_dtype != PA_BF16)
+            return PA_ERR_UNSUPPORTED;
+        if (!(pool->k_scale > 0.f) || !(pool->v_scale > 0.f) || !isfinite(pool->k_scale) ||
+            !isfinite(pool->v_scale))
+            return PA_ERR_INVALID_ARG;
+    } else if (pool->act_dtype != pool->dtype) {
+        return PA_ERR_UNSUPPORTED;
+    }
     return PA_OK;
 }
 
@@ -141,7 +153,10 @@ pa_status pa_cache_append(const pa_kv_pool *pool, const void *k_new, const void 
     a.num_tokens = num_tokens;
     a.num_blocks = pool->num_blocks;
     a.num_kv_heads = pool->num_kv_heads;
-    hipError_t e = pa::launch_append(pool->dtype, pool->head_dim, a,
+    a.k_scale = pool->k_scale;
+    a.v_scale = pool->v_scale;
+    a.bf16 = pool->act_dtype == PA_BF16 ? 1 : 0;
+    hipError_t e = pa::launch_append(pool->dtype, pool->act_dtype, pool->head_dim, a,
                                      static_cast<hipStream_t>(stream));
     return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
@@ -225,12 +240,14 @@ pa_status pa_decode(const pa_kv_pool *pool, const void *q, void *out, int32_t nu
     a.max_context_len = max_context_len;
     a.part_blocks = pb;
     a.num_parts = parts;
-    a.scale_log2 = scale * 1.4426950408889634f;
+    const bool fp8 = pool->dtype == PA_FP8_E4M3;
+    a.scale_log2 = scale * 1.4426950408889634f * (fp8 ? pool->k_scale : 1.0f);
+    a.v_scale = fp8 ? pool->v_scale : 1.0f;
     a.split = parts > 1 ? 1 : 0;
     a.longest_first = (num_seqs > 1 && num_seqs <= pa::kLongestFirstMax) ? 1 : 0;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = pa::launch_decode(pool->dtype, pool->head_dim, a, num_seqs, s);
+    hipError_t e = pa::launch_decode(pool->dtype, pool->act_dtype, pool->head_dim, a, num_seqs, s);
     return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 

@@ -9,6 +9,10 @@
 // One thread moves one 16-byte chunk of one (token, kv-head) row: a single 16-byte
 // store into the token-major K block, and 16/elem scalar stores into the token-minor
 // V block (stride 16 elements).
+//
+// An fp8 pool stores OCP E4M3 codes of x / scale (the KV-cache write fused with its
+// quantisation, one of the fused kernels "Deep dive into vLLM 06" lists): the
+// division is IEEE fp32, the code rounds to nearest-even and saturates at 448.
 #include "pa_common.h"
 
 namespace pa {
@@ -58,6 +62,70 @@ __global__ __launch_bounds__(256) void pa_cache_append_kernel(AppendArgs a)
     }
 }
 
+// fp32 -> E4M3 code by bit arithmetic on the binary32 encoding: round the 23-bit
+// fraction to 3 bits (nearest, ties to even) and rebias the exponent 127 -> 7; below
+// 2^-6 the code counts steps of 2^-9; NaN stays NaN, |x| >= 448 gives +-448.
+__device__ __forceinline__ uint32_t e4m3_code(float x)
+{
+    const uint32_t u = __float_as_uint(x);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const uint32_t a = u & 0x7FFFFFFFu;
+    if (a > 0x7F800000u)
+        return sign | 0x7Fu;                              // NaN
+    if (a >= 0x43E00000u)
+        return sign | 0x7Eu;                              // >= 448 (and inf): 448
+    if (a < 0x3C800000u)                                  // < 2^-6: subnormal codes
+        return sign | (uint32_t)rintf(__uint_as_float(a) * 512.0f);
+    const uint32_t rounded = a + 0x7FFFFu + ((a >> 20) & 1u);
+    return sign | ((rounded >> 20) - (120u << 3));
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void pa_cache_append_fp8_kernel(AppendArgs a)
+{
+    constexpr int CPR = D / 8;                // 8 elements (16 bytes of f16/bf16) per thread
+    const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const size_t total = (size_t)a.num_tokens * a.num_kv_heads * CPR;
+    if (idx >= total)
+        return;
+    const int c = (int)(idx % CPR);
+    const size_t row = idx / CPR;
+    const int h = (int)(row % a.num_kv_heads);
+    const int i = (int)(row / a.num_kv_heads);
+    const u32x4 kv = *reinterpret_cast<const u32x4 *>(
+        static_cast<const uint16_t *>(a.k_new) + row * D + (size_t)c * 8);
+    const u32x4 vv = *reinterpret_cast<const u32x4 *>(
+        static_cast<const uint16_t *>(a.v_new) + row * D + (size_t)c * 8);
+    const int32_t slot = a.slot_mapping[i];
+    if (slot < 0 || (int64_t)slot >= (int64_t)a.num_blocks * kBlock)
+        return;
+    const size_t blk = (size_t)(slot / kBlock);
+    const int off = slot % kBlock;
+    const size_t tile = (blk * a.num_kv_heads + h) * (size_t)kBlock * D;   // bytes
+    uint32_t kc[2] = {0u, 0u};
+    uint8_t *vdst = static_cast<uint8_t *>(a.v_pool) + tile + (size_t)c * 8 * kBlock + off;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const uint32_t kw = (kv[j / 2] >> (16 * (j & 1))) & 0xFFFFu;
+        const uint32_t vw = (vv[j / 2] >> (16 * (j & 1))) & 0xFFFFu;
+        const float kx = a.bf16 ? __uint_as_float(kw << 16) : (float)__builtin_bit_cast(_Float16, (uint16_t)kw);
+        const float vx = a.bf16 ? __uint_as_float(vw << 16) : (float)__builtin_bit_cast(_Float16, (uint16_t)vw);
+        kc[j / 4] |= e4m3_code(__fdiv_rn(kx, a.k_scale)) << (8 * (j & 3));
+        vdst[j * kBlock] = (uint8_t)e4m3_code(__fdiv_rn(vx, a.v_scale));
+    }
+    *reinterpret_cast<uint2 *>(static_cast<uint8_t *>(a.k_pool) + tile + (size_t)off * D +
+                               (size_t)c * 8) = make_uint2(kc[0], kc[1]);
+}
+
+template <int D>
+hipError_t launch_append_fp8_t(const AppendArgs &a, hipStream_t stream)
+{
+    const size_t total = (size_t)a.num_tokens * a.num_kv_heads * (D / 8);
+    const unsigned blocks = (unsigned)((total + 255) / 256);
+    hipLaunchKernelGGL((pa_cache_append_fp8_kernel<D>), dim3(blocks), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
 template <int EB, int D>
 hipError_t launch_append_t(const AppendArgs &a, hipStream_t stream)
 {
@@ -70,8 +138,21 @@ hipError_t launch_append_t(const AppendArgs &a, hipStream_t stream)
 
 }  // namespace
 
-hipError_t launch_append(int dtype, int head_dim, const AppendArgs &a, hipStream_t stream)
+hipError_t launch_append(int dtype, int act_dtype, int head_dim, const AppendArgs &a,
+                         hipStream_t stream)
 {
+    if (dtype == DT_FP8) {
+        if (act_dtype != DT_F16 && act_dtype != DT_BF16)
+            return hipErrorInvalidValue;
+        AppendArgs b = a;
+        b.bf16 = act_dtype == DT_BF16 ? 1 : 0;
+        switch (head_dim) {
+        case 64: return launch_append_fp8_t<64>(b, stream);
+        case 128: return launch_append_fp8_t<128>(b, stream);
+        case 256: return launch_append_fp8_t<256>(b, stream);
+        default: return hipErrorInvalidValue;
+        }
+    }
     const int eb = dtype == DT_F32 ? 4 : 2;
     switch (eb * 1000 + head_dim) {
     case 4064: return launch_append_t<4, 64>(a, stream);

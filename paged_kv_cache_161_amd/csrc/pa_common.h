@@ -6,7 +6,7 @@
 
 namespace pa {
 
-enum Dt : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
+enum Dt : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_FP8 = 3 };
 
 constexpr int kBlock = 16;            // tokens per physical block
 constexpr int kWave = 64;             // CDNA4 wavefront width
@@ -31,7 +31,8 @@ struct DecodeArgs {
     int32_t max_context_len;
     int32_t part_blocks;              // blocks per partition
     int32_t num_parts;                // P (grid x)
-    float scale_log2;                 // scale * log2(e)
+    float scale_log2;                 // scale * log2(e) (* k_scale for fp8 pools)
+    float v_scale;                    // multiplies the output (fp8 pools; else 1)
     int32_t split;                    // 1: write partials, 0: write out
     int32_t longest_first;            // 1: workgroup z takes the z-th longest sequence
 };
@@ -48,12 +49,18 @@ struct AppendArgs {
     int32_t num_tokens;
     int32_t num_blocks;
     int32_t num_kv_heads;
+    float k_scale;                    // fp8 pools: stored code = E4M3(x / scale)
+    float v_scale;
+    int32_t bf16;                     // fp8 pools: new rows are bf16 (else f16)
 };
 
 // Launchers (return hipSuccess or the launch error).
-hipError_t launch_decode(int dtype, int head_dim, const DecodeArgs &a, int num_seqs,
+// dtype: the pools' element type; act_dtype: q / out / new rows (== dtype except for
+// fp8 pools, where it is f16 or bf16).
+hipError_t launch_decode(int dtype, int act_dtype, int head_dim, const DecodeArgs &a,
+                         int num_seqs, hipStream_t stream);
+hipError_t launch_append(int dtype, int act_dtype, int head_dim, const AppendArgs &a,
                          hipStream_t stream);
-hipError_t launch_append(int dtype, int head_dim, const AppendArgs &a, hipStream_t stream);
 
 // Decode launch shape for 16-bit K/V with head_dim <= 128: waves per workgroup and
 // blocks each wave keeps in flight ahead of the one it is computing.

@@ -143,81 +143,159 @@ struct Q32 {
     }
 };
 
-template <int DT, int D> struct Frags {
+// FP8 (OCP E4M3) K/V with 16-bit q.  The same lane roles as the 16-bit tiles, with
+// half the bytes: each code converts exactly to the 16-bit MFMA type in registers
+// (every E4M3 value is a bf16 and an f16 value), the per-tensor scales are applied
+// in fp32 outside the MFMAs.
+template <int AT, int D>
+struct Tile8 {
+    static constexpr int NQK = D / 32;
+    static constexpr int NPV = D / 16;
+    u32x2 k[NQK];                        // 8 codes of K[r][32i + 8g .. +7]
+    uint32_t v[NPV];                     // 4 codes of V^T[16n + r][4g .. 4g+3]
+
+    __device__ __forceinline__ void load(const uint8_t *kt, const uint8_t *vt, int r, int g)
+    {
+#pragma unroll
+        for (int i = 0; i < NQK; ++i)
+            k[i] = *reinterpret_cast<const u32x2 *>(kt + r * D + 32 * i + 8 * g);
+#pragma unroll
+        for (int n = 0; n < NPV; ++n)
+            v[n] = *reinterpret_cast<const uint32_t *>(vt + (16 * n + r) * kBlock + 4 * g);
+    }
+};
+
+// Two E4M3 codes (low or high half of w) -> two 16-bit values of type AT, packed.
+template <int AT, bool HIGH>
+__device__ __forceinline__ uint32_t e4m3x2_to_16(uint32_t w)
+{
+    if constexpr (AT == DT_BF16)
+        return __builtin_bit_cast(uint32_t,
+                                  __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, HIGH));
+    else
+        return __builtin_bit_cast(uint32_t,
+                                  __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w, 1.0f, HIGH));
+}
+
+template <int DT, int AT, int D> struct Frags {          // 16-bit K/V, DT == AT
     using Tile = Tile16<DT, D>;
     using Q = Q16<DT, D>;
     using Elem = uint16_t;
+    using QElem = uint16_t;
 };
-template <int D> struct Frags<DT_F32, D> {
+template <int D> struct Frags<DT_F32, DT_F32, D> {
     using Tile = Tile32<D>;
     using Q = Q32<D>;
     using Elem = float;
+    using QElem = float;
+};
+template <int AT, int D> struct Frags<DT_FP8, AT, D> {
+    using Tile = Tile8<AT, D>;
+    using Q = Q16<AT, D>;
+    using Elem = uint8_t;
+    using QElem = uint16_t;
 };
 
+// 16x16x32 MFMA on 16-bit operands of type AT.
+template <int AT>
+__device__ __forceinline__ f32x4 mfma_k32(u32x4 a, u32x4 b, f32x4 c)
+{
+    if constexpr (AT == DT_BF16)
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// 16x16x16 MFMA on 16-bit operands of type AT.
+template <int AT>
+__device__ __forceinline__ f32x4 mfma_k16(u32x2 a, u32x2 b, f32x4 c)
+{
+    if constexpr (AT == DT_BF16)
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a),
+                                                         __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
+                                                     __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
+}
+
+// fp32 weights -> two packed 16-bit words of type AT (RNE), and back to fp32.
+template <int AT>
+__device__ __forceinline__ u32x2 pack16(f32x4 p, f32x4 &rounded)
+{
+    if constexpr (AT == DT_BF16) {
+        bf16x4 pb = __builtin_convertvector(p, bf16x4);
+        rounded = __builtin_convertvector(pb, f32x4);
+        return __builtin_bit_cast(u32x2, pb);
+    } else {
+        f16x4 ph = __builtin_convertvector(p, f16x4);
+        rounded = __builtin_convertvector(ph, f32x4);
+        return __builtin_bit_cast(u32x2, ph);
+    }
+}
+
 // S[t][h] for the 16 tokens of a block (lane holds tokens 4g..4g+3 of head r).
-template <int DT, int D>
-__device__ __forceinline__ f32x4 scores(const typename Frags<DT, D>::Tile &t,
-                                        const typename Frags<DT, D>::Q &q)
+template <int DT, int AT, int D>
+__device__ __forceinline__ f32x4 scores(const typename Frags<DT, AT, D>::Tile &t,
+                                        const typename Frags<DT, AT, D>::Q &q)
 {
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
-    if constexpr (DT == DT_BF16) {
-#pragma unroll
-        for (int i = 0; i < D / 32; ++i)
-            s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, t.k[i]),
-                                                        __builtin_bit_cast(bf16x8, q.f[i]), s,
-                                                        0, 0, 0);
-    } else if constexpr (DT == DT_F16) {
-#pragma unroll
-        for (int i = 0; i < D / 32; ++i)
-            s = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, t.k[i]),
-                                                       __builtin_bit_cast(f16x8, q.f[i]), s,
-                                                       0, 0, 0);
-    } else {
+    if constexpr (DT == DT_F32) {
 #pragma unroll
         for (int c = 0; c < D / 16; ++c)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 s = __builtin_amdgcn_mfma_f32_16x16x4f32(t.k[c][j], q.f[c][j], s, 0, 0, 0);
+    } else if constexpr (DT == DT_FP8) {
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i) {
+            const u32x4 kk = {e4m3x2_to_16<AT, false>(t.k[i][0]), e4m3x2_to_16<AT, true>(t.k[i][0]),
+                              e4m3x2_to_16<AT, false>(t.k[i][1]), e4m3x2_to_16<AT, true>(t.k[i][1])};
+            s = mfma_k32<AT>(kk, q.f[i], s);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i)
+            s = mfma_k32<AT>(t.k[i], q.f[i], s);
     }
     return s;
 }
 
 // O^T[e][h] += V^T[e][t] P[t][h].  p holds this lane's 4 weights (tokens 4g..4g+3 of
-// head r).  Returns the weights as the MFMA consumed them (16-bit rounded for
-// 16-bit K/V), so the caller's normaliser sums exactly what was multiplied into V.
-template <int DT, int D>
-__device__ __forceinline__ f32x4 accumulate_pv(typename Frags<DT, D>::Tile &t, f32x4 p,
+// head r).  Returns the weights as the MFMA consumed them (16-bit rounded for 16-bit
+// and fp8 K/V), so the caller's normaliser sums exactly what was multiplied into V.
+template <int DT, int AT, int D>
+__device__ __forceinline__ f32x4 accumulate_pv(typename Frags<DT, AT, D>::Tile &t, f32x4 p,
                                                f32x4 (&o)[D / 16])
 {
-    if constexpr (DT == DT_BF16) {
-        bf16x4 pb = __builtin_convertvector(p, bf16x4);
-        i16x4 pk = __builtin_bit_cast(i16x4, pb);
-#pragma unroll
-        for (int n = 0; n < D / 16; ++n)
-            o[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, t.v[n]),
-                                                             pk, o[n], 0, 0, 0);
-        return __builtin_convertvector(pb, f32x4);
-    } else if constexpr (DT == DT_F16) {
-        f16x4 ph = __builtin_convertvector(p, f16x4);
-#pragma unroll
-        for (int n = 0; n < D / 16; ++n)
-            o[n] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, t.v[n]), ph,
-                                                         o[n], 0, 0, 0);
-        return __builtin_convertvector(ph, f32x4);
-    } else {
+    if constexpr (DT == DT_F32) {
 #pragma unroll
         for (int n = 0; n < D / 16; ++n)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 o[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(t.v[n][j], p[j], o[n], 0, 0, 0);
         return p;
+    } else {
+        f32x4 used;
+        const u32x2 pk = pack16<AT>(p, used);
+#pragma unroll
+        for (int n = 0; n < D / 16; ++n) {
+            if constexpr (DT == DT_FP8) {
+                const u32x2 vv = {e4m3x2_to_16<AT, false>(t.v[n]), e4m3x2_to_16<AT, true>(t.v[n])};
+                o[n] = mfma_k16<AT>(vv, pk, o[n]);
+            } else {
+                o[n] = mfma_k16<AT>(t.v[n], pk, o[n]);
+            }
+        }
+        return used;
     }
 }
 
 // Zero the V^T entries of tokens >= valid in a partial block.  Rows past the context
 // may hold anything (NaN included); a zero weight alone would not cancel them.
-template <int DT, int D>
-__device__ __forceinline__ void mask_tail_v(typename Frags<DT, D>::Tile &t, int valid, int g)
+template <int DT, int AT, int D>
+__device__ __forceinline__ void mask_tail_v(typename Frags<DT, AT, D>::Tile &t, int valid, int g)
 {
     const int t0 = 4 * g;
     if constexpr (DT == DT_F32) {
@@ -226,6 +304,14 @@ __device__ __forceinline__ void mask_tail_v(typename Frags<DT, D>::Tile &t, int 
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 t.v[n][j] = (t0 + j < valid) ? t.v[n][j] : 0.f;
+    } else if constexpr (DT == DT_FP8) {
+        uint32_t m = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            m |= (t0 + j < valid) ? (0xFFu << (8 * j)) : 0u;
+#pragma unroll
+        for (int n = 0; n < D / 16; ++n)
+            t.v[n] &= m;
     } else {
         const uint32_t m0 = (t0 < valid ? 0x0000FFFFu : 0u) | (t0 + 1 < valid ? 0xFFFF0000u : 0u);
         const uint32_t m1 = (t0 + 2 < valid ? 0x0000FFFFu : 0u) | (t0 + 3 < valid ? 0xFFFF0000u : 0u);
@@ -239,17 +325,23 @@ __device__ __forceinline__ void mask_tail_v(typename Frags<DT, D>::Tile &t, int 
 
 // ------------------------------------------------------------------ partition kernel
 
-// Waves per SIMD the register budget must allow for a prefetch depth.
+// Waves per SIMD the register budget must allow: a tile ring of up to 64 VGPRs (two
+// 16-bit tiles, or four fp8 tiles, at d = 128) fits three waves per SIMD.
 constexpr int min_waves_per_simd(int dt, int d, int pf)
 {
-    return (d > 128 || dt == DT_F32) ? 1 : (pf <= 1 ? 3 : (pf == 2 ? 2 : 1));
+    return (d > 128 || dt == DT_F32)
+               ? 1
+               : ((pf + 1) * (dt == DT_FP8 ? 16 : 32) * d / 128 <= 64
+                      ? 3
+                      : ((pf + 1) * (dt == DT_FP8 ? 16 : 32) * d / 128 <= 96 ? 2 : 1));
 }
 
-template <int DT, int D, int NW, int PF>
+template <int DT, int AT, int D, int NW, int PF>
 __global__ __launch_bounds__(NW *kWave, min_waves_per_simd(DT, D, PF)) void pa_decode_partition(DecodeArgs a)
 {
-    using F = Frags<DT, D>;
-    using Elem = typename F::Elem;
+    using F = Frags<DT, AT, D>;
+    using Elem = typename F::Elem;        // K/V storage element
+    using QElem = typename F::QElem;      // q / out element
     constexpr int DP = D + 4;                       // padded LDS row (floats)
 
     extern __shared__ float smem[];
@@ -281,7 +373,7 @@ __global__ __launch_bounds__(NW *kWave, min_waves_per_simd(DT, D, PF)) void pa_d
     auto load_seq = [&](int seq) {
         bt_lane = lb_lane < lb_cap ? a.block_tables[(size_t)seq * a.max_blocks + lb_lane] : 0;
         const bool hvalid = r < gs;
-        const Elem *qrow = static_cast<const Elem *>(a.q) +
+        const QElem *qrow = static_cast<const QElem *>(a.q) +
                            ((size_t)seq * a.num_q_heads + hq0 + (hvalid ? r : 0)) * D;
         qf.load(qrow, hvalid, g);
     };
@@ -329,7 +421,7 @@ __global__ __launch_bounds__(NW *kWave, min_waves_per_simd(DT, D, PF)) void pa_d
         if (p == 0 && (bad_ctx || nblk_seq == 0)) {
             const float fill = bad_ctx ? __builtin_nanf("") : 0.f;
             for (int idx = tid; idx < gs * D; idx += NW * kWave)
-                store_elem<DT>(a.out, ((size_t)b * a.num_q_heads + hq0) * D + idx, fill);
+                store_elem<AT>(a.out, ((size_t)b * a.num_q_heads + hq0) * D + idx, fill);
         }
         return;
     }
@@ -361,13 +453,13 @@ __global__ __launch_bounds__(NW *kWave, min_waves_per_simd(DT, D, PF)) void pa_d
     auto process = [&](typename F::Tile &t, int i) {
         const int lb = lb_begin + wave + i * NW;
         const int valid = ctx - lb * kBlock;            // >= 1
-        f32x4 s = scores<DT, D>(t, qf);
+        f32x4 s = scores<DT, AT, D>(t, qf);
         f32x4 x = s * a.scale_log2;
         if (valid < kBlock) {
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 x[j] = (4 * g + j < valid) ? x[j] : -INFINITY;
-            mask_tail_v<DT, D>(t, valid, g);
+            mask_tail_v<DT, AT, D>(t, valid, g);
         }
         const float mx = wave_max_rows(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
         const float m_new = fmaxf(m_run, mx);
@@ -379,7 +471,7 @@ __global__ __launch_bounds__(NW *kWave, min_waves_per_simd(DT, D, PF)) void pa_d
 #pragma unroll
         for (int n = 0; n < D / 16; ++n)
             o[n] *= alpha;
-        const f32x4 pu = accumulate_pv<DT, D>(t, pw, o);
+        const f32x4 pu = accumulate_pv<DT, AT, D>(t, pw, o);
         l_run = l_run * alpha + ((pu[0] + pu[1]) + (pu[2] + pu[3]));
         m_run = m_new;
     };
@@ -450,11 +542,11 @@ __global__ __launch_bounds__(NW *kWave, min_waves_per_simd(DT, D, PF)) void pa_d
         }
         const size_t row = (size_t)b * a.num_q_heads + hq0 + h;
         if (!partial) {
-            const float val = any_bad ? qnan : (den > 0.f ? num / den : 0.f);
-            store_elem<DT>(a.out, row * D + e, val);
+            const float val = any_bad ? qnan : (den > 0.f ? num / den * a.v_scale : 0.f);
+            store_elem<AT>(a.out, row * D + e, val);
         } else {
             const size_t slot = row * a.num_parts + p;
-            a.ws_o[slot * D + e] = any_bad ? qnan : num;
+            a.ws_o[slot * D + e] = any_bad ? qnan : num * a.v_scale;
             if (e == 0) {
                 a.ws_m[slot] = any_bad ? qnan : M;
                 a.ws_l[slot] = any_bad ? qnan : den;
@@ -471,7 +563,7 @@ __global__ __launch_bounds__(NW *kWave, min_waves_per_simd(DT, D, PF)) void pa_d
 // workgroup per (sequence, kv-head, head chunk); a thread owns 4 consecutive elements
 // of one q-head and walks the partials 8 at a time, issuing all 8 partitions' loads
 // before using any of them.
-template <int DT, int D>
+template <int AT, int D>
 __global__ __launch_bounds__(256) void pa_decode_reduce(DecodeArgs a)
 {
     constexpr int QB = 8;
@@ -528,20 +620,22 @@ __global__ __launch_bounds__(256) void pa_decode_reduce(DecodeArgs a)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const float val = nan_seen ? qnan : (den > 0.f ? acc[j] / den : 0.f);
-            store_elem<DT>(a.out, row * D + 4 * c4 + j, val);
+            store_elem<AT>(a.out, row * D + 4 * c4 + j, val);
         }
     }
 }
 
-template <int DT, int D>
+template <int DT, int AT, int D>
 hipError_t launch_decode_t(const DecodeArgs &a, int num_seqs, hipStream_t stream)
 {
     constexpr int NW = waves_per_group(D);
-    constexpr int PF = (D <= 128 && DT != DT_F32) ? kPrefetchMain : 1;
+    // fp8 tiles are half the bytes: keep the same bytes in flight with a deeper ring
+    constexpr int PF = (D > 128 || DT == DT_F32) ? 1 : (DT == DT_FP8 ? 2 * kPrefetchMain + 1
+                                                                      : kPrefetchMain);
     const int gs_max = min(16, a.group);
     const size_t lds = sizeof(float) * (NW * 32 + 16 + (size_t)NW * gs_max * (D + 4)) +
                        (a.longest_first ? sizeof(int) * (num_seqs + 1) : 0);
-    auto kern = pa_decode_partition<DT, D, NW, PF>;
+    auto kern = pa_decode_partition<DT, AT, D, NW, PF>;
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -554,30 +648,34 @@ hipError_t launch_decode_t(const DecodeArgs &a, int num_seqs, hipStream_t stream
     if (e != hipSuccess || !a.split)
         return e;
     dim3 rgrid(a.num_kv_heads * a.head_chunks, num_seqs);
-    hipLaunchKernelGGL((pa_decode_reduce<DT, D>), rgrid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((pa_decode_reduce<AT, D>), rgrid, dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 
 }  // namespace
 
-#define PA_DISPATCH(FN, ...)                                                              \
-    switch (dtype * 1000 + head_dim) {                                                    \
-    case DT_F32 * 1000 + 64: return FN<DT_F32, 64>(__VA_ARGS__);                          \
-    case DT_F32 * 1000 + 128: return FN<DT_F32, 128>(__VA_ARGS__);                        \
-    case DT_F16 * 1000 + 64: return FN<DT_F16, 64>(__VA_ARGS__);                          \
-    case DT_F16 * 1000 + 128: return FN<DT_F16, 128>(__VA_ARGS__);                        \
-    case DT_F16 * 1000 + 256: return FN<DT_F16, 256>(__VA_ARGS__);                        \
-    case DT_BF16 * 1000 + 64: return FN<DT_BF16, 64>(__VA_ARGS__);                        \
-    case DT_BF16 * 1000 + 128: return FN<DT_BF16, 128>(__VA_ARGS__);                      \
-    case DT_BF16 * 1000 + 256: return FN<DT_BF16, 256>(__VA_ARGS__);                      \
-    default: return hipErrorInvalidValue;                                                 \
-    }
-
-hipError_t launch_decode(int dtype, int head_dim, const DecodeArgs &a, int num_seqs,
-                         hipStream_t stream)
+hipError_t launch_decode(int dtype, int act_dtype, int head_dim, const DecodeArgs &a,
+                         int num_seqs, hipStream_t stream)
 {
-    PA_DISPATCH(launch_decode_t, a, num_seqs, stream)
+#define PA_CASE(DT, AT, D)                                                                \
+    if (dtype == DT && act_dtype == AT && head_dim == D)                                  \
+        return launch_decode_t<DT, AT, D>(a, num_seqs, stream);
+    PA_CASE(DT_F32, DT_F32, 64)
+    PA_CASE(DT_F32, DT_F32, 128)
+    PA_CASE(DT_F16, DT_F16, 64)
+    PA_CASE(DT_F16, DT_F16, 128)
+    PA_CASE(DT_F16, DT_F16, 256)
+    PA_CASE(DT_BF16, DT_BF16, 64)
+    PA_CASE(DT_BF16, DT_BF16, 128)
+    PA_CASE(DT_BF16, DT_BF16, 256)
+    PA_CASE(DT_FP8, DT_F16, 64)
+    PA_CASE(DT_FP8, DT_F16, 128)
+    PA_CASE(DT_FP8, DT_F16, 256)
+    PA_CASE(DT_FP8, DT_BF16, 64)
+    PA_CASE(DT_FP8, DT_BF16, 128)
+    PA_CASE(DT_FP8, DT_BF16, 256)
+#undef PA_CASE
+    return hipErrorInvalidValue;
 }
-
 
 }  // namespace pa

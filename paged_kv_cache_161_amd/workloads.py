@@ -20,7 +20,10 @@ Recipe (every workload is synthetic; the pages use no dataset for this path):
     fragmented free list); entries past a sequence's last block point at a poisoned
     spare block, so a stray read stays in bounds but poisons the result.
 
-Storage in numpy: f32 -> float32, f16 -> float16, bf16 -> uint16 bit patterns.
+Storage in numpy: f32 -> float32, f16 -> float16, bf16 -> uint16 bit patterns,
+fp8 -> uint8 OCP E4M3 codes.  An fp8 workload keeps q and the new rows in its
+activation type (f16 or bf16); its pool history holds the codes of value / scale
+(torch's float8_e4m3fn conversion: the input, not the method, decides them).
 """
 from __future__ import annotations
 
@@ -34,17 +37,23 @@ from typing import List, Optional, Sequence, Tuple
 import numpy as np
 
 BLOCK = 16
-STORAGE = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16}
-ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
-NAN_BITS = {"f32": np.uint32(0x7FC00000), "f16": np.uint16(0x7E00), "bf16": np.uint16(0x7FC0)}
+STORAGE = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16, "fp8": np.uint8}
+ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}
+NAN_BITS = {"f32": np.uint32(0x7FC00000), "f16": np.uint16(0x7E00), "bf16": np.uint16(0x7FC0),
+            "fp8": np.uint8(0x7F)}
 _CHUNK = 1 << 22  # values drawn per generator call
 
 
 def round_to_storage(x: np.ndarray, dtype: str) -> np.ndarray:
-    """float32 -> storage representation, round-to-nearest-even."""
+    """float32 -> storage representation, round-to-nearest-even (fp8: E4M3 codes of x,
+    magnitudes clamped to 448 first)."""
     x = np.ascontiguousarray(x, np.float32)
     if dtype == "f32":
         return x
+    if dtype == "fp8":
+        import torch
+        t = torch.from_numpy(x).clamp(-448.0, 448.0).to(torch.float8_e4m3fn)
+        return t.view(torch.uint8).numpy()
     if dtype == "f16":
         return x.astype(np.float16)
     u = x.view(np.uint32)
@@ -70,6 +79,9 @@ class Spec:
     # groups of sequences sharing their first n blocks: [(seq ids, n_shared_blocks)]
     prefix_groups: Sequence[Tuple[Sequence[int], int]] = ()
     append: bool = True             # deliver token ctx-1 through cache_append
+    kv_dtype: Optional[str] = None  # pool type; None = dtype; "fp8" keeps q/new rows in dtype
+    k_scale: float = 1.0            # fp8 pools: K = code x k_scale, V = code x v_scale
+    v_scale: float = 1.0
 
 
 @dataclasses.dataclass
@@ -83,7 +95,10 @@ class Workload:
     0..n-1 (and the poisoned block to n), which leaves every logical K/V row unchanged.
     """
     spec: Spec
-    dtype: str
+    dtype: str                      # q, out and new rows
+    kv_dtype: str                   # pools
+    k_scale: np.float32
+    v_scale: np.float32
     q: np.ndarray                   # [B][Hq][d]
     num_blocks: int                 # size of the physical pool
     live_blocks: np.ndarray         # [n] distinct physical ids holding live tokens
@@ -124,7 +139,7 @@ class Workload:
     def logical_kv_bytes(self) -> int:
         """K+V bytes of every (token, kv-head) the step attends to, per sequence."""
         return int(self.context_lens.astype(np.int64).sum()) * self.num_kv_heads * 2 * \
-            self.head_dim * ELEM_BYTES[self.dtype]
+            self.head_dim * ELEM_BYTES[self.kv_dtype]
 
     def unique_kv_bytes(self) -> int:
         """K+V bytes of distinct physical token rows attended to (shared blocks once)."""
@@ -135,7 +150,7 @@ class Workload:
                 p = int(self.block_tables[b, lb])
                 seen[p] = max(seen.get(p, 0), min(BLOCK, n - lb * BLOCK))
         rows = sum(seen.values())
-        return rows * self.num_kv_heads * 2 * self.head_dim * ELEM_BYTES[self.dtype]
+        return rows * self.num_kv_heads * 2 * self.head_dim * ELEM_BYTES[self.kv_dtype]
 
     def pool_shapes(self):
         hkv, d = self.num_kv_heads, self.head_dim
@@ -144,8 +159,8 @@ class Workload:
     def host_pools(self):
         """Full poisoned pools with the live blocks in place (before the append)."""
         ks, vs = self.pool_shapes()
-        k = _poison(ks, self.dtype)
-        v = _poison(vs, self.dtype)
+        k = _poison(ks, self.kv_dtype)
+        v = _poison(vs, self.kv_dtype)
         k[self.live_blocks] = self.k_live[:-1]
         v[self.live_blocks] = self.v_live[:-1]
         return k, v
@@ -181,6 +196,8 @@ def _poison(shape, dtype):
         return np.full(shape, NAN_BITS["f32"], np.uint32).view(np.float32)
     if dtype == "f16":
         return np.full(shape, NAN_BITS["f16"], np.uint16).view(np.float16)
+    if dtype == "fp8":
+        return np.full(shape, NAN_BITS["fp8"], np.uint8)
     return np.full(shape, NAN_BITS["bf16"], np.uint16)
 
 
@@ -195,8 +212,8 @@ def _chunk_rng(seed: int, tag: int, chunk: int) -> np.random.Generator:
 
 
 def _fill_normals(seed: int, tag: int, dst: np.ndarray, sigma: float, dtype: str,
-                  transpose_blocks: bool = False):
-    """Fill dst (storage dtype) with sigma * N(0, 1) rounded to the storage type.
+                  transpose_blocks: bool = False, divisor: float = 1.0):
+    """Fill dst (storage dtype) with sigma * N(0, 1) / divisor rounded to the storage type.
 
     transpose_blocks: dst is [n][Hkv][d][16] and values are drawn in [n][Hkv][16][d]
     order (a V pool block drawn token-major, stored token-minor).
@@ -215,6 +232,8 @@ def _fill_normals(seed: int, tag: int, dst: np.ndarray, sigma: float, dtype: str
         vals = _chunk_rng(seed, tag, c).standard_normal(size=(b - a) * per, dtype=np.float32)
         if sigma != 1.0:
             vals *= np.float32(sigma)
+        if divisor != 1.0:
+            vals /= np.float32(divisor)
         vals = round_to_storage(vals, dtype).reshape(shape)
         if transpose_blocks:
             dst[a:b] = vals.transpose(0, 1, 3, 2)
@@ -232,6 +251,10 @@ def build(spec: Spec, seed: Optional[int] = None) -> Workload:
     seed = spec.seed if seed is None else seed
     rng = np.random.Generator(np.random.PCG64(seed))
     dt = spec.dtype
+    kdt = spec.kv_dtype or dt
+    assert kdt != "fp8" or dt in ("f16", "bf16"), "fp8 pools pair with f16/bf16 activations"
+    ks = np.float32(spec.k_scale if kdt == "fp8" else 1.0)
+    vsc = np.float32(spec.v_scale if kdt == "fp8" else 1.0)
     B = len(spec.context_lens)
     hq, hkv, d = spec.num_q_heads, spec.num_kv_heads, spec.head_dim
     assert hq % hkv == 0
@@ -293,12 +316,13 @@ def build(spec: Spec, seed: Optional[int] = None) -> Workload:
     # ---- values: each array from its own seeded streams (tags 1..5)
     q = np.empty((B, hq, d), STORAGE[dt])
     _fill_normals(seed, 1, q, spec.sigma, dt)
-    k_live = np.empty((live.size + 1, hkv, BLOCK, d), STORAGE[dt])
-    v_live = np.empty((live.size + 1, hkv, d, BLOCK), STORAGE[dt])
-    _fill_normals(seed, 2, k_live[:-1], spec.sigma, dt)
-    _fill_normals(seed, 3, v_live[:-1], spec.sigma, dt, transpose_blocks=True)
-    k_live[-1] = _poison((hkv, BLOCK, d), dt)
-    v_live[-1] = _poison((hkv, d, BLOCK), dt)
+    k_live = np.empty((live.size + 1, hkv, BLOCK, d), STORAGE[kdt])
+    v_live = np.empty((live.size + 1, hkv, d, BLOCK), STORAGE[kdt])
+    _fill_normals(seed, 2, k_live[:-1], spec.sigma, kdt, divisor=float(ks))
+    _fill_normals(seed, 3, v_live[:-1], spec.sigma, kdt, transpose_blocks=True,
+                  divisor=float(vsc))
+    k_live[-1] = _poison((hkv, BLOCK, d), kdt)
+    v_live[-1] = _poison((hkv, d, BLOCK), kdt)
     pos_of = {int(p): i for i, p in enumerate(live)}
 
     # tail rows past each context stay poisoned
@@ -306,8 +330,8 @@ def build(spec: Spec, seed: Optional[int] = None) -> Workload:
         n = int(ctx[b])
         if n % BLOCK:
             i = pos_of[int(tables[b, n // BLOCK])]
-            k_live[i, :, n % BLOCK:, :] = _poison((hkv, BLOCK - n % BLOCK, d), dt)
-            v_live[i, :, :, n % BLOCK:] = _poison((hkv, d, BLOCK - n % BLOCK), dt)
+            k_live[i, :, n % BLOCK:, :] = _poison((hkv, BLOCK - n % BLOCK, d), kdt)
+            v_live[i, :, :, n % BLOCK:] = _poison((hkv, d, BLOCK - n % BLOCK), kdt)
 
     # the step's own token (ctx-1): poisoned in the pool, delivered by the append
     appending = [b for b in range(B) if spec.append and ctx[b] > 0]
@@ -321,13 +345,13 @@ def build(spec: Spec, seed: Optional[int] = None) -> Workload:
         pos = int(ctx[b]) - 1
         p = int(tables[b, pos // BLOCK])
         i = pos_of[p]
-        k_live[i, :, pos % BLOCK, :] = _poison((hkv, d), dt)
-        v_live[i, :, :, pos % BLOCK] = _poison((hkv, d), dt)
+        k_live[i, :, pos % BLOCK, :] = _poison((hkv, d), kdt)
+        v_live[i, :, :, pos % BLOCK] = _poison((hkv, d), kdt)
         slots[j] = p * BLOCK + pos % BLOCK
 
     scale = np.float32(1.0 / math.sqrt(d))
-    return Workload(spec, dt, q, n_pool, live.astype(np.int64), k_live, v_live, k_new, v_new,
-                    slots, tables, ctx.astype(np.int32), scale, poison_block)
+    return Workload(spec, dt, kdt, ks, vsc, q, n_pool, live.astype(np.int64), k_live, v_live,
+                    k_new, v_new, slots, tables, ctx.astype(np.int32), scale, poison_block)
 
 
 # ----------------------------------------------------------------- named configs
@@ -347,6 +371,7 @@ def config_spec(i: int) -> Spec:
       pool where a random 30% of blocks is free and the rest belongs to other requests.
     5 long + shared prefix bf16: 4 seqs x 32768 and 8 beams x 2304 that share their first
       2048 tokens (128 physical blocks), 64/8 heads, d 128.
+    6 config 3 with an FP8 E4M3 KV cache (k_scale 0.0117, v_scale 0.0093), bf16 q/out.
     """
     if i == 1:
         return Spec("tiny_fp32", "f32", 4, 1, 64, [37], sigma=1.0, seed=1, exact_pool=8)
@@ -364,6 +389,10 @@ def config_spec(i: int) -> Spec:
                     [32768] * 4 + [2304] * 8, seed=5, spare_blocks=12,
                     max_blocks_per_seq=2048,
                     prefix_groups=[(list(range(4, 12)), 128)])
+    if i == 6:
+        # config 3's shape with an FP8 E4M3 KV cache (per-tensor scales), bf16 q/out
+        return Spec("llama70b_gqa_fp8kv", "bf16", 64, 8, 128, [4096] * 32, seed=3,
+                    spare_blocks=32, kv_dtype="fp8", k_scale=0.0117, v_scale=0.0093)
     raise ValueError(f"no config {i}")
 
 

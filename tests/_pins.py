@@ -24,7 +24,21 @@ def to_f64(a, dtype):
     """The tests' own widening (independent of the oracle's)."""
     if dtype == "bf16":
         return (a.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    if dtype == "fp8":
+        t = torch.from_numpy(np.ascontiguousarray(a)).view(torch.float8_e4m3fn)
+        return t.to(torch.float64).numpy()
     return a.astype(np.float64)
+
+
+def kv_f64(w, K, V):
+    """Logical K, V as values: stored element widened, times the pool's scales."""
+    return to_f64(K, w.kv_dtype) * float(w.k_scale), to_f64(V, w.kv_dtype) * float(w.v_scale)
+
+
+def oracle_paged(w, kp, vp, tables=None, lib=None, **kw):
+    return O.decode_paged(w.q, kp, vp, w.kv_dtype, w.block_tables if tables is None else tables,
+                          w.context_lens, w.scale, lib=lib, q_dtype=w.dtype, k_scale=w.k_scale,
+                          v_scale=w.v_scale, **kw)
 
 
 def small_specs():
@@ -34,13 +48,18 @@ def small_specs():
         W.Spec("pin_bf16_gqa", "bf16", 8, 2, 32, [1, 17, 45], seed=11, spare_blocks=2),
         W.Spec("pin_f16_gqa", "f16", 6, 3, 16, [33, 5], seed=12, spare_blocks=1),
         W.Spec("pin_f32_mha", "f32", 2, 2, 8, [16, 31, 0], seed=13, spare_blocks=1),
+        W.Spec("pin_fp8_gqa", "bf16", 8, 2, 32, [1, 30, 47], seed=14, spare_blocks=1,
+               kv_dtype="fp8", k_scale=0.0117, v_scale=0.0093),
+        W.Spec("pin_fp8_f16", "f16", 4, 1, 16, [20], seed=15, spare_blocks=1,
+               kv_dtype="fp8", k_scale=0.25, v_scale=0.0625),
     ]
 
 
 def appended(w, lib):
     """Full host pools after the oracle's append of the step's rows."""
     kp, vp = w.host_pools()
-    return O.cache_append(kp, vp, w.k_new, w.v_new, w.slot_mapping, w.dtype, lib=lib)
+    return O.cache_append(kp, vp, w.k_new, w.v_new, w.slot_mapping, w.kv_dtype, lib=lib,
+                          act_dtype=w.dtype, k_scale=w.k_scale, v_scale=w.v_scale)
 
 
 def gather_contig(w, k_pool, v_pool):
@@ -60,9 +79,8 @@ def gather_contig(w, k_pool, v_pool):
 
 def brute_force(w, K, V):
     """Pure-Python loops with math.exp and math.fsum over the gathered cache."""
-    dt = w.dtype
-    q = to_f64(w.q, dt)
-    Kf, Vf = to_f64(K, dt), to_f64(V, dt)
+    q = to_f64(w.q, w.dtype)
+    Kf, Vf = kv_f64(w, K, V)
     scale = float(w.scale)
     G = w.num_q_heads // w.num_kv_heads
     out = np.zeros(q.shape, np.float64)
@@ -85,10 +103,9 @@ def brute_force(w, K, V):
 
 def torch_sdpa(w, K, V):
     """torch CPU float64 scaled_dot_product_attention, kv heads repeated per group."""
-    dt = w.dtype
     G = w.num_q_heads // w.num_kv_heads
-    q = torch.from_numpy(to_f64(w.q, dt))
-    Kf, Vf = torch.from_numpy(to_f64(K, dt)), torch.from_numpy(to_f64(V, dt))
+    q = torch.from_numpy(to_f64(w.q, w.dtype))
+    Kf, Vf = (torch.from_numpy(x) for x in kv_f64(w, K, V))
     out = torch.zeros(q.shape, dtype=torch.float64)
     for b in range(w.num_seqs):
         n = int(w.context_lens[b])
@@ -122,15 +139,55 @@ def check_widen_bf16(lib):
     assert np.array_equal(got[ok], ref[ok]), "bf16 widening differs from torch"
 
 
+def check_widen_fp8(lib):
+    codes = np.arange(256, dtype=np.uint8)
+    got = O.widen(codes, "fp8", lib=lib)
+    ref = to_f64(codes, "fp8")
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    assert np.isnan(got[[0x7F, 0xFF]]).all() and np.isnan(got).sum() == 2
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok]), "E4M3 widening differs from torch"
+    assert got[0x7E] == 448.0 and got[0x01] == 2.0 ** -9 and got[0x08] == 2.0 ** -6
+
+
+def _e4m3_torch(x):
+    """torch's E4M3 rounding (nearest, ties to even) after clamping to +-448."""
+    t = torch.from_numpy(np.ascontiguousarray(x, np.float32)).clamp(-448.0, 448.0)
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def check_encode_fp8(lib):
+    rng = np.random.Generator(np.random.PCG64(41))
+    # log-uniform magnitudes from deep subnormal to past the range, both signs
+    mag = np.exp2(rng.uniform(-14, 10, 200000)).astype(np.float32)
+    x = np.where(rng.random(mag.size) < 0.5, -mag, mag).astype(np.float32)
+    # every exact tie between neighbouring codes, and the codes themselves
+    vals = to_f64(np.arange(256, dtype=np.uint8), "fp8")
+    fin = np.sort(np.unique(vals[np.isfinite(vals)]))
+    ties = ((fin[:-1] + fin[1:]) / 2).astype(np.float32)
+    x = np.concatenate([x, ties, fin.astype(np.float32), np.float32([0.0, -0.0])])
+    got = O.encode_e4m3(x, lib=lib)
+    assert np.array_equal(got, _e4m3_torch(x))
+    # saturation and NaN (the quantiser's own rule; torch would give NaN past 448)
+    special = np.float32([448.0, 464.0, 1e6, np.inf, -500.0, -np.inf, np.nan, -np.nan])
+    assert O.encode_e4m3(special, lib=lib).tolist() == [0x7E, 0x7E, 0x7E, 0x7E, 0xFE, 0xFE,
+                                                        0x7F, 0xFF]
+
+
 def check_append(lib):
     for spec in small_specs():
         w = W.build(spec)
         k2, v2 = appended(w, lib)
         kref, vref = w.host_pools()
+        if w.kv_dtype == "fp8":       # codes of x / scale, the quotient in float32
+            kn = _e4m3_torch(to_f64(w.k_new, w.dtype).astype(np.float32) / w.k_scale)
+            vn = _e4m3_torch(to_f64(w.v_new, w.dtype).astype(np.float32) / w.v_scale)
+        else:
+            kn, vn = w.k_new, w.v_new
         for i, s in enumerate(w.slot_mapping.tolist()):
             if s >= 0:
-                kref[s // BLOCK, :, s % BLOCK, :] = w.k_new[i]
-                vref[s // BLOCK, :, :, s % BLOCK] = w.v_new[i]
+                kref[s // BLOCK, :, s % BLOCK, :] = kn[i]
+                vref[s // BLOCK, :, :, s % BLOCK] = vn[i]
         assert k2.view(np.uint8).tobytes() == kref.view(np.uint8).tobytes()
         assert v2.view(np.uint8).tobytes() == vref.view(np.uint8).tobytes()
     # negative slots write nothing
@@ -146,8 +203,7 @@ def check_bruteforce(lib):
     for spec in small_specs():
         w = W.build(spec)
         kp, vp = appended(w, lib)
-        out, _ = O.decode_paged(w.q, kp, vp, w.dtype, w.block_tables, w.context_lens, w.scale,
-                                lib=lib)
+        out, _ = oracle_paged(w, kp, vp, lib=lib)
         K, V = gather_contig(w, kp, vp)
         bf = brute_force(w, K, V)
         assert np.isfinite(out).all()
@@ -162,7 +218,8 @@ def check_permutation(lib):
         w = W.build(spec)
         kp, vp = appended(w, lib)
         K, V = gather_contig(w, kp, vp)
-        ref, _ = O.decode_contig(w.q, K, V, w.dtype, w.context_lens, w.scale, lib=lib)
+        ref, _ = O.decode_contig(w.q, K, V, w.kv_dtype, w.context_lens, w.scale, lib=lib,
+                                 q_dtype=w.dtype, k_scale=w.k_scale, v_scale=w.v_scale)
         for _ in range(3):
             perm = rng.permutation(w.num_blocks)
             kq = np.empty_like(kp)
@@ -170,8 +227,7 @@ def check_permutation(lib):
             kq[perm] = kp
             vq[perm] = vp
             tables = perm[w.block_tables].astype(np.int32)
-            out, _ = O.decode_paged(w.q, kq, vq, w.dtype, tables, w.context_lens, w.scale,
-                                    lib=lib)
+            out, _ = oracle_paged(w, kq, vq, tables=tables, lib=lib)
             assert out.tobytes() == ref.tobytes(), spec.name
 
 
@@ -179,8 +235,7 @@ def check_weight_sum(lib):
     for spec in small_specs():
         w = W.build(spec)
         kp, vp = appended(w, lib)
-        _, ws = O.decode_paged(w.q, kp, vp, w.dtype, w.block_tables, w.context_lens, w.scale,
-                               lib=lib)
+        _, ws = oracle_paged(w, kp, vp, lib=lib)
         for b in range(w.num_seqs):
             if w.context_lens[b] == 0:
                 assert (ws[b] == 0).all()
@@ -344,6 +399,7 @@ def check_block_table_example(lib):
     assert out.tobytes() == ref.tobytes()
 
 
-ALL_CHECKS = [check_widen_f16, check_widen_bf16, check_append, check_bruteforce,
+ALL_CHECKS = [check_widen_f16, check_widen_bf16, check_widen_fp8, check_encode_fp8,
+              check_append, check_bruteforce,
               check_permutation, check_weight_sum, check_closed_forms, check_split_combine,
               check_kv_size, check_block_table_example]

@@ -4,8 +4,9 @@ import torch
 
 from paged_kv_cache_161_amd import workloads as W
 
-TORCH_DTYPE = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
-NAN_INT = {"f32": 0x7FC00000, "f16": 0x7E00, "bf16": 0x7FC0}
+TORCH_DTYPE = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16,
+               "fp8": torch.uint8}
+NAN_INT = {"f32": 0x7FC00000, "f16": 0x7E00, "bf16": 0x7FC0, "fp8": 0x7F}
 
 
 def to_dev(arr, dtype=None, device="cuda"):
@@ -17,11 +18,15 @@ def to_dev(arr, dtype=None, device="cuda"):
 
 
 def from_dev(t, dtype):
-    """torch tensor -> numpy storage array (bf16 as uint16 bits)."""
+    """torch tensor -> numpy storage array (bf16 as uint16 bits, fp8 as uint8 codes)."""
     t = t.detach().cpu().contiguous()
     if dtype == "bf16":
         return t.view(torch.int16).numpy().view(np.uint16)
     return t.numpy()
+
+
+def scales(w):
+    return dict(k_scale=float(w.k_scale), v_scale=float(w.v_scale))
 
 
 def widen(a, dtype):
@@ -31,21 +36,23 @@ def widen(a, dtype):
 
 
 def int_view(t):
+    if t.dtype == torch.uint8:
+        return t
     return t.view(torch.int32) if t.dtype == torch.float32 else t.view(torch.int16)
 
 
 def device_pools(w: W.Workload, device="cuda"):
     """Full poisoned pools on the device with the workload's live blocks scattered in."""
     ks, vs = w.pool_shapes()
-    dt = TORCH_DTYPE[w.dtype]
+    dt = TORCH_DTYPE[w.kv_dtype]
     kp = torch.empty(ks, dtype=dt, device=device)
     vp = torch.empty(vs, dtype=dt, device=device)
-    int_view(kp).fill_(NAN_INT[w.dtype] if w.dtype != "f32" else NAN_INT["f32"])
-    int_view(vp).fill_(NAN_INT[w.dtype] if w.dtype != "f32" else NAN_INT["f32"])
+    int_view(kp).fill_(NAN_INT[w.kv_dtype])
+    int_view(vp).fill_(NAN_INT[w.kv_dtype])
     if w.live_blocks.size:
         idx = torch.from_numpy(w.live_blocks).to(device)
-        kp[idx] = to_dev(w.k_live[:-1], w.dtype, device)
-        vp[idx] = to_dev(w.v_live[:-1], w.dtype, device)
+        kp[idx] = to_dev(w.k_live[:-1], w.kv_dtype, device)
+        vp[idx] = to_dev(w.v_live[:-1], w.kv_dtype, device)
     return kp, vp
 
 

@@ -38,6 +38,7 @@ def test_pool_bytes(lib):
     assert lib.pa_pool_bytes(8, 1, 256, B.PA_F32) == 0       # fp32 stops at 128
     assert lib.pa_pool_bytes(0, 1, 64, B.PA_F16) == 0
     assert lib.pa_pool_bytes(8, 1, 64, 7) == 0
+    assert lib.pa_pool_bytes(8224, 8, 128, B.PA_FP8_E4M3) == 8224 * 8 * 16 * 128
 
 
 def test_status_strings(lib):
@@ -48,8 +49,10 @@ def test_status_strings(lib):
 
 def _pool(**kw):
     base = dict(k_pool=0x1000, v_pool=0x2000, num_blocks=64, block_size=16, num_kv_heads=2,
-                head_dim=128, dtype=B.PA_BF16)
+                head_dim=128, dtype=B.PA_BF16, act_dtype=None, k_scale=1.0, v_scale=1.0)
     base.update(kw)
+    if base["act_dtype"] is None:
+        base["act_dtype"] = base["dtype"] if base["dtype"] != B.PA_FP8_E4M3 else B.PA_BF16
     return B.PaKvPool(**base)
 
 
@@ -69,6 +72,13 @@ def test_decode_rejects_bad_arguments(lib):
     assert _decode(lib, _pool(block_size=8)) == unsup
     assert _decode(lib, _pool(head_dim=96)) == unsup
     assert _decode(lib, _pool(dtype=9)) == unsup
+    assert _decode(lib, _pool(act_dtype=B.PA_F16)) == unsup     # bf16 pool, f16 q
+    fp8 = dict(dtype=B.PA_FP8_E4M3, act_dtype=B.PA_BF16, k_scale=0.01, v_scale=0.02)
+    assert _decode(lib, _pool(**{**fp8, "act_dtype": B.PA_F32})) == unsup
+    assert _decode(lib, _pool(**{**fp8, "k_scale": 0.0})) == inval
+    assert _decode(lib, _pool(**{**fp8, "v_scale": float("inf")})) == inval
+    assert _decode(lib, _pool(**{**fp8, "v_scale": -1.0})) == inval
+    assert _decode(lib, _pool(**fp8), hq=3) == inval
     assert _decode(lib, _pool(num_blocks=0)) == inval
     assert _decode(lib, _pool(), hq=3) == inval                 # 3 % 2 != 0
     assert _decode(lib, _pool(), num_seqs=-1) == inval

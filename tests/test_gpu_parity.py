@@ -45,8 +45,10 @@ def config(i):
 def oracle_decode(w):
     """Oracle result for the workload: append then attend, over the relabelled pool."""
     kp, vp, bt, sl = w.oracle_view()
-    kp, vp = O.cache_append(kp, vp, w.k_new, w.v_new, sl, w.dtype)
-    out, _ = O.decode_paged(w.q, kp, vp, w.dtype, bt, w.context_lens, w.scale)
+    kp, vp = O.cache_append(kp, vp, w.k_new, w.v_new, sl, w.kv_dtype, act_dtype=w.dtype,
+                            k_scale=w.k_scale, v_scale=w.v_scale)
+    out, _ = O.decode_paged(w.q, kp, vp, w.kv_dtype, bt, w.context_lens, w.scale,
+                            q_dtype=w.dtype, k_scale=w.k_scale, v_scale=w.v_scale)
     return out
 
 
@@ -54,9 +56,9 @@ def gpu_step(w, partition_tokens=0, pools=None):
     """Append then decode on the GPU; returns (out fp64, k_pool, v_pool)."""
     kp, vp = pools if pools is not None else U.device_pools(w)
     d = U.device_inputs(w)
-    PA.cache_append(kp, vp, d["k_new"], d["v_new"], d["slot_mapping"])
+    PA.cache_append(kp, vp, d["k_new"], d["v_new"], d["slot_mapping"], **U.scales(w))
     out = PA.decode(d["q"], kp, vp, d["block_tables"], d["context_lens"], float(w.scale),
-                    w.max_context_len, partition_tokens)
+                    w.max_context_len, partition_tokens, **U.scales(w))
     torch.cuda.synchronize()
     return U.widen(U.from_dev(out, w.dtype), w.dtype), kp, vp
 
@@ -79,6 +81,15 @@ SMALL = [
     W.Spec("f32_g2_d128", "f32", 4, 2, 128, [65, 16], seed=107, spare_blocks=1),
     W.Spec("bf16_g5_d128", "bf16", 10, 2, 128, [190, 3, 0, 512], seed=108, spare_blocks=1),
     W.Spec("bf16_empty_batch_rows", "bf16", 8, 8, 128, [0, 0, 5], seed=109, spare_blocks=1),
+    # FP8 E4M3 pools with per-tensor scales, bf16 / f16 activations
+    W.Spec("fp8_bf16_g8_d128", "bf16", 16, 2, 128, [1, 15, 16, 17, 100, 257], seed=111,
+           spare_blocks=3, kv_dtype="fp8", k_scale=0.0117, v_scale=0.0093),
+    W.Spec("fp8_f16_g4_d64", "f16", 8, 2, 64, [40, 1, 96, 0], seed=112, spare_blocks=1,
+           kv_dtype="fp8", k_scale=0.02, v_scale=0.004),
+    W.Spec("fp8_bf16_g16_d256", "bf16", 32, 2, 256, [300, 7], seed=113, spare_blocks=1,
+           kv_dtype="fp8", k_scale=0.0125, v_scale=0.0125),
+    W.Spec("fp8_f16_g1_d128", "f16", 4, 4, 128, [33, 64, 5], seed=114, spare_blocks=2,
+           kv_dtype="fp8", k_scale=0.008, v_scale=0.011),
     # more sequences than the longest-first ordering handles (it covers <= 256)
     W.Spec("bf16_300_ragged_seqs", "bf16", 8, 2, 128,
            [int(x) for x in np.random.Generator(np.random.PCG64(110)).integers(0, 70, 300)],
@@ -98,7 +109,7 @@ def test_decode_small(spec, ptok):
     assert (got[zero] == 0).all()
 
 
-@pytest.mark.parametrize("i", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("i", [1, 2, 3, 4, 5, 6])
 def test_append_bit_exact(i):
     """The whole pool after the GPU append equals the oracle's append, byte for byte."""
     w = config(i)
@@ -106,7 +117,7 @@ def test_append_bit_exact(i):
     kp, vp = U.device_pools(w)
     k0, v0 = kp.clone(), vp.clone()
     d = U.device_inputs(w)
-    PA.cache_append(kp, vp, d["k_new"], d["v_new"], d["slot_mapping"])
+    PA.cache_append(kp, vp, d["k_new"], d["v_new"], d["slot_mapping"], **U.scales(w))
     torch.cuda.synchronize()
     touched = np.unique(w.slot_mapping[w.slot_mapping >= 0] // BLOCK)
     # expected touched blocks: the oracle's append on just those blocks
@@ -115,10 +126,11 @@ def test_append_bit_exact(i):
     local = {int(p): j for j, p in enumerate(touched)}
     slots = np.array([local[int(s) // BLOCK] * BLOCK + int(s) % BLOCK if s >= 0 else -1
                       for s in w.slot_mapping], np.int32)
-    ke, ve = O.cache_append(ke, ve, w.k_new, w.v_new, slots, w.dtype, inplace=True)
+    ke, ve = O.cache_append(ke, ve, w.k_new, w.v_new, slots, w.kv_dtype, inplace=True,
+                            act_dtype=w.dtype, k_scale=w.k_scale, v_scale=w.v_scale)
     tdev = torch.from_numpy(touched).cuda()
-    assert U.from_dev(kp[tdev], w.dtype).tobytes() == ke.tobytes()
-    assert U.from_dev(vp[tdev], w.dtype).tobytes() == ve.tobytes()
+    assert U.from_dev(kp[tdev], w.kv_dtype).tobytes() == ke.tobytes()
+    assert U.from_dev(vp[tdev], w.kv_dtype).tobytes() == ve.tobytes()
     # every other byte of both pools is unchanged
     kp[tdev] = k0[tdev]
     vp[tdev] = v0[tdev]
@@ -139,7 +151,7 @@ def test_append_skips_padding_and_out_of_pool_slots():
     assert torch.equal(U.int_view(vp), U.int_view(v0))
 
 
-@pytest.mark.parametrize("i", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("i", [1, 2, 3, 4, 5, 6])
 def test_decode_config(i):
     w = config(i)
     say(f"[decode] config {i} {w.spec.name} B={w.num_seqs} Hq={w.num_q_heads} "
@@ -160,25 +172,27 @@ def test_decode_config3_forced_partitions(ptok):
     check(w, got, ref, f"config 3 p{ptok}")
 
 
-def _probe_workload(dtype, d, ctx, hkv=2, group=4):
+def _probe_workload(dtype, d, ctx, hkv=2, group=4, kv_dtype=None):
     """One sequence per target position j: q = 1, keys 0 except key j = 16, and value
-    rows holding small integers that name (physical block mod 256, row, kv-head)."""
+    rows holding small integers that name (physical block mod 256, row, kv-head);
+    mod 16 for fp8 pools, where only integers up to 16 are all exact."""
     B = ctx
+    kdt = kv_dtype or dtype
     spec = W.Spec(f"probe_{dtype}_{d}", dtype, hkv * group, hkv, d, [ctx] * B, seed=7,
-                  spare_blocks=1, append=False)
+                  spare_blocks=1, append=False, kv_dtype=kv_dtype)
     w = W.build(spec)
     one = W.round_to_storage(np.array([1.0], np.float32), dtype)[0]
-    sixteen = W.round_to_storage(np.array([16.0], np.float32), dtype)[0]
-    zero = np.zeros(1, W.STORAGE[dtype])[0]
+    sixteen = W.round_to_storage(np.array([16.0], np.float32), kdt)[0]
+    zero = np.zeros(1, W.STORAGE[kdt])[0]
     w.q[...] = one
     live = w.k_live[:-1]
     vl = w.v_live[:-1]
     live[...] = zero
     codes = np.zeros(vl.shape, np.float32)                 # [n][hkv][d][16]
-    codes[:, :, 0, :] = (w.live_blocks % 256)[:, None, None]
+    codes[:, :, 0, :] = (w.live_blocks % (16 if kdt == "fp8" else 256))[:, None, None]
     codes[:, :, 1, :] = np.arange(BLOCK)[None, None, :]
     codes[:, :, 2, :] = np.arange(hkv)[None, :, None]
-    vl[...] = W.round_to_storage(codes.reshape(-1), dtype).reshape(vl.shape)
+    vl[...] = W.round_to_storage(codes.reshape(-1), kdt).reshape(vl.shape)
     for b in range(B):
         j = b
         p = int(w.block_tables[b, j // BLOCK])
@@ -189,28 +203,33 @@ def _probe_workload(dtype, d, ctx, hkv=2, group=4):
         for b in range(B):
             p = int(w.block_tables[b, ctx // BLOCK])
             i = int(np.searchsorted(w.live_blocks, p))
-            nanv = W._poison((hkv, BLOCK - ctx % BLOCK, d), dtype)
+            nanv = W._poison((hkv, BLOCK - ctx % BLOCK, d), kdt)
             live[i, :, ctx % BLOCK:, :] = nanv
             vl[i, :, :, ctx % BLOCK:] = nanv.transpose(0, 2, 1)
     return w
 
 
-@pytest.mark.parametrize("dtype,d,ctx,ptok", [("bf16", 128, 45, 0), ("f16", 128, 45, 0),
-                                              ("f32", 64, 45, 0), ("bf16", 128, 300, 32),
-                                              ("bf16", 64, 33, 16)])
-def test_gather_probe(dtype, d, ctx, ptok):
+@pytest.mark.parametrize("dtype,d,ctx,ptok,kv", [("bf16", 128, 45, 0, None),
+                                                 ("f16", 128, 45, 0, None),
+                                                 ("f32", 64, 45, 0, None),
+                                                 ("bf16", 128, 300, 32, None),
+                                                 ("bf16", 64, 33, 16, None),
+                                                 ("bf16", 128, 45, 0, "fp8"),
+                                                 ("f16", 64, 40, 16, "fp8")])
+def test_gather_probe(dtype, d, ctx, ptok, kv):
     """Each output must be exactly the value row of the one selected token: proves which
     physical (block, row, kv-head) the kernel read for every logical position."""
-    w = _probe_workload(dtype, d, ctx)
-    say(f"[probe] {dtype} d={d} ctx={ctx} partition_tokens={ptok}")
+    w = _probe_workload(dtype, d, ctx, kv_dtype=kv)
+    say(f"[probe] {dtype}/{kv or dtype} d={d} ctx={ctx} partition_tokens={ptok}")
     got, _, _ = gpu_step(w, ptok)
     G = w.num_q_heads // w.num_kv_heads
+    mod = 16 if kv == "fp8" else 256
     for b in range(w.num_seqs):
         j = b
         p = int(w.block_tables[b, j // BLOCK])
         for h in range(w.num_q_heads):
             want = np.zeros(d)
-            want[:3] = [p % 256, j % BLOCK, h // G]
+            want[:3] = [p % mod, j % BLOCK, h // G]
             assert np.array_equal(got[b, h], want), (b, h, got[b, h, :4], want[:4])
 
 
@@ -223,7 +242,7 @@ def test_bad_table_entry_and_context_give_nan_not_fault():
     cl = d["context_lens"].clone()
     cl[5] = w.max_context_len + 1         # beyond the host bound
     cl[0] = -3
-    PA.cache_append(kp, vp, d["k_new"], d["v_new"], d["slot_mapping"])
+    PA.cache_append(kp, vp, d["k_new"], d["v_new"], d["slot_mapping"], **U.scales(w))
     out = PA.decode(d["q"], kp, vp, bt, cl, float(w.scale), w.max_context_len)
     torch.cuda.synchronize()
     got = U.widen(U.from_dev(out, w.dtype), w.dtype)
@@ -255,11 +274,13 @@ def test_split_workspace_reuse_and_garbage():
                 assert 0 < need <= ws.numel()
                 kp, vp = U.device_pools(w)
                 d = U.device_inputs(w)
-                PA.cache_append(kp, vp, d["k_new"], d["v_new"], d["slot_mapping"])
+                PA.cache_append(kp, vp, d["k_new"], d["v_new"], d["slot_mapping"],
+                                **U.scales(w))
                 out = PA.decode(d["q"], kp, vp, d["block_tables"], d["context_lens"],
-                                float(w.scale), w.max_context_len, ptok, workspace=ws)
+                                float(w.scale), w.max_context_len, ptok, workspace=ws,
+                                **U.scales(w))
                 ref_out = PA.decode(d["q"], kp, vp, d["block_tables"], d["context_lens"],
-                                    float(w.scale), w.max_context_len, 0)
+                                    float(w.scale), w.max_context_len, 0, **U.scales(w))
                 torch.cuda.synchronize()
                 got = U.widen(U.from_dev(out, w.dtype), w.dtype)
                 ref = oracle_decode(w)

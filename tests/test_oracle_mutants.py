@@ -37,6 +37,16 @@ MUTANTS = {
     "kv_size_factor_dropped": ("return 2ull * layers * kv_heads", "return layers * kv_heads"),
     "max_over_first_token_only": ("if (J->scores[t] > m)", "if (t == 0)"),
     "weight_sum_unnormalised": ("s += J->scores[t] / z;", "s += J->scores[t];"),
+    "e4m3_exponent_bias": ("v = ldexp((double)(frac | 0x8), expo - 10);",
+                           "v = ldexp((double)(frac | 0x8), expo - 9);"),
+    "e4m3_subnormal_step": ("v = ldexp((double)frac, -9);", "v = ldexp((double)frac, -8);"),
+    "e4m3_encode_truncates": ("float steps = rintf(ldexpf(a, 3 - k));",
+                              "float steps = floorf(ldexpf(a, 3 - k));"),
+    "e4m3_encode_no_saturation": ("if (a >= 448.0f)\n        return sign | 0x7e;",
+                                  "if (a >= 448.0f)\n        return sign | 0x7f;"),
+    "fp8_k_scale_dropped": ("return widen_at(P->k_pool, idx, P->dtype) * P->k_scale;",
+                            "return widen_at(P->k_pool, idx, P->dtype);"),
+    "fp8_append_scale_multiplied": ("encode_e4m3(vx / v_scale)", "encode_e4m3(vx * v_scale)"),
 }
 
 
