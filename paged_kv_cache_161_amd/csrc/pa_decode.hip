@@ -146,22 +146,39 @@ struct Q32 {
 // FP8 (OCP E4M3) K/V with 16-bit q.  The same lane roles as the 16-bit tiles, with
 // half the bytes: each code converts exactly to the 16-bit MFMA type in registers
 // (every E4M3 value is a bf16 and an f16 value), the per-tensor scales are applied
-// in fp32 outside the MFMAs.
+// in fp32 outside the MFMAs.  A lane loads K in 16-byte pieces (16 codes, two MFMAs'
+// worth): chunk c = 4j + g of its row, so one load instruction covers 64 contiguous
+// bytes of each of the 16 rows, as the 16-bit tile does.  MFMA i = 2j + h uses codes
+// 8h .. 8h+7 of piece j, and the q fragments follow the same e mapping.
 template <int AT, int D>
 struct Tile8 {
-    static constexpr int NQK = D / 32;
+    static constexpr int NKL = D / 64;   // 16-byte K pieces per lane
     static constexpr int NPV = D / 16;
-    u32x2 k[NQK];                        // 8 codes of K[r][32i + 8g .. +7]
+    u32x4 k[NKL];                        // 16 codes of K[r][64j + 16g .. +15]
     uint32_t v[NPV];                     // 4 codes of V^T[16n + r][4g .. 4g+3]
 
     __device__ __forceinline__ void load(const uint8_t *kt, const uint8_t *vt, int r, int g)
     {
 #pragma unroll
-        for (int i = 0; i < NQK; ++i)
-            k[i] = *reinterpret_cast<const u32x2 *>(kt + r * D + 32 * i + 8 * g);
+        for (int j = 0; j < NKL; ++j)
+            k[j] = *reinterpret_cast<const u32x4 *>(kt + r * D + 64 * j + 16 * g);
 #pragma unroll
         for (int n = 0; n < NPV; ++n)
             v[n] = *reinterpret_cast<const uint32_t *>(vt + (16 * n + r) * kBlock + 4 * g);
+    }
+};
+
+// q fragments in the fp8 tile's e mapping: f[2j + h] = Q[r][64j + 16g + 8h .. +7].
+template <int AT, int D>
+struct Q8 {
+    u32x4 f[D / 32];
+    __device__ __forceinline__ void load(const uint16_t *qrow, bool valid, int g)
+    {
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i)
+            f[i] = valid ? *reinterpret_cast<const u32x4 *>(qrow + 64 * (i / 2) + 16 * g +
+                                                            8 * (i % 2))
+                         : u32x4{0u, 0u, 0u, 0u};
     }
 };
 
@@ -191,7 +208,7 @@ template <int D> struct Frags<DT_F32, DT_F32, D> {
 };
 template <int AT, int D> struct Frags<DT_FP8, AT, D> {
     using Tile = Tile8<AT, D>;
-    using Q = Q16<AT, D>;
+    using Q = Q8<AT, D>;
     using Elem = uint8_t;
     using QElem = uint16_t;
 };
@@ -249,10 +266,14 @@ __device__ __forceinline__ f32x4 scores(const typename Frags<DT, AT, D>::Tile &t
                 s = __builtin_amdgcn_mfma_f32_16x16x4f32(t.k[c][j], q.f[c][j], s, 0, 0, 0);
     } else if constexpr (DT == DT_FP8) {
 #pragma unroll
-        for (int i = 0; i < D / 32; ++i) {
-            const u32x4 kk = {e4m3x2_to_16<AT, false>(t.k[i][0]), e4m3x2_to_16<AT, true>(t.k[i][0]),
-                              e4m3x2_to_16<AT, false>(t.k[i][1]), e4m3x2_to_16<AT, true>(t.k[i][1])};
-            s = mfma_k32<AT>(kk, q.f[i], s);
+        for (int j = 0; j < D / 64; ++j) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const uint32_t w0 = t.k[j][2 * h], w1 = t.k[j][2 * h + 1];
+                const u32x4 kk = {e4m3x2_to_16<AT, false>(w0), e4m3x2_to_16<AT, true>(w0),
+                                  e4m3x2_to_16<AT, false>(w1), e4m3x2_to_16<AT, true>(w1)};
+                s = mfma_k32<AT>(kk, q.f[2 * j + h], s);
+            }
         }
     } else {
 #pragma unroll
@@ -461,19 +482,26 @@ __global__ __launch_bounds__(NW *kWave, min_waves_per_simd(DT, D, PF)) void pa_d
                 x[j] = (4 * g + j < valid) ? x[j] : -INFINITY;
             mask_tail_v<DT, AT, D>(t, valid, g);
         }
-        const float mx = wave_max_rows(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = fast_exp2(m_run - m_new);
+        // The running max of a head changes only if one of its 4 lanes sees a score
+        // above it; when no lane of the wave does, the rescale factor would be exactly
+        // 1, so the cross-row max, the exp2 and the rescale of O and l are skipped
+        // (bit-identical to doing them).  After the first blocks this is the usual case.
+        const float lmx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+        if (__any(lmx > m_run)) {
+            const float m_new = fmaxf(m_run, wave_max_rows(lmx));
+            const float alpha = fast_exp2(m_run - m_new);
+#pragma unroll
+            for (int n = 0; n < D / 16; ++n)
+                o[n] *= alpha;
+            l_run *= alpha;
+            m_run = m_new;
+        }
         f32x4 pw;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            pw[j] = fast_exp2(x[j] - m_new);
-#pragma unroll
-        for (int n = 0; n < D / 16; ++n)
-            o[n] *= alpha;
+            pw[j] = fast_exp2(x[j] - m_run);
         const f32x4 pu = accumulate_pv<DT, AT, D>(t, pw, o);
-        l_run = l_run * alpha + ((pu[0] + pu[1]) + (pu[2] + pu[3]));
-        m_run = m_new;
+        l_run += (pu[0] + pu[1]) + (pu[2] + pu[3]);
     };
 
     // Ring of PF + 1 tiles: block i + PF is loaded while block i is computed.  The
