@@ -192,6 +192,27 @@ def main():
         f"launches -> {achieved:.0f} GB/s")
     traffic = recorded_traffic(w.spec.name, ptok)
 
+    # the same step captured as one HIP graph per layer pool and replayed (the
+    # library enqueues only kernels, so the graphs hold exactly the eager launches)
+    graphs = []
+    cap = torch.cuda.Stream(dev)
+    cap.wait_stream(torch.cuda.current_stream(dev))
+    for i in range(LAYERS):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            step(i)
+        graphs.append(g)
+    torch.cuda.current_stream(dev).wait_stream(cap)
+    for i in range(args.warmup):
+        graphs[i % LAYERS].replay()
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        graphs[i % LAYERS].replay()
+    torch.cuda.synchronize()
+    graph_ms = (time.perf_counter() - t_start) * 1e3 / args.steps
+    log(f"[bench] {args.steps} graph-replayed steps: {graph_ms * 1e3:.1f} us/step")
+
     # parity on the timed inputs (sampled rows against the oracle)
     parity = None
     try:
@@ -245,6 +266,8 @@ def main():
         "tokens_per_s": round(tokens_per_s, 1),
         "context_tokens_per_s": round(float(w.context_lens.sum()) / (ms_per_step * 1e-3), 1),
         "kv_bytes_per_step": kv_bytes,
+        "graph_ms_per_step": round(graph_ms, 5),
+        "graph_tokens_per_s": round(w.num_seqs / (graph_ms * 1e-3), 1),
         "unique_kv_bytes_per_step": uniq_bytes,
         "roofline": {"bound": "hbm", "kernel": "pa_decode_partition (+ pa_decode_reduce when "
                                                "a sequence spans several partitions)",
