@@ -64,7 +64,8 @@ typedef enum pa_status {
     PA_ERR_INVALID_ARG = 1,   /* null pointer, negative size, inconsistent shapes      */
     PA_ERR_UNSUPPORTED = 2,   /* valid but not built: dtype, head_dim, block size     */
     PA_ERR_WORKSPACE = 3,     /* workspace pointer null or smaller than required      */
-    PA_ERR_HIP = 4            /* the HIP runtime reported an error at launch          */
+    PA_ERR_HIP = 4,           /* the HIP runtime reported an error at launch          */
+    PA_ERR_OUT_OF_BLOCKS = 5  /* the block allocator has too few free blocks           */
 } pa_status;
 
 typedef enum pa_dtype {
@@ -154,6 +155,76 @@ pa_status pa_decode(const pa_kv_pool *pool, const void *q, void *out, int32_t nu
                     int32_t max_blocks_per_seq, const int32_t *context_lens,
                     int32_t max_context_len, int32_t partition_tokens, void *workspace,
                     size_t workspace_bytes, void *stream);
+
+/* Copy whole physical blocks inside the pool: for each pair i, block pairs[2i] (src)
+ * is copied to block pairs[2i+1] (dst), every kv-head, in both K and V, bytes
+ * unchanged -- the copy half of copy-on-write (LLM-101-CN "推理优化", section
+ * "Copy-on-Write 优化": a shared block is copied only when one sharer modifies it).
+ *   pairs   [num_pairs][2] int32, device.  A pair with either id outside
+ *           [0, num_blocks) is skipped.  Destinations must be distinct and must not be
+ *           a source of another pair in the same call (caller error otherwise).
+ * num_pairs == 0 is a valid no-op. */
+pa_status pa_copy_blocks(const pa_kv_pool *pool, const int32_t *pairs, int32_t num_pairs,
+                         void *stream);
+
+/* ---------------------------------------------------------------- host block allocator
+ * Bookkeeping of which physical blocks are free, with reference counts so that blocks
+ * can be shared by several sequences (beam-search prefixes) and copied on first write
+ * (LLM-101-CN "推理优化", sections "物理块与逻辑块" (PageAllocator: a FIFO free
+ * pool, acquire takes from the front and fails as a whole when too few blocks are
+ * free, release returns blocks to the back) and "Copy-on-Write 优化" (blocks shared
+ * with a reference count > 1 are copied only when one sharer writes)).  Host memory
+ * only, no device access; one caller at a time per allocator.  Block tables passed
+ * here are host int32 rows of max_blocks entries; entries past a sequence's last
+ * block are set to -1.  Every call either succeeds completely or changes nothing. */
+typedef struct pa_block_allocator pa_block_allocator;
+
+/* A new allocator owning blocks 0 .. num_blocks-1, all free, in that order.  NULL on
+ * num_blocks <= 0 or allocation failure.  Free it with pa_allocator_destroy. */
+pa_block_allocator *pa_allocator_create(int32_t num_blocks);
+void pa_allocator_destroy(pa_block_allocator *alloc);
+
+int32_t pa_allocator_num_free(const pa_block_allocator *alloc);
+
+/* Reference count of a block: 0 when free, -1 for an id outside the pool. */
+int32_t pa_allocator_ref_count(const pa_block_allocator *alloc, int32_t block);
+
+/* Take count free blocks (front of the free pool first), each with reference count 1,
+ * into ids_out[0 .. count).  PA_ERR_OUT_OF_BLOCKS (nothing taken) when fewer are free. */
+pa_status pa_allocator_acquire(pa_block_allocator *alloc, int32_t count, int32_t *ids_out);
+
+/* Add one reference to each listed block (all must be in use). */
+pa_status pa_allocator_share(pa_block_allocator *alloc, const int32_t *ids, int32_t count);
+
+/* Drop one reference from each listed block (all must be in use); a block whose count
+ * reaches 0 goes to the back of the free pool, in list order. */
+pa_status pa_allocator_release(pa_block_allocator *alloc, const int32_t *ids, int32_t count);
+
+/* Reserve slots for num_new tokens appended to a sequence of context_len tokens whose
+ * blocks are table_row[0 .. ceil(context_len/16)).  Token context_len + i gets
+ * slots_out[i] = block * 16 + row, ready for pa_cache_append.  New blocks are acquired
+ * when the tokens cross block boundaries.  If the sequence's last block is partly
+ * filled and shared (reference count > 1), it is first replaced by a fresh block: the
+ * pair (old, new) is written to copy_pairs_out (room for one pair) for
+ * pa_copy_blocks, the old block loses this sequence's reference and table_row points
+ * at the new block.  *num_copies_out gets 0 or 1.  PA_ERR_OUT_OF_BLOCKS when the pool
+ * cannot supply the blocks; PA_ERR_INVALID_ARG when context_len + num_new exceeds
+ * max_blocks * 16. */
+pa_status pa_seq_reserve(pa_block_allocator *alloc, int32_t *table_row, int32_t max_blocks,
+                         int32_t context_len, int32_t num_new, int32_t *slots_out,
+                         int32_t *copy_pairs_out, int32_t *num_copies_out);
+
+/* A new sequence sharing every block of another (a beam fork): dst_row gets
+ * src_row's first ceil(context_len/16) entries, each block gains one reference, the
+ * rest of dst_row (max_blocks entries) is set to -1. */
+pa_status pa_seq_fork(pa_block_allocator *alloc, const int32_t *src_row, int32_t *dst_row,
+                      int32_t max_blocks, int32_t context_len);
+
+/* Shorten a sequence from context_len to new_len tokens (rolling back rejected
+ * speculative tokens, or freeing a finished sequence with new_len = 0): the blocks
+ * past ceil(new_len/16) lose this sequence's reference and their entries become -1. */
+pa_status pa_seq_truncate(pa_block_allocator *alloc, int32_t *table_row, int32_t max_blocks,
+                          int32_t context_len, int32_t new_len);
 
 /* Static, human-readable text for a status code. */
 const char *pa_status_string(int32_t status);

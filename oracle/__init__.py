@@ -55,6 +55,8 @@ def _bind(lib):
     lib.oracle_cache_append_ex.restype = I
     lib.oracle_encode_e4m3.argtypes = [P, ctypes.c_size_t, P]
     lib.oracle_encode_e4m3.restype = None
+    lib.oracle_copy_blocks.argtypes = [P, P, I, I, I, I, P, I]
+    lib.oracle_copy_blocks.restype = I
     lib.oracle_decode_contig.argtypes = [P, P, P, I, I, I, I, I, I, P, ctypes.c_float, P, P, I]
     lib.oracle_decode_contig.restype = I
     lib.oracle_decode_contig_ex.argtypes = [P, I, P, P, I, ctypes.c_double, ctypes.c_double, I,
@@ -177,4 +179,21 @@ def cache_append(k_pool, v_pool, k_new, v_new, slot_mapping, dtype, inplace=Fals
                                     _ptr(k_new), _ptr(v_new), _ptr(sm), sm.size)
     if rc:
         raise ValueError(f"oracle_cache_append returned {rc}")
+    return k_out, v_out
+
+
+def copy_blocks(k_pool, v_pool, pairs, dtype, inplace=False, lib=None):
+    """Copies of (k_pool, v_pool) (or the inputs, if inplace) with block src of each
+    (src, dst) pair copied to dst."""
+    lib = lib or load()
+    for a in (k_pool, v_pool):
+        _check(a, dtype)
+    k_out = k_pool if inplace else k_pool.copy()
+    v_out = v_pool if inplace else v_pool.copy()
+    nblk, hkv, _, d = k_pool.shape
+    pr = np.ascontiguousarray(pairs, np.int32).reshape(-1, 2)
+    rc = lib.oracle_copy_blocks(_ptr(k_out), _ptr(v_out), DTYPE_CODES[dtype], nblk, hkv, d,
+                                _ptr(pr), pr.shape[0])
+    if rc:
+        raise ValueError(f"oracle_copy_blocks returned {rc}")
     return k_out, v_out

@@ -490,3 +490,24 @@ int oracle_cache_append(void *k_pool, void *v_pool, int dtype, int num_blocks,
                                   num_kv_heads, head_dim, k_new, v_new, slot_mapping,
                                   num_tokens);
 }
+
+/* Copy-on-write's copy: for each pair, block src of both pools is copied to block dst
+ * as exact bytes (every kv-head; a block of a pool is Hkv * 16 * d elements).  Pairs
+ * with an id outside the pool are skipped.                                           */
+int oracle_copy_blocks(void *k_pool, void *v_pool, int dtype, int num_blocks, int num_kv_heads,
+                       int head_dim, const int32_t *pairs, int num_pairs)
+{
+    if (check_common(dtype, 1, num_kv_heads, num_kv_heads, head_dim) || num_pairs < 0)
+        return -1;
+    const size_t bytes = (size_t)num_kv_heads * ORACLE_BLOCK * head_dim * elem_bytes(dtype);
+    for (int i = 0; i < num_pairs; ++i) {
+        int32_t src = pairs[2 * i], dst = pairs[2 * i + 1];
+        if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks)
+            continue;
+        memmove((char *)k_pool + (size_t)dst * bytes, (const char *)k_pool + (size_t)src * bytes,
+                bytes);
+        memmove((char *)v_pool + (size_t)dst * bytes, (const char *)v_pool + (size_t)src * bytes,
+                bytes);
+    }
+    return 0;
+}

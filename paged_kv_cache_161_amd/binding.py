@@ -22,7 +22,7 @@ PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3 = 0, 1, 2, 3
 DTYPE_CODE = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}
 FP8_STORAGE = (torch.uint8, torch.float8_e4m3fn)   # tensors holding OCP E4M3 codes
 STATUS = {0: "PA_OK", 1: "PA_ERR_INVALID_ARG", 2: "PA_ERR_UNSUPPORTED", 3: "PA_ERR_WORKSPACE",
-          4: "PA_ERR_HIP"}
+          4: "PA_ERR_HIP", 5: "PA_ERR_OUT_OF_BLOCKS"}
 
 
 class PaError(RuntimeError):
@@ -65,6 +65,28 @@ def load(path: str = LIB_PATH):
     lib.pa_decode.restype = ctypes.c_int
     lib.pa_status_string.argtypes = [I32]
     lib.pa_status_string.restype = ctypes.c_char_p
+    lib.pa_copy_blocks.argtypes = [ctypes.POINTER(PaKvPool), P, I32, P]
+    lib.pa_copy_blocks.restype = ctypes.c_int
+    lib.pa_allocator_create.argtypes = [I32]
+    lib.pa_allocator_create.restype = P
+    lib.pa_allocator_destroy.argtypes = [P]
+    lib.pa_allocator_destroy.restype = None
+    lib.pa_allocator_num_free.argtypes = [P]
+    lib.pa_allocator_num_free.restype = I32
+    lib.pa_allocator_ref_count.argtypes = [P, I32]
+    lib.pa_allocator_ref_count.restype = I32
+    for name in ("pa_allocator_acquire",):
+        getattr(lib, name).argtypes = [P, I32, P]
+        getattr(lib, name).restype = ctypes.c_int
+    for name in ("pa_allocator_share", "pa_allocator_release"):
+        getattr(lib, name).argtypes = [P, P, I32]
+        getattr(lib, name).restype = ctypes.c_int
+    lib.pa_seq_reserve.argtypes = [P, P, I32, I32, I32, P, P, P]
+    lib.pa_seq_reserve.restype = ctypes.c_int
+    lib.pa_seq_fork.argtypes = [P, P, P, I32, I32]
+    lib.pa_seq_fork.restype = ctypes.c_int
+    lib.pa_seq_truncate.argtypes = [P, P, I32, I32, I32]
+    lib.pa_seq_truncate.restype = ctypes.c_int
     if path == LIB_PATH:
         _lib = lib
     return lib
@@ -189,3 +211,78 @@ def decode(q, k_pool, v_pool, block_tables, context_lens, scale: float, max_cont
                           _stream_handle(q.device))
     _raise(st)
     return out
+
+
+def copy_blocks(k_pool, v_pool, pairs: torch.Tensor) -> None:
+    """Copy block pairs[i, 0] to block pairs[i, 1] in both pools (pairs: device int32
+    [n][2]); the copy half of copy-on-write."""
+    pool = make_pool(k_pool, v_pool, torch.bfloat16 if k_pool.dtype in FP8_STORAGE else None)
+    n = int(pairs.numel() // 2)
+    st = load().pa_copy_blocks(ctypes.byref(pool), _dev_ptr(pairs, "pairs", torch.int32), n,
+                               _stream_handle(k_pool.device))
+    _raise(st)
+
+
+def _np_ptr(a):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+class BlockAllocator:
+    """Host block allocator of the C library (FIFO free pool, reference counts,
+    copy-on-write, rollback).  Block-table rows are numpy int32 arrays, updated in place."""
+
+    def __init__(self, num_blocks: int):
+        import numpy as np  # noqa: F401  (rows are numpy arrays)
+        self._lib = load()
+        self._h = self._lib.pa_allocator_create(num_blocks)
+        if not self._h:
+            raise PaError(1, "pa_allocator_create failed")
+        self.num_blocks = num_blocks
+
+    def __del__(self):
+        h, self._h = getattr(self, "_h", None), None
+        if h:
+            self._lib.pa_allocator_destroy(h)
+
+    @property
+    def num_free(self) -> int:
+        return int(self._lib.pa_allocator_num_free(self._h))
+
+    def ref_count(self, block: int) -> int:
+        return int(self._lib.pa_allocator_ref_count(self._h, block))
+
+    def acquire(self, count: int):
+        import numpy as np
+        ids = np.zeros(max(count, 1), np.int32)
+        _raise(self._lib.pa_allocator_acquire(self._h, count, _np_ptr(ids)))
+        return ids[:count].tolist()
+
+    def share(self, ids):
+        import numpy as np
+        a = np.ascontiguousarray(ids, np.int32)
+        _raise(self._lib.pa_allocator_share(self._h, _np_ptr(a), a.size))
+
+    def release(self, ids):
+        import numpy as np
+        a = np.ascontiguousarray(ids, np.int32)
+        _raise(self._lib.pa_allocator_release(self._h, _np_ptr(a), a.size))
+
+    def reserve(self, row, context_len: int, num_new: int):
+        """Slots for num_new tokens after context_len; returns (slots, copy_pairs)."""
+        import numpy as np
+        assert row.dtype == np.int32 and row.flags.c_contiguous
+        slots = np.zeros(max(num_new, 1), np.int32)
+        pairs = np.zeros(2, np.int32)
+        ncopy = ctypes.c_int32(0)
+        _raise(self._lib.pa_seq_reserve(self._h, _np_ptr(row), row.size, context_len, num_new,
+                                        _np_ptr(slots), _np_ptr(pairs), ctypes.byref(ncopy)))
+        return slots[:num_new], [tuple(pairs.tolist())] if ncopy.value else []
+
+    def fork(self, src_row, dst_row, context_len: int):
+        import numpy as np
+        assert src_row.dtype == np.int32 and dst_row.dtype == np.int32
+        _raise(self._lib.pa_seq_fork(self._h, _np_ptr(src_row), _np_ptr(dst_row), dst_row.size,
+                                     context_len))
+
+    def truncate(self, row, context_len: int, new_len: int):
+        _raise(self._lib.pa_seq_truncate(self._h, _np_ptr(row), row.size, context_len, new_len))

@@ -128,6 +128,7 @@ const char *pa_status_string(int32_t status)
     case PA_ERR_UNSUPPORTED: return "unsupported configuration";
     case PA_ERR_WORKSPACE: return "workspace missing or too small";
     case PA_ERR_HIP: return "HIP runtime error";
+    case PA_ERR_OUT_OF_BLOCKS: return "not enough free blocks";
     default: return "unknown status";
     }
 }
@@ -158,6 +159,26 @@ pa_status pa_cache_append(const pa_kv_pool *pool, const void *k_new, const void 
     a.bf16 = pool->act_dtype == PA_BF16 ? 1 : 0;
     hipError_t e = pa::launch_append(pool->dtype, pool->act_dtype, pool->head_dim, a,
                                      static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+pa_status pa_copy_blocks(const pa_kv_pool *pool, const int32_t *pairs, int32_t num_pairs,
+                         void *stream)
+{
+    pa_status st = check_pool(pool);
+    if (st != PA_OK)
+        return st;
+    if (num_pairs < 0)
+        return PA_ERR_INVALID_ARG;
+    if (num_pairs == 0)
+        return PA_OK;
+    if (!pairs || num_pairs > 65535)
+        return num_pairs > 65535 ? PA_ERR_UNSUPPORTED : PA_ERR_INVALID_ARG;
+    const size_t block_bytes =
+        (size_t)pool->num_kv_heads * kBlock * pool->head_dim * elem_bytes(pool->dtype);
+    hipError_t e = pa::launch_copy_blocks(pool->k_pool, pool->v_pool, pairs, num_pairs,
+                                          pool->num_blocks, block_bytes,
+                                          static_cast<hipStream_t>(stream));
     return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 

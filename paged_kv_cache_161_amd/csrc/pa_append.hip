@@ -136,7 +136,42 @@ hipError_t launch_append_t(const AppendArgs &a, hipStream_t stream)
     return hipGetLastError();
 }
 
+// Copies whole physical blocks (every kv-head of K and of V) for (src, dst) pairs: the
+// copy half of copy-on-write.  A block of either pool is one contiguous run of
+// block_bytes bytes; a thread moves one 16-byte unit of each pool.  Pairs with an id
+// outside the pool are skipped.
+__global__ __launch_bounds__(256) void pa_copy_blocks_kernel(void *k_pool, void *v_pool,
+                                                             const int32_t *pairs,
+                                                             int32_t num_blocks,
+                                                             size_t block_bytes)
+{
+    const int32_t src = pairs[2 * blockIdx.y];
+    const int32_t dst = pairs[2 * blockIdx.y + 1];
+    if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks)
+        return;
+    const size_t units = block_bytes / 16;
+    for (size_t u = (size_t)blockIdx.x * blockDim.x + threadIdx.x; u < units;
+         u += (size_t)gridDim.x * blockDim.x) {
+        const size_t so = (size_t)src * block_bytes + u * 16;
+        const size_t d = (size_t)dst * block_bytes + u * 16;
+        const u32x4 kv = *reinterpret_cast<const u32x4 *>(static_cast<const char *>(k_pool) + so);
+        const u32x4 vv = *reinterpret_cast<const u32x4 *>(static_cast<const char *>(v_pool) + so);
+        *reinterpret_cast<u32x4 *>(static_cast<char *>(k_pool) + d) = kv;
+        *reinterpret_cast<u32x4 *>(static_cast<char *>(v_pool) + d) = vv;
+    }
+}
+
 }  // namespace
+
+hipError_t launch_copy_blocks(void *k_pool, void *v_pool, const int32_t *pairs, int32_t num_pairs,
+                              int32_t num_blocks, size_t block_bytes, hipStream_t stream)
+{
+    const size_t units = block_bytes / 16;
+    const unsigned gx = (unsigned)((units + 255) / 256 < 64 ? (units + 255) / 256 : 64);
+    hipLaunchKernelGGL(pa_copy_blocks_kernel, dim3(gx, num_pairs), dim3(256), 0, stream, k_pool,
+                       v_pool, pairs, num_blocks, block_bytes);
+    return hipGetLastError();
+}
 
 hipError_t launch_append(int dtype, int act_dtype, int head_dim, const AppendArgs &a,
                          hipStream_t stream)

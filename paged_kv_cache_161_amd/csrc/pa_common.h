@@ -61,6 +61,8 @@ hipError_t launch_decode(int dtype, int act_dtype, int head_dim, const DecodeArg
                          int num_seqs, hipStream_t stream);
 hipError_t launch_append(int dtype, int act_dtype, int head_dim, const AppendArgs &a,
                          hipStream_t stream);
+hipError_t launch_copy_blocks(void *k_pool, void *v_pool, const int32_t *pairs, int32_t num_pairs,
+                              int32_t num_blocks, size_t block_bytes, hipStream_t stream);
 
 // Decode launch shape for 16-bit K/V with head_dim <= 128: waves per workgroup and
 // blocks each wave keeps in flight ahead of the one it is computing.
