@@ -30,6 +30,7 @@ import torch
 HBM_PEAK_GBS = 8000.0
 ROOT = os.path.dirname(os.path.abspath(__file__))
 LAYERS = 4
+W_ELEM = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}
 CALIBRATION_BYTES = 256 << 20
 HEADLINE = 3
 
@@ -49,6 +50,9 @@ def parse():
     ap.add_argument("--partition-tokens", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--roofline-launches", type=int, default=100)
+    ap.add_argument("--op", choices=["step", "copy_blocks"], default="step",
+                    help="step: the decode step (default); copy_blocks: the copy-on-write "
+                         "block copy on the workload's pool")
     ap.add_argument("--calibrate", action="store_true",
                     help="also run one 256 MiB device copy (a kernel of known traffic for "
                          "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
@@ -103,6 +107,47 @@ def cpu_baseline(w):
                       f"{w.num_seqs / t:.1f} tokens/s"}
 
 
+def bench_copy_blocks(args, w, PA, U, dev):
+    """pa_copy_blocks on the workload's pool: 1024 (src, dst) pairs of distinct blocks
+    per launch, launches back to back between two HIP events; bytes = read + write of
+    both pools' blocks."""
+    kp, vp = U.device_pools(w, dev)
+    rng = np.random.Generator(np.random.PCG64(7))
+    n_pairs = min(1024, w.num_blocks // 2)
+    perm = rng.permutation(w.num_blocks)
+    pairs = torch.from_numpy(np.stack([perm[:n_pairs], perm[n_pairs:2 * n_pairs]], 1)
+                             .astype(np.int32)).to(dev)
+    block_bytes = w.num_kv_heads * 16 * w.head_dim * W_ELEM[w.kv_dtype]
+    moved = 2 * 2 * n_pairs * block_bytes          # K and V, read and write
+    for _ in range(args.warmup):
+        PA.copy_blocks(kp, vp, pairs)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        PA.copy_blocks(kp, vp, pairs)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    dur = e0.elapsed_time(e1) * 1e-3 / args.steps
+    gbs = moved / dur / 1e9
+    log(f"[bench] copy_blocks: {n_pairs} pairs of {block_bytes} B blocks, {dur * 1e6:.1f} us "
+        f"per launch -> {gbs:.0f} GB/s")
+    print(json.dumps({
+        "metric": "copy-on-write block copy GB/s (read + write), 1 MI355X",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(dur * 1e3, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.kv_dtype,
+        "data": "synthetic", "config": {"workload": f"{w.spec.name} pool, {n_pairs} block pairs",
+                                         "block_bytes_per_pool": block_bytes},
+        "roofline": {"bound": "hbm", "kernel": "pa_copy_blocks_kernel",
+                     "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "launch_us_mean": round(dur * 1e6, 2), "bytes_per_launch": moved},
+    }), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -125,6 +170,9 @@ def main():
     log(f"[bench] built {w.spec.name} in {time.time() - t0:.1f}s: B={w.num_seqs} "
         f"Hq={w.num_q_heads} Hkv={w.num_kv_heads} d={w.head_dim} "
         f"max_ctx={w.max_context_len} pool={w.num_blocks} blocks")
+
+    if args.op == "copy_blocks":
+        return bench_copy_blocks(args, w, PA, U, dev)
 
     pools = [U.device_pools(w, dev) for _ in range(LAYERS)]
     d = U.device_inputs(w, dev)
