@@ -1,4 +1,4 @@
-"""fp64 CPU oracle for decode-phase paged attention: TEST INFRASTRUCTURE ONLY.
+"""fp64 CPU oracle for paged attention (decode, prefill): TEST INFRASTRUCTURE ONLY.
 
 Only tests/, the package smoke check and bench.py's CPU-baseline leg may import this
 package.  The GPU product path must never call it.  The arithmetic lives in
@@ -50,6 +50,9 @@ def _bind(lib):
     lib.oracle_decode_paged_ex.argtypes = [P, I, P, P, I, D, D, I, I, I, I, I, P, I, P,
                                            ctypes.c_float, P, P, I]
     lib.oracle_decode_paged_ex.restype = I
+    lib.oracle_prefill_paged_ex.argtypes = [P, I, P, P, I, D, D, I, P, I, I, I, I, P, I, P,
+                                            ctypes.c_float, P, P, I]
+    lib.oracle_prefill_paged_ex.restype = I
     lib.oracle_cache_append_ex.argtypes = [P, P, I, I, ctypes.c_float, ctypes.c_float, I, I, I,
                                            P, P, P, I]
     lib.oracle_cache_append_ex.restype = I
@@ -130,6 +133,37 @@ def decode_paged(q, k_pool, v_pool, dtype, block_tables, context_lens, scale,
                                     _ptr(out), _ptr(wsum), threads or default_threads())
     if rc:
         raise ValueError(f"oracle_decode_paged returned {rc}")
+    return out, wsum
+
+
+def prefill_paged(q, k_pool, v_pool, dtype, query_start, block_tables, context_lens, scale,
+                  threads=None, lib=None, q_dtype=None, k_scale=1.0, v_scale=1.0):
+    """Causal paged prefill.  q [T][Hq][d]; the query rows of sequence b are
+    query_start[b] .. query_start[b+1]-1 and sit at the end of its context_lens[b]
+    tokens.  Returns (out [T][Hq][d] fp64, wsum [T][Hq] fp64)."""
+    lib = lib or load()
+    q_dtype = q_dtype or dtype
+    _check(q, q_dtype)
+    for a in (k_pool, v_pool):
+        _check(a, dtype)
+    T, hq, d = q.shape
+    nblk, hkv, bs, d2 = k_pool.shape
+    assert bs == 16 and d2 == d and v_pool.shape == (nblk, hkv, d, 16)
+    bt = np.ascontiguousarray(block_tables, np.int32)
+    cl = np.ascontiguousarray(context_lens, np.int32)
+    qs = np.ascontiguousarray(query_start, np.int32)
+    B = cl.shape[0]
+    assert bt.shape[0] == B and qs.shape == (B + 1,) and qs[-1] == T
+    out = np.zeros((T, hq, d), np.float64)
+    wsum = np.zeros((T, hq), np.float64)
+    rc = lib.oracle_prefill_paged_ex(_ptr(q), DTYPE_CODES[q_dtype], _ptr(k_pool), _ptr(v_pool),
+                                     DTYPE_CODES[dtype], float(np.float32(k_scale)),
+                                     float(np.float32(v_scale)), B, _ptr(qs), hq, hkv, d, nblk,
+                                     _ptr(bt), bt.shape[1], _ptr(cl),
+                                     ctypes.c_float(np.float32(scale)), _ptr(out), _ptr(wsum),
+                                     threads or default_threads())
+    if rc:
+        raise ValueError(f"oracle_prefill_paged returned {rc}")
     return out, wsum
 
 

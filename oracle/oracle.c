@@ -1,5 +1,5 @@
 /*
- * oracle.c -- plain, slow, fp64 CPU reference for decode-phase paged attention.
+ * oracle.c -- plain, slow, fp64 CPU reference for paged attention (decode and prefill).
  *
  * TEST INFRASTRUCTURE ONLY.  Only the test suite, the package smoke check and the
  * benchmark's CPU-baseline leg may load this library.  The GPU product path never
@@ -22,6 +22,10 @@
  *
  *  - GQA: q-heads are split into contiguous groups, each group reads one KV head
  *    ("大模型推理的三维本质原理解析与工程实践", section 6 GQA): kv_head = h / (Hq/Hkv).
+ *
+ *  - Paged prefill: the queries of a prompt chunk attend to the cache over the same
+ *    block tables, each to its own prefix (causal); a decode query is the one-row case
+ *    (oracle_prefill_paged_ex below gives the sources).
  *
  * It is written as the plain definition: resolve each token through the table, form
  * every score, take the maximum, exponentiate, sum, weight V, divide once.  It does
@@ -270,7 +274,25 @@ typedef struct {
     double scale;
     double *out, *wsum;
     int nthreads;
+    /* prefill only (NULL / 0 for decode): query rows of sequence b are
+     * q_start[b] .. q_start[b+1]-1 of q [num_tokens][Hq][d]                          */
+    const int32_t *q_start;
+    int num_tokens;
 } decode_args;
+
+/* Sequence that owns query row `tok` (q_start is non-decreasing, q_start[0] = 0).    */
+static int owner_of(const int32_t *q_start, int B, int tok)
+{
+    int lo = 0, hi = B - 1;
+    while (lo < hi) {
+        int mid = (lo + hi + 1) / 2;
+        if (q_start[mid] <= tok)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    return lo;
+}
 
 typedef struct {
     const decode_args *A;
@@ -286,16 +308,28 @@ static void *decode_worker(void *p)
     double *scores = (double *)malloc(sizeof(double) * (size_t)(cap > 0 ? cap : 1));
     if (!scores)
         return (void *)1;
-    /* units (sequence, q-head) are dealt round-robin; each unit is self-contained */
-    for (int u = W->tid; u < A->B * A->hq; u += A->nthreads) {
-        int b = u / A->hq, h = u % A->hq;
+    /* units (query row, q-head) are dealt round-robin; each unit is self-contained.
+     * Decode has one query row per sequence, the sequence's newest token, which sees
+     * the whole context.  Prefill row r of sequence b is token ctx - q_len + i of it
+     * (i = r - q_start[b]; the chunk was appended before attending) and sees tokens
+     * 0 .. ctx - q_len + i: its own prefix, itself included.                         */
+    const int rows = A->q_start ? A->num_tokens : A->B;
+    for (int u = W->tid; u < rows * A->hq; u += A->nthreads) {
+        int r = u / A->hq, h = u % A->hq;
+        int b = A->q_start ? owner_of(A->q_start, A->B, r) : r;
+        int n = A->ctx_lens[b];
+        if (A->q_start) {
+            int q_len = A->q_start[b + 1] - A->q_start[b];
+            int pos = n - q_len + (r - A->q_start[b]);
+            n = pos < 0 ? 0 : pos + 1;
+        }
         int kvh = h / group;
         attn_job J;
-        J.q_row = (const char *)A->q + ((size_t)b * A->hq + h) * A->d * elem_bytes(A->q_dtype);
+        J.q_row = (const char *)A->q + ((size_t)r * A->hq + h) * A->d * elem_bytes(A->q_dtype);
         J.q_dtype = A->q_dtype;
         J.d = A->d;
         J.scale = A->scale;
-        J.n = A->ctx_lens[b];
+        J.n = n;
         J.scores = scores;
         paged_ctx pc;
         contig_ctx cc;
@@ -386,6 +420,50 @@ int oracle_decode_paged_ex(const void *q, int q_dtype, const void *k_pool, const
     decode_args A = {1, q, k_pool, v_pool, kv_dtype, q_dtype, k_scale, v_scale, num_seqs,
                      num_q_heads, num_kv_heads, head_dim, num_blocks, max_blocks_per_seq, 0,
                      block_tables, context_lens, (double)scale, out, wsum, num_threads};
+    return run_decode(&A);
+}
+
+/* Paged prefill attention (a prompt chunk, or several, over the paged cache).
+ * LLM-101-CN "推理优化", section "Chunked Prefill": a chunk's queries attend to the
+ * cached K/V of the earlier chunks joined with the chunk's own K/V, with the same
+ * 1/sqrt(d_h)-scaled softmax; its mixed-batch section runs the requests of one batch
+ * with different chunk lengths.  "Deep dive into vLLM 06", section 4.2: one forward
+ * computes every position from its own known prefix, i.e. the causal rule.
+ * Query rows of sequence b are q_start[b] .. q_start[b+1]-1 of q [T][Hq][d]
+ * (q_start has B + 1 entries, non-decreasing, q_start[0] = 0, q_start[B] = T).  The
+ * chunk is already in the pool, counted in context_lens[b]; its i-th query is token
+ * ctx - q_len + i and attends to tokens 0 .. ctx - q_len + i.  A query with no key
+ * (q_len > ctx) gives a zero row.  out [T][Hq][d], wsum [T][Hq] fp64.  Returns 0, -1
+ * on bad shapes, -2 on an out-of-range context length, block-table entry or q_start.  */
+int oracle_prefill_paged_ex(const void *q, int q_dtype, const void *k_pool, const void *v_pool,
+                            int kv_dtype, double k_scale, double v_scale, int num_seqs,
+                            const int32_t *query_start, int num_q_heads, int num_kv_heads,
+                            int head_dim, int num_blocks, const int32_t *block_tables,
+                            int max_blocks_per_seq, const int32_t *context_lens, float scale,
+                            double *out, double *wsum, int num_threads)
+{
+    if (check_common(kv_dtype, num_seqs, num_q_heads, num_kv_heads, head_dim) ||
+        check_common(q_dtype, num_seqs, num_q_heads, num_kv_heads, head_dim) ||
+        q_dtype == ORACLE_FP8_E4M3 || num_seqs < 1)
+        return -1;
+    if (query_start[0] != 0)
+        return -2;
+    for (int b = 0; b < num_seqs; ++b) {
+        int n = context_lens[b];
+        if (query_start[b + 1] < query_start[b])
+            return -2;
+        if (n < 0 || n > max_blocks_per_seq * ORACLE_BLOCK)
+            return -2;
+        for (int lb = 0; lb < (n + ORACLE_BLOCK - 1) / ORACLE_BLOCK; ++lb) {
+            int32_t p = block_tables[(size_t)b * max_blocks_per_seq + lb];
+            if (p < 0 || p >= num_blocks)
+                return -2;
+        }
+    }
+    decode_args A = {1, q, k_pool, v_pool, kv_dtype, q_dtype, k_scale, v_scale, num_seqs,
+                     num_q_heads, num_kv_heads, head_dim, num_blocks, max_blocks_per_seq, 0,
+                     block_tables, context_lens, (double)scale, out, wsum, num_threads,
+                     query_start, query_start[num_seqs]};
     return run_decode(&A);
 }
 

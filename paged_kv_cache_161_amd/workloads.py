@@ -1,4 +1,4 @@
-"""Seeded synthetic workloads for decode-phase paged attention.
+"""Seeded synthetic workloads for paged attention (decode steps and prefill chunks).
 
 This module only builds inputs: random values, a physical block pool, block tables,
 context lengths, the rows a decode step appends and their slots.  It computes no
@@ -82,11 +82,14 @@ class Spec:
     kv_dtype: Optional[str] = None  # pool type; None = dtype; "fp8" keeps q/new rows in dtype
     k_scale: float = 1.0            # fp8 pools: K = code x k_scale, V = code x v_scale
     v_scale: float = 1.0
+    # prefill: query (chunk) tokens per sequence, the last query_lens[b] tokens of its
+    # context; None = decode (one query, the newest token)
+    query_lens: Optional[Sequence[int]] = None
 
 
 @dataclasses.dataclass
 class Workload:
-    """Inputs of one decode step (one layer).
+    """Inputs of one decode or prefill step (one layer).
 
     Only live blocks are held on the host: k_live / v_live hold the blocks listed in
     live_blocks (ascending physical id) followed by one entirely poisoned block.  The
@@ -99,7 +102,7 @@ class Workload:
     kv_dtype: str                   # pools
     k_scale: np.float32
     v_scale: np.float32
-    q: np.ndarray                   # [B][Hq][d]
+    q: np.ndarray                   # [B][Hq][d] (decode) or [T][Hq][d] (prefill)
     num_blocks: int                 # size of the physical pool
     live_blocks: np.ndarray         # [n] distinct physical ids holding live tokens
     k_live: np.ndarray              # [n+1][Hkv][16][d]: live blocks, then a poison block
@@ -111,10 +114,40 @@ class Workload:
     context_lens: np.ndarray        # [B] int32
     scale: np.float32
     poison_block: int               # physical id of a block that is entirely poisoned
+    query_start: Optional[np.ndarray] = None  # prefill: [B+1] int32, rows of q per sequence
 
     @property
     def num_seqs(self):
+        return self.context_lens.shape[0]
+
+    @property
+    def is_prefill(self):
+        return self.query_start is not None
+
+    @property
+    def num_query_tokens(self):
         return self.q.shape[0]
+
+    @property
+    def max_query_len(self):
+        if self.query_start is None:
+            return 1
+        return int(np.diff(self.query_start).max()) if self.num_seqs else 0
+
+    def attended_keys(self) -> int:
+        """Sum over query rows of the keys each attends to (per q-head)."""
+        ctx = self.context_lens.astype(np.int64)
+        if self.query_start is None:
+            return int(ctx.sum())
+        ql = np.diff(self.query_start.astype(np.int64))
+        first = ctx - ql                     # position of each chunk's first query
+        # query i sits at first + i and sees first + i + 1 keys (none if that is <= 0)
+        total = 0
+        for f, n in zip(first.tolist(), ql.tolist()):
+            lo = max(0, -f)                  # queries before the context starts see none
+            if n > lo:
+                total += (n - lo) * f + (lo + 1 + n) * (n - lo) // 2
+        return int(total)
 
     @property
     def num_q_heads(self):
@@ -187,6 +220,8 @@ class Workload:
         for a in (self.q, self.live_blocks, self.k_live, self.v_live, self.k_new, self.v_new,
                   self.slot_mapping, self.block_tables, self.context_lens):
             h.update(np.ascontiguousarray(a).view(np.uint8).tobytes())
+        if self.query_start is not None:
+            h.update(self.query_start.view(np.uint8).tobytes())
         h.update(str(self.num_blocks).encode())
         return h.hexdigest()
 
@@ -313,8 +348,13 @@ def build(spec: Spec, seed: Optional[int] = None) -> Workload:
             assert poison_block >= 0, "table padding needs a poisoned spare block"
             tables[b, nblk[b]:] = poison_block
 
+    qlens = None
+    if spec.query_lens is not None:
+        qlens = np.asarray(spec.query_lens, np.int64)
+        assert qlens.shape == (B,) and (qlens >= 0).all()
+
     # ---- values: each array from its own seeded streams (tags 1..5)
-    q = np.empty((B, hq, d), STORAGE[dt])
+    q = np.empty((B if qlens is None else int(qlens.sum()), hq, d), STORAGE[dt])
     _fill_normals(seed, 1, q, spec.sigma, dt)
     k_live = np.empty((live.size + 1, hkv, BLOCK, d), STORAGE[kdt])
     v_live = np.empty((live.size + 1, hkv, d, BLOCK), STORAGE[kdt])
@@ -333,16 +373,22 @@ def build(spec: Spec, seed: Optional[int] = None) -> Workload:
             k_live[i, :, n % BLOCK:, :] = _poison((hkv, BLOCK - n % BLOCK, d), kdt)
             v_live[i, :, :, n % BLOCK:] = _poison((hkv, d, BLOCK - n % BLOCK), kdt)
 
-    # the step's own token (ctx-1): poisoned in the pool, delivered by the append
-    appending = [b for b in range(B) if spec.append and ctx[b] > 0]
+    # the step's own tokens (decode: ctx-1; prefill: the chunk's last query_lens[b]
+    # positions): poisoned in the pool, delivered by the append
+    if not spec.append:
+        appending = []
+    elif qlens is None:
+        appending = [(b, int(ctx[b]) - 1) for b in range(B) if ctx[b] > 0]
+    else:
+        appending = [(b, pos) for b in range(B)
+                     for pos in range(max(0, int(ctx[b] - qlens[b])), int(ctx[b]))]
     T = len(appending)
     k_new = np.empty((T, hkv, d), STORAGE[dt])
     v_new = np.empty((T, hkv, d), STORAGE[dt])
     _fill_normals(seed, 4, k_new, spec.sigma, dt)
     _fill_normals(seed, 5, v_new, spec.sigma, dt)
     slots = np.full(T, -1, np.int32)
-    for j, b in enumerate(appending):
-        pos = int(ctx[b]) - 1
+    for j, (b, pos) in enumerate(appending):
         p = int(tables[b, pos // BLOCK])
         i = pos_of[p]
         k_live[i, :, pos % BLOCK, :] = _poison((hkv, d), kdt)
@@ -350,8 +396,11 @@ def build(spec: Spec, seed: Optional[int] = None) -> Workload:
         slots[j] = p * BLOCK + pos % BLOCK
 
     scale = np.float32(1.0 / math.sqrt(d))
+    qstart = None if qlens is None else \
+        np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
     return Workload(spec, dt, kdt, ks, vsc, q, n_pool, live.astype(np.int64), k_live, v_live,
-                    k_new, v_new, slots, tables, ctx.astype(np.int32), scale, poison_block)
+                    k_new, v_new, slots, tables, ctx.astype(np.int32), scale, poison_block,
+                    qstart)
 
 
 # ----------------------------------------------------------------- named configs
@@ -372,6 +421,10 @@ def config_spec(i: int) -> Spec:
     5 long + shared prefix bf16: 4 seqs x 32768 and 8 beams x 2304 that share their first
       2048 tokens (128 physical blocks), 64/8 heads, d 128.
     6 config 3 with an FP8 E4M3 KV cache (k_scale 0.0117, v_scale 0.0093), bf16 q/out.
+    7 chunked prefill: 16 prompts of 4096 tokens whose last 512-token chunk attends
+      (causally) to the whole cache, 64/8 heads, d 128, bf16.
+    8 mixed prefill + decode batch: 24 ragged decodes, four 512-token chunks ending at
+      512 / 1024 / 2560 / 4096 and a fresh 300-token prompt.
     """
     if i == 1:
         return Spec("tiny_fp32", "f32", 4, 1, 64, [37], sigma=1.0, seed=1, exact_pool=8)
@@ -393,6 +446,17 @@ def config_spec(i: int) -> Spec:
         # config 3's shape with an FP8 E4M3 KV cache (per-tensor scales), bf16 q/out
         return Spec("llama70b_gqa_fp8kv", "bf16", 64, 8, 128, [4096] * 32, seed=3,
                     spare_blocks=32, kv_dtype="fp8", k_scale=0.0117, v_scale=0.0093)
+    if i == 7:
+        # chunked prefill: the last 512-token chunk of 16 prompts of 4096 tokens
+        return Spec("chunked_prefill_llama70b_gqa_bf16", "bf16", 64, 8, 128, [4096] * 16,
+                    seed=7, spare_blocks=16, query_lens=[512] * 16)
+    if i == 8:
+        # one mixed batch: 24 decodes of ragged length, four 512-token chunks at
+        # different offsets and a fresh 300-token prompt
+        dec = _ragged_lens(8, 24, 1, 4096)
+        return Spec("mixed_prefill_decode_gqa_bf16", "bf16", 64, 8, 128,
+                    dec + [512, 1024, 2560, 4096, 300], seed=8, spare_blocks=8,
+                    query_lens=[1] * 24 + [512, 512, 512, 512, 300])
     raise ValueError(f"no config {i}")
 
 

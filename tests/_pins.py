@@ -399,7 +399,151 @@ def check_block_table_example(lib):
     assert out.tobytes() == ref.tobytes()
 
 
+# ------------------------------------------------------------------ prefill
+
+def prefill_specs():
+    """Small prefill workloads: whole prompts, chunks at offsets, ragged and empty
+    chunks, a chunk longer than its context, and an fp8 pool."""
+    return [
+        W.Spec("pf_prompt_bf16", "bf16", 8, 2, 32, [1, 17, 45], seed=21, spare_blocks=2,
+               query_lens=[1, 17, 45]),
+        W.Spec("pf_chunk_f16", "f16", 6, 3, 16, [33, 40, 9], seed=22, spare_blocks=1,
+               query_lens=[5, 16, 9]),
+        W.Spec("pf_mixed_f32", "f32", 4, 1, 8, [20, 7, 0, 3], seed=23, spare_blocks=1,
+               query_lens=[1, 7, 0, 5]),
+        W.Spec("pf_fp8", "bf16", 8, 2, 32, [30, 47], seed=24, spare_blocks=1, kv_dtype="fp8",
+               k_scale=0.0117, v_scale=0.0093, query_lens=[30, 12]),
+    ]
+
+
+def oracle_prefill(w, kp, vp, tables=None, lib=None, **kw):
+    return O.prefill_paged(w.q, kp, vp, w.kv_dtype, w.query_start,
+                           w.block_tables if tables is None else tables, w.context_lens,
+                           w.scale, lib=lib, q_dtype=w.dtype, k_scale=w.k_scale,
+                           v_scale=w.v_scale, **kw)
+
+
+def _chunk_rows(w):
+    """(b, first query row, number of query rows, first position) per sequence."""
+    qs = w.query_start
+    for b in range(w.num_seqs):
+        n = int(qs[b + 1] - qs[b])
+        yield b, int(qs[b]), n, int(w.context_lens[b]) - n
+
+
+def check_prefill_sdpa(lib):
+    """torch's CPU float64 attention with its lower-right causal mask (the chunk's
+    queries are the last rows of the context) on the gathered cache."""
+    from torch.nn.attention.bias import causal_lower_right
+    for spec in prefill_specs():
+        w = W.build(spec)
+        kp, vp = appended(w, lib)
+        out, _ = oracle_prefill(w, kp, vp, lib=lib)
+        K, V = gather_contig(w, kp, vp)
+        Kf, Vf = (torch.from_numpy(x) for x in kv_f64(w, K, V))
+        q = torch.from_numpy(to_f64(w.q, w.dtype))
+        G = w.num_q_heads // w.num_kv_heads
+        for b, r0, n, first in _chunk_rows(w):
+            ctx = int(w.context_lens[b])
+            empty = max(0, -first)            # queries before the context: no keys
+            assert np.all(out[r0:r0 + empty] == 0.0)
+            m = n - empty
+            if m == 0:
+                continue
+            k = Kf[b, :, :ctx].repeat_interleave(G, dim=0).contiguous()   # [Hq][ctx][d]
+            v = Vf[b, :, :ctx].repeat_interleave(G, dim=0).contiguous()
+            qq = q[r0 + empty:r0 + n].transpose(0, 1).contiguous()        # [Hq][m][d]
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                qq, k, v, attn_mask=causal_lower_right(m, ctx), scale=float(w.scale))
+            got = out[r0 + empty:r0 + n]
+            err = np.abs(got - ref.transpose(0, 1).numpy()).max()
+            assert err <= 1e-12, (spec.name, b, err)
+
+
+def check_prefill_bruteforce(lib):
+    """Pure-Python loops: query i of a chunk of n rows over a context of ctx tokens
+    sees tokens t with t <= ctx - n + i."""
+    spec = prefill_specs()[1]
+    w = W.build(spec)
+    kp, vp = appended(w, lib)
+    out, _ = oracle_prefill(w, kp, vp, lib=lib)
+    K, V = gather_contig(w, kp, vp)
+    Kf, Vf = kv_f64(w, K, V)
+    q = to_f64(w.q, w.dtype)
+    G = w.num_q_heads // w.num_kv_heads
+    for b, r0, n, first in _chunk_rows(w):
+        ctx = int(w.context_lens[b])
+        for i in range(n):
+            for h in range(w.num_q_heads):
+                keys = [t for t in range(ctx) if t <= ctx - n + i]
+                if not keys:
+                    assert np.all(out[r0 + i, h] == 0.0)
+                    continue
+                qs = q[r0 + i, h].tolist()
+                xs = [float(w.scale) * math.fsum(a * c for a, c in zip(qs, Kf[b, h // G, t]))
+                      for t in keys]
+                mx = max(xs)
+                ws = [math.exp(x - mx) for x in xs]
+                z = math.fsum(ws)
+                for e in range(w.head_dim):
+                    ref = math.fsum(wt * Vf[b, h // G, t, e] for wt, t in zip(ws, keys)) / z
+                    assert abs(out[r0 + i, h, e] - ref) <= 1e-13 * max(1.0, abs(ref))
+
+
+def check_prefill_chunked_prompt(lib):
+    """The pages' chunk loop: appending a prompt chunk by chunk and attending each
+    chunk over the cache so far gives the same rows, bit for bit, as one pass over the
+    whole prompt."""
+    w = W.build(prefill_specs()[0])                 # whole prompts, delivered by append
+    kp0, vp0 = w.host_pools()
+    full_k, full_v = O.cache_append(kp0, vp0, w.k_new, w.v_new, w.slot_mapping, w.kv_dtype,
+                                    lib=lib, act_dtype=w.dtype)
+    ref, _ = oracle_prefill(w, full_k, full_v, lib=lib)
+    for chunk in (4, 16, 7):
+        kp, vp = kp0.copy(), vp0.copy()
+        got = np.full(ref.shape, np.nan)
+        for b, r0, n, first in _chunk_rows(w):
+            assert first == 0
+            for s0 in range(0, n, chunk):
+                s1 = min(n, s0 + chunk)
+                rows = slice(r0 + s0, r0 + s1)      # prompt tokens s0..s1-1 of sequence b
+                kp, vp = O.cache_append(kp, vp, w.k_new[rows], w.v_new[rows],
+                                        w.slot_mapping[rows], w.kv_dtype, lib=lib,
+                                        act_dtype=w.dtype)
+                o, _ = O.prefill_paged(np.ascontiguousarray(w.q[rows]), kp, vp, w.kv_dtype,
+                                       [0, s1 - s0], w.block_tables[b:b + 1], [s1], w.scale,
+                                       lib=lib, q_dtype=w.dtype)
+                got[rows] = o
+        assert got.tobytes() == ref.tobytes(), chunk
+    assert full_k.tobytes() == kp.tobytes() and full_v.tobytes() == vp.tobytes()
+
+
+def check_prefill_weight_sum(lib):
+    for spec in prefill_specs():
+        w = W.build(spec)
+        kp, vp = appended(w, lib)
+        _, wsum = oracle_prefill(w, kp, vp, lib=lib)
+        for b, r0, n, first in _chunk_rows(w):
+            for i in range(n):
+                want = 1.0 if first + i >= 0 else 0.0
+                assert np.all(np.abs(wsum[r0 + i] - want) <= 1e-12), (spec.name, b, i)
+
+
+def check_prefill_one_row_is_decode(lib):
+    """A chunk of one query is the decode step: same rows as decode_paged."""
+    spec = small_specs()[1]
+    w = W.build(spec)
+    kp, vp = appended(w, lib)
+    dec, _ = oracle_paged(w, kp, vp, lib=lib)
+    qs = np.arange(w.num_seqs + 1, dtype=np.int32)
+    pf, _ = O.prefill_paged(w.q, kp, vp, w.kv_dtype, qs, w.block_tables, w.context_lens,
+                            w.scale, lib=lib, q_dtype=w.dtype)
+    assert pf.tobytes() == dec.tobytes()
+
+
 ALL_CHECKS = [check_widen_f16, check_widen_bf16, check_widen_fp8, check_encode_fp8,
               check_append, check_bruteforce,
               check_permutation, check_weight_sum, check_closed_forms, check_split_combine,
-              check_kv_size, check_block_table_example]
+              check_kv_size, check_block_table_example, check_prefill_sdpa,
+              check_prefill_bruteforce, check_prefill_chunked_prompt, check_prefill_weight_sum,
+              check_prefill_one_row_is_decode]

@@ -47,6 +47,13 @@ MUTANTS = {
     "fp8_k_scale_dropped": ("return widen_at(P->k_pool, idx, P->dtype) * P->k_scale;",
                             "return widen_at(P->k_pool, idx, P->dtype);"),
     "fp8_append_scale_multiplied": ("encode_e4m3(vx / v_scale)", "encode_e4m3(vx * v_scale)"),
+    "prefill_causal_mask_dropped": ("n = pos < 0 ? 0 : pos + 1;", "n = pos < 0 ? 0 : n;"),
+    "prefill_own_token_excluded": ("n = pos < 0 ? 0 : pos + 1;", "n = pos < 0 ? 0 : pos;"),
+    "prefill_upper_left_alignment": ("int pos = n - q_len + (r - A->q_start[b]);",
+                                     "int pos = r - A->q_start[b];"),
+    "prefill_q_row_of_sequence": ("J.q_row = (const char *)A->q + ((size_t)r * A->hq + h)",
+                                  "J.q_row = (const char *)A->q + ((size_t)b * A->hq + h)"),
+    "prefill_owner_off_by_one": ("if (q_start[mid] <= tok)", "if (q_start[mid] < tok)"),
 }
 
 
