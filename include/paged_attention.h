@@ -156,6 +156,38 @@ pa_status pa_decode(const pa_kv_pool *pool, const void *q, void *out, int32_t nu
                     int32_t max_context_len, int32_t partition_tokens, void *workspace,
                     size_t workspace_bytes, void *stream);
 
+/* Paged prefill (chunked prefill) attention for one layer: the query rows of prompt
+ * chunks attend to the cache through the same pool and block tables as decode
+ * (LLM-101-CN "推理优化", section "Chunked Prefill": a chunk's queries attend to the
+ * earlier chunks' cache joined with the chunk's own K/V, with the 1/sqrt(d_h) softmax;
+ * its mixed prefill/decode batch gives each request its own chunk length.  "Deep dive
+ * into vLLM 06", section 4.2: each position is computed from its own prefix, i.e. the
+ * attention is causal).
+ *   q              [num_query_tokens][num_q_heads][head_dim], act_dtype, device
+ *   out            same shape and type; fp32 result rounded to nearest-even
+ *   query_start    [num_seqs + 1] int32, device: sequence b owns query rows
+ *                  query_start[b] .. query_start[b+1]-1 (non-decreasing, from 0)
+ *   num_query_tokens  host: the number of q rows, T
+ *   max_query_len  host-side upper bound of the chunk lengths, sizes the launch grid
+ *   scale          finite and > 0 (normally 1/sqrt(head_dim)), applied in fp32
+ *   block_tables, max_blocks_per_seq, context_lens, max_context_len: as for pa_decode;
+ *                  context_lens[b] counts the chunk, whose K/V rows must already be in
+ *                  the pool (pa_cache_append first)
+ * Query i of sequence b is token context_lens[b] - q_len + i and attends to tokens
+ * 0 .. context_lens[b] - q_len + i; a query placed before the context (q_len >
+ * context_lens[b]) gets a zero row.  A chunk of one query is exactly a decode step.
+ * Supported: 16-bit pools (f16, bf16) and fp8 pools with f16/bf16 activations, head_dim
+ * 64 or 128, num_q_heads / num_kv_heads <= 256 (PA_ERR_UNSUPPORTED otherwise).
+ * Device-side inconsistency: a bad context length or a needed table entry outside
+ * [0, num_blocks) makes that sequence's rows NaN; a query range that is decreasing,
+ * longer than max_query_len or outside [0, num_query_tokens) leaves that sequence's
+ * rows unwritten.  Nothing out of bounds is ever read or written.  No workspace. */
+pa_status pa_prefill(const pa_kv_pool *pool, const void *q, void *out, int32_t num_seqs,
+                     int32_t num_q_heads, float scale, const int32_t *query_start,
+                     int32_t num_query_tokens, int32_t max_query_len,
+                     const int32_t *block_tables, int32_t max_blocks_per_seq,
+                     const int32_t *context_lens, int32_t max_context_len, void *stream);
+
 /* Copy whole physical blocks inside the pool: for each pair i, block pairs[2i] (src)
  * is copied to block pairs[2i+1] (dst), every kv-head, in both K and V, bytes
  * unchanged -- the copy half of copy-on-write (LLM-101-CN "推理优化", section

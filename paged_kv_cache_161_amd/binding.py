@@ -63,6 +63,9 @@ def load(path: str = LIB_PATH):
     lib.pa_decode.argtypes = [ctypes.POINTER(PaKvPool), P, P, I32, I32, ctypes.c_float, P, I32,
                               P, I32, I32, P, ctypes.c_size_t, P]
     lib.pa_decode.restype = ctypes.c_int
+    lib.pa_prefill.argtypes = [ctypes.POINTER(PaKvPool), P, P, I32, I32, ctypes.c_float, P, I32,
+                               I32, P, I32, P, I32, P]
+    lib.pa_prefill.restype = I32
     lib.pa_status_string.argtypes = [I32]
     lib.pa_status_string.restype = ctypes.c_char_p
     lib.pa_copy_blocks.argtypes = [ctypes.POINTER(PaKvPool), P, I32, P]
@@ -209,6 +212,38 @@ def decode(q, k_pool, v_pool, block_tables, context_lens, scale: float, max_cont
                                                           torch.int32),
                           max_context_len, partition_tokens, ws_ptr, ws_len,
                           _stream_handle(q.device))
+    _raise(st)
+    return out
+
+
+def prefill(q, k_pool, v_pool, query_start, block_tables, context_lens, scale: float,
+            max_context_len: int, max_query_len: int, out: Optional[torch.Tensor] = None,
+            k_scale: float = 1.0, v_scale: float = 1.0) -> torch.Tensor:
+    """Causal attention of prompt-chunk queries over the paged cache.
+
+    q [T][Hq][d]; query_start [B+1] int32 (rows of sequence b: query_start[b] ..
+    query_start[b+1]-1); block_tables [B][max_blocks] int32; context_lens [B] int32
+    (chunk included, appended beforehand); max_context_len / max_query_len: host-side
+    bounds.  Returns out [T][Hq][d] in q's dtype.
+    """
+    act = q.dtype if k_pool.dtype in FP8_STORAGE else None
+    pool = make_pool(k_pool, v_pool, act, k_scale, v_scale)
+    T, hq, d = q.shape
+    if d != pool.head_dim:
+        raise ValueError("q head_dim differs from the pool's")
+    B = context_lens.shape[0]
+    if query_start.shape != (B + 1,):
+        raise ValueError("query_start must hold num_seqs + 1 entries")
+    if out is None:
+        out = torch.empty_like(q)
+    act = _act_dtype(pool)
+    st = load().pa_prefill(ctypes.byref(pool), _dev_ptr(q, "q", act), _dev_ptr(out, "out", act),
+                           B, hq, ctypes.c_float(scale),
+                           _dev_ptr(query_start, "query_start", torch.int32), T, max_query_len,
+                           _dev_ptr(block_tables, "block_tables", torch.int32),
+                           block_tables.shape[1],
+                           _dev_ptr(context_lens, "context_lens", torch.int32),
+                           max_context_len, _stream_handle(q.device))
     _raise(st)
     return out
 

@@ -12,7 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libpa_mi355x.so")
-SOURCES = ["pa_api.cpp", "pa_alloc.cpp", "pa_decode.hip", "pa_append.hip"]
+SOURCES = ["pa_api.cpp", "pa_alloc.cpp", "pa_decode.hip", "pa_append.hip", "pa_prefill.hip"]
 ARCH = "gfx950"
 
 

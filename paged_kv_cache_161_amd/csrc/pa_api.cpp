@@ -272,4 +272,63 @@ pa_status pa_decode(const pa_kv_pool *pool, const void *q, void *out, int32_t nu
     return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
+pa_status pa_prefill(const pa_kv_pool *pool, const void *q, void *out, int32_t num_seqs,
+                     int32_t num_q_heads, float scale, const int32_t *query_start,
+                     int32_t num_query_tokens, int32_t max_query_len,
+                     const int32_t *block_tables, int32_t max_blocks_per_seq,
+                     const int32_t *context_lens, int32_t max_context_len, void *stream)
+{
+    pa_status st = check_pool(pool);
+    if (st != PA_OK)
+        return st;
+    if (num_seqs < 0 || num_q_heads <= 0 || num_q_heads % pool->num_kv_heads != 0 ||
+        num_query_tokens < 0 || max_query_len < 0 || max_context_len < 0 ||
+        max_blocks_per_seq < 0 || !isfinite(scale) || !(scale > 0.f))
+        return PA_ERR_INVALID_ARG;
+    // 16-bit MFMA kernels only (fp8 pools convert to their 16-bit activation type)
+    if (pool->dtype == PA_F32 || pool->head_dim > 128)
+        return PA_ERR_UNSUPPORTED;
+    const int32_t group = num_q_heads / pool->num_kv_heads;
+    const int32_t rows = pa::prefill_rows_per_group();
+    if (group > rows)
+        return PA_ERR_UNSUPPORTED;
+    if ((int64_t)num_query_tokens * num_q_heads > INT32_MAX)
+        return PA_ERR_UNSUPPORTED;
+    if (num_seqs == 0 || num_query_tokens == 0 || max_query_len == 0)
+        return PA_OK;
+    if (!q || !out || !query_start || !block_tables || !context_lens || max_blocks_per_seq == 0)
+        return PA_ERR_INVALID_ARG;
+    const int32_t q_tile = rows / group;
+    const int64_t qtiles = ((int64_t)max_query_len + q_tile - 1) / q_tile;
+    const int64_t pairs = (int64_t)num_seqs * pool->num_kv_heads;
+    if (pairs > INT32_MAX || ((pairs + 7) / 8) * 8 * qtiles > INT32_MAX)
+        return PA_ERR_UNSUPPORTED;
+
+    pa::PrefillArgs a;
+    a.k_pool = pool->k_pool;
+    a.v_pool = pool->v_pool;
+    a.q = q;
+    a.out = out;
+    a.query_start = query_start;
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.num_seqs = num_seqs;
+    a.num_blocks = pool->num_blocks;
+    a.num_kv_heads = pool->num_kv_heads;
+    a.num_q_heads = num_q_heads;
+    a.group = group;
+    a.max_blocks = max_blocks_per_seq;
+    a.max_context_len = max_context_len;
+    a.num_tokens = num_query_tokens;
+    a.max_query_len = max_query_len;
+    a.q_tile = q_tile;
+    a.num_qtiles = (int32_t)qtiles;
+    const bool fp8 = pool->dtype == PA_FP8_E4M3;
+    a.scale_log2 = scale * 1.4426950408889634f * (fp8 ? pool->k_scale : 1.0f);
+    a.v_scale = fp8 ? pool->v_scale : 1.0f;
+    hipError_t e = pa::launch_prefill(pool->dtype, pool->act_dtype, pool->head_dim, a,
+                                      static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
 }  // extern "C"

@@ -1,0 +1,461 @@
+// pa_prefill.hip -- paged prefill (chunked prefill) attention for CDNA4 (gfx950).
+//
+// What is computed: the query rows of a prompt chunk attend to the paged cache through
+// the same block tables as decode.  Sequence b's chunk is rows query_start[b] ..
+// query_start[b+1]-1 of q; the chunk's K/V rows were appended first, so its i-th query
+// is token ctx - q_len + i and attends, causally, to tokens 0 .. ctx - q_len + i.
+// Sources: LLM-101-CN "推理优化", section "Chunked Prefill" (the chunk's queries over
+// the earlier chunks' cache joined with the chunk's own K/V, 1/sqrt(d_h) softmax; the
+// mixed prefill/decode batch with per-request chunk lengths); "Deep dive into vLLM 06",
+// section 4.2 (one forward yields every position from its own prefix: the causal rule);
+// the block layout, online softmax and GQA sources are those of the decode kernel.
+//
+// Work decomposition
+//   One workgroup of NW waves owns one (sequence, kv-head, query tile).  Its R =
+//   NW * C * 16 rows are (position, q-head of the group) pairs, position-major, so
+//   every q-head of a GQA group shares one stream of K/V.  Wave w owns rows
+//   [16 C w, 16 C (w + 1)) as C MFMA column blocks.
+//   Keys are walked 32 at a time (two pool blocks).  The workgroup stages each step's
+//   K and V in LDS, double-buffered, in MFMA fragment order, so every wave's operand
+//   read is one conflict-free 16-byte LDS load per lane:
+//     S^T[t][row]  = sum_e K[t][e] Q[row][e]        16x16x32, A = K rows, B = Q rows
+//     O^T[e][row] += sum_t V^T[e][t] P[t][row]       16x16x32, A = V^T, B = P
+//   S^T's accumulator layout (lane: row lane % 16, tokens 4 (lane / 16) .. +3 of each
+//   16-token block) is the PV B operand once the 32 keys are ordered as
+//   k = 8 g + j -> block j / 4, token 4 g + j % 4; the V^T fragments use the same order.
+//   The softmax normaliser is a third product, ones[16][32] . P: it sums exactly the
+//   16-bit weights the PV product used, lands already reduced over the wave's four
+//   row groups, and keeps that work off the vector ALU, which the exponentials load.
+//   Workgroup ids go round-robin over the 8 XCDs; the id -> (pair, tile) map keeps all
+//   query tiles of one (sequence, kv-head) on one XCD, so they share its L2.
+#include <limits.h>
+#include <math.h>
+
+#include <type_traits>
+
+#include "pa_common.h"
+
+namespace pa {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kXcds = 8;                 // MI355X: workgroups go round-robin over 8 XCDs
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float max_over_row_groups(float v)
+{
+    v = fmaxf(v, __shfl_xor(v, 16));
+    v = fmaxf(v, __shfl_xor(v, 32));
+    return v;
+}
+
+template <int AT>
+__device__ __forceinline__ f32x4 mma32(u32x4 a, u32x4 b, f32x4 c)
+{
+    if constexpr (AT == DT_BF16)
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// Eight fp32 weights -> eight 16-bit values (RNE), packed as one MFMA operand.
+template <int AT>
+__device__ __forceinline__ u32x4 pack8(f32x4 lo, f32x4 hi)
+{
+    u32x2 a, b;
+    if constexpr (AT == DT_BF16) {
+        a = __builtin_bit_cast(u32x2, __builtin_convertvector(lo, bf16x4));
+        b = __builtin_bit_cast(u32x2, __builtin_convertvector(hi, bf16x4));
+    } else {
+        a = __builtin_bit_cast(u32x2, __builtin_convertvector(lo, f16x4));
+        b = __builtin_bit_cast(u32x2, __builtin_convertvector(hi, f16x4));
+    }
+    return u32x4{a[0], a[1], b[0], b[1]};
+}
+
+// The 16-bit pattern of 1.0, twice.
+template <int AT>
+constexpr uint32_t one_pair() { return AT == DT_BF16 ? 0x3F803F80u : 0x3C003C00u; }
+
+// Two E4M3 codes (low or high half of w) -> two 16-bit values of type AT (exact).
+template <int AT, bool HIGH>
+__device__ __forceinline__ uint32_t fp8x2_to_16(uint32_t w)
+{
+    if constexpr (AT == DT_BF16)
+        return __builtin_bit_cast(uint32_t,
+                                  __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, HIGH));
+    else
+        return __builtin_bit_cast(uint32_t,
+                                  __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w, 1.0f, HIGH));
+}
+
+// Keep the 16-bit elements of an 8-token V^T piece (tokens t0 .. t0+7) below `valid`.
+__device__ __forceinline__ u32x4 keep_tokens16(u32x4 v, int t0, int valid)
+{
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const uint32_t m = (t0 + 2 * w < valid ? 0x0000FFFFu : 0u) |
+                           (t0 + 2 * w + 1 < valid ? 0xFFFF0000u : 0u);
+        v[w] &= m;
+    }
+    return v;
+}
+
+// The same for 16 fp8 codes (tokens t0 .. t0+15).
+__device__ __forceinline__ u32x4 keep_tokens8(u32x4 v, int t0, int valid)
+{
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        uint32_t m = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            m |= (t0 + 4 * w + j < valid) ? (0xFFu << (8 * j)) : 0u;
+        v[w] &= m;
+    }
+    return v;
+}
+
+template <int DT, int AT, int D, int NW, int C>
+__global__ __launch_bounds__(NW *kWave, 1) void pa_prefill_kernel(PrefillArgs a)
+{
+    using Elem = typename std::conditional<DT == DT_FP8, uint8_t, uint16_t>::type;
+    constexpr int NT = NW * kWave;
+    constexpr int NKC = D / 32;              // QK MFMAs per 16-token block
+    constexpr int NDB = D / 16;              // 16-row blocks of O^T
+    constexpr int KSLOTS = 2 * NKC * kWave;  // one step's K fragments (16 bytes each)
+    constexpr int VSLOTS = NDB * kWave;      // one step's V^T fragments
+    // 16-byte global pieces per step: 16-bit K rows hold 8 elements per piece, fp8 16.
+    constexpr int EPP = DT == DT_FP8 ? 16 : 8;
+    constexpr int KCH = 2 * kBlock * (D / EPP);
+    constexpr int VCH = 2 * D * (kBlock / EPP);
+    constexpr int KPT = (KCH + NT - 1) / NT;
+    constexpr int VPT = (VCH + NT - 1) / NT;
+
+    __shared__ u32x4 s_k[2][KSLOTS];
+    __shared__ u32x4 s_v[2][VSLOTS];
+
+    // ---- which (sequence, kv-head, query tile): tiles of one pair share an XCD, the
+    // last tile (most keys) first
+    const int id = blockIdx.x;
+    const int xcd = id % kXcds;
+    const int rr = id / kXcds;
+    const int pair = (rr / a.num_qtiles) * kXcds + xcd;
+    if (pair >= a.num_seqs * a.num_kv_heads)
+        return;
+    const int qt = a.num_qtiles - 1 - rr % a.num_qtiles;
+    const int b = pair / a.num_kv_heads;
+    const int kvh = pair - b * a.num_kv_heads;
+    const int q0 = a.query_start[b];
+    const int q_len = a.query_start[b + 1] - q0;
+    // A malformed query range has no rows that can be written safely.
+    if (q0 < 0 || q_len < 0 || q_len > a.max_query_len || q0 > a.num_tokens - q_len)
+        return;
+    const int p_lo = qt * a.q_tile;
+    if (p_lo >= q_len)
+        return;
+    const int ctx = a.context_lens[b];
+    const bool bad_ctx = ctx < 0 || ctx > a.max_context_len ||
+                         (ctx + kBlock - 1) / kBlock > a.max_blocks;
+    const int n_here = min(a.q_tile, q_len - p_lo);      // query positions in this tile
+    const int first = ctx - q_len + p_lo;                // position of the tile's first
+    const int key_end = bad_ctx ? 0 : max(0, first + n_here);   // keys [0, key_end)
+    const int nsteps = (key_end + 31) / 32;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r16 = lane & 15;
+    const int g = lane >> 4;
+
+    // ---- this lane's rows: q fragments, positions, output offsets
+    const uint16_t *qp = static_cast<const uint16_t *>(a.q);
+    u32x4 qf[C][NKC];
+    int pos[C];
+    int orow[C];                             // q-row * Hq + head, or -1 for an idle row
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        const int row = (wave * C + c) * 16 + r16;
+        const int lp = row / a.group;
+        const int hh = row - lp * a.group;
+        const bool ok = lp < n_here;
+        orow[c] = ok ? (q0 + p_lo + lp) * a.num_q_heads + kvh * a.group + hh : -1;
+        pos[c] = ok ? first + lp : INT_MIN / 2;
+        const uint16_t *qrow = qp + (size_t)(ok ? orow[c] : 0) * D;
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc)
+            qf[c][kc] = ok ? *reinterpret_cast<const u32x4 *>(qrow + 32 * kc + 8 * g)
+                           : u32x4{0u, 0u, 0u, 0u};
+    }
+
+    const Elem *kbase = static_cast<const Elem *>(a.k_pool) + (size_t)kvh * kBlock * D;
+    const Elem *vbase = static_cast<const Elem *>(a.v_pool) + (size_t)kvh * kBlock * D;
+    const size_t blk_stride = (size_t)a.num_kv_heads * kBlock * D;
+    const int32_t *trow = a.block_tables + (size_t)b * a.max_blocks;
+    bool bad = false;
+
+    // ---- global -> registers for step s (blocks 2s, 2s+1); blocks past key_end are
+    // not read (their table entries may be padding) and stage as zeros
+    u32x4 kreg[KPT], vreg[VPT];
+    auto fetch = [&](int s) {
+        int ph[2];
+#pragma unroll
+        for (int tl = 0; tl < 2; ++tl) {
+            const int lb = 2 * s + tl;
+            ph[tl] = -1;
+            if (lb * kBlock < key_end) {
+                int p = trow[lb];
+                if ((unsigned)p >= (unsigned)a.num_blocks) {   // never read outside the pool
+                    bad = true;
+                    p = 0;
+                }
+                ph[tl] = p;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+            const int q = tid + i * NT;
+            kreg[i] = u32x4{0u, 0u, 0u, 0u};
+            if (KCH % NT == 0 || q < KCH) {
+                const int tl = q / (KCH / 2);
+                const int rem = q - tl * (KCH / 2);
+                const int tok = rem % kBlock;
+                const int ch = rem / kBlock;
+                if (ph[tl] >= 0)
+                    kreg[i] = *reinterpret_cast<const u32x4 *>(
+                        kbase + (size_t)ph[tl] * blk_stride + tok * D + ch * EPP);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            const int q = tid + i * NT;
+            vreg[i] = u32x4{0u, 0u, 0u, 0u};
+            if (VCH % NT == 0 || q < VCH) {
+                const int tl = q / (VCH / 2);
+                const int rem = q - tl * (VCH / 2);
+                constexpr int PPR = kBlock / EPP;           // pieces per V^T row
+                const int half = rem % PPR;
+                const int d = rem / PPR;
+                if (ph[tl] >= 0)
+                    vreg[i] = *reinterpret_cast<const u32x4 *>(
+                        vbase + (size_t)ph[tl] * blk_stride + d * kBlock + half * EPP);
+            }
+        }
+    };
+
+    // ---- registers -> LDS buffer, in fragment order; V^T entries of tokens past the
+    // context are zeroed (those rows may hold anything, NaN included, and a zero weight
+    // alone would not cancel them)
+    auto stash = [&](int s, int buf) {
+        u32x2 *sv = reinterpret_cast<u32x2 *>(s_v[buf]);
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+            const int q = tid + i * NT;
+            if (KCH % NT == 0 || q < KCH) {
+                const int tl = q / (KCH / 2);
+                const int rem = q - tl * (KCH / 2);
+                const int tok = rem % kBlock;
+                const int ch = rem / kBlock;
+                if constexpr (DT == DT_FP8) {
+                    const u32x4 w = kreg[i];
+                    const u32x4 lo = {fp8x2_to_16<AT, false>(w[0]), fp8x2_to_16<AT, true>(w[0]),
+                                      fp8x2_to_16<AT, false>(w[1]), fp8x2_to_16<AT, true>(w[1])};
+                    const u32x4 hi = {fp8x2_to_16<AT, false>(w[2]), fp8x2_to_16<AT, true>(w[2]),
+                                      fp8x2_to_16<AT, false>(w[3]), fp8x2_to_16<AT, true>(w[3])};
+                    const int c0 = 2 * ch, c1 = 2 * ch + 1;   // 8-element chunks
+                    s_k[buf][(tl * NKC + c0 / 4) * kWave + tok + 16 * (c0 % 4)] = lo;
+                    s_k[buf][(tl * NKC + c1 / 4) * kWave + tok + 16 * (c1 % 4)] = hi;
+                } else {
+                    s_k[buf][(tl * NKC + ch / 4) * kWave + tok + 16 * (ch % 4)] = kreg[i];
+                }
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            const int q = tid + i * NT;
+            if (VCH % NT == 0 || q < VCH) {
+                const int tl = q / (VCH / 2);
+                const int rem = q - tl * (VCH / 2);
+                constexpr int PPR = kBlock / EPP;
+                const int half = rem % PPR;
+                const int d = rem / PPR;
+                const int t0 = (2 * s + tl) * kBlock + half * EPP;   // first token held
+                const int base = (d / 16) * kWave + (d % 16);
+                if constexpr (DT == DT_FP8) {
+                    u32x4 w = vreg[i];
+                    if (t0 + 16 > ctx)
+                        w = keep_tokens8(w, t0, ctx);
+#pragma unroll
+                    for (int gq = 0; gq < 4; ++gq)
+                        sv[(base + 16 * gq) * 2 + tl] =
+                            u32x2{fp8x2_to_16<AT, false>(w[gq]), fp8x2_to_16<AT, true>(w[gq])};
+                } else {
+                    u32x4 w = vreg[i];
+                    if (t0 + 8 > ctx)
+                        w = keep_tokens16(w, t0, ctx);
+                    sv[(base + 16 * (2 * half)) * 2 + tl] = u32x2{w[0], w[1]};
+                    sv[(base + 16 * (2 * half + 1)) * 2 + tl] = u32x2{w[2], w[3]};
+                }
+            }
+        }
+    };
+
+    // ---- running state per column block
+    f32x4 o[C][NDB];
+    f32x4 lacc[C];
+    float m_run[C];
+    float mneg[C];                           // -m_run * scale_log2 (0 while m_run = -inf)
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+#pragma unroll
+        for (int n = 0; n < NDB; ++n)
+            o[c][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+        lacc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+        m_run[c] = -INFINITY;
+        mneg[c] = 0.f;
+    }
+    const float sl = a.scale_log2;           // > 0 (host-checked): max commutes with it
+    const u32x4 ones = {one_pair<AT>(), one_pair<AT>(), one_pair<AT>(), one_pair<AT>()};
+
+    auto compute = [&](int s, int buf) {
+        f32x4 sc[C][2];
+#pragma unroll
+        for (int c = 0; c < C; ++c)
+            sc[c][0] = sc[c][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int tl = 0; tl < 2; ++tl)
+#pragma unroll
+            for (int kc = 0; kc < NKC; ++kc) {
+                const u32x4 kf = s_k[buf][(tl * NKC + kc) * kWave + lane];
+#pragma unroll
+                for (int c = 0; c < C; ++c)
+                    sc[c][tl] = mma32<AT>(kf, qf[c][kc], sc[c][tl]);
+            }
+        // keys after a row's position are masked; only steps reaching past the tile's
+        // first position can hold such keys
+        const bool diag = 32 * s + 31 > first;
+        u32x4 pb[C];
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            if (diag) {
+#pragma unroll
+                for (int tl = 0; tl < 2; ++tl)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        sc[c][tl][j] = (32 * s + 16 * tl + 4 * g + j <= pos[c]) ? sc[c][tl][j]
+                                                                                : -INFINITY;
+            }
+            const float lmx = fmaxf(fmaxf(fmaxf(sc[c][0][0], sc[c][0][1]),
+                                          fmaxf(sc[c][0][2], sc[c][0][3])),
+                                    fmaxf(fmaxf(sc[c][1][0], sc[c][1][1]),
+                                          fmaxf(sc[c][1][2], sc[c][1][3])));
+            // The rescale is skipped when no lane's max grows: its factor would be 1.
+            if (__any(lmx > m_run[c])) {
+                const float m_new = fmaxf(m_run[c], max_over_row_groups(lmx));
+                const float alpha = (m_new == -INFINITY) ? 1.f : exp2_fast((m_run[c] - m_new) * sl);
+#pragma unroll
+                for (int n = 0; n < NDB; ++n)
+                    o[c][n] *= alpha;
+                lacc[c] *= alpha;
+                m_run[c] = m_new;
+                mneg[c] = (m_new == -INFINITY) ? 0.f : -m_new * sl;
+            }
+            f32x4 p0, p1;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                p0[j] = exp2_fast(fmaf(sc[c][0][j], sl, mneg[c]));
+                p1[j] = exp2_fast(fmaf(sc[c][1][j], sl, mneg[c]));
+            }
+            pb[c] = pack8<AT>(p0, p1);
+        }
+#pragma unroll
+        for (int n = 0; n < NDB; ++n) {
+            const u32x4 vf = s_v[buf][n * kWave + lane];
+#pragma unroll
+            for (int c = 0; c < C; ++c)
+                o[c][n] = mma32<AT>(vf, pb[c], o[c][n]);
+        }
+#pragma unroll
+        for (int c = 0; c < C; ++c)
+            lacc[c] = mma32<AT>(ones, pb[c], lacc[c]);
+    };
+
+    if (nsteps > 0) {
+        fetch(0);
+        stash(0, 0);
+    }
+    __syncthreads();
+    for (int s = 0; s < nsteps; ++s) {
+        const int buf = s & 1;
+        if (s + 1 < nsteps)
+            fetch(s + 1);
+        compute(s, buf);
+        if (s + 1 < nsteps)
+            stash(s + 1, buf ^ 1);
+        __syncthreads();
+    }
+
+    const bool any_bad = __syncthreads_or(bad ? 1 : 0) != 0 || bad_ctx;
+    const float qnan = __builtin_nanf("");
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        if (orow[c] < 0)
+            continue;
+        const float l = lacc[c][0];
+        const float f = l > 0.f ? a.v_scale / l : 0.f;
+#pragma unroll
+        for (int n = 0; n < NDB; ++n) {
+            f32x4 v = o[c][n] * f;
+            if (any_bad)
+                v = f32x4{qnan, qnan, qnan, qnan};
+            uint16_t *dst = static_cast<uint16_t *>(a.out) + (size_t)orow[c] * D + 16 * n + 4 * g;
+            if constexpr (AT == DT_BF16)
+                *reinterpret_cast<bf16x4 *>(dst) = __builtin_convertvector(v, bf16x4);
+            else
+                *reinterpret_cast<f16x4 *>(dst) = __builtin_convertvector(v, f16x4);
+        }
+    }
+}
+
+template <int DT, int AT, int D>
+hipError_t launch_prefill_t(const PrefillArgs &a, int grid, hipStream_t stream)
+{
+    hipLaunchKernelGGL((pa_prefill_kernel<DT, AT, D, kPrefillWaves, kPrefillCols>), dim3(grid),
+                       dim3(kPrefillWaves * kWave), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+int prefill_rows_per_group() { return kPrefillWaves * kPrefillCols * 16; }
+
+hipError_t launch_prefill(int dtype, int act_dtype, int head_dim, const PrefillArgs &a,
+                          hipStream_t stream)
+{
+    const int pairs = a.num_seqs * a.num_kv_heads;
+    const int grid = (pairs + kXcds - 1) / kXcds * kXcds * a.num_qtiles;
+#define PA_PF_CASE(DT, AT, D)                                                      \
+    if (dtype == DT && act_dtype == AT && head_dim == D)                          \
+        return launch_prefill_t<DT, AT, D>(a, grid, stream);
+    PA_PF_CASE(DT_BF16, DT_BF16, 128)
+    PA_PF_CASE(DT_BF16, DT_BF16, 64)
+    PA_PF_CASE(DT_F16, DT_F16, 128)
+    PA_PF_CASE(DT_F16, DT_F16, 64)
+    PA_PF_CASE(DT_FP8, DT_BF16, 128)
+    PA_PF_CASE(DT_FP8, DT_BF16, 64)
+    PA_PF_CASE(DT_FP8, DT_F16, 128)
+    PA_PF_CASE(DT_FP8, DT_F16, 64)
+#undef PA_PF_CASE
+    return hipErrorInvalidValue;
+}
+
+}  // namespace pa

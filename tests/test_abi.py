@@ -22,7 +22,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("pa_cache_append", "pa_decode", "pa_decode_workspace_bytes",
-              "pa_decode_partition_tokens", "pa_pool_bytes", "pa_status_string"):
+              "pa_decode_partition_tokens", "pa_pool_bytes", "pa_status_string", "pa_prefill",
+              "pa_copy_blocks", "pa_seq_reserve", "pa_seq_fork", "pa_seq_truncate"):
         assert n in names
 
 
@@ -96,6 +97,37 @@ def test_decode_rejects_bad_arguments(lib):
     assert _decode(lib, _pool(), ptok=32) == wsp
     assert _decode(lib, _pool(), ptok=32, ws=FAKE, ws_bytes=need - 1) == wsp
     assert _decode(lib, _pool(), num_seqs=0) == 0               # nothing to do
+
+
+def _prefill(lib, pool, num_seqs=2, hq=4, scale=0.125, qs=FAKE, T=10, maxq=8, bt=FAKE, maxb=8,
+             cl=FAKE, max_ctx=100, q=FAKE, out=FAKE):
+    return lib.pa_prefill(ctypes.byref(pool) if pool is not None else None, q, out, num_seqs,
+                          hq, ctypes.c_float(scale), qs, T, maxq, bt, maxb, cl, max_ctx, None)
+
+
+def test_prefill_rejects_bad_arguments(lib):
+    inval, unsup = 1, 2
+    assert _prefill(lib, None) == inval
+    assert _prefill(lib, _pool(k_pool=None)) == inval
+    assert _prefill(lib, _pool(dtype=B.PA_F32)) == unsup        # 16-bit MFMA path only
+    assert _prefill(lib, _pool(head_dim=256)) == unsup
+    assert _prefill(lib, _pool(), hq=3) == inval                 # 3 % 2 != 0
+    assert _prefill(lib, _pool(), hq=2 * 512) == unsup           # group above 256 rows
+    for bad in (0.0, -0.125, float("nan"), float("inf")):
+        assert _prefill(lib, _pool(), scale=bad) == inval
+    assert _prefill(lib, _pool(), num_seqs=-1) == inval
+    assert _prefill(lib, _pool(), T=-1) == inval
+    assert _prefill(lib, _pool(), maxq=-1) == inval
+    assert _prefill(lib, _pool(), max_ctx=-1) == inval
+    assert _prefill(lib, _pool(), qs=None) == inval
+    assert _prefill(lib, _pool(), bt=None) == inval
+    assert _prefill(lib, _pool(), q=None) == inval
+    assert _prefill(lib, _pool(), maxb=0) == inval
+    assert _prefill(lib, _pool(), T=1 << 30, hq=4) == unsup     # rows x heads past int32
+    assert _prefill(lib, _pool(), T=0) == 0                     # nothing to do
+    assert _prefill(lib, _pool(), num_seqs=0) == 0
+    fp8 = dict(dtype=B.PA_FP8_E4M3, act_dtype=B.PA_BF16, k_scale=0.01, v_scale=0.0)
+    assert _prefill(lib, _pool(**fp8)) == inval
 
 
 def test_append_rejects_bad_arguments(lib):

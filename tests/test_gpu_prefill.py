@@ -1,0 +1,212 @@
+"""GPU parity of paged prefill (pa_prefill through the C ABI) against the fp64 oracle.
+
+Small workloads are compared on every output; the two full-size prefill workloads
+(16 x 512-token chunks over 4096-token contexts, and a mixed prefill + decode batch)
+on sampled query rows, each of which the oracle computes as its own one-row chunk.
+Bars as for decode: max |err| <= 2e-2 and mean <= 5e-3 for 16-bit activations; the
+appended pools are compared bit for bit.  Pools are NaN-poisoned outside live rows.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from paged_kv_cache_161_amd import binding as PA
+from paged_kv_cache_161_amd import workloads as W
+from tests import devutil as U
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def hip_library():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    PA.load()
+
+
+SMALL = [
+    W.Spec("pf_prompt_bf16_d64", "bf16", 8, 2, 64, [1, 17, 45, 300], seed=31, spare_blocks=2,
+           query_lens=[1, 17, 45, 300]),
+    W.Spec("pf_chunk_f16_d128", "f16", 6, 3, 128, [33, 40, 9, 530], seed=32, spare_blocks=1,
+           query_lens=[5, 16, 9, 200]),
+    W.Spec("pf_gqa8_bf16", "bf16", 64, 8, 128, [700, 40, 3, 0, 129], seed=33, spare_blocks=1,
+           query_lens=[300, 40, 5, 0, 64]),
+    W.Spec("pf_mha_f16_d64", "f16", 32, 32, 64, [300, 257], seed=34, spare_blocks=1,
+           query_lens=[300, 1]),
+    W.Spec("pf_g32_bf16", "bf16", 64, 2, 128, [100, 33], seed=35, spare_blocks=1,
+           query_lens=[20, 33]),
+    W.Spec("pf_fp8_bf16", "bf16", 8, 2, 128, [30, 47, 260], seed=36, spare_blocks=1,
+           kv_dtype="fp8", k_scale=0.0117, v_scale=0.0093, query_lens=[30, 12, 100]),
+    W.Spec("pf_fp8_f16_d64", "f16", 16, 1, 64, [77, 160], seed=37, spare_blocks=1,
+           kv_dtype="fp8", k_scale=0.25, v_scale=0.0625, query_lens=[77, 33]),
+]
+
+
+def oracle_pools(w):
+    kp, vp, bt, sl = w.oracle_view()
+    kp, vp = O.cache_append(kp, vp, w.k_new, w.v_new, sl, w.kv_dtype, act_dtype=w.dtype,
+                            k_scale=w.k_scale, v_scale=w.v_scale)
+    return kp, vp, bt
+
+
+def gpu_prefill(w, pools=None):
+    """Append the chunks, then prefill, on the GPU; returns (out fp64, k_pool, v_pool)."""
+    kp, vp = pools if pools is not None else U.device_pools(w)
+    d = U.device_inputs(w)
+    PA.cache_append(kp, vp, d["k_new"], d["v_new"], d["slot_mapping"], **U.scales(w))
+    qs = torch.from_numpy(w.query_start).cuda()
+    out = PA.prefill(d["q"], kp, vp, qs, d["block_tables"], d["context_lens"], float(w.scale),
+                     w.max_context_len, w.max_query_len, **U.scales(w))
+    torch.cuda.synchronize()
+    return U.widen(U.from_dev(out, w.dtype), w.dtype), kp, vp
+
+
+def oracle_rows(w, kp, vp, bt, rows):
+    """Oracle output of the given q rows, each as a chunk of one query over its prefix."""
+    rows = np.asarray(rows)
+    owner = np.searchsorted(w.query_start, rows, side="right") - 1
+    q_len = np.diff(w.query_start)[owner]
+    pos = w.context_lens[owner] - q_len + (rows - w.query_start[owner])
+    ctx = np.maximum(pos + 1, 0).astype(np.int32)
+    out, _ = O.prefill_paged(np.ascontiguousarray(w.q[rows]), kp, vp, w.kv_dtype,
+                             np.arange(rows.size + 1, dtype=np.int32),
+                             np.ascontiguousarray(bt[owner]), ctx, w.scale, q_dtype=w.dtype,
+                             k_scale=w.k_scale, v_scale=w.v_scale)
+    return out
+
+
+@pytest.mark.parametrize("spec", SMALL, ids=lambda s: s.name)
+def test_prefill_small(spec):
+    say(f"[prefill] {spec.name}")
+    w = W.build(spec)
+    kpo, vpo, bt = oracle_pools(w)
+    ref, _ = O.prefill_paged(w.q, kpo, vpo, w.kv_dtype, w.query_start, bt, w.context_lens,
+                             w.scale, q_dtype=w.dtype, k_scale=w.k_scale, v_scale=w.v_scale)
+    got, kd, vd = gpu_prefill(w)
+    # the append went to the same rows (relabelled) bit for bit
+    idx = torch.from_numpy(w.live_blocks).cuda()
+    assert U.from_dev(kd[idx], w.kv_dtype).tobytes() == kpo[:-1].tobytes()
+    assert U.from_dev(vd[idx], w.kv_dtype).tobytes() == vpo[:-1].tobytes()
+    assert np.isfinite(got).all()
+    ok, mx, mean = U.tolerance_ok(got, ref, w.dtype)
+    say(f"  max {mx:.3e} mean {mean:.3e}")
+    assert ok, (mx, mean)
+    # queries placed before the context get exact zeros
+    for b in range(w.num_seqs):
+        n = int(w.query_start[b + 1] - w.query_start[b])
+        empty = max(0, n - int(w.context_lens[b]))
+        if empty:
+            r0 = int(w.query_start[b])
+            assert np.all(got[r0:r0 + empty] == 0.0)
+
+
+def sample_rows(w, per_seq=3, seed=0):
+    r = np.random.Generator(np.random.PCG64(seed))
+    rows = []
+    for b in range(w.num_seqs):
+        lo, hi = int(w.query_start[b]), int(w.query_start[b + 1])
+        if hi == lo:
+            continue
+        rows += [lo, hi - 1]
+        rows += r.integers(lo, hi, size=per_seq).tolist()
+    return np.unique(np.asarray(rows))
+
+
+@pytest.mark.parametrize("cfg", [7, 8])
+def test_prefill_full_size_sampled(cfg):
+    say(f"[prefill] config {cfg} (full size, sampled rows)")
+    w = W.make_config(cfg)
+    got, _, _ = gpu_prefill(w)
+    assert np.isfinite(got).all()
+    kpo, vpo, bt = oracle_pools(w)
+    rows = sample_rows(w, per_seq=2 if cfg == 8 else 3, seed=cfg)
+    ref = oracle_rows(w, kpo, vpo, bt, rows)
+    ok, mx, mean = U.tolerance_ok(got[rows], ref, w.dtype)
+    say(f"  {rows.size} rows: max {mx:.3e} mean {mean:.3e}")
+    assert ok, (mx, mean)
+
+
+def test_prefill_chunk_by_chunk_equals_whole_prompt():
+    """Append + prefill a 200-token prompt in chunks of 64 on the GPU; every chunk's
+    rows match the oracle's one-pass prefill of the whole prompt."""
+    spec = W.Spec("pf_loop", "bf16", 16, 2, 128, [200, 131], seed=38, spare_blocks=1,
+                  query_lens=[200, 131])
+    w = W.build(spec)
+    kpo, vpo, bt = oracle_pools(w)
+    ref, _ = O.prefill_paged(w.q, kpo, vpo, w.kv_dtype, w.query_start, bt, w.context_lens,
+                             w.scale, q_dtype=w.dtype)
+    kd, vd = U.device_pools(w)
+    d = U.device_inputs(w)
+    got = np.full(ref.shape, np.nan)
+    for b in range(w.num_seqs):
+        r0, n = int(w.query_start[b]), int(w.query_start[b + 1] - w.query_start[b])
+        for s0 in range(0, n, 64):
+            s1 = min(n, s0 + 64)
+            rows = slice(r0 + s0, r0 + s1)
+            PA.cache_append(kd, vd, d["k_new"][rows], d["v_new"][rows], d["slot_mapping"][rows])
+            out = PA.prefill(d["q"][rows].contiguous(), kd, vd,
+                             torch.tensor([0, s1 - s0], dtype=torch.int32, device="cuda"),
+                             d["block_tables"][b:b + 1].contiguous(),
+                             torch.tensor([s1], dtype=torch.int32, device="cuda"),
+                             float(w.scale), s1, s1 - s0)
+            torch.cuda.synchronize()
+            got[rows] = U.widen(U.from_dev(out, w.dtype), w.dtype)
+    ok, mx, mean = U.tolerance_ok(got, ref, w.dtype)
+    say(f"[prefill] chunk loop: max {mx:.3e} mean {mean:.3e}")
+    assert ok, (mx, mean)
+
+
+def test_prefill_bad_table_entry_and_length_poison_only_their_sequence():
+    spec = W.Spec("pf_bad", "bf16", 16, 2, 128, [90, 60, 50], seed=39, spare_blocks=1,
+                  query_lens=[30, 60, 10])
+    w = W.build(spec)
+    kpo, vpo, bt = oracle_pools(w)
+    ref, _ = O.prefill_paged(w.q, kpo, vpo, w.kv_dtype, w.query_start, bt, w.context_lens,
+                             w.scale, q_dtype=w.dtype)
+    kd, vd = U.device_pools(w)
+    d = U.device_inputs(w)
+    PA.cache_append(kd, vd, d["k_new"], d["v_new"], d["slot_mapping"])
+    tables = d["block_tables"].clone()
+    tables[0, 2] = w.num_blocks + 5                # sequence 0 reads a bad id
+    ctx = d["context_lens"].clone()
+    ctx[2] = w.max_context_len + 7                 # sequence 2 exceeds the stated bound
+    out = PA.prefill(d["q"], kd, vd, torch.from_numpy(w.query_start).cuda(), tables, ctx,
+                     float(w.scale), w.max_context_len, w.max_query_len)
+    torch.cuda.synchronize()
+    got = U.widen(U.from_dev(out, w.dtype), w.dtype)
+    qs = w.query_start
+    # sequence 0: rows whose keys reach block 2 (positions >= 32) are NaN
+    pos0 = w.context_lens[0] - (qs[1] - qs[0]) + np.arange(qs[1] - qs[0])
+    assert np.isnan(got[qs[0]:qs[1]][pos0 >= 32]).all()
+    assert np.isnan(got[qs[2]:qs[3]]).all()
+    ok, mx, mean = U.tolerance_ok(got[qs[1]:qs[2]], ref[qs[1]:qs[2]], w.dtype)
+    assert ok, (mx, mean)
+
+
+def test_prefill_rejects_unsupported_and_invalid():
+    kp = torch.zeros((4, 1, 16, 64), dtype=torch.float32, device="cuda")
+    vp = torch.zeros((4, 1, 64, 16), dtype=torch.float32, device="cuda")
+    q = torch.zeros((3, 2, 64), dtype=torch.float32, device="cuda")
+    qs = torch.tensor([0, 3], dtype=torch.int32, device="cuda")
+    bt = torch.zeros((1, 4), dtype=torch.int32, device="cuda")
+    cl = torch.tensor([3], dtype=torch.int32, device="cuda")
+    with pytest.raises(PA.PaError) as e:
+        PA.prefill(q, kp, vp, qs, bt, cl, 0.125, 3, 3)
+    assert e.value.status == 2                     # fp32 pools: unsupported
+    kp16, vp16, q16 = kp.to(torch.bfloat16), vp.to(torch.bfloat16), q.to(torch.bfloat16)
+    for bad_scale in (0.0, -0.125, float("inf")):
+        with pytest.raises(PA.PaError) as e:
+            PA.prefill(q16, kp16, vp16, qs, bt, cl, bad_scale, 3, 3)
+        assert e.value.status == 1
+    # no query rows: a no-op that writes nothing
+    out = torch.full((0, 2, 64), 7.0, dtype=torch.bfloat16, device="cuda")
+    PA.prefill(q16[:0], kp16, vp16, torch.tensor([0, 0], dtype=torch.int32, device="cuda"),
+               bt, cl, 0.125, 3, 0, out=out)
+    torch.cuda.synchronize()
