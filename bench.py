@@ -33,6 +33,8 @@ LAYERS = 4
 W_ELEM = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}
 CALIBRATION_BYTES = 256 << 20
 HEADLINE = 3
+PREFILL_HEADLINE = 7
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 / f16
 
 
 def log(msg):
@@ -44,15 +46,17 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=HEADLINE,
-                    help="workload id 1..6 (default: the Llama-70B GQA headline; 6 is the "
-                         "same shape with an FP8 E4M3 KV cache)")
+    ap.add_argument("--config", type=int, default=None,
+                    help="workload id 1..8 (default: the Llama-70B GQA decode headline for "
+                         "step / copy_blocks, the 512-token chunked prefill (7) for "
+                         "prefill; 6 is the decode shape with an FP8 E4M3 KV cache)")
     ap.add_argument("--partition-tokens", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--roofline-launches", type=int, default=100)
-    ap.add_argument("--op", choices=["step", "copy_blocks"], default="step",
+    ap.add_argument("--op", choices=["step", "copy_blocks", "prefill"], default="step",
                     help="step: the decode step (default); copy_blocks: the copy-on-write "
-                         "block copy on the workload's pool")
+                         "block copy on the workload's pool; prefill: append + paged "
+                         "prefill of prompt chunks")
     ap.add_argument("--calibrate", action="store_true",
                     help="also run one 256 MiB device copy (a kernel of known traffic for "
                          "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
@@ -148,6 +152,173 @@ def bench_copy_blocks(args, w, PA, U, dev):
     }), flush=True)
 
 
+def calibration_copy(dev):
+    """One device copy of known size: rocprofv3's FETCH_SIZE / WRITE_SIZE readings of
+    it scale the kernel's readings to bytes."""
+    src = torch.ones(CALIBRATION_BYTES // 2, dtype=torch.int16, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"[bench] calibration copy: {CALIBRATION_BYTES} bytes read, {CALIBRATION_BYTES} "
+        "written")
+    del src, dst
+
+
+def prefill_flops(w):
+    """Algorithmic FLOPs of a prefill call: per (query row, q-head, attended key) one
+    d-long dot product for the score and one d-long axpy into the output, 2 FLOPs per
+    multiply-add."""
+    return 4 * w.head_dim * w.num_q_heads * w.attended_keys()
+
+
+def prefill_recorded_traffic(workload):
+    """HBM bytes per prefill launch from committed rocprofv3 counter passes, or None
+    unless they were taken on this exact kernel source."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "pa_prefill_counters.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except OSError:
+        return None
+    h = hashlib.sha256()
+    for f in ("pa_prefill.hip", "pa_common.h"):
+        with open(os.path.join(ROOT, "paged_kv_cache_161_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    entry = rec.get("workloads", {}).get(workload)
+    if not entry or rec.get("kernel_source_sha256") != h.hexdigest():
+        return None
+    return entry["traffic_bytes_per_launch"]
+
+
+def prefill_oracle_rows(w, rows, threads=None):
+    """The oracle on the given q rows of a prefill workload, each as a one-row chunk
+    over its own prefix (the causal definition); returns (out, seconds)."""
+    import oracle as O
+    kp, vp, bt, sl = w.oracle_view()
+    kp, vp = O.cache_append(kp, vp, w.k_new, w.v_new, sl, w.kv_dtype, act_dtype=w.dtype,
+                            k_scale=w.k_scale, v_scale=w.v_scale)
+    owner = np.searchsorted(w.query_start, rows, side="right") - 1
+    q_len = np.diff(w.query_start)[owner]
+    pos = w.context_lens[owner] - q_len + (rows - w.query_start[owner])
+    ctx = np.maximum(pos + 1, 0).astype(np.int32)
+    q = np.ascontiguousarray(w.q[rows])
+    t0 = time.perf_counter()
+    out, _ = O.prefill_paged(q, kp, vp, w.kv_dtype, np.arange(rows.size + 1, dtype=np.int32),
+                             np.ascontiguousarray(bt[owner]), ctx, w.scale,
+                             threads=threads or O.default_threads(), q_dtype=w.dtype,
+                             k_scale=w.k_scale, v_scale=w.v_scale)
+    return out, time.perf_counter() - t0, int(ctx.astype(np.int64).sum())
+
+
+def bench_prefill(args, w, PA, U, dev):
+    """One step = pa_cache_append of the chunks' K/V rows + pa_prefill of the chunks'
+    queries, one layer; four layer pools cycled as in the decode step."""
+    assert w.is_prefill, "--op prefill needs a prefill workload (7 or 8)"
+    pools = [U.device_pools(w, dev) for _ in range(LAYERS)]
+    d = U.device_inputs(w, dev)
+    qs = torch.from_numpy(w.query_start).to(dev)
+    out = torch.empty_like(d["q"])
+    sc = U.scales(w)
+    scale, max_ctx, max_q = float(w.scale), w.max_context_len, w.max_query_len
+    flops = prefill_flops(w)
+    n_tok = w.num_query_tokens
+
+    def prefill(i):
+        kp, vp = pools[i % LAYERS]
+        PA.prefill(d["q"], kp, vp, qs, d["block_tables"], d["context_lens"], scale, max_ctx,
+                   max_q, out=out, **sc)
+
+    def step(i):
+        kp, vp = pools[i % LAYERS]
+        PA.cache_append(kp, vp, d["k_new"], d["v_new"], d["slot_mapping"], **sc)
+        prefill(i)
+
+    if args.calibrate:
+        calibration_copy(dev)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t_start) * 1e3 / args.steps
+    log(f"[bench] {args.steps} prefill steps: {ms_per_step * 1e3:.1f} us/step")
+
+    stream = torch.cuda.current_stream(dev)
+    n_l = args.roofline_launches
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(n_l):
+        prefill(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    dur = e0.elapsed_time(e1) * 1e-3 / n_l
+    tflops = flops / dur / 1e12
+    log(f"[bench] prefill call: {dur * 1e6:.1f} us per launch over {n_l} back-to-back "
+        f"launches -> {tflops:.1f} TFLOP/s")
+
+    parity = None
+    try:
+        rows = np.unique(np.random.Generator(np.random.PCG64(1)).integers(0, n_tok, size=32))
+        ref, _, _ = prefill_oracle_rows(w, rows)
+        got = U.widen(U.from_dev(out, w.dtype), w.dtype)[rows]
+        ok, mx, mean = U.tolerance_ok(got, ref, w.dtype)
+        parity = {"rows_checked": int(rows.size), "max_abs_err": mx, "mean_abs_err": mean,
+                  "pass": bool(ok and np.isfinite(got).all())}
+        log(f"[bench] parity on timed inputs: {parity}")
+    except Exception as exc:
+        parity = {"error": repr(exc)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        rows = np.sort(np.random.Generator(np.random.PCG64(2)).choice(n_tok, size=min(512, n_tok),
+                                                                    replace=False))
+        _, t, keys = prefill_oracle_rows(w, rows)
+        import oracle as O
+        f = 4 * w.head_dim * w.num_q_heads * keys
+        cpu = {"value": round(f / t / 1e12, 6), "unit": "TFLOP/s",
+               "cores": O.default_threads(), "kind": "oracle",
+               "sample": f"{rows.size} of the {n_tok} query rows (all {w.num_q_heads} "
+                         f"q-heads), each over its causal prefix: {t:.2f} s, "
+                         f"{rows.size / t:.1f} query tokens/s"}
+        log(f"[bench] cpu baseline: {cpu}")
+
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    kv = w.logical_kv_bytes()
+    print(json.dumps({
+        "metric": "prefill-attention TFLOP/s (% of MFMA peak) and query tokens/s, 1 MI355X",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype if w.kv_dtype == w.dtype else f"{w.kv_dtype} KV, {w.dtype} q/out",
+        "data": "synthetic (seeded PCG64 normals x0.5, NaN-poisoned paged pool)",
+        "config": {"workload": f"{w.spec.name}: {w.num_seqs} seqs, {n_tok} query tokens "
+                               f"(chunks up to {max_q}), contexts up to {max_ctx}, "
+                               f"{w.num_q_heads} q / {w.num_kv_heads} kv heads, d "
+                               f"{w.head_dim}, 16-token blocks; step = append + prefill "
+                               f"of one layer",
+                   "num_seqs": w.num_seqs, "query_tokens": n_tok, "max_query_len": max_q,
+                   "max_context_len": max_ctx, "num_q_heads": w.num_q_heads,
+                   "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": 16,
+                   "parallelism": "none (1 GPU)"},
+        "query_tokens_per_s": round(n_tok / (ms_per_step * 1e-3), 1),
+        "flops_per_step": flops,
+        "kv_bytes_attended": kv,
+        "roofline": {"bound": "mfma", "kernel": "pa_prefill_kernel",
+                     "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": prefill_recorded_traffic(w.spec.name),
+                     "launch_us_mean": round(dur * 1e6, 2), "flops_per_launch": flops},
+        "cpu_baseline": cpu,
+        "parity": parity,
+    }), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -166,6 +337,8 @@ def main():
     PA.load()
     dev = torch.device("cuda:0")
     t0 = time.time()
+    if args.config is None:
+        args.config = PREFILL_HEADLINE if args.op == "prefill" else HEADLINE
     w = W.make_config(args.config)
     log(f"[bench] built {w.spec.name} in {time.time() - t0:.1f}s: B={w.num_seqs} "
         f"Hq={w.num_q_heads} Hkv={w.num_kv_heads} d={w.head_dim} "
@@ -173,6 +346,8 @@ def main():
 
     if args.op == "copy_blocks":
         return bench_copy_blocks(args, w, PA, U, dev)
+    if args.op == "prefill":
+        return bench_prefill(args, w, PA, U, dev)
 
     pools = [U.device_pools(w, dev) for _ in range(LAYERS)]
     d = U.device_inputs(w, dev)
@@ -195,14 +370,7 @@ def main():
                   out=out, workspace=ws, **sc)
 
     if args.calibrate:
-        src = torch.ones(CALIBRATION_BYTES // 2, dtype=torch.int16, device=dev)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        log(f"[bench] calibration copy: {CALIBRATION_BYTES} bytes read, {CALIBRATION_BYTES} "
-            "written")
-        del src, dst
+        calibration_copy(dev)
 
     for i in range(args.warmup):
         step(i)

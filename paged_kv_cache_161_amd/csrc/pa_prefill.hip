@@ -125,8 +125,8 @@ __device__ __forceinline__ u32x4 keep_tokens8(u32x4 v, int t0, int valid)
     return v;
 }
 
-template <int DT, int AT, int D, int NW, int C>
-__global__ __launch_bounds__(NW *kWave, 1) void pa_prefill_kernel(PrefillArgs a)
+template <int DT, int AT, int D, int NW, int C, int PF>
+__global__ __launch_bounds__(NW *kWave, (NW * C >= 16) ? 2 : 1) void pa_prefill_kernel(PrefillArgs a)
 {
     using Elem = typename std::conditional<DT == DT_FP8, uint8_t, uint16_t>::type;
     constexpr int NT = NW * kWave;
@@ -200,63 +200,68 @@ __global__ __launch_bounds__(NW *kWave, 1) void pa_prefill_kernel(PrefillArgs a)
     const Elem *kbase = static_cast<const Elem *>(a.k_pool) + (size_t)kvh * kBlock * D;
     const Elem *vbase = static_cast<const Elem *>(a.v_pool) + (size_t)kvh * kBlock * D;
     const size_t blk_stride = (size_t)a.num_kv_heads * kBlock * D;
-    const int32_t *trow = a.block_tables + (size_t)b * a.max_blocks;
+    // the table row through the constant address space: uniform reads of it stay
+    // scalar loads, whose wait does not hold up the vector loads in flight
+    typedef const __attribute__((address_space(4))) int32_t const_i32;
+    const_i32 *trow = (const_i32 *)(a.block_tables + (size_t)b * a.max_blocks);
     bool bad = false;
 
-    // ---- global -> registers for step s (blocks 2s, 2s+1); blocks past key_end are
-    // not read (their table entries may be padding) and stage as zeros
-    u32x4 kreg[KPT], vreg[VPT];
-    auto fetch = [&](int s) {
-        int ph[2];
+    // ---- block ids of step s (blocks 2s, 2s+1), read one step before their loads are
+    // issued and checked only then, so the scalar loads' latency is hidden.  Entries
+    // past key_end may be padding and are never used: such a block, and an id outside
+    // the pool, use block 0, whose rows stay in bounds and are zeroed or flagged below.
+    auto table = [&](int s, int (&raw)[2]) {
+#pragma unroll
+        for (int tl = 0; tl < 2; ++tl)
+            raw[tl] = trow[min(2 * s + tl, a.max_blocks - 1)];
+    };
+    auto resolve = [&](int s, const int (&raw)[2], int (&ph)[2]) {
 #pragma unroll
         for (int tl = 0; tl < 2; ++tl) {
-            const int lb = 2 * s + tl;
-            ph[tl] = -1;
-            if (lb * kBlock < key_end) {
-                int p = trow[lb];
-                if ((unsigned)p >= (unsigned)a.num_blocks) {   // never read outside the pool
-                    bad = true;
-                    p = 0;
-                }
-                ph[tl] = p;
-            }
+            const bool need = (2 * s + tl) * kBlock < key_end;
+            const bool in_pool = (unsigned)raw[tl] < (unsigned)a.num_blocks;
+            bad |= need && !in_pool;                  // never read outside the pool
+            ph[tl] = (need && in_pool) ? raw[tl] : 0;
         }
+    };
+
+    // ---- global -> registers for one step into ring slot `slot`.  Every call issues
+    // the same KPT + VPT loads (pieces past the step's count repeat the last one), so
+    // the number of loads in flight is fixed and each wait covers exactly the slot it
+    // needs, PF - 1 steps after the loads were issued.
+    u32x4 kreg[PF][KPT], vreg[PF][VPT];
+    auto fetch = [&](const int (&ph)[2], int slot) {
 #pragma unroll
         for (int i = 0; i < KPT; ++i) {
-            const int q = tid + i * NT;
-            kreg[i] = u32x4{0u, 0u, 0u, 0u};
-            if (KCH % NT == 0 || q < KCH) {
-                const int tl = q / (KCH / 2);
-                const int rem = q - tl * (KCH / 2);
-                const int tok = rem % kBlock;
-                const int ch = rem / kBlock;
-                if (ph[tl] >= 0)
-                    kreg[i] = *reinterpret_cast<const u32x4 *>(
-                        kbase + (size_t)ph[tl] * blk_stride + tok * D + ch * EPP);
-            }
+            const int q = min(tid + i * NT, KCH - 1);
+            const int tl = q / (KCH / 2);
+            const int rem = q - tl * (KCH / 2);
+            const int tok = rem % kBlock;
+            const int ch = rem / kBlock;
+            kreg[slot][i] = *reinterpret_cast<const u32x4 *>(
+                kbase + (size_t)ph[tl] * blk_stride + tok * D + ch * EPP);
         }
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
-            const int q = tid + i * NT;
-            vreg[i] = u32x4{0u, 0u, 0u, 0u};
-            if (VCH % NT == 0 || q < VCH) {
-                const int tl = q / (VCH / 2);
-                const int rem = q - tl * (VCH / 2);
-                constexpr int PPR = kBlock / EPP;           // pieces per V^T row
-                const int half = rem % PPR;
-                const int d = rem / PPR;
-                if (ph[tl] >= 0)
-                    vreg[i] = *reinterpret_cast<const u32x4 *>(
-                        vbase + (size_t)ph[tl] * blk_stride + d * kBlock + half * EPP);
-            }
+            const int q = min(tid + i * NT, VCH - 1);
+            const int tl = q / (VCH / 2);
+            const int rem = q - tl * (VCH / 2);
+            constexpr int PPR = kBlock / EPP;           // pieces per V^T row
+            const int half = rem % PPR;
+            const int d = rem / PPR;
+            vreg[slot][i] = *reinterpret_cast<const u32x4 *>(
+                vbase + (size_t)ph[tl] * blk_stride + d * kBlock + half * EPP);
         }
     };
 
     // ---- registers -> LDS buffer, in fragment order; V^T entries of tokens past the
     // context are zeroed (those rows may hold anything, NaN included, and a zero weight
     // alone would not cancel them)
-    auto stash = [&](int s, int buf) {
+    auto stash = [&](int s, int buf, int slot) {
         u32x2 *sv = reinterpret_cast<u32x2 *>(s_v[buf]);
+        const bool need0 = (2 * s) * kBlock < key_end;       // blocks past key_end: zeros
+        const bool need1 = (2 * s + 1) * kBlock < key_end;
+        const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
         for (int i = 0; i < KPT; ++i) {
             const int q = tid + i * NT;
@@ -265,8 +270,9 @@ __global__ __launch_bounds__(NW *kWave, 1) void pa_prefill_kernel(PrefillArgs a)
                 const int rem = q - tl * (KCH / 2);
                 const int tok = rem % kBlock;
                 const int ch = rem / kBlock;
+                const bool need = tl == 0 ? need0 : need1;
                 if constexpr (DT == DT_FP8) {
-                    const u32x4 w = kreg[i];
+                    const u32x4 w = need ? kreg[slot][i] : zero;
                     const u32x4 lo = {fp8x2_to_16<AT, false>(w[0]), fp8x2_to_16<AT, true>(w[0]),
                                       fp8x2_to_16<AT, false>(w[1]), fp8x2_to_16<AT, true>(w[1])};
                     const u32x4 hi = {fp8x2_to_16<AT, false>(w[2]), fp8x2_to_16<AT, true>(w[2]),
@@ -275,7 +281,8 @@ __global__ __launch_bounds__(NW *kWave, 1) void pa_prefill_kernel(PrefillArgs a)
                     s_k[buf][(tl * NKC + c0 / 4) * kWave + tok + 16 * (c0 % 4)] = lo;
                     s_k[buf][(tl * NKC + c1 / 4) * kWave + tok + 16 * (c1 % 4)] = hi;
                 } else {
-                    s_k[buf][(tl * NKC + ch / 4) * kWave + tok + 16 * (ch % 4)] = kreg[i];
+                    s_k[buf][(tl * NKC + ch / 4) * kWave + tok + 16 * (ch % 4)] =
+                        need ? kreg[slot][i] : zero;
                 }
             }
         }
@@ -290,8 +297,9 @@ __global__ __launch_bounds__(NW *kWave, 1) void pa_prefill_kernel(PrefillArgs a)
                 const int d = rem / PPR;
                 const int t0 = (2 * s + tl) * kBlock + half * EPP;   // first token held
                 const int base = (d / 16) * kWave + (d % 16);
+                const bool need = tl == 0 ? need0 : need1;
                 if constexpr (DT == DT_FP8) {
-                    u32x4 w = vreg[i];
+                    u32x4 w = need ? vreg[slot][i] : zero;
                     if (t0 + 16 > ctx)
                         w = keep_tokens8(w, t0, ctx);
 #pragma unroll
@@ -299,7 +307,7 @@ __global__ __launch_bounds__(NW *kWave, 1) void pa_prefill_kernel(PrefillArgs a)
                         sv[(base + 16 * gq) * 2 + tl] =
                             u32x2{fp8x2_to_16<AT, false>(w[gq]), fp8x2_to_16<AT, true>(w[gq])};
                 } else {
-                    u32x4 w = vreg[i];
+                    u32x4 w = need ? vreg[slot][i] : zero;
                     if (t0 + 8 > ctx)
                         w = keep_tokens16(w, t0, ctx);
                     sv[(base + 16 * (2 * half)) * 2 + tl] = u32x2{w[0], w[1]};
@@ -327,19 +335,31 @@ __global__ __launch_bounds__(NW *kWave, 1) void pa_prefill_kernel(PrefillArgs a)
     const u32x4 ones = {one_pair<AT>(), one_pair<AT>(), one_pair<AT>(), one_pair<AT>()};
 
     auto compute = [&](int s, int buf) {
+        // all of the step's K fragments are read before the first product, the V
+        // fragments right after the last one, so LDS latency overlaps the MFMAs and
+        // the softmax
+        u32x4 kf[2][NKC];
+#pragma unroll
+        for (int tl = 0; tl < 2; ++tl)
+#pragma unroll
+            for (int kc = 0; kc < NKC; ++kc)
+                kf[tl][kc] = s_k[buf][(tl * NKC + kc) * kWave + lane];
         f32x4 sc[C][2];
 #pragma unroll
         for (int c = 0; c < C; ++c)
             sc[c][0] = sc[c][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // e-chunk outermost: the 2 C accumulators form independent chains
 #pragma unroll
-        for (int tl = 0; tl < 2; ++tl)
+        for (int kc = 0; kc < NKC; ++kc)
 #pragma unroll
-            for (int kc = 0; kc < NKC; ++kc) {
-                const u32x4 kf = s_k[buf][(tl * NKC + kc) * kWave + lane];
+            for (int tl = 0; tl < 2; ++tl)
 #pragma unroll
                 for (int c = 0; c < C; ++c)
-                    sc[c][tl] = mma32<AT>(kf, qf[c][kc], sc[c][tl]);
-            }
+                    sc[c][tl] = mma32<AT>(kf[tl][kc], qf[c][kc], sc[c][tl]);
+        u32x4 vf[NDB];
+#pragma unroll
+        for (int n = 0; n < NDB; ++n)
+            vf[n] = s_v[buf][n * kWave + lane];
         // keys after a row's position are masked; only steps reaching past the tile's
         // first position can hold such keys
         const bool diag = 32 * s + 31 > first;
@@ -378,30 +398,48 @@ __global__ __launch_bounds__(NW *kWave, 1) void pa_prefill_kernel(PrefillArgs a)
             pb[c] = pack8<AT>(p0, p1);
         }
 #pragma unroll
-        for (int n = 0; n < NDB; ++n) {
-            const u32x4 vf = s_v[buf][n * kWave + lane];
+        for (int n = 0; n < NDB; ++n)
 #pragma unroll
             for (int c = 0; c < C; ++c)
-                o[c][n] = mma32<AT>(vf, pb[c], o[c][n]);
-        }
+                o[c][n] = mma32<AT>(vf[n], pb[c], o[c][n]);
 #pragma unroll
         for (int c = 0; c < C; ++c)
             lacc[c] = mma32<AT>(ones, pb[c], lacc[c]);
     };
 
+    // Step it computes from LDS buffer it % 2 while the loads of step it + PF are in
+    // flight; at its end step it + 1 moves from its register slot into the other
+    // buffer, and one barrier publishes it.  The loop is unrolled by PF, so every ring
+    // slot is a fixed register range, and runs whole groups of PF steps with no other
+    // exit: every pass issues the same loads and waits, so each wait covers exactly
+    // the slot it needs.  Loads past the last step are clamped to it; steps past the
+    // last stage zeros, and every key of theirs lies after every row's position, so
+    // they are masked out entirely and change nothing.
     if (nsteps > 0) {
-        fetch(0);
-        stash(0, 0);
-    }
-    __syncthreads();
-    for (int s = 0; s < nsteps; ++s) {
-        const int buf = s & 1;
-        if (s + 1 < nsteps)
-            fetch(s + 1);
-        compute(s, buf);
-        if (s + 1 < nsteps)
-            stash(s + 1, buf ^ 1);
+        int raw_next[2], ph[2];
+#pragma unroll
+        for (int u = 0; u < PF; ++u) {
+            table(min(u, nsteps - 1), raw_next);
+            resolve(min(u, nsteps - 1), raw_next, ph);
+            fetch(ph, u);
+        }
+        table(min(PF, nsteps - 1), raw_next);
+        stash(0, 0, 0);                              // waits for slot 0 and for q
         __syncthreads();
+        const int ngroups = (nsteps + PF - 1) / PF;
+        for (int grp = 0; grp < ngroups; ++grp) {
+#pragma unroll
+            for (int u = 0; u < PF; ++u) {
+                const int it = grp * PF + u;
+                const int sf = min(it + PF, nsteps - 1);   // the step loaded into slot u
+                resolve(sf, raw_next, ph);
+                fetch(ph, u);
+                table(min(it + PF + 1, nsteps - 1), raw_next);
+                compute(it, it & 1);
+                stash(it + 1, (it + 1) & 1, (u + 1) % PF);
+                __syncthreads();
+            }
+        }
     }
 
     const bool any_bad = __syncthreads_or(bad ? 1 : 0) != 0 || bad_ctx;
@@ -429,7 +467,8 @@ __global__ __launch_bounds__(NW *kWave, 1) void pa_prefill_kernel(PrefillArgs a)
 template <int DT, int AT, int D>
 hipError_t launch_prefill_t(const PrefillArgs &a, int grid, hipStream_t stream)
 {
-    hipLaunchKernelGGL((pa_prefill_kernel<DT, AT, D, kPrefillWaves, kPrefillCols>), dim3(grid),
+    hipLaunchKernelGGL((pa_prefill_kernel<DT, AT, D, kPrefillWaves, kPrefillCols, kPrefillPrefetch>),
+                       dim3(grid),
                        dim3(kPrefillWaves * kWave), 0, stream, a);
     return hipGetLastError();
 }
