@@ -183,7 +183,7 @@ def prefill_recorded_traffic(workload):
     except OSError:
         return None
     h = hashlib.sha256()
-    for f in ("pa_prefill.hip", "pa_common.h"):
+    for f in ("pa_prefill.hip", "pa_prefill.h", "pa_common.h"):
         with open(os.path.join(ROOT, "paged_kv_cache_161_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     entry = rec.get("workloads", {}).get(workload)

@@ -8,6 +8,7 @@
 
 #include "../../include/paged_attention.h"
 #include "pa_common.h"
+#include "pa_prefill.h"
 
 namespace {
 

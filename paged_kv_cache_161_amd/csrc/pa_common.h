@@ -54,48 +54,6 @@ struct AppendArgs {
     int32_t bf16;                     // fp8 pools: new rows are bf16 (else f16)
 };
 
-// Arguments of the prefill kernel.
-struct PrefillArgs {
-    const void *k_pool;               // [num_blocks][hkv][16][D]
-    const void *v_pool;               // [num_blocks][hkv][D][16]
-    const void *q;                    // [T][hq][D]
-    void *out;                        // [T][hq][D]
-    const int32_t *query_start;       // [B+1]: q rows of sequence b
-    const int32_t *block_tables;      // [B][max_blocks]
-    const int32_t *context_lens;      // [B], chunk included
-    int32_t num_seqs;
-    int32_t num_blocks;
-    int32_t num_kv_heads;
-    int32_t num_q_heads;
-    int32_t group;                    // hq / hkv
-    int32_t max_blocks;
-    int32_t max_context_len;
-    int32_t num_tokens;               // T
-    int32_t max_query_len;
-    int32_t q_tile;                   // query positions per workgroup
-    int32_t num_qtiles;               // ceil(max_query_len / q_tile)
-    float scale_log2;                 // scale * log2(e) (* k_scale for fp8 pools), > 0
-    float v_scale;
-};
-
-// Prefill workgroup shape: waves, 16-row MFMA column blocks per wave, and key steps
-// whose global loads are in flight ahead of the one being staged.
-#ifndef PA_PREFILL_WAVES
-#define PA_PREFILL_WAVES 8
-#endif
-#ifndef PA_PREFILL_COLS
-#define PA_PREFILL_COLS 2
-#endif
-#ifndef PA_PREFILL_PREFETCH
-#define PA_PREFILL_PREFETCH 2
-#endif
-constexpr int kPrefillWaves = PA_PREFILL_WAVES;
-constexpr int kPrefillCols = PA_PREFILL_COLS;
-constexpr int kPrefillPrefetch = PA_PREFILL_PREFETCH;
-
-// Query rows ((position, q-head) pairs) one prefill workgroup holds.
-int prefill_rows_per_group();
-
 // Launchers (return hipSuccess or the launch error).
 // dtype: the pools' element type; act_dtype: q / out / new rows (== dtype except for
 // fp8 pools, where it is f16 or bf16).
@@ -103,8 +61,6 @@ hipError_t launch_decode(int dtype, int act_dtype, int head_dim, const DecodeArg
                          int num_seqs, hipStream_t stream);
 hipError_t launch_append(int dtype, int act_dtype, int head_dim, const AppendArgs &a,
                          hipStream_t stream);
-hipError_t launch_prefill(int dtype, int act_dtype, int head_dim, const PrefillArgs &a,
-                          hipStream_t stream);
 hipError_t launch_copy_blocks(void *k_pool, void *v_pool, const int32_t *pairs, int32_t num_pairs,
                               int32_t num_blocks, size_t block_bytes, hipStream_t stream);
 

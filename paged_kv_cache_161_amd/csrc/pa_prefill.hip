@@ -34,6 +34,7 @@
 #include <type_traits>
 
 #include "pa_common.h"
+#include "pa_prefill.h"
 
 namespace pa {
 namespace {
