@@ -29,20 +29,15 @@ struct PrefillArgs {
     float v_scale;
 };
 
-// Prefill workgroup shape: waves, 16-row MFMA column blocks per wave, and key steps
-// whose global loads are in flight ahead of the one being staged.
+// Prefill workgroup shape: waves and 16-row MFMA column blocks per wave.
 #ifndef PA_PREFILL_WAVES
 #define PA_PREFILL_WAVES 8
 #endif
 #ifndef PA_PREFILL_COLS
 #define PA_PREFILL_COLS 2
 #endif
-#ifndef PA_PREFILL_PREFETCH
-#define PA_PREFILL_PREFETCH 2
-#endif
 constexpr int kPrefillWaves = PA_PREFILL_WAVES;
 constexpr int kPrefillCols = PA_PREFILL_COLS;
-constexpr int kPrefillPrefetch = PA_PREFILL_PREFETCH;
 
 // Query rows ((position, q-head) pairs) one prefill workgroup holds.
 int prefill_rows_per_group();

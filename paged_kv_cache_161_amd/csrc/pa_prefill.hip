@@ -58,6 +58,19 @@ __device__ __forceinline__ float max_over_row_groups(float v)
     return v;
 }
 
+// Largest of a step's 8 scores in this lane.  IEEE maximum needs no canonicalising of
+// the MFMA results (it maps onto three-input v_maximum3); the scores are never NaN
+// (finite, or -inf once masked).
+__device__ __forceinline__ float max8(const f32x4 (&x)[2])
+{
+    const float a = __builtin_elementwise_maximum(__builtin_elementwise_maximum(x[0][0], x[0][1]),
+                                                  x[0][2]);
+    const float b = __builtin_elementwise_maximum(__builtin_elementwise_maximum(x[0][3], x[1][0]),
+                                                  x[1][1]);
+    const float c = __builtin_elementwise_maximum(__builtin_elementwise_maximum(x[1][2], x[1][3]), a);
+    return __builtin_elementwise_maximum(b, c);
+}
+
 template <int AT>
 __device__ __forceinline__ f32x4 mma32(u32x4 a, u32x4 b, f32x4 c)
 {
@@ -126,7 +139,7 @@ __device__ __forceinline__ u32x4 keep_tokens8(u32x4 v, int t0, int valid)
     return v;
 }
 
-template <int DT, int AT, int D, int NW, int C, int PF>
+template <int DT, int AT, int D, int NW, int C>
 __global__ __launch_bounds__(NW *kWave, (NW * C >= 16) ? 2 : 1) void pa_prefill_kernel(PrefillArgs a)
 {
     using Elem = typename std::conditional<DT == DT_FP8, uint8_t, uint16_t>::type;
@@ -226,93 +239,106 @@ __global__ __launch_bounds__(NW *kWave, (NW * C >= 16) ? 2 : 1) void pa_prefill_
         }
     };
 
-    // ---- global -> registers for one step into ring slot `slot`.  Every call issues
-    // the same KPT + VPT loads (pieces past the step's count repeat the last one), so
-    // the number of loads in flight is fixed and each wait covers exactly the slot it
-    // needs, PF - 1 steps after the loads were issued.
-    u32x4 kreg[PF][KPT], vreg[PF][VPT];
-    auto fetch = [&](const int (&ph)[2], int slot) {
+    // ---- each thread's 16-byte pieces of a step, fixed for the whole loop: which of
+    // the step's two blocks (the same for a whole wave, kept scalar), the element
+    // offset inside that block, and the LDS fragment slot(s) it fills.  Pieces past
+    // the step's count repeat the last one (loaded, never staged).
+    int k_tl[KPT], k_off[KPT], k_slot[KPT][DT == DT_FP8 ? 2 : 1];
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+        const int q = min(tid + i * NT, KCH - 1);
+        const int tl = q / (KCH / 2);
+        const int rem = q - tl * (KCH / 2);
+        const int tok = rem % kBlock;
+        const int ch = rem / kBlock;
+        k_tl[i] = __builtin_amdgcn_readfirstlane(tl);   // KCH / 2 is a multiple of 64
+        k_off[i] = tok * D + ch * EPP;
+        if constexpr (DT == DT_FP8) {
+            const int c0 = 2 * ch, c1 = 2 * ch + 1;     // 8-element chunks
+            k_slot[i][0] = (tl * NKC + c0 / 4) * kWave + tok + 16 * (c0 % 4);
+            k_slot[i][1] = (tl * NKC + c1 / 4) * kWave + tok + 16 * (c1 % 4);
+        } else {
+            k_slot[i][0] = (tl * NKC + ch / 4) * kWave + tok + 16 * (ch % 4);
+        }
+    }
+    constexpr int PPR = kBlock / EPP;                   // pieces per V^T row
+    int v_tl[VPT], v_off[VPT], v_t0[VPT], v_slot[VPT];
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+        const int q = min(tid + i * NT, VCH - 1);
+        const int tl = q / (VCH / 2);
+        const int rem = q - tl * (VCH / 2);
+        const int half = rem % PPR;
+        const int d = rem / PPR;
+        v_tl[i] = __builtin_amdgcn_readfirstlane(tl);   // VCH / 2 is a multiple of 64
+        v_off[i] = d * kBlock + half * EPP;
+        v_t0[i] = half * EPP;                           // first token held, in the block
+        v_slot[i] = ((d / 16) * kWave + (d % 16) + 16 * (PPR == 2 ? 2 * half : 0)) * 2 + tl;
+    }
+
+    // ---- global -> registers: one step's K (or V) pieces into ring slot `slot`, from
+    // a scalar block base plus the thread's fixed offset.  Every call issues the same
+    // loads, so the number in flight is fixed and each wait covers exactly its slot.
+    u32x4 kreg[2][KPT], vreg[2][VPT];
+    auto fetch_k = [&](const int (&ph)[2], int slot) {
 #pragma unroll
         for (int i = 0; i < KPT; ++i) {
-            const int q = min(tid + i * NT, KCH - 1);
-            const int tl = q / (KCH / 2);
-            const int rem = q - tl * (KCH / 2);
-            const int tok = rem % kBlock;
-            const int ch = rem / kBlock;
-            kreg[slot][i] = *reinterpret_cast<const u32x4 *>(
-                kbase + (size_t)ph[tl] * blk_stride + tok * D + ch * EPP);
+            const Elem *blk = kbase + (size_t)(k_tl[i] ? ph[1] : ph[0]) * blk_stride;
+            kreg[slot][i] = *reinterpret_cast<const u32x4 *>(blk + k_off[i]);
         }
+    };
+    auto fetch_v = [&](const int (&ph)[2], int slot) {
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
-            const int q = min(tid + i * NT, VCH - 1);
-            const int tl = q / (VCH / 2);
-            const int rem = q - tl * (VCH / 2);
-            constexpr int PPR = kBlock / EPP;           // pieces per V^T row
-            const int half = rem % PPR;
-            const int d = rem / PPR;
-            vreg[slot][i] = *reinterpret_cast<const u32x4 *>(
-                vbase + (size_t)ph[tl] * blk_stride + d * kBlock + half * EPP);
+            const Elem *blk = vbase + (size_t)(v_tl[i] ? ph[1] : ph[0]) * blk_stride;
+            vreg[slot][i] = *reinterpret_cast<const u32x4 *>(blk + v_off[i]);
         }
     };
 
-    // ---- registers -> LDS buffer, in fragment order; V^T entries of tokens past the
-    // context are zeroed (those rows may hold anything, NaN included, and a zero weight
-    // alone would not cancel them)
-    auto stash = [&](int s, int buf, int slot) {
-        u32x2 *sv = reinterpret_cast<u32x2 *>(s_v[buf]);
-        const bool need0 = (2 * s) * kBlock < key_end;       // blocks past key_end: zeros
-        const bool need1 = (2 * s + 1) * kBlock < key_end;
-        const u32x4 zero = {0u, 0u, 0u, 0u};
+    // ---- registers -> LDS buffer, in fragment order.  K needs no clean-up: every key
+    // of a block past key_end (or past the context) lies after every row's position,
+    // so its scores are masked whatever the rows hold.  V^T entries of tokens past the
+    // context, and whole blocks past key_end, are zeroed: those rows may hold anything,
+    // NaN included, and a zero weight alone would not cancel them.  That happens only
+    // in a sequence's last steps, behind a wave-uniform test.
+    auto stash_k = [&](int buf, int slot) {
 #pragma unroll
         for (int i = 0; i < KPT; ++i) {
-            const int q = tid + i * NT;
-            if (KCH % NT == 0 || q < KCH) {
-                const int tl = q / (KCH / 2);
-                const int rem = q - tl * (KCH / 2);
-                const int tok = rem % kBlock;
-                const int ch = rem / kBlock;
-                const bool need = tl == 0 ? need0 : need1;
+            if (KCH % NT == 0 || tid + i * NT < KCH) {
                 if constexpr (DT == DT_FP8) {
-                    const u32x4 w = need ? kreg[slot][i] : zero;
-                    const u32x4 lo = {fp8x2_to_16<AT, false>(w[0]), fp8x2_to_16<AT, true>(w[0]),
-                                      fp8x2_to_16<AT, false>(w[1]), fp8x2_to_16<AT, true>(w[1])};
-                    const u32x4 hi = {fp8x2_to_16<AT, false>(w[2]), fp8x2_to_16<AT, true>(w[2]),
-                                      fp8x2_to_16<AT, false>(w[3]), fp8x2_to_16<AT, true>(w[3])};
-                    const int c0 = 2 * ch, c1 = 2 * ch + 1;   // 8-element chunks
-                    s_k[buf][(tl * NKC + c0 / 4) * kWave + tok + 16 * (c0 % 4)] = lo;
-                    s_k[buf][(tl * NKC + c1 / 4) * kWave + tok + 16 * (c1 % 4)] = hi;
+                    const u32x4 w = kreg[slot][i];
+                    s_k[buf][k_slot[i][0]] =
+                        u32x4{fp8x2_to_16<AT, false>(w[0]), fp8x2_to_16<AT, true>(w[0]),
+                              fp8x2_to_16<AT, false>(w[1]), fp8x2_to_16<AT, true>(w[1])};
+                    s_k[buf][k_slot[i][1]] =
+                        u32x4{fp8x2_to_16<AT, false>(w[2]), fp8x2_to_16<AT, true>(w[2]),
+                              fp8x2_to_16<AT, false>(w[3]), fp8x2_to_16<AT, true>(w[3])};
                 } else {
-                    s_k[buf][(tl * NKC + ch / 4) * kWave + tok + 16 * (ch % 4)] =
-                        need ? kreg[slot][i] : zero;
+                    s_k[buf][k_slot[i][0]] = kreg[slot][i];
                 }
             }
         }
+    };
+    auto stash_v = [&](int s, int buf, int slot) {
+        u32x2 *sv = reinterpret_cast<u32x2 *>(s_v[buf]);
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
-            const int q = tid + i * NT;
-            if (VCH % NT == 0 || q < VCH) {
-                const int tl = q / (VCH / 2);
-                const int rem = q - tl * (VCH / 2);
-                constexpr int PPR = kBlock / EPP;
-                const int half = rem % PPR;
-                const int d = rem / PPR;
-                const int t0 = (2 * s + tl) * kBlock + half * EPP;   // first token held
-                const int base = (d / 16) * kWave + (d % 16);
-                const bool need = tl == 0 ? need0 : need1;
+            if (VCH % NT == 0 || tid + i * NT < VCH) {
+                u32x4 w = vreg[slot][i];
+                const int blk0 = (2 * s + v_tl[i]) * kBlock;    // first token of the block
+                if (blk0 + kBlock > ctx || blk0 >= key_end) {   // wave-uniform, rare
+                    const int valid = blk0 >= key_end ? 0 : ctx - blk0;
+                    w = DT == DT_FP8 ? keep_tokens8(w, v_t0[i], valid)
+                                     : keep_tokens16(w, v_t0[i], valid);
+                }
                 if constexpr (DT == DT_FP8) {
-                    u32x4 w = need ? vreg[slot][i] : zero;
-                    if (t0 + 16 > ctx)
-                        w = keep_tokens8(w, t0, ctx);
 #pragma unroll
                     for (int gq = 0; gq < 4; ++gq)
-                        sv[(base + 16 * gq) * 2 + tl] =
+                        sv[v_slot[i] + 32 * gq] =
                             u32x2{fp8x2_to_16<AT, false>(w[gq]), fp8x2_to_16<AT, true>(w[gq])};
                 } else {
-                    u32x4 w = need ? vreg[slot][i] : zero;
-                    if (t0 + 8 > ctx)
-                        w = keep_tokens16(w, t0, ctx);
-                    sv[(base + 16 * (2 * half)) * 2 + tl] = u32x2{w[0], w[1]};
-                    sv[(base + 16 * (2 * half + 1)) * 2 + tl] = u32x2{w[2], w[3]};
+                    sv[v_slot[i]] = u32x2{w[0], w[1]};
+                    sv[v_slot[i] + 32] = u32x2{w[2], w[3]};
                 }
             }
         }
@@ -335,21 +361,19 @@ __global__ __launch_bounds__(NW *kWave, (NW * C >= 16) ? 2 : 1) void pa_prefill_
     const float sl = a.scale_log2;           // > 0 (host-checked): max commutes with it
     const u32x4 ones = {one_pair<AT>(), one_pair<AT>(), one_pair<AT>(), one_pair<AT>()};
 
-    auto compute = [&](int s, int buf) {
-        // all of the step's K fragments are read before the first product, the V
-        // fragments right after the last one, so LDS latency overlaps the MFMAs and
-        // the softmax
+    // S^T of step s from K buffer kb: all of the step's K fragments are read before
+    // the first product; the e-chunk is outermost so the 2 C accumulators form
+    // independent chains.
+    auto qk = [&](int kb, f32x4 (&sc)[C][2]) {
         u32x4 kf[2][NKC];
 #pragma unroll
         for (int tl = 0; tl < 2; ++tl)
 #pragma unroll
             for (int kc = 0; kc < NKC; ++kc)
-                kf[tl][kc] = s_k[buf][(tl * NKC + kc) * kWave + lane];
-        f32x4 sc[C][2];
+                kf[tl][kc] = s_k[kb][(tl * NKC + kc) * kWave + lane];
 #pragma unroll
         for (int c = 0; c < C; ++c)
             sc[c][0] = sc[c][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-        // e-chunk outermost: the 2 C accumulators form independent chains
 #pragma unroll
         for (int kc = 0; kc < NKC; ++kc)
 #pragma unroll
@@ -357,14 +381,14 @@ __global__ __launch_bounds__(NW *kWave, (NW * C >= 16) ? 2 : 1) void pa_prefill_
 #pragma unroll
                 for (int c = 0; c < C; ++c)
                     sc[c][tl] = mma32<AT>(kf[tl][kc], qf[c][kc], sc[c][tl]);
-        u32x4 vf[NDB];
-#pragma unroll
-        for (int n = 0; n < NDB; ++n)
-            vf[n] = s_v[buf][n * kWave + lane];
-        // keys after a row's position are masked; only steps reaching past the tile's
-        // first position can hold such keys
+    };
+
+    // Step s's scores: causal mask, running max, and the rescale of O and l when the
+    // max grows.  Only steps reaching past the tile's first position can hold keys
+    // after a row's position.  The rescale is skipped when no lane's max grows: its
+    // factor would be exactly 1.
+    auto mask_max = [&](int s, f32x4 (&sc)[C][2]) {
         const bool diag = 32 * s + 31 > first;
-        u32x4 pb[C];
 #pragma unroll
         for (int c = 0; c < C; ++c) {
             if (diag) {
@@ -375,14 +399,20 @@ __global__ __launch_bounds__(NW *kWave, (NW * C >= 16) ? 2 : 1) void pa_prefill_
                         sc[c][tl][j] = (32 * s + 16 * tl + 4 * g + j <= pos[c]) ? sc[c][tl][j]
                                                                                 : -INFINITY;
             }
-            const float lmx = fmaxf(fmaxf(fmaxf(sc[c][0][0], sc[c][0][1]),
-                                          fmaxf(sc[c][0][2], sc[c][0][3])),
-                                    fmaxf(fmaxf(sc[c][1][0], sc[c][1][1]),
-                                          fmaxf(sc[c][1][2], sc[c][1][3])));
-            // The rescale is skipped when no lane's max grows: its factor would be 1.
-            if (__any(lmx > m_run[c])) {
-                const float m_new = fmaxf(m_run[c], max_over_row_groups(lmx));
-                const float alpha = (m_new == -INFINITY) ? 1.f : exp2_fast((m_run[c] - m_new) * sl);
+        }
+        float lmx[C];
+        bool grow = false;
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            lmx[c] = max8(sc[c]);
+            grow |= lmx[c] > m_run[c];
+        }
+        if (__any(grow)) {
+#pragma unroll
+            for (int c = 0; c < C; ++c) {
+                const float m_new = fmaxf(m_run[c], max_over_row_groups(lmx[c]));
+                const float alpha =
+                    (m_new == -INFINITY) ? 1.f : exp2_fast((m_run[c] - m_new) * sl);
 #pragma unroll
                 for (int n = 0; n < NDB; ++n)
                     o[c][n] *= alpha;
@@ -390,6 +420,13 @@ __global__ __launch_bounds__(NW *kWave, (NW * C >= 16) ? 2 : 1) void pa_prefill_
                 m_run[c] = m_new;
                 mneg[c] = (m_new == -INFINITY) ? 0.f : -m_new * sl;
             }
+        }
+    };
+
+    // Weights of a masked step against the current max, rounded to 16 bits.
+    auto weights = [&](const f32x4 (&sc)[C][2], u32x4 (&pb)[C]) {
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
             f32x4 p0, p1;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -398,6 +435,10 @@ __global__ __launch_bounds__(NW *kWave, (NW * C >= 16) ? 2 : 1) void pa_prefill_
             }
             pb[c] = pack8<AT>(p0, p1);
         }
+    };
+
+    // O += V^T P and l += ones P from V buffer vb.
+    auto pv = [&](const u32x4 (&vf)[NDB], const u32x4 (&pb)[C]) {
 #pragma unroll
         for (int n = 0; n < NDB; ++n)
 #pragma unroll
@@ -408,37 +449,79 @@ __global__ __launch_bounds__(NW *kWave, (NW * C >= 16) ? 2 : 1) void pa_prefill_
             lacc[c] = mma32<AT>(ones, pb[c], lacc[c]);
     };
 
-    // Step it computes from LDS buffer it % 2 while the loads of step it + PF are in
-    // flight; at its end step it + 1 moves from its register slot into the other
-    // buffer, and one barrier publishes it.  The loop is unrolled by PF, so every ring
-    // slot is a fixed register range, and runs whole groups of PF steps with no other
-    // exit: every pass issues the same loads and waits, so each wait covers exactly
-    // the slot it needs.  Loads past the last step are clamped to it; steps past the
-    // last stage zeros, and every key of theirs lies after every row's position, so
-    // they are masked out entirely and change nothing.
+    // Two-stage pipeline over 32-key steps.  K is staged one step ahead of V.  Pass
+    // it, in one branch-free stretch, issues step it+1's QK products interleaved with
+    // step it's weights (its mask and max were settled in the previous pass), then step
+    // it's PV products; it then stages K of step it+2 and V of step it+1 into the LDS
+    // buffers those steps last used, reissues the freed register slots for K of step
+    // it+4 and V of step it+3 (two passes ahead of their staging), and after the
+    // barrier masks step it+1's scores and updates the running max.  The loop is
+    // unrolled by two, so the ring slots and the two score sets are fixed registers,
+    // and runs whole pairs of passes with no other exit: every pass issues the same
+    // loads and waits, so each wait covers exactly the slot it needs.  Loads past the
+    // last step are clamped to it; steps past the last stage zeros, and every key of
+    // theirs lies after every row's position, so they are masked out entirely and
+    // change nothing.
     if (nsteps > 0) {
-        int raw_next[2], ph[2];
-#pragma unroll
-        for (int u = 0; u < PF; ++u) {
-            table(min(u, nsteps - 1), raw_next);
-            resolve(min(u, nsteps - 1), raw_next, ph);
-            fetch(ph, u);
-        }
-        table(min(PF, nsteps - 1), raw_next);
-        stash(0, 0, 0);                              // waits for slot 0 and for q
+        const int last = nsteps - 1;
+        int raw[2], ph_a[2], ph_b[2];
+        table(0, raw);
+        resolve(0, raw, ph_a);
+        table(min(1, last), raw);
+        resolve(min(1, last), raw, ph_b);
+        fetch_k(ph_a, 0);
+        fetch_k(ph_b, 1);
+        fetch_v(ph_a, 0);
+        stash_k(0, 0);                            // waits for these loads and for q
+        stash_k(1, 1);
+        stash_v(0, 0, 0);
+        table(min(2, last), raw);
+        resolve(min(2, last), raw, ph_a);            // step 2
+        fetch_k(ph_a, 0);
+        table(min(3, last), raw);
+        int ph_k[2];                                 // block ids of the last K fetch
+        resolve(min(3, last), raw, ph_k);            // step 3
+        fetch_k(ph_k, 1);
+        fetch_v(ph_b, 1);                            // V of step 1
+        fetch_v(ph_a, 0);                            // V of step 2
+        table(min(4, last), raw);
         __syncthreads();
-        const int ngroups = (nsteps + PF - 1) / PF;
-        for (int grp = 0; grp < ngroups; ++grp) {
+        f32x4 sc[2][C][2];
+        qk(0, sc[0]);
+        mask_max(0, sc[0]);
+        const int npairs = (nsteps + 1) / 2;
+        for (int pr = 0; pr < npairs; ++pr) {
 #pragma unroll
-            for (int u = 0; u < PF; ++u) {
-                const int it = grp * PF + u;
-                const int sf = min(it + PF, nsteps - 1);   // the step loaded into slot u
-                resolve(sf, raw_next, ph);
-                fetch(ph, u);
-                table(min(it + PF + 1, nsteps - 1), raw_next);
-                compute(it, it & 1);
-                stash(it + 1, (it + 1) & 1, (u + 1) % PF);
+            for (int u = 0; u < 2; ++u) {
+                const int it = 2 * pr + u;
+                u32x4 vf[NDB];
+#pragma unroll
+                for (int n = 0; n < NDB; ++n)
+                    vf[n] = s_v[u][n * kWave + lane];
+                qk(u ^ 1, sc[u ^ 1]);
+                u32x4 pb[C];
+                weights(sc[u], pb);
+                pv(vf, pb);
+                // issue order: the K and V fragment reads, then each QK product
+                // followed by a share of the weights' vector work, then the PV products
+                __builtin_amdgcn_sched_group_barrier(0x100, 2 * NKC + NDB, 0);
+#pragma unroll
+                for (int k = 0; k < 2 * NKC * C; ++k) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, NDB * C + C, 0);
+                stash_k(u, u);
+                stash_v(it + 1, u ^ 1, u ^ 1);
+                int ph_n[2];
+                resolve(min(it + 4, last), raw, ph_n);
+                fetch_k(ph_n, u);                    // K of step it+4
+                fetch_v(ph_k, u ^ 1);                // V of step it+3
+                ph_k[0] = ph_n[0];
+                ph_k[1] = ph_n[1];
+                table(min(it + 5, last), raw);
                 __syncthreads();
+                mask_max(it + 1, sc[u ^ 1]);
             }
         }
     }
@@ -468,7 +551,7 @@ __global__ __launch_bounds__(NW *kWave, (NW * C >= 16) ? 2 : 1) void pa_prefill_
 template <int DT, int AT, int D>
 hipError_t launch_prefill_t(const PrefillArgs &a, int grid, hipStream_t stream)
 {
-    hipLaunchKernelGGL((pa_prefill_kernel<DT, AT, D, kPrefillWaves, kPrefillCols, kPrefillPrefetch>),
+    hipLaunchKernelGGL((pa_prefill_kernel<DT, AT, D, kPrefillWaves, kPrefillCols>),
                        dim3(grid),
                        dim3(kPrefillWaves * kWave), 0, stream, a);
     return hipGetLastError();
