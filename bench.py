@@ -1,9 +1,10 @@
 #!/usr/bin/env python3
 """Decode-phase PagedAttention benchmark on one MI355X.
 
-A step is one layer of one decode step over one batch: pa_cache_append of the step's
-new K/V rows, then pa_decode (partition kernel + reduce when split) over the whole
-batch.  The headline workload is the Llama-70B-shaped GQA decode: 32 sequences x 4096
+A step is one layer of one decode step over one batch: the step's new K/V rows are
+appended to the pool and the whole batch attends (pa_decode_append: one launch of the
+partition kernel, plus the reduce when split; the same work as pa_cache_append followed
+by pa_decode, which is timed beside it).  The headline workload is the Llama-70B-shaped GQA decode: 32 sequences x 4096
 tokens, 64 q-heads / 8 kv-heads, head_dim 128, bf16 KV, 16-token blocks in a shuffled
 pool.  Inputs are seeded and synthetic and already resident in HBM when timing starts.
 The step cycles over four copies of the layer's pools at distinct addresses, as the
@@ -362,12 +363,29 @@ def main():
     max_ctx = w.max_context_len
 
     sc = U.scales(w)
+    # each sequence's new row, laid out per sequence for the fused call
+    appending = np.flatnonzero(w.context_lens > 0)
+    rows_k = np.zeros((w.num_seqs,) + w.k_new.shape[1:], w.k_new.dtype)
+    rows_v = np.zeros_like(rows_k)
+    rows_k[appending] = w.k_new
+    rows_v[appending] = w.v_new
+    k_rows = U.to_dev(rows_k, w.dtype, dev)
+    v_rows = U.to_dev(rows_v, w.dtype, dev)
 
-    def step(i):
+    def fused(i):
+        kp, vp = pools[i % LAYERS]
+        PA.decode_append(d["q"], kp, vp, k_rows, v_rows, d["block_tables"], d["context_lens"],
+                         scale, max_ctx, ptok, out=out, workspace=ws, **sc)
+
+    def two_calls(i):
         kp, vp = pools[i % LAYERS]
         PA.cache_append(kp, vp, d["k_new"], d["v_new"], d["slot_mapping"], **sc)
         PA.decode(d["q"], kp, vp, d["block_tables"], d["context_lens"], scale, max_ctx, ptok,
                   out=out, workspace=ws, **sc)
+
+    # a step is one decode_append launch (the append fused into the attention); the
+    # same work as two calls is timed beside it
+    step = fused
 
     if args.calibrate:
         calibration_copy(dev)
@@ -385,6 +403,13 @@ def main():
     wall = time.perf_counter() - t_start
     ms_per_step = wall * 1e3 / args.steps
     log(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.1f} us/step")
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        two_calls(i)
+    torch.cuda.synchronize()
+    two_call_ms = (time.perf_counter() - t_start) * 1e3 / args.steps
+    log(f"[bench] {args.steps} steps as append + decode: {two_call_ms * 1e3:.1f} us/step")
 
     # roofline: decode calls launched back to back on one stream, bracketed by HIP
     # events on that stream, cycling over the layers' pools so each launch's K/V is
@@ -397,14 +422,12 @@ def main():
     torch.cuda.synchronize()
     e0.record(stream)
     for i in range(n_l):
-        kp, vp = pools[i % LAYERS]
-        PA.decode(d["q"], kp, vp, d["block_tables"], d["context_lens"], scale, max_ctx, ptok,
-                  out=out, workspace=ws, **sc)
+        fused(i)
     e1.record(stream)
     torch.cuda.synchronize()
     dur = e0.elapsed_time(e1) * 1e-3 / n_l
     achieved = kv_bytes / dur / 1e9
-    log(f"[bench] decode call: {dur * 1e6:.1f} us per launch over {n_l} back-to-back "
+    log(f"[bench] decode_append call: {dur * 1e6:.1f} us per launch over {n_l} back-to-back "
         f"launches -> {achieved:.0f} GB/s")
     traffic = recorded_traffic(w.spec.name, ptok)
 
@@ -471,7 +494,7 @@ def main():
         "config": {"workload": f"{w.spec.name}: {w.num_seqs} seqs x ctx {max_ctx}, "
                                f"{w.num_q_heads} q / {w.num_kv_heads} kv heads, d "
                                f"{w.head_dim}, 16-token blocks, {w.num_blocks}-block shuffled pool; "
-                               f"step = append + decode of one layer",
+                               f"step = append + decode of one layer (one fused launch)",
                    "num_seqs": w.num_seqs, "context_len": max_ctx,
                    "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
                    "head_dim": w.head_dim, "block_size": 16,
@@ -482,11 +505,13 @@ def main():
         "tokens_per_s": round(tokens_per_s, 1),
         "context_tokens_per_s": round(float(w.context_lens.sum()) / (ms_per_step * 1e-3), 1),
         "kv_bytes_per_step": kv_bytes,
+        "two_call_ms_per_step": round(two_call_ms, 5),
         "graph_ms_per_step": round(graph_ms, 5),
         "graph_tokens_per_s": round(w.num_seqs / (graph_ms * 1e-3), 1),
         "unique_kv_bytes_per_step": uniq_bytes,
-        "roofline": {"bound": "hbm", "kernel": "pa_decode_partition (+ pa_decode_reduce when "
-                                               "a sequence spans several partitions)",
+        "roofline": {"bound": "hbm", "kernel": "pa_decode_partition with the fused append "
+                                               "(+ pa_decode_reduce when a sequence spans "
+                                               "several partitions)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "launch_us_mean": round(dur * 1e6, 2),

@@ -156,6 +156,26 @@ pa_status pa_decode(const pa_kv_pool *pool, const void *q, void *out, int32_t nu
                     int32_t max_context_len, int32_t partition_tokens, void *workspace,
                     size_t workspace_bytes, void *stream);
 
+/* A decode step's append and attention in one launch: for every sequence b with
+ * context_lens[b] >= 1, its new row k_new[b], v_new[b] ([num_seqs][num_kv_heads]
+ * [head_dim], the pool's act_dtype, device) becomes token context_lens[b] - 1 -- it is
+ * written into the pool at block block_tables[b][(ctx-1)/16], row (ctx-1)%16 (fp8
+ * pools store its E4M3 codes, as pa_cache_append does) -- and the attention is
+ * pa_decode's over tokens 0 .. ctx-1.  The result, and the pool afterwards, equal
+ * pa_cache_append of those rows at those slots followed by pa_decode, bit for bit
+ * ("Deep dive into vLLM 06", kernel fusion: the KV-cache write fused with the work
+ * around it; LLM-101-CN "推理优化": a decode step appends one token, then attends).
+ * The block that receives the row must not be read by another sequence of the same
+ * call (copy-on-write keeps a written block private).  Other arguments, errors and
+ * the workspace are as for pa_decode; a sequence whose context length or needed
+ * table entry is bad gets NaN output and no row is written. */
+pa_status pa_decode_append(const pa_kv_pool *pool, const void *q, const void *k_new,
+                           const void *v_new, void *out, int32_t num_seqs, int32_t num_q_heads,
+                           float scale, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                           const int32_t *context_lens, int32_t max_context_len,
+                           int32_t partition_tokens, void *workspace, size_t workspace_bytes,
+                           void *stream);
+
 /* Paged prefill (chunked prefill) attention for one layer: the query rows of prompt
  * chunks attend to the cache through the same pool and block tables as decode
  * (LLM-101-CN "推理优化", section "Chunked Prefill": a chunk's queries attend to the

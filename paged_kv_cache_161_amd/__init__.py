@@ -6,7 +6,7 @@ include/paged_attention.h); `binding` marshals torch tensors into it.
 `workloads` builds seeded synthetic inputs and holds no attention arithmetic.
 """
 from .binding import (BLOCK_SIZE, BlockAllocator, PaError, cache_append, copy_blocks, decode,
-                      load, partition_tokens, pool_bytes, prefill, workspace_bytes)
+                      decode_append, load, partition_tokens, pool_bytes, prefill, workspace_bytes)
 
 __all__ = ["BLOCK_SIZE", "BlockAllocator", "PaError", "cache_append", "copy_blocks", "decode",
-           "load", "partition_tokens", "pool_bytes", "prefill", "workspace_bytes"]
+           "decode_append", "load", "partition_tokens", "pool_bytes", "prefill", "workspace_bytes"]

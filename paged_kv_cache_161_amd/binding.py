@@ -63,6 +63,9 @@ def load(path: str = LIB_PATH):
     lib.pa_decode.argtypes = [ctypes.POINTER(PaKvPool), P, P, I32, I32, ctypes.c_float, P, I32,
                               P, I32, I32, P, ctypes.c_size_t, P]
     lib.pa_decode.restype = ctypes.c_int
+    lib.pa_decode_append.argtypes = [ctypes.POINTER(PaKvPool), P, P, P, P, I32, I32,
+                                     ctypes.c_float, P, I32, P, I32, I32, P, ctypes.c_size_t, P]
+    lib.pa_decode_append.restype = I32
     lib.pa_prefill.argtypes = [ctypes.POINTER(PaKvPool), P, P, I32, I32, ctypes.c_float, P, I32,
                                I32, P, I32, P, I32, P]
     lib.pa_prefill.restype = I32
@@ -212,6 +215,39 @@ def decode(q, k_pool, v_pool, block_tables, context_lens, scale: float, max_cont
                                                           torch.int32),
                           max_context_len, partition_tokens, ws_ptr, ws_len,
                           _stream_handle(q.device))
+    _raise(st)
+    return out
+
+
+def decode_append(q, k_pool, v_pool, k_new, v_new, block_tables, context_lens, scale: float,
+                  max_context_len: int, partition_tokens: int = 0,
+                  out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                  k_scale: float = 1.0, v_scale: float = 1.0) -> torch.Tensor:
+    """One launch for a decode step: each sequence's new row (k_new / v_new [B][Hkv][d])
+    becomes token context_lens[b] - 1 in the pool, then decode attention as decode()."""
+    act = q.dtype if k_pool.dtype in FP8_STORAGE else None
+    pool = make_pool(k_pool, v_pool, act, k_scale, v_scale)
+    B, hq, d = q.shape
+    if d != pool.head_dim:
+        raise ValueError("q head_dim differs from the pool's")
+    if tuple(k_new.shape) != (B, pool.num_kv_heads, d) or k_new.shape != v_new.shape:
+        raise ValueError("k_new / v_new must be [num_seqs][num_kv_heads][head_dim]")
+    if out is None:
+        out = torch.empty_like(q)
+    need = workspace_bytes(B, hq, pool.num_kv_heads, d, max_context_len, partition_tokens)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = _dev_ptr(workspace, "workspace") if need else None
+    ws_len = workspace.numel() * workspace.element_size() if need else 0
+    act = _act_dtype(pool)
+    st = load().pa_decode_append(ctypes.byref(pool), _dev_ptr(q, "q", act),
+                                 _dev_ptr(k_new, "k_new", act), _dev_ptr(v_new, "v_new", act),
+                                 _dev_ptr(out, "out", act), B, hq, ctypes.c_float(scale),
+                                 _dev_ptr(block_tables, "block_tables", torch.int32),
+                                 block_tables.shape[1],
+                                 _dev_ptr(context_lens, "context_lens", torch.int32),
+                                 max_context_len, partition_tokens, ws_ptr, ws_len,
+                                 _stream_handle(q.device))
     _raise(st)
     return out
 

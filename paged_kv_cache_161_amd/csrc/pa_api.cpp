@@ -210,11 +210,17 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
     return rows * (size_t)head_dim * sizeof(float) + 2 * rows * sizeof(float);
 }
 
-pa_status pa_decode(const pa_kv_pool *pool, const void *q, void *out, int32_t num_seqs,
-                    int32_t num_q_heads, float scale, const int32_t *block_tables,
-                    int32_t max_blocks_per_seq, const int32_t *context_lens,
-                    int32_t max_context_len, int32_t partition_tokens, void *workspace,
-                    size_t workspace_bytes, void *stream)
+}  // extern "C"
+
+namespace {
+
+// pa_decode, and pa_decode_append when k_new / v_new are given.
+pa_status decode_impl(const pa_kv_pool *pool, const void *q, const void *k_new,
+                      const void *v_new, void *out, int32_t num_seqs, int32_t num_q_heads,
+                      float scale, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                      const int32_t *context_lens, int32_t max_context_len,
+                      int32_t partition_tokens, void *workspace, size_t workspace_bytes,
+                      void *stream)
 {
     pa_status st = check_pool(pool);
     if (st != PA_OK)
@@ -267,10 +273,44 @@ pa_status pa_decode(const pa_kv_pool *pool, const void *q, void *out, int32_t nu
     a.v_scale = fp8 ? pool->v_scale : 1.0f;
     a.split = parts > 1 ? 1 : 0;
     a.longest_first = (num_seqs > 1 && num_seqs <= pa::kLongestFirstMax) ? 1 : 0;
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.k_quant = pool->k_scale;
+    a.v_quant = pool->v_scale;
+    a.act_bf16 = pool->act_dtype == PA_BF16 ? 1 : 0;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = pa::launch_decode(pool->dtype, pool->act_dtype, pool->head_dim, a, num_seqs, s);
     return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_decode(const pa_kv_pool *pool, const void *q, void *out, int32_t num_seqs,
+                    int32_t num_q_heads, float scale, const int32_t *block_tables,
+                    int32_t max_blocks_per_seq, const int32_t *context_lens,
+                    int32_t max_context_len, int32_t partition_tokens, void *workspace,
+                    size_t workspace_bytes, void *stream)
+{
+    return decode_impl(pool, q, nullptr, nullptr, out, num_seqs, num_q_heads, scale,
+                       block_tables, max_blocks_per_seq, context_lens, max_context_len,
+                       partition_tokens, workspace, workspace_bytes, stream);
+}
+
+pa_status pa_decode_append(const pa_kv_pool *pool, const void *q, const void *k_new,
+                           const void *v_new, void *out, int32_t num_seqs, int32_t num_q_heads,
+                           float scale, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                           const int32_t *context_lens, int32_t max_context_len,
+                           int32_t partition_tokens, void *workspace, size_t workspace_bytes,
+                           void *stream)
+{
+    if (num_seqs > 0 && (!k_new || !v_new))
+        return PA_ERR_INVALID_ARG;
+    return decode_impl(pool, q, k_new, v_new, out, num_seqs, num_q_heads, scale, block_tables,
+                       max_blocks_per_seq, context_lens, max_context_len, partition_tokens,
+                       workspace, workspace_bytes, stream);
 }
 
 pa_status pa_prefill(const pa_kv_pool *pool, const void *q, void *out, int32_t num_seqs,

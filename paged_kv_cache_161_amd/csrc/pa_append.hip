@@ -14,6 +14,7 @@
 // quantisation, one of the fused kernels "Deep dive into vLLM 06" lists): the
 // division is IEEE fp32, the code rounds to nearest-even and saturates at 448.
 #include "pa_common.h"
+#include "pa_fp8.h"
 
 namespace pa {
 namespace {
@@ -60,24 +61,6 @@ __global__ __launch_bounds__(256) void pa_cache_append_kernel(AppendArgs a)
             reinterpret_cast<uint16_t *>(vdst)[(2 * j + 1) * kBlock] = (uint16_t)(vv[j] >> 16);
         }
     }
-}
-
-// fp32 -> E4M3 code by bit arithmetic on the binary32 encoding: round the 23-bit
-// fraction to 3 bits (nearest, ties to even) and rebias the exponent 127 -> 7; below
-// 2^-6 the code counts steps of 2^-9; NaN stays NaN, |x| >= 448 gives +-448.
-__device__ __forceinline__ uint32_t e4m3_code(float x)
-{
-    const uint32_t u = __float_as_uint(x);
-    const uint32_t sign = (u >> 24) & 0x80u;
-    const uint32_t a = u & 0x7FFFFFFFu;
-    if (a > 0x7F800000u)
-        return sign | 0x7Fu;                              // NaN
-    if (a >= 0x43E00000u)
-        return sign | 0x7Eu;                              // >= 448 (and inf): 448
-    if (a < 0x3C800000u)                                  // < 2^-6: subnormal codes
-        return sign | (uint32_t)rintf(__uint_as_float(a) * 512.0f);
-    const uint32_t rounded = a + 0x7FFFFu + ((a >> 20) & 1u);
-    return sign | ((rounded >> 20) - (120u << 3));
 }
 
 template <int D>

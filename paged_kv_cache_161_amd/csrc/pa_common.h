@@ -35,6 +35,13 @@ struct DecodeArgs {
     float v_scale;                    // multiplies the output (fp8 pools; else 1)
     int32_t split;                    // 1: write partials, 0: write out
     int32_t longest_first;            // 1: workgroup z takes the z-th longest sequence
+    // Fused append (pa_decode_append): sequence b's new K/V row, token ctx-1, is
+    // written into the pool and used for that token; null for plain decode.
+    const void *k_new;                // [B][hkv][D], activation type
+    const void *v_new;
+    float k_quant;                    // fp8 pools: stored code = E4M3(x / scale)
+    float v_quant;
+    int32_t act_bf16;                 // fp8 pools: new rows are bf16 (else f16)
 };
 
 // Batches up to this size are dispatched longest sequence first.

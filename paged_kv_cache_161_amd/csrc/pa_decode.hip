@@ -34,7 +34,10 @@
 //   tile max needs two cross-row exchanges, the O rescale none (O^T's head is lane % 16).
 #include <math.h>
 
+#include <type_traits>
+
 #include "pa_common.h"
+#include "pa_fp8.h"
 
 namespace pa {
 namespace {
@@ -99,6 +102,37 @@ struct Tile16 {
         for (int n = 0; n < NPV; ++n)
             v[n] = *reinterpret_cast<const u32x2 *>(vt + (16 * n + r) * kBlock + 4 * g);
     }
+
+    // Write the patched block back: K row `off` and every V^T piece (whole rows, so the
+    // stores fill whole sectors; only token off's values differ from the pool's).
+    __device__ __forceinline__ void store_row(uint16_t *kt, uint16_t *vt, int off, int r, int g) const
+    {
+        if (r == off) {
+#pragma unroll
+            for (int i = 0; i < NQK; ++i)
+                *reinterpret_cast<u32x4 *>(kt + r * D + 32 * i + 8 * g) = k[i];
+        }
+#pragma unroll
+        for (int n = 0; n < NPV; ++n)
+            *reinterpret_cast<u32x2 *>(vt + (16 * n + r) * kBlock + 4 * g) = v[n];
+    }
+
+    // Replace token `off` of this block by a new row (k_row, v_row: D elements).
+    __device__ __forceinline__ void patch(const uint16_t *k_row, const uint16_t *v_row, int off,
+                                          int r, int g)
+    {
+        if (r == off) {
+#pragma unroll
+            for (int i = 0; i < NQK; ++i)
+                k[i] = *reinterpret_cast<const u32x4 *>(k_row + 32 * i + 8 * g);
+        }
+        if (g == off / 4) {
+            const int w = (off % 4) / 2, sh = 16 * (off % 2);
+#pragma unroll
+            for (int n = 0; n < NPV; ++n)
+                v[n][w] = (v[n][w] & ~(0xFFFFu << sh)) | ((uint32_t)v_row[16 * n + r] << sh);
+        }
+    }
 };
 
 template <int DT, int D>
@@ -128,6 +162,33 @@ struct Tile32 {
 #pragma unroll
         for (int n = 0; n < NC; ++n)
             v[n] = *reinterpret_cast<const f32x4 *>(vt + (16 * n + r) * kBlock + 4 * g);
+    }
+
+    __device__ __forceinline__ void store_row(float *kt, float *vt, int off, int r, int g) const
+    {
+        if (r == off) {
+#pragma unroll
+            for (int c = 0; c < NC; ++c)
+                *reinterpret_cast<f32x4 *>(kt + r * D + (D / 4) * g + 4 * c) = k[c];
+        }
+#pragma unroll
+        for (int n = 0; n < NC; ++n)
+            *reinterpret_cast<f32x4 *>(vt + (16 * n + r) * kBlock + 4 * g) = v[n];
+    }
+
+    __device__ __forceinline__ void patch(const float *k_row, const float *v_row, int off, int r,
+                                          int g)
+    {
+        if (r == off) {
+#pragma unroll
+            for (int c = 0; c < NC; ++c)
+                k[c] = *reinterpret_cast<const f32x4 *>(k_row + (D / 4) * g + 4 * c);
+        }
+        if (g == off / 4) {
+#pragma unroll
+            for (int n = 0; n < NC; ++n)
+                v[n][off % 4] = v_row[16 * n + r];
+        }
     }
 };
 
@@ -165,6 +226,35 @@ struct Tile8 {
 #pragma unroll
         for (int n = 0; n < NPV; ++n)
             v[n] = *reinterpret_cast<const uint32_t *>(vt + (16 * n + r) * kBlock + 4 * g);
+    }
+
+    __device__ __forceinline__ void store_row(uint8_t *kt, uint8_t *vt, int off, int r, int g) const
+    {
+        if (r == off) {
+#pragma unroll
+            for (int j = 0; j < NKL; ++j)
+                *reinterpret_cast<u32x4 *>(kt + r * D + 64 * j + 16 * g) = k[j];
+        }
+#pragma unroll
+        for (int n = 0; n < NPV; ++n)
+            *reinterpret_cast<uint32_t *>(vt + (16 * n + r) * kBlock + 4 * g) = v[n];
+    }
+
+    // The new row arrives already as the codes the append stores.
+    __device__ __forceinline__ void patch(const uint8_t *k_row, const uint8_t *v_row, int off,
+                                          int r, int g)
+    {
+        if (r == off) {
+#pragma unroll
+            for (int j = 0; j < NKL; ++j)
+                k[j] = *reinterpret_cast<const u32x4 *>(k_row + 64 * j + 16 * g);
+        }
+        if (g == off / 4) {
+            const int sh = 8 * (off % 4);
+#pragma unroll
+            for (int n = 0; n < NPV; ++n)
+                v[n] = (v[n] & ~(0xFFu << sh)) | ((uint32_t)v_row[16 * n + r] << sh);
+        }
     }
 };
 
@@ -357,7 +447,7 @@ constexpr int min_waves_per_simd(int dt, int d, int pf)
                       : ((pf + 1) * (dt == DT_FP8 ? 16 : 32) * d / 128 <= 96 ? 2 : 1));
 }
 
-template <int DT, int AT, int D, int NW, int PF>
+template <int DT, int AT, int D, int NW, int PF, bool FUSE>
 __global__ __launch_bounds__(NW *kWave, min_waves_per_simd(DT, D, PF)) void pa_decode_partition(DecodeArgs a)
 {
     using F = Frags<DT, AT, D>;
@@ -447,6 +537,20 @@ __global__ __launch_bounds__(NW *kWave, min_waves_per_simd(DT, D, PF)) void pa_d
         return;
     }
 
+    // Fused append: the sequence's new row is token ctx - 1, in logical block lb_new.
+    // In every workgroup whose partition holds that block, the wave that computes on
+    // it stages the row in LDS and patches it into its registers from there instead of
+    // reading it back from the pool; in head chunk 0's workgroup it also writes the row
+    // into the pool.  Nothing in this launch depends on the order of that write and
+    // the pool reads (the block is private to the sequence).
+    const bool fuse = FUSE && ctx >= 1;
+    const int lb_new = fuse ? (ctx - 1) / kBlock : -1;
+    const int off_new = fuse ? (ctx - 1) % kBlock : 0;
+    const bool has_new = fuse && lb_new >= lb_begin && lb_new < lb_end;   // workgroup-uniform
+    int ph_new = -1;       // block lb_new's physical id, where this workgroup writes the row
+    __shared__ __align__(16) Elem s_newk[FUSE ? D : 16];   // the row as the pool stores it
+    __shared__ __align__(16) Elem s_newv[FUSE ? D : 16];
+
     const int nb = lb_end - lb_begin;
     const int my_n = nb > wave ? (nb - wave + NW - 1) / NW : 0;   // <= 64 (host-checked)
 
@@ -471,9 +575,22 @@ __global__ __launch_bounds__(NW *kWave, min_waves_per_simd(DT, D, PF)) void pa_d
         return (size_t)ph * blk_stride;
     };
 
-    auto process = [&](typename F::Tile &t, int i) {
+    // PATCH: this call may hold the block that receives the new row (fused append).
+    auto process = [&](auto patch_tag, typename F::Tile &t, int i) {
+        constexpr bool PATCH = decltype(patch_tag)::value;
         const int lb = lb_begin + wave + i * NW;
         const int valid = ctx - lb * kBlock;            // >= 1
+        if constexpr (PATCH) {
+            if (lb == lb_new) {                         // wave-uniform
+                t.patch(s_newk, s_newv, off_new, r, g);
+                if (ph_new >= 0) {                      // head chunk 0: into the pool
+                    const size_t tile = ((size_t)ph_new * a.num_kv_heads + kvh) * kBlock * D;
+                    t.store_row(static_cast<Elem *>(const_cast<void *>(a.k_pool)) + tile,
+                                static_cast<Elem *>(const_cast<void *>(a.v_pool)) + tile,
+                                off_new, r, g);
+                }
+            }
+        }
         f32x4 s = scores<DT, AT, D>(t, qf);
         f32x4 x = s * a.scale_log2;
         if (valid < kBlock) {
@@ -506,8 +623,9 @@ __global__ __launch_bounds__(NW *kWave, min_waves_per_simd(DT, D, PF)) void pa_d
 
     // Ring of PF + 1 tiles: block i + PF is loaded while block i is computed.  The
     // inner loop is fully unrolled so every ring slot stays a fixed register range.
-    if (my_n > 0) {
-        typename F::Tile ring[PF + 1];
+    // Ring of PF + 1 tiles: block i + PF is loaded while block i is computed.  The
+    // inner loop is fully unrolled so every ring slot stays a fixed register range.
+    auto prologue = [&](typename F::Tile (&ring)[PF + 1]) {
 #pragma unroll
         for (int k = 0; k < PF; ++k) {
             if (k < my_n) {
@@ -515,19 +633,89 @@ __global__ __launch_bounds__(NW *kWave, min_waves_per_simd(DT, D, PF)) void pa_d
                 ring[k].load(kbase + off, vbase + off, r, g);
             }
         }
-        for (int i = 0; i < my_n; i += PF + 1) {
+    };
+    // The new row of a fused append lands in the sequence's last block, which is the
+    // last block of the wave that holds it; with FUSE the loop stops one block short
+    // and that block is computed apart, so the loop itself carries no patch test.
+    using NoPatch = std::integral_constant<bool, false>;
+    using Patch = std::integral_constant<bool, true>;
+    auto stream_blocks = [&](typename F::Tile (&ring)[PF + 1]) {
+        const int n_loop = FUSE ? my_n - 1 : my_n;
+        for (int i = 0; i < n_loop; i += PF + 1) {
 #pragma unroll
             for (int u = 0; u <= PF; ++u) {
                 const int it = i + u;
-                if (it < my_n) {
+                if (it < n_loop) {
                     if (it + PF < my_n) {
                         const size_t off = phys_of(it + PF);
                         ring[(u + PF) % (PF + 1)].load(kbase + off, vbase + off, r, g);
                     }
-                    process(ring[u], it);
+                    process(NoPatch{}, ring[u], it);
                 }
             }
         }
+        if constexpr (FUSE) {
+            const int ul = n_loop % (PF + 1);
+#pragma unroll
+            for (int u = 0; u <= PF; ++u)
+                if (u == ul)
+                    process(Patch{}, ring[u], n_loop);
+        }
+    };
+    if constexpr (FUSE) {
+        // The new row's block is the last block of wave w_new, and that wave alone
+        // stages the row (its table lane already holds the block's id), later patches it
+        // into the block's tile from its own LDS copy and, in head chunk 0, writes the
+        // patched tile's row back (whole V^T rows, so the stores fill whole sectors), so
+        // no other wave waits.  Its loads go out before the first tiles' loads, which
+        // are issued for every wave (a wave without blocks loads pool block 0, which
+        // always exists, without consulting the table, and never uses it): the count of
+        // loads issued after the row's is fixed, and staging waits for the row alone.
+        const bool stager = has_new && wave == (lb_new - lb_begin) % NW;    // wave-uniform
+        QElem nk[(D + kWave - 1) / kWave], nv[(D + kWave - 1) / kWave];
+        if (stager) {
+            const QElem *kr = static_cast<const QElem *>(a.k_new) +
+                              ((size_t)b * a.num_kv_heads + kvh) * D;
+            const QElem *vr = static_cast<const QElem *>(a.v_new) +
+                              ((size_t)b * a.num_kv_heads + kvh) * D;
+#pragma unroll
+            for (int j = 0; j < (D + kWave - 1) / kWave; ++j) {
+                nk[j] = kr[min(lane + j * kWave, D - 1)];
+                nv[j] = vr[min(lane + j * kWave, D - 1)];
+            }
+        }
+        typename F::Tile ring[PF + 1];
+#pragma unroll
+        for (int k = 0; k < PF; ++k) {
+            const size_t off = my_n > 0 ? phys_of(min(k, my_n - 1)) : 0;
+            ring[k].load(kbase + off, vbase + off, r, g);
+        }
+        if (stager) {
+            const int ph = __builtin_amdgcn_readlane(bt_lane, (lb_new - lb_begin) / NW);
+            ph_new = (chunk == 0 && (unsigned)ph < (unsigned)a.num_blocks) ? ph : -1;
+#pragma unroll
+            for (int j = 0; j < (D + kWave - 1) / kWave; ++j) {
+                const int e = lane + j * kWave;
+                if (e < D) {
+                    Elem sk, sv;
+                    if constexpr (DT == DT_FP8) {
+                        sk = (Elem)e4m3_of_16(nk[j], a.act_bf16 != 0, a.k_quant);
+                        sv = (Elem)e4m3_of_16(nv[j], a.act_bf16 != 0, a.v_quant);
+                    } else {
+                        sk = nk[j];
+                        sv = nv[j];
+                    }
+                    s_newk[e] = sk;
+                    s_newv[e] = sv;
+                }
+            }
+        }
+        if (my_n > 0)
+            stream_blocks(ring);
+    } else if (my_n > 0) {
+        typename F::Tile ring[PF + 1];
+        prologue(ring);
+        stream_blocks(ring);
     }
     l_run = wave_sum_rows(l_run);
 
@@ -663,7 +851,8 @@ hipError_t launch_decode_t(const DecodeArgs &a, int num_seqs, hipStream_t stream
     const int gs_max = min(16, a.group);
     const size_t lds = sizeof(float) * (NW * 32 + 16 + (size_t)NW * gs_max * (D + 4)) +
                        (a.longest_first ? sizeof(int) * (num_seqs + 1) : 0);
-    auto kern = pa_decode_partition<DT, AT, D, NW, PF>;
+    auto kern = a.k_new ? pa_decode_partition<DT, AT, D, NW, PF, true>
+                        : pa_decode_partition<DT, AT, D, NW, PF, false>;
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

@@ -23,7 +23,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("pa_cache_append", "pa_decode", "pa_decode_workspace_bytes",
               "pa_decode_partition_tokens", "pa_pool_bytes", "pa_status_string", "pa_prefill",
-              "pa_copy_blocks", "pa_seq_reserve", "pa_seq_fork", "pa_seq_truncate"):
+              "pa_decode_append", "pa_copy_blocks", "pa_seq_reserve", "pa_seq_fork", "pa_seq_truncate"):
         assert n in names
 
 
@@ -128,6 +128,23 @@ def test_prefill_rejects_bad_arguments(lib):
     assert _prefill(lib, _pool(), num_seqs=0) == 0
     fp8 = dict(dtype=B.PA_FP8_E4M3, act_dtype=B.PA_BF16, k_scale=0.01, v_scale=0.0)
     assert _prefill(lib, _pool(**fp8)) == inval
+
+
+def test_decode_append_rejects_bad_arguments(lib):
+    f = lib.pa_decode_append
+
+    def call(pool, k_new=FAKE, v_new=FAKE, num_seqs=2, hq=4, ptok=0, ws=None, ws_bytes=0):
+        return f(ctypes.byref(pool) if pool is not None else None, FAKE, k_new, v_new, FAKE,
+                 num_seqs, hq, ctypes.c_float(0.125), FAKE, 8, FAKE, 100, ptok, ws, ws_bytes,
+                 None)
+
+    assert call(None) == 1
+    assert call(_pool(), k_new=None) == 1
+    assert call(_pool(), v_new=None) == 1
+    assert call(_pool(), hq=3) == 1
+    assert call(_pool(head_dim=96)) == 2
+    assert call(_pool(), ptok=32) == 3                       # split without workspace
+    assert call(_pool(), num_seqs=0, k_new=None, v_new=None) == 0
 
 
 def test_append_rejects_bad_arguments(lib):

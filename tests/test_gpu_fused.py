@@ -1,0 +1,117 @@
+"""GPU: pa_decode_append (append and attention in one launch) against the two-call path
+(pa_cache_append, then pa_decode) and against the oracle.
+
+The fused call must leave the pool byte-identical to the append and give bit-identical
+outputs (the attention reads the same values in the same order), for 16-bit, fp32 and
+fp8 pools, GQA groups spanning several head chunks, split partitions, empty contexts
+and ragged tails; and its output must be within the decode bars of the oracle.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from paged_kv_cache_161_amd import binding as PA
+from paged_kv_cache_161_amd import workloads as W
+from tests import devutil as U
+from tests.test_gpu_parity import SMALL
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def hip_library():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    PA.load()
+
+
+def per_sequence_rows(w, rows):
+    """The workload's new rows ([T][Hkv][d], one per sequence with ctx >= 1, in order)
+    laid out per sequence ([B][Hkv][d]); rows of empty sequences are zero."""
+    out = np.zeros((w.num_seqs,) + rows.shape[1:], rows.dtype)
+    out[np.flatnonzero(w.context_lens > 0)] = rows
+    return out
+
+
+def run_both(w, ptok):
+    d = U.device_inputs(w)
+    sc = U.scales(w)
+    ka, va = U.device_pools(w)
+    PA.cache_append(ka, va, d["k_new"], d["v_new"], d["slot_mapping"], **sc)
+    out_a = PA.decode(d["q"], ka, va, d["block_tables"], d["context_lens"], float(w.scale),
+                      w.max_context_len, ptok, **sc)
+    kb, vb = U.device_pools(w)
+    k_rows = U.to_dev(per_sequence_rows(w, w.k_new), w.dtype)
+    v_rows = U.to_dev(per_sequence_rows(w, w.v_new), w.dtype)
+    out_b = PA.decode_append(d["q"], kb, vb, k_rows, v_rows, d["block_tables"],
+                             d["context_lens"], float(w.scale), w.max_context_len, ptok, **sc)
+    torch.cuda.synchronize()
+    return out_a, out_b, (ka, va), (kb, vb)
+
+
+CASES = [(s, 0) for s in SMALL] + [(SMALL[0], 16), (SMALL[0], 48), (SMALL[4], 32),
+                                    (SMALL[9], 16), (SMALL[7], 64)]
+
+
+@pytest.mark.parametrize("spec,ptok", CASES, ids=lambda v: v.name if hasattr(v, "name") else f"p{v}")
+def test_fused_equals_append_then_decode(spec, ptok):
+    say(f"[fused] {spec.name} ptok={ptok}")
+    w = W.build(spec)
+    out_a, out_b, (ka, va), (kb, vb) = run_both(w, ptok)
+    assert U.int_view(ka).equal(U.int_view(kb)) and U.int_view(va).equal(U.int_view(vb))
+    assert U.int_view(out_a).equal(U.int_view(out_b))
+    kp, vp, bt, sl = w.oracle_view()
+    kp, vp = O.cache_append(kp, vp, w.k_new, w.v_new, sl, w.kv_dtype, act_dtype=w.dtype,
+                            k_scale=w.k_scale, v_scale=w.v_scale)
+    ref, _ = O.decode_paged(w.q, kp, vp, w.kv_dtype, bt, w.context_lens, w.scale,
+                            q_dtype=w.dtype, k_scale=w.k_scale, v_scale=w.v_scale)
+    got = U.widen(U.from_dev(out_b, w.dtype), w.dtype)
+    ok, mx, mean = U.tolerance_ok(got, ref, w.dtype)
+    say(f"  max {mx:.3e} mean {mean:.3e}")
+    assert np.isfinite(got).all() and ok, (mx, mean)
+
+
+@pytest.mark.parametrize("cfg", [3, 6])
+def test_fused_full_size(cfg):
+    say(f"[fused] config {cfg}")
+    w = W.make_config(cfg)
+    out_a, out_b, (ka, va), (kb, vb) = run_both(w, 0)
+    assert U.int_view(ka).equal(U.int_view(kb)) and U.int_view(va).equal(U.int_view(vb))
+    assert U.int_view(out_a).equal(U.int_view(out_b))
+
+
+def test_fused_bad_table_entry_writes_nothing():
+    w = W.build(SMALL[0])
+    d = U.device_inputs(w)
+    kp, vp = U.device_pools(w)
+    k0, v0 = kp.clone(), vp.clone()
+    tables = d["block_tables"].clone()
+    b = 5                                            # ctx 257: new row in logical block 16
+    tables[b, (int(w.context_lens[b]) - 1) // 16] = w.num_blocks + 3
+    k_rows = U.to_dev(per_sequence_rows(w, w.k_new), w.dtype)
+    v_rows = U.to_dev(per_sequence_rows(w, w.v_new), w.dtype)
+    kb, vb = kp.clone(), vp.clone()
+    out = PA.decode_append(d["q"], kb, vb, k_rows, v_rows, tables, d["context_lens"],
+                           float(w.scale), w.max_context_len)
+    torch.cuda.synchronize()
+    got = U.widen(U.from_dev(out, w.dtype), w.dtype)
+    assert np.isnan(got[b]).all()
+    assert np.isfinite(np.delete(got, b, axis=0)).all()
+    # every other sequence's row landed; nothing was written for sequence b
+    ref_k, ref_v = kp.clone(), vp.clone()
+    keep = torch.from_numpy(np.flatnonzero((w.context_lens > 0)
+                                           & (np.arange(w.num_seqs) != b))).cuda()
+    slots = torch.from_numpy(w.slot_mapping).cuda()
+    rows_of = torch.from_numpy(np.cumsum(w.context_lens > 0) - 1).cuda()
+    PA.cache_append(ref_k, ref_v, d["k_new"][rows_of[keep]], d["v_new"][rows_of[keep]],
+                    slots[rows_of[keep]].contiguous())
+    torch.cuda.synchronize()
+    assert U.int_view(kb).equal(U.int_view(ref_k)) and U.int_view(vb).equal(U.int_view(ref_v))
+    del k0, v0
