@@ -353,7 +353,10 @@ def main():
     pools = [U.device_pools(w, dev) for _ in range(LAYERS)]
     d = U.device_inputs(w, dev)
     out = torch.empty_like(d["q"])
-    ptok = args.partition_tokens
+    # the partition length a serving loop would plan from the host's context lengths
+    # (pa_decode_plan), unless one is forced
+    ptok = args.partition_tokens or PA.plan_partition_tokens(
+        w.num_q_heads, w.num_kv_heads, w.head_dim, w.context_lens)
     ws_bytes = PA.workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim,
                                   w.max_context_len, ptok)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
@@ -498,8 +501,7 @@ def main():
                    "num_seqs": w.num_seqs, "context_len": max_ctx,
                    "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
                    "head_dim": w.head_dim, "block_size": 16,
-                   "partition_tokens": ptok or PA.partition_tokens(
-                       w.num_seqs, w.num_q_heads, w.num_kv_heads, max_ctx),
+                   "partition_tokens": ptok,
                    "parallelism": "none (1 GPU)"},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(tokens_per_s, 1),

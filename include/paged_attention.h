@@ -122,6 +122,21 @@ pa_status pa_cache_append(const pa_kv_pool *pool, const void *k_new, const void 
 int32_t pa_decode_partition_tokens(int32_t num_seqs, int32_t num_q_heads,
                                    int32_t num_kv_heads, int32_t max_context_len);
 
+/* A partition length for pa_decode / pa_decode_append planned from the batch's context
+ * lengths as the host knows them (a serving scheduler tracks each request's KV length:
+ * LLM-101-CN "推理优化", Chunked Prefill scheduler, kv_len per request).  The split
+ * cuts the KV axis so that the GPU's CUs all work ("Deep dive into vLLM 06",
+ * Flash-Decoding): the longest sequence is cut into the most partitions that still
+ * keep every workgroup with work in one round of the MI355X's 256 CUs, each as long as
+ * that count allows; when no partition allows one round, it returns the automatic
+ * choice.  A batch of
+ * equal lengths gets the automatic choice.  The lengths must be those passed on the
+ * device to the call that uses the result (anything else is still correct, only
+ * planned for other lengths).  Host-only; returns a positive multiple of 16, or -1 on
+ * bad input. */
+int32_t pa_decode_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                       int32_t head_dim, const int32_t *context_lens_host);
+
 /* Workspace bytes pa_decode needs for these arguments (partition_tokens as passed to
  * pa_decode, 0 = auto).  0 when the call runs in a single pass.  Returns SIZE_MAX on
  * invalid arguments.  Host-only. */

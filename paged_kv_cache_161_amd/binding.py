@@ -58,6 +58,8 @@ def load(path: str = LIB_PATH):
     lib.pa_cache_append.restype = ctypes.c_int
     lib.pa_decode_partition_tokens.argtypes = [I32, I32, I32, I32]
     lib.pa_decode_partition_tokens.restype = I32
+    lib.pa_decode_plan.argtypes = [I32, I32, I32, I32, P]
+    lib.pa_decode_plan.restype = I32
     lib.pa_decode_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32]
     lib.pa_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.pa_decode.argtypes = [ctypes.POINTER(PaKvPool), P, P, I32, I32, ctypes.c_float, P, I32,
@@ -174,6 +176,19 @@ def partition_tokens(num_seqs: int, num_q_heads: int, num_kv_heads: int,
                      max_context_len: int) -> int:
     return int(load().pa_decode_partition_tokens(num_seqs, num_q_heads, num_kv_heads,
                                                  max_context_len))
+
+
+def plan_partition_tokens(num_q_heads: int, num_kv_heads: int, head_dim: int,
+                          context_lens_host) -> int:
+    """pa_decode_plan: a partition length (tokens) for decode() / decode_append() from
+    the batch's context lengths as known on the host."""
+    import numpy as np
+    cl = np.ascontiguousarray(np.asarray(context_lens_host, dtype=np.int32))
+    r = load().pa_decode_plan(cl.size, num_q_heads, num_kv_heads, head_dim,
+                              cl.ctypes.data_as(ctypes.c_void_p))
+    if r < 0:
+        raise ValueError("invalid arguments to pa_decode_plan")
+    return int(r)
 
 
 def workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,

@@ -193,6 +193,65 @@ int32_t pa_decode_partition_tokens(int32_t num_seqs, int32_t num_q_heads, int32_
            kBlock;
 }
 
+int32_t pa_decode_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                       int32_t head_dim, const int32_t *context_lens_host)
+{
+    if (num_seqs < 0 || (num_seqs > 0 && !context_lens_host) || head_dim <= 0)
+        return -1;
+    int32_t max_ctx = 0;
+    for (int32_t b = 0; b < num_seqs; ++b) {
+        if (context_lens_host[b] < 0)
+            return -1;
+        if (context_lens_host[b] > max_ctx)
+            max_ctx = context_lens_host[b];
+    }
+    if (check_decode_scalars(num_seqs, num_q_heads, num_kv_heads, head_dim, max_ctx, 0) != PA_OK)
+        return -1;
+    const int32_t auto_pb =
+        choose_part_blocks(num_seqs, num_q_heads, num_kv_heads, head_dim, max_ctx, 0);
+    const int32_t max_blocks = (max_ctx + kBlock - 1) / kBlock;
+    if (max_blocks == 0)
+        return auto_pb * kBlock;
+    // Workgroups that stream at least one block, for partitions of pb blocks (empty
+    // partitions exit at once).  Non-increasing in pb.
+    const int64_t per_seq = (int64_t)num_kv_heads * ((num_q_heads / num_kv_heads + 15) / 16);
+    auto busy_groups = [&](int64_t pb) {
+        int64_t w = 0;
+        for (int32_t b = 0; b < num_seqs; ++b)
+            w += ((context_lens_host[b] + kBlock - 1) / kBlock + pb - 1) / pb;
+        return w * per_seq;
+    };
+    // The longest sequence is cut into the most partitions that still keep every busy
+    // workgroup in one round of the GPU's CUs, and those partitions are made as long as
+    // that count allows (the last one short): measured on the long + shared-prefix
+    // decode, 6 partitions of 408 blocks run 7 % faster than 6 of 344.  When no
+    // partition allows one round, the automatic rule.
+    const int64_t nw = pa::waves_per_group(head_dim);
+    const int64_t max_pb = max_part_blocks(head_dim);
+    int64_t lo = 2 * nw, hi = max_pb < max_blocks ? max_pb : max_blocks;
+    if (lo > hi)
+        lo = hi;
+    if (busy_groups(hi) > pa::kTargetGroups)
+        return auto_pb * kBlock;
+    while (lo < hi) {
+        const int64_t mid = (lo + hi) / 2;
+        if (busy_groups(mid) <= pa::kTargetGroups)
+            hi = mid;
+        else
+            lo = mid + 1;
+    }
+    const int64_t parts = (max_blocks + lo - 1) / lo;  // of the longest sequence
+    if (parts <= 1)                                    // one partition per sequence
+        return auto_pb * kBlock;
+    int64_t pb = (max_blocks - 1) / (parts - 1) / nw * nw;   // longest with that count,
+    const int64_t pb_min = (lo + nw - 1) / nw * nw;           // whole blocks per wave
+    if (pb < pb_min)
+        pb = pb_min;
+    if (pb > max_pb)
+        pb = max_pb;
+    return (int32_t)(pb * kBlock);
+}
+
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t max_context_len,
                                  int32_t partition_tokens)

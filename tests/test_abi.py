@@ -23,7 +23,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("pa_cache_append", "pa_decode", "pa_decode_workspace_bytes",
               "pa_decode_partition_tokens", "pa_pool_bytes", "pa_status_string", "pa_prefill",
-              "pa_decode_append", "pa_copy_blocks", "pa_seq_reserve", "pa_seq_fork", "pa_seq_truncate"):
+              "pa_decode_append", "pa_decode_plan", "pa_copy_blocks", "pa_seq_reserve", "pa_seq_fork", "pa_seq_truncate"):
         assert n in names
 
 
@@ -174,6 +174,27 @@ def test_partition_choice_is_deterministic_and_sane(lib):
     assert f(12, 64, 8, 32768) < 32768
     assert f(0, 64, 8, 0) >= 0
     assert f(2, 3, 2, 10) == -1
+
+
+def test_decode_plan(lib):
+    def plan(hq, hkv, d, lens):
+        arr = (ctypes.c_int32 * max(1, len(lens)))(*lens)
+        return lib.pa_decode_plan(len(lens), hq, hkv, d, arr)
+
+    auto = lambda hq, hkv, n, mx: lib.pa_decode_partition_tokens(n, hq, hkv, mx)
+    # equal lengths: the automatic choice
+    assert plan(64, 8, 128, [4096] * 32) == auto(64, 8, 32, 4096) == 4096
+    assert plan(32, 8, 128, [8160] * 64) == auto(32, 8, 64, 8160)
+    # 4 long + 8 short: the long ones in the most partitions that keep one round
+    # (8 kv-heads x (4 x 6 + 8) = 256 busy workgroups), each as long as 6 allow
+    p = plan(64, 8, 128, [32768] * 4 + [2304] * 8)
+    assert p == 408 * 16
+    assert 8 * (4 * -(-2048 // 408) + 8) <= 256 < 8 * (4 * -(-2048 // 340) + 8)
+    # no partition fits one round: the automatic choice
+    assert plan(8, 8, 128, [65536] * 64) == auto(8, 8, 64, 65536)
+    assert plan(64, 8, 128, []) > 0 and plan(64, 8, 128, []) % 16 == 0
+    assert plan(64, 8, 128, [5, -1]) == -1
+    assert plan(64, 8, 128, [100] * 3) % 16 == 0
 
 
 def test_workspace_matches_partitions(lib):

@@ -172,6 +172,18 @@ def test_decode_config3_forced_partitions(ptok):
     check(w, got, ref, f"config 3 p{ptok}")
 
 
+@pytest.mark.parametrize("i", [4, 5])
+def test_decode_config_planned_partitions(i):
+    """The partition length pa_decode_plan picks from the host context lengths (config
+    5: the long sequences cut into 6 partitions) meets the same bar."""
+    w = config(i)
+    ptok = PA.plan_partition_tokens(w.num_q_heads, w.num_kv_heads, w.head_dim, w.context_lens)
+    say(f"[plan] config {i} planned partition_tokens={ptok}")
+    ref = oracle_decode(w)
+    got, _, _ = gpu_step(w, ptok)
+    check(w, got, ref, f"config {i} planned p{ptok}")
+
+
 def _probe_workload(dtype, d, ctx, hkv=2, group=4, kv_dtype=None):
     """One sequence per target position j: q = 1, keys 0 except key j = 16, and value
     rows holding small integers that name (physical block mod 256, row, kv-head);
