@@ -399,6 +399,32 @@ def check_block_table_example(lib):
     assert out.tobytes() == ref.tobytes()
 
 
+def check_copy_blocks(lib):
+    """Copy-on-write's copy, pinned by what it is for: a sequence whose table points at
+    the copies attends exactly as one pointing at the originals (bit for bit), blocks
+    outside the destinations are untouched, and negative ids are skipped."""
+    for spec in (small_specs()[1], small_specs()[4]):
+        w = W.build(spec)
+        kp, vp = appended(w, lib)
+        n = kp.shape[0]
+        live = sorted({int(x) for b in range(w.num_seqs)
+                       for x in w.block_tables[b, :(int(w.context_lens[b]) + BLOCK - 1) // BLOCK]})
+        # grow the pool so every live block has a fresh destination
+        extra = len(live)
+        kq = np.concatenate([kp, kp[:1].repeat(extra, 0)], 0)
+        vq = np.concatenate([vp, vp[:1].repeat(extra, 0)], 0)
+        dst = list(range(n, n + extra))
+        pairs = np.array([[s_, d_] for s_, d_ in zip(live, dst)] + [[-1, 0], [0, -1]],
+                         np.int32)
+        kc, vc = O.copy_blocks(kq, vq, pairs, w.kv_dtype, lib=lib)
+        remap = dict(zip(live, dst))
+        tables = np.vectorize(lambda x: remap.get(int(x), int(x)))(w.block_tables).astype(np.int32)
+        a, _ = oracle_paged(w, kc, vc, lib=lib)
+        b, _ = oracle_paged(w, kc, vc, tables, lib=lib)
+        assert a.tobytes() == b.tobytes()
+        assert kc[:n].tobytes() == kq[:n].tobytes() and vc[:n].tobytes() == vq[:n].tobytes()
+
+
 # ------------------------------------------------------------------ prefill
 
 def prefill_specs():
@@ -546,4 +572,4 @@ ALL_CHECKS = [check_widen_f16, check_widen_bf16, check_widen_fp8, check_encode_f
               check_permutation, check_weight_sum, check_closed_forms, check_split_combine,
               check_kv_size, check_block_table_example, check_prefill_sdpa,
               check_prefill_bruteforce, check_prefill_chunked_prompt, check_prefill_weight_sum,
-              check_prefill_one_row_is_decode]
+              check_prefill_one_row_is_decode, check_copy_blocks]

@@ -54,6 +54,11 @@ MUTANTS = {
     "prefill_q_row_of_sequence": ("J.q_row = (const char *)A->q + ((size_t)r * A->hq + h)",
                                   "J.q_row = (const char *)A->q + ((size_t)b * A->hq + h)"),
     "prefill_owner_off_by_one": ("if (q_start[mid] <= tok)", "if (q_start[mid] < tok)"),
+    "copy_v_block_skipped": (
+        "        memmove((char *)v_pool + (size_t)dst * bytes, (const char *)v_pool + (size_t)src * bytes,\n                bytes);\n",
+        ""),
+    "copy_to_source": ("memmove((char *)k_pool + (size_t)dst * bytes, (const char *)k_pool + (size_t)src * bytes,",
+                       "memmove((char *)k_pool + (size_t)src * bytes, (const char *)k_pool + (size_t)dst * bytes,"),
 }
 
 
