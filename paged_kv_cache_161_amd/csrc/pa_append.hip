@@ -13,6 +13,8 @@
 // An fp8 pool stores OCP E4M3 codes of x / scale (the KV-cache write fused with its
 // quantisation, one of the fused kernels "Deep dive into vLLM 06" lists): the
 // division is IEEE fp32, the code rounds to nearest-even and saturates at 448.
+#include <type_traits>
+
 #include "pa_common.h"
 #include "pa_fp8.h"
 
@@ -100,6 +102,96 @@ __global__ __launch_bounds__(256) void pa_cache_append_fp8_kernel(AppendArgs a)
                                (size_t)c * 8) = make_uint2(kc[0], kc[1]);
 }
 
+// Groups of 16 consecutive new rows, one workgroup per (group, kv-head).  A group whose
+// 16 slots are one whole block in order (a prompt chunk being ingested) writes that
+// block's K rows contiguously and its V^T rows whole: the 16 rows are staged in LDS and
+// each store covers 8 consecutive tokens of one e, so no store is a partial-sector
+// write.  Any other group takes the per-row path (16-byte K pieces, V scattered by
+// token), as the single-row kernels do.  fp8 pools store E4M3(x / scale).
+template <int DT, int AT, int D>
+__global__ __launch_bounds__(256) void pa_cache_append_group_kernel(AppendArgs a)
+{
+    using In = typename std::conditional<AT == DT_F32, float, uint16_t>::type;
+    using Out = typename std::conditional<DT == DT_F32, float,
+                typename std::conditional<DT == DT_FP8, uint8_t, uint16_t>::type>::type;
+    constexpr int PC = D / 8;                   // 8-element pieces per row
+    __shared__ int s_slot[kBlock];
+    __shared__ In s_v[kBlock][D + 8];
+    const int tid = threadIdx.x;
+    const int h = blockIdx.y;
+    const int i0 = blockIdx.x * kBlock;
+    const int n = min(kBlock, a.num_tokens - i0);
+    if (tid < kBlock)
+        s_slot[tid] = tid < n ? a.slot_mapping[i0 + tid] : -1;
+    __syncthreads();
+    const int s0 = s_slot[0];
+    bool whole = n == kBlock && s0 >= 0 && s0 % kBlock == 0 &&
+                 (int64_t)s0 < (int64_t)a.num_blocks * kBlock;
+#pragma unroll
+    for (int j = 1; j < kBlock; ++j)
+        whole = whole && s_slot[j] == s0 + j;
+
+    auto conv = [&](In x, float scale) -> Out {
+        if constexpr (DT == DT_FP8)
+            return (Out)e4m3_of_16(x, a.bf16 != 0, scale);
+        else
+            return (Out)x;
+    };
+    const In *kin = static_cast<const In *>(a.k_new);
+    const In *vin = static_cast<const In *>(a.v_new);
+    Out *kpool = static_cast<Out *>(a.k_pool);
+    Out *vpool = static_cast<Out *>(a.v_pool);
+
+    if (whole) {
+        const size_t tile = ((size_t)(s0 / kBlock) * a.num_kv_heads + h) * kBlock * D;
+        for (int c = tid; c < kBlock * PC; c += blockDim.x) {
+            const int j = c / PC, col = (c % PC) * 8;
+            const size_t src = ((size_t)(i0 + j) * a.num_kv_heads + h) * D + col;
+            In kx[8], vx[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                kx[e] = kin[src + e];
+                vx[e] = vin[src + e];
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                kpool[tile + (size_t)j * D + col + e] = conv(kx[e], a.k_scale);
+                s_v[j][col + e] = vx[e];
+            }
+        }
+        __syncthreads();
+        for (int c = tid; c < D * 2; c += blockDim.x) {
+            const int d = c / 2, t0 = (c % 2) * 8;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                vpool[tile + (size_t)d * kBlock + t0 + e] = conv(s_v[t0 + e][d], a.v_scale);
+        }
+        return;
+    }
+    for (int c = tid; c < n * PC; c += blockDim.x) {
+        const int j = c / PC, col = (c % PC) * 8;
+        const int slot = s_slot[j];
+        if (slot < 0 || (int64_t)slot >= (int64_t)a.num_blocks * kBlock)
+            continue;
+        const size_t tile = ((size_t)(slot / kBlock) * a.num_kv_heads + h) * kBlock * D;
+        const int off = slot % kBlock;
+        const size_t src = ((size_t)(i0 + j) * a.num_kv_heads + h) * D + col;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            kpool[tile + (size_t)off * D + col + e] = conv(kin[src + e], a.k_scale);
+            vpool[tile + (size_t)(col + e) * kBlock + off] = conv(vin[src + e], a.v_scale);
+        }
+    }
+}
+
+template <int DT, int AT, int D>
+hipError_t launch_append_group_t(const AppendArgs &a, hipStream_t stream)
+{
+    dim3 grid((a.num_tokens + kBlock - 1) / kBlock, a.num_kv_heads);
+    hipLaunchKernelGGL((pa_cache_append_group_kernel<DT, AT, D>), grid, dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
 template <int D>
 hipError_t launch_append_fp8_t(const AppendArgs &a, hipStream_t stream)
 {
@@ -159,6 +251,30 @@ hipError_t launch_copy_blocks(void *k_pool, void *v_pool, const int32_t *pairs, 
 hipError_t launch_append(int dtype, int act_dtype, int head_dim, const AppendArgs &a,
                          hipStream_t stream)
 {
+    // 16 rows or more (a prompt chunk): groups of 16, whole blocks written whole
+    if (a.num_tokens >= kBlock && a.num_kv_heads <= 65535) {
+        AppendArgs b = a;
+        b.bf16 = act_dtype == DT_BF16 ? 1 : 0;
+#define PA_AG_CASE(DT, AT, D)                                                      \
+        if (dtype == DT && act_dtype == AT && head_dim == D)                      \
+            return launch_append_group_t<DT, AT, D>(b, stream);
+        PA_AG_CASE(DT_F32, DT_F32, 64)
+        PA_AG_CASE(DT_F32, DT_F32, 128)
+        PA_AG_CASE(DT_F16, DT_F16, 64)
+        PA_AG_CASE(DT_F16, DT_F16, 128)
+        PA_AG_CASE(DT_F16, DT_F16, 256)
+        PA_AG_CASE(DT_BF16, DT_BF16, 64)
+        PA_AG_CASE(DT_BF16, DT_BF16, 128)
+        PA_AG_CASE(DT_BF16, DT_BF16, 256)
+        PA_AG_CASE(DT_FP8, DT_F16, 64)
+        PA_AG_CASE(DT_FP8, DT_F16, 128)
+        PA_AG_CASE(DT_FP8, DT_F16, 256)
+        PA_AG_CASE(DT_FP8, DT_BF16, 64)
+        PA_AG_CASE(DT_FP8, DT_BF16, 128)
+        PA_AG_CASE(DT_FP8, DT_BF16, 256)
+#undef PA_AG_CASE
+        return hipErrorInvalidValue;
+    }
     if (dtype == DT_FP8) {
         if (act_dtype != DT_F16 && act_dtype != DT_BF16)
             return hipErrorInvalidValue;
