@@ -13,8 +13,10 @@ layers of a real step do, so K/V is not reused from the 256 MB last-level cache.
 Printed: ONE JSON line on stdout.
   value      KV GB/s over the whole step (algorithmic K+V bytes / wall time per step)
   roofline   the decode call, timed over back-to-back launches with HIP events on the
-             launching stream, against the 8 TB/s HBM peak; traffic from the committed
-             rocprofv3 counter passes when they match the current kernel source
+             launching stream, against the 8 TB/s HBM peak (unique K/V bytes; shared
+             prefix blocks count once) and against the read rate a plain 16-byte-load
+             kernel measures in the same run; traffic from the committed rocprofv3
+             counter passes when they match the current kernel source
   cpu_baseline  the fp64 oracle on the host cores, on the same workload
 Progress goes to stderr.
 """
@@ -77,7 +79,7 @@ def kernel_source_digest():
 def recorded_traffic(workload, ptok):
     """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE passes,
     scaled by the calibration copy; None unless they were taken on this exact kernel
-    source and workload."""
+    source, workload and partition length."""
     path = os.path.join(ROOT, "profiles", "pa_decode_counters.json")
     try:
         with open(path) as f:
@@ -85,7 +87,8 @@ def recorded_traffic(workload, ptok):
     except OSError:
         return None
     entry = rec.get("workloads", {}).get(workload)
-    if not entry or ptok != 0 or rec.get("kernel_source_sha256") != kernel_source_digest():
+    if (not entry or entry.get("partition_tokens") != ptok
+            or rec.get("kernel_source_sha256") != kernel_source_digest()):
         return None
     return entry["traffic_bytes_per_launch"]
 
@@ -164,6 +167,47 @@ def calibration_copy(dev):
     log(f"[bench] calibration copy: {CALIBRATION_BYTES} bytes read, {CALIBRATION_BYTES} "
         "written")
     del src, dst
+
+
+READ_PROBE_BYTES = 2 << 30
+
+
+def measured_read_ceiling(dev, launches=10):
+    """The practical HBM read rate on this device: the benchmark's plain read kernel
+    (16-byte loads, grid-stride, libpa_hbm_probe.so) over 2 GiB, median of `launches`
+    launches timed with HIP events on the launching stream.  None if the probe library
+    is not built."""
+    import ctypes
+    path = os.path.join(ROOT, "paged_kv_cache_161_amd", "libpa_hbm_probe.so")
+    if not os.path.exists(path):
+        log("[bench] read probe not built; no measured read ceiling")
+        return None
+    lib = ctypes.CDLL(path)
+    lib.pa_probe_read.restype = ctypes.c_int32
+    lib.pa_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                  ctypes.c_int32, ctypes.c_void_p]
+    buf = torch.ones(READ_PROBE_BYTES, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    groups = torch.cuda.get_device_properties(dev).multi_processor_count * 8
+    stream = torch.cuda.current_stream(dev)
+    times = []
+    for r in range(launches + 2):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        rc = lib.pa_probe_read(buf.data_ptr(), READ_PROBE_BYTES, sink.data_ptr(), groups,
+                               ctypes.c_void_p(stream.cuda_stream))
+        e1.record(stream)
+        if rc != 0:
+            raise RuntimeError(f"pa_probe_read returned {rc}")
+        torch.cuda.synchronize()
+        if r >= 2:
+            times.append(e0.elapsed_time(e1) * 1e-3)
+    del buf, sink
+    gbs = READ_PROBE_BYTES / statistics.median(times) / 1e9
+    log(f"[bench] measured read ceiling: {gbs:.0f} GB/s (2 GiB plain read, median of "
+        f"{launches})")
+    return gbs
 
 
 def prefill_flops(w):
@@ -429,9 +473,12 @@ def main():
     e1.record(stream)
     torch.cuda.synchronize()
     dur = e0.elapsed_time(e1) * 1e-3 / n_l
-    achieved = kv_bytes / dur / 1e9
+    # the least HBM traffic the method must move is each physical K/V row once: shared
+    # prefix blocks count once (the logical rate is reported beside it)
+    achieved = uniq_bytes / dur / 1e9
     log(f"[bench] decode_append call: {dur * 1e6:.1f} us per launch over {n_l} back-to-back "
-        f"launches -> {achieved:.0f} GB/s")
+        f"launches -> {achieved:.0f} GB/s unique, {kv_bytes / dur / 1e9:.0f} logical")
+    ceiling = measured_read_ceiling(dev)
     traffic = recorded_traffic(w.spec.name, ptok)
 
     # the same step captured as one HIP graph per layer pool and replayed (the
@@ -517,7 +564,11 @@ def main():
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "launch_us_mean": round(dur * 1e6, 2),
-                     "bytes_per_launch": kv_bytes},
+                     "bytes_per_launch": uniq_bytes,
+                     "achieved_logical": round(kv_bytes / dur / 1e9, 1),
+                     "measured_read_ceiling": None if ceiling is None else round(ceiling, 1),
+                     "frac_of_measured_read_ceiling":
+                         None if ceiling is None else round(achieved / ceiling, 4)},
         "cpu_baseline": cpu,
         "parity": parity,
         "context_figures": {"A100_ridge_flop_per_byte": 156, "H100_hbm_TBps": 3.35},

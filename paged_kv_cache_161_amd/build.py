@@ -1,4 +1,6 @@
-"""Build the HIP library libpa_mi355x.so for gfx950 (in-tree, next to this file).
+"""Build the HIP library libpa_mi355x.so for gfx950 (in-tree, next to this file), and
+the benchmark's HBM read probe libpa_hbm_probe.so (a measurement helper, no part of
+the attention path).
 
 hipcc cross-compiles without a GPU.  Packed-fp32 instruction selection is switched
 off for device code; hipcc's host pass warns that it does not know that feature,
@@ -12,6 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libpa_mi355x.so")
+PROBE_LIB = os.path.join(HERE, "libpa_hbm_probe.so")
 SOURCES = ["pa_api.cpp", "pa_alloc.cpp", "pa_decode.hip", "pa_append.hip", "pa_prefill.hip"]
 ARCH = "gfx950"
 
@@ -43,5 +46,19 @@ def build_library(out=LIB, verbose=False):
     return out
 
 
+def build_probe(out=PROBE_LIB):
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    tmp = out + ".tmp"
+    cmd = [hipcc, *hip_flags(), "-shared", "-x", "hip",
+           os.path.join(CSRC, "hbm_read_probe.hip"), "-o", tmp]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError("hipcc failed on hbm_read_probe.hip")
+    os.replace(tmp, out)
+    return out
+
+
 if __name__ == "__main__":
     print(build_library(verbose="-v" in sys.argv))
+    print(build_probe())
