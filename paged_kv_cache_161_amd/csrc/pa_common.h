@@ -11,6 +11,10 @@ enum Dt : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_FP8 = 3 };
 constexpr int kBlock = 16;            // tokens per physical block
 constexpr int kWave = 64;             // CDNA4 wavefront width
 
+// Online softmax: the running max is moved only when a score exceeds it by more than
+// this many doublings (exp2 domain), so weights stay <= 2^kRescaleSlack = 256.
+constexpr float kRescaleSlack = 8.0f;
+
 // Arguments of the decode partition kernel (by value, host -> kernel).
 struct DecodeArgs {
     const void *k_pool;               // [num_blocks][hkv][16][D]

@@ -599,12 +599,15 @@ __global__ __launch_bounds__(NW *kWave, min_waves_per_simd(DT, D, PF)) void pa_d
                 x[j] = (4 * g + j < valid) ? x[j] : -INFINITY;
             mask_tail_v<DT, AT, D>(t, valid, g);
         }
-        // The running max of a head changes only if one of its 4 lanes sees a score
-        // above it; when no lane of the wave does, the rescale factor would be exactly
-        // 1, so the cross-row max, the exp2 and the rescale of O and l are skipped
-        // (bit-identical to doing them).  After the first blocks this is the usual case.
+        // The running max is only a reference point: O and l are both scaled by
+        // 2^(-m), which cancels in O / l (and in the merges of waves and partitions).
+        // It is moved only when a score exceeds it by more than kRescaleSlack (weights
+        // stay <= 256), so the cross-row max, the exp2 and the rescale of O and l run
+        // about once per wave instead of whenever a head sees a new maximum.  An empty
+        // history (-inf) always takes the first finite max; an all-masked lane never
+        // moves it.
         const float lmx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-        if (__any(lmx > m_run)) {
+        if (__any(lmx - m_run > kRescaleSlack)) {
             const float m_new = fmaxf(m_run, wave_max_rows(lmx));
             const float alpha = fast_exp2(m_run - m_new);
 #pragma unroll

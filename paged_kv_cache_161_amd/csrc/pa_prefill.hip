@@ -359,6 +359,12 @@ __global__ __launch_bounds__(NW *kWave, C <= 2 ? 2 : 1) void pa_prefill_kernel(P
         mneg[c] = 0.f;
     }
     const float sl = a.scale_log2;           // > 0 (host-checked): max commutes with it
+    // The running max is only a reference point: O and l are both scaled by 2^(-m sl),
+    // which cancels in O / l whatever m is.  It is therefore moved only when a score
+    // exceeds it by more than 2^kRescaleSlack in the exp2 domain; weights stay at most
+    // 2^kRescaleSlack (well inside 16-bit and fp32 range) and the rescale of O, which
+    // would otherwise run whenever any row sees a new maximum, runs about once.
+    const float grow_thr = fminf(kRescaleSlack / sl, 3.0e38f);
     const u32x4 ones = {one_pair<AT>(), one_pair<AT>(), one_pair<AT>(), one_pair<AT>()};
 
     // S^T of step s from K buffer kb: all of the step's K fragments are read before
@@ -383,10 +389,10 @@ __global__ __launch_bounds__(NW *kWave, C <= 2 ? 2 : 1) void pa_prefill_kernel(P
                     sc[c][tl] = mma32<AT>(kf[tl][kc], qf[c][kc], sc[c][tl]);
     };
 
-    // Step s's scores: causal mask, running max, and the rescale of O and l when the
-    // max grows.  Only steps reaching past the tile's first position can hold keys
-    // after a row's position.  The rescale is skipped when no lane's max grows: its
-    // factor would be exactly 1.
+    // Step s's scores: causal mask, running max, and the rescale of O and l when some
+    // score exceeds a row's reference max by more than the slack.  Only steps reaching
+    // past the tile's first position can hold keys after a row's position.  An empty
+    // history (-inf) always takes the first finite max; an all-masked lane never moves it.
     auto mask_max = [&](int s, f32x4 (&sc)[C][2]) {
         const bool diag = 32 * s + 31 > first;
 #pragma unroll
@@ -405,7 +411,7 @@ __global__ __launch_bounds__(NW *kWave, C <= 2 ? 2 : 1) void pa_prefill_kernel(P
 #pragma unroll
         for (int c = 0; c < C; ++c) {
             lmx[c] = max8(sc[c]);
-            grow |= lmx[c] > m_run[c];
+            grow |= lmx[c] - m_run[c] > grow_thr;
         }
         if (__any(grow)) {
 #pragma unroll
