@@ -367,16 +367,16 @@ __global__ __launch_bounds__(NW *kWave, C <= 2 ? 2 : 1) void pa_prefill_kernel(P
     const float grow_thr = fminf(kRescaleSlack / sl, 3.0e38f);
     const u32x4 ones = {one_pair<AT>(), one_pair<AT>(), one_pair<AT>(), one_pair<AT>()};
 
-    // S^T of step s from K buffer kb: all of the step's K fragments are read before
-    // the first product; the e-chunk is outermost so the 2 C accumulators form
-    // independent chains.
+    // S^T of step s from K buffer kb.  The K fragments are read e-chunk-major, in the
+    // order the products use them; the e-chunk is outermost so the 2 C accumulators
+    // form independent chains.
     auto qk = [&](int kb, f32x4 (&sc)[C][2]) {
-        u32x4 kf[2][NKC];
+        u32x4 kf[NKC][2];
 #pragma unroll
-        for (int tl = 0; tl < 2; ++tl)
+        for (int kc = 0; kc < NKC; ++kc)
 #pragma unroll
-            for (int kc = 0; kc < NKC; ++kc)
-                kf[tl][kc] = s_k[kb][(tl * NKC + kc) * kWave + lane];
+            for (int tl = 0; tl < 2; ++tl)
+                kf[kc][tl] = s_k[kb][(tl * NKC + kc) * kWave + lane];
 #pragma unroll
         for (int c = 0; c < C; ++c)
             sc[c][0] = sc[c][1] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -386,7 +386,7 @@ __global__ __launch_bounds__(NW *kWave, C <= 2 ? 2 : 1) void pa_prefill_kernel(P
             for (int tl = 0; tl < 2; ++tl)
 #pragma unroll
                 for (int c = 0; c < C; ++c)
-                    sc[c][tl] = mma32<AT>(kf[tl][kc], qf[c][kc], sc[c][tl]);
+                    sc[c][tl] = mma32<AT>(kf[kc][tl], qf[c][kc], sc[c][tl]);
     };
 
     // Step s's scores: causal mask, running max, and the rescale of O and l when some
@@ -500,21 +500,35 @@ __global__ __launch_bounds__(NW *kWave, C <= 2 ? 2 : 1) void pa_prefill_kernel(P
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
                 const int it = 2 * pr + u;
+                qk(u ^ 1, sc[u ^ 1]);                // step it+1's scores
                 u32x4 vf[NDB];
 #pragma unroll
                 for (int n = 0; n < NDB; ++n)
                     vf[n] = s_v[u][n * kWave + lane];
-                qk(u ^ 1, sc[u ^ 1]);
                 u32x4 pb[C];
                 weights(sc[u], pb);
                 pv(vf, pb);
-                // issue order: the K and V fragment reads, then each QK product
-                // followed by a share of the weights' vector work, then the PV products
-                __builtin_amdgcn_sched_group_barrier(0x100, 2 * NKC + NDB, 0);
+                // Issue order.  All 8 waves leave the barrier together, so fragment
+                // reads issued in one burst keep the LDS busy while the MFMA pipes
+                // wait; instead the reads are spread over the QK products, each one
+                // e-chunk or more ahead of its use: the first two e-chunks' K
+                // fragments, then per e-chunk its QK products (each followed by a
+                // share of step it's weights), with the later K fragments and the V
+                // fragments issued between them; then the PV and normaliser products.
+                __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-                for (int k = 0; k < 2 * NKC * C; ++k) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+                for (int kc = 0; kc < NKC; ++kc) {
+#pragma unroll
+                    for (int k = 0; k < 2 * C; ++k) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+                    }
+                    if (kc == 0)
+                        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                    else if (kc == 1)
+                        __builtin_amdgcn_sched_group_barrier(0x100, 2 + NDB / 2, 0);
+                    else if (kc == 2)
+                        __builtin_amdgcn_sched_group_barrier(0x100, NDB / 2, 0);
                 }
                 __builtin_amdgcn_sched_group_barrier(0x008, NDB * C + C, 0);
                 stash_k(u, u);
