@@ -139,7 +139,7 @@ __device__ __forceinline__ u32x4 keep_tokens8(u32x4 v, int t0, int valid)
     return v;
 }
 
-template <int DT, int AT, int D, int NW, int C>
+template <int DT, int AT, int D, int NW, int C, bool IDLE>
 __global__ __launch_bounds__(NW *kWave, C <= 2 ? 2 : 1) void pa_prefill_kernel(PrefillArgs a)
 {
     using Elem = typename std::conditional<DT == DT_FP8, uint8_t, uint16_t>::type;
@@ -467,7 +467,8 @@ __global__ __launch_bounds__(NW *kWave, C <= 2 ? 2 : 1) void pa_prefill_kernel(P
     // loads and waits, so each wait covers exactly the slot it needs.  Loads past the
     // last step are clamped to it; steps past the last stage zeros, and every key of
     // theirs lies after every row's position, so they are masked out entirely and
-    // change nothing.
+    // change nothing.  Every LDS buffer is rewritten only after a barrier that follows
+    // all reads of its previous contents.
     if (nsteps > 0) {
         const int last = nsteps - 1;
         int raw[2], ph_a[2], ph_b[2];
@@ -492,56 +493,81 @@ __global__ __launch_bounds__(NW *kWave, C <= 2 ? 2 : 1) void pa_prefill_kernel(P
         fetch_v(ph_a, 0);                            // V of step 2
         table(min(4, last), raw);
         __syncthreads();
-        f32x4 sc[2][C][2];
-        qk(0, sc[0]);
-        mask_max(0, sc[0]);
+        // Step it's staging between its products and the barrier: K of step it+2 and
+        // V of step it+1 into the LDS buffers those steps last used, then the freed
+        // register slots reissued for K of step it+4 and V of step it+3.
+        auto stage = [&](int it, int u) {
+            stash_k(u, u);
+            stash_v(it + 1, u ^ 1, u ^ 1);
+            int ph_n[2];
+            resolve(min(it + 4, last), raw, ph_n);
+            fetch_k(ph_n, u);                        // K of step it+4
+            fetch_v(ph_k, u ^ 1);                    // V of step it+3
+            ph_k[0] = ph_n[0];
+            ph_k[1] = ph_n[1];
+            table(min(it + 5, last), raw);
+        };
         const int npairs = (nsteps + 1) / 2;
-        for (int pr = 0; pr < npairs; ++pr) {
+        // A wave whose rows are all idle (a short chunk, a decode row in the tile)
+        // runs only the staging: the same loads, stores and barriers, no products.
+        // Launches where every tile is full (IDLE false) carry no such branch.
+        const bool idle = IDLE && wave * C * 16 >= n_here * a.group;   // wave-uniform
+        f32x4 sc[2][C][2];
+        if (!idle) {
+            qk(0, sc[0]);
+            mask_max(0, sc[0]);
+        }
+        // Pass 0 restages buffer 0 (K of step 2): every wave's reads of step 0's K
+        // must be done first.
+        __syncthreads();
+        if (idle) {
+            for (int pr = 0; pr < npairs; ++pr) {
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int it = 2 * pr + u;
-                qk(u ^ 1, sc[u ^ 1]);                // step it+1's scores
-                u32x4 vf[NDB];
-#pragma unroll
-                for (int n = 0; n < NDB; ++n)
-                    vf[n] = s_v[u][n * kWave + lane];
-                u32x4 pb[C];
-                weights(sc[u], pb);
-                pv(vf, pb);
-                // Issue order.  All 8 waves leave the barrier together, so fragment
-                // reads issued in one burst keep the LDS busy while the MFMA pipes
-                // wait; instead the reads are spread over the QK products, each one
-                // e-chunk or more ahead of its use: the first two e-chunks' K
-                // fragments, then per e-chunk its QK products (each followed by a
-                // share of step it's weights), with the later K fragments and the V
-                // fragments issued between them; then the PV and normaliser products.
-                __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-                for (int kc = 0; kc < NKC; ++kc) {
-#pragma unroll
-                    for (int k = 0; k < 2 * C; ++k) {
-                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
-                    }
-                    if (kc == 0)
-                        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-                    else if (kc == 1)
-                        __builtin_amdgcn_sched_group_barrier(0x100, 2 + NDB / 2, 0);
-                    else if (kc == 2)
-                        __builtin_amdgcn_sched_group_barrier(0x100, NDB / 2, 0);
+                for (int u = 0; u < 2; ++u) {
+                    stage(2 * pr + u, u);
+                    __syncthreads();
                 }
-                __builtin_amdgcn_sched_group_barrier(0x008, NDB * C + C, 0);
-                stash_k(u, u);
-                stash_v(it + 1, u ^ 1, u ^ 1);
-                int ph_n[2];
-                resolve(min(it + 4, last), raw, ph_n);
-                fetch_k(ph_n, u);                    // K of step it+4
-                fetch_v(ph_k, u ^ 1);                // V of step it+3
-                ph_k[0] = ph_n[0];
-                ph_k[1] = ph_n[1];
-                table(min(it + 5, last), raw);
-                __syncthreads();
-                mask_max(it + 1, sc[u ^ 1]);
+            }
+        } else {
+            for (int pr = 0; pr < npairs; ++pr) {
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const int it = 2 * pr + u;
+                    qk(u ^ 1, sc[u ^ 1]);                // step it+1's scores
+                    u32x4 vf[NDB];
+#pragma unroll
+                    for (int n = 0; n < NDB; ++n)
+                        vf[n] = s_v[u][n * kWave + lane];
+                    u32x4 pb[C];
+                    weights(sc[u], pb);
+                    pv(vf, pb);
+                    // Issue order.  All 8 waves leave the barrier together, so fragment
+                    // reads issued in one burst keep the LDS busy while the MFMA pipes
+                    // wait; instead the reads are spread over the QK products, each one
+                    // e-chunk or more ahead of its use: the first two e-chunks' K
+                    // fragments, then per e-chunk its QK products (each followed by a
+                    // share of step it's weights), with the later K fragments and the V
+                    // fragments issued between them; then the PV and normaliser products.
+                    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+                    for (int kc = 0; kc < NKC; ++kc) {
+#pragma unroll
+                        for (int k = 0; k < 2 * C; ++k) {
+                            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                            __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+                        }
+                        if (kc == 0)
+                            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                        else if (kc == 1)
+                            __builtin_amdgcn_sched_group_barrier(0x100, 2 + NDB / 2, 0);
+                        else if (kc == 2)
+                            __builtin_amdgcn_sched_group_barrier(0x100, NDB / 2, 0);
+                    }
+                    __builtin_amdgcn_sched_group_barrier(0x008, NDB * C + C, 0);
+                    stage(it, u);
+                    __syncthreads();
+                    mask_max(it + 1, sc[u ^ 1]);
+                }
             }
         }
     }
@@ -569,11 +595,14 @@ __global__ __launch_bounds__(NW *kWave, C <= 2 ? 2 : 1) void pa_prefill_kernel(P
 }
 
 template <int DT, int AT, int D>
-hipError_t launch_prefill_t(const PrefillArgs &a, int grid, hipStream_t stream)
+hipError_t launch_prefill_t(const PrefillArgs &a, int grid, bool idle, hipStream_t stream)
 {
-    hipLaunchKernelGGL((pa_prefill_kernel<DT, AT, D, kPrefillWaves, kPrefillCols>),
-                       dim3(grid),
-                       dim3(kPrefillWaves * kWave), 0, stream, a);
+    if (idle)
+        hipLaunchKernelGGL((pa_prefill_kernel<DT, AT, D, kPrefillWaves, kPrefillCols, true>),
+                           dim3(grid), dim3(kPrefillWaves * kWave), 0, stream, a);
+    else
+        hipLaunchKernelGGL((pa_prefill_kernel<DT, AT, D, kPrefillWaves, kPrefillCols, false>),
+                           dim3(grid), dim3(kPrefillWaves * kWave), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -586,9 +615,16 @@ hipError_t launch_prefill(int dtype, int act_dtype, int head_dim, const PrefillA
 {
     const int pairs = a.num_seqs * a.num_kv_heads;
     const int grid = (pairs + kXcds - 1) / kXcds * kXcds * a.num_qtiles;
+    // Every tile is full, and so every wave has rows, when all chunks have the
+    // longest length, that length is a whole number of tiles, and a tile's rows reach
+    // the last wave; otherwise idle waves may occur and the kernel that lets them
+    // skip the products is launched.
+    const bool full = (int64_t)a.num_tokens == (int64_t)a.num_seqs * a.max_query_len &&
+                      a.max_query_len % a.q_tile == 0 &&
+                      a.q_tile * a.group > (kPrefillWaves - 1) * kPrefillCols * 16;
 #define PA_PF_CASE(DT, AT, D)                                                      \
     if (dtype == DT && act_dtype == AT && head_dim == D)                          \
-        return launch_prefill_t<DT, AT, D>(a, grid, stream);
+        return launch_prefill_t<DT, AT, D>(a, grid, !full, stream);
     PA_PF_CASE(DT_BF16, DT_BF16, 128)
     PA_PF_CASE(DT_BF16, DT_BF16, 64)
     PA_PF_CASE(DT_F16, DT_F16, 128)

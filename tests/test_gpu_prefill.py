@@ -1,6 +1,8 @@
 """GPU parity of paged prefill (pa_prefill through the C ABI) against the fp64 oracle.
 
-Small workloads are compared on every output; the two full-size prefill workloads
+Small workloads are compared on every output (ragged chunks, which launch the kernel
+whose idle waves skip the products, and equal whole-tile chunks, which launch the one
+without that path); the two full-size prefill workloads
 (16 x 512-token chunks over 4096-token contexts, and a mixed prefill + decode batch)
 on sampled query rows, each of which the oracle computes as its own one-row chunk.
 Bars as for decode: max |err| <= 2e-2 and mean <= 5e-3 for 16-bit activations; the
@@ -46,6 +48,10 @@ SMALL = [
            kv_dtype="fp8", k_scale=0.0117, v_scale=0.0093, query_lens=[30, 12, 100]),
     W.Spec("pf_fp8_f16_d64", "f16", 16, 1, 64, [77, 160], seed=37, spare_blocks=1,
            kv_dtype="fp8", k_scale=0.25, v_scale=0.0625, query_lens=[77, 33]),
+    # every chunk the same whole number of 32-position tiles: the launch without the
+    # idle-wave path
+    W.Spec("pf_full_tiles_bf16", "bf16", 64, 8, 128, [100, 64, 333], seed=40, spare_blocks=1,
+           query_lens=[64, 64, 64]),
 ]
 
 
