@@ -501,6 +501,23 @@ def main():
     torch.cuda.synchronize()
     graph_ms = (time.perf_counter() - t_start) * 1e3 / args.steps
     log(f"[bench] {args.steps} graph-replayed steps: {graph_ms * 1e3:.1f} us/step")
+    # as a serving loop captures a whole step: the four layers' steps in one graph
+    g4 = torch.cuda.CUDAGraph()
+    cap.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.graph(g4, stream=cap):
+        for i in range(LAYERS):
+            step(i)
+    torch.cuda.current_stream(dev).wait_stream(cap)
+    reps = max(1, args.steps // LAYERS)
+    for _ in range(max(1, args.warmup // LAYERS)):
+        g4.replay()
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(reps):
+        g4.replay()
+    torch.cuda.synchronize()
+    graph4_ms = (time.perf_counter() - t_start) * 1e3 / (reps * LAYERS)
+    log(f"[bench] {reps} replays of one {LAYERS}-layer graph: {graph4_ms * 1e3:.1f} us per layer step")
 
     # parity on the timed inputs (sampled rows against the oracle)
     parity = None
@@ -557,6 +574,7 @@ def main():
         "two_call_ms_per_step": round(two_call_ms, 5),
         "graph_ms_per_step": round(graph_ms, 5),
         "graph_tokens_per_s": round(w.num_seqs / (graph_ms * 1e-3), 1),
+        "graph4_ms_per_step": round(graph4_ms, 5),
         "unique_kv_bytes_per_step": uniq_bytes,
         "roofline": {"bound": "hbm", "kernel": "pa_decode_partition with the fused append "
                                                "(+ pa_decode_reduce when a sequence spans "
