@@ -112,7 +112,8 @@ size_t pa_pool_bytes(int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
  * quantisation).  A negative slot means "no row" (padding) and is skipped.  A slot
  * >= num_blocks * 16 is also skipped (never written), so a bad slot cannot corrupt
  * memory outside the pool.  Two rows with the same slot race (caller
- * error).  num_tokens == 0 is a valid no-op. */
+ * error).  num_tokens == 0 is a valid no-op; num_tokens * num_kv_heads above 2^34
+ * returns PA_ERR_UNSUPPORTED. */
 pa_status pa_cache_append(const pa_kv_pool *pool, const void *k_new, const void *v_new,
                           const int32_t *slot_mapping, int32_t num_tokens, void *stream);
 
@@ -153,7 +154,8 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
  *                  >= ceil(context_lens[s] / 16) are never read
  *   context_lens   [num_seqs] int32, device; token count attended by each sequence
  *                  (the step's own token included: append first, then decode)
- *   max_context_len  host-side upper bound of context_lens, sizes the launch grid
+ *   max_context_len  host-side upper bound of context_lens, sizes the launch grid;
+ *                  at most INT32_MAX - 16 (PA_ERR_UNSUPPORTED above)
  *   partition_tokens 0 = automatic; otherwise a positive multiple of 16: the KV axis
  *                  of each sequence is cut into partitions of this many tokens,
  *                  computed independently and merged by the max/normaliser rule

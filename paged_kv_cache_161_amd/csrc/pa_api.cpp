@@ -96,6 +96,8 @@ pa_status check_decode_scalars(int32_t num_seqs, int32_t num_q_heads, int32_t nu
 {
     if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_context_len < 0)
         return PA_ERR_INVALID_ARG;
+    if (max_context_len > INT32_MAX - kBlock)         // block counts stay in int32
+        return PA_ERR_UNSUPPORTED;
     if (num_q_heads % num_kv_heads != 0)
         return PA_ERR_INVALID_ARG;
     if (partition_tokens < 0 || partition_tokens % kBlock != 0)
@@ -144,6 +146,8 @@ pa_status pa_cache_append(const pa_kv_pool *pool, const void *k_new, const void 
         return PA_ERR_INVALID_ARG;
     if (num_tokens == 0)
         return PA_OK;
+    if ((int64_t)num_tokens * pool->num_kv_heads > (int64_t(1) << 34))   // launch size
+        return PA_ERR_UNSUPPORTED;
     if (!k_new || !v_new || !slot_mapping)
         return PA_ERR_INVALID_ARG;
     pa::AppendArgs a;
@@ -393,6 +397,8 @@ pa_status pa_prefill(const pa_kv_pool *pool, const void *q, void *out, int32_t n
     if (group > rows)
         return PA_ERR_UNSUPPORTED;
     if ((int64_t)num_query_tokens * num_q_heads > INT32_MAX)
+        return PA_ERR_UNSUPPORTED;
+    if (max_context_len > INT32_MAX - kBlock)         // block counts stay in int32
         return PA_ERR_UNSUPPORTED;
     if (num_seqs == 0 || num_query_tokens == 0 || max_query_len == 0)
         return PA_OK;

@@ -187,7 +187,7 @@ __global__ __launch_bounds__(256) void pa_cache_append_group_kernel(AppendArgs a
 template <int DT, int AT, int D>
 hipError_t launch_append_group_t(const AppendArgs &a, hipStream_t stream)
 {
-    dim3 grid((a.num_tokens + kBlock - 1) / kBlock, a.num_kv_heads);
+    dim3 grid((unsigned)(((int64_t)a.num_tokens + kBlock - 1) / kBlock), a.num_kv_heads);
     hipLaunchKernelGGL((pa_cache_append_group_kernel<DT, AT, D>), grid, dim3(256), 0, stream, a);
     return hipGetLastError();
 }

@@ -521,7 +521,8 @@ __global__ __launch_bounds__(NW *kWave, min_waves_per_simd(DT, D, PF)) void pa_d
     } else {
         ctx = a.context_lens[b];
     }
-    const int nblk_seq = (ctx + kBlock - 1) / kBlock;
+    // unsigned: defined for any device value (a negative one is flagged just below)
+    const int nblk_seq = ctx > 0 ? (int)(((unsigned)ctx + (kBlock - 1)) / kBlock) : 0;
     const bool bad_ctx = ctx < 0 || ctx > a.max_context_len || nblk_seq > a.max_blocks;
     const int lb_end = min(lb_begin + a.part_blocks, nblk_seq);
 
@@ -792,7 +793,7 @@ __global__ __launch_bounds__(256) void pa_decode_reduce(DecodeArgs a)
     const int gs = min(16, a.group - chunk * 16);
     const int hq0 = kvh * a.group + chunk * 16;
     const int ctx = a.context_lens[b];
-    const int nblk = (ctx + kBlock - 1) / kBlock;
+    const int nblk = ctx > 0 ? (int)(((unsigned)ctx + (kBlock - 1)) / kBlock) : 0;
     const bool bad_ctx = ctx < 0 || ctx > a.max_context_len || nblk > a.max_blocks;
     if (bad_ctx || nblk <= a.part_blocks)
         return;                                  // finished by the partition kernel

@@ -179,7 +179,7 @@ __global__ __launch_bounds__(NW *kWave, C <= 2 ? 2 : 1) void pa_prefill_kernel(P
         return;
     const int ctx = a.context_lens[b];
     const bool bad_ctx = ctx < 0 || ctx > a.max_context_len ||
-                         (ctx + kBlock - 1) / kBlock > a.max_blocks;
+                         (int)(((unsigned)ctx + (kBlock - 1)) / kBlock) > a.max_blocks;
     const int n_here = min(a.q_tile, q_len - p_lo);      // query positions in this tile
     const int first = ctx - q_len + p_lo;                // position of the tile's first
     const int key_end = bad_ctx ? 0 : max(0, first + n_here);   // keys [0, key_end)

@@ -97,6 +97,12 @@ def test_decode_rejects_bad_arguments(lib):
     assert _decode(lib, _pool(), ptok=32) == wsp
     assert _decode(lib, _pool(), ptok=32, ws=FAKE, ws_bytes=need - 1) == wsp
     assert _decode(lib, _pool(), num_seqs=0) == 0               # nothing to do
+    # block counts of the largest context stay in int32
+    assert _decode(lib, _pool(), max_ctx=2 ** 31 - 1) == unsup
+    assert lib.pa_decode_workspace_bytes(2, 4, 2, 128, 2 ** 31 - 1, 0) == 2 ** 64 - 1
+    assert lib.pa_decode_partition_tokens(2, 4, 2, 2 ** 31 - 1) == -1
+    lens = (ctypes.c_int32 * 2)(5, 2 ** 31 - 1)
+    assert lib.pa_decode_plan(2, 4, 2, 128, lens) == -1
 
 
 def _prefill(lib, pool, num_seqs=2, hq=4, scale=0.125, qs=FAKE, T=10, maxq=8, bt=FAKE, maxb=8,
@@ -124,6 +130,7 @@ def test_prefill_rejects_bad_arguments(lib):
     assert _prefill(lib, _pool(), q=None) == inval
     assert _prefill(lib, _pool(), maxb=0) == inval
     assert _prefill(lib, _pool(), T=1 << 30, hq=4) == unsup     # rows x heads past int32
+    assert _prefill(lib, _pool(), max_ctx=2 ** 31 - 1) == unsup  # block counts past int32
     assert _prefill(lib, _pool(), T=0) == 0                     # nothing to do
     assert _prefill(lib, _pool(), num_seqs=0) == 0
     fp8 = dict(dtype=B.PA_FP8_E4M3, act_dtype=B.PA_BF16, k_scale=0.01, v_scale=0.0)
@@ -156,6 +163,8 @@ def test_append_rejects_bad_arguments(lib):
     assert f(ctypes.byref(pool), FAKE, FAKE, FAKE, -1, None) == 1
     assert f(ctypes.byref(_pool(block_size=32)), FAKE, FAKE, FAKE, 4, None) == 2
     assert f(ctypes.byref(pool), None, None, None, 0, None) == 0   # empty step: no-op
+    big = _pool(num_kv_heads=16)
+    assert f(ctypes.byref(big), FAKE, FAKE, FAKE, 2 ** 31 - 1, None) == 2   # launch size
 
 
 def test_partition_choice_is_deterministic_and_sane(lib):
