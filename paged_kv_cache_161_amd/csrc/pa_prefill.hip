@@ -456,12 +456,13 @@ __global__ __launch_bounds__(NW *kWave, C <= 2 ? 2 : 1) void pa_prefill_kernel(P
     };
 
     // Two-stage pipeline over 32-key steps.  K is staged one step ahead of V.  Pass
-    // it, in one branch-free stretch, issues step it+1's QK products interleaved with
-    // step it's weights (its mask and max were settled in the previous pass), then step
-    // it's PV products; it then stages K of step it+2 and V of step it+1 into the LDS
-    // buffers those steps last used, reissues the freed register slots for K of step
-    // it+4 and V of step it+3 (two passes ahead of their staging), and after the
-    // barrier masks step it+1's scores and updates the running max.  The loop is
+    // it first stages K of step it+2 and V of step it+1 into the LDS buffers those
+    // steps last used and reissues the freed register slots for K of step it+4 and V
+    // of step it+3 (two passes ahead of their staging); then, in one branch-free
+    // stretch, it issues step it+1's QK products interleaved with step it's weights
+    // (its mask and max were settled in the previous pass), then step it's PV
+    // products; after the barrier it masks step it+1's scores and updates the running
+    // max.  The loop is
     // unrolled by two, so the ring slots and the two score sets are fixed registers,
     // and runs whole pairs of passes with no other exit: every pass issues the same
     // loads and waits, so each wait covers exactly the slot it needs.  Loads past the
@@ -493,9 +494,11 @@ __global__ __launch_bounds__(NW *kWave, C <= 2 ? 2 : 1) void pa_prefill_kernel(P
         fetch_v(ph_a, 0);                            // V of step 2
         table(min(4, last), raw);
         __syncthreads();
-        // Step it's staging between its products and the barrier: K of step it+2 and
-        // V of step it+1 into the LDS buffers those steps last used, then the freed
-        // register slots reissued for K of step it+4 and V of step it+3.
+        // Pass it's staging, first thing after the barrier that ended pass it-1: K of
+        // step it+2 and V of step it+1 into the LDS buffers whose contents (steps it and
+        // it-1) were last read in pass it-1, then the freed register slots reissued for
+        // K of step it+4 and V of step it+3.  Done at the start of the pass, the stores
+        // have the whole pass to complete before the next barrier waits on them.
         auto stage = [&](int it, int u) {
             stash_k(u, u);
             stash_v(it + 1, u ^ 1, u ^ 1);
@@ -533,6 +536,7 @@ __global__ __launch_bounds__(NW *kWave, C <= 2 ? 2 : 1) void pa_prefill_kernel(P
 #pragma unroll
                 for (int u = 0; u < 2; ++u) {
                     const int it = 2 * pr + u;
+                    stage(it, u);
                     qk(u ^ 1, sc[u ^ 1]);                // step it+1's scores
                     u32x4 vf[NDB];
 #pragma unroll
@@ -564,7 +568,6 @@ __global__ __launch_bounds__(NW *kWave, C <= 2 ? 2 : 1) void pa_prefill_kernel(P
                             __builtin_amdgcn_sched_group_barrier(0x100, NDB / 2, 0);
                     }
                     __builtin_amdgcn_sched_group_barrier(0x008, NDB * C + C, 0);
-                    stage(it, u);
                     __syncthreads();
                     mask_max(it + 1, sc[u ^ 1]);
                 }
