@@ -105,7 +105,15 @@ def _raise(status: int):
         raise PaError(status, load().pa_status_string(status).decode())
 
 
+# torch's current-stream accessor that returns the raw handle without building a
+# Stream object (about 2 us less per call); the public route where it is absent
+_RAW_STREAM = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream_handle(device: torch.device) -> int:
+    if _RAW_STREAM is not None:
+        return _RAW_STREAM(device.index if device.index is not None
+                           else torch.cuda.current_device())
     return torch.cuda.current_stream(device).cuda_stream
 
 
@@ -146,8 +154,11 @@ def make_pool(k_pool, v_pool, act_dtype: Optional[torch.dtype] = None, k_scale: 
                     code, act, float(k_scale), float(v_scale))
 
 
+_DTYPE_OF_CODE = {v: k for k, v in DTYPE_CODE.items()}
+
+
 def _act_dtype(pool: PaKvPool) -> torch.dtype:
-    return {v: k for k, v in DTYPE_CODE.items()}[pool.act_dtype]
+    return _DTYPE_OF_CODE[pool.act_dtype]
 
 
 def pool_bytes(num_blocks: int, num_kv_heads: int, head_dim: int, dtype: torch.dtype) -> int:
@@ -200,6 +211,24 @@ def workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim
     return n
 
 
+PA_ERR_WORKSPACE = 3
+
+
+def _call_with_workspace(fn, args, workspace, device, dims):
+    """fn(*args, workspace, workspace_bytes, stream).  A given workspace goes straight
+    to the library, which checks its size; only when there is none, or the library
+    reports it too small, is the size asked for and a workspace allocated."""
+    stream = _stream_handle(device)
+    if workspace is not None:
+        st = fn(*args, _dev_ptr(workspace, "workspace"),
+                workspace.numel() * workspace.element_size(), stream)
+        if st != PA_ERR_WORKSPACE:
+            return st
+    need = workspace_bytes(*dims)
+    ws = torch.empty(need, dtype=torch.uint8, device=device) if need else None
+    return fn(*args, ws.data_ptr() if need else None, need, stream)
+
+
 def decode(q, k_pool, v_pool, block_tables, context_lens, scale: float, max_context_len: int,
            partition_tokens: int = 0, out: Optional[torch.Tensor] = None,
            workspace: Optional[torch.Tensor] = None, k_scale: float = 1.0,
@@ -217,19 +246,13 @@ def decode(q, k_pool, v_pool, block_tables, context_lens, scale: float, max_cont
         raise ValueError("q head_dim differs from the pool's")
     if out is None:
         out = torch.empty_like(q)
-    need = workspace_bytes(B, hq, pool.num_kv_heads, d, max_context_len, partition_tokens)
-    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_ptr = _dev_ptr(workspace, "workspace") if need else None
-    ws_len = workspace.numel() * workspace.element_size() if need else 0
     act = _act_dtype(pool)
-    st = load().pa_decode(ctypes.byref(pool), _dev_ptr(q, "q", act), _dev_ptr(out, "out", act),
-                          B, hq, ctypes.c_float(scale),
-                          _dev_ptr(block_tables, "block_tables", torch.int32),
-                          block_tables.shape[1], _dev_ptr(context_lens, "context_lens",
-                                                          torch.int32),
-                          max_context_len, partition_tokens, ws_ptr, ws_len,
-                          _stream_handle(q.device))
+    args = [ctypes.byref(pool), _dev_ptr(q, "q", act), _dev_ptr(out, "out", act), B, hq,
+            ctypes.c_float(scale), _dev_ptr(block_tables, "block_tables", torch.int32),
+            block_tables.shape[1], _dev_ptr(context_lens, "context_lens", torch.int32),
+            max_context_len, partition_tokens]
+    st = _call_with_workspace(load().pa_decode, args, workspace, q.device,
+                              (B, hq, pool.num_kv_heads, d, max_context_len, partition_tokens))
     _raise(st)
     return out
 
@@ -249,20 +272,14 @@ def decode_append(q, k_pool, v_pool, k_new, v_new, block_tables, context_lens, s
         raise ValueError("k_new / v_new must be [num_seqs][num_kv_heads][head_dim]")
     if out is None:
         out = torch.empty_like(q)
-    need = workspace_bytes(B, hq, pool.num_kv_heads, d, max_context_len, partition_tokens)
-    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_ptr = _dev_ptr(workspace, "workspace") if need else None
-    ws_len = workspace.numel() * workspace.element_size() if need else 0
     act = _act_dtype(pool)
-    st = load().pa_decode_append(ctypes.byref(pool), _dev_ptr(q, "q", act),
-                                 _dev_ptr(k_new, "k_new", act), _dev_ptr(v_new, "v_new", act),
-                                 _dev_ptr(out, "out", act), B, hq, ctypes.c_float(scale),
-                                 _dev_ptr(block_tables, "block_tables", torch.int32),
-                                 block_tables.shape[1],
-                                 _dev_ptr(context_lens, "context_lens", torch.int32),
-                                 max_context_len, partition_tokens, ws_ptr, ws_len,
-                                 _stream_handle(q.device))
+    args = [ctypes.byref(pool), _dev_ptr(q, "q", act), _dev_ptr(k_new, "k_new", act),
+            _dev_ptr(v_new, "v_new", act), _dev_ptr(out, "out", act), B, hq,
+            ctypes.c_float(scale), _dev_ptr(block_tables, "block_tables", torch.int32),
+            block_tables.shape[1], _dev_ptr(context_lens, "context_lens", torch.int32),
+            max_context_len, partition_tokens]
+    st = _call_with_workspace(load().pa_decode_append, args, workspace, q.device,
+                              (B, hq, pool.num_kv_heads, d, max_context_len, partition_tokens))
     _raise(st)
     return out
 

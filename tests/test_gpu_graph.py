@@ -157,3 +157,14 @@ def test_graph_replay_prefill():
         step(kp_e, vp_e, out_e)
         torch.cuda.synchronize()
         assert torch.equal(U.int_view(out_e), ref)
+
+
+def test_binding_stream_is_torchs_current_stream():
+    """The binding launches on torch's current stream: the default one, and a side
+    stream inside `torch.cuda.stream(s)` (which is how the captures above work)."""
+    dev = torch.device("cuda")
+    assert PA._stream_handle(dev) == torch.cuda.current_stream(dev).cuda_stream
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        assert PA._stream_handle(dev) == s.cuda_stream
+    assert PA._stream_handle(dev) == torch.cuda.current_stream(dev).cuda_stream
