@@ -400,6 +400,8 @@ pa_status pa_prefill(const pa_kv_pool *pool, const void *q, void *out, int32_t n
         return PA_ERR_UNSUPPORTED;
     if (max_context_len > INT32_MAX - kBlock)         // block counts stay in int32
         return PA_ERR_UNSUPPORTED;
+    if ((int64_t)pool->num_kv_heads * kBlock * pool->head_dim > UINT32_MAX)
+        return PA_ERR_UNSUPPORTED;                    // block stride in 32 bits
     if (num_seqs == 0 || num_query_tokens == 0 || max_query_len == 0)
         return PA_OK;
     if (!q || !out || !query_start || !block_tables || !context_lens || max_blocks_per_seq == 0)

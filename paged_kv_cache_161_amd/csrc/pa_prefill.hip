@@ -214,6 +214,7 @@ __global__ __launch_bounds__(NW *kWave, C <= 2 ? 2 : 1) void pa_prefill_kernel(P
     const Elem *kbase = static_cast<const Elem *>(a.k_pool) + (size_t)kvh * kBlock * D;
     const Elem *vbase = static_cast<const Elem *>(a.v_pool) + (size_t)kvh * kBlock * D;
     const size_t blk_stride = (size_t)a.num_kv_heads * kBlock * D;
+    const uint32_t blk_stride32 = (uint32_t)blk_stride;     // < 2^32 (host-checked)
     // the table row through the constant address space: uniform reads of it stay
     // scalar loads, whose wait does not hold up the vector loads in flight
     typedef const __attribute__((address_space(4))) int32_t const_i32;
@@ -283,14 +284,14 @@ __global__ __launch_bounds__(NW *kWave, C <= 2 ? 2 : 1) void pa_prefill_kernel(P
     auto fetch_k = [&](const int (&ph)[2], int slot) {
 #pragma unroll
         for (int i = 0; i < KPT; ++i) {
-            const Elem *blk = kbase + (size_t)(k_tl[i] ? ph[1] : ph[0]) * blk_stride;
+            const Elem *blk = kbase + (uint64_t)(uint32_t)(k_tl[i] ? ph[1] : ph[0]) * blk_stride32;
             kreg[slot][i] = *reinterpret_cast<const u32x4 *>(blk + k_off[i]);
         }
     };
     auto fetch_v = [&](const int (&ph)[2], int slot) {
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
-            const Elem *blk = vbase + (size_t)(v_tl[i] ? ph[1] : ph[0]) * blk_stride;
+            const Elem *blk = vbase + (uint64_t)(uint32_t)(v_tl[i] ? ph[1] : ph[0]) * blk_stride32;
             vreg[slot][i] = *reinterpret_cast<const u32x4 *>(blk + v_off[i]);
         }
     };

@@ -131,6 +131,7 @@ def test_prefill_rejects_bad_arguments(lib):
     assert _prefill(lib, _pool(), maxb=0) == inval
     assert _prefill(lib, _pool(), T=1 << 30, hq=4) == unsup     # rows x heads past int32
     assert _prefill(lib, _pool(), max_ctx=2 ** 31 - 1) == unsup  # block counts past int32
+    assert _prefill(lib, _pool(num_kv_heads=1 << 21), hq=1 << 21) == unsup   # block stride
     assert _prefill(lib, _pool(), T=0) == 0                     # nothing to do
     assert _prefill(lib, _pool(), num_seqs=0) == 0
     fp8 = dict(dtype=B.PA_FP8_E4M3, act_dtype=B.PA_BF16, k_scale=0.01, v_scale=0.0)
