@@ -390,10 +390,10 @@ pa_status pa_prefill(const pa_kv_pool *pool, const void *q, void *out, int32_t n
         max_blocks_per_seq < 0 || !isfinite(scale) || !(scale > 0.f))
         return PA_ERR_INVALID_ARG;
     // 16-bit MFMA kernels only (fp8 pools convert to their 16-bit activation type)
-    if (pool->dtype == PA_F32 || pool->head_dim > 128)
+    if (pool->dtype == PA_F32)
         return PA_ERR_UNSUPPORTED;
     const int32_t group = num_q_heads / pool->num_kv_heads;
-    const int32_t rows = pa::prefill_rows_per_group();
+    const int32_t rows = pa::prefill_rows_per_group(pool->head_dim);
     if (group > rows)
         return PA_ERR_UNSUPPORTED;
     if ((int64_t)num_query_tokens * num_q_heads > INT32_MAX)

@@ -39,8 +39,12 @@ struct PrefillArgs {
 constexpr int kPrefillWaves = PA_PREFILL_WAVES;
 constexpr int kPrefillCols = PA_PREFILL_COLS;
 
-// Query rows ((position, q-head) pairs) one prefill workgroup holds.
-int prefill_rows_per_group();
+// Column blocks per wave at head_dim d: kPrefillCols up to d = 128, one at d = 256,
+// whose O accumulators, q fragments and K/V fragments take twice the registers per row.
+constexpr int prefill_cols(int head_dim) { return head_dim > 128 ? 1 : kPrefillCols; }
+
+// Query rows ((position, q-head) pairs) one prefill workgroup holds at head_dim d.
+int prefill_rows_per_group(int head_dim);
 
 hipError_t launch_prefill(int dtype, int act_dtype, int head_dim, const PrefillArgs &a,
                           hipStream_t stream);

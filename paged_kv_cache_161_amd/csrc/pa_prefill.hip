@@ -601,18 +601,19 @@ __global__ __launch_bounds__(NW *kWave, C <= 2 ? 2 : 1) void pa_prefill_kernel(P
 template <int DT, int AT, int D>
 hipError_t launch_prefill_t(const PrefillArgs &a, int grid, bool idle, hipStream_t stream)
 {
+    constexpr int C = prefill_cols(D);
     if (idle)
-        hipLaunchKernelGGL((pa_prefill_kernel<DT, AT, D, kPrefillWaves, kPrefillCols, true>),
+        hipLaunchKernelGGL((pa_prefill_kernel<DT, AT, D, kPrefillWaves, C, true>),
                            dim3(grid), dim3(kPrefillWaves * kWave), 0, stream, a);
     else
-        hipLaunchKernelGGL((pa_prefill_kernel<DT, AT, D, kPrefillWaves, kPrefillCols, false>),
+        hipLaunchKernelGGL((pa_prefill_kernel<DT, AT, D, kPrefillWaves, C, false>),
                            dim3(grid), dim3(kPrefillWaves * kWave), 0, stream, a);
     return hipGetLastError();
 }
 
 }  // namespace
 
-int prefill_rows_per_group() { return kPrefillWaves * kPrefillCols * 16; }
+int prefill_rows_per_group(int head_dim) { return kPrefillWaves * prefill_cols(head_dim) * 16; }
 
 hipError_t launch_prefill(int dtype, int act_dtype, int head_dim, const PrefillArgs &a,
                           hipStream_t stream)
@@ -625,18 +626,22 @@ hipError_t launch_prefill(int dtype, int act_dtype, int head_dim, const PrefillA
     // skip the products is launched.
     const bool full = (int64_t)a.num_tokens == (int64_t)a.num_seqs * a.max_query_len &&
                       a.max_query_len % a.q_tile == 0 &&
-                      a.q_tile * a.group > (kPrefillWaves - 1) * kPrefillCols * 16;
+                      a.q_tile * a.group > (kPrefillWaves - 1) * prefill_cols(head_dim) * 16;
 #define PA_PF_CASE(DT, AT, D)                                                      \
     if (dtype == DT && act_dtype == AT && head_dim == D)                          \
         return launch_prefill_t<DT, AT, D>(a, grid, !full, stream);
     PA_PF_CASE(DT_BF16, DT_BF16, 128)
     PA_PF_CASE(DT_BF16, DT_BF16, 64)
+    PA_PF_CASE(DT_BF16, DT_BF16, 256)
     PA_PF_CASE(DT_F16, DT_F16, 128)
     PA_PF_CASE(DT_F16, DT_F16, 64)
+    PA_PF_CASE(DT_F16, DT_F16, 256)
     PA_PF_CASE(DT_FP8, DT_BF16, 128)
     PA_PF_CASE(DT_FP8, DT_BF16, 64)
+    PA_PF_CASE(DT_FP8, DT_BF16, 256)
     PA_PF_CASE(DT_FP8, DT_F16, 128)
     PA_PF_CASE(DT_FP8, DT_F16, 64)
+    PA_PF_CASE(DT_FP8, DT_F16, 256)
 #undef PA_PF_CASE
     return hipErrorInvalidValue;
 }

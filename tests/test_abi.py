@@ -116,7 +116,7 @@ def test_prefill_rejects_bad_arguments(lib):
     assert _prefill(lib, None) == inval
     assert _prefill(lib, _pool(k_pool=None)) == inval
     assert _prefill(lib, _pool(dtype=B.PA_F32)) == unsup        # 16-bit MFMA path only
-    assert _prefill(lib, _pool(head_dim=256)) == unsup
+    assert _prefill(lib, _pool(head_dim=96)) == unsup
     assert _prefill(lib, _pool(), hq=3) == inval                 # 3 % 2 != 0
     assert _prefill(lib, _pool(), hq=2 * 512) == unsup           # group above 256 rows
     for bad in (0.0, -0.125, float("nan"), float("inf")):

@@ -52,6 +52,13 @@ SMALL = [
     # idle-wave path
     W.Spec("pf_full_tiles_bf16", "bf16", 64, 8, 128, [100, 64, 333], seed=40, spare_blocks=1,
            query_lens=[64, 64, 64]),
+    # head_dim 256: one 16-row column block per wave, 128-row tiles
+    W.Spec("pf_bf16_d256", "bf16", 16, 2, 256, [70, 300], seed=41, spare_blocks=1,
+           query_lens=[70, 45]),
+    W.Spec("pf_fp8_f16_d256", "f16", 8, 2, 256, [40, 130], seed=42, spare_blocks=1,
+           kv_dtype="fp8", k_scale=0.0117, v_scale=0.0093, query_lens=[40, 33]),
+    W.Spec("pf_full_tiles_f16_d256", "f16", 32, 4, 256, [64, 96], seed=43, spare_blocks=1,
+           query_lens=[32, 32]),
 ]
 
 
