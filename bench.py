@@ -367,8 +367,9 @@ def bench_prefill(args, w, PA, U, dev):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: every GPU box here has one MI355X and this "
-              "decode path is not sharded across GPUs; run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU: this decode path is not sharded across GPUs "
+              "(how it would shard is described with the design); run with --gpus 1",
+              file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
         print("bench.py needs a ROCm GPU", file=sys.stderr)
