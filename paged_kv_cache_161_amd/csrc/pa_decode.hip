@@ -218,14 +218,29 @@ struct Tile8 {
     u32x4 k[NKL];                        // 16 codes of K[r][64j + 16g .. +15]
     uint32_t v[NPV];                     // 4 codes of V^T[16n + r][4g .. 4g+3]
 
+    // V^T rows are 16 bytes.  Lane (r, g) loads whole rows 16 (g + 4 i) + r, i < NPV / 4
+    // (each load instruction: 64 contiguous rows, 1 KiB), and the four lanes sharing r
+    // transpose their 4 x 4 blocks of 4-byte pieces with two rounds of lane swaps
+    // (16-lane, then 32-lane), so that v[4 i + j] = V^T[16 (4 i + j) + r][4 g .. 4 g + 3]
+    // as the MFMA operand wants: 2 loads per block at d = 128 instead of 8.
     __device__ __forceinline__ void load(const uint8_t *kt, const uint8_t *vt, int r, int g)
     {
 #pragma unroll
         for (int j = 0; j < NKL; ++j)
             k[j] = *reinterpret_cast<const u32x4 *>(kt + r * D + 64 * j + 16 * g);
 #pragma unroll
-        for (int n = 0; n < NPV; ++n)
-            v[n] = *reinterpret_cast<const uint32_t *>(vt + (16 * n + r) * kBlock + 4 * g);
+        for (int i = 0; i < NPV / 4; ++i) {
+            const u32x4 w = *reinterpret_cast<const u32x4 *>(vt + (16 * (g + 4 * i) + r) * kBlock);
+            // lane g holds e[g][j] = w[j]; afterwards lane g's register j holds e[j][g]
+            auto s01 = __builtin_amdgcn_permlane16_swap(w[0], w[1], false, false);
+            auto s23 = __builtin_amdgcn_permlane16_swap(w[2], w[3], false, false);
+            auto s02 = __builtin_amdgcn_permlane32_swap(s01[0], s23[0], false, false);
+            auto s13 = __builtin_amdgcn_permlane32_swap(s01[1], s23[1], false, false);
+            v[4 * i + 0] = s02[0];
+            v[4 * i + 1] = s13[0];
+            v[4 * i + 2] = s02[1];
+            v[4 * i + 3] = s13[1];
+        }
     }
 
     __device__ __forceinline__ void store_row(uint8_t *kt, uint8_t *vt, int off, int r, int g) const
