@@ -48,7 +48,9 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=200,
+                    help="untimed steps first; the GPU's clocks need some 20 ms of steady "
+                         "work to settle, which 200 decode steps give")
     ap.add_argument("--config", type=int, default=None,
                     help="workload id 1..8 (default: the Llama-70B GQA decode headline for "
                          "step / copy_blocks, the 512-token chunked prefill (7) for "
