@@ -1,4 +1,5 @@
-// pa_append.hip -- scatter a decode step's new K/V rows into the paged pool.
+// pa_append.hip -- scatter new K/V rows (a decode step's, or a prompt chunk's) into the
+// paged pool, and copy whole blocks for copy-on-write.
 //
 // Row i of k_new / v_new goes to slot s = slot_mapping[i]: physical block s / 16, row
 // s % 16 (the page / offset split of "LLM应用 12 推理优化", PagedKVCache.update, and the
@@ -6,9 +7,10 @@
 // Bytes are copied unchanged.  Negative slots are padding; slots past the pool are
 // dropped so that no write ever leaves the pool.
 //
-// One thread moves one 16-byte chunk of one (token, kv-head) row: a single 16-byte
-// store into the token-major K block, and 16/elem scalar stores into the token-minor
-// V block (stride 16 elements).
+// Fewer than 16 rows: one thread moves one 16-byte chunk of one (token, kv-head) row:
+// a single 16-byte store into the token-major K block, and 16/elem scalar stores into
+// the token-minor V block (stride 16 elements).  16 rows or more: groups of 16 rows,
+// a whole in-order block written block-wise (see the group kernel).
 //
 // An fp8 pool stores OCP E4M3 codes of x / scale (the KV-cache write fused with its
 // quantisation, one of the fused kernels "Deep dive into vLLM 06" lists): the

@@ -642,8 +642,6 @@ __global__ __launch_bounds__(NW *kWave, min_waves_per_simd(DT, D, PF)) void pa_d
 
     // Ring of PF + 1 tiles: block i + PF is loaded while block i is computed.  The
     // inner loop is fully unrolled so every ring slot stays a fixed register range.
-    // Ring of PF + 1 tiles: block i + PF is loaded while block i is computed.  The
-    // inner loop is fully unrolled so every ring slot stays a fixed register range.
     auto prologue = [&](typename F::Tile (&ring)[PF + 1]) {
 #pragma unroll
         for (int k = 0; k < PF; ++k) {
