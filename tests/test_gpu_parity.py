@@ -298,3 +298,21 @@ def test_split_workspace_reuse_and_garbage():
                 ref = oracle_decode(w)
                 check(w, got, ref, f"reuse {rep} {spec.name} p{ptok}")
                 assert np.isfinite(U.widen(U.from_dev(ref_out, w.dtype), w.dtype)).all()
+
+
+def test_binding_grows_a_too_small_workspace():
+    """A caller's workspace below the split launch's need is reported by the library
+    (nothing launched), and the binding then allocates one of the right size."""
+    w = W.build(SMALL[0])
+    ptok = 16
+    need = PA.workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                              w.max_context_len, ptok)
+    assert need > 64
+    small = torch.full((need // 2,), 0xA5, dtype=torch.uint8, device="cuda")
+    kp, vp = U.device_pools(w)
+    d = U.device_inputs(w)
+    PA.cache_append(kp, vp, d["k_new"], d["v_new"], d["slot_mapping"], **U.scales(w))
+    out = PA.decode(d["q"], kp, vp, d["block_tables"], d["context_lens"], float(w.scale),
+                    w.max_context_len, ptok, workspace=small, **U.scales(w))
+    torch.cuda.synchronize()
+    check(w, U.widen(U.from_dev(out, w.dtype), w.dtype), oracle_decode(w), "grown workspace")
