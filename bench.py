@@ -110,11 +110,31 @@ def cpu_baseline(w):
                        q_dtype=w.dtype, k_scale=w.k_scale, v_scale=w.v_scale)
         times.append(time.perf_counter() - t0)
     t = statistics.median(times)
+    # the same on one host thread, once (the oracle's result does not depend on it)
+    t0 = time.perf_counter()
+    O.decode_paged(w.q, kp, vp, w.kv_dtype, bt, w.context_lens, w.scale, threads=1,
+                   q_dtype=w.dtype, k_scale=w.k_scale, v_scale=w.v_scale)
+    t1 = time.perf_counter() - t0
     return {"value": round(w.logical_kv_bytes() / t / 1e9, 4), "unit": "GB/s",
             "cores": threads, "kind": "oracle",
             "sample": f"whole workload ({w.spec.name}, {w.num_seqs} seqs), decode only, "
                       f"median of 3 runs: {t:.3f} s/step, "
-                      f"{w.num_seqs / t:.1f} tokens/s"}
+                      f"{w.num_seqs / t:.1f} tokens/s",
+            "one_thread_value": round(w.logical_kv_bytes() / t1 / 1e9, 4),
+            "one_thread_s_per_step": round(t1, 3),
+            "cpu_model": cpu_model()}
+
+
+def cpu_model():
+    """The host CPU's model name, as /proc/cpuinfo gives it (None elsewhere)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def bench_copy_blocks(args, w, PA, U, dev):
