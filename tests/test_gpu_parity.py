@@ -316,3 +316,35 @@ def test_binding_grows_a_too_small_workspace():
                     w.max_context_len, ptok, workspace=small, **U.scales(w))
     torch.cuda.synchronize()
     check(w, U.widen(U.from_dev(out, w.dtype), w.dtype), oracle_decode(w), "grown workspace")
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["decode", "decode_append"])
+def test_generous_host_bounds_change_nothing(fused):
+    """max_context_len (the host's bound, which sizes the grid) well above every context
+    length only adds workgroups with nothing to stream: at the same partition length
+    the outputs, and the pool after a fused append, equal the tight-bound call's bit
+    for bit."""
+    w = W.build(SMALL[0])
+    d = U.device_inputs(w)
+    sc = U.scales(w)
+    ptok = 48
+    rows = np.zeros((w.num_seqs,) + w.k_new.shape[1:], w.k_new.dtype)
+    rows[np.flatnonzero(w.context_lens > 0)] = w.k_new
+    kr = U.to_dev(rows, w.dtype)
+    vrows = np.zeros_like(rows)
+    vrows[np.flatnonzero(w.context_lens > 0)] = w.v_new
+    vr = U.to_dev(vrows, w.dtype)
+    results = []
+    for bound in (w.max_context_len, 4 * w.max_context_len + 5):
+        kp, vp = U.device_pools(w)
+        if fused:
+            out = PA.decode_append(d["q"], kp, vp, kr, vr, d["block_tables"], d["context_lens"],
+                                   float(w.scale), bound, ptok, **sc)
+        else:
+            PA.cache_append(kp, vp, d["k_new"], d["v_new"], d["slot_mapping"], **sc)
+            out = PA.decode(d["q"], kp, vp, d["block_tables"], d["context_lens"],
+                            float(w.scale), bound, ptok, **sc)
+        torch.cuda.synchronize()
+        results.append((U.int_view(out).clone(), U.int_view(kp).clone(), U.int_view(vp).clone()))
+    for a, b in zip(results[0], results[1]):
+        assert torch.equal(a, b)

@@ -223,3 +223,21 @@ def test_prefill_rejects_unsupported_and_invalid():
     PA.prefill(q16[:0], kp16, vp16, torch.tensor([0, 0], dtype=torch.int32, device="cuda"),
                bt, cl, 0.125, 3, 0, out=out)
     torch.cuda.synchronize()
+
+
+def test_generous_host_bounds_change_nothing():
+    """max_query_len and max_context_len above the real maxima only add workgroups that
+    exit at once: outputs equal the tight-bound call's bit for bit."""
+    w = W.build(SMALL[2])
+    kp, vp = U.device_pools(w)
+    d = U.device_inputs(w)
+    PA.cache_append(kp, vp, d["k_new"], d["v_new"], d["slot_mapping"])
+    qs = torch.from_numpy(w.query_start).cuda()
+    outs = []
+    for max_ctx, max_q in ((w.max_context_len, w.max_query_len),
+                           (3 * w.max_context_len + 7, 2 * w.max_query_len + 33)):
+        out = PA.prefill(d["q"], kp, vp, qs, d["block_tables"], d["context_lens"],
+                         float(w.scale), max_ctx, max_q)
+        torch.cuda.synchronize()
+        outs.append(U.int_view(out).clone())
+    assert torch.equal(outs[0], outs[1])
