@@ -24,6 +24,7 @@ namespace pa {
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 template <int EB, int D>
 __global__ __launch_bounds__(256) void pa_cache_append_kernel(AppendArgs a)
@@ -110,6 +111,25 @@ __global__ __launch_bounds__(256) void pa_cache_append_fp8_kernel(AppendArgs a)
 // each store covers 8 consecutive tokens of one e, so no store is a partial-sector
 // write.  Any other group takes the per-row path (16-byte K pieces, V scattered by
 // token), as the single-row kernels do.  fp8 pools store E4M3(x / scale).
+// Eight consecutive pool elements (a run 8 x element-size bytes long and as aligned)
+// written with whole-run vector stores.
+template <typename Out>
+__device__ __forceinline__ void store_run(Out *dst, const Out (&run)[8])
+{
+    if constexpr (sizeof(Out) == 1) {
+        u32x2 w;
+        __builtin_memcpy(&w, run, sizeof(w));
+        *reinterpret_cast<u32x2 *>(dst) = w;
+    } else {
+#pragma unroll
+        for (int h = 0; h < (int)sizeof(run) / 16; ++h) {
+            u32x4 w;
+            __builtin_memcpy(&w, reinterpret_cast<const char *>(run) + 16 * h, sizeof(w));
+            reinterpret_cast<u32x4 *>(dst)[h] = w;
+        }
+    }
+}
+
 template <int DT, int AT, int D>
 __global__ __launch_bounds__(256) void pa_cache_append_group_kernel(AppendArgs a)
 {
@@ -155,18 +175,23 @@ __global__ __launch_bounds__(256) void pa_cache_append_group_kernel(AppendArgs a
                 kx[e] = kin[src + e];
                 vx[e] = vin[src + e];
             }
+            Out run[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                kpool[tile + (size_t)j * D + col + e] = conv(kx[e], a.k_scale);
+                run[e] = conv(kx[e], a.k_scale);
                 s_v[j][col + e] = vx[e];
             }
+            store_run(kpool + tile + (size_t)j * D + col, run);
         }
         __syncthreads();
         for (int c = tid; c < D * 2; c += blockDim.x) {
             const int d = c / 2, t0 = (c % 2) * 8;
+            // tokens t0 .. t0+7 of V^T row d: one contiguous run
+            Out run[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                vpool[tile + (size_t)d * kBlock + t0 + e] = conv(s_v[t0 + e][d], a.v_scale);
+                run[e] = conv(s_v[t0 + e][d], a.v_scale);
+            store_run(vpool + tile + (size_t)d * kBlock + t0, run);
         }
         return;
     }
