@@ -105,12 +105,6 @@ __global__ __launch_bounds__(256) void pa_cache_append_fp8_kernel(AppendArgs a)
                                (size_t)c * 8) = make_uint2(kc[0], kc[1]);
 }
 
-// Groups of 16 consecutive new rows, one workgroup per (group, kv-head).  A group whose
-// 16 slots are one whole block in order (a prompt chunk being ingested) writes that
-// block's K rows contiguously and its V^T rows whole: the 16 rows are staged in LDS and
-// each store covers 8 consecutive tokens of one e, so no store is a partial-sector
-// write.  Any other group takes the per-row path (16-byte K pieces, V scattered by
-// token), as the single-row kernels do.  fp8 pools store E4M3(x / scale).
 // Eight consecutive pool elements (a run 8 x element-size bytes long and as aligned)
 // written with whole-run vector stores.
 template <typename Out>
@@ -130,6 +124,13 @@ __device__ __forceinline__ void store_run(Out *dst, const Out (&run)[8])
     }
 }
 
+// Groups of 16 consecutive new rows, one workgroup per (group, kv-head).  A group whose
+// 16 slots are one whole block in order (a prompt chunk being ingested) writes that
+// block's K rows contiguously and its V^T rows whole: the 16 rows are staged in LDS and
+// each store covers 8 consecutive tokens of one V^T row, so no store is a partial-sector
+// write.  Any other group writes each row's K pieces to its slot and its V^T elements
+// with lanes along the token axis (rows of one block that follow each other coalesce).
+// fp8 pools store E4M3(x / scale).
 template <int DT, int AT, int D>
 __global__ __launch_bounds__(256) void pa_cache_append_group_kernel(AppendArgs a)
 {
@@ -195,19 +196,40 @@ __global__ __launch_bounds__(256) void pa_cache_append_group_kernel(AppendArgs a
         }
         return;
     }
+    // Any other group: K row pieces go straight to their slots; V rows are staged in
+    // LDS and written with lanes along the token axis, so the rows of one block that
+    // follow each other in the group land as one run of V^T row d.
+    const int64_t slots = (int64_t)a.num_blocks * kBlock;
     for (int c = tid; c < n * PC; c += blockDim.x) {
         const int j = c / PC, col = (c % PC) * 8;
-        const int slot = s_slot[j];
-        if (slot < 0 || (int64_t)slot >= (int64_t)a.num_blocks * kBlock)
-            continue;
-        const size_t tile = ((size_t)(slot / kBlock) * a.num_kv_heads + h) * kBlock * D;
-        const int off = slot % kBlock;
         const size_t src = ((size_t)(i0 + j) * a.num_kv_heads + h) * D + col;
+        In kx[8], vx[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            kpool[tile + (size_t)off * D + col + e] = conv(kin[src + e], a.k_scale);
-            vpool[tile + (size_t)(col + e) * kBlock + off] = conv(vin[src + e], a.v_scale);
+            kx[e] = kin[src + e];
+            vx[e] = vin[src + e];
         }
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            s_v[j][col + e] = vx[e];
+        const int slot = s_slot[j];
+        if (slot < 0 || (int64_t)slot >= slots)
+            continue;
+        Out run[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            run[e] = conv(kx[e], a.k_scale);
+        const size_t tile = ((size_t)(slot / kBlock) * a.num_kv_heads + h) * kBlock * D;
+        store_run(kpool + tile + (size_t)(slot % kBlock) * D + col, run);
+    }
+    __syncthreads();
+    for (int c = tid; c < D * kBlock; c += blockDim.x) {
+        const int d = c / kBlock, j = c % kBlock;
+        const int slot = s_slot[j];               // -1 past the last row
+        if (slot < 0 || (int64_t)slot >= slots)
+            continue;
+        const size_t tile = ((size_t)(slot / kBlock) * a.num_kv_heads + h) * kBlock * D;
+        vpool[tile + (size_t)d * kBlock + slot % kBlock] = conv(s_v[j][d], a.v_scale);
     }
 }
 
