@@ -24,6 +24,10 @@
  *   - Pointers named *_pool, q, out, k_new, v_new, slot_mapping, block_tables,
  *     context_lens and workspace are DEVICE pointers (hipMalloc'd or torch CUDA
  *     tensors).  pa_kv_pool itself lives in host memory and is read during the call.
+ *   - Alignment: pools (k_pool, v_pool), q, out, k_new, v_new and workspace start on a
+ *     16-byte boundary (every hipMalloc and torch allocation does; a view that starts
+ *     inside one may not); the int32 arrays on a 4-byte boundary.  A misaligned pointer
+ *     is PA_ERR_INVALID_ARG.
  *   - The caller owns every buffer.  The library allocates nothing, keeps no state
  *     across calls other than cached device attributes, and never frees caller memory.
  *   - Calls are asynchronous on `stream` (a hipStream_t passed as void*, NULL = the
@@ -61,7 +65,7 @@ extern "C" {
 
 typedef enum pa_status {
     PA_OK = 0,
-    PA_ERR_INVALID_ARG = 1,   /* null pointer, negative size, inconsistent shapes      */
+    PA_ERR_INVALID_ARG = 1,   /* null or misaligned pointer, negative size, bad shapes */
     PA_ERR_UNSUPPORTED = 2,   /* valid but not built: dtype, head_dim, block size     */
     PA_ERR_WORKSPACE = 3,     /* workspace pointer null or smaller than required      */
     PA_ERR_HIP = 4,           /* the HIP runtime reported an error at launch          */

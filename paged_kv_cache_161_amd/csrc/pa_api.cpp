@@ -32,9 +32,16 @@ size_t elem_bytes(int32_t dtype) { return dtype == PA_F32 ? 4 : (dtype == PA_FP8
 // one per lane of a single register.
 int32_t max_part_blocks(int32_t head_dim) { return pa::waves_per_group(head_dim) * pa::kWave; }
 
+// The kernels move pool tiles, q, out, new rows and workspace partials in 16-byte
+// vectors, and index arrays as 32-bit words.
+bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
+bool aligned4(const void *p) { return ((uintptr_t)p & 3) == 0; }
+
 pa_status check_pool(const pa_kv_pool *pool)
 {
     if (!pool || !pool->k_pool || !pool->v_pool)
+        return PA_ERR_INVALID_ARG;
+    if (!aligned16(pool->k_pool) || !aligned16(pool->v_pool))
         return PA_ERR_INVALID_ARG;
     if (pool->num_blocks <= 0 || pool->num_kv_heads <= 0 || pool->head_dim <= 0)
         return PA_ERR_INVALID_ARG;
@@ -150,6 +157,8 @@ pa_status pa_cache_append(const pa_kv_pool *pool, const void *k_new, const void 
         return PA_ERR_UNSUPPORTED;
     if (!k_new || !v_new || !slot_mapping)
         return PA_ERR_INVALID_ARG;
+    if (!aligned16(k_new) || !aligned16(v_new) || !aligned4(slot_mapping))
+        return PA_ERR_INVALID_ARG;
     pa::AppendArgs a;
     a.k_pool = pool->k_pool;
     a.v_pool = pool->v_pool;
@@ -179,6 +188,8 @@ pa_status pa_copy_blocks(const pa_kv_pool *pool, const int32_t *pairs, int32_t n
         return PA_OK;
     if (!pairs || num_pairs > 65535)
         return num_pairs > 65535 ? PA_ERR_UNSUPPORTED : PA_ERR_INVALID_ARG;
+    if (!aligned4(pairs))
+        return PA_ERR_INVALID_ARG;
     const size_t block_bytes =
         (size_t)pool->num_kv_heads * kBlock * pool->head_dim * elem_bytes(pool->dtype);
     hipError_t e = pa::launch_copy_blocks(pool->k_pool, pool->v_pool, pairs, num_pairs,
@@ -298,6 +309,10 @@ pa_status decode_impl(const pa_kv_pool *pool, const void *q, const void *k_new,
         return PA_OK;
     if (!q || !out || !block_tables || !context_lens || max_blocks_per_seq == 0)
         return PA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(out) || !aligned4(block_tables) || !aligned4(context_lens))
+        return PA_ERR_INVALID_ARG;
+    if ((k_new && !aligned16(k_new)) || (v_new && !aligned16(v_new)))
+        return PA_ERR_INVALID_ARG;
 
     const int32_t pb = choose_part_blocks(num_seqs, num_q_heads, pool->num_kv_heads,
                                           pool->head_dim, max_context_len, partition_tokens);
@@ -308,6 +323,8 @@ pa_status decode_impl(const pa_kv_pool *pool, const void *q, const void *k_new,
                                                   partition_tokens);
     if (need > 0 && (!workspace || workspace_bytes < need))
         return PA_ERR_WORKSPACE;
+    if (need > 0 && !aligned16(workspace))
+        return PA_ERR_INVALID_ARG;
     if (pb > max_part_blocks(pool->head_dim))
         return PA_ERR_UNSUPPORTED;
 
@@ -406,6 +423,9 @@ pa_status pa_prefill(const pa_kv_pool *pool, const void *q, void *out, int32_t n
         return PA_OK;
     if (!q || !out || !query_start || !block_tables || !context_lens || max_blocks_per_seq == 0)
         return PA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(out) || !aligned4(query_start) || !aligned4(block_tables) ||
+        !aligned4(context_lens))
+        return PA_ERR_INVALID_ARG;
     const int32_t q_tile = rows / group;
     const int64_t qtiles = ((int64_t)max_query_len + q_tile - 1) / q_tile;
     const int64_t pairs = (int64_t)num_seqs * pool->num_kv_heads;
@@ -434,6 +454,7 @@ pa_status pa_prefill(const pa_kv_pool *pool, const void *q, void *out, int32_t n
     const bool fp8 = pool->dtype == PA_FP8_E4M3;
     a.scale_log2 = scale * 1.4426950408889634f * (fp8 ? pool->k_scale : 1.0f);
     a.v_scale = fp8 ? pool->v_scale : 1.0f;
+    a.longest_first = (num_seqs > 1 && num_seqs <= pa::kLongestFirstMax) ? 1 : 0;
     hipError_t e = pa::launch_prefill(pool->dtype, pool->act_dtype, pool->head_dim, a,
                                       static_cast<hipStream_t>(stream));
     return e == hipSuccess ? PA_OK : PA_ERR_HIP;

@@ -27,6 +27,7 @@ struct PrefillArgs {
     int32_t num_qtiles;               // ceil(max_query_len / q_tile)
     float scale_log2;                 // scale * log2(e) (* k_scale for fp8 pools), > 0
     float v_scale;
+    int32_t longest_first;            // 1: sequences taken in order of estimated tile cost
 };
 
 // Prefill workgroup shape: waves and 16-row MFMA column blocks per wave.

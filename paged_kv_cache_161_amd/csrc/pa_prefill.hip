@@ -31,6 +31,7 @@
 #include <limits.h>
 #include <math.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "pa_common.h"
@@ -158,17 +159,113 @@ __global__ __launch_bounds__(NW *kWave, C <= 2 ? 2 : 1) void pa_prefill_kernel(P
     __shared__ u32x4 s_k[2][KSLOTS];
     __shared__ u32x4 s_v[2][VSLOTS];
 
-    // ---- which (sequence, kv-head, query tile): tiles of one pair share an XCD, the
-    // last tile (most keys) first
+    // ---- which (sequence, kv-head, query tile).  Workgroup ids go round-robin over
+    // the XCDs; XCD x takes the (sequence, kv-head) pairs p with p % 8 == x, pair p
+    // being kv-head p % Hkv of the (p / Hkv)-th sequence, so all query tiles of a pair
+    // share that XCD's L2.  A pair's tiles run last tile (most keys) first.
     const int id = blockIdx.x;
     const int xcd = id % kXcds;
-    const int rr = id / kXcds;
-    const int pair = (rr / a.num_qtiles) * kXcds + xcd;
-    if (pair >= a.num_seqs * a.num_kv_heads)
-        return;
-    const int qt = a.num_qtiles - 1 - rr % a.num_qtiles;
-    const int b = pair / a.num_kv_heads;
-    const int kvh = pair - b * a.num_kv_heads;
+    const int k_x = id / kXcds;                  // this workgroup's rank on its XCD
+    int b, kvh, qt;
+    if (a.longest_first) {
+        // Sequences are taken in order of estimated tile cost, highest first (ties by
+        // index), so the tiles that walk the most keys start first instead of behind
+        // a batch of short ones.  The estimate is the key count of a sequence's last
+        // tile (its whole context), halved for tiles whose keys are split over the
+        // waves (measured to take about half as long as a full tile over the same
+        // keys).  In the launch that allows partial tiles, the grid is also compact:
+        // XCD x's work items are its pairs' tiles in that order, found by a prefix
+        // sum over the ranked sequences, so no workgroup is spent on a tile past a
+        // short chunk's end.  The scratch sits in the K staging buffer, free until
+        // the first staging.
+        __shared__ int s_pick[3];
+        int *s_cost = reinterpret_cast<int *>(&s_k[0][0]);   // [kLongestFirstMax] each
+        int *s_ntl = s_cost + kLongestFirstMax;
+        int *s_seq = s_ntl + kLongestFirstMax;
+        const int nseq = a.num_seqs;                 // <= kLongestFirstMax (host-checked)
+        const int tid0 = threadIdx.x;
+        if (tid0 < nseq) {
+            const int q0t = a.query_start[tid0];
+            const int qlt = a.query_start[tid0 + 1] - q0t;
+            const int cx = a.context_lens[tid0];
+            const bool valid = q0t >= 0 && qlt >= 0 && qlt <= a.max_query_len &&
+                               q0t <= a.num_tokens - qlt;
+            int cost = valid && qlt > 0 && cx > 0 ? cx : 0;
+            if (IDLE && D <= 128 && qlt * a.group <= 16)
+                cost /= 2;
+            s_cost[tid0] = cost;
+            s_ntl[tid0] = valid ? (qlt + a.q_tile - 1) / a.q_tile : 0;
+        }
+        __syncthreads();
+        // the plain map's pair, for the full-tile launch (every sequence has the same
+        // tile count there)
+        const int pair = (k_x / a.num_qtiles) * kXcds + xcd;
+        if (tid0 < nseq) {
+            const int c = s_cost[tid0];
+            int rank = 0;
+            for (int u = 0; u < nseq; ++u) {
+                const int cu = s_cost[u];
+                rank += (cu > c || (cu == c && u < tid0)) ? 1 : 0;
+            }
+            s_seq[rank] = tid0;
+            if (!IDLE && rank == pair / a.num_kv_heads)
+                s_pick[0] = tid0;
+        }
+        __syncthreads();
+        if constexpr (IDLE) {
+            // rank r's pairs on this XCD: kv-heads h0, h0 + 8, ... below Hkv, with
+            // h0 = (x - r Hkv) mod 8; each has the sequence's tile count.  An
+            // inclusive prefix over ranks (ranks are thread ids, four waves at most).
+            const int hkv = a.num_kv_heads;
+            int cnt = 0, h0 = 0, ntl = 0;
+            if (tid0 < nseq) {
+                h0 = ((xcd - (int)(((int64_t)tid0 * hkv) % kXcds)) % kXcds + kXcds) % kXcds;
+                ntl = s_ntl[s_seq[tid0]];
+                cnt = h0 < hkv ? ((hkv - 1 - h0) / kXcds + 1) * ntl : 0;
+            }
+            int incl = cnt;
+#pragma unroll
+            for (int o = 1; o < kWave; o *= 2) {
+                const int v = __shfl_up(incl, o);
+                if ((tid0 & (kWave - 1)) >= o)
+                    incl += v;
+            }
+            int *s_wsum = s_seq + kLongestFirstMax;          // [NW]
+            if ((tid0 & (kWave - 1)) == kWave - 1)
+                s_wsum[tid0 / kWave] = incl;
+            __syncthreads();
+            for (int w = 0; w < tid0 / kWave; ++w)
+                incl += s_wsum[w];
+            const int excl = incl - cnt;
+            if (tid0 < nseq && excl <= k_x && k_x < incl) {
+                const int off = k_x - excl;
+                s_pick[0] = s_seq[tid0];
+                s_pick[1] = h0 + kXcds * (off / ntl);
+                s_pick[2] = ntl - 1 - off % ntl;
+            }
+            if (tid0 == nseq - 1 && k_x >= incl)
+                s_pick[0] = -1;                      // past this XCD's last item
+            __syncthreads();
+            b = __builtin_amdgcn_readfirstlane(s_pick[0]);
+            if (b < 0)
+                return;
+            kvh = __builtin_amdgcn_readfirstlane(s_pick[1]);
+            qt = __builtin_amdgcn_readfirstlane(s_pick[2]);
+        } else {
+            if (pair >= a.num_seqs * a.num_kv_heads)
+                return;
+            qt = a.num_qtiles - 1 - k_x % a.num_qtiles;
+            kvh = pair % a.num_kv_heads;
+            b = __builtin_amdgcn_readfirstlane(s_pick[0]);
+        }
+    } else {
+        const int pair = (k_x / a.num_qtiles) * kXcds + xcd;
+        if (pair >= a.num_seqs * a.num_kv_heads)
+            return;
+        qt = a.num_qtiles - 1 - k_x % a.num_qtiles;
+        kvh = pair % a.num_kv_heads;
+        b = pair / a.num_kv_heads;
+    }
     const int q0 = a.query_start[b];
     const int q_len = a.query_start[b + 1] - q0;
     // A malformed query range has no rows that can be written safely.
@@ -239,6 +336,219 @@ __global__ __launch_bounds__(NW *kWave, C <= 2 ? 2 : 1) void pa_prefill_kernel(P
             ph[tl] = (need && in_pool) ? raw[tl] : 0;
         }
     };
+
+    // ---- a tile whose rows all fit one MFMA column block (a decode row, a chunk's
+    // last position or two): with the usual split, one wave would own every row and
+    // the other waves would only stage its keys.  Instead every wave takes those same
+    // rows and a contiguous 1/NW of the key steps, loads its K and V fragments straight
+    // from the pool into registers (no LDS staging, two steps in flight), and the NW
+    // partial (max, sum, O) sets are merged through LDS at the end with the same
+    // rescaling rule as the online softmax.  Only in the launch that allows partial
+    // tiles, and where the two steps' fragments fit the register file (d <= 128).
+    if constexpr (IDLE && D <= 128) {
+        if (n_here * a.group <= 16) {
+            using KRaw = typename std::conditional<DT == DT_FP8, u32x2, u32x4>::type;
+            using VRaw = typename std::conditional<DT == DT_FP8, uint32_t, u32x2>::type;
+            const float sl = a.scale_log2;
+            const float grow_thr = fminf(kRescaleSlack / sl, 3.0e38f);
+            const u32x4 ones = {one_pair<AT>(), one_pair<AT>(), one_pair<AT>(), one_pair<AT>()};
+            // row r16 of the tile (the first column block's layout), for every wave
+            const int lp = r16 / a.group;
+            const int hh = r16 - lp * a.group;
+            const bool ok = lp < n_here;
+            const int orow1 = ok ? (q0 + p_lo + lp) * a.num_q_heads + kvh * a.group + hh : -1;
+            const int pos1 = ok ? first + lp : INT_MIN / 2;
+            u32x4 q1[NKC];
+            const uint16_t *qrow = qp + (size_t)(ok ? orow1 : 0) * D;
+#pragma unroll
+            for (int kc = 0; kc < NKC; ++kc)
+                q1[kc] = ok ? *reinterpret_cast<const u32x4 *>(qrow + 32 * kc + 8 * g)
+                            : u32x4{0u, 0u, 0u, 0u};
+            const int s_lo = (int)(((int64_t)nsteps * wave) / NW);
+            const int s_hi = (int)(((int64_t)nsteps * (wave + 1)) / NW);
+
+            // Step s's fragments, in the operand order of the staged path: K rows of
+            // token r16, e = 32 kc + 8 g .. +7; V^T rows e = 16 n + r16, tokens
+            // 4 g .. 4 g + 3 of each of the step's two blocks.
+            auto load_step = [&](int s, KRaw (&kr)[NKC][2], VRaw (&vr)[NDB][2]) {
+                int raw[2], ph[2];
+                table(s, raw);
+                resolve(s, raw, ph);
+#pragma unroll
+                for (int tl = 0; tl < 2; ++tl) {
+                    const size_t blk = (uint64_t)(uint32_t)ph[tl] * blk_stride32;
+                    const Elem *kp = kbase + blk + r16 * D + 8 * g;
+                    const Elem *vp = vbase + blk + r16 * kBlock + 4 * g;
+#pragma unroll
+                    for (int kc = 0; kc < NKC; ++kc)
+                        kr[kc][tl] = *reinterpret_cast<const KRaw *>(kp + 32 * kc);
+#pragma unroll
+                    for (int n = 0; n < NDB; ++n)
+                        vr[n][tl] = *reinterpret_cast<const VRaw *>(vp + 16 * kBlock * n);
+                }
+            };
+
+            f32x4 o1[NDB];
+#pragma unroll
+            for (int n = 0; n < NDB; ++n)
+                o1[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+            f32x4 l1 = {0.f, 0.f, 0.f, 0.f};
+            float m1 = -INFINITY, mneg1 = 0.f;
+
+            auto step = [&](int s, const KRaw (&kr)[NKC][2], const VRaw (&vr)[NDB][2]) {
+                f32x4 sc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+                for (int kc = 0; kc < NKC; ++kc)
+#pragma unroll
+                    for (int tl = 0; tl < 2; ++tl) {
+                        u32x4 kf;
+                        if constexpr (DT == DT_FP8) {
+                            const u32x2 w = kr[kc][tl];
+                            kf = u32x4{fp8x2_to_16<AT, false>(w[0]), fp8x2_to_16<AT, true>(w[0]),
+                                       fp8x2_to_16<AT, false>(w[1]), fp8x2_to_16<AT, true>(w[1])};
+                        } else {
+                            kf = kr[kc][tl];
+                        }
+                        sc[tl] = mma32<AT>(kf, q1[kc], sc[tl]);
+                    }
+                if (32 * s + 31 > first) {
+#pragma unroll
+                    for (int tl = 0; tl < 2; ++tl)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            sc[tl][j] = (32 * s + 16 * tl + 4 * g + j <= pos1) ? sc[tl][j]
+                                                                               : -INFINITY;
+                }
+                const float lmx = max8(sc);
+                if (__any(lmx - m1 > grow_thr)) {
+                    const float m_new = fmaxf(m1, max_over_row_groups(lmx));
+                    const float alpha = (m_new == -INFINITY) ? 1.f : exp2_fast((m1 - m_new) * sl);
+#pragma unroll
+                    for (int n = 0; n < NDB; ++n)
+                        o1[n] *= alpha;
+                    l1 *= alpha;
+                    m1 = m_new;
+                    mneg1 = (m_new == -INFINITY) ? 0.f : -m_new * sl;
+                }
+                f32x4 p0, p1;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    p0[j] = exp2_fast(fmaf(sc[0][j], sl, mneg1));
+                    p1[j] = exp2_fast(fmaf(sc[1][j], sl, mneg1));
+                }
+                const u32x4 pb = pack8<AT>(p0, p1);
+                // V^T tokens past the context, and whole blocks past key_end (padding
+                // entries read as block 0), may hold anything: zero them
+                uint32_t keep[2][2];
+#pragma unroll
+                for (int tl = 0; tl < 2; ++tl) {
+                    const int blk0 = (2 * s + tl) * kBlock;
+                    const int valid = blk0 >= key_end ? 0 : ctx - blk0;
+#pragma unroll
+                    for (int w = 0; w < 2; ++w) {
+                        if constexpr (DT == DT_FP8) {
+                            uint32_t m = 0;
+#pragma unroll
+                            for (int j = 0; j < 2; ++j)
+                                m |= (4 * g + 2 * w + j < valid) ? (0xFFu << (8 * (2 * w + j))) : 0u;
+                            keep[tl][w] = m;
+                        } else {
+                            keep[tl][w] = (4 * g + 2 * w < valid ? 0x0000FFFFu : 0u) |
+                                          (4 * g + 2 * w + 1 < valid ? 0xFFFF0000u : 0u);
+                        }
+                    }
+                }
+#pragma unroll
+                for (int n = 0; n < NDB; ++n) {
+                    u32x4 vf;
+                    if constexpr (DT == DT_FP8) {
+                        const uint32_t w0 = vr[n][0] & (keep[0][0] | keep[0][1]);
+                        const uint32_t w1 = vr[n][1] & (keep[1][0] | keep[1][1]);
+                        vf = u32x4{fp8x2_to_16<AT, false>(w0), fp8x2_to_16<AT, true>(w0),
+                                   fp8x2_to_16<AT, false>(w1), fp8x2_to_16<AT, true>(w1)};
+                    } else {
+                        vf = u32x4{vr[n][0][0] & keep[0][0], vr[n][0][1] & keep[0][1],
+                                   vr[n][1][0] & keep[1][0], vr[n][1][1] & keep[1][1]};
+                    }
+                    o1[n] = mma32<AT>(vf, pb, o1[n]);
+                }
+                l1 = mma32<AT>(ones, pb, l1);
+            };
+
+            // two steps in flight: the loads of the step after next are issued before
+            // a step's products; the last step's loads are repeated past the end so
+            // every pass issues the same loads
+            if (s_lo < s_hi) {
+                KRaw ka[NKC][2], kb[NKC][2];
+                VRaw va[NDB][2], vb[NDB][2];
+                load_step(s_lo, ka, va);
+                for (int s = s_lo; s < s_hi; s += 2) {
+                    load_step(min(s + 1, s_hi - 1), kb, vb);
+                    step(s, ka, va);
+                    load_step(min(s + 2, s_hi - 1), ka, va);
+                    if (s + 1 < s_hi)
+                        step(s + 1, kb, vb);
+                }
+            }
+
+            // ---- merge: each row's reference max over the waves, every wave's O and
+            // l rescaled to it, then summed (a tree over four LDS slots: the staging
+            // buffers, idle here, each hold one wave's O^T fragments exactly)
+            __shared__ float s_m[NW][16];
+            __shared__ float s_l[NW][16];
+            if (g == 0)
+                s_m[wave][r16] = m1;
+            const bool any_bad = __syncthreads_or(bad ? 1 : 0) != 0 || bad_ctx;
+            float mx = -INFINITY;
+#pragma unroll
+            for (int w = 0; w < NW; ++w)
+                mx = fmaxf(mx, s_m[w][r16]);
+            const float f = (m1 == -INFINITY) ? 0.f : exp2_fast((m1 - mx) * sl);
+#pragma unroll
+            for (int n = 0; n < NDB; ++n)
+                o1[n] *= f;
+            if (g == 0)
+                s_l[wave][r16] = l1[0] * f;
+#pragma unroll
+            for (int half = NW / 2; half >= 1; half /= 2) {
+                if (wave >= half && wave < 2 * half) {
+                    const int k = wave - half;
+                    u32x4 *slot = k < 2 ? s_k[k] : s_v[k - 2];
+#pragma unroll
+                    for (int n = 0; n < NDB; ++n)
+                        slot[n * kWave + lane] = __builtin_bit_cast(u32x4, o1[n]);
+                }
+                __syncthreads();
+                if (wave < half) {
+                    const u32x4 *slot = wave < 2 ? s_k[wave] : s_v[wave - 2];
+#pragma unroll
+                    for (int n = 0; n < NDB; ++n)
+                        o1[n] += __builtin_bit_cast(f32x4, slot[n * kWave + lane]);
+                }
+                __syncthreads();
+            }
+            if (wave == 0 && orow1 >= 0) {
+                float l = 0.f;
+#pragma unroll
+                for (int w = 0; w < NW; ++w)
+                    l += s_l[w][r16];
+                const float fo = l > 0.f ? a.v_scale / l : 0.f;
+                const float qnan = __builtin_nanf("");
+#pragma unroll
+                for (int n = 0; n < NDB; ++n) {
+                    f32x4 v = o1[n] * fo;
+                    if (any_bad)
+                        v = f32x4{qnan, qnan, qnan, qnan};
+                    uint16_t *dst = static_cast<uint16_t *>(a.out) + (size_t)orow1 * D + 16 * n + 4 * g;
+                    if constexpr (AT == DT_BF16)
+                        *reinterpret_cast<bf16x4 *>(dst) = __builtin_convertvector(v, bf16x4);
+                    else
+                        *reinterpret_cast<f16x4 *>(dst) = __builtin_convertvector(v, f16x4);
+                }
+            }
+            return;
+        }
+    }
 
     // ---- each thread's 16-byte pieces of a step, fixed for the whole loop: which of
     // the step's two blocks (the same for a whole wave, kept scalar), the element
@@ -619,7 +929,7 @@ hipError_t launch_prefill(int dtype, int act_dtype, int head_dim, const PrefillA
                           hipStream_t stream)
 {
     const int pairs = a.num_seqs * a.num_kv_heads;
-    const int grid = (pairs + kXcds - 1) / kXcds * kXcds * a.num_qtiles;
+    const int grid_plain = (pairs + kXcds - 1) / kXcds * kXcds * a.num_qtiles;
     // Every tile is full, and so every wave has rows, when all chunks have the
     // longest length, that length is a whole number of tiles, and a tile's rows reach
     // the last wave; otherwise idle waves may occur and the kernel that lets them
@@ -627,6 +937,19 @@ hipError_t launch_prefill(int dtype, int act_dtype, int head_dim, const PrefillA
     const bool full = (int64_t)a.num_tokens == (int64_t)a.num_seqs * a.max_query_len &&
                       a.max_query_len % a.q_tile == 0 &&
                       a.q_tile * a.group > (kPrefillWaves - 1) * prefill_cols(head_dim) * 16;
+    // The compact map (partial tiles possible, ranked batch) needs as many workgroups
+    // per XCD as its busiest XCD has tiles: a sequence puts at most ceil(Hkv / 8) of its
+    // pairs on one XCD, and the chunks hold at most T / q_tile + B tiles when their
+    // query ranges do not overlap (ranges that do are outside the contract and may then
+    // lose tiles).  Never more than the plain map's share per XCD.
+    int grid = grid_plain;
+    if (!full && a.longest_first) {
+        const int64_t tiles = std::min<int64_t>((int64_t)a.num_tokens / a.q_tile + a.num_seqs,
+                                                (int64_t)a.num_seqs * a.num_qtiles);
+        const int64_t per_xcd = std::min<int64_t>((a.num_kv_heads + kXcds - 1) / kXcds * tiles,
+                                                  (int64_t)grid_plain / kXcds);
+        grid = (int)(per_xcd * kXcds);
+    }
 #define PA_PF_CASE(DT, AT, D)                                                      \
     if (dtype == DT && act_dtype == AT && head_dim == D)                          \
         return launch_prefill_t<DT, AT, D>(a, grid, !full, stream);

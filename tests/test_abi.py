@@ -218,3 +218,36 @@ def test_workspace_matches_partitions(lib):
     assert ws(32, 64, 8, 128, 4096, 512) == 32 * 64 * 8 * (128 + 2) * 4
     assert ws(2, 64, 2, 128, 4096, 512) == 2 * 64 * 8 * (128 + 2) * 4
     assert ws(2, 3, 2, 128, 10, 0) == ctypes.c_size_t(-1).value
+
+
+def test_misaligned_pointers_are_rejected(lib):
+    """Pool tiles, q, out, new rows and workspace are moved in 16-byte vectors and the
+    index arrays as 32-bit words: a pointer off those boundaries is refused on the host
+    (every call below fails its argument check, so nothing is launched)."""
+    inval = 1
+    off8, off2 = ctypes.c_void_p(0x3008), ctypes.c_void_p(0x3002)
+    assert _decode(lib, _pool(k_pool=0x1008)) == inval
+    assert _decode(lib, _pool(v_pool=0x2004)) == inval
+    assert _decode(lib, _pool(), q=off8) == inval
+    assert _decode(lib, _pool(), out=off8) == inval
+    assert _decode(lib, _pool(), bt=off2) == inval
+    assert _decode(lib, _pool(), cl=off2) == inval
+    need = lib.pa_decode_workspace_bytes(2, 4, 2, 128, 100, 32)
+    assert _decode(lib, _pool(), ptok=32, ws=off8, ws_bytes=need) == inval
+    assert _prefill(lib, _pool(), q=off8) == inval
+    assert _prefill(lib, _pool(), out=off8) == inval
+    assert _prefill(lib, _pool(), qs=off2) == inval
+    assert _prefill(lib, _pool(), bt=off2) == inval
+    assert _prefill(lib, _pool(), cl=off2) == inval
+    da = lib.pa_decode_append
+    for k, v in ((off8, FAKE), (FAKE, off8)):
+        assert da(ctypes.byref(_pool()), FAKE, k, v, FAKE, 2, 4, ctypes.c_float(0.125), FAKE, 8,
+                  FAKE, 100, 0, None, 0, None) == inval
+    ap = lib.pa_cache_append
+    pool = _pool()
+    assert ap(ctypes.byref(pool), off8, FAKE, FAKE, 4, None) == inval
+    assert ap(ctypes.byref(pool), FAKE, off8, FAKE, 4, None) == inval
+    assert ap(ctypes.byref(pool), FAKE, FAKE, off2, 4, None) == inval
+    assert ap(ctypes.byref(_pool(k_pool=0x1001)), FAKE, FAKE, FAKE, 4, None) == inval
+    assert lib.pa_copy_blocks(ctypes.byref(pool), off2, 1, None) == inval
+    assert lib.pa_copy_blocks(ctypes.byref(_pool(v_pool=0x2008)), FAKE, 1, None) == inval

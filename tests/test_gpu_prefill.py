@@ -59,6 +59,18 @@ SMALL = [
            kv_dtype="fp8", k_scale=0.0117, v_scale=0.0093, query_lens=[40, 33]),
     W.Spec("pf_full_tiles_f16_d256", "f16", 32, 4, 256, [64, 96], seed=43, spare_blocks=1,
            query_lens=[32, 32]),
+    # decode rows and 2- or 3-position chunks: tiles whose rows fit one 16-row column
+    # block, whose key steps are split over the workgroup's waves and merged (contexts
+    # of 1, 15, 16 and 17 tokens leave most waves without a step)
+    W.Spec("pf_decode_rows_bf16", "bf16", 64, 8, 128, [1, 15, 16, 17, 255, 1000, 2049, 70],
+           seed=44, spare_blocks=1, query_lens=[1, 1, 1, 1, 1, 1, 1, 70]),
+    W.Spec("pf_decode_rows_fp8_bf16", "bf16", 16, 2, 128, [5, 33, 600, 1500], seed=45,
+           spare_blocks=1, kv_dtype="fp8", k_scale=0.0117, v_scale=0.0093,
+           query_lens=[1, 1, 1, 2]),
+    W.Spec("pf_decode_rows_fp8_f16", "f16", 32, 4, 128, [2000, 19], seed=46, spare_blocks=1,
+           kv_dtype="fp8", k_scale=0.25, v_scale=0.0625, query_lens=[1, 2]),
+    W.Spec("pf_decode_rows_f16_mha_d64", "f16", 16, 16, 64, [40, 900, 500], seed=47,
+           spare_blocks=1, query_lens=[1, 16, 3]),
 ]
 
 
@@ -75,8 +87,10 @@ def gpu_prefill(w, pools=None):
     d = U.device_inputs(w)
     PA.cache_append(kp, vp, d["k_new"], d["v_new"], d["slot_mapping"], **U.scales(w))
     qs = torch.from_numpy(w.query_start).cuda()
-    out = PA.prefill(d["q"], kp, vp, qs, d["block_tables"], d["context_lens"], float(w.scale),
-                     w.max_context_len, w.max_query_len, **U.scales(w))
+    # NaN first: a row the launch fails to write cannot pass for a computed one
+    out = torch.full_like(d["q"], float("nan"))
+    PA.prefill(d["q"], kp, vp, qs, d["block_tables"], d["context_lens"], float(w.scale),
+               w.max_context_len, w.max_query_len, out=out, **U.scales(w))
     torch.cuda.synchronize()
     return U.widen(U.from_dev(out, w.dtype), w.dtype), kp, vp
 
@@ -200,6 +214,32 @@ def test_prefill_bad_table_entry_and_length_poison_only_their_sequence():
     assert np.isnan(got[qs[0]:qs[1]][pos0 >= 32]).all()
     assert np.isnan(got[qs[2]:qs[3]]).all()
     ok, mx, mean = U.tolerance_ok(got[qs[1]:qs[2]], ref[qs[1]:qs[2]], w.dtype)
+    assert ok, (mx, mean)
+
+
+def test_prefill_split_tile_bad_entry_poisons_only_its_row():
+    """Decode rows (tiles whose keys are split over the waves): a bad id inside one
+    row's context turns that row into NaN; a bad id in the table past another row's
+    context is never read."""
+    spec = W.Spec("pf_bad_split", "bf16", 16, 2, 128, [300, 300, 45], seed=48,
+                  spare_blocks=1, max_blocks_per_seq=24, query_lens=[1, 1, 1])
+    w = W.build(spec)
+    kpo, vpo, bt = oracle_pools(w)
+    ref, _ = O.prefill_paged(w.q, kpo, vpo, w.kv_dtype, w.query_start, bt, w.context_lens,
+                             w.scale, q_dtype=w.dtype)
+    kd, vd = U.device_pools(w)
+    d = U.device_inputs(w)
+    PA.cache_append(kd, vd, d["k_new"], d["v_new"], d["slot_mapping"])
+    tables = d["block_tables"].clone()
+    tables[0, 5] = w.num_blocks + 5                # inside sequence 0's 19 blocks
+    tables[1, 21] = -7                             # past sequence 1's context
+    out = PA.prefill(d["q"], kd, vd, torch.from_numpy(w.query_start).cuda(), tables,
+                     d["context_lens"], float(w.scale), w.max_context_len, w.max_query_len)
+    torch.cuda.synchronize()
+    got = U.widen(U.from_dev(out, w.dtype), w.dtype)
+    assert np.isnan(got[0]).all()
+    assert not np.isnan(got[1:]).any()
+    ok, mx, mean = U.tolerance_ok(got[1:], ref[1:], w.dtype)
     assert ok, (mx, mean)
 
 
