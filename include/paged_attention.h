@@ -218,7 +218,7 @@ pa_status pa_decode_append(const pa_kv_pool *pool, const void *q, const void *k_
  * 0 .. context_lens[b] - q_len + i; a query placed before the context (q_len >
  * context_lens[b]) gets a zero row.  A chunk of one query is exactly a decode step.
  * Supported: 16-bit pools (f16, bf16) and fp8 pools with f16/bf16 activations, head_dim
- * 64, 128 or 256, num_q_heads / num_kv_heads <= 256 (<= 128 at head_dim 256),
+ * 64, 128 or 256, num_q_heads / num_kv_heads <= 256 (512 at head_dim 64, 128 at 256),
  * num_kv_heads * 16 * head_dim < 2^32 (PA_ERR_UNSUPPORTED otherwise).
  * Device-side inconsistency: a bad context length or a needed table entry outside
  * [0, num_blocks) makes that sequence's rows NaN; a query range that is decreasing,

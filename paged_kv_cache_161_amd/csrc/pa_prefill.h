@@ -40,9 +40,14 @@ struct PrefillArgs {
 constexpr int kPrefillWaves = PA_PREFILL_WAVES;
 constexpr int kPrefillCols = PA_PREFILL_COLS;
 
-// Column blocks per wave at head_dim d: kPrefillCols up to d = 128, one at d = 256,
-// whose O accumulators, q fragments and K/V fragments take twice the registers per row.
-constexpr int prefill_cols(int head_dim) { return head_dim > 128 ? 1 : kPrefillCols; }
+// Column blocks per wave at head_dim d, so that C * d = 256 at every size (the same
+// registers for O accumulators, q fragments and K/V fragments): four at d = 64, where
+// more rows per wave halve the LDS fragment bytes per product; kPrefillCols at
+// d = 128; one at d = 256.
+constexpr int prefill_cols(int head_dim)
+{
+    return head_dim > 128 ? 1 : (head_dim <= 64 ? 2 * kPrefillCols : kPrefillCols);
+}
 
 // Query rows ((position, q-head) pairs) one prefill workgroup holds at head_dim d.
 int prefill_rows_per_group(int head_dim);

@@ -141,7 +141,7 @@ __device__ __forceinline__ u32x4 keep_tokens8(u32x4 v, int t0, int valid)
 }
 
 template <int DT, int AT, int D, int NW, int C, bool IDLE>
-__global__ __launch_bounds__(NW *kWave, C <= 2 ? 2 : 1) void pa_prefill_kernel(PrefillArgs a)
+__global__ __launch_bounds__(NW *kWave, C * D <= 256 ? 2 : 1) void pa_prefill_kernel(PrefillArgs a)
 {
     using Elem = typename std::conditional<DT == DT_FP8, uint8_t, uint16_t>::type;
     constexpr int NT = NW * kWave;
