@@ -254,7 +254,8 @@ pa_status pa_copy_blocks(const pa_kv_pool *pool, const int32_t *pairs, int32_t n
 typedef struct pa_block_allocator pa_block_allocator;
 
 /* A new allocator owning blocks 0 .. num_blocks-1, all free, in that order.  NULL on
- * num_blocks <= 0 or allocation failure.  Free it with pa_allocator_destroy. */
+ * num_blocks <= 0, on num_blocks * 16 > INT32_MAX (slots are int32, as for the pool),
+ * or on allocation failure.  Free it with pa_allocator_destroy. */
 pa_block_allocator *pa_allocator_create(int32_t num_blocks);
 void pa_allocator_destroy(pa_block_allocator *alloc);
 

@@ -8,6 +8,7 @@
 // write is replaced by a private copy first (same page, section "Copy-on-Write 优化").
 // Every entry point validates all of its input before changing anything, so a failed
 // call leaves the allocator and the caller's arrays as they were.
+#include <limits.h>
 #include <stdint.h>
 
 #include <new>
@@ -80,7 +81,7 @@ extern "C" {
 
 pa_block_allocator *pa_allocator_create(int32_t num_blocks)
 {
-    if (num_blocks <= 0)
+    if (num_blocks <= 0 || (int64_t)num_blocks * kBlock > INT32_MAX)   // slots are int32
         return nullptr;
     pa_block_allocator *a = new (std::nothrow) pa_block_allocator;
     if (!a)

@@ -163,3 +163,14 @@ def test_shortfall_and_bad_arguments_change_nothing():
     with pytest.raises(B.PaError):
         a.reserve(bad, 20, 1)
     assert (r == before[0]).all() and a.num_free == before[1]
+
+
+def test_create_rejects_sizes_whose_slots_overflow_int32():
+    """Slots are block * 16 + row in int32: at most 2^31 / 16 blocks (the pool's bound
+    too), and at least one."""
+    lib = B.load()
+    assert not lib.pa_allocator_create(0)
+    assert not lib.pa_allocator_create(-5)
+    assert not lib.pa_allocator_create((2 ** 31 - 1) // 16 + 1)
+    with pytest.raises(B.PaError):
+        B.BlockAllocator(2 ** 27)
