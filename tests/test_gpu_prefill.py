@@ -33,6 +33,13 @@ def hip_library():
     PA.load()
 
 
+# 300 sequences: contexts of 1..80 tokens, chunks of 1..4 positions (decode rows and
+# split tiles) and every tenth one up to 40 positions
+_r300 = np.random.Generator(np.random.PCG64(300))
+_CTX300 = [int(x) for x in _r300.integers(1, 81, 300)]
+_Q300 = [int(min(c, 1 + (_r300.integers(0, 40) if i % 10 == 0 else _r300.integers(0, 4))))
+         for i, c in enumerate(_CTX300)]
+
 SMALL = [
     W.Spec("pf_prompt_bf16_d64", "bf16", 8, 2, 64, [1, 17, 45, 300], seed=31, spare_blocks=2,
            query_lens=[1, 17, 45, 300]),
@@ -71,6 +78,12 @@ SMALL = [
            kv_dtype="fp8", k_scale=0.25, v_scale=0.0625, query_lens=[1, 2]),
     W.Spec("pf_decode_rows_f16_mha_d64", "f16", 16, 16, 64, [40, 900, 500], seed=47,
            spare_blocks=1, query_lens=[1, 16, 3]),
+    # more sequences than the ranked map takes (plain map, launch order by index), and a
+    # single sequence (nothing to rank)
+    W.Spec("pf_300_seqs_bf16", "bf16", 8, 2, 128, _CTX300, seed=49, spare_blocks=1,
+           query_lens=_Q300),
+    W.Spec("pf_single_seq_bf16", "bf16", 64, 8, 128, [530], seed=50, spare_blocks=1,
+           query_lens=[300]),
 ]
 
 
