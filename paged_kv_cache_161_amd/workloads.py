@@ -420,7 +420,8 @@ def config_spec(i: int) -> Spec:
       pool where a random 30% of blocks is free and the rest belongs to other requests.
     5 long + shared prefix bf16: 4 seqs x 32768 and 8 beams x 2304 that share their first
       2048 tokens (128 physical blocks), 64/8 heads, d 128.
-    6 config 3 with an FP8 E4M3 KV cache (k_scale 0.0117, v_scale 0.0093), bf16 q/out.
+    6 the Llama-70B-shaped GQA workload (32 x 4096) with an FP8 E4M3 KV cache
+      (k_scale 0.0117, v_scale 0.0093), bf16 q/out.
     7 chunked prefill: 16 prompts of 4096 tokens whose last 512-token chunk attends
       (causally) to the whole cache, 64/8 heads, d 128, bf16.
     8 mixed prefill + decode batch: 24 ragged decodes, four 512-token chunks ending at
@@ -443,7 +444,8 @@ def config_spec(i: int) -> Spec:
                     max_blocks_per_seq=2048,
                     prefix_groups=[(list(range(4, 12)), 128)])
     if i == 6:
-        # config 3's shape with an FP8 E4M3 KV cache (per-tensor scales), bf16 q/out
+        # the Llama-70B-shaped GQA workload with an FP8 E4M3 KV cache (per-tensor
+        # scales), bf16 q/out
         return Spec("llama70b_gqa_fp8kv", "bf16", 64, 8, 128, [4096] * 32, seed=3,
                     spare_blocks=32, kv_dtype="fp8", k_scale=0.0117, v_scale=0.0093)
     if i == 7:

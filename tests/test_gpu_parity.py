@@ -163,13 +163,14 @@ def test_decode_config(i):
 
 
 @pytest.mark.parametrize("ptok", [16, 512, 4096])
-def test_decode_config3_forced_partitions(ptok):
-    """Split-context with other partition lengths meets the same bar."""
+def test_decode_llama70b_gqa_forced_partitions(ptok):
+    """Split-context with other partition lengths meets the same bar (Llama-70B-shaped
+    GQA, 32 x 4096 tokens)."""
     w = config(3)
-    say(f"[split] config 3 partition_tokens={ptok}")
+    say(f"[split] llama70b_gqa_bf16 partition_tokens={ptok}")
     ref = oracle_decode(w)
     got, _, _ = gpu_step(w, ptok)
-    check(w, got, ref, f"config 3 p{ptok}")
+    check(w, got, ref, f"llama70b_gqa_bf16 p{ptok}")
 
 
 @pytest.mark.parametrize("i", [4, 5])
