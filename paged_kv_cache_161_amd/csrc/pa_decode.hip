@@ -473,7 +473,7 @@ __global__ __launch_bounds__(NW *kWave, min_waves_per_simd(DT, D, PF)) void pa_d
     extern __shared__ float smem[];
     float *s_m = smem;                              // [NW][16]
     float *s_l = smem + NW * 16;                    // [NW][16]
-    int *s_bad = reinterpret_cast<int *>(smem + NW * 32);   // [NW], then a flag at [8]
+    int *s_bad = reinterpret_cast<int *>(smem + NW * 32);   // [NW] (16 ints reserved)
     float *s_o = smem + NW * 32 + 16;               // [NW][GS][DP]
 
     const int p = blockIdx.x;
