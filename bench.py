@@ -239,6 +239,74 @@ def prefill_flops(w):
     return 4 * w.head_dim * w.num_q_heads * w.attended_keys()
 
 
+def time_sub_batch(w, d, pools, k_rows, v_rows, idx, sc, n_launch, warmup, dev):
+    """One sub-batch of a decode workload (sequences idx) stepped on its own through the
+    fused decode_append: µs per launch over n_launch back-to-back launches (HIP events
+    on the launching stream, cycling over the layers' pools), its unique-KV rate, and
+    the step as one graph of the layers' steps, replayed."""
+    from paged_kv_cache_161_amd import binding as PA
+    sel = torch.tensor(idx, dtype=torch.long, device=dev)
+    q = d["q"].index_select(0, sel).contiguous()
+    bt = d["block_tables"].index_select(0, sel).contiguous()
+    cl = d["context_lens"].index_select(0, sel).contiguous()
+    kr = k_rows.index_select(0, sel).contiguous()
+    vr = v_rows.index_select(0, sel).contiguous()
+    ctx = w.context_lens[idx]
+    max_ctx = int(ctx.max())
+    ptok = PA.plan_partition_tokens(w.num_q_heads, w.num_kv_heads, w.head_dim, ctx)
+    ws = torch.empty(max(PA.workspace_bytes(len(idx), w.num_q_heads, w.num_kv_heads,
+                                            w.head_dim, max_ctx, ptok), 1),
+                     dtype=torch.uint8, device=dev)
+    out = torch.empty_like(q)
+    layers = len(pools)
+
+    def step(i):
+        kp, vp = pools[i % layers]
+        PA.decode_append(q, kp, vp, kr, vr, bt, cl, float(w.scale), max_ctx, ptok, out=out,
+                         workspace=ws, **sc)
+
+    for i in range(warmup):
+        step(i)
+    stream = torch.cuda.current_stream(dev)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(n_launch):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    dur = e0.elapsed_time(e1) * 1e-3 / n_launch
+    # distinct physical K/V rows of the sub-batch (shared prefix blocks once)
+    seen = {}
+    for b in idx:
+        n = int(w.context_lens[b])
+        for lb in range((n + 15) // 16):
+            p = int(w.block_tables[b, lb])
+            seen[p] = max(seen.get(p, 0), min(16, n - lb * 16))
+    uniq = sum(seen.values()) * w.num_kv_heads * 2 * w.head_dim * W_ELEM[w.kv_dtype]
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream(dev)
+    cap.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.graph(g, stream=cap):
+        for i in range(layers):
+            step(i)
+    torch.cuda.current_stream(dev).wait_stream(cap)
+    for _ in range(max(1, warmup // layers)):
+        g.replay()
+    reps = max(1, n_launch // layers)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        g.replay()
+    torch.cuda.synchronize()
+    graph4_us = (time.perf_counter() - t0) * 1e6 / (reps * layers)
+    return {"num_seqs": len(idx), "partition_tokens": ptok,
+            "launch_us_mean": round(dur * 1e6, 2),
+            "unique_kv_bytes": int(uniq), "achieved_GBps": round(uniq / dur / 1e9, 1),
+            "graph4_us_per_step": round(graph4_us, 2)}
+
+
 def prefill_recorded_traffic(workload):
     """HBM bytes per prefill launch from committed rocprofv3 counter passes, or None
     unless they were taken on this exact kernel source."""
@@ -542,6 +610,21 @@ def main():
     graph4_ms = (time.perf_counter() - t_start) * 1e3 / (reps * LAYERS)
     log(f"[bench] {reps} replays of one {LAYERS}-layer graph: {graph4_ms * 1e3:.1f} us per layer step")
 
+    # a batch that shares a prefix (beams) is also timed as its two sub-batches, each
+    # on its own: the long sequences, and the beams, whose step is µs-scale, eagerly
+    # and as one graph of the four layers' steps
+    sub_batches = None
+    if w.spec.prefix_groups:
+        beams = sorted({b for grp, _ in w.spec.prefix_groups for b in grp})
+        sub_batches = {}
+        for name, idx in (("long", [b for b in range(w.num_seqs) if b not in beams]),
+                          ("beams", beams)):
+            if not idx:
+                continue
+            sub_batches[name] = time_sub_batch(w, d, pools, k_rows, v_rows, idx, sc, n_l,
+                                               args.warmup, dev)
+            log(f"[bench] sub-batch {name}: {sub_batches[name]}")
+
     # parity on the timed inputs (sampled rows against the oracle)
     parity = None
     try:
@@ -599,6 +682,7 @@ def main():
         "graph_tokens_per_s": round(w.num_seqs / (graph_ms * 1e-3), 1),
         "graph4_ms_per_step": round(graph4_ms, 5),
         "unique_kv_bytes_per_step": uniq_bytes,
+        "sub_batches": sub_batches,
         "roofline": {"bound": "hbm", "kernel": "pa_decode_partition with the fused append "
                                                "(+ pa_decode_reduce when a sequence spans "
                                                "several partitions)",
