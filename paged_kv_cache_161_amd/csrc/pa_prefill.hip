@@ -347,8 +347,20 @@ __global__ __launch_bounds__(NW *kWave, C * D <= 256 ? 2 : 1) void pa_prefill_ke
     // tiles, and where the two steps' fragments fit the register file (d <= 128).
     if constexpr (IDLE && D <= 128) {
         if (n_here * a.group <= 16) {
-            using KRaw = typename std::conditional<DT == DT_FP8, u32x2, u32x4>::type;
-            using VRaw = typename std::conditional<DT == DT_FP8, uint32_t, u32x2>::type;
+            // Key order inside a 32-key step: QK product t's output row 4 gr + j is
+            // key 16 (gr / 2) + 8 (gr % 2) + 4 t + j, so lane group g of the weights
+            // holds keys 16 (g / 2) + 8 (g % 2) + 0 .. 7: eight consecutive tokens of
+            // one block.  The V^T operand is then one piece per row block (16 bytes,
+            // 8 for fp8) and K one 16-byte piece per product (fp8: per two products,
+            // whose e ranges are interleaved so a lane's 16 codes are contiguous, q
+            // following the same e order): 16 load instructions per step (fp8: 12)
+            // instead of 24, which sets how fast one CU streams a long row.
+            constexpr int KL = DT == DT_FP8 ? NKC / 2 : NKC;      // K pieces per product row
+            using VRaw = typename std::conditional<DT == DT_FP8, u32x2, u32x4>::type;
+            struct Frag {
+                u32x4 k[KL][2];
+                VRaw v[NDB];
+            };
             const float sl = a.scale_log2;
             const float grow_thr = fminf(kRescaleSlack / sl, 3.0e38f);
             const u32x4 ones = {one_pair<AT>(), one_pair<AT>(), one_pair<AT>(), one_pair<AT>()};
@@ -358,34 +370,54 @@ __global__ __launch_bounds__(NW *kWave, C * D <= 256 ? 2 : 1) void pa_prefill_ke
             const bool ok = lp < n_here;
             const int orow1 = ok ? (q0 + p_lo + lp) * a.num_q_heads + kvh * a.group + hh : -1;
             const int pos1 = ok ? first + lp : INT_MIN / 2;
+            // q fragment of product kc: e = 32 kc + 8 g .. +7 (16-bit pools), or
+            // 64 (kc / 2) + 16 g + 8 (kc % 2) .. +7 (fp8 pools)
             u32x4 q1[NKC];
             const uint16_t *qrow = qp + (size_t)(ok ? orow1 : 0) * D;
 #pragma unroll
-            for (int kc = 0; kc < NKC; ++kc)
-                q1[kc] = ok ? *reinterpret_cast<const u32x4 *>(qrow + 32 * kc + 8 * g)
-                            : u32x4{0u, 0u, 0u, 0u};
+            for (int kc = 0; kc < NKC; ++kc) {
+                const int e0 = DT == DT_FP8 ? 64 * (kc / 2) + 16 * g + 8 * (kc % 2) : 32 * kc + 8 * g;
+                q1[kc] = ok ? *reinterpret_cast<const u32x4 *>(qrow + e0) : u32x4{0u, 0u, 0u, 0u};
+            }
             const int s_lo = (int)(((int64_t)nsteps * wave) / NW);
             const int s_hi = (int)(((int64_t)nsteps * (wave + 1)) / NW);
+            // this lane's K row (product row r16) and V^T piece, inside a step
+            const int k_blk = r16 >> 3;                                    // 0 or 1
+            const int k_tok0 = 8 * ((r16 >> 2) & 1) + (r16 & 3);          // + 4 t
+            const int v_blk = g >> 1;
+            const int v_tok0 = 8 * (g & 1);
 
-            // Step s's fragments, in the operand order of the staged path: K rows of
-            // token r16, e = 32 kc + 8 g .. +7; V^T rows e = 16 n + r16, tokens
-            // 4 g .. 4 g + 3 of each of the step's two blocks.
-            auto load_step = [&](int s, KRaw (&kr)[NKC][2], VRaw (&vr)[NDB][2]) {
-                int raw[2], ph[2];
-                table(s, raw);
-                resolve(s, raw, ph);
-#pragma unroll
-                for (int tl = 0; tl < 2; ++tl) {
-                    const size_t blk = (uint64_t)(uint32_t)ph[tl] * blk_stride32;
-                    const Elem *kp = kbase + blk + r16 * D + 8 * g;
-                    const Elem *vp = vbase + blk + r16 * kBlock + 4 * g;
-#pragma unroll
-                    for (int kc = 0; kc < NKC; ++kc)
-                        kr[kc][tl] = *reinterpret_cast<const KRaw *>(kp + 32 * kc);
-#pragma unroll
-                    for (int n = 0; n < NDB; ++n)
-                        vr[n][tl] = *reinterpret_cast<const VRaw *>(vp + 16 * kBlock * n);
+            // The wave's block ids, one per lane, for logical blocks ids_base ..
+            // ids_base + 63 (32 steps), read with one vector load and picked out with
+            // readlane.  Scalar loads of the table would not do here: using any scalar
+            // load's result waits for every scalar load in flight, so a step could not
+            // start before the table read issued for a later one had come back.
+            const int32_t *trow_v = a.block_tables + (size_t)b * a.max_blocks;
+            int ids_base = 2 * s_lo;
+            int ids = trow_v[min(ids_base + lane, a.max_blocks - 1)];
+            auto load_step = [&](int s, Frag &fr) {
+                if (2 * s + 1 >= ids_base + kWave) {              // wave-uniform, rare
+                    ids_base = 2 * s;
+                    ids = trow_v[min(ids_base + lane, a.max_blocks - 1)];
                 }
+                int raw[2], ph[2];
+                raw[0] = __builtin_amdgcn_readlane(ids, 2 * s - ids_base);
+                raw[1] = __builtin_amdgcn_readlane(ids, 2 * s + 1 - ids_base);
+                resolve(s, raw, ph);
+                const size_t kblk = (uint64_t)(uint32_t)(k_blk ? ph[1] : ph[0]) * blk_stride32;
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const Elem *kp = kbase + kblk + (size_t)(k_tok0 + 4 * t) * D;
+#pragma unroll
+                    for (int i = 0; i < KL; ++i)
+                        fr.k[i][t] = *reinterpret_cast<const u32x4 *>(
+                            kp + (DT == DT_FP8 ? 64 * i + 16 * g : 32 * i + 8 * g));
+                }
+                const size_t vblk = (uint64_t)(uint32_t)(v_blk ? ph[1] : ph[0]) * blk_stride32;
+                const Elem *vp = vbase + vblk + r16 * kBlock + v_tok0;
+#pragma unroll
+                for (int n = 0; n < NDB; ++n)
+                    fr.v[n] = *reinterpret_cast<const VRaw *>(vp + 16 * kBlock * n);
             };
 
             f32x4 o1[NDB];
@@ -395,29 +427,32 @@ __global__ __launch_bounds__(NW *kWave, C * D <= 256 ? 2 : 1) void pa_prefill_ke
             f32x4 l1 = {0.f, 0.f, 0.f, 0.f};
             float m1 = -INFINITY, mneg1 = 0.f;
 
-            auto step = [&](int s, const KRaw (&kr)[NKC][2], const VRaw (&vr)[NDB][2]) {
+            auto step = [&](int s, const Frag &fr) {
                 f32x4 sc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-                for (int kc = 0; kc < NKC; ++kc)
+                for (int i = 0; i < KL; ++i)
 #pragma unroll
-                    for (int tl = 0; tl < 2; ++tl) {
-                        u32x4 kf;
+                    for (int t = 0; t < 2; ++t) {
+                        const u32x4 w = fr.k[i][t];
                         if constexpr (DT == DT_FP8) {
-                            const u32x2 w = kr[kc][tl];
-                            kf = u32x4{fp8x2_to_16<AT, false>(w[0]), fp8x2_to_16<AT, true>(w[0]),
-                                       fp8x2_to_16<AT, false>(w[1]), fp8x2_to_16<AT, true>(w[1])};
+                            const u32x4 lo = {fp8x2_to_16<AT, false>(w[0]), fp8x2_to_16<AT, true>(w[0]),
+                                              fp8x2_to_16<AT, false>(w[1]), fp8x2_to_16<AT, true>(w[1])};
+                            const u32x4 hi = {fp8x2_to_16<AT, false>(w[2]), fp8x2_to_16<AT, true>(w[2]),
+                                              fp8x2_to_16<AT, false>(w[3]), fp8x2_to_16<AT, true>(w[3])};
+                            sc[t] = mma32<AT>(lo, q1[2 * i], sc[t]);
+                            sc[t] = mma32<AT>(hi, q1[2 * i + 1], sc[t]);
                         } else {
-                            kf = kr[kc][tl];
+                            sc[t] = mma32<AT>(w, q1[i], sc[t]);
                         }
-                        sc[tl] = mma32<AT>(kf, q1[kc], sc[tl]);
                     }
+                // score (t, j) of lane group g is key 32 s + 16 (g / 2) + 8 (g % 2) + 4 t + j
                 if (32 * s + 31 > first) {
 #pragma unroll
-                    for (int tl = 0; tl < 2; ++tl)
+                    for (int t = 0; t < 2; ++t)
 #pragma unroll
                         for (int j = 0; j < 4; ++j)
-                            sc[tl][j] = (32 * s + 16 * tl + 4 * g + j <= pos1) ? sc[tl][j]
-                                                                               : -INFINITY;
+                            sc[t][j] = (32 * s + 16 * v_blk + v_tok0 + 4 * t + j <= pos1)
+                                           ? sc[t][j] : -INFINITY;
                 }
                 const float lmx = max8(sc);
                 if (__any(lmx - m1 > grow_thr)) {
@@ -436,39 +471,44 @@ __global__ __launch_bounds__(NW *kWave, C * D <= 256 ? 2 : 1) void pa_prefill_ke
                     p0[j] = exp2_fast(fmaf(sc[0][j], sl, mneg1));
                     p1[j] = exp2_fast(fmaf(sc[1][j], sl, mneg1));
                 }
-                const u32x4 pb = pack8<AT>(p0, p1);
+                const u32x4 pb = pack8<AT>(p0, p1);       // weights of keys v_tok0 + 0 .. 7
                 // V^T tokens past the context, and whole blocks past key_end (padding
-                // entries read as block 0), may hold anything: zero them
-                uint32_t keep[2][2];
-#pragma unroll
-                for (int tl = 0; tl < 2; ++tl) {
-                    const int blk0 = (2 * s + tl) * kBlock;
+                // entries read as block 0), may hold anything: zero them.  Only a step
+                // that reaches past key_end (<= ctx) has such tokens.
+                VRaw keep;
+                if constexpr (DT == DT_FP8)
+                    keep = VRaw{~0u, ~0u};
+                else
+                    keep = VRaw{~0u, ~0u, ~0u, ~0u};
+                if (32 * s + 32 > key_end) {                            // wave-uniform
+                    const int blk0 = (2 * s + v_blk) * kBlock;
                     const int valid = blk0 >= key_end ? 0 : ctx - blk0;
+                    if constexpr (DT == DT_FP8) {
 #pragma unroll
-                    for (int w = 0; w < 2; ++w) {
-                        if constexpr (DT == DT_FP8) {
+                        for (int w = 0; w < 2; ++w) {
                             uint32_t m = 0;
 #pragma unroll
-                            for (int j = 0; j < 2; ++j)
-                                m |= (4 * g + 2 * w + j < valid) ? (0xFFu << (8 * (2 * w + j))) : 0u;
-                            keep[tl][w] = m;
-                        } else {
-                            keep[tl][w] = (4 * g + 2 * w < valid ? 0x0000FFFFu : 0u) |
-                                          (4 * g + 2 * w + 1 < valid ? 0xFFFF0000u : 0u);
+                            for (int j = 0; j < 4; ++j)
+                                m |= (v_tok0 + 4 * w + j < valid) ? (0xFFu << (8 * j)) : 0u;
+                            keep[w] = m;
                         }
+                    } else {
+#pragma unroll
+                        for (int w = 0; w < 4; ++w)
+                            keep[w] = (v_tok0 + 2 * w < valid ? 0x0000FFFFu : 0u) |
+                                      (v_tok0 + 2 * w + 1 < valid ? 0xFFFF0000u : 0u);
                     }
                 }
 #pragma unroll
                 for (int n = 0; n < NDB; ++n) {
                     u32x4 vf;
                     if constexpr (DT == DT_FP8) {
-                        const uint32_t w0 = vr[n][0] & (keep[0][0] | keep[0][1]);
-                        const uint32_t w1 = vr[n][1] & (keep[1][0] | keep[1][1]);
+                        const uint32_t w0 = fr.v[n][0] & keep[0];
+                        const uint32_t w1 = fr.v[n][1] & keep[1];
                         vf = u32x4{fp8x2_to_16<AT, false>(w0), fp8x2_to_16<AT, true>(w0),
                                    fp8x2_to_16<AT, false>(w1), fp8x2_to_16<AT, true>(w1)};
                     } else {
-                        vf = u32x4{vr[n][0][0] & keep[0][0], vr[n][0][1] & keep[0][1],
-                                   vr[n][1][0] & keep[1][0], vr[n][1][1] & keep[1][1]};
+                        vf = fr.v[n] & keep;
                     }
                     o1[n] = mma32<AT>(vf, pb, o1[n]);
                 }
@@ -479,15 +519,14 @@ __global__ __launch_bounds__(NW *kWave, C * D <= 256 ? 2 : 1) void pa_prefill_ke
             // a step's products; the last step's loads are repeated past the end so
             // every pass issues the same loads
             if (s_lo < s_hi) {
-                KRaw ka[NKC][2], kb[NKC][2];
-                VRaw va[NDB][2], vb[NDB][2];
-                load_step(s_lo, ka, va);
+                Frag fa, fb;
+                load_step(s_lo, fa);
                 for (int s = s_lo; s < s_hi; s += 2) {
-                    load_step(min(s + 1, s_hi - 1), kb, vb);
-                    step(s, ka, va);
-                    load_step(min(s + 2, s_hi - 1), ka, va);
+                    load_step(min(s + 1, s_hi - 1), fb);
+                    step(s, fa);
+                    load_step(min(s + 2, s_hi - 1), fa);
                     if (s + 1 < s_hi)
-                        step(s + 1, kb, vb);
+                        step(s + 1, fb);
                 }
             }
 
