@@ -78,6 +78,13 @@ SMALL = [
            kv_dtype="fp8", k_scale=0.25, v_scale=0.0625, query_lens=[1, 2]),
     W.Spec("pf_decode_rows_f16_mha_d64", "f16", 16, 16, 64, [40, 900, 500], seed=47,
            spare_blocks=1, query_lens=[1, 16, 3]),
+    # chunks whose last tile holds one or two positions (32-position tiles at G = 8):
+    # split tiles in the middle of a context, with the causal limit inside the step
+    W.Spec("pf_chunk_tails_bf16", "bf16", 64, 8, 128, [100, 700, 66], seed=51, spare_blocks=1,
+           query_lens=[33, 65, 34]),
+    W.Spec("pf_chunk_tails_fp8_bf16", "bf16", 64, 8, 128, [100, 700, 66], seed=52,
+           spare_blocks=1, kv_dtype="fp8", k_scale=0.0117, v_scale=0.0093,
+           query_lens=[33, 65, 34]),
     # more sequences than the ranked map takes (plain map, launch order by index), and a
     # single sequence (nothing to rank)
     W.Spec("pf_300_seqs_bf16", "bf16", 8, 2, 128, _CTX300, seed=49, spare_blocks=1,
