@@ -98,9 +98,30 @@ struct Tile16 {
 #pragma unroll
         for (int i = 0; i < NQK; ++i)
             k[i] = *reinterpret_cast<const u32x4 *>(kt + r * D + 32 * i + 8 * g);
+        // V^T as 16-byte half rows (half as many load instructions as 8-byte pieces,
+        // which sets how fast one CU streams): lane (r, g) loads tokens 8 (g / 2) .. +7
+        // of row 16 (2 i + g % 2) + r into v[2 i] (its first 4 tokens) and v[2 i + 1];
+        // finish() swaps halves between lanes g and g ^ 1, once the loads have landed
+        // (swapping here would make a prefetched tile wait for its own loads).
 #pragma unroll
-        for (int n = 0; n < NPV; ++n)
-            v[n] = *reinterpret_cast<const u32x2 *>(vt + (16 * n + r) * kBlock + 4 * g);
+        for (int i = 0; i < NPV / 2; ++i) {
+            const u32x4 w = *reinterpret_cast<const u32x4 *>(
+                vt + (16 * (2 * i + (g & 1)) + r) * kBlock + 8 * (g >> 1));
+            v[2 * i] = u32x2{w[0], w[1]};
+            v[2 * i + 1] = u32x2{w[2], w[3]};
+        }
+    }
+
+    // After the loads have landed: v[n] = V^T[16 n + r][4 g .. 4 g + 3].
+    __device__ __forceinline__ void finish()
+    {
+#pragma unroll
+        for (int i = 0; i < NPV / 2; ++i) {
+            auto a = __builtin_amdgcn_permlane16_swap(v[2 * i][0], v[2 * i + 1][0], false, false);
+            auto b = __builtin_amdgcn_permlane16_swap(v[2 * i][1], v[2 * i + 1][1], false, false);
+            v[2 * i] = u32x2{a[0], b[0]};
+            v[2 * i + 1] = u32x2{a[1], b[1]};
+        }
     }
 
     // Write the patched block back: K row `off` and every V^T piece (whole rows, so the
@@ -150,6 +171,7 @@ struct Q16 {
 // fp32 K/V.  QK uses 16x16x4 MFMAs: lane (r, g) covers e in [g*D/4, (g+1)*D/4).
 template <int D>
 struct Tile32 {
+    __device__ __forceinline__ void finish() {}
     static constexpr int NC = D / 16;    // float4 chunks
     f32x4 k[NC];                         // K[r][(D/4)g + 4c .. +3]
     f32x4 v[NC];                         // V^T[16n + r][4g .. 4g+3]
@@ -242,6 +264,8 @@ struct Tile8 {
             v[4 * i + 3] = s13[1];
         }
     }
+
+    __device__ __forceinline__ void finish() {}
 
     __device__ __forceinline__ void store_row(uint8_t *kt, uint8_t *vt, int off, int r, int g) const
     {
@@ -594,6 +618,7 @@ __global__ __launch_bounds__(NW *kWave, min_waves_per_simd(DT, D, PF)) void pa_d
     // PATCH: this call may hold the block that receives the new row (fused append).
     auto process = [&](auto patch_tag, typename F::Tile &t, int i) {
         constexpr bool PATCH = decltype(patch_tag)::value;
+        t.finish();
         const int lb = lb_begin + wave + i * NW;
         const int valid = ctx - lb * kBlock;            // >= 1
         if constexpr (PATCH) {
