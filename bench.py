@@ -57,6 +57,9 @@ def parse():
                          "prefill; 6 is the decode shape with an FP8 E4M3 KV cache)")
     ap.add_argument("--partition-tokens", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sub-batches", action="store_true",
+                    help="skip the sub-batch timings of a shared-prefix batch (profiler passes "
+                         "then see only the whole batch's launches)")
     ap.add_argument("--roofline-launches", type=int, default=100)
     ap.add_argument("--op", choices=["step", "copy_blocks", "prefill"], default="step",
                     help="step: the decode step (default); copy_blocks: the copy-on-write "
@@ -614,7 +617,7 @@ def main():
     # on its own: the long sequences, and the beams, whose step is µs-scale, eagerly
     # and as one graph of the four layers' steps
     sub_batches = None
-    if w.spec.prefix_groups:
+    if w.spec.prefix_groups and not args.no_sub_batches:
         beams = sorted({b for grp, _ in w.spec.prefix_groups for b in grp})
         sub_batches = {}
         for name, idx in (("long", [b for b in range(w.num_seqs) if b not in beams]),
