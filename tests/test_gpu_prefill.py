@@ -78,6 +78,12 @@ SMALL = [
            kv_dtype="fp8", k_scale=0.25, v_scale=0.0625, query_lens=[1, 2]),
     W.Spec("pf_decode_rows_f16_mha_d64", "f16", 16, 16, 64, [40, 900, 500], seed=47,
            spare_blocks=1, query_lens=[1, 16, 3]),
+    # decode rows longer than 8,192 tokens: a wave walks more than 32 steps and reloads
+    # its block ids (one 64-entry vector load per 32 steps)
+    W.Spec("pf_long_decode_rows_bf16", "bf16", 8, 1, 128, [20000, 9000, 8193], seed=53,
+           spare_blocks=1, query_lens=[1, 1, 1]),
+    W.Spec("pf_long_decode_rows_fp8_f16", "f16", 8, 1, 64, [20000, 8200], seed=54,
+           spare_blocks=1, kv_dtype="fp8", k_scale=0.25, v_scale=0.0625, query_lens=[1, 2]),
     # chunks whose last tile holds one or two positions (32-position tiles at G = 8):
     # split tiles in the middle of a context, with the causal limit inside the step
     W.Spec("pf_chunk_tails_bf16", "bf16", 64, 8, 128, [100, 700, 66], seed=51, spare_blocks=1,
