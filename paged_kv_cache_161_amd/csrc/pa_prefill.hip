@@ -27,7 +27,12 @@
 //   16-bit weights the PV product used, lands already reduced over the wave's four
 //   row groups, and keeps that work off the vector ALU, which the exponentials load.
 //   Workgroup ids go round-robin over the 8 XCDs; the id -> (pair, tile) map keeps all
-//   query tiles of one (sequence, kv-head) on one XCD, so they share its L2.
+//   query tiles of one (sequence, kv-head) on one XCD, so they share its L2.  Batches
+//   of up to 256 sequences are taken in order of estimated tile cost (longest first),
+//   and where tiles can be partial the grid enumerates only the tiles that exist.
+//   A tile whose rows fit one column block (a decode row, a chunk's last position or
+//   two) is split over the waves by keys instead of rows: each wave streams its share
+//   straight into registers and the partial (m, l, O) sets are merged in LDS.
 #include <limits.h>
 #include <math.h>
 
