@@ -307,3 +307,45 @@ def test_generous_host_bounds_change_nothing():
         torch.cuda.synchronize()
         outs.append(U.int_view(out).clone())
     assert torch.equal(outs[0], outs[1])
+
+
+def _random_spec(i):
+    """A seeded random small batch: kv-heads, group, head size and pool type drawn at
+    random; sequences mixing decode rows, short chunks (split or idle-wave tiles) and
+    chunks of several tiles, some with empty chunks."""
+    r = np.random.Generator(np.random.PCG64(7000 + i))
+    hkv = int(r.choice([1, 2, 3, 4, 8]))
+    group = int(r.choice([1, 2, 4, 8, 16]))
+    d = int(r.choice([64, 128]))
+    kind = ["bf16", "f16", "fp8_bf16", "fp8_f16"][int(r.integers(0, 4))]
+    act = "bf16" if kind in ("bf16", "fp8_bf16") else "f16"
+    extra = dict(kv_dtype="fp8", k_scale=0.0117, v_scale=0.0093) if kind.startswith("fp8") else {}
+    b = int(r.integers(1, 24))
+    ctx, ql = [], []
+    for _ in range(b):
+        c = int(r.integers(1, 320))
+        u = r.random()
+        q = 1 if u < 0.4 else (int(r.integers(2, 6)) if u < 0.6 else
+                               (0 if u < 0.65 else int(r.integers(6, c + 1)) if c >= 6 else c))
+        ctx.append(c)
+        ql.append(min(q, c))
+    return W.Spec(f"pf_random_{i}", act, hkv * group, hkv, d, ctx, seed=7100 + i,
+                  spare_blocks=1, query_lens=ql, **extra)
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_prefill_random_batches(i):
+    """Every output row of a seeded random batch against the oracle (rows pre-filled
+    with NaN, so a tile the grid misses fails)."""
+    spec = _random_spec(i)
+    say(f"[prefill random {i}] hq {spec.num_q_heads} hkv {spec.num_kv_heads} d "
+        f"{spec.head_dim} {spec.dtype}/{spec.kv_dtype or spec.dtype} B {len(spec.context_lens)}")
+    w = W.build(spec)
+    kpo, vpo, bt = oracle_pools(w)
+    ref, _ = O.prefill_paged(w.q, kpo, vpo, w.kv_dtype, w.query_start, bt, w.context_lens,
+                             w.scale, q_dtype=w.dtype, k_scale=w.k_scale, v_scale=w.v_scale)
+    got, _, _ = gpu_prefill(w)
+    ok, mx, mean = U.tolerance_ok(got, ref, w.dtype)
+    say(f"  rows {got.shape[0]}: max {mx:.3e} mean {mean:.3e}")
+    assert np.isfinite(got).all()
+    assert ok, (mx, mean)
