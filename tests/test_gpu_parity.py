@@ -349,3 +349,34 @@ def test_generous_host_bounds_change_nothing(fused):
         results.append((U.int_view(out).clone(), U.int_view(kp).clone(), U.int_view(vp).clone()))
     for a, b in zip(results[0], results[1]):
         assert torch.equal(a, b)
+
+
+def _random_decode_spec(i):
+    """A seeded random decode batch: kv-heads, group (up to 32: two head chunks), head
+    size and pool type drawn at random; ragged contexts with empty sequences."""
+    r = np.random.Generator(np.random.PCG64(8000 + i))
+    hkv = int(r.choice([1, 2, 3, 4, 8]))
+    group = int(r.choice([1, 2, 4, 5, 8, 16, 32]))
+    kind = ["bf16", "f16", "f32", "fp8_bf16", "fp8_f16"][int(r.integers(0, 5))]
+    d = int(r.choice([64, 128])) if kind == "f32" else int(r.choice([64, 128, 256]))
+    act = "bf16" if kind in ("bf16", "fp8_bf16") else ("f32" if kind == "f32" else "f16")
+    extra = dict(kv_dtype="fp8", k_scale=0.0117, v_scale=0.0093) if kind.startswith("fp8") else {}
+    b = int(r.integers(1, 20))
+    ctx = [int(x) if r.random() > 0.1 else 0 for x in r.integers(1, 1500, b)]
+    return W.Spec(f"dec_random_{i}", act, hkv * group, hkv, d, ctx, seed=8100 + i,
+                  spare_blocks=2, **extra)
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_decode_random_batches(i):
+    """A seeded random batch against the oracle, at the planned partition length and
+    at a forced short one (split and reduce)."""
+    spec = _random_decode_spec(i)
+    say(f"[decode random {i}] hq {spec.num_q_heads} hkv {spec.num_kv_heads} d "
+        f"{spec.head_dim} {spec.dtype}/{spec.kv_dtype or spec.dtype} B {len(spec.context_lens)}")
+    w = W.build(spec)
+    ref = oracle_decode(w)
+    plan = PA.plan_partition_tokens(w.num_q_heads, w.num_kv_heads, w.head_dim, w.context_lens)
+    for ptok in (plan, 64):
+        got, _, _ = gpu_step(w, ptok)
+        check(w, got, ref, f"dec_random_{i} p{ptok}")
