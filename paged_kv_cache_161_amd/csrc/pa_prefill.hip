@@ -145,7 +145,7 @@ __device__ __forceinline__ u32x4 keep_tokens8(u32x4 v, int t0, int valid)
     return v;
 }
 
-template <int DT, int AT, int D, int NW, int C, bool IDLE>
+template <int DT, int AT, int D, int NW, int C, bool IDLE, bool SMALLQ>
 __global__ __launch_bounds__(NW *kWave, C * D <= 256 ? 2 : 1) void pa_prefill_kernel(PrefillArgs a)
 {
     using Elem = typename std::conditional<DT == DT_FP8, uint8_t, uint16_t>::type;
@@ -196,7 +196,7 @@ __global__ __launch_bounds__(NW *kWave, C * D <= 256 ? 2 : 1) void pa_prefill_ke
             const bool valid = q0t >= 0 && qlt >= 0 && qlt <= a.max_query_len &&
                                q0t <= a.num_tokens - qlt;
             int cost = valid && qlt > 0 && cx > 0 ? cx : 0;
-            if (IDLE && D <= 128 && qlt * a.group <= 16)
+            if (IDLE && D <= 128 && qlt * a.group <= (SMALLQ ? 32 : 16))
                 cost /= 2;
             s_cost[tid0] = cost;
             s_ntl[tid0] = valid ? (qlt + a.q_tile - 1) / a.q_tile : 0;
@@ -342,16 +342,17 @@ __global__ __launch_bounds__(NW *kWave, C * D <= 256 ? 2 : 1) void pa_prefill_ke
         }
     };
 
-    // ---- a tile whose rows all fit one MFMA column block (a decode row, a chunk's
-    // last position or two): with the usual split, one wave would own every row and
-    // the other waves would only stage its keys.  Instead every wave takes those same
-    // rows and a contiguous 1/NW of the key steps, loads its K and V fragments straight
-    // from the pool into registers (no LDS staging, two steps in flight), and the NW
-    // partial (max, sum, O) sets are merged through LDS at the end with the same
-    // rescaling rule as the online softmax.  Only in the launch that allows partial
-    // tiles, and where the two steps' fragments fit the register file (d <= 128).
+    // ---- a tile whose rows all fit one or two MFMA column blocks (a decode row, a
+    // chunk's last few positions): with the usual split, one wave would own every row
+    // and the other waves would only stage its keys.  Instead every wave takes those
+    // same rows and a contiguous 1/NW of the key steps, loads its K and V fragments
+    // straight from the pool into registers (no LDS staging, two steps in flight),
+    // and the NW partial (max, sum, O) sets are merged through LDS at the end with the
+    // same rescaling rule as the online softmax.  Only in the launch that allows
+    // partial tiles, at d <= 128.
     if constexpr (IDLE && D <= 128) {
-        if (n_here * a.group <= 16) {
+        const int tile_rows = n_here * a.group;
+        if (tile_rows <= 16 || (SMALLQ && tile_rows <= 32)) {
             // Key order inside a 32-key step: QK product t's output row 4 gr + j is
             // key 16 (gr / 2) + 8 (gr % 2) + 4 t + j, so lane group g of the weights
             // holds keys 16 (g / 2) + 8 (g % 2) + 0 .. 7: eight consecutive tokens of
@@ -369,21 +370,6 @@ __global__ __launch_bounds__(NW *kWave, C * D <= 256 ? 2 : 1) void pa_prefill_ke
             const float sl = a.scale_log2;
             const float grow_thr = fminf(kRescaleSlack / sl, 3.0e38f);
             const u32x4 ones = {one_pair<AT>(), one_pair<AT>(), one_pair<AT>(), one_pair<AT>()};
-            // row r16 of the tile (the first column block's layout), for every wave
-            const int lp = r16 / a.group;
-            const int hh = r16 - lp * a.group;
-            const bool ok = lp < n_here;
-            const int orow1 = ok ? (q0 + p_lo + lp) * a.num_q_heads + kvh * a.group + hh : -1;
-            const int pos1 = ok ? first + lp : INT_MIN / 2;
-            // q fragment of product kc: e = 32 kc + 8 g .. +7 (16-bit pools), or
-            // 64 (kc / 2) + 16 g + 8 (kc % 2) .. +7 (fp8 pools)
-            u32x4 q1[NKC];
-            const uint16_t *qrow = qp + (size_t)(ok ? orow1 : 0) * D;
-#pragma unroll
-            for (int kc = 0; kc < NKC; ++kc) {
-                const int e0 = DT == DT_FP8 ? 64 * (kc / 2) + 16 * g + 8 * (kc % 2) : 32 * kc + 8 * g;
-                q1[kc] = ok ? *reinterpret_cast<const u32x4 *>(qrow + e0) : u32x4{0u, 0u, 0u, 0u};
-            }
             const int s_lo = (int)(((int64_t)nsteps * wave) / NW);
             const int s_hi = (int)(((int64_t)nsteps * (wave + 1)) / NW);
             // this lane's K row (product row r16) and V^T piece, inside a step
@@ -398,8 +384,7 @@ __global__ __launch_bounds__(NW *kWave, C * D <= 256 ? 2 : 1) void pa_prefill_ke
             // load's result waits for every scalar load in flight, so a step could not
             // start before the table read issued for a later one had come back.
             const int32_t *trow_v = a.block_tables + (size_t)b * a.max_blocks;
-            int ids_base = 2 * s_lo;
-            int ids = trow_v[min(ids_base + lane, a.max_blocks - 1)];
+            int ids_base = 0, ids = 0;                   // set at the start of each run
             auto load_step = [&](int s, Frag &fr) {
                 if (2 * s + 1 >= ids_base + kWave) {              // wave-uniform, rare
                     ids_base = 2 * s;
@@ -425,174 +410,273 @@ __global__ __launch_bounds__(NW *kWave, C * D <= 256 ? 2 : 1) void pa_prefill_ke
                     fr.v[n] = *reinterpret_cast<const VRaw *>(vp + 16 * kBlock * n);
             };
 
-            f32x4 o1[NDB];
-#pragma unroll
-            for (int n = 0; n < NDB; ++n)
-                o1[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-            f32x4 l1 = {0.f, 0.f, 0.f, 0.f};
-            float m1 = -INFINITY, mneg1 = 0.f;
+            __shared__ float s_m[2][NW][16];
+            __shared__ float s_l[2][NW][16];
 
-            auto step = [&](int s, const Frag &fr) {
-                f32x4 sc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+            // CS column blocks (tile rows row0 + 16 c + r16), PF steps in flight
+            auto run = [&](auto cs_tag, auto pf_tag, int row0) {
+                constexpr int CS = decltype(cs_tag)::value;
+                constexpr int PF = decltype(pf_tag)::value;
+                ids_base = 2 * s_lo;
+                ids = trow_v[min(ids_base + lane, a.max_blocks - 1)];
+                int orow1[CS], pos1[CS];
+                // q fragment of product kc: e = 32 kc + 8 g .. +7 (16-bit pools), or
+                // 64 (kc / 2) + 16 g + 8 (kc % 2) .. +7 (fp8 pools)
+                u32x4 q1[CS][NKC];
 #pragma unroll
-                for (int i = 0; i < KL; ++i)
+                for (int c = 0; c < CS; ++c) {
+                    const int row = row0 + 16 * c + r16;
+                    const int lp = row / a.group;
+                    const int hh = row - lp * a.group;
+                    const bool ok = lp < n_here;
+                    orow1[c] = ok ? (q0 + p_lo + lp) * a.num_q_heads + kvh * a.group + hh : -1;
+                    pos1[c] = ok ? first + lp : INT_MIN / 2;
+                    const uint16_t *qrow = qp + (size_t)(ok ? orow1[c] : 0) * D;
 #pragma unroll
-                    for (int t = 0; t < 2; ++t) {
-                        const u32x4 w = fr.k[i][t];
-                        if constexpr (DT == DT_FP8) {
-                            const u32x4 lo = {fp8x2_to_16<AT, false>(w[0]), fp8x2_to_16<AT, true>(w[0]),
-                                              fp8x2_to_16<AT, false>(w[1]), fp8x2_to_16<AT, true>(w[1])};
-                            const u32x4 hi = {fp8x2_to_16<AT, false>(w[2]), fp8x2_to_16<AT, true>(w[2]),
-                                              fp8x2_to_16<AT, false>(w[3]), fp8x2_to_16<AT, true>(w[3])};
-                            sc[t] = mma32<AT>(lo, q1[2 * i], sc[t]);
-                            sc[t] = mma32<AT>(hi, q1[2 * i + 1], sc[t]);
-                        } else {
-                            sc[t] = mma32<AT>(w, q1[i], sc[t]);
+                    for (int kc = 0; kc < NKC; ++kc) {
+                        const int e0 = DT == DT_FP8 ? 64 * (kc / 2) + 16 * g + 8 * (kc % 2)
+                                                    : 32 * kc + 8 * g;
+                        q1[c][kc] = ok ? *reinterpret_cast<const u32x4 *>(qrow + e0)
+                                       : u32x4{0u, 0u, 0u, 0u};
+                    }
+                }
+                f32x4 o1[CS][NDB], l1[CS];
+                float m1[CS], mneg1[CS];
+#pragma unroll
+                for (int c = 0; c < CS; ++c) {
+#pragma unroll
+                    for (int n = 0; n < NDB; ++n)
+                        o1[c][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    l1[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    m1[c] = -INFINITY;
+                    mneg1[c] = 0.f;
+                }
+
+                auto step = [&](int s, const Frag &fr) {
+                    f32x4 sc[CS][2];
+#pragma unroll
+                    for (int c = 0; c < CS; ++c)
+                        sc[c][0] = sc[c][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int i = 0; i < KL; ++i)
+#pragma unroll
+                        for (int t = 0; t < 2; ++t) {
+                            const u32x4 w = fr.k[i][t];
+                            if constexpr (DT == DT_FP8) {
+                                const u32x4 lo = {fp8x2_to_16<AT, false>(w[0]), fp8x2_to_16<AT, true>(w[0]),
+                                                  fp8x2_to_16<AT, false>(w[1]), fp8x2_to_16<AT, true>(w[1])};
+                                const u32x4 hi = {fp8x2_to_16<AT, false>(w[2]), fp8x2_to_16<AT, true>(w[2]),
+                                                  fp8x2_to_16<AT, false>(w[3]), fp8x2_to_16<AT, true>(w[3])};
+#pragma unroll
+                                for (int c = 0; c < CS; ++c) {
+                                    sc[c][t] = mma32<AT>(lo, q1[c][2 * i], sc[c][t]);
+                                    sc[c][t] = mma32<AT>(hi, q1[c][2 * i + 1], sc[c][t]);
+                                }
+                            } else {
+#pragma unroll
+                                for (int c = 0; c < CS; ++c)
+                                    sc[c][t] = mma32<AT>(w, q1[c][i], sc[c][t]);
+                            }
+                        }
+                    // score (t, j) of lane group g is key 32 s + 16 (g / 2) + 8 (g % 2) + 4 t + j
+                    if (32 * s + 31 > first) {
+#pragma unroll
+                        for (int c = 0; c < CS; ++c)
+#pragma unroll
+                            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                                for (int j = 0; j < 4; ++j)
+                                    sc[c][t][j] = (32 * s + 16 * v_blk + v_tok0 + 4 * t + j <= pos1[c])
+                                                      ? sc[c][t][j] : -INFINITY;
+                    }
+                    float lmx[CS];
+                    bool grow = false;
+#pragma unroll
+                    for (int c = 0; c < CS; ++c) {
+                        lmx[c] = max8(sc[c]);
+                        grow |= lmx[c] - m1[c] > grow_thr;
+                    }
+                    if (__any(grow)) {
+#pragma unroll
+                        for (int c = 0; c < CS; ++c) {
+                            const float m_new = fmaxf(m1[c], max_over_row_groups(lmx[c]));
+                            const float alpha =
+                                (m_new == -INFINITY) ? 1.f : exp2_fast((m1[c] - m_new) * sl);
+#pragma unroll
+                            for (int n = 0; n < NDB; ++n)
+                                o1[c][n] *= alpha;
+                            l1[c] *= alpha;
+                            m1[c] = m_new;
+                            mneg1[c] = (m_new == -INFINITY) ? 0.f : -m_new * sl;
                         }
                     }
-                // score (t, j) of lane group g is key 32 s + 16 (g / 2) + 8 (g % 2) + 4 t + j
-                if (32 * s + 31 > first) {
+                    u32x4 pb[CS];                       // weights of keys v_tok0 + 0 .. 7
 #pragma unroll
-                    for (int t = 0; t < 2; ++t)
+                    for (int c = 0; c < CS; ++c) {
+                        f32x4 p0, p1;
 #pragma unroll
-                        for (int j = 0; j < 4; ++j)
-                            sc[t][j] = (32 * s + 16 * v_blk + v_tok0 + 4 * t + j <= pos1)
-                                           ? sc[t][j] : -INFINITY;
-                }
-                const float lmx = max8(sc);
-                if (__any(lmx - m1 > grow_thr)) {
-                    const float m_new = fmaxf(m1, max_over_row_groups(lmx));
-                    const float alpha = (m_new == -INFINITY) ? 1.f : exp2_fast((m1 - m_new) * sl);
-#pragma unroll
-                    for (int n = 0; n < NDB; ++n)
-                        o1[n] *= alpha;
-                    l1 *= alpha;
-                    m1 = m_new;
-                    mneg1 = (m_new == -INFINITY) ? 0.f : -m_new * sl;
-                }
-                f32x4 p0, p1;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    p0[j] = exp2_fast(fmaf(sc[0][j], sl, mneg1));
-                    p1[j] = exp2_fast(fmaf(sc[1][j], sl, mneg1));
-                }
-                const u32x4 pb = pack8<AT>(p0, p1);       // weights of keys v_tok0 + 0 .. 7
-                // V^T tokens past the context, and whole blocks past key_end (padding
-                // entries read as block 0), may hold anything: zero them.  Only a step
-                // that reaches past key_end (<= ctx) has such tokens.
-                VRaw keep;
-                if constexpr (DT == DT_FP8)
-                    keep = VRaw{~0u, ~0u};
-                else
-                    keep = VRaw{~0u, ~0u, ~0u, ~0u};
-                if (32 * s + 32 > key_end) {                            // wave-uniform
-                    const int blk0 = (2 * s + v_blk) * kBlock;
-                    const int valid = blk0 >= key_end ? 0 : ctx - blk0;
-                    if constexpr (DT == DT_FP8) {
-#pragma unroll
-                        for (int w = 0; w < 2; ++w) {
-                            uint32_t m = 0;
-#pragma unroll
-                            for (int j = 0; j < 4; ++j)
-                                m |= (v_tok0 + 4 * w + j < valid) ? (0xFFu << (8 * j)) : 0u;
-                            keep[w] = m;
+                        for (int j = 0; j < 4; ++j) {
+                            p0[j] = exp2_fast(fmaf(sc[c][0][j], sl, mneg1[c]));
+                            p1[j] = exp2_fast(fmaf(sc[c][1][j], sl, mneg1[c]));
                         }
-                    } else {
-#pragma unroll
-                        for (int w = 0; w < 4; ++w)
-                            keep[w] = (v_tok0 + 2 * w < valid ? 0x0000FFFFu : 0u) |
-                                      (v_tok0 + 2 * w + 1 < valid ? 0xFFFF0000u : 0u);
+                        pb[c] = pack8<AT>(p0, p1);
                     }
-                }
-#pragma unroll
-                for (int n = 0; n < NDB; ++n) {
-                    u32x4 vf;
-                    if constexpr (DT == DT_FP8) {
-                        const uint32_t w0 = fr.v[n][0] & keep[0];
-                        const uint32_t w1 = fr.v[n][1] & keep[1];
-                        vf = u32x4{fp8x2_to_16<AT, false>(w0), fp8x2_to_16<AT, true>(w0),
-                                   fp8x2_to_16<AT, false>(w1), fp8x2_to_16<AT, true>(w1)};
-                    } else {
-                        vf = fr.v[n] & keep;
-                    }
-                    o1[n] = mma32<AT>(vf, pb, o1[n]);
-                }
-                l1 = mma32<AT>(ones, pb, l1);
-            };
-
-            // two steps in flight: the loads of the step after next are issued before
-            // a step's products; the last step's loads are repeated past the end so
-            // every pass issues the same loads
-            if (s_lo < s_hi) {
-                Frag fa, fb;
-                load_step(s_lo, fa);
-                for (int s = s_lo; s < s_hi; s += 2) {
-                    load_step(min(s + 1, s_hi - 1), fb);
-                    step(s, fa);
-                    load_step(min(s + 2, s_hi - 1), fa);
-                    if (s + 1 < s_hi)
-                        step(s + 1, fb);
-                }
-            }
-
-            // ---- merge: each row's reference max over the waves, every wave's O and
-            // l rescaled to it, then summed (a tree over four LDS slots: the staging
-            // buffers, idle here, each hold one wave's O^T fragments exactly)
-            __shared__ float s_m[NW][16];
-            __shared__ float s_l[NW][16];
-            if (g == 0)
-                s_m[wave][r16] = m1;
-            const bool any_bad = __syncthreads_or(bad ? 1 : 0) != 0 || bad_ctx;
-            float mx = -INFINITY;
-#pragma unroll
-            for (int w = 0; w < NW; ++w)
-                mx = fmaxf(mx, s_m[w][r16]);
-            const float f = (m1 == -INFINITY) ? 0.f : exp2_fast((m1 - mx) * sl);
-#pragma unroll
-            for (int n = 0; n < NDB; ++n)
-                o1[n] *= f;
-            if (g == 0)
-                s_l[wave][r16] = l1[0] * f;
-#pragma unroll
-            for (int half = NW / 2; half >= 1; half /= 2) {
-                if (wave >= half && wave < 2 * half) {
-                    const int k = wave - half;
-                    u32x4 *slot = k < 2 ? s_k[k] : s_v[k - 2];
-#pragma unroll
-                    for (int n = 0; n < NDB; ++n)
-                        slot[n * kWave + lane] = __builtin_bit_cast(u32x4, o1[n]);
-                }
-                __syncthreads();
-                if (wave < half) {
-                    const u32x4 *slot = wave < 2 ? s_k[wave] : s_v[wave - 2];
-#pragma unroll
-                    for (int n = 0; n < NDB; ++n)
-                        o1[n] += __builtin_bit_cast(f32x4, slot[n * kWave + lane]);
-                }
-                __syncthreads();
-            }
-            if (wave == 0 && orow1 >= 0) {
-                float l = 0.f;
-#pragma unroll
-                for (int w = 0; w < NW; ++w)
-                    l += s_l[w][r16];
-                const float fo = l > 0.f ? a.v_scale / l : 0.f;
-                const float qnan = __builtin_nanf("");
-#pragma unroll
-                for (int n = 0; n < NDB; ++n) {
-                    f32x4 v = o1[n] * fo;
-                    if (any_bad)
-                        v = f32x4{qnan, qnan, qnan, qnan};
-                    uint16_t *dst = static_cast<uint16_t *>(a.out) + (size_t)orow1 * D + 16 * n + 4 * g;
-                    if constexpr (AT == DT_BF16)
-                        *reinterpret_cast<bf16x4 *>(dst) = __builtin_convertvector(v, bf16x4);
+                    // V^T tokens past the context, and whole blocks past key_end (padding
+                    // entries read as block 0), may hold anything: zero them.  Only a
+                    // step that reaches past key_end (<= ctx) has such tokens.
+                    VRaw keep;
+                    if constexpr (DT == DT_FP8)
+                        keep = VRaw{~0u, ~0u};
                     else
-                        *reinterpret_cast<f16x4 *>(dst) = __builtin_convertvector(v, f16x4);
+                        keep = VRaw{~0u, ~0u, ~0u, ~0u};
+                    if (32 * s + 32 > key_end) {                        // wave-uniform
+                        const int blk0 = (2 * s + v_blk) * kBlock;
+                        const int valid = blk0 >= key_end ? 0 : ctx - blk0;
+                        if constexpr (DT == DT_FP8) {
+#pragma unroll
+                            for (int w = 0; w < 2; ++w) {
+                                uint32_t m = 0;
+#pragma unroll
+                                for (int j = 0; j < 4; ++j)
+                                    m |= (v_tok0 + 4 * w + j < valid) ? (0xFFu << (8 * j)) : 0u;
+                                keep[w] = m;
+                            }
+                        } else {
+#pragma unroll
+                            for (int w = 0; w < 4; ++w)
+                                keep[w] = (v_tok0 + 2 * w < valid ? 0x0000FFFFu : 0u) |
+                                          (v_tok0 + 2 * w + 1 < valid ? 0xFFFF0000u : 0u);
+                        }
+                    }
+#pragma unroll
+                    for (int n = 0; n < NDB; ++n) {
+                        u32x4 vf;
+                        if constexpr (DT == DT_FP8) {
+                            const uint32_t w0 = fr.v[n][0] & keep[0];
+                            const uint32_t w1 = fr.v[n][1] & keep[1];
+                            vf = u32x4{fp8x2_to_16<AT, false>(w0), fp8x2_to_16<AT, true>(w0),
+                                       fp8x2_to_16<AT, false>(w1), fp8x2_to_16<AT, true>(w1)};
+                        } else {
+                            vf = fr.v[n] & keep;
+                        }
+#pragma unroll
+                        for (int c = 0; c < CS; ++c)
+                            o1[c][n] = mma32<AT>(vf, pb[c], o1[c][n]);
+                    }
+#pragma unroll
+                    for (int c = 0; c < CS; ++c)
+                        l1[c] = mma32<AT>(ones, pb[c], l1[c]);
+                };
+
+                // PF = 2: the loads of the step after next are issued before a step's
+                // products, and the last step's loads are repeated past the end so every
+                // pass issues the same loads; PF = 1: each step's loads, then its products
+                if (s_lo < s_hi) {
+                    if constexpr (PF == 2) {
+                        Frag fa, fb;
+                        load_step(s_lo, fa);
+                        for (int s = s_lo; s < s_hi; s += 2) {
+                            load_step(min(s + 1, s_hi - 1), fb);
+                            step(s, fa);
+                            load_step(min(s + 2, s_hi - 1), fa);
+                            if (s + 1 < s_hi)
+                                step(s + 1, fb);
+                        }
+                    } else {
+                        Frag fa;
+                        for (int s = s_lo; s < s_hi; ++s) {
+                            load_step(s, fa);
+                            step(s, fa);
+                        }
+                    }
                 }
-            }
+
+                // ---- merge: each row's reference max over the waves, every wave's O
+                // and l rescaled to it, then summed (a tree over four LDS slots: the
+                // staging buffers, idle here, each hold one column block of one wave's
+                // O^T fragments exactly)
+                if (g == 0) {
+#pragma unroll
+                    for (int c = 0; c < CS; ++c)
+                        s_m[c][wave][r16] = m1[c];
+                }
+                const bool any_bad = __syncthreads_or(bad ? 1 : 0) != 0 || bad_ctx;
+#pragma unroll
+                for (int c = 0; c < CS; ++c) {
+                    float mx = -INFINITY;
+#pragma unroll
+                    for (int w = 0; w < NW; ++w)
+                        mx = fmaxf(mx, s_m[c][w][r16]);
+                    const float f = (m1[c] == -INFINITY) ? 0.f : exp2_fast((m1[c] - mx) * sl);
+#pragma unroll
+                    for (int n = 0; n < NDB; ++n)
+                        o1[c][n] *= f;
+                    if (g == 0)
+                        s_l[c][wave][r16] = l1[c][0] * f;
+                }
+#pragma unroll
+                for (int c = 0; c < CS; ++c) {
+#pragma unroll
+                    for (int half = NW / 2; half >= 1; half /= 2) {
+                        if (wave >= half && wave < 2 * half) {
+                            const int k = wave - half;
+                            u32x4 *slot = k < 2 ? s_k[k] : s_v[k - 2];
+#pragma unroll
+                            for (int n = 0; n < NDB; ++n)
+                                slot[n * kWave + lane] = __builtin_bit_cast(u32x4, o1[c][n]);
+                        }
+                        __syncthreads();
+                        if (wave < half) {
+                            const u32x4 *slot = wave < 2 ? s_k[wave] : s_v[wave - 2];
+#pragma unroll
+                            for (int n = 0; n < NDB; ++n)
+                                o1[c][n] += __builtin_bit_cast(f32x4, slot[n * kWave + lane]);
+                        }
+                        __syncthreads();
+                    }
+                }
+                if (wave == 0) {
+                    const float qnan = __builtin_nanf("");
+#pragma unroll
+                    for (int c = 0; c < CS; ++c) {
+                        if (orow1[c] < 0)
+                            continue;
+                        float l = 0.f;
+#pragma unroll
+                        for (int w = 0; w < NW; ++w)
+                            l += s_l[c][w][r16];
+                        const float fo = l > 0.f ? a.v_scale / l : 0.f;
+#pragma unroll
+                        for (int n = 0; n < NDB; ++n) {
+                            f32x4 v = o1[c][n] * fo;
+                            if (any_bad)
+                                v = f32x4{qnan, qnan, qnan, qnan};
+                            uint16_t *dst = static_cast<uint16_t *>(a.out) + (size_t)orow1[c] * D +
+                                            16 * n + 4 * g;
+                            if constexpr (AT == DT_BF16)
+                                *reinterpret_cast<bf16x4 *>(dst) = __builtin_convertvector(v, bf16x4);
+                            else
+                                *reinterpret_cast<f16x4 *>(dst) = __builtin_convertvector(v, f16x4);
+                        }
+                    }
+                }
+            };
+            // 17 .. 32 rows: the two column blocks one after the other, each as above
+            // (both passes read the same keys; one pass over both blocks would need
+            // registers the rest of this kernel instance would then also pay for)
+            // Two column blocks (17 .. 32 rows) only in the launch whose tiles are all
+            // this small: their registers would otherwise be paid by the whole kernel.
+            if (tile_rows <= 16)
+                run(std::integral_constant<int, 1>{}, std::integral_constant<int, 2>{}, 0);
+            else if constexpr (SMALLQ)
+                run(std::integral_constant<int, 2>{}, std::integral_constant<int, 1>{}, 0);
             return;
         }
     }
+
+    // Every tile of a small-query launch took the split path above.
+    if constexpr (SMALLQ)
+        return;
 
     // ---- each thread's 16-byte pieces of a step, fixed for the whole loop: which of
     // the step's two blocks (the same for a whole wave, kept scalar), the element
@@ -953,14 +1037,22 @@ __global__ __launch_bounds__(NW *kWave, C * D <= 256 ? 2 : 1) void pa_prefill_ke
 }
 
 template <int DT, int AT, int D>
-hipError_t launch_prefill_t(const PrefillArgs &a, int grid, bool idle, hipStream_t stream)
+hipError_t launch_prefill_t(const PrefillArgs &a, int grid, bool idle, bool smallq,
+                            hipStream_t stream)
 {
     constexpr int C = prefill_cols(D);
+    if constexpr (D <= 128) {
+        if (smallq) {
+            hipLaunchKernelGGL((pa_prefill_kernel<DT, AT, D, kPrefillWaves, C, true, true>),
+                               dim3(grid), dim3(kPrefillWaves * kWave), 0, stream, a);
+            return hipGetLastError();
+        }
+    }
     if (idle)
-        hipLaunchKernelGGL((pa_prefill_kernel<DT, AT, D, kPrefillWaves, C, true>),
+        hipLaunchKernelGGL((pa_prefill_kernel<DT, AT, D, kPrefillWaves, C, true, false>),
                            dim3(grid), dim3(kPrefillWaves * kWave), 0, stream, a);
     else
-        hipLaunchKernelGGL((pa_prefill_kernel<DT, AT, D, kPrefillWaves, C, false>),
+        hipLaunchKernelGGL((pa_prefill_kernel<DT, AT, D, kPrefillWaves, C, false, false>),
                            dim3(grid), dim3(kPrefillWaves * kWave), 0, stream, a);
     return hipGetLastError();
 }
@@ -986,6 +1078,9 @@ hipError_t launch_prefill(int dtype, int act_dtype, int head_dim, const PrefillA
     // pairs on one XCD, and the chunks hold at most T / q_tile + B tiles when their
     // query ranges do not overlap (ranges that do are outside the contract and may then
     // lose tiles).  Never more than the plain map's share per XCD.
+    // Every tile has at most two column blocks of rows: the instance that holds only
+    // the split path (its registers are not shared with the staged loop).
+    const bool smallq = head_dim <= 128 && (int64_t)a.max_query_len * a.group <= 32;
     int grid = grid_plain;
     if (!full && a.longest_first) {
         const int64_t tiles = std::min<int64_t>((int64_t)a.num_tokens / a.q_tile + a.num_seqs,
@@ -996,7 +1091,7 @@ hipError_t launch_prefill(int dtype, int act_dtype, int head_dim, const PrefillA
     }
 #define PA_PF_CASE(DT, AT, D)                                                      \
     if (dtype == DT && act_dtype == AT && head_dim == D)                          \
-        return launch_prefill_t<DT, AT, D>(a, grid, !full, stream);
+        return launch_prefill_t<DT, AT, D>(a, grid, !full, smallq, stream);
     PA_PF_CASE(DT_BF16, DT_BF16, 128)
     PA_PF_CASE(DT_BF16, DT_BF16, 64)
     PA_PF_CASE(DT_BF16, DT_BF16, 256)

@@ -91,6 +91,23 @@ SMALL = [
     W.Spec("pf_chunk_tails_fp8_bf16", "bf16", 64, 8, 128, [100, 700, 66], seed=52,
            spare_blocks=1, kv_dtype="fp8", k_scale=0.0117, v_scale=0.0093,
            query_lens=[33, 65, 34]),
+    # every chunk at most 32 rows of a tile (q_len x group <= 32, d <= 128): the launch
+    # whose tiles all take the split path, 17-32-row tiles as two column blocks; short
+    # contexts, a chunk longer than its context's last step, and contexts past 8,192
+    # tokens (block-id reloads)
+    W.Spec("pf_spec_rows_bf16", "bf16", 64, 8, 128, [4, 40, 3000, 9000, 17, 1], seed=55,
+           spare_blocks=1, query_lens=[4, 3, 4, 2, 1, 1]),
+    W.Spec("pf_spec_rows_fp8_bf16", "bf16", 64, 8, 128, [4, 300, 2000, 33], seed=56,
+           spare_blocks=1, kv_dtype="fp8", k_scale=0.0117, v_scale=0.0093,
+           query_lens=[4, 4, 3, 4]),
+    W.Spec("pf_spec_rows_fp8_f16_g16", "f16", 32, 2, 128, [2, 700, 65, 9000], seed=57,
+           spare_blocks=1, kv_dtype="fp8", k_scale=0.25, v_scale=0.0625,
+           query_lens=[2, 2, 1, 2]),
+    W.Spec("pf_spec_rows_f16_mha_d64", "f16", 16, 16, 64, [32, 500, 20, 1200], seed=58,
+           spare_blocks=1, query_lens=[32, 17, 20, 1]),
+    W.Spec("pf_spec_rows_fp8_bf16_d64_g4", "bf16", 16, 4, 64, [8, 100, 5000], seed=59,
+           spare_blocks=1, kv_dtype="fp8", k_scale=0.0117, v_scale=0.0093,
+           query_lens=[8, 5, 7]),
     # more sequences than the ranked map takes (plain map, launch order by index), and a
     # single sequence (nothing to rank)
     W.Spec("pf_300_seqs_bf16", "bf16", 8, 2, 128, _CTX300, seed=49, spare_blocks=1,
