@@ -133,9 +133,9 @@ int32_t pa_decode_partition_tokens(int32_t num_seqs, int32_t num_q_heads,
  * cuts the KV axis so that the GPU's CUs all work ("Deep dive into vLLM 06",
  * Flash-Decoding): the longest sequence is cut into the most partitions that still
  * keep every workgroup with work in one round of the MI355X's 256 CUs, each as long as
- * that count allows; when no partition allows one round, it returns the automatic
- * choice.  A batch of
- * equal lengths gets the automatic choice.  The lengths must be those passed on the
+ * that count allows (two partitions are cut evenly instead); when no partition allows
+ * one round, it returns the automatic choice.  A batch of equal lengths gets the
+ * automatic choice.  The lengths must be those passed on the
  * device to the call that uses the result (anything else is still correct, only
  * planned for other lengths).  Host-only; returns a positive multiple of 16, or -1 on
  * bad input. */

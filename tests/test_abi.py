@@ -201,7 +201,19 @@ def test_decode_plan(lib):
     assert p == 408 * 16
     assert 8 * (4 * -(-2048 // 408) + 8) <= 256 < 8 * (4 * -(-2048 // 340) + 8)
     # no partition fits one round: the automatic choice
-    assert plan(8, 8, 128, [65536] * 64) == auto(8, 8, 64, 65536)
+    assert plan(8, 8, 128, [65536] * 63 + [65520]) == auto(8, 8, 64, 65536)
+    # equal lengths at G = 16: the automatic split, two even halves of 128 blocks (the
+    # rule for unequal lengths would give 248 + 8)
+    assert plan(64, 4, 128, [4096] * 32) == auto(64, 4, 32, 4096) == 2048
+    # unequal lengths whose longest takes two partitions: even halves, rounded up to
+    # whole blocks per wave (257 blocks -> 136 + 121), still one round of 256
+    # workgroups (4 kv-heads x 32 x 2)
+    assert plan(64, 4, 128, [4100] + [4000] * 31) == 136 * 16
+    # a bound from the other sequences above the even half wins: 1 long + 62 sequences
+    # of 3,000 tokens (188 blocks) at 4 kv-heads keep one round only with partitions of
+    # at least 188 blocks, so 257 blocks -> 192 + 65
+    assert plan(64, 4, 128, [4100] + [3000] * 62) == 192 * 16
+    assert 4 * (2 + 62 * -(-188 // 188)) <= 256 < 4 * (2 + 62 * -(-188 // 187))
     assert plan(64, 8, 128, []) > 0 and plan(64, 8, 128, []) % 16 == 0
     assert plan(64, 8, 128, [5, -1]) == -1
     assert plan(64, 8, 128, [100] * 3) % 16 == 0
