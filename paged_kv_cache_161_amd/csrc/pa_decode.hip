@@ -40,6 +40,9 @@
 #include "pa_fp8.h"
 
 namespace pa {
+
+constexpr int kXcds = 8;   // MI355X: workgroup ids go round-robin over its 8 XCDs
+
 namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -500,9 +503,38 @@ __global__ __launch_bounds__(NW *kWave, min_waves_per_simd(DT, D, PF)) void pa_d
     int *s_bad = reinterpret_cast<int *>(smem + NW * 32);   // [NW] (16 ints reserved)
     float *s_o = smem + NW * 32 + 16;               // [NW][GS][DP]
 
-    const int p = blockIdx.x;
-    const int kvh = blockIdx.y / a.head_chunks;
-    const int chunk = blockIdx.y - kvh * a.head_chunks;
+    // (partition, kv-head x head chunk, sequence rank).  A group above 16 q-heads runs
+    // one workgroup per head chunk, each streaming the same K/V: the ids are then
+    // regrouped so a (sequence, kv-head, partition) unit's chunks are dispatched back
+    // to back on one XCD (ids round-robin over the XCDs, so ids L, L + 8, ... share
+    // one L2), where the later chunks find the K/V in that L2.  Units keep the plain
+    // order (partition fastest, then kv-head, then sequence rank); the last group of
+    // fewer than 8 units is spread without that alignment.
+    int px = blockIdx.x, py = blockIdx.y, pz = blockIdx.z;
+    if (a.head_chunks > 1) {
+        const int64_t C = a.head_chunks;
+        const int64_t hkv = gridDim.y / C;
+        const int64_t L = blockIdx.x + (int64_t)gridDim.x * (blockIdx.y + (int64_t)gridDim.y * blockIdx.z);
+        const int64_t U = (int64_t)gridDim.x * hkv * gridDim.z;
+        const int64_t full = U / kXcds * kXcds;
+        int64_t u, c;
+        if (L < full * C) {
+            const int64_t rr = L % (kXcds * C);
+            c = rr / kXcds;
+            u = L / (kXcds * C) * kXcds + rr % kXcds;
+        } else {
+            const int64_t rem = U - full, rr = L - full * C;
+            c = rr / rem;
+            u = full + rr % rem;
+        }
+        px = (int)(u % gridDim.x);
+        const int64_t t = u / gridDim.x;
+        py = (int)(t % hkv * C + c);
+        pz = (int)(t / hkv);
+    }
+    const int p = px;
+    const int kvh = py / a.head_chunks;
+    const int chunk = py - kvh * a.head_chunks;
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -533,7 +565,7 @@ __global__ __launch_bounds__(NW *kWave, min_waves_per_simd(DT, D, PF)) void pa_d
     // batch then starts its longest streams first instead of last.  The loads for
     // sequence z go out first; they are kept when the rank maps z to itself (always,
     // in a batch of equal lengths) and reissued otherwise.
-    int b = blockIdx.z;
+    int b = pz;
     load_seq(b);
     int ctx = -1;
     if (a.longest_first) {
@@ -549,13 +581,13 @@ __global__ __launch_bounds__(NW *kWave, min_waves_per_simd(DT, D, PF)) void pa_d
                 const int cu = s_ctx[u];
                 rank += (cu > c || (cu == c && u < t)) ? 1 : 0;
             }
-            if (rank == (int)blockIdx.z)
+            if (rank == pz)
                 s_ctx[nseq] = t;
         }
         __syncthreads();
         b = __builtin_amdgcn_readfirstlane(s_ctx[nseq]);
         ctx = s_ctx[b];
-        if (b != (int)blockIdx.z)
+        if (b != pz)
             load_seq(b);
     } else {
         ctx = a.context_lens[b];
