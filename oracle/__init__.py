@@ -7,7 +7,8 @@ oracle.c; this module only marshals numpy arrays into it.
 Array conventions (numpy, host memory, C-contiguous):
   dtype "f32": np.float32 arrays; "f16": np.float16; "bf16": np.uint16 bit patterns;
   "fp8": np.uint8 OCP E4M3 codes (pools only; q and new rows are then f16 or bf16,
-  and the pool holds code value x k_scale / v_scale).
+  and the pool holds code value x k_scale / v_scale: one scale pair for the pool, or
+  arrays with one fp32 scale per kv-head).
   q [B][Hq][d], k_pool [N][Hkv][16][d], v_pool [N][Hkv][d][16],
   block_tables [B][max_blocks] int32, context_lens [B] int32.
 """
@@ -67,7 +68,37 @@ def _bind(lib):
     lib.oracle_decode_contig_ex.restype = I
     lib.oracle_cache_append.argtypes = [P, P, I, I, I, I, P, P, P, I]
     lib.oracle_cache_append.restype = I
+    lib.oracle_decode_paged_hs.argtypes = [P, I, P, P, I, D, D, P, P, I, I, I, I, I, P, I, P,
+                                           ctypes.c_float, P, P, I]
+    lib.oracle_decode_paged_hs.restype = I
+    lib.oracle_prefill_paged_hs.argtypes = [P, I, P, P, I, D, D, P, P, I, P, I, I, I, I, P, I,
+                                            P, ctypes.c_float, P, P, I]
+    lib.oracle_prefill_paged_hs.restype = I
+    lib.oracle_decode_contig_hs.argtypes = [P, I, P, P, I, D, D, P, P, I, I, I, I, I, P,
+                                            ctypes.c_float, P, P, I]
+    lib.oracle_decode_contig_hs.restype = I
+    lib.oracle_cache_append_hs.argtypes = [P, P, I, I, ctypes.c_float, ctypes.c_float, P, P, I,
+                                           I, I, P, P, P, I]
+    lib.oracle_cache_append_hs.restype = I
     return lib
+
+
+def _scale_args(k_scale, v_scale, num_kv_heads):
+    """Scales as the C entry points take them: a number is one scale for the whole pool
+    (as fp32, widened); an array of num_kv_heads values is one fp32 scale per kv-head.
+    Returns (k, v, k_heads, v_heads, keep): k_heads / v_heads are pointers or None, and
+    keep holds the arrays they point into."""
+    out, keep = [], []
+    for x in (k_scale, v_scale):
+        if np.ndim(x) == 0:
+            out.append((float(np.float32(x)), None))
+        else:
+            a = np.ascontiguousarray(x, np.float32)
+            assert a.shape == (num_kv_heads,), "one scale per kv-head"
+            keep.append(a)
+            out.append((1.0, _ptr(a)))
+    (k, kh), (v, vh) = out
+    return k, v, kh, vh, keep
 
 
 def default_threads():
@@ -112,7 +143,8 @@ def encode_e4m3(x, lib=None):
 def decode_paged(q, k_pool, v_pool, dtype, block_tables, context_lens, scale,
                  threads=None, lib=None, q_dtype=None, k_scale=1.0, v_scale=1.0):
     """Returns (out [B][Hq][d] fp64, wsum [B][Hq] fp64).  dtype is the pools' type;
-    q_dtype (default: dtype) the type of q; fp8 pools read code x k_scale / v_scale."""
+    q_dtype (default: dtype) the type of q; fp8 pools read code x k_scale / v_scale,
+    each a number (the pool) or an array of one fp32 scale per kv-head."""
     lib = lib or load()
     q_dtype = q_dtype or dtype
     _check(q, q_dtype)
@@ -126,11 +158,12 @@ def decode_paged(q, k_pool, v_pool, dtype, block_tables, context_lens, scale,
     assert bt.shape[0] == B and cl.shape == (B,)
     out = np.zeros((B, hq, d), np.float64)
     wsum = np.zeros((B, hq), np.float64)
-    rc = lib.oracle_decode_paged_ex(_ptr(q), DTYPE_CODES[q_dtype], _ptr(k_pool), _ptr(v_pool),
-                                    DTYPE_CODES[dtype], float(np.float32(k_scale)),
-                                    float(np.float32(v_scale)), B, hq, hkv, d, nblk, _ptr(bt),
-                                    bt.shape[1], _ptr(cl), ctypes.c_float(np.float32(scale)),
-                                    _ptr(out), _ptr(wsum), threads or default_threads())
+    ks, vs, kh, vh, _keep = _scale_args(k_scale, v_scale, hkv)
+    rc = lib.oracle_decode_paged_hs(_ptr(q), DTYPE_CODES[q_dtype], _ptr(k_pool), _ptr(v_pool),
+                                    DTYPE_CODES[dtype], ks, vs, kh, vh, B, hq, hkv, d, nblk,
+                                    _ptr(bt), bt.shape[1], _ptr(cl),
+                                    ctypes.c_float(np.float32(scale)), _ptr(out), _ptr(wsum),
+                                    threads or default_threads())
     if rc:
         raise ValueError(f"oracle_decode_paged returned {rc}")
     return out, wsum
@@ -156,10 +189,10 @@ def prefill_paged(q, k_pool, v_pool, dtype, query_start, block_tables, context_l
     assert bt.shape[0] == B and qs.shape == (B + 1,) and qs[-1] == T
     out = np.zeros((T, hq, d), np.float64)
     wsum = np.zeros((T, hq), np.float64)
-    rc = lib.oracle_prefill_paged_ex(_ptr(q), DTYPE_CODES[q_dtype], _ptr(k_pool), _ptr(v_pool),
-                                     DTYPE_CODES[dtype], float(np.float32(k_scale)),
-                                     float(np.float32(v_scale)), B, _ptr(qs), hq, hkv, d, nblk,
-                                     _ptr(bt), bt.shape[1], _ptr(cl),
+    ks, vs, kh, vh, _keep = _scale_args(k_scale, v_scale, hkv)
+    rc = lib.oracle_prefill_paged_hs(_ptr(q), DTYPE_CODES[q_dtype], _ptr(k_pool), _ptr(v_pool),
+                                     DTYPE_CODES[dtype], ks, vs, kh, vh, B, _ptr(qs), hq, hkv, d,
+                                     nblk, _ptr(bt), bt.shape[1], _ptr(cl),
                                      ctypes.c_float(np.float32(scale)), _ptr(out), _ptr(wsum),
                                      threads or default_threads())
     if rc:
@@ -181,11 +214,11 @@ def decode_contig(q, k, v, dtype, context_lens, scale, threads=None, lib=None, q
     cl = np.ascontiguousarray(context_lens, np.int32)
     out = np.zeros((B, hq, d), np.float64)
     wsum = np.zeros((B, hq), np.float64)
-    rc = lib.oracle_decode_contig_ex(_ptr(q), DTYPE_CODES[q_dtype], _ptr(k), _ptr(v),
-                                     DTYPE_CODES[dtype], float(np.float32(k_scale)),
-                                     float(np.float32(v_scale)), B, hq, hkv, d, s_max, _ptr(cl),
-                                     ctypes.c_float(np.float32(scale)), _ptr(out), _ptr(wsum),
-                                     threads or default_threads())
+    ks, vs, kh, vh, _keep = _scale_args(k_scale, v_scale, hkv)
+    rc = lib.oracle_decode_contig_hs(_ptr(q), DTYPE_CODES[q_dtype], _ptr(k), _ptr(v),
+                                     DTYPE_CODES[dtype], ks, vs, kh, vh, B, hq, hkv, d, s_max,
+                                     _ptr(cl), ctypes.c_float(np.float32(scale)), _ptr(out),
+                                     _ptr(wsum), threads or default_threads())
     if rc:
         raise ValueError(f"oracle_decode_contig returned {rc}")
     return out, wsum
@@ -207,10 +240,11 @@ def cache_append(k_pool, v_pool, k_new, v_new, slot_mapping, dtype, inplace=Fals
     nblk, hkv, _, d = k_pool.shape
     sm = np.ascontiguousarray(slot_mapping, np.int32)
     assert k_new.shape == (sm.size, hkv, d) and v_new.shape == k_new.shape
-    rc = lib.oracle_cache_append_ex(_ptr(k_out), _ptr(v_out), DTYPE_CODES[dtype],
-                                    DTYPE_CODES[act_dtype], ctypes.c_float(np.float32(k_scale)),
-                                    ctypes.c_float(np.float32(v_scale)), nblk, hkv, d,
-                                    _ptr(k_new), _ptr(v_new), _ptr(sm), sm.size)
+    ks, vs, kh, vh, _keep = _scale_args(k_scale, v_scale, hkv)
+    rc = lib.oracle_cache_append_hs(_ptr(k_out), _ptr(v_out), DTYPE_CODES[dtype],
+                                    DTYPE_CODES[act_dtype], ctypes.c_float(ks), ctypes.c_float(vs),
+                                    kh, vh, nblk, hkv, d, _ptr(k_new), _ptr(v_new), _ptr(sm),
+                                    sm.size)
     if rc:
         raise ValueError(f"oracle_cache_append returned {rc}")
     return k_out, v_out

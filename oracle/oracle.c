@@ -278,7 +278,12 @@ typedef struct {
      * q_start[b] .. q_start[b+1]-1 of q [num_tokens][Hq][d]                          */
     const int32_t *q_start;
     int num_tokens;
+    /* fp8 pools: a scale per kv-head (NULL: k_scale / v_scale for every head)        */
+    const float *k_head_scales, *v_head_scales;
 } decode_args;
+
+/* A usable scale is finite and > 0.                                                  */
+static int scale_ok(double s) { return s > 0.0 && isfinite(s); }
 
 /* Sequence that owns query row `tok` (q_start is non-decreasing, q_start[0] = 0).    */
 static int owner_of(const int32_t *q_start, int B, int tok)
@@ -324,6 +329,19 @@ static void *decode_worker(void *p)
             n = pos < 0 ? 0 : pos + 1;
         }
         int kvh = h / group;
+        /* K of kv-head kvh = stored value x its scale (V likewise): the head's entry of
+         * a per-head array when one is given, else the pool's one scale.  The FP8
+         * format scales a tensor ("Deep dive into vLLM 06", FP8 section); a per-head
+         * array treats each head's slice of the cache as its own tensor.  A head whose
+         * scale is unusable has no defined attention: its rows are NaN.               */
+        double ks = A->k_head_scales ? (double)A->k_head_scales[kvh] : A->k_scale;
+        double vs = A->v_head_scales ? (double)A->v_head_scales[kvh] : A->v_scale;
+        if (!scale_ok(ks) || !scale_ok(vs)) {
+            for (int e = 0; e < A->d; ++e)
+                A->out[(size_t)u * A->d + e] = NAN;
+            A->wsum[u] = NAN;
+            continue;
+        }
         attn_job J;
         J.q_row = (const char *)A->q + ((size_t)r * A->hq + h) * A->d * elem_bytes(A->q_dtype);
         J.q_dtype = A->q_dtype;
@@ -335,13 +353,13 @@ static void *decode_worker(void *p)
         contig_ctx cc;
         if (A->paged) {
             pc.k_pool = A->k; pc.v_pool = A->v; pc.dtype = A->dtype; pc.hkv = A->hkv;
-            pc.d = A->d; pc.kv_head = kvh; pc.k_scale = A->k_scale; pc.v_scale = A->v_scale;
+            pc.d = A->d; pc.kv_head = kvh; pc.k_scale = ks; pc.v_scale = vs;
             pc.table_row = A->tables + (size_t)b * A->max_blocks;
             J.key = paged_key; J.val = paged_val; J.ctx = &pc;
         } else {
             cc.k = A->k; cc.v = A->v; cc.dtype = A->dtype; cc.hkv = A->hkv; cc.d = A->d;
             cc.s_max = A->s_max; cc.seq = b; cc.kv_head = kvh;
-            cc.k_scale = A->k_scale; cc.v_scale = A->v_scale;
+            cc.k_scale = ks; cc.v_scale = vs;
             J.key = contig_key; J.val = contig_val; J.ctx = &cc;
         }
         attend(&J, A->out + (size_t)u * A->d, A->wsum + u);
@@ -396,8 +414,9 @@ static int check_common(int dtype, int B, int hq, int hkv, int d)
  * (sum of the normalised softmax weights of each row) are fp64.  Returns 0, or -1 on
  * bad shapes, -2 when a context length or a block-table entry it would read is out
  * of range.                                                                          */
-int oracle_decode_paged_ex(const void *q, int q_dtype, const void *k_pool, const void *v_pool,
-                           int kv_dtype, double k_scale, double v_scale, int num_seqs,
+int oracle_decode_paged_hs(const void *q, int q_dtype, const void *k_pool, const void *v_pool,
+                           int kv_dtype, double k_scale, double v_scale,
+                           const float *k_head_scales, const float *v_head_scales, int num_seqs,
                            int num_q_heads, int num_kv_heads, int head_dim, int num_blocks,
                            const int32_t *block_tables, int max_blocks_per_seq,
                            const int32_t *context_lens, float scale, double *out, double *wsum,
@@ -420,7 +439,23 @@ int oracle_decode_paged_ex(const void *q, int q_dtype, const void *k_pool, const
     decode_args A = {1, q, k_pool, v_pool, kv_dtype, q_dtype, k_scale, v_scale, num_seqs,
                      num_q_heads, num_kv_heads, head_dim, num_blocks, max_blocks_per_seq, 0,
                      block_tables, context_lens, (double)scale, out, wsum, num_threads};
+    A.k_head_scales = k_head_scales;
+    A.v_head_scales = v_head_scales;
     return run_decode(&A);
+}
+
+/* The same with one scale pair for the whole pool.                                   */
+int oracle_decode_paged_ex(const void *q, int q_dtype, const void *k_pool, const void *v_pool,
+                           int kv_dtype, double k_scale, double v_scale, int num_seqs,
+                           int num_q_heads, int num_kv_heads, int head_dim, int num_blocks,
+                           const int32_t *block_tables, int max_blocks_per_seq,
+                           const int32_t *context_lens, float scale, double *out, double *wsum,
+                           int num_threads)
+{
+    return oracle_decode_paged_hs(q, q_dtype, k_pool, v_pool, kv_dtype, k_scale, v_scale, NULL,
+                                  NULL, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                  num_blocks, block_tables, max_blocks_per_seq, context_lens,
+                                  scale, out, wsum, num_threads);
 }
 
 /* Paged prefill attention (a prompt chunk, or several, over the paged cache).
@@ -435,12 +470,14 @@ int oracle_decode_paged_ex(const void *q, int q_dtype, const void *k_pool, const
  * ctx - q_len + i and attends to tokens 0 .. ctx - q_len + i.  A query with no key
  * (q_len > ctx) gives a zero row.  out [T][Hq][d], wsum [T][Hq] fp64.  Returns 0, -1
  * on bad shapes, -2 on an out-of-range context length, block-table entry or q_start.  */
-int oracle_prefill_paged_ex(const void *q, int q_dtype, const void *k_pool, const void *v_pool,
-                            int kv_dtype, double k_scale, double v_scale, int num_seqs,
-                            const int32_t *query_start, int num_q_heads, int num_kv_heads,
-                            int head_dim, int num_blocks, const int32_t *block_tables,
-                            int max_blocks_per_seq, const int32_t *context_lens, float scale,
-                            double *out, double *wsum, int num_threads)
+int oracle_prefill_paged_hs(const void *q, int q_dtype, const void *k_pool, const void *v_pool,
+                            int kv_dtype, double k_scale, double v_scale,
+                            const float *k_head_scales, const float *v_head_scales,
+                            int num_seqs, const int32_t *query_start, int num_q_heads,
+                            int num_kv_heads, int head_dim, int num_blocks,
+                            const int32_t *block_tables, int max_blocks_per_seq,
+                            const int32_t *context_lens, float scale, double *out,
+                            double *wsum, int num_threads)
 {
     if (check_common(kv_dtype, num_seqs, num_q_heads, num_kv_heads, head_dim) ||
         check_common(q_dtype, num_seqs, num_q_heads, num_kv_heads, head_dim) ||
@@ -464,7 +501,22 @@ int oracle_prefill_paged_ex(const void *q, int q_dtype, const void *k_pool, cons
                      num_q_heads, num_kv_heads, head_dim, num_blocks, max_blocks_per_seq, 0,
                      block_tables, context_lens, (double)scale, out, wsum, num_threads,
                      query_start, query_start[num_seqs]};
+    A.k_head_scales = k_head_scales;
+    A.v_head_scales = v_head_scales;
     return run_decode(&A);
+}
+
+int oracle_prefill_paged_ex(const void *q, int q_dtype, const void *k_pool, const void *v_pool,
+                            int kv_dtype, double k_scale, double v_scale, int num_seqs,
+                            const int32_t *query_start, int num_q_heads, int num_kv_heads,
+                            int head_dim, int num_blocks, const int32_t *block_tables,
+                            int max_blocks_per_seq, const int32_t *context_lens, float scale,
+                            double *out, double *wsum, int num_threads)
+{
+    return oracle_prefill_paged_hs(q, q_dtype, k_pool, v_pool, kv_dtype, k_scale, v_scale, NULL,
+                                   NULL, num_seqs, query_start, num_q_heads, num_kv_heads,
+                                   head_dim, num_blocks, block_tables, max_blocks_per_seq,
+                                   context_lens, scale, out, wsum, num_threads);
 }
 
 /* Same with q and K/V all of one type and unit scales.                             */
@@ -482,10 +534,11 @@ int oracle_decode_paged(const void *q, const void *k_pool, const void *v_pool, i
 
 /* The same attention over an ordinary contiguous cache k, v [B][Hkv][S_max][d] of
  * kv_dtype (read as value x scale), q of q_dtype.                                     */
-int oracle_decode_contig_ex(const void *q, int q_dtype, const void *k, const void *v,
-                            int kv_dtype, double k_scale, double v_scale, int num_seqs,
-                            int num_q_heads, int num_kv_heads, int head_dim, int s_max,
-                            const int32_t *context_lens, float scale, double *out,
+int oracle_decode_contig_hs(const void *q, int q_dtype, const void *k, const void *v,
+                            int kv_dtype, double k_scale, double v_scale,
+                            const float *k_head_scales, const float *v_head_scales,
+                            int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                            int s_max, const int32_t *context_lens, float scale, double *out,
                             double *wsum, int num_threads)
 {
     if (check_common(kv_dtype, num_seqs, num_q_heads, num_kv_heads, head_dim) ||
@@ -498,7 +551,20 @@ int oracle_decode_contig_ex(const void *q, int q_dtype, const void *k, const voi
     decode_args A = {0, q, k, v, kv_dtype, q_dtype, k_scale, v_scale, num_seqs, num_q_heads,
                      num_kv_heads, head_dim, 0, 0, s_max, NULL, context_lens, (double)scale,
                      out, wsum, num_threads};
+    A.k_head_scales = k_head_scales;
+    A.v_head_scales = v_head_scales;
     return run_decode(&A);
+}
+
+int oracle_decode_contig_ex(const void *q, int q_dtype, const void *k, const void *v,
+                            int kv_dtype, double k_scale, double v_scale, int num_seqs,
+                            int num_q_heads, int num_kv_heads, int head_dim, int s_max,
+                            const int32_t *context_lens, float scale, double *out,
+                            double *wsum, int num_threads)
+{
+    return oracle_decode_contig_hs(q, q_dtype, k, v, kv_dtype, k_scale, v_scale, NULL, NULL,
+                                   num_seqs, num_q_heads, num_kv_heads, head_dim, s_max,
+                                   context_lens, scale, out, wsum, num_threads);
 }
 
 int oracle_decode_contig(const void *q, const void *k, const void *v, int dtype, int num_seqs,
@@ -519,8 +585,9 @@ int oracle_decode_contig(const void *q, const void *k, const void *v, int dtype,
  * bytes are copied unchanged.  An fp8 pool stores encode_e4m3(x / scale), the
  * division done in fp32 (the KV-cache write fused with quantisation that "Deep dive
  * into vLLM 06" lists among vLLM's fused kernels).  Returns -2 on a slot past the pool. */
-int oracle_cache_append_ex(void *k_pool, void *v_pool, int kv_dtype, int act_dtype,
-                           float k_scale, float v_scale, int num_blocks, int num_kv_heads,
+int oracle_cache_append_hs(void *k_pool, void *v_pool, int kv_dtype, int act_dtype,
+                           float k_scale, float v_scale, const float *k_head_scales,
+                           const float *v_head_scales, int num_blocks, int num_kv_heads,
                            int head_dim, const void *k_new, const void *v_new,
                            const int32_t *slot_mapping, int num_tokens)
 {
@@ -541,6 +608,9 @@ int oracle_cache_append_ex(void *k_pool, void *v_pool, int kv_dtype, int act_dty
             return -2;
         size_t blk = (size_t)(s / ORACLE_BLOCK), off = (size_t)(s % ORACLE_BLOCK);
         for (int h = 0; h < num_kv_heads; ++h) {
+            /* the row's kv-head scale: its per-head entry, else the pool's            */
+            float ks = k_head_scales ? k_head_scales[h] : k_scale;
+            float vs = v_head_scales ? v_head_scales[h] : v_scale;
             for (int e = 0; e < head_dim; ++e) {
                 size_t src = ((size_t)i * num_kv_heads + h) * head_dim + e;
                 size_t kdst = ((blk * num_kv_heads + h) * ORACLE_BLOCK + off) * head_dim + e;
@@ -548,8 +618,9 @@ int oracle_cache_append_ex(void *k_pool, void *v_pool, int kv_dtype, int act_dty
                 if (quantise) {
                     float kx = (float)widen_at(k_new, src, act_dtype);
                     float vx = (float)widen_at(v_new, src, act_dtype);
-                    ((uint8_t *)k_pool)[kdst] = encode_e4m3(kx / k_scale);
-                    ((uint8_t *)v_pool)[vdst] = encode_e4m3(vx / v_scale);
+                    /* an unusable scale quantises to the NaN code                     */
+                    ((uint8_t *)k_pool)[kdst] = scale_ok(ks) ? encode_e4m3(kx / ks) : 0x7F;
+                    ((uint8_t *)v_pool)[vdst] = scale_ok(vs) ? encode_e4m3(vx / vs) : 0x7F;
                 } else {
                     memcpy((char *)k_pool + kdst * eb, (const char *)k_new + src * eb, eb);
                     memcpy((char *)v_pool + vdst * eb, (const char *)v_new + src * eb, eb);
@@ -558,6 +629,16 @@ int oracle_cache_append_ex(void *k_pool, void *v_pool, int kv_dtype, int act_dty
         }
     }
     return 0;
+}
+
+int oracle_cache_append_ex(void *k_pool, void *v_pool, int kv_dtype, int act_dtype,
+                           float k_scale, float v_scale, int num_blocks, int num_kv_heads,
+                           int head_dim, const void *k_new, const void *v_new,
+                           const int32_t *slot_mapping, int num_tokens)
+{
+    return oracle_cache_append_hs(k_pool, v_pool, kv_dtype, act_dtype, k_scale, v_scale, NULL,
+                                  NULL, num_blocks, num_kv_heads, head_dim, k_new, v_new,
+                                  slot_mapping, num_tokens);
 }
 
 int oracle_cache_append(void *k_pool, void *v_pool, int dtype, int num_blocks,

@@ -80,8 +80,10 @@ class Spec:
     prefix_groups: Sequence[Tuple[Sequence[int], int]] = ()
     append: bool = True             # deliver token ctx-1 through cache_append
     kv_dtype: Optional[str] = None  # pool type; None = dtype; "fp8" keeps q/new rows in dtype
-    k_scale: float = 1.0            # fp8 pools: K = code x k_scale, V = code x v_scale
-    v_scale: float = 1.0
+    # fp8 pools: K = code x k_scale, V = code x v_scale; a number (the whole pool) or a
+    # sequence of one scale per kv-head
+    k_scale: object = 1.0
+    v_scale: object = 1.0
     # prefill: query (chunk) tokens per sequence, the last query_lens[b] tokens of its
     # context; None = decode (one query, the newest token)
     query_lens: Optional[Sequence[int]] = None
@@ -100,8 +102,8 @@ class Workload:
     spec: Spec
     dtype: str                      # q, out and new rows
     kv_dtype: str                   # pools
-    k_scale: np.float32
-    v_scale: np.float32
+    k_scale: np.ndarray             # np.float32 scalar, or float32 [Hkv] per-head scales
+    v_scale: np.ndarray
     q: np.ndarray                   # [B][Hq][d] (decode) or [T][Hq][d] (prefill)
     num_blocks: int                 # size of the physical pool
     live_blocks: np.ndarray         # [n] distinct physical ids holding live tokens
@@ -247,11 +249,12 @@ def _chunk_rng(seed: int, tag: int, chunk: int) -> np.random.Generator:
 
 
 def _fill_normals(seed: int, tag: int, dst: np.ndarray, sigma: float, dtype: str,
-                  transpose_blocks: bool = False, divisor: float = 1.0):
+                  transpose_blocks: bool = False, divisor=1.0):
     """Fill dst (storage dtype) with sigma * N(0, 1) / divisor rounded to the storage type.
 
     transpose_blocks: dst is [n][Hkv][d][16] and values are drawn in [n][Hkv][16][d]
     order (a V pool block drawn token-major, stored token-minor).
+    divisor: a number, or one value per index of dst's second axis (a pool's kv-head).
     """
     if dst.size == 0:
         return
@@ -267,7 +270,10 @@ def _fill_normals(seed: int, tag: int, dst: np.ndarray, sigma: float, dtype: str
         vals = _chunk_rng(seed, tag, c).standard_normal(size=(b - a) * per, dtype=np.float32)
         if sigma != 1.0:
             vals *= np.float32(sigma)
-        if divisor != 1.0:
+        if np.ndim(divisor) > 0:
+            per_axis1 = np.asarray(divisor, np.float32).reshape((1, -1) + (1,) * (len(shape) - 2))
+            vals = (vals.reshape(shape) / per_axis1).reshape(-1)
+        elif divisor != 1.0:
             vals /= np.float32(divisor)
         vals = round_to_storage(vals, dtype).reshape(shape)
         if transpose_blocks:
@@ -288,10 +294,19 @@ def build(spec: Spec, seed: Optional[int] = None) -> Workload:
     dt = spec.dtype
     kdt = spec.kv_dtype or dt
     assert kdt != "fp8" or dt in ("f16", "bf16"), "fp8 pools pair with f16/bf16 activations"
-    ks = np.float32(spec.k_scale if kdt == "fp8" else 1.0)
-    vsc = np.float32(spec.v_scale if kdt == "fp8" else 1.0)
     B = len(spec.context_lens)
     hq, hkv, d = spec.num_q_heads, spec.num_kv_heads, spec.head_dim
+
+    def _scale(x):
+        if kdt != "fp8":
+            return np.float32(1.0)
+        if np.ndim(x) == 0:
+            return np.float32(x)
+        a = np.asarray(x, np.float32)
+        assert a.shape == (hkv,), "one scale per kv-head"
+        return a
+
+    ks, vsc = _scale(spec.k_scale), _scale(spec.v_scale)
     assert hq % hkv == 0
     ctx = np.asarray(spec.context_lens, np.int64)
     nblk = (ctx + BLOCK - 1) // BLOCK
@@ -358,9 +373,8 @@ def build(spec: Spec, seed: Optional[int] = None) -> Workload:
     _fill_normals(seed, 1, q, spec.sigma, dt)
     k_live = np.empty((live.size + 1, hkv, BLOCK, d), STORAGE[kdt])
     v_live = np.empty((live.size + 1, hkv, d, BLOCK), STORAGE[kdt])
-    _fill_normals(seed, 2, k_live[:-1], spec.sigma, kdt, divisor=float(ks))
-    _fill_normals(seed, 3, v_live[:-1], spec.sigma, kdt, transpose_blocks=True,
-                  divisor=float(vsc))
+    _fill_normals(seed, 2, k_live[:-1], spec.sigma, kdt, divisor=ks)
+    _fill_normals(seed, 3, v_live[:-1], spec.sigma, kdt, transpose_blocks=True, divisor=vsc)
     k_live[-1] = _poison((hkv, BLOCK, d), kdt)
     v_live[-1] = _poison((hkv, d, BLOCK), kdt)
     pos_of = {int(p): i for i, p in enumerate(live)}

@@ -30,9 +30,21 @@ def to_f64(a, dtype):
     return a.astype(np.float64)
 
 
+def head_axis(x, axis, ndim):
+    """A workload scale as a factor: a number, or its per-kv-head array placed on
+    `axis` of an ndim-dimensional array (broadcast over the other axes)."""
+    if np.ndim(x) == 0:
+        return float(x)
+    shape = [1] * ndim
+    shape[axis] = -1
+    return np.asarray(x, np.float64).reshape(shape)
+
+
 def kv_f64(w, K, V):
-    """Logical K, V as values: stored element widened, times the pool's scales."""
-    return to_f64(K, w.kv_dtype) * float(w.k_scale), to_f64(V, w.kv_dtype) * float(w.v_scale)
+    """Logical K, V [B][Hkv][S][d] as values: stored element widened, times the pool's
+    scale or the kv-head's own."""
+    return (to_f64(K, w.kv_dtype) * head_axis(w.k_scale, 1, 4),
+            to_f64(V, w.kv_dtype) * head_axis(w.v_scale, 1, 4))
 
 
 def oracle_paged(w, kp, vp, tables=None, lib=None, **kw):
@@ -52,6 +64,9 @@ def small_specs():
                kv_dtype="fp8", k_scale=0.0117, v_scale=0.0093),
         W.Spec("pin_fp8_f16", "f16", 4, 1, 16, [20], seed=15, spare_blocks=1,
                kv_dtype="fp8", k_scale=0.25, v_scale=0.0625),
+        # one scale per kv-head, all different (and different between K and V)
+        W.Spec("pin_fp8_heads", "bf16", 12, 3, 32, [9, 40, 33], seed=16, spare_blocks=1,
+               kv_dtype="fp8", k_scale=(0.0117, 0.03, 0.005), v_scale=(0.0093, 0.002, 0.04)),
     ]
 
 
@@ -180,8 +195,10 @@ def check_append(lib):
         k2, v2 = appended(w, lib)
         kref, vref = w.host_pools()
         if w.kv_dtype == "fp8":       # codes of x / scale, the quotient in float32
-            kn = _e4m3_torch(to_f64(w.k_new, w.dtype).astype(np.float32) / w.k_scale)
-            vn = _e4m3_torch(to_f64(w.v_new, w.dtype).astype(np.float32) / w.v_scale)
+            ks = np.asarray(w.k_scale, np.float32).reshape((1, -1, 1) if np.ndim(w.k_scale) else ())
+            vs = np.asarray(w.v_scale, np.float32).reshape((1, -1, 1) if np.ndim(w.v_scale) else ())
+            kn = _e4m3_torch(to_f64(w.k_new, w.dtype).astype(np.float32) / ks)
+            vn = _e4m3_torch(to_f64(w.v_new, w.dtype).astype(np.float32) / vs)
         else:
             kn, vn = w.k_new, w.v_new
         for i, s in enumerate(w.slot_mapping.tolist()):
@@ -439,6 +456,9 @@ def prefill_specs():
                query_lens=[1, 7, 0, 5]),
         W.Spec("pf_fp8", "bf16", 8, 2, 32, [30, 47], seed=24, spare_blocks=1, kv_dtype="fp8",
                k_scale=0.0117, v_scale=0.0093, query_lens=[30, 12]),
+        W.Spec("pf_fp8_heads", "f16", 6, 3, 16, [25, 40], seed=25, spare_blocks=1,
+               kv_dtype="fp8", k_scale=(0.02, 0.006, 0.011), v_scale=(0.004, 0.03, 0.0125),
+               query_lens=[9, 18]),
     ]
 
 
@@ -567,9 +587,70 @@ def check_prefill_one_row_is_decode(lib):
     assert pf.tobytes() == dec.tobytes()
 
 
+def check_head_scales(lib):
+    """Per-kv-head fp8 scales.  (1) Each kv-head with its own scale attends exactly as
+    that head alone (its slice of the pool, its q-heads) with that scale as the pool's
+    one scale, bit for bit, in decode and in prefill.  (2) An unusable scale (0, < 0,
+    inf, NaN) in one head poisons exactly that head: its q-heads' rows are NaN (decode
+    and prefill) and its appended codes are the NaN code 0x7F; every other head is
+    unchanged bit for bit."""
+    for spec, prefill in ((small_specs()[6], False), (prefill_specs()[4], True)):
+        w = W.build(spec)
+        kp, vp = appended(w, lib)
+        run = oracle_prefill if prefill else oracle_paged
+        full, _ = run(w, kp, vp, lib=lib)
+        G = w.num_q_heads // w.num_kv_heads
+        for g in range(w.num_kv_heads):
+            heads = slice(g * G, (g + 1) * G)
+            q1 = np.ascontiguousarray(w.q[:, heads])
+            k1, v1 = np.ascontiguousarray(kp[:, g:g + 1]), np.ascontiguousarray(vp[:, g:g + 1])
+            kw = dict(lib=lib, q_dtype=w.dtype, k_scale=float(w.k_scale[g]),
+                      v_scale=float(w.v_scale[g]))
+            if prefill:
+                one, _ = O.prefill_paged(q1, k1, v1, w.kv_dtype, w.query_start, w.block_tables,
+                                         w.context_lens, w.scale, **kw)
+            else:
+                one, _ = O.decode_paged(q1, k1, v1, w.kv_dtype, w.block_tables, w.context_lens,
+                                        w.scale, **kw)
+            assert one.tobytes() == np.ascontiguousarray(full[:, heads]).tobytes(), (spec.name, g)
+        for bad in (0.0, -0.5, np.inf, np.nan):
+            for which in ("k", "v"):
+                ks, vs = w.k_scale.copy(), w.v_scale.copy()
+                (ks if which == "k" else vs)[1] = bad
+                if prefill:
+                    got, _ = O.prefill_paged(w.q, kp, vp, w.kv_dtype, w.query_start,
+                                             w.block_tables, w.context_lens, w.scale, lib=lib,
+                                             q_dtype=w.dtype, k_scale=ks, v_scale=vs)
+                else:
+                    got, _ = O.decode_paged(w.q, kp, vp, w.kv_dtype, w.block_tables,
+                                            w.context_lens, w.scale, lib=lib, q_dtype=w.dtype,
+                                            k_scale=ks, v_scale=vs)
+                assert np.isnan(got[:, G:2 * G]).all(), (spec.name, bad, which)
+                keep = np.r_[0:G, 2 * G:w.num_q_heads]
+                assert got[:, keep].tobytes() == full[:, keep].tobytes()
+    # append: the bad head's rows are NaN codes, the others as with good scales
+    w = W.build(small_specs()[6])
+    kp0, vp0 = w.host_pools()
+    good_k, good_v = appended(w, lib)
+    ks = w.k_scale.copy()
+    ks[2] = np.nan
+    vs = w.v_scale.copy()
+    vs[0] = 0.0
+    k2, v2 = O.cache_append(kp0, vp0, w.k_new, w.v_new, w.slot_mapping, w.kv_dtype, lib=lib,
+                            act_dtype=w.dtype, k_scale=ks, v_scale=vs)
+    for i, sl in enumerate(w.slot_mapping.tolist()):
+        if sl < 0:
+            continue
+        blk, off = sl // BLOCK, sl % BLOCK
+        assert (k2[blk, 2, off] == 0x7F).all() and (v2[blk, 0, :, off] == 0x7F).all()
+    k2[:, 2], good_k[:, 2] = 0, 0
+    v2[:, 0], good_v[:, 0] = 0, 0
+    assert k2.tobytes() == good_k.tobytes() and v2.tobytes() == good_v.tobytes()
+
+
 ALL_CHECKS = [check_widen_f16, check_widen_bf16, check_widen_fp8, check_encode_fp8,
               check_append, check_bruteforce,
               check_permutation, check_weight_sum, check_closed_forms, check_split_combine,
               check_kv_size, check_block_table_example, check_prefill_sdpa,
               check_prefill_bruteforce, check_prefill_chunked_prompt, check_prefill_weight_sum,
-              check_prefill_one_row_is_decode, check_copy_blocks]
+              check_prefill_one_row_is_decode, check_copy_blocks, check_head_scales]

@@ -46,7 +46,17 @@ MUTANTS = {
                                   "if (a >= 448.0f)\n        return sign | 0x7f;"),
     "fp8_k_scale_dropped": ("return widen_at(P->k_pool, idx, P->dtype) * P->k_scale;",
                             "return widen_at(P->k_pool, idx, P->dtype);"),
-    "fp8_append_scale_multiplied": ("encode_e4m3(vx / v_scale)", "encode_e4m3(vx * v_scale)"),
+    "fp8_append_scale_multiplied": ("encode_e4m3(vx / vs)", "encode_e4m3(vx * vs)"),
+    "fp8_head_scale_of_first_head": (
+        "double ks = A->k_head_scales ? (double)A->k_head_scales[kvh] : A->k_scale;",
+        "double ks = A->k_head_scales ? (double)A->k_head_scales[0] : A->k_scale;"),
+    "fp8_v_head_scale_from_k": (
+        "double vs = A->v_head_scales ? (double)A->v_head_scales[kvh] : A->v_scale;",
+        "double vs = A->v_head_scales ? (double)A->k_head_scales[kvh] : A->v_scale;"),
+    "fp8_append_head_scale_of_next_head": (
+        "float ks = k_head_scales ? k_head_scales[h] : k_scale;",
+        "float ks = k_head_scales ? k_head_scales[(h + 1) % num_kv_heads] : k_scale;"),
+    "fp8_bad_head_scale_not_poisoned": ("if (!scale_ok(ks) || !scale_ok(vs)) {", "if (0) {"),
     "prefill_causal_mask_dropped": ("n = pos < 0 ? 0 : pos + 1;", "n = pos < 0 ? 0 : n;"),
     "prefill_own_token_excluded": ("n = pos < 0 ? 0 : pos + 1;", "n = pos < 0 ? 0 : pos;"),
     "prefill_upper_left_alignment": ("int pos = n - q_len + (r - A->q_start[b]);",
