@@ -38,9 +38,10 @@
  *     PA_FP8_E4M3 (OCP 8-bit float, 4 exponent bits, 3 fraction bits, max 448, no
  *     infinities).  q, out and the new rows use the pool's act_dtype; for f32/f16/bf16
  *     pools that is the pool's own type.  An fp8 pool holds codes c with K = c * k_scale
- *     and V = c * v_scale (per-tensor scales), q/out/new rows being f16 or bf16 (the
- *     pages' FP8 E4M3 inference format with per-tensor scaling, "Deep dive into vLLM
- *     06", FP8 section).  Arithmetic is fp32.
+ *     and V = c * v_scale, q/out/new rows being f16 or bf16 (the pages' FP8 E4M3
+ *     inference format with a scale per tensor, "Deep dive into vLLM 06", FP8 section).
+ *     The scale is either one per pool or one per kv-head (each head's slice of the
+ *     cache treated as its own tensor; see pa_kv_pool).  Arithmetic is fp32.
  *   - Calls on different streams touching disjoint buffers may run concurrently.
  *
  * Pool layout (one layer; K and V are two separate buffers of equal size):
@@ -82,9 +83,17 @@ typedef enum pa_dtype {
 /* One layer's paged KV pool.  block_size must be PA_BLOCK_SIZE; head_dim must be one
  * of 64, 128, 256 (64 or 128 for PA_F32).  dtype is the pools' element type;
  * act_dtype the type of q, out and the new rows: equal to dtype for f32/f16/bf16
- * pools, PA_F16 or PA_BF16 for fp8 pools.  k_scale, v_scale (fp8 pools only; finite,
- * > 0) turn stored codes into values: K = code * k_scale, V = code * v_scale; they are
- * ignored for other pools. */
+ * pools, PA_F16 or PA_BF16 for fp8 pools.
+ * Scales (fp8 pools only; ignored for other pools) turn stored codes into values:
+ *   k_head_scales, v_head_scales  NULL, or DEVICE arrays of num_kv_heads fp32 values
+ *                  (4-byte aligned): K of kv-head h = code * k_head_scales[h], and V
+ *                  likewise.  Read on the device by every call that uses the pool, so
+ *                  they may change between calls (and between replays of a captured
+ *                  graph) without touching the host.  A head whose scale is not finite
+ *                  and > 0 gets NaN codes on append and NaN outputs from decode and
+ *                  prefill; no other head is affected.
+ *   k_scale, v_scale  one scale for the whole pool (finite, > 0), used where the
+ *                  corresponding per-head array is NULL. */
 typedef struct pa_kv_pool {
     void *k_pool;
     void *v_pool;
@@ -96,10 +105,15 @@ typedef struct pa_kv_pool {
     int32_t act_dtype;
     float k_scale;
     float v_scale;
+    const float *k_head_scales;
+    const float *v_head_scales;
 } pa_kv_pool;
 
 /* Bytes of ONE of the two pools (K or V) for these dimensions; 0 if any argument is
- * invalid or unsupported.  Host-only, no device access. */
+ * invalid or unsupported.  Host-only, no device access.  This is one layer's K (or
+ * V) share of the pages' KV-cache size, 2 * L * H * d_h * S * B * dtype_size
+ * (LLM-101-CN "推理优化", section "KV Cache 的显存计算"), taken at L = 1 and for one of
+ * K and V, with num_blocks * 16 token slots in place of S * B. */
 size_t pa_pool_bytes(int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
                      int32_t dtype);
 /* (dtype is the pools' element type: 4, 2, 2 or 1 bytes per element.) */
@@ -110,10 +124,10 @@ size_t pa_pool_bytes(int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
  *   slot_mapping   [num_tokens] int32, device: row i goes to physical block
  *                  slot_mapping[i] / 16, row slot_mapping[i] % 16, for every kv-head.
  * Bytes are copied unchanged; an fp8 pool instead stores the E4M3 code of
- * x / k_scale (x / v_scale), the quotient taken in IEEE fp32 and rounded to the
- * nearest code (ties to even), magnitudes >= 448 saturating to +-448 and NaN kept
- * NaN ("Deep dive into vLLM 06", kernel fusion: KV-cache write fused with
- * quantisation).  A negative slot means "no row" (padding) and is skipped.  A slot
+ * x / s, s being the row's kv-head scale for K (for V), the quotient taken in IEEE
+ * fp32 and rounded to the nearest code (ties to even), magnitudes >= 448 saturating
+ * to +-448 and NaN kept NaN ("Deep dive into vLLM 06", kernel fusion: KV-cache write
+ * fused with quantisation).  A negative slot means "no row" (padding) and is skipped.  A slot
  * >= num_blocks * 16 is also skipped (never written), so a bad slot cannot corrupt
  * memory outside the pool.  Two rows with the same slot race (caller
  * error).  num_tokens == 0 is a valid no-op; num_tokens * num_kv_heads above 2^34
@@ -121,11 +135,14 @@ size_t pa_pool_bytes(int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
 pa_status pa_cache_append(const pa_kv_pool *pool, const void *k_new, const void *v_new,
                           const int32_t *slot_mapping, int32_t num_tokens, void *stream);
 
-/* The partition length, in tokens, pa_decode uses when partition_tokens == 0 (auto).
- * A return value >= max_context_len means a single pass (no partials, no workspace).
- * Host-only; the same inputs always give the same answer.  Returns -1 on bad input. */
+/* The partition length, in tokens, pa_decode uses when partition_tokens == 0 (auto)
+ * for a pool of this head_dim (the waves per workgroup, and so the longest partition,
+ * depend on it).  A return value >= max_context_len means a single pass (no partials,
+ * no workspace).  Host-only; the same inputs always give the same answer.  Returns -1
+ * on bad input. */
 int32_t pa_decode_partition_tokens(int32_t num_seqs, int32_t num_q_heads,
-                                   int32_t num_kv_heads, int32_t max_context_len);
+                                   int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t max_context_len);
 
 /* A partition length for pa_decode / pa_decode_append planned from the batch's context
  * lengths as the host knows them (a serving scheduler tracks each request's KV length:
@@ -143,8 +160,12 @@ int32_t pa_decode_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_hea
                        int32_t head_dim, const int32_t *context_lens_host);
 
 /* Workspace bytes pa_decode needs for these arguments (partition_tokens as passed to
- * pa_decode, 0 = auto).  0 when the call runs in a single pass.  Returns SIZE_MAX on
- * invalid arguments.  Host-only. */
+ * pa_decode, 0 = auto): the Flash-Decoding partials of a split KV axis, one
+ * unnormalised output row and its running max and normaliser per (sequence, q-head,
+ * partition), all fp32 ("Deep dive into vLLM 06", Flash-Decoding section: each split
+ * yields a partial result with its own max and sum, merged afterwards), i.e.
+ * num_seqs * num_q_heads * partitions * (head_dim + 2) * 4 bytes.  0 when the call
+ * runs in a single pass.  Returns SIZE_MAX on invalid arguments.  Host-only. */
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t max_context_len,
                                  int32_t partition_tokens);

@@ -36,7 +36,8 @@ class PaKvPool(ctypes.Structure):
                 ("num_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32),
                 ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("act_dtype", ctypes.c_int32),
-                ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float)]
+                ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float),
+                ("k_head_scales", ctypes.c_void_p), ("v_head_scales", ctypes.c_void_p)]
 
 
 _lib = None
@@ -56,7 +57,7 @@ def load(path: str = LIB_PATH):
     lib.pa_pool_bytes.restype = ctypes.c_size_t
     lib.pa_cache_append.argtypes = [ctypes.POINTER(PaKvPool), P, P, P, I32, P]
     lib.pa_cache_append.restype = ctypes.c_int
-    lib.pa_decode_partition_tokens.argtypes = [I32, I32, I32, I32]
+    lib.pa_decode_partition_tokens.argtypes = [I32, I32, I32, I32, I32]
     lib.pa_decode_partition_tokens.restype = I32
     lib.pa_decode_plan.argtypes = [I32, I32, I32, I32, P]
     lib.pa_decode_plan.restype = I32
@@ -129,11 +130,23 @@ def _dev_ptr(t: Optional[torch.Tensor], name: str, dtype=None) -> Optional[int]:
     return t.data_ptr()
 
 
-def make_pool(k_pool, v_pool, act_dtype: Optional[torch.dtype] = None, k_scale: float = 1.0,
-              v_scale: float = 1.0) -> PaKvPool:
+def _scale_arg(x, name: str, num_kv_heads: int):
+    """A pool-wide scale (a number) -> (value, None); a per-kv-head scale (a CUDA float32
+    tensor of num_kv_heads entries) -> (1.0, device pointer)."""
+    if isinstance(x, torch.Tensor):
+        if x.numel() != num_kv_heads:
+            raise ValueError(f"{name} must hold one scale per kv-head ({num_kv_heads})")
+        return 1.0, _dev_ptr(x, name, torch.float32)
+    return float(x), None
+
+
+def make_pool(k_pool, v_pool, act_dtype: Optional[torch.dtype] = None, k_scale=1.0,
+              v_scale=1.0) -> PaKvPool:
     """k_pool [N][Hkv][16][d] and v_pool [N][Hkv][d][16], same dtype.  FP8 pools are
     uint8 (or float8_e4m3fn) tensors of E4M3 codes; act_dtype (f16/bf16) is then the
-    type of q, out and the new rows, and K = code * k_scale, V = code * v_scale."""
+    type of q, out and the new rows, and K = code * k_scale, V = code * v_scale, each
+    scale a number (the whole pool) or a CUDA float32 tensor [Hkv] (one per kv-head,
+    read on the device at every call)."""
     if k_pool.dim() != 4 or v_pool.dim() != 4:
         raise ValueError("pools are 4-D: k [N][Hkv][16][d], v [N][Hkv][d][16]")
     n, hkv, bs, d = k_pool.shape
@@ -150,8 +163,10 @@ def make_pool(k_pool, v_pool, act_dtype: Optional[torch.dtype] = None, k_scale: 
         k_scale = v_scale = 1.0
     else:
         raise ValueError(f"unsupported dtype {k_pool.dtype}")
+    ks, k_heads = _scale_arg(k_scale, "k_scale", hkv)
+    vs, v_heads = _scale_arg(v_scale, "v_scale", hkv)
     return PaKvPool(_dev_ptr(k_pool, "k_pool"), _dev_ptr(v_pool, "v_pool"), n, bs, hkv, d,
-                    code, act, float(k_scale), float(v_scale))
+                    code, act, ks, vs, k_heads, v_heads)
 
 
 _DTYPE_OF_CODE = {v: k for k, v in DTYPE_CODE.items()}
@@ -166,10 +181,10 @@ def pool_bytes(num_blocks: int, num_kv_heads: int, head_dim: int, dtype: torch.d
     return int(load().pa_pool_bytes(num_blocks, num_kv_heads, head_dim, code))
 
 
-def cache_append(k_pool, v_pool, k_new, v_new, slot_mapping, k_scale: float = 1.0,
-                 v_scale: float = 1.0) -> None:
+def cache_append(k_pool, v_pool, k_new, v_new, slot_mapping, k_scale=1.0, v_scale=1.0) -> None:
     """Write k_new/v_new [T][Hkv][d] rows into the pools at slot_mapping [T] (int32);
-    an fp8 pool stores the E4M3 codes of k_new / k_scale and v_new / v_scale."""
+    an fp8 pool stores the E4M3 codes of k_new / k_scale and v_new / v_scale (the
+    row's kv-head entry when a scale is a per-head tensor)."""
     act = k_new.dtype if k_pool.dtype in FP8_STORAGE else None
     pool = make_pool(k_pool, v_pool, act, k_scale, v_scale)
     T = int(slot_mapping.numel())
@@ -183,9 +198,9 @@ def cache_append(k_pool, v_pool, k_new, v_new, slot_mapping, k_scale: float = 1.
     _raise(st)
 
 
-def partition_tokens(num_seqs: int, num_q_heads: int, num_kv_heads: int,
+def partition_tokens(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
                      max_context_len: int) -> int:
-    return int(load().pa_decode_partition_tokens(num_seqs, num_q_heads, num_kv_heads,
+    return int(load().pa_decode_partition_tokens(num_seqs, num_q_heads, num_kv_heads, head_dim,
                                                  max_context_len))
 
 
@@ -231,13 +246,13 @@ def _call_with_workspace(fn, args, workspace, device, dims):
 
 def decode(q, k_pool, v_pool, block_tables, context_lens, scale: float, max_context_len: int,
            partition_tokens: int = 0, out: Optional[torch.Tensor] = None,
-           workspace: Optional[torch.Tensor] = None, k_scale: float = 1.0,
-           v_scale: float = 1.0) -> torch.Tensor:
+           workspace: Optional[torch.Tensor] = None, k_scale=1.0, v_scale=1.0) -> torch.Tensor:
     """softmax(q K^T scale) V per sequence and q-head through the block tables.
 
     q [B][Hq][d]; block_tables [B][max_blocks] int32; context_lens [B] int32;
     max_context_len: host-side bound of context_lens.  Returns out [B][Hq][d] in q's
-    dtype.  For an fp8 pool, K = code * k_scale and V = code * v_scale.
+    dtype.  For an fp8 pool, K = code * k_scale and V = code * v_scale (numbers, or
+    per-kv-head CUDA float32 tensors).
     """
     act = q.dtype if k_pool.dtype in FP8_STORAGE else None
     pool = make_pool(k_pool, v_pool, act, k_scale, v_scale)
@@ -260,7 +275,7 @@ def decode(q, k_pool, v_pool, block_tables, context_lens, scale: float, max_cont
 def decode_append(q, k_pool, v_pool, k_new, v_new, block_tables, context_lens, scale: float,
                   max_context_len: int, partition_tokens: int = 0,
                   out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                  k_scale: float = 1.0, v_scale: float = 1.0) -> torch.Tensor:
+                  k_scale=1.0, v_scale=1.0) -> torch.Tensor:
     """One launch for a decode step: each sequence's new row (k_new / v_new [B][Hkv][d])
     becomes token context_lens[b] - 1 in the pool, then decode attention as decode()."""
     act = q.dtype if k_pool.dtype in FP8_STORAGE else None
@@ -286,7 +301,7 @@ def decode_append(q, k_pool, v_pool, k_new, v_new, block_tables, context_lens, s
 
 def prefill(q, k_pool, v_pool, query_start, block_tables, context_lens, scale: float,
             max_context_len: int, max_query_len: int, out: Optional[torch.Tensor] = None,
-            k_scale: float = 1.0, v_scale: float = 1.0) -> torch.Tensor:
+            k_scale=1.0, v_scale=1.0) -> torch.Tensor:
     """Causal attention of prompt-chunk queries over the paged cache.
 
     q [T][Hq][d]; query_start [B+1] int32 (rows of sequence b: query_start[b] ..

@@ -37,6 +37,16 @@ int32_t max_part_blocks(int32_t head_dim) { return pa::waves_per_group(head_dim)
 bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
 bool aligned4(const void *p) { return ((uintptr_t)p & 3) == 0; }
 
+// The per-head scale arrays the kernels see: only fp8 pools use them.
+const float *k_heads(const pa_kv_pool *pool)
+{
+    return pool->dtype == PA_FP8_E4M3 ? pool->k_head_scales : nullptr;
+}
+const float *v_heads(const pa_kv_pool *pool)
+{
+    return pool->dtype == PA_FP8_E4M3 ? pool->v_head_scales : nullptr;
+}
+
 pa_status check_pool(const pa_kv_pool *pool)
 {
     if (!pool || !pool->k_pool || !pool->v_pool)
@@ -54,8 +64,13 @@ pa_status check_pool(const pa_kv_pool *pool)
     if (pool->dtype == PA_FP8_E4M3) {
         if (pool->act_dtype != PA_F16 && pool->act_dtype != PA_BF16)
             return PA_ERR_UNSUPPORTED;
-        if (!(pool->k_scale > 0.f) || !(pool->v_scale > 0.f) || !isfinite(pool->k_scale) ||
-            !isfinite(pool->v_scale))
+        // a pool-wide scale must be valid where no per-head array replaces it; per-head
+        // values live on the device and are checked there (a bad one poisons its head)
+        if (!pool->k_head_scales && (!(pool->k_scale > 0.f) || !isfinite(pool->k_scale)))
+            return PA_ERR_INVALID_ARG;
+        if (!pool->v_head_scales && (!(pool->v_scale > 0.f) || !isfinite(pool->v_scale)))
+            return PA_ERR_INVALID_ARG;
+        if (!aligned4(pool->k_head_scales) || !aligned4(pool->v_head_scales))
             return PA_ERR_INVALID_ARG;
     } else if (pool->act_dtype != pool->dtype) {
         return PA_ERR_UNSUPPORTED;
@@ -171,6 +186,8 @@ pa_status pa_cache_append(const pa_kv_pool *pool, const void *k_new, const void 
     a.k_scale = pool->k_scale;
     a.v_scale = pool->v_scale;
     a.bf16 = pool->act_dtype == PA_BF16 ? 1 : 0;
+    a.k_head_scales = k_heads(pool);
+    a.v_head_scales = v_heads(pool);
     hipError_t e = pa::launch_append(pool->dtype, pool->act_dtype, pool->head_dim, a,
                                      static_cast<hipStream_t>(stream));
     return e == hipSuccess ? PA_OK : PA_ERR_HIP;
@@ -199,12 +216,12 @@ pa_status pa_copy_blocks(const pa_kv_pool *pool, const int32_t *pairs, int32_t n
 }
 
 int32_t pa_decode_partition_tokens(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                                   int32_t max_context_len)
+                                   int32_t head_dim, int32_t max_context_len)
 {
-    if (check_decode_scalars(num_seqs, num_q_heads, num_kv_heads, 128, max_context_len, 0) !=
-        PA_OK)
+    if (head_dim <= 0 || check_decode_scalars(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                              max_context_len, 0) != PA_OK)
         return -1;
-    return choose_part_blocks(num_seqs, num_q_heads, num_kv_heads, 128, max_context_len, 0) *
+    return choose_part_blocks(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len, 0) *
            kBlock;
 }
 
@@ -360,8 +377,11 @@ pa_status decode_impl(const pa_kv_pool *pool, const void *q, const void *k_new,
     a.part_blocks = pb;
     a.num_parts = parts;
     const bool fp8 = pool->dtype == PA_FP8_E4M3;
-    a.scale_log2 = scale * 1.4426950408889634f * (fp8 ? pool->k_scale : 1.0f);
+    // a per-head K scale multiplies scale * log2(e) on the device, in this same order
+    a.scale_log2 = scale * 1.4426950408889634f * (fp8 && !k_heads(pool) ? pool->k_scale : 1.0f);
     a.v_scale = fp8 ? pool->v_scale : 1.0f;
+    a.k_head_scales = k_heads(pool);
+    a.v_head_scales = v_heads(pool);
     a.split = parts > 1 ? 1 : 0;
     a.longest_first = (num_seqs > 1 && num_seqs <= pa::kLongestFirstMax) ? 1 : 0;
     a.k_new = k_new;
@@ -463,8 +483,10 @@ pa_status pa_prefill(const pa_kv_pool *pool, const void *q, void *out, int32_t n
     a.q_tile = q_tile;
     a.num_qtiles = (int32_t)qtiles;
     const bool fp8 = pool->dtype == PA_FP8_E4M3;
-    a.scale_log2 = scale * 1.4426950408889634f * (fp8 ? pool->k_scale : 1.0f);
+    a.scale_log2 = scale * 1.4426950408889634f * (fp8 && !k_heads(pool) ? pool->k_scale : 1.0f);
     a.v_scale = fp8 ? pool->v_scale : 1.0f;
+    a.k_head_scales = k_heads(pool);
+    a.v_head_scales = v_heads(pool);
     a.longest_first = (num_seqs > 1 && num_seqs <= pa::kLongestFirstMax) ? 1 : 0;
     hipError_t e = pa::launch_prefill(pool->dtype, pool->act_dtype, pool->head_dim, a,
                                       static_cast<hipStream_t>(stream));

@@ -14,7 +14,9 @@
 //
 // An fp8 pool stores OCP E4M3 codes of x / scale (the KV-cache write fused with its
 // quantisation, one of the fused kernels "Deep dive into vLLM 06" lists): the
-// division is IEEE fp32, the code rounds to nearest-even and saturates at 448.
+// division is IEEE fp32, the code rounds to nearest-even and saturates at 448.  The
+// scale is the row's kv-head entry of a per-head array when the pool has one, else the
+// pool's; a per-head scale that is not finite and > 0 stores NaN codes.
 #include <type_traits>
 
 #include "pa_common.h"
@@ -90,6 +92,8 @@ __global__ __launch_bounds__(256) void pa_cache_append_fp8_kernel(AppendArgs a)
     const size_t blk = (size_t)(slot / kBlock);
     const int off = slot % kBlock;
     const size_t tile = (blk * a.num_kv_heads + h) * (size_t)kBlock * D;   // bytes
+    const float ks = head_scale(a.k_head_scales, a.k_scale, h);
+    const float vs = head_scale(a.v_head_scales, a.v_scale, h);
     uint32_t kc[2] = {0u, 0u};
     uint8_t *vdst = static_cast<uint8_t *>(a.v_pool) + tile + (size_t)c * 8 * kBlock + off;
 #pragma unroll
@@ -98,8 +102,8 @@ __global__ __launch_bounds__(256) void pa_cache_append_fp8_kernel(AppendArgs a)
         const uint32_t vw = (vv[j / 2] >> (16 * (j & 1))) & 0xFFFFu;
         const float kx = a.bf16 ? __uint_as_float(kw << 16) : (float)__builtin_bit_cast(_Float16, (uint16_t)kw);
         const float vx = a.bf16 ? __uint_as_float(vw << 16) : (float)__builtin_bit_cast(_Float16, (uint16_t)vw);
-        kc[j / 4] |= e4m3_code(__fdiv_rn(kx, a.k_scale)) << (8 * (j & 3));
-        vdst[j * kBlock] = (uint8_t)e4m3_code(__fdiv_rn(vx, a.v_scale));
+        kc[j / 4] |= e4m3_scaled(kx, ks) << (8 * (j & 3));
+        vdst[j * kBlock] = (uint8_t)e4m3_scaled(vx, vs);
     }
     *reinterpret_cast<uint2 *>(static_cast<uint8_t *>(a.k_pool) + tile + (size_t)off * D +
                                (size_t)c * 8) = make_uint2(kc[0], kc[1]);
@@ -154,6 +158,9 @@ __global__ __launch_bounds__(256) void pa_cache_append_group_kernel(AppendArgs a
     for (int j = 1; j < kBlock; ++j)
         whole = whole && s_slot[j] == s0 + j;
 
+    // fp8 pools: this kv-head's scales (per-head arrays, else the pool's)
+    const float ks = DT == DT_FP8 ? head_scale(a.k_head_scales, a.k_scale, h) : 1.f;
+    const float vs = DT == DT_FP8 ? head_scale(a.v_head_scales, a.v_scale, h) : 1.f;
     auto conv = [&](In x, float scale) -> Out {
         if constexpr (DT == DT_FP8)
             return (Out)e4m3_of_16(x, a.bf16 != 0, scale);
@@ -179,7 +186,7 @@ __global__ __launch_bounds__(256) void pa_cache_append_group_kernel(AppendArgs a
             Out run[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                run[e] = conv(kx[e], a.k_scale);
+                run[e] = conv(kx[e], ks);
                 s_v[j][col + e] = vx[e];
             }
             store_run(kpool + tile + (size_t)j * D + col, run);
@@ -191,7 +198,7 @@ __global__ __launch_bounds__(256) void pa_cache_append_group_kernel(AppendArgs a
             Out run[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                run[e] = conv(s_v[t0 + e][d], a.v_scale);
+                run[e] = conv(s_v[t0 + e][d], vs);
             store_run(vpool + tile + (size_t)d * kBlock + t0, run);
         }
         return;
@@ -218,7 +225,7 @@ __global__ __launch_bounds__(256) void pa_cache_append_group_kernel(AppendArgs a
         Out run[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-            run[e] = conv(kx[e], a.k_scale);
+            run[e] = conv(kx[e], ks);
         const size_t tile = ((size_t)(slot / kBlock) * a.num_kv_heads + h) * kBlock * D;
         store_run(kpool + tile + (size_t)(slot % kBlock) * D + col, run);
     }
@@ -229,7 +236,7 @@ __global__ __launch_bounds__(256) void pa_cache_append_group_kernel(AppendArgs a
         if (slot < 0 || (int64_t)slot >= slots)
             continue;
         const size_t tile = ((size_t)(slot / kBlock) * a.num_kv_heads + h) * kBlock * D;
-        vpool[tile + (size_t)d * kBlock + slot % kBlock] = conv(s_v[j][d], a.v_scale);
+        vpool[tile + (size_t)d * kBlock + slot % kBlock] = conv(s_v[j][d], vs);
     }
 }
 

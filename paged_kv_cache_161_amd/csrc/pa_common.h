@@ -46,6 +46,10 @@ struct DecodeArgs {
     float k_quant;                    // fp8 pools: stored code = E4M3(x / scale)
     float v_quant;
     int32_t act_bf16;                 // fp8 pools: new rows are bf16 (else f16)
+    // fp8 pools: per-kv-head scales ([hkv], device) or null.  A non-null k_head_scales
+    // multiplies scale_log2 and replaces k_quant for its head (v likewise v_scale).
+    const float *k_head_scales;
+    const float *v_head_scales;
 };
 
 // Batches up to this size are dispatched longest sequence first.
@@ -63,7 +67,24 @@ struct AppendArgs {
     float k_scale;                    // fp8 pools: stored code = E4M3(x / scale)
     float v_scale;
     int32_t bf16;                     // fp8 pools: new rows are bf16 (else f16)
+    const float *k_head_scales;       // fp8 pools: [hkv] per-head scales, or null
+    const float *v_head_scales;
 };
+
+// The scale a kv-head's K (or V) uses: its per-head entry when the array is given,
+// else the pool's.  A per-head value that is not finite and > 0 is returned as is;
+// scale_ok() tells the kernels to poison that head.
+__device__ __forceinline__ float head_scale(const float *per_head, float pool_scale, int head)
+{
+    return per_head ? per_head[head] : pool_scale;
+}
+__device__ __forceinline__ bool scale_ok(float s) { return s > 0.f && s <= 3.402823466e38f; }
+
+// A float every lane of the wave holds alike, moved to a scalar register.
+__device__ __forceinline__ float uniform(float x)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
+}
 
 // Launchers (return hipSuccess or the launch error).
 // dtype: the pools' element type; act_dtype: q / out / new rows (== dtype except for

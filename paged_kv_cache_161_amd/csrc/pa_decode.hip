@@ -232,7 +232,7 @@ struct Q32 {
 // FP8 (OCP E4M3) K/V with 16-bit q.  The same lane roles as the 16-bit tiles, with
 // half the bytes: each code converts exactly to the 16-bit MFMA type in registers
 // (every E4M3 value is a bf16 and an f16 value), the per-tensor scales are applied
-// in fp32 outside the MFMAs.  A lane loads K in 16-byte pieces (16 codes, two MFMAs'
+// in fp32 outside the MFMAs (one pair per pool, or per kv-head).  A lane loads K in 16-byte pieces (16 codes, two MFMAs'
 // worth): chunk c = 4j + g of its row, so one load instruction covers 64 contiguous
 // bytes of each of the 16 rows, as the 16-bit tile does.  MFMA i = 2j + h uses codes
 // 8h .. 8h+7 of piece j, and the q fragments follow the same e mapping.
@@ -567,6 +567,31 @@ __global__ __launch_bounds__(NW *kWave, min_waves_per_simd(DT, D, PF)) void pa_d
     // in a batch of equal lengths) and reissued otherwise.
     int b = pz;
     load_seq(b);
+    // This kv-head's scales: fp8 pools with per-head arrays read them here (a bad one
+    // poisons the head's outputs); otherwise the pool's, folded in on the host.
+    float sl_h = a.scale_log2, vs_h = a.v_scale, kq_h = a.k_quant, vq_h = a.v_quant;
+    bool bad_scale = false;
+    if constexpr (DT == DT_FP8) {
+        if (a.k_head_scales) {
+            const float s = a.k_head_scales[kvh];
+            bad_scale |= !scale_ok(s);
+            sl_h *= s;
+            kq_h = s;
+        }
+        if (a.v_head_scales) {
+            const float s = a.v_head_scales[kvh];
+            bad_scale |= !scale_ok(s);
+            vs_h = s;
+            vq_h = s;
+        }
+        if (bad_scale)
+            sl_h = 1.f;       // keeps the arithmetic tame; every output is NaN anyway
+        // workgroup-uniform: kept in scalar registers, as kernel arguments are
+        sl_h = uniform(sl_h);
+        vs_h = uniform(vs_h);
+        kq_h = uniform(kq_h);
+        vq_h = uniform(vq_h);
+    }
     int ctx = -1;
     if (a.longest_first) {
         int *s_ctx = reinterpret_cast<int *>(smem + NW * 32 + 16 + NW * min(16, a.group) * DP);
@@ -602,7 +627,7 @@ __global__ __launch_bounds__(NW *kWave, min_waves_per_simd(DT, D, PF)) void pa_d
         // partition 0 writes its answer: zeros for an empty context, NaN for an
         // inconsistent length.
         if (p == 0 && (bad_ctx || nblk_seq == 0)) {
-            const float fill = bad_ctx ? __builtin_nanf("") : 0.f;
+            const float fill = (bad_ctx || bad_scale) ? __builtin_nanf("") : 0.f;
             for (int idx = tid; idx < gs * D; idx += NW * kWave)
                 store_elem<AT>(a.out, ((size_t)b * a.num_q_heads + hq0) * D + idx, fill);
         }
@@ -636,7 +661,7 @@ __global__ __launch_bounds__(NW *kWave, min_waves_per_simd(DT, D, PF)) void pa_d
 #pragma unroll
     for (int n = 0; n < D / 16; ++n)
         o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-    bool tbl_bad = false;
+    bool tbl_bad = bad_scale;   // (workgroup-uniform)
 
     auto phys_of = [&](int i) -> size_t {
         int ph = __builtin_amdgcn_readlane(bt_lane, i);
@@ -665,7 +690,7 @@ __global__ __launch_bounds__(NW *kWave, min_waves_per_simd(DT, D, PF)) void pa_d
             }
         }
         f32x4 s = scores<DT, AT, D>(t, qf);
-        f32x4 x = s * a.scale_log2;
+        f32x4 x = s * sl_h;
         if (valid < kBlock) {
 #pragma unroll
             for (int j = 0; j < 4; ++j)
@@ -773,8 +798,8 @@ __global__ __launch_bounds__(NW *kWave, min_waves_per_simd(DT, D, PF)) void pa_d
                 if (e < D) {
                     Elem sk, sv;
                     if constexpr (DT == DT_FP8) {
-                        sk = (Elem)e4m3_of_16(nk[j], a.act_bf16 != 0, a.k_quant);
-                        sv = (Elem)e4m3_of_16(nv[j], a.act_bf16 != 0, a.v_quant);
+                        sk = (Elem)e4m3_of_16(nk[j], a.act_bf16 != 0, kq_h);
+                        sv = (Elem)e4m3_of_16(nv[j], a.act_bf16 != 0, vq_h);
                     } else {
                         sk = nk[j];
                         sv = nv[j];
@@ -832,11 +857,11 @@ __global__ __launch_bounds__(NW *kWave, min_waves_per_simd(DT, D, PF)) void pa_d
         }
         const size_t row = (size_t)b * a.num_q_heads + hq0 + h;
         if (!partial) {
-            const float val = any_bad ? qnan : (den > 0.f ? num / den * a.v_scale : 0.f);
+            const float val = any_bad ? qnan : (den > 0.f ? num / den * vs_h : 0.f);
             store_elem<AT>(a.out, row * D + e, val);
         } else {
             const size_t slot = row * a.num_parts + p;
-            a.ws_o[slot * D + e] = any_bad ? qnan : num * a.v_scale;
+            a.ws_o[slot * D + e] = any_bad ? qnan : num * vs_h;
             if (e == 0) {
                 a.ws_m[slot] = any_bad ? qnan : M;
                 a.ws_l[slot] = any_bad ? qnan : den;

@@ -25,13 +25,20 @@ __device__ __forceinline__ uint32_t e4m3_code(float x)
     return sign | ((rounded >> 20) - (120u << 3));
 }
 
+// E4M3 code of x / scale, the division in IEEE fp32; a scale that is not finite and
+// > 0 (a bad per-head scale) gives the NaN code.
+__device__ __forceinline__ uint32_t e4m3_scaled(float x, float scale)
+{
+    return (scale > 0.f && scale <= 3.402823466e38f) ? e4m3_code(__fdiv_rn(x, scale)) : 0x7Fu;
+}
+
 // A 16-bit activation element (bf16 bits when bf16, else f16 bits) -> E4M3 code of
-// x / scale, the division in IEEE fp32.
+// x / scale.
 __device__ __forceinline__ uint32_t e4m3_of_16(uint32_t bits, bool bf16, float scale)
 {
     const float x = bf16 ? __uint_as_float(bits << 16)
                          : (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
-    return e4m3_code(__fdiv_rn(x, scale));
+    return e4m3_scaled(x, scale);
 }
 
 }  // namespace pa

@@ -28,6 +28,10 @@ struct PrefillArgs {
     float scale_log2;                 // scale * log2(e) (* k_scale for fp8 pools), > 0
     float v_scale;
     int32_t longest_first;            // 1: sequences taken in order of estimated tile cost
+    // fp8 pools: per-kv-head scales ([hkv], device) or null; a non-null k_head_scales
+    // multiplies scale_log2 for its head, a non-null v_head_scales replaces v_scale.
+    const float *k_head_scales;
+    const float *v_head_scales;
 };
 
 // Prefill workgroup shape: waves and 16-row MFMA column blocks per wave.

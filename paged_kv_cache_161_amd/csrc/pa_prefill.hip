@@ -287,6 +287,28 @@ __global__ __launch_bounds__(NW *kWave, C * D <= 256 ? 2 : 1) void pa_prefill_ke
     const int key_end = bad_ctx ? 0 : max(0, first + n_here);   // keys [0, key_end)
     const int nsteps = (key_end + 31) / 32;
 
+    // This kv-head's scales: fp8 pools with per-head arrays read them here (a bad one
+    // poisons the head's rows); otherwise the pool's, folded in on the host.
+    float sl_h = a.scale_log2, vs_h = a.v_scale;
+    bool bad_scale = false;
+    if constexpr (DT == DT_FP8) {
+        if (a.k_head_scales) {
+            const float s = a.k_head_scales[kvh];
+            bad_scale |= !scale_ok(s);
+            sl_h *= s;
+        }
+        if (a.v_head_scales) {
+            const float s = a.v_head_scales[kvh];
+            bad_scale |= !scale_ok(s);
+            vs_h = s;
+        }
+        if (bad_scale)
+            sl_h = 1.f;       // keeps the arithmetic tame; every row is NaN anyway
+        // workgroup-uniform: kept in scalar registers, as kernel arguments are
+        sl_h = uniform(sl_h);
+        vs_h = uniform(vs_h);
+    }
+
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -321,7 +343,7 @@ __global__ __launch_bounds__(NW *kWave, C * D <= 256 ? 2 : 1) void pa_prefill_ke
     // scalar loads, whose wait does not hold up the vector loads in flight
     typedef const __attribute__((address_space(4))) int32_t const_i32;
     const_i32 *trow = (const_i32 *)(a.block_tables + (size_t)b * a.max_blocks);
-    bool bad = false;
+    bool bad = bad_scale;
 
     // ---- block ids of step s (blocks 2s, 2s+1), read one step before their loads are
     // issued and checked only then, so the scalar loads' latency is hidden.  Entries
@@ -367,7 +389,7 @@ __global__ __launch_bounds__(NW *kWave, C * D <= 256 ? 2 : 1) void pa_prefill_ke
                 u32x4 k[KL][2];
                 VRaw v[NDB];
             };
-            const float sl = a.scale_log2;
+            const float sl = sl_h;
             const float grow_thr = fminf(kRescaleSlack / sl, 3.0e38f);
             const u32x4 ones = {one_pair<AT>(), one_pair<AT>(), one_pair<AT>(), one_pair<AT>()};
             const int s_lo = (int)(((int64_t)nsteps * wave) / NW);
@@ -645,7 +667,7 @@ __global__ __launch_bounds__(NW *kWave, C * D <= 256 ? 2 : 1) void pa_prefill_ke
 #pragma unroll
                         for (int w = 0; w < NW; ++w)
                             l += s_l[c][w][r16];
-                        const float fo = l > 0.f ? a.v_scale / l : 0.f;
+                        const float fo = l > 0.f ? vs_h / l : 0.f;
 #pragma unroll
                         for (int n = 0; n < NDB; ++n) {
                             f32x4 v = o1[c][n] * fo;
@@ -797,7 +819,7 @@ __global__ __launch_bounds__(NW *kWave, C * D <= 256 ? 2 : 1) void pa_prefill_ke
         m_run[c] = -INFINITY;
         mneg[c] = 0.f;
     }
-    const float sl = a.scale_log2;           // > 0 (host-checked): max commutes with it
+    const float sl = sl_h;                   // > 0 (checked scales): max commutes with it
     // The running max is only a reference point: O and l are both scaled by 2^(-m sl),
     // which cancels in O / l whatever m is.  It is therefore moved only when a score
     // exceeds it by more than 2^kRescaleSlack in the exp2 domain; weights stay at most
@@ -1021,7 +1043,7 @@ __global__ __launch_bounds__(NW *kWave, C * D <= 256 ? 2 : 1) void pa_prefill_ke
         if (orow[c] < 0)
             continue;
         const float l = lacc[c][0];
-        const float f = l > 0.f ? a.v_scale / l : 0.f;
+        const float f = l > 0.f ? vs_h / l : 0.f;
 #pragma unroll
         for (int n = 0; n < NDB; ++n) {
             f32x4 v = o[c][n] * f;

@@ -25,8 +25,14 @@ def from_dev(t, dtype):
     return t.numpy()
 
 
-def scales(w):
-    return dict(k_scale=float(w.k_scale), v_scale=float(w.v_scale))
+def scales(w, device="cuda"):
+    """The workload's fp8 scales as the binding takes them: numbers for one scale per
+    pool, CUDA float32 tensors for one scale per kv-head."""
+    def one(x):
+        if np.ndim(x) == 0:
+            return float(x)
+        return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(device)
+    return dict(k_scale=one(w.k_scale), v_scale=one(w.v_scale))
 
 
 def widen(a, dtype):

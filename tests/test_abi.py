@@ -100,7 +100,7 @@ def test_decode_rejects_bad_arguments(lib):
     # block counts of the largest context stay in int32
     assert _decode(lib, _pool(), max_ctx=2 ** 31 - 1) == unsup
     assert lib.pa_decode_workspace_bytes(2, 4, 2, 128, 2 ** 31 - 1, 0) == 2 ** 64 - 1
-    assert lib.pa_decode_partition_tokens(2, 4, 2, 2 ** 31 - 1) == -1
+    assert lib.pa_decode_partition_tokens(2, 4, 2, 128, 2 ** 31 - 1) == -1
     lens = (ctypes.c_int32 * 2)(5, 2 ** 31 - 1)
     assert lib.pa_decode_plan(2, 4, 2, 128, lens) == -1
 
@@ -169,7 +169,7 @@ def test_append_rejects_bad_arguments(lib):
 
 
 def test_partition_choice_is_deterministic_and_sane(lib):
-    f = lib.pa_decode_partition_tokens
+    f = lambda n, hq, hkv, mx: lib.pa_decode_partition_tokens(n, hq, hkv, 128, mx)
     # one sequence of 37 tokens: single pass
     assert f(1, 4, 1, 37) >= 37
     # 32 x 4096 GQA-8: 256 (sequence, kv-head) units already give one workgroup per CU,
@@ -191,7 +191,7 @@ def test_decode_plan(lib):
         arr = (ctypes.c_int32 * max(1, len(lens)))(*lens)
         return lib.pa_decode_plan(len(lens), hq, hkv, d, arr)
 
-    auto = lambda hq, hkv, n, mx: lib.pa_decode_partition_tokens(n, hq, hkv, mx)
+    auto = lambda hq, hkv, n, mx: lib.pa_decode_partition_tokens(n, hq, hkv, 128, mx)
     # equal lengths: the automatic choice
     assert plan(64, 8, 128, [4096] * 32) == auto(64, 8, 32, 4096) == 4096
     assert plan(32, 8, 128, [8160] * 64) == auto(32, 8, 64, 8160)
@@ -222,7 +222,7 @@ def test_decode_plan(lib):
 def test_workspace_matches_partitions(lib):
     ws = lib.pa_decode_workspace_bytes
     assert ws(1, 4, 1, 64, 37, 0) == 0
-    pt = lib.pa_decode_partition_tokens(32, 8, 1, 4096)
+    pt = lib.pa_decode_partition_tokens(32, 8, 1, 128, 4096)
     parts = -(-4096 // pt)
     assert parts > 1
     assert ws(32, 8, 1, 128, 4096, 0) == 32 * 8 * parts * (128 + 2) * 4

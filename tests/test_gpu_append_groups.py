@@ -75,6 +75,13 @@ def test_group_append_bit_exact(kv, act, d, hkv):
     sm = slot_mapping(rng)
     T = sm.size
     k_scale, v_scale = (0.0117, 0.0093) if kv == "fp8" else (1.0, 1.0)
+    if kv == "fp8" and hkv == 3:                      # one scale per kv-head
+        k_scale = np.array([0.0117, 0.03, 0.005], np.float32)
+        v_scale = np.array([0.0093, 0.002, 0.04], np.float32)
+    dev_scale = {"k_scale": k_scale, "v_scale": v_scale}
+    if np.ndim(k_scale):
+        dev_scale = {n: torch.from_numpy(x).cuda() for n, x in
+                     (("k_scale", k_scale), ("v_scale", v_scale))}
     kn = rng.standard_normal((T, hkv, d)).astype(np.float32) * 0.5
     vn = rng.standard_normal((T, hkv, d)).astype(np.float32) * 0.5
     if kv == "fp8":
@@ -89,7 +96,7 @@ def test_group_append_bit_exact(kv, act, d, hkv):
                             v_scale=v_scale)
     kd, vd = U.to_dev(kp, kv), U.to_dev(vp, kv)
     PA.cache_append(kd, vd, U.to_dev(kn, act), U.to_dev(vn, act),
-                    torch.from_numpy(sm).cuda(), k_scale=k_scale, v_scale=v_scale)
+                    torch.from_numpy(sm).cuda(), **dev_scale)
     torch.cuda.synchronize()
     assert U.from_dev(kd, kv).tobytes() == ke.tobytes()
     assert U.from_dev(vd, kv).tobytes() == ve.tobytes()

@@ -102,6 +102,16 @@ SMALL = [
            kv_dtype="fp8", k_scale=0.0117, v_scale=0.0093),
     W.Spec("f16_mqa_g64_d128", "f16", 64, 1, 128, [1000, 64, 513, 0, 2], seed=117,
            spare_blocks=1),
+    # FP8 pools with one K and one V scale per kv-head, all different
+    W.Spec("fp8_heads_bf16_g8_d128", "bf16", 16, 2, 128, [1, 15, 16, 17, 100, 257], seed=118,
+           spare_blocks=3, kv_dtype="fp8", k_scale=(0.0117, 0.02), v_scale=(0.0093, 0.004)),
+    W.Spec("fp8_heads_f16_g4_d64", "f16", 12, 3, 64, [40, 1, 96, 0], seed=119, spare_blocks=1,
+           kv_dtype="fp8", k_scale=(0.02, 0.008, 0.0125), v_scale=(0.004, 0.011, 0.0093)),
+    W.Spec("fp8_heads_bf16_g32_d128", "bf16", 64, 2, 128, [129, 31, 700], seed=120,
+           spare_blocks=1, kv_dtype="fp8", k_scale=(0.0117, 0.03), v_scale=(0.02, 0.0093)),
+    W.Spec("fp8_heads_bf16_g8_d256", "bf16", 32, 4, 256, [300, 7], seed=121, spare_blocks=1,
+           kv_dtype="fp8", k_scale=(0.0125, 0.006, 0.02, 0.01),
+           v_scale=(0.0125, 0.03, 0.004, 0.008)),
 ]
 
 
@@ -164,7 +174,7 @@ def test_decode_config(i):
     w = config(i)
     say(f"[decode] config {i} {w.spec.name} B={w.num_seqs} Hq={w.num_q_heads} "
         f"Hkv={w.num_kv_heads} d={w.head_dim} max_ctx={w.max_context_len} "
-        f"auto partition={PA.partition_tokens(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.max_context_len)}")
+        f"auto partition={PA.partition_tokens(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.max_context_len)}")
     ref = oracle_decode(w)
     got, _, _ = gpu_step(w)
     check(w, got, ref, f"config {i}")
@@ -281,9 +291,10 @@ def test_rejects_unsupported_partition():
 
 
 def test_split_workspace_reuse_and_garbage():
-    """The split-mode arrival counters need no initialisation: a garbage-filled
-    workspace, reused across calls whose partition counts differ, gives the same
-    results as fresh calls."""
+    """A workspace full of garbage, reused across calls whose partition counts
+    differ, gives oracle-correct results: every partial the reduce launch reads is
+    written by the partition launch of the same call, so the workspace needs no
+    initialisation."""
     specs = [SMALL[0], SMALL[7], SMALL[4]]
     ws = torch.full((1 << 22,), 0xA5, dtype=torch.uint8, device="cuda")
     for rep in range(3):
@@ -388,3 +399,62 @@ def test_decode_random_batches(i):
     for ptok in (plan, 64):
         got, _, _ = gpu_step(w, ptok)
         check(w, got, ref, f"dec_random_{i} p{ptok}")
+
+
+BAD_SCALES = [0.0, -0.5, float("inf"), float("nan")]
+
+
+@pytest.mark.parametrize("bad", BAD_SCALES, ids=["zero", "negative", "inf", "nan"])
+def test_bad_head_scale_poisons_only_that_head(bad):
+    """A per-head fp8 scale that is not finite and > 0 (one kv-head's K scale, another
+    case its V scale) makes exactly that head's rows NaN in decode (single pass and
+    split), in the fused decode + append and in prefill, and its appended codes the NaN
+    code; every other head equals the run with good scales bit for bit."""
+    spec = SMALL[18]                                      # 3 kv-heads, G = 4, d = 64
+    w = W.build(spec)
+    G = w.num_q_heads // w.num_kv_heads
+    other = np.r_[0:G, 2 * G:w.num_q_heads]
+    d = U.device_inputs(w)
+    for which in ("k", "v"):
+        good = U.scales(w)
+        bad_sc = U.scales(w)
+        bad_sc[f"{which}_scale"] = bad_sc[f"{which}_scale"].clone()
+        bad_sc[f"{which}_scale"][1] = bad
+        say(f"[bad scale] {which}[1] = {bad}")
+        for ptok in (0, 16):
+            res = []
+            for sc in (good, bad_sc):
+                kp, vp = U.device_pools(w)
+                PA.cache_append(kp, vp, d["k_new"], d["v_new"], d["slot_mapping"], **sc)
+                out = PA.decode(d["q"], kp, vp, d["block_tables"], d["context_lens"],
+                                float(w.scale), w.max_context_len, ptok, **sc)
+                torch.cuda.synchronize()
+                res.append((U.int_view(out).cpu().numpy(),
+                            U.widen(U.from_dev(out, w.dtype), w.dtype), kp, vp))
+            (gi, _, gk, gv), (bi, bf, bk, bv) = res
+            assert np.isnan(bf[:, G:2 * G]).all()
+            assert np.array_equal(gi[:, other], bi[:, other])
+            pool = bk if which == "k" else bv
+            slots = w.slot_mapping[w.slot_mapping >= 0]
+            codes = U.from_dev(pool, "fp8")
+            for sl in slots.tolist():
+                row = codes[sl // BLOCK, 1, sl % BLOCK] if which == "k" else \
+                    codes[sl // BLOCK, 1, :, sl % BLOCK]
+                assert (row == 0x7F).all()
+            # everything but the bad head's appended rows is as with good scales
+            gpool = U.from_dev(gk if which == "k" else gv, "fp8").copy()
+            gpool[:, 1], codes[:, 1] = 0, 0
+            assert gpool.tobytes() == codes.tobytes()
+        # the fused step: the same outputs as the two calls
+        kp, vp = U.device_pools(w)
+        rows = np.flatnonzero(w.context_lens > 0)
+        kn = np.zeros((w.num_seqs,) + w.k_new.shape[1:], w.k_new.dtype)
+        vn = np.zeros_like(kn)
+        kn[rows], vn[rows] = w.k_new, w.v_new
+        out = PA.decode_append(d["q"], kp, vp, U.to_dev(kn, w.dtype), U.to_dev(vn, w.dtype),
+                               d["block_tables"], d["context_lens"], float(w.scale),
+                               w.max_context_len, **bad_sc)
+        torch.cuda.synchronize()
+        fi = U.int_view(out).cpu().numpy()
+        assert np.isnan(U.widen(U.from_dev(out, w.dtype), w.dtype)[:, G:2 * G]).all()
+        assert np.array_equal(fi[:, other], bi[:, other])

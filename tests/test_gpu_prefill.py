@@ -114,6 +114,14 @@ SMALL = [
            query_lens=_Q300),
     W.Spec("pf_single_seq_bf16", "bf16", 64, 8, 128, [530], seed=50, spare_blocks=1,
            query_lens=[300]),
+    # FP8 pools with one K and one V scale per kv-head: whole tiles, idle-wave tiles
+    # and split (decode-row) tiles
+    W.Spec("pf_fp8_heads_bf16", "bf16", 32, 4, 128, [300, 47, 1000, 5], seed=60,
+           spare_blocks=1, kv_dtype="fp8", k_scale=(0.0117, 0.03, 0.005, 0.02),
+           v_scale=(0.0093, 0.002, 0.04, 0.011), query_lens=[300, 12, 1, 5]),
+    W.Spec("pf_fp8_heads_f16_d64", "f16", 12, 3, 64, [77, 160, 2000], seed=61, spare_blocks=1,
+           kv_dtype="fp8", k_scale=(0.25, 0.0625, 0.1), v_scale=(0.0625, 0.2, 0.03),
+           query_lens=[77, 33, 2]),
 ]
 
 
@@ -366,3 +374,28 @@ def test_prefill_random_batches(i):
     say(f"  rows {got.shape[0]}: max {mx:.3e} mean {mean:.3e}")
     assert np.isfinite(got).all()
     assert ok, (mx, mean)
+
+
+def test_prefill_bad_head_scale_poisons_only_that_head():
+    """A per-head fp8 scale that is not finite and > 0 makes exactly that head's prefill
+    rows NaN (whole tiles and split tiles); the other heads' rows are unchanged."""
+    spec = next(s for s in SMALL if s.name == "pf_fp8_heads_bf16")
+    w = W.build(spec)
+    G = w.num_q_heads // w.num_kv_heads
+    other = np.r_[0:2 * G, 3 * G:w.num_q_heads]
+    good, _, _ = gpu_prefill(w)
+    for bad in (0.0, float("nan")):
+        sc = U.scales(w)
+        sc["v_scale"] = sc["v_scale"].clone()
+        sc["v_scale"][2] = bad
+        kp, vp = U.device_pools(w)
+        d = U.device_inputs(w)
+        PA.cache_append(kp, vp, d["k_new"], d["v_new"], d["slot_mapping"], **U.scales(w))
+        out = torch.full_like(d["q"], float("nan"))
+        PA.prefill(d["q"], kp, vp, torch.from_numpy(w.query_start).cuda(), d["block_tables"],
+                   d["context_lens"], float(w.scale), w.max_context_len, w.max_query_len,
+                   out=out, **sc)
+        torch.cuda.synchronize()
+        got = U.widen(U.from_dev(out, w.dtype), w.dtype)
+        assert np.isnan(got[:, 2 * G:3 * G]).all()
+        assert got[:, other].tobytes() == good[:, other].tobytes()
