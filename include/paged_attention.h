@@ -70,7 +70,8 @@ typedef enum pa_status {
     PA_ERR_UNSUPPORTED = 2,   /* valid but not built: dtype, head_dim, block size     */
     PA_ERR_WORKSPACE = 3,     /* workspace pointer null or smaller than required      */
     PA_ERR_HIP = 4,           /* the HIP runtime reported an error at launch          */
-    PA_ERR_OUT_OF_BLOCKS = 5  /* the block allocator has too few free blocks           */
+    PA_ERR_OUT_OF_BLOCKS = 5, /* the block allocator has too few free blocks           */
+    PA_ERR_SCRATCH = 6        /* pa_decode_noalloc: more than its static buffer holds  */
 } pa_status;
 
 typedef enum pa_dtype {
@@ -197,6 +198,27 @@ pa_status pa_decode(const pa_kv_pool *pool, const void *q, void *out, int32_t nu
                     int32_t max_blocks_per_seq, const int32_t *context_lens,
                     int32_t max_context_len, int32_t partition_tokens, void *workspace,
                     size_t workspace_bytes, void *stream);
+
+/* Bytes of the static device buffer pa_decode_noalloc keeps its partials in (16 MiB). */
+#define PA_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+
+/* pa_decode for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Arguments, results
+ * and errors are pa_decode's (the output is bit-identical to pa_decode's for the same
+ * arguments), without the workspace: the partials of a split KV axis go to a static
+ * device array of PA_NOALLOC_SCRATCH_BYTES bytes that the library holds on every GPU it
+ * runs on until the process ends.  The call allocates nothing (no hipMalloc, no
+ * library allocation).  A call that would need more than that array
+ * (pa_decode_workspace_bytes(...) > PA_NOALLOC_SCRATCH_BYTES) returns PA_ERR_SCRATCH and
+ * enqueues nothing.  The array belongs to the calling thread's current device, which
+ * must be the device of `stream`.  Every call on one GPU shares that GPU's array and
+ * leaves its partials there: calls that can overlap in time on one GPU (other streams,
+ * other host threads) race on it, so the caller must order them.  No clearing is
+ * needed: each call writes every partial it reads. */
+pa_status pa_decode_noalloc(const pa_kv_pool *pool, const void *q, void *out, int32_t num_seqs,
+                            int32_t num_q_heads, float scale, const int32_t *block_tables,
+                            int32_t max_blocks_per_seq, const int32_t *context_lens,
+                            int32_t max_context_len, int32_t partition_tokens, void *stream);
 
 /* A decode step's append and attention in one launch: for every sequence b with
  * context_lens[b] >= 1, its new row k_new[b], v_new[b] ([num_seqs][num_kv_heads]

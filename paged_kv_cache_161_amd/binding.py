@@ -18,11 +18,12 @@ LIB_PATH = os.path.join(HERE, "libpa_mi355x.so")
 HEADER_PATH = os.path.join(os.path.dirname(HERE), "include", "paged_attention.h")
 
 BLOCK_SIZE = 16
+NOALLOC_SCRATCH_BYTES = 16 << 20      # PA_NOALLOC_SCRATCH_BYTES
 PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3 = 0, 1, 2, 3
 DTYPE_CODE = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}
 FP8_STORAGE = (torch.uint8, torch.float8_e4m3fn)   # tensors holding OCP E4M3 codes
 STATUS = {0: "PA_OK", 1: "PA_ERR_INVALID_ARG", 2: "PA_ERR_UNSUPPORTED", 3: "PA_ERR_WORKSPACE",
-          4: "PA_ERR_HIP", 5: "PA_ERR_OUT_OF_BLOCKS"}
+          4: "PA_ERR_HIP", 5: "PA_ERR_OUT_OF_BLOCKS", 6: "PA_ERR_SCRATCH"}
 
 
 class PaError(RuntimeError):
@@ -66,6 +67,9 @@ def load(path: str = LIB_PATH):
     lib.pa_decode.argtypes = [ctypes.POINTER(PaKvPool), P, P, I32, I32, ctypes.c_float, P, I32,
                               P, I32, I32, P, ctypes.c_size_t, P]
     lib.pa_decode.restype = ctypes.c_int
+    lib.pa_decode_noalloc.argtypes = [ctypes.POINTER(PaKvPool), P, P, I32, I32, ctypes.c_float,
+                                      P, I32, P, I32, I32, P]
+    lib.pa_decode_noalloc.restype = I32
     lib.pa_decode_append.argtypes = [ctypes.POINTER(PaKvPool), P, P, P, P, I32, I32,
                                      ctypes.c_float, P, I32, P, I32, I32, P, ctypes.c_size_t, P]
     lib.pa_decode_append.restype = I32
@@ -268,6 +272,31 @@ def decode(q, k_pool, v_pool, block_tables, context_lens, scale: float, max_cont
             max_context_len, partition_tokens]
     st = _call_with_workspace(load().pa_decode, args, workspace, q.device,
                               (B, hq, pool.num_kv_heads, d, max_context_len, partition_tokens))
+    _raise(st)
+    return out
+
+
+def decode_noalloc(q, k_pool, v_pool, block_tables, context_lens, scale: float,
+                   max_context_len: int, partition_tokens: int = 0,
+                   out: Optional[torch.Tensor] = None, k_scale=1.0,
+                   v_scale=1.0) -> torch.Tensor:
+    """decode() without a workspace and without allocating on the device (out must then
+    be given): the split partials live in the library's static per-GPU buffer of
+    NOALLOC_SCRATCH_BYTES.  Calls that overlap in time on one GPU race on that buffer."""
+    act = q.dtype if k_pool.dtype in FP8_STORAGE else None
+    pool = make_pool(k_pool, v_pool, act, k_scale, v_scale)
+    B, hq, d = q.shape
+    if d != pool.head_dim:
+        raise ValueError("q head_dim differs from the pool's")
+    if out is None:
+        raise ValueError("decode_noalloc allocates nothing: pass out")
+    act = _act_dtype(pool)
+    st = load().pa_decode_noalloc(ctypes.byref(pool), _dev_ptr(q, "q", act),
+                                  _dev_ptr(out, "out", act), B, hq, ctypes.c_float(scale),
+                                  _dev_ptr(block_tables, "block_tables", torch.int32),
+                                  block_tables.shape[1],
+                                  _dev_ptr(context_lens, "context_lens", torch.int32),
+                                  max_context_len, partition_tokens, _stream_handle(q.device))
     _raise(st)
     return out
 

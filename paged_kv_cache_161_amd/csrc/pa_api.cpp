@@ -5,6 +5,9 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 
 #include "../../include/paged_attention.h"
 #include "pa_common.h"
@@ -154,6 +157,7 @@ const char *pa_status_string(int32_t status)
     case PA_ERR_WORKSPACE: return "workspace missing or too small";
     case PA_ERR_HIP: return "HIP runtime error";
     case PA_ERR_OUT_OF_BLOCKS: return "not enough free blocks";
+    case PA_ERR_SCRATCH: return "needs more than pa_decode_noalloc's static scratch buffer";
     default: return "unknown status";
     }
 }
@@ -395,9 +399,58 @@ pa_status decode_impl(const pa_kv_pool *pool, const void *q, const void *k_new,
     return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
+// ---------------------------------------------------- allocation-free decode's buffer
+// pa_decode_noalloc keeps its split partials here instead of in a caller's workspace.
+// Each GPU the library runs on holds its own copy of the array until the process ends.
+// On the host, `scratch` names only a host-side stand-in: its device address on each
+// GPU comes from hipGetSymbolAddress, taken once per device with that device current,
+// and only that address is ever handed to a kernel.
+static __device__ __align__(256) unsigned char scratch[PA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// This thread's current device's address of `scratch` (looked up on its first use).
+pa_status current_device_scratch(void **ptr)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return PA_ERR_HIP;
+    void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+                return PA_ERR_HIP;
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *ptr = p;
+    return PA_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+pa_status pa_decode_noalloc(const pa_kv_pool *pool, const void *q, void *out, int32_t num_seqs,
+                            int32_t num_q_heads, float scale, const int32_t *block_tables,
+                            int32_t max_blocks_per_seq, const int32_t *context_lens,
+                            int32_t max_context_len, int32_t partition_tokens, void *stream)
+{
+    void *ws = nullptr;
+    pa_status st = current_device_scratch(&ws);
+    if (st != PA_OK)
+        return st;
+    // pa_decode's checks and launches, the static array as the workspace; the only
+    // workspace error left is a need beyond the array's size
+    st = decode_impl(pool, q, nullptr, nullptr, out, num_seqs, num_q_heads, scale, block_tables,
+                     max_blocks_per_seq, context_lens, max_context_len, partition_tokens, ws,
+                     PA_NOALLOC_SCRATCH_BYTES, stream);
+    return st == PA_ERR_WORKSPACE ? PA_ERR_SCRATCH : st;
+}
 
 pa_status pa_decode(const pa_kv_pool *pool, const void *q, void *out, int32_t num_seqs,
                     int32_t num_q_heads, float scale, const int32_t *block_tables,

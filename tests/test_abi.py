@@ -46,6 +46,7 @@ def test_status_strings(lib):
     for code in range(5):
         assert lib.pa_status_string(code)
     assert lib.pa_status_string(99) == b"unknown status"
+    assert b"scratch" in lib.pa_status_string(6)          # PA_ERR_SCRATCH
 
 
 def _pool(**kw):

@@ -1,0 +1,102 @@
+"""pa_decode_noalloc (the decode entry point that allocates nothing and keeps its split
+partials in the library's static per-GPU buffer) against pa_decode with a caller's
+workspace, through the C ABI.  Its kernels are pa_decode's, so outputs must be
+identical bit for bit; two calls in a row, the second smaller, show that the
+buffer's leftover contents never reach a result.  A call needing more than the buffer
+is refused before anything is enqueued."""
+import ctypes
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from paged_kv_cache_161_amd import binding as PA
+from paged_kv_cache_161_amd import workloads as W
+from tests import devutil as U
+
+pytestmark = pytest.mark.gpu
+
+PA_ERR_SCRATCH = 6
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def lib():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    return PA.load()
+
+
+def noalloc_call(lib, w, d, kp, vp, out, ptok):
+    """pa_decode_noalloc through the C ABI (ctypes), on torch's current stream."""
+    pool = PA.make_pool(kp, vp, d["q"].dtype if w.kv_dtype == "fp8" else None, **U.scales(w))
+    return lib.pa_decode_noalloc(ctypes.byref(pool), d["q"].data_ptr(), out.data_ptr(),
+                                 w.num_seqs, w.num_q_heads, ctypes.c_float(float(w.scale)),
+                                 d["block_tables"].data_ptr(), d["block_tables"].shape[1],
+                                 d["context_lens"].data_ptr(), w.max_context_len, ptok,
+                                 PA._stream_handle(d["q"].device))
+
+
+# (workload, partition tokens): each splits its longest sequences, so the partials go
+# through the static buffer; the second of each pair is the smaller call
+PAIRS = [
+    ((W.Spec("na_bf16_big", "bf16", 32, 4, 128, [2000, 1500, 700, 3000, 33, 0], seed=401,
+             spare_blocks=1), 256),
+     (W.Spec("na_bf16_small", "bf16", 16, 2, 128, [300, 90], seed=402, spare_blocks=1), 64)),
+    ((W.Spec("na_fp8_heads_big", "f16", 24, 3, 128, [4000, 1200, 2222], seed=403,
+             spare_blocks=1, kv_dtype="fp8", k_scale=(0.0117, 0.03, 0.006),
+             v_scale=(0.0093, 0.004, 0.02)), 512),
+     (W.Spec("na_fp8_small", "f16", 8, 2, 64, [100, 37], seed=404, spare_blocks=1,
+             kv_dtype="fp8", k_scale=0.02, v_scale=0.004), 32)),
+]
+
+
+@pytest.mark.parametrize("pair", PAIRS, ids=[p[0][0].name for p in PAIRS])
+def test_noalloc_equals_decode_twice_second_smaller(lib, pair):
+    for spec, ptok in pair:
+        w = W.build(spec)
+        need = PA.workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                                  w.max_context_len, ptok)
+        say(f"[noalloc] {spec.name} ptok={ptok} partials {need} B")
+        assert 0 < need <= PA.NOALLOC_SCRATCH_BYTES
+        d = U.device_inputs(w)
+        kp, vp = U.device_pools(w)
+        PA.cache_append(kp, vp, d["k_new"], d["v_new"], d["slot_mapping"], **U.scales(w))
+        ws = torch.full((need,), 0xA5, dtype=torch.uint8, device="cuda")
+        ref = PA.decode(d["q"], kp, vp, d["block_tables"], d["context_lens"], float(w.scale),
+                        w.max_context_len, ptok, workspace=ws, **U.scales(w))
+        out = torch.full_like(d["q"], float("nan"))
+        st = noalloc_call(lib, w, d, kp, vp, out, ptok)
+        torch.cuda.synchronize()
+        assert st == 0, PA.STATUS.get(st, st)
+        assert torch.equal(U.int_view(out), U.int_view(ref)), spec.name
+        got = U.widen(U.from_dev(out, w.dtype), w.dtype)
+        assert np.isfinite(got).all()
+
+
+def test_noalloc_refuses_more_than_its_buffer(lib):
+    """64 sequences x 64 q-heads x 8 partitions x (128 + 2) fp32 = 17.0 MB of partials,
+    above the 16 MiB buffer: PA_ERR_SCRATCH, output untouched.  Every pointer is a real,
+    consistent device buffer, so even a launch would stay in bounds."""
+    B, hq, hkv, d, ctx, ptok = 64, 64, 8, 128, 128, 16
+    assert B * hq * (ctx // ptok) * (d + 2) * 4 > PA.NOALLOC_SCRATCH_BYTES
+    nblk = B * ctx // 16
+    kp = torch.zeros((nblk, hkv, 16, d), dtype=torch.bfloat16, device="cuda")
+    vp = torch.zeros((nblk, hkv, d, 16), dtype=torch.bfloat16, device="cuda")
+    q = torch.zeros((B, hq, d), dtype=torch.bfloat16, device="cuda")
+    out = torch.full_like(q, 7.0)
+    bt = torch.arange(nblk, dtype=torch.int32, device="cuda").reshape(B, ctx // 16)
+    cl = torch.full((B,), ctx, dtype=torch.int32, device="cuda")
+    pool = PA.make_pool(kp, vp)
+    st = lib.pa_decode_noalloc(ctypes.byref(pool), q.data_ptr(), out.data_ptr(), B, hq,
+                               ctypes.c_float(0.088), bt.data_ptr(), bt.shape[1], cl.data_ptr(),
+                               ctx, ptok, PA._stream_handle(q.device))
+    torch.cuda.synchronize()
+    assert st == PA_ERR_SCRATCH
+    assert bool((out == 7.0).all())
+    with pytest.raises(PA.PaError):
+        PA.decode_noalloc(q, kp, vp, bt, cl, 0.088, ctx, ptok, out=out)
