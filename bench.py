@@ -256,9 +256,9 @@ def time_sub_batch(w, d, pools, k_rows, v_rows, idx, sc, n_launch, warmup, dev):
     vr = v_rows.index_select(0, sel).contiguous()
     ctx = w.context_lens[idx]
     max_ctx = int(ctx.max())
-    ptok = PA.plan_partition_tokens(w.num_q_heads, w.num_kv_heads, w.head_dim, ctx)
+    ptok = PA.plan_partition_tokens(w.num_q_heads, w.num_kv_heads, w.head_dim, ctx, w.kv_dtype)
     ws = torch.empty(max(PA.workspace_bytes(len(idx), w.num_q_heads, w.num_kv_heads,
-                                            w.head_dim, max_ctx, ptok), 1),
+                                            w.head_dim, max_ctx, ptok, w.kv_dtype), 1),
                      dtype=torch.uint8, device=dev)
     out = torch.empty_like(q)
     layers = len(pools)
@@ -494,9 +494,9 @@ def main():
     # the partition length a serving loop would plan from the host's context lengths
     # (pa_decode_plan), unless one is forced
     ptok = args.partition_tokens or PA.plan_partition_tokens(
-        w.num_q_heads, w.num_kv_heads, w.head_dim, w.context_lens)
+        w.num_q_heads, w.num_kv_heads, w.head_dim, w.context_lens, w.kv_dtype)
     ws_bytes = PA.workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim,
-                                  w.max_context_len, ptok)
+                                  w.max_context_len, ptok, w.kv_dtype)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     kv_bytes = w.logical_kv_bytes()
     uniq_bytes = w.unique_kv_bytes()

@@ -137,12 +137,12 @@ pa_status pa_cache_append(const pa_kv_pool *pool, const void *k_new, const void 
                           const int32_t *slot_mapping, int32_t num_tokens, void *stream);
 
 /* The partition length, in tokens, pa_decode uses when partition_tokens == 0 (auto)
- * for a pool of this head_dim (the waves per workgroup, and so the longest partition,
- * depend on it).  A return value >= max_context_len means a single pass (no partials,
- * no workspace).  Host-only; the same inputs always give the same answer.  Returns -1
- * on bad input. */
+ * for a pool of this head_dim and element type dtype (the pools' pa_dtype: the kernel,
+ * its waves per workgroup and so the longest partition depend on both).  A return value
+ * >= max_context_len means a single pass (no partials, no workspace).  Host-only; the
+ * same inputs always give the same answer.  Returns -1 on bad input. */
 int32_t pa_decode_partition_tokens(int32_t num_seqs, int32_t num_q_heads,
-                                   int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
                                    int32_t max_context_len);
 
 /* A partition length for pa_decode / pa_decode_append planned from the batch's context
@@ -155,20 +155,21 @@ int32_t pa_decode_partition_tokens(int32_t num_seqs, int32_t num_q_heads,
  * one round, it returns the automatic choice.  A batch of equal lengths gets the
  * automatic choice.  The lengths must be those passed on the
  * device to the call that uses the result (anything else is still correct, only
- * planned for other lengths).  Host-only; returns a positive multiple of 16, or -1 on
- * bad input. */
+ * planned for other lengths).  dtype is the pools' pa_dtype.  Host-only; returns a
+ * positive multiple of 16, or -1 on bad input. */
 int32_t pa_decode_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                       int32_t head_dim, const int32_t *context_lens_host);
+                       int32_t head_dim, int32_t dtype, const int32_t *context_lens_host);
 
 /* Workspace bytes pa_decode needs for these arguments (partition_tokens as passed to
  * pa_decode, 0 = auto): the Flash-Decoding partials of a split KV axis, one
  * unnormalised output row and its running max and normaliser per (sequence, q-head,
  * partition), all fp32 ("Deep dive into vLLM 06", Flash-Decoding section: each split
  * yields a partial result with its own max and sum, merged afterwards), i.e.
- * num_seqs * num_q_heads * partitions * (head_dim + 2) * 4 bytes.  0 when the call
- * runs in a single pass.  Returns SIZE_MAX on invalid arguments.  Host-only. */
+ * num_seqs * num_q_heads * partitions * (head_dim + 2) * 4 bytes, for pools of element
+ * type dtype.  0 when the call runs in a single pass.  Returns SIZE_MAX on invalid
+ * arguments.  Host-only. */
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                                 int32_t head_dim, int32_t max_context_len,
+                                 int32_t head_dim, int32_t dtype, int32_t max_context_len,
                                  int32_t partition_tokens);
 
 /* Decode attention for one layer (definitions as cited at the top of this file).

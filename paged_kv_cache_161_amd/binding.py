@@ -58,11 +58,11 @@ def load(path: str = LIB_PATH):
     lib.pa_pool_bytes.restype = ctypes.c_size_t
     lib.pa_cache_append.argtypes = [ctypes.POINTER(PaKvPool), P, P, P, I32, P]
     lib.pa_cache_append.restype = ctypes.c_int
-    lib.pa_decode_partition_tokens.argtypes = [I32, I32, I32, I32, I32]
+    lib.pa_decode_partition_tokens.argtypes = [I32, I32, I32, I32, I32, I32]
     lib.pa_decode_partition_tokens.restype = I32
-    lib.pa_decode_plan.argtypes = [I32, I32, I32, I32, P]
+    lib.pa_decode_plan.argtypes = [I32, I32, I32, I32, I32, P]
     lib.pa_decode_plan.restype = I32
-    lib.pa_decode_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32]
+    lib.pa_decode_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32, I32]
     lib.pa_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.pa_decode.argtypes = [ctypes.POINTER(PaKvPool), P, P, I32, I32, ctypes.c_float, P, I32,
                               P, I32, I32, P, ctypes.c_size_t, P]
@@ -202,19 +202,33 @@ def cache_append(k_pool, v_pool, k_new, v_new, slot_mapping, k_scale=1.0, v_scal
     _raise(st)
 
 
+_CODE_OF_NAME = {"f32": PA_F32, "f16": PA_F16, "bf16": PA_BF16, "fp8": PA_FP8_E4M3}
+
+
+def dtype_code(dtype) -> int:
+    """A pool element type as its pa_dtype code: a torch dtype (uint8 / float8_e4m3fn
+    for fp8 pools), a name ("f32", "f16", "bf16", "fp8") or the code itself."""
+    if isinstance(dtype, int):
+        return dtype
+    if isinstance(dtype, str):
+        return _CODE_OF_NAME[dtype]
+    return PA_FP8_E4M3 if dtype in FP8_STORAGE else DTYPE_CODE[dtype]
+
+
 def partition_tokens(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
-                     max_context_len: int) -> int:
+                     max_context_len: int, dtype=torch.bfloat16) -> int:
+    """pa_decode_partition_tokens for pools of element type dtype."""
     return int(load().pa_decode_partition_tokens(num_seqs, num_q_heads, num_kv_heads, head_dim,
-                                                 max_context_len))
+                                                 dtype_code(dtype), max_context_len))
 
 
 def plan_partition_tokens(num_q_heads: int, num_kv_heads: int, head_dim: int,
-                          context_lens_host) -> int:
+                          context_lens_host, dtype=torch.bfloat16) -> int:
     """pa_decode_plan: a partition length (tokens) for decode() / decode_append() from
-    the batch's context lengths as known on the host."""
+    the batch's context lengths as known on the host, for pools of element type dtype."""
     import numpy as np
     cl = np.ascontiguousarray(np.asarray(context_lens_host, dtype=np.int32))
-    r = load().pa_decode_plan(cl.size, num_q_heads, num_kv_heads, head_dim,
+    r = load().pa_decode_plan(cl.size, num_q_heads, num_kv_heads, head_dim, dtype_code(dtype),
                               cl.ctypes.data_as(ctypes.c_void_p))
     if r < 0:
         raise ValueError("invalid arguments to pa_decode_plan")
@@ -222,9 +236,12 @@ def plan_partition_tokens(num_q_heads: int, num_kv_heads: int, head_dim: int,
 
 
 def workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
-                    max_context_len: int, partition_tokens: int = 0) -> int:
+                    max_context_len: int, partition_tokens: int = 0,
+                    dtype=torch.bfloat16) -> int:
+    """pa_decode_workspace_bytes for pools of element type dtype."""
     n = int(load().pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
-                                             max_context_len, partition_tokens))
+                                             dtype_code(dtype), max_context_len,
+                                             partition_tokens))
     if n == ctypes.c_size_t(-1).value:
         raise PaError(1, "invalid arguments for pa_decode_workspace_bytes")
     return n
@@ -271,7 +288,8 @@ def decode(q, k_pool, v_pool, block_tables, context_lens, scale: float, max_cont
             block_tables.shape[1], _dev_ptr(context_lens, "context_lens", torch.int32),
             max_context_len, partition_tokens]
     st = _call_with_workspace(load().pa_decode, args, workspace, q.device,
-                              (B, hq, pool.num_kv_heads, d, max_context_len, partition_tokens))
+                              (B, hq, pool.num_kv_heads, d, max_context_len, partition_tokens,
+                               pool.dtype))
     _raise(st)
     return out
 
@@ -323,7 +341,8 @@ def decode_append(q, k_pool, v_pool, k_new, v_new, block_tables, context_lens, s
             block_tables.shape[1], _dev_ptr(context_lens, "context_lens", torch.int32),
             max_context_len, partition_tokens]
     st = _call_with_workspace(load().pa_decode_append, args, workspace, q.device,
-                              (B, hq, pool.num_kv_heads, d, max_context_len, partition_tokens))
+                              (B, hq, pool.num_kv_heads, d, max_context_len, partition_tokens,
+                               pool.dtype))
     _raise(st)
     return out
 

@@ -31,9 +31,20 @@ bool head_dim_ok(int32_t dtype, int32_t head_dim)
 
 size_t elem_bytes(int32_t dtype) { return dtype == PA_F32 ? 4 : (dtype == PA_FP8_E4M3 ? 1 : 2); }
 
-// Most blocks one wave may walk in one partition: the kernel keeps a wave's block ids
-// one per lane of a single register.
-int32_t max_part_blocks(int32_t head_dim) { return pa::waves_per_group(head_dim) * pa::kWave; }
+// Most blocks one partition may hold: the kernels keep the block ids a wave (or block
+// lane) walks one per lane of a single register, 64 per lane.
+int32_t max_part_blocks(int32_t dtype, int32_t head_dim, int32_t group)
+{
+    return pa::decode_lanes(dtype, head_dim, group) * pa::kWave;
+}
+
+// Partition workgroups per (sequence, kv-head, partition): one per
+// decode_chunks(dtype, head_dim, group) x 16 q-heads of the group.
+int64_t wg_chunks(int32_t dtype, int32_t head_dim, int32_t group)
+{
+    const int64_t hs = 16 * pa::decode_chunks(dtype, head_dim, group);
+    return (group + hs - 1) / hs;
+}
 
 // The kernels move pool tiles, q, out, new rows and workspace partials in 16-byte
 // vectors, and index arrays as 32-bit words.
@@ -83,7 +94,8 @@ pa_status check_pool(const pa_kv_pool *pool)
 
 // Partition length in blocks for a (validated) decode call; 0 on invalid input.
 int32_t choose_part_blocks(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                           int32_t head_dim, int32_t max_context_len, int32_t partition_tokens)
+                           int32_t head_dim, int32_t dtype, int32_t max_context_len,
+                           int32_t partition_tokens)
 {
     const int32_t max_blocks = (max_context_len + kBlock - 1) / kBlock;
     if (max_blocks == 0)
@@ -94,10 +106,10 @@ int32_t choose_part_blocks(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv
     // each workgroup streams long runs and no merge pass is needed when a sequence fits
     // one; cut finer only when that leaves fewer workgroups than the GPU has CUs, but
     // not below ~2 blocks per wave.
-    const int32_t nw = pa::waves_per_group(head_dim);
-    const int64_t chunks = (num_q_heads / num_kv_heads + 15) / 16;
-    const int64_t units = (int64_t)num_seqs * num_kv_heads * chunks;
-    const int64_t max_pb = max_part_blocks(head_dim);
+    const int32_t group = num_q_heads / num_kv_heads;
+    const int32_t nw = pa::decode_lanes(dtype, head_dim, group);
+    const int64_t units = (int64_t)num_seqs * num_kv_heads * wg_chunks(dtype, head_dim, group);
+    const int64_t max_pb = max_part_blocks(dtype, head_dim, group);
     int64_t parts = (max_blocks + max_pb - 1) / max_pb;
     if (units * parts < pa::kTargetGroups) {
         const int64_t fill = (pa::kTargetGroups + units - 1) / units;
@@ -109,16 +121,18 @@ int32_t choose_part_blocks(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv
     if (parts < 1)
         parts = 1;
     int32_t pb = (int32_t)((max_blocks + parts - 1) / parts);
-    if (pb > max_part_blocks(head_dim))
-        pb = max_part_blocks(head_dim);
+    if (pb > max_pb)
+        pb = (int32_t)max_pb;
     return pb;
 }
 
-// Host-side validation of pa_decode's scalar arguments.
+// Host-side validation of pa_decode's scalar arguments (dtype: the pools' element type).
 pa_status check_decode_scalars(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                               int32_t head_dim, int32_t max_context_len,
+                               int32_t head_dim, int32_t dtype, int32_t max_context_len,
                                int32_t partition_tokens)
 {
+    if (!dtype_ok(dtype) || head_dim <= 0)
+        return PA_ERR_INVALID_ARG;
     if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_context_len < 0)
         return PA_ERR_INVALID_ARG;
     if (max_context_len > INT32_MAX - kBlock)         // block counts stay in int32
@@ -127,12 +141,15 @@ pa_status check_decode_scalars(int32_t num_seqs, int32_t num_q_heads, int32_t nu
         return PA_ERR_INVALID_ARG;
     if (partition_tokens < 0 || partition_tokens % kBlock != 0)
         return PA_ERR_INVALID_ARG;
-    if (partition_tokens > 0 && partition_tokens / kBlock > max_part_blocks(head_dim))
+    const int32_t group = num_q_heads / num_kv_heads;
+    if (partition_tokens > 0 &&
+        partition_tokens / kBlock > max_part_blocks(dtype, head_dim, group))
         return PA_ERR_UNSUPPORTED;
     if (num_seqs > 65535)
         return PA_ERR_UNSUPPORTED;
-    const int64_t chunks = (num_q_heads / num_kv_heads + 15) / 16;
-    if ((int64_t)num_kv_heads * chunks > 65535)
+    // grid y of the partition kernel and of the reduce
+    if ((int64_t)num_kv_heads * wg_chunks(dtype, head_dim, group) > 65535 ||
+        (int64_t)num_kv_heads * ((group + 15) / 16) > 65535)
         return PA_ERR_UNSUPPORTED;
     return PA_OK;
 }
@@ -220,17 +237,18 @@ pa_status pa_copy_blocks(const pa_kv_pool *pool, const int32_t *pairs, int32_t n
 }
 
 int32_t pa_decode_partition_tokens(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                                   int32_t head_dim, int32_t max_context_len)
+                                   int32_t head_dim, int32_t dtype, int32_t max_context_len)
 {
-    if (head_dim <= 0 || check_decode_scalars(num_seqs, num_q_heads, num_kv_heads, head_dim,
-                                              max_context_len, 0) != PA_OK)
+    if (check_decode_scalars(num_seqs, num_q_heads, num_kv_heads, head_dim, dtype,
+                             max_context_len, 0) != PA_OK)
         return -1;
-    return choose_part_blocks(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len, 0) *
+    return choose_part_blocks(num_seqs, num_q_heads, num_kv_heads, head_dim, dtype,
+                              max_context_len, 0) *
            kBlock;
 }
 
 int32_t pa_decode_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                       int32_t head_dim, const int32_t *context_lens_host)
+                       int32_t head_dim, int32_t dtype, const int32_t *context_lens_host)
 {
     if (num_seqs < 0 || (num_seqs > 0 && !context_lens_host) || head_dim <= 0)
         return -1;
@@ -241,10 +259,11 @@ int32_t pa_decode_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_hea
         if (context_lens_host[b] > max_ctx)
             max_ctx = context_lens_host[b];
     }
-    if (check_decode_scalars(num_seqs, num_q_heads, num_kv_heads, head_dim, max_ctx, 0) != PA_OK)
+    if (check_decode_scalars(num_seqs, num_q_heads, num_kv_heads, head_dim, dtype, max_ctx, 0) !=
+        PA_OK)
         return -1;
     const int32_t auto_pb =
-        choose_part_blocks(num_seqs, num_q_heads, num_kv_heads, head_dim, max_ctx, 0);
+        choose_part_blocks(num_seqs, num_q_heads, num_kv_heads, head_dim, dtype, max_ctx, 0);
     const int32_t max_blocks = (max_ctx + kBlock - 1) / kBlock;
     if (max_blocks == 0)
         return auto_pb * kBlock;
@@ -255,7 +274,8 @@ int32_t pa_decode_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_hea
         return auto_pb * kBlock;
     // Workgroups that stream at least one block, for partitions of pb blocks (empty
     // partitions exit at once).  Non-increasing in pb.
-    const int64_t per_seq = (int64_t)num_kv_heads * ((num_q_heads / num_kv_heads + 15) / 16);
+    const int32_t group = num_q_heads / num_kv_heads;
+    const int64_t per_seq = (int64_t)num_kv_heads * wg_chunks(dtype, head_dim, group);
     auto busy_groups = [&](int64_t pb) {
         int64_t w = 0;
         for (int32_t b = 0; b < num_seqs; ++b)
@@ -267,8 +287,8 @@ int32_t pa_decode_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_hea
     // that count allows (the last one short): measured on the long + shared-prefix
     // decode, 6 partitions of 408 blocks run 7 % faster than 6 of 344.  When no
     // partition allows one round, the automatic rule.
-    const int64_t nw = pa::waves_per_group(head_dim);
-    const int64_t max_pb = max_part_blocks(head_dim);
+    const int64_t nw = pa::decode_lanes(dtype, head_dim, group);
+    const int64_t max_pb = max_part_blocks(dtype, head_dim, group);
     int64_t lo = 2 * nw, hi = max_pb < max_blocks ? max_pb : max_blocks;
     if (lo > hi)
         lo = hi;
@@ -300,13 +320,13 @@ int32_t pa_decode_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_hea
 }
 
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                                 int32_t head_dim, int32_t max_context_len,
+                                 int32_t head_dim, int32_t dtype, int32_t max_context_len,
                                  int32_t partition_tokens)
 {
-    if (head_dim <= 0 || check_decode_scalars(num_seqs, num_q_heads, num_kv_heads, head_dim,
-                                              max_context_len, partition_tokens) != PA_OK)
+    if (check_decode_scalars(num_seqs, num_q_heads, num_kv_heads, head_dim, dtype,
+                             max_context_len, partition_tokens) != PA_OK)
         return SIZE_MAX;
-    const int32_t pb = choose_part_blocks(num_seqs, num_q_heads, num_kv_heads, head_dim,
+    const int32_t pb = choose_part_blocks(num_seqs, num_q_heads, num_kv_heads, head_dim, dtype,
                                           max_context_len, partition_tokens);
     const int32_t max_blocks = (max_context_len + kBlock - 1) / kBlock;
     const int64_t parts = max_blocks == 0 ? 1 : (max_blocks + pb - 1) / pb;
@@ -332,7 +352,7 @@ pa_status decode_impl(const pa_kv_pool *pool, const void *q, const void *k_new,
     if (st != PA_OK)
         return st;
     st = check_decode_scalars(num_seqs, num_q_heads, pool->num_kv_heads, pool->head_dim,
-                              max_context_len, partition_tokens);
+                              pool->dtype, max_context_len, partition_tokens);
     if (st != PA_OK)
         return st;
     if (max_blocks_per_seq < 0 || !isfinite(scale))
@@ -347,17 +367,18 @@ pa_status decode_impl(const pa_kv_pool *pool, const void *q, const void *k_new,
         return PA_ERR_INVALID_ARG;
 
     const int32_t pb = choose_part_blocks(num_seqs, num_q_heads, pool->num_kv_heads,
-                                          pool->head_dim, max_context_len, partition_tokens);
+                                          pool->head_dim, pool->dtype, max_context_len,
+                                          partition_tokens);
     const int32_t max_blocks = (max_context_len + kBlock - 1) / kBlock;
     const int32_t parts = max_blocks == 0 ? 1 : (max_blocks + pb - 1) / pb;
     const size_t need = pa_decode_workspace_bytes(num_seqs, num_q_heads, pool->num_kv_heads,
-                                                  pool->head_dim, max_context_len,
+                                                  pool->head_dim, pool->dtype, max_context_len,
                                                   partition_tokens);
     if (need > 0 && (!workspace || workspace_bytes < need))
         return PA_ERR_WORKSPACE;
     if (need > 0 && !aligned16(workspace))
         return PA_ERR_INVALID_ARG;
-    if (pb > max_part_blocks(pool->head_dim))
+    if (pb > max_part_blocks(pool->dtype, pool->head_dim, num_q_heads / pool->num_kv_heads))
         return PA_ERR_UNSUPPORTED;
 
     pa::DecodeArgs a;
@@ -376,6 +397,8 @@ pa_status decode_impl(const pa_kv_pool *pool, const void *q, const void *k_new,
     a.num_q_heads = num_q_heads;
     a.group = num_q_heads / pool->num_kv_heads;
     a.head_chunks = (a.group + 15) / 16;
+    a.wg_heads = 16 * pa::decode_chunks(pool->dtype, pool->head_dim, a.group);
+    a.wg_chunks = (a.group + a.wg_heads - 1) / a.wg_heads;
     a.max_blocks = max_blocks_per_seq;
     a.max_context_len = max_context_len;
     a.part_blocks = pb;

@@ -96,11 +96,13 @@ struct Tile16 {
     u32x4 k[NQK];                        // K[r][32i + 8g .. +7]
     u32x2 v[NPV];                        // V^T[16n + r][4g .. 4g+3]
 
-    __device__ __forceinline__ void load(const uint16_t *kt, const uint16_t *vt, int r, int g)
+    // ks: elements from one K row to the next (D in the pool; padded rows in LDS)
+    __device__ __forceinline__ void load(const uint16_t *kt, const uint16_t *vt, int r, int g,
+                                         int ks = D)
     {
 #pragma unroll
         for (int i = 0; i < NQK; ++i)
-            k[i] = *reinterpret_cast<const u32x4 *>(kt + r * D + 32 * i + 8 * g);
+            k[i] = *reinterpret_cast<const u32x4 *>(kt + r * ks + 32 * i + 8 * g);
         // V^T as 16-byte half rows (half as many load instructions as 8-byte pieces,
         // which sets how fast one CU streams): lane (r, g) loads tokens 8 (g / 2) .. +7
         // of row 16 (2 i + g % 2) + r into v[2 i] (its first 4 tokens) and v[2 i + 1];
@@ -179,11 +181,12 @@ struct Tile32 {
     f32x4 k[NC];                         // K[r][(D/4)g + 4c .. +3]
     f32x4 v[NC];                         // V^T[16n + r][4g .. 4g+3]
 
-    __device__ __forceinline__ void load(const float *kt, const float *vt, int r, int g)
+    __device__ __forceinline__ void load(const float *kt, const float *vt, int r, int g,
+                                         int ks = D)
     {
 #pragma unroll
         for (int c = 0; c < NC; ++c)
-            k[c] = *reinterpret_cast<const f32x4 *>(kt + r * D + (D / 4) * g + 4 * c);
+            k[c] = *reinterpret_cast<const f32x4 *>(kt + r * ks + (D / 4) * g + 4 * c);
 #pragma unroll
         for (int n = 0; n < NC; ++n)
             v[n] = *reinterpret_cast<const f32x4 *>(vt + (16 * n + r) * kBlock + 4 * g);
@@ -248,11 +251,12 @@ struct Tile8 {
     // transpose their 4 x 4 blocks of 4-byte pieces with two rounds of lane swaps
     // (16-lane, then 32-lane), so that v[4 i + j] = V^T[16 (4 i + j) + r][4 g .. 4 g + 3]
     // as the MFMA operand wants: 2 loads per block at d = 128 instead of 8.
-    __device__ __forceinline__ void load(const uint8_t *kt, const uint8_t *vt, int r, int g)
+    __device__ __forceinline__ void load(const uint8_t *kt, const uint8_t *vt, int r, int g,
+                                         int ks = D)
     {
 #pragma unroll
         for (int j = 0; j < NKL; ++j)
-            k[j] = *reinterpret_cast<const u32x4 *>(kt + r * D + 64 * j + 16 * g);
+            k[j] = *reinterpret_cast<const u32x4 *>(kt + r * ks + 64 * j + 16 * g);
 #pragma unroll
         for (int i = 0; i < NPV / 4; ++i) {
             const u32x4 w = *reinterpret_cast<const u32x4 *>(vt + (16 * (g + 4 * i) + r) * kBlock);
@@ -511,8 +515,8 @@ __global__ __launch_bounds__(NW *kWave, min_waves_per_simd(DT, D, PF)) void pa_d
     // order (partition fastest, then kv-head, then sequence rank); the last group of
     // fewer than 8 units is spread without that alignment.
     int px = blockIdx.x, py = blockIdx.y, pz = blockIdx.z;
-    if (a.head_chunks > 1) {
-        const int64_t C = a.head_chunks;
+    if (a.wg_chunks > 1) {
+        const int64_t C = a.wg_chunks;
         const int64_t hkv = gridDim.y / C;
         const int64_t L = blockIdx.x + (int64_t)gridDim.x * (blockIdx.y + (int64_t)gridDim.y * blockIdx.z);
         const int64_t U = (int64_t)gridDim.x * hkv * gridDim.z;
@@ -533,8 +537,8 @@ __global__ __launch_bounds__(NW *kWave, min_waves_per_simd(DT, D, PF)) void pa_d
         pz = (int)(t / hkv);
     }
     const int p = px;
-    const int kvh = py / a.head_chunks;
-    const int chunk = py - kvh * a.head_chunks;
+    const int kvh = py / a.wg_chunks;
+    const int chunk = py - kvh * a.wg_chunks;
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -870,6 +874,412 @@ __global__ __launch_bounds__(NW *kWave, min_waves_per_simd(DT, D, PF)) void pa_d
     }
 }
 
+// ------------------------------------------------------------------ shared-tile kernel
+
+// Groups above 16 q-heads (head_dim <= 128).  One 8-wave workgroup owns (sequence,
+// kv-head, up to 16 CH q-heads of its group, partition).  Wave w computes head chunk
+// c = w % CH over the blocks of block lane j = w / CH (blocks j, j + NB, ... of the
+// partition, NB = 8 / CH).  Each K/V tile is read from HBM once per workgroup: the CH
+// waves of a block lane each load a share of it and write it to LDS, and after a
+// barrier every one of them reads the whole tile into its MFMA fragments, so one
+// stream of K/V serves 16 CH q-heads, each wave holding the registers of one chunk
+// (q fragments, O accumulators).  K rows are padded by 16 bytes in LDS so the fragment
+// reads of a row group fall on distinct banks.  Groups above 64 q-heads take several
+// such workgroups per (sequence, kv-head, partition), regrouped onto one XCD as in
+// the per-chunk kernel.
+constexpr int kSharedWaves = 8;
+
+template <int DT, int D, int CH>
+struct SharedShape {
+    static constexpr int EB = DT == DT_F32 ? 4 : (DT == DT_FP8 ? 1 : 2);
+    static constexpr int NB = kSharedWaves / CH;       // block lanes
+    static constexpr int HS = 16 * CH;                 // q-head slots of the workgroup
+    static constexpr int DP = D + 4;
+    static constexpr int KROW = D * EB + 16;           // padded K row in LDS (bytes)
+    static constexpr int KBYTES = kBlock * KROW;
+    static constexpr int VBYTES = D * kBlock * EB;
+    static constexpr int TBYTES = KBYTES + VBYTES;     // one tile in LDS
+    static constexpr int KP = D * EB;                  // 16-byte pieces of a K tile
+    static constexpr int PIECES = KP + VBYTES / 16;
+    static constexpr int PPL = (PIECES + CH * kWave - 1) / (CH * kWave);   // per lane
+    // Tiles a block lane takes between two barriers (16 KB of K/V at head_dim 128, so
+    // the dependent chains of several tiles overlap; an fp32 tile is 16 KB alone), and
+    // two groups of them in flight per block lane.
+    static constexpr int TPI = DT == DT_F32 ? 1 : (DT == DT_FP8 ? 4 : 2);
+    static constexpr int RING = 2;
+    static constexpr int TILE_AREA = NB * 2 * TPI * TBYTES;
+    static constexpr int MERGE_AREA = (2 * NB * HS + NB * HS * DP) * 4 + kSharedWaves * 4;
+    static constexpr int AREA = TILE_AREA > MERGE_AREA ? TILE_AREA : MERGE_AREA;
+};
+
+template <int DT, int AT, int D, int CH, bool FUSE>
+__global__ __launch_bounds__(kSharedWaves *kWave, 2) void pa_decode_shared(DecodeArgs a)
+{
+    using F = Frags<DT, AT, D>;
+    using Elem = typename F::Elem;
+    using QElem = typename F::QElem;
+    using S = SharedShape<DT, D, CH>;
+    constexpr int NW = kSharedWaves;
+    constexpr int NB = S::NB, HS = S::HS, DP = S::DP, PPL = S::PPL, R = S::RING, TPI = S::TPI;
+
+    // [NB][2][TPI][TBYTES] tile buffers while streaming; after the loop the same bytes
+    // hold the merge; the longest-first ranks sit behind both
+    extern __shared__ __align__(16) unsigned char s_raw[];
+    int *s_ctx = reinterpret_cast<int *>(s_raw + S::AREA);
+
+    int px = blockIdx.x, py = blockIdx.y, pz = blockIdx.z;
+    if (a.wg_chunks > 1) {
+        const int64_t C = a.wg_chunks;
+        const int64_t hkv = gridDim.y / C;
+        const int64_t L = blockIdx.x + (int64_t)gridDim.x * (blockIdx.y + (int64_t)gridDim.y * blockIdx.z);
+        const int64_t U = (int64_t)gridDim.x * hkv * gridDim.z;
+        const int64_t full = U / kXcds * kXcds;
+        int64_t u, cc;
+        if (L < full * C) {
+            const int64_t rr = L % (kXcds * C);
+            cc = rr / kXcds;
+            u = L / (kXcds * C) * kXcds + rr % kXcds;
+        } else {
+            const int64_t rem = U - full, rr = L - full * C;
+            cc = rr / rem;
+            u = full + rr % rem;
+        }
+        px = (int)(u % gridDim.x);
+        const int64_t t = u / gridDim.x;
+        py = (int)(t % hkv * C + cc);
+        pz = (int)(t / hkv);
+    }
+    const int p = px;
+    const int kvh = py / a.wg_chunks;
+    const int chunk = py - kvh * a.wg_chunks;
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r = lane & 15;
+    const int g = lane >> 4;
+    const int c = wave % CH;                            // this wave's head chunk
+    const int j = wave / CH;                            // its block lane
+
+    const int gs = min(HS, a.group - chunk * HS);       // q-heads handled here
+    const int hq0 = kvh * a.group + chunk * HS;         // first q-head of this workgroup
+    const bool chunk_live = 16 * c < gs;                // wave-uniform
+
+    const int lb_begin = p * a.part_blocks;
+    const int lb_cap = min(lb_begin + a.part_blocks, a.max_blocks);
+    const int lb_lane = lb_begin + j + lane * NB;       // this block lane's (lane)-th block
+    typename F::Q qf;
+    int bt_lane;
+    auto load_seq = [&](int seq) {
+        bt_lane = lb_lane < lb_cap ? a.block_tables[(size_t)seq * a.max_blocks + lb_lane] : 0;
+        const bool hvalid = 16 * c + r < gs;
+        const QElem *qrow = static_cast<const QElem *>(a.q) +
+                           ((size_t)seq * a.num_q_heads + hq0 + (hvalid ? 16 * c + r : 0)) * D;
+        qf.load(qrow, hvalid, g);
+    };
+
+    int b = pz;
+    load_seq(b);
+    float sl_h = a.scale_log2, vs_h = a.v_scale, kq_h = a.k_quant, vq_h = a.v_quant;
+    bool bad_scale = false;
+    if constexpr (DT == DT_FP8) {
+        if (a.k_head_scales) {
+            const float s = a.k_head_scales[kvh];
+            bad_scale |= !scale_ok(s);
+            sl_h *= s;
+            kq_h = s;
+        }
+        if (a.v_head_scales) {
+            const float s = a.v_head_scales[kvh];
+            bad_scale |= !scale_ok(s);
+            vs_h = s;
+            vq_h = s;
+        }
+        if (bad_scale)
+            sl_h = 1.f;       // keeps the arithmetic tame; every output is NaN anyway
+        sl_h = uniform(sl_h);
+        vs_h = uniform(vs_h);
+        kq_h = uniform(kq_h);
+        vq_h = uniform(vq_h);
+    }
+    int ctx = -1;
+    if (a.longest_first) {
+        const int nseq = gridDim.z;
+        for (int t = tid; t < nseq; t += NW * kWave)
+            s_ctx[t] = a.context_lens[t];
+        __syncthreads();
+        for (int t = tid; t < nseq; t += NW * kWave) {
+            const int cx = s_ctx[t];
+            int rank = 0;
+            for (int u = 0; u < nseq; ++u) {
+                const int cu = s_ctx[u];
+                rank += (cu > cx || (cu == cx && u < t)) ? 1 : 0;
+            }
+            if (rank == pz)
+                s_ctx[nseq] = t;
+        }
+        __syncthreads();
+        b = __builtin_amdgcn_readfirstlane(s_ctx[nseq]);
+        ctx = s_ctx[b];
+        if (b != pz)
+            load_seq(b);
+    } else {
+        ctx = a.context_lens[b];
+    }
+    const int nblk_seq = ctx > 0 ? (int)(((unsigned)ctx + (kBlock - 1)) / kBlock) : 0;
+    const bool bad_ctx = ctx < 0 || ctx > a.max_context_len || nblk_seq > a.max_blocks;
+    const int lb_end = min(lb_begin + a.part_blocks, nblk_seq);
+
+    if (bad_ctx || lb_begin >= lb_end) {
+        if (p == 0 && (bad_ctx || nblk_seq == 0)) {
+            const float fill = (bad_ctx || bad_scale) ? __builtin_nanf("") : 0.f;
+            for (int idx = tid; idx < gs * D; idx += NW * kWave)
+                store_elem<AT>(a.out, ((size_t)b * a.num_q_heads + hq0) * D + idx, fill);
+        }
+        return;
+    }
+
+    // Fused append: token ctx - 1 (in logical block lb_new) arrives as a new row.  The
+    // chunk-0 wave of the block lane holding that block stages the row in LDS (its table
+    // register holds the block's id); every wave of that lane patches it into its
+    // registers when it reaches the block, and the staging wave, in head chunk 0's
+    // workgroup, writes the patched row into the pool.
+    const bool fuse = FUSE && ctx >= 1;
+    const int lb_new = fuse ? (ctx - 1) / kBlock : -1;
+    const int off_new = fuse ? (ctx - 1) % kBlock : 0;
+    const bool has_new = fuse && lb_new >= lb_begin && lb_new < lb_end;   // workgroup-uniform
+    int ph_new = -1;
+    __shared__ __align__(16) Elem s_newk[FUSE ? D : 16];
+    __shared__ __align__(16) Elem s_newv[FUSE ? D : 16];
+    if constexpr (FUSE) {
+        if (has_new && wave == ((lb_new - lb_begin) % NB) * CH) {
+            const QElem *kr = static_cast<const QElem *>(a.k_new) +
+                              ((size_t)b * a.num_kv_heads + kvh) * D;
+            const QElem *vr = static_cast<const QElem *>(a.v_new) +
+                              ((size_t)b * a.num_kv_heads + kvh) * D;
+            const int ph = __builtin_amdgcn_readlane(bt_lane, (lb_new - lb_begin) / NB);
+            ph_new = (chunk == 0 && (unsigned)ph < (unsigned)a.num_blocks) ? ph : -1;
+            for (int e = lane; e < D; e += kWave) {
+                Elem sk, sv;
+                if constexpr (DT == DT_FP8) {
+                    sk = (Elem)e4m3_of_16(kr[e], a.act_bf16 != 0, kq_h);
+                    sv = (Elem)e4m3_of_16(vr[e], a.act_bf16 != 0, vq_h);
+                } else {
+                    sk = kr[e];
+                    sv = vr[e];
+                }
+                s_newk[e] = sk;
+                s_newv[e] = sv;
+            }
+        }
+    }
+
+    const int nb = lb_end - lb_begin;                           // >= 1
+    const int my_n = nb > j ? (nb - j + NB - 1) / NB : 0;       // tiles of this block lane
+    const int niter = ((nb + NB - 1) / NB + TPI - 1) / TPI;     // iterations, every wave
+
+    const Elem *kbase = static_cast<const Elem *>(a.k_pool) + (size_t)kvh * kBlock * D;
+    const Elem *vbase = static_cast<const Elem *>(a.v_pool) + (size_t)kvh * kBlock * D;
+    const size_t blk_stride = (size_t)a.num_kv_heads * kBlock * D;
+
+    float m_run = -INFINITY;
+    float l_run = 0.f;
+    f32x4 o[D / 16];
+#pragma unroll
+    for (int n = 0; n < D / 16; ++n)
+        o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    bool tbl_bad = bad_scale;
+
+    auto phys_of = [&](int i) -> size_t {
+        int ph = __builtin_amdgcn_readlane(bt_lane, i);
+        if ((unsigned)ph >= (unsigned)a.num_blocks) {   // never read outside the pool
+            tbl_bad = true;
+            ph = 0;
+        }
+        return (size_t)ph * blk_stride;
+    };
+
+    // This lane's 16-byte pieces of a tile (piece q = (i CH + c) 64 + lane): where it
+    // sits in the pool's K or V tile, and where in the LDS tile.  A lane past the last
+    // piece takes the last one again: it loads and stores the same bytes as its owner.
+    int g_off[PPL], l_off[PPL];
+    bool is_k[PPL];
+#pragma unroll
+    for (int i = 0; i < PPL; ++i) {
+        const int q = min((i * CH + c) * kWave + lane, S::PIECES - 1);
+        if (q < S::KP) {
+            const int row = q / (D * S::EB / 16), col = q % (D * S::EB / 16);
+            g_off[i] = row * D * S::EB + col * 16;
+            l_off[i] = row * S::KROW + col * 16;
+            is_k[i] = true;
+        } else {
+            const int qv = q - S::KP;
+            g_off[i] = qv * 16;
+            l_off[i] = S::KBYTES + qv * 16;
+            is_k[i] = false;
+        }
+    }
+    // Every fetch issues the same PPL loads (a tile past the lane's last one reloads
+    // that last tile, a lane without tiles reads pool block 0, neither is stored), so
+    // the count of loads in flight is fixed and each wait covers exactly its slot.
+    u32x4 ring[R][TPI][PPL];
+    auto fetch = [&](int grp, int slot) {               // tile group grp -> ring slot
+#pragma unroll
+        for (int k = 0; k < TPI; ++k) {
+            const size_t off = my_n > 0 ? phys_of(min(grp * TPI + k, my_n - 1)) : 0;
+            const char *kb = reinterpret_cast<const char *>(kbase + off);
+            const char *vb = reinterpret_cast<const char *>(vbase + off);
+#pragma unroll
+            for (int i = 0; i < PPL; ++i)
+                ring[slot][k][i] =
+                    *reinterpret_cast<const u32x4 *>((is_k[i] ? kb : vb) + g_off[i]);
+        }
+    };
+    // Stashes are unconditional too: a tile past the lane's last one lands in a buffer
+    // slot that no wave reads before its next stash.
+    auto stash = [&](int grp, int slot) {               // ring slot -> LDS buffer grp & 1
+#pragma unroll
+        for (int k = 0; k < TPI; ++k) {
+            unsigned char *dst = s_raw + ((j * 2 + (grp & 1)) * TPI + k) * S::TBYTES;
+#pragma unroll
+            for (int i = 0; i < PPL; ++i)
+                *reinterpret_cast<u32x4 *>(dst + l_off[i]) = ring[slot][k][i];
+        }
+    };
+    auto process = [&](typename F::Tile &t, int i) {
+        t.finish();
+        const int lb = lb_begin + j + i * NB;
+        const int valid = ctx - lb * kBlock;            // >= 1
+        if constexpr (FUSE) {
+            if (lb == lb_new) {                         // wave-uniform
+                t.patch(s_newk, s_newv, off_new, r, g);
+                if (ph_new >= 0) {                      // head chunk 0: into the pool
+                    const size_t tile = ((size_t)ph_new * a.num_kv_heads + kvh) * kBlock * D;
+                    t.store_row(static_cast<Elem *>(const_cast<void *>(a.k_pool)) + tile,
+                                static_cast<Elem *>(const_cast<void *>(a.v_pool)) + tile,
+                                off_new, r, g);
+                }
+            }
+        }
+        f32x4 s = scores<DT, AT, D>(t, qf);
+        f32x4 x = s * sl_h;
+        if (valid < kBlock) {
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+                x[jj] = (4 * g + jj < valid) ? x[jj] : -INFINITY;
+            mask_tail_v<DT, AT, D>(t, valid, g);
+        }
+        // lazy running max, as in the per-chunk kernel
+        const float lmx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+        if (__any(lmx - m_run > kRescaleSlack)) {
+            const float m_new = fmaxf(m_run, wave_max_rows(lmx));
+            const float alpha = fast_exp2(m_run - m_new);
+#pragma unroll
+            for (int n = 0; n < D / 16; ++n)
+                o[n] *= alpha;
+            l_run *= alpha;
+            m_run = m_new;
+        }
+        f32x4 pw;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+            pw[jj] = fast_exp2(x[jj] - m_run);
+        const f32x4 pu = accumulate_pv<DT, AT, D>(t, pw, o);
+        l_run += (pu[0] + pu[1]) + (pu[2] + pu[3]);
+    };
+
+    // Group g (tiles g TPI .. g TPI + TPI - 1) of a block lane sits in ring slot g % R
+    // from its fetch until its stash, and in LDS buffer g & 1 from its stash until the
+    // barrier after it is read.  In iteration i each wave stashes group i + 1 (its share
+    // of it), refills the freed slot with group i + R, reads group i from LDS and
+    // computes its chunk on those tiles; the barrier at the end makes group i + 1
+    // visible and frees buffer i & 1 for group i + 2.  The loop runs whole rounds of R
+    // iterations with the same loads and stores in each, and no exit but its end, so
+    // every wait for a ring slot covers exactly that slot's loads.
+#pragma unroll
+    for (int k = 0; k < R; ++k)
+        fetch(k, k);
+    stash(0, 0);
+    __syncthreads();                                    // (and the staged new row)
+    for (int i0 = 0; i0 < niter; i0 += R) {
+#pragma unroll
+        for (int u = 0; u < R; ++u) {
+            const int i = i0 + u;
+            stash(i + 1, (u + 1) % R);
+            fetch(i + R, u);
+#pragma unroll
+            for (int k = 0; k < TPI; ++k) {
+                const int t_idx = i * TPI + k;          // tile of this block lane
+                if (t_idx < my_n && chunk_live) {       // wave-uniform
+                    const unsigned char *src = s_raw + ((j * 2 + (i & 1)) * TPI + k) * S::TBYTES;
+                    typename F::Tile t;
+                    t.load(reinterpret_cast<const Elem *>(src),
+                           reinterpret_cast<const Elem *>(src + S::KBYTES), r, g,
+                           S::KROW / S::EB);
+                    process(t, t_idx);
+                }
+            }
+            __syncthreads();
+        }
+    }
+    l_run = wave_sum_rows(l_run);
+
+    // ---- merge the NB block lanes' (m, l, O) of each head in LDS (tile buffers free)
+    float *s_m = reinterpret_cast<float *>(s_raw);      // [NB][HS]
+    float *s_l = s_m + NB * HS;                          // [NB][HS]
+    float *s_o = s_l + NB * HS;                          // [NB][HS][DP]
+    int *s_bad = reinterpret_cast<int *>(s_o + NB * HS * DP);   // [NW]
+    if (lane == 0)
+        s_bad[wave] = tbl_bad ? 1 : 0;
+    if (chunk_live) {
+        const int hs = 16 * c + r;
+        if (g == 0) {
+            s_m[j * HS + hs] = m_run;
+            s_l[j * HS + hs] = l_run;
+        }
+        if (hs < gs) {
+#pragma unroll
+            for (int n = 0; n < D / 16; ++n)
+                *reinterpret_cast<f32x4 *>(s_o + (j * HS + hs) * DP + 16 * n + 4 * g) = o[n];
+        }
+    }
+    __syncthreads();
+    bool any_bad = false;
+#pragma unroll
+    for (int w = 0; w < NW; ++w)
+        any_bad |= s_bad[w] != 0;
+    const bool partial = a.split && nblk_seq > a.part_blocks;
+    const float qnan = __builtin_nanf("");
+    for (int idx = tid; idx < gs * D; idx += NW * kWave) {
+        const int h = idx / D;
+        const int e = idx - h * D;
+        // (a block lane without tiles left m = -inf, l = 0, O = 0: weight 0)
+        float M = -INFINITY;
+#pragma unroll
+        for (int jj = 0; jj < NB; ++jj)
+            M = fmaxf(M, s_m[jj * HS + h]);
+        float num = 0.f, den = 0.f;
+#pragma unroll
+        for (int jj = 0; jj < NB; ++jj) {
+            const float mw = s_m[jj * HS + h];
+            const float f = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
+            num += f * s_o[(jj * HS + h) * DP + e];
+            den += f * s_l[jj * HS + h];
+        }
+        const size_t row = (size_t)b * a.num_q_heads + hq0 + h;
+        if (!partial) {
+            const float val = any_bad ? qnan : (den > 0.f ? num / den * vs_h : 0.f);
+            store_elem<AT>(a.out, row * D + e, val);
+        } else {
+            const size_t slot = row * a.num_parts + p;
+            a.ws_o[slot * D + e] = any_bad ? qnan : num * vs_h;
+            if (e == 0) {
+                a.ws_m[slot] = any_bad ? qnan : M;
+                a.ws_l[slot] = any_bad ? qnan : den;
+            }
+        }
+    }
+}
+
 // ------------------------------------------------------------------ reduce kernel
 
 // Merges the partials of every sequence that spans more than one partition:
@@ -940,9 +1350,45 @@ __global__ __launch_bounds__(256) void pa_decode_reduce(DecodeArgs a)
     }
 }
 
+template <int DT, int AT, int D, int CH>
+hipError_t launch_shared_t(const DecodeArgs &a, int num_seqs, hipStream_t stream)
+{
+    using S = SharedShape<DT, D, CH>;
+    const size_t lds = (size_t)S::AREA + (a.longest_first ? sizeof(int) * (num_seqs + 1) : 0);
+    auto kern = a.k_new ? pa_decode_shared<DT, AT, D, CH, true>
+                        : pa_decode_shared<DT, AT, D, CH, false>;
+    if (lds > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess)
+            return e;
+    }
+    dim3 grid(a.num_parts, a.num_kv_heads * a.wg_chunks, num_seqs);
+    hipLaunchKernelGGL(kern, grid, dim3(kSharedWaves * kWave), lds, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !a.split)
+        return e;
+    dim3 rgrid(a.num_kv_heads * a.head_chunks, num_seqs);
+    hipLaunchKernelGGL((pa_decode_reduce<AT, D>), rgrid, dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
 template <int DT, int AT, int D>
 hipError_t launch_decode_t(const DecodeArgs &a, int num_seqs, hipStream_t stream)
 {
+    // the host sized the grid and the partitions for decode_chunks(D, group) chunks per
+    // workgroup; the launch must hold exactly that many
+    const int ch = decode_chunks(DT, D, a.group);
+    if (a.wg_heads != 16 * ch)
+        return hipErrorInvalidValue;
+    if constexpr (D <= 128) {
+        if (ch == 4)
+            return launch_shared_t<DT, AT, D, 4>(a, num_seqs, stream);
+        if (ch == 2)
+            return launch_shared_t<DT, AT, D, 2>(a, num_seqs, stream);
+    }
+    if (ch != 1)
+        return hipErrorInvalidValue;
     constexpr int NW = waves_per_group(D);
     // fp8 tiles are half the bytes: keep the same bytes in flight with a deeper ring
     constexpr int PF = (D > 128 || DT == DT_F32) ? 1 : (DT == DT_FP8 ? 2 * kPrefetchMain + 1
@@ -958,7 +1404,7 @@ hipError_t launch_decode_t(const DecodeArgs &a, int num_seqs, hipStream_t stream
         if (e != hipSuccess)
             return e;
     }
-    dim3 grid(a.num_parts, a.num_kv_heads * a.head_chunks, num_seqs);
+    dim3 grid(a.num_parts, a.num_kv_heads * a.wg_chunks, num_seqs);
     hipLaunchKernelGGL(kern, grid, dim3(NW * kWave), lds, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !a.split)

@@ -93,17 +93,17 @@ def test_decode_rejects_bad_arguments(lib):
     assert _decode(lib, _pool(), bt=None) == inval
     assert _decode(lib, _pool(), maxb=0) == inval
     # a split launch needs the workspace it asked for
-    need = lib.pa_decode_workspace_bytes(2, 4, 2, 128, 100, 32)
+    need = lib.pa_decode_workspace_bytes(2, 4, 2, 128, B.PA_BF16, 100, 32)
     assert need > 0
     assert _decode(lib, _pool(), ptok=32) == wsp
     assert _decode(lib, _pool(), ptok=32, ws=FAKE, ws_bytes=need - 1) == wsp
     assert _decode(lib, _pool(), num_seqs=0) == 0               # nothing to do
     # block counts of the largest context stay in int32
     assert _decode(lib, _pool(), max_ctx=2 ** 31 - 1) == unsup
-    assert lib.pa_decode_workspace_bytes(2, 4, 2, 128, 2 ** 31 - 1, 0) == 2 ** 64 - 1
-    assert lib.pa_decode_partition_tokens(2, 4, 2, 128, 2 ** 31 - 1) == -1
+    assert lib.pa_decode_workspace_bytes(2, 4, 2, 128, B.PA_BF16, 2 ** 31 - 1, 0) == 2 ** 64 - 1
+    assert lib.pa_decode_partition_tokens(2, 4, 2, 128, B.PA_BF16, 2 ** 31 - 1) == -1
     lens = (ctypes.c_int32 * 2)(5, 2 ** 31 - 1)
-    assert lib.pa_decode_plan(2, 4, 2, 128, lens) == -1
+    assert lib.pa_decode_plan(2, 4, 2, 128, B.PA_BF16, lens) == -1
 
 
 def _prefill(lib, pool, num_seqs=2, hq=4, scale=0.125, qs=FAKE, T=10, maxq=8, bt=FAKE, maxb=8,
@@ -170,7 +170,7 @@ def test_append_rejects_bad_arguments(lib):
 
 
 def test_partition_choice_is_deterministic_and_sane(lib):
-    f = lambda n, hq, hkv, mx: lib.pa_decode_partition_tokens(n, hq, hkv, 128, mx)
+    f = lambda n, hq, hkv, mx: lib.pa_decode_partition_tokens(n, hq, hkv, 128, B.PA_BF16, mx)
     # one sequence of 37 tokens: single pass
     assert f(1, 4, 1, 37) >= 37
     # 32 x 4096 GQA-8: 256 (sequence, kv-head) units already give one workgroup per CU,
@@ -190,9 +190,9 @@ def test_partition_choice_is_deterministic_and_sane(lib):
 def test_decode_plan(lib):
     def plan(hq, hkv, d, lens):
         arr = (ctypes.c_int32 * max(1, len(lens)))(*lens)
-        return lib.pa_decode_plan(len(lens), hq, hkv, d, arr)
+        return lib.pa_decode_plan(len(lens), hq, hkv, d, B.PA_BF16, arr)
 
-    auto = lambda hq, hkv, n, mx: lib.pa_decode_partition_tokens(n, hq, hkv, 128, mx)
+    auto = lambda hq, hkv, n, mx: lib.pa_decode_partition_tokens(n, hq, hkv, 128, B.PA_BF16, mx)
     # equal lengths: the automatic choice
     assert plan(64, 8, 128, [4096] * 32) == auto(64, 8, 32, 4096) == 4096
     assert plan(32, 8, 128, [8160] * 64) == auto(32, 8, 64, 8160)
@@ -221,9 +221,9 @@ def test_decode_plan(lib):
 
 
 def test_workspace_matches_partitions(lib):
-    ws = lib.pa_decode_workspace_bytes
+    ws = lambda n, hq, hkv, d, mx, pt: lib.pa_decode_workspace_bytes(n, hq, hkv, d, B.PA_BF16, mx, pt)
     assert ws(1, 4, 1, 64, 37, 0) == 0
-    pt = lib.pa_decode_partition_tokens(32, 8, 1, 128, 4096)
+    pt = lib.pa_decode_partition_tokens(32, 8, 1, 128, B.PA_BF16, 4096)
     parts = -(-4096 // pt)
     assert parts > 1
     assert ws(32, 8, 1, 128, 4096, 0) == 32 * 8 * parts * (128 + 2) * 4
@@ -245,7 +245,7 @@ def test_misaligned_pointers_are_rejected(lib):
     assert _decode(lib, _pool(), out=off8) == inval
     assert _decode(lib, _pool(), bt=off2) == inval
     assert _decode(lib, _pool(), cl=off2) == inval
-    need = lib.pa_decode_workspace_bytes(2, 4, 2, 128, 100, 32)
+    need = lib.pa_decode_workspace_bytes(2, 4, 2, 128, B.PA_BF16, 100, 32)
     assert _decode(lib, _pool(), ptok=32, ws=off8, ws_bytes=need) == inval
     assert _prefill(lib, _pool(), q=off8) == inval
     assert _prefill(lib, _pool(), out=off8) == inval
@@ -264,3 +264,27 @@ def test_misaligned_pointers_are_rejected(lib):
     assert ap(ctypes.byref(_pool(k_pool=0x1001)), FAKE, FAKE, FAKE, 4, None) == inval
     assert lib.pa_copy_blocks(ctypes.byref(pool), off2, 1, None) == inval
     assert lib.pa_copy_blocks(ctypes.byref(_pool(v_pool=0x2008)), FAKE, 1, None) == inval
+
+
+def test_planner_follows_the_decode_kernel_of_the_pool_type(lib):
+    """Above 16 q-heads per kv-head, 16-bit pools run the shared-tile kernel (up to 64
+    q-heads per workgroup, 8 / chunks block lanes of at most 64 blocks each), fp8 and
+    fp32 pools one workgroup per 16 q-heads (8 waves of at most 64 blocks each): the
+    planner, the partition bound and the workspace follow the pool type."""
+    pt = lambda dt, n, hq, hkv, mx: lib.pa_decode_partition_tokens(n, hq, hkv, 128, dt, mx)
+    # 32 x 4096 at 64 q-heads over one kv-head: bf16 has 32 units of work, fp8 128
+    bf, f8 = pt(B.PA_BF16, 32, 64, 1, 4096), pt(B.PA_FP8_E4M3, 32, 64, 1, 4096)
+    assert bf % 16 == 0 and f8 % 16 == 0
+    assert 32 * -(-4096 // bf) >= 256 and 32 * 4 * -(-4096 // f8) >= 256
+    assert bf < f8
+    # the longest partition: 2 block lanes x 64 blocks (bf16, G = 64) against 8 x 64
+    ws = lambda dt, ptok: lib.pa_decode_workspace_bytes(2, 64, 1, 128, dt, 8192, ptok)
+    assert ws(B.PA_BF16, 128 * 16) > 0 and ws(B.PA_BF16, 129 * 16) == 2 ** 64 - 1
+    assert ws(B.PA_FP8_E4M3, 512 * 16) == 0 and ws(B.PA_FP8_E4M3, 513 * 16) == 2 ** 64 - 1
+    # G = 32: 4 block lanes of 64 blocks
+    ws32 = lambda ptok: lib.pa_decode_workspace_bytes(2, 64, 2, 128, B.PA_F16, 8192, ptok)
+    assert ws32(256 * 16) > 0 and ws32(257 * 16) == 2 ** 64 - 1
+    # head_dim 256 keeps one chunk per workgroup (4 waves) whatever the pool type
+    ws256 = lambda ptok: lib.pa_decode_workspace_bytes(2, 64, 1, 256, B.PA_BF16, 8192, ptok)
+    assert ws256(256 * 16) > 0 and ws256(257 * 16) == 2 ** 64 - 1
+    assert lib.pa_decode_partition_tokens(2, 4, 2, 128, 9, 100) == -1   # bad dtype

@@ -58,7 +58,7 @@ def test_graph_replay_matches_eager(spec, ptok):
     d = U.device_inputs(w)
     sc = U.scales(w)
     need = PA.workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim,
-                              w.max_context_len, ptok)
+                              w.max_context_len, ptok, dtype=w.kv_dtype)
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
 
     def step(kp, vp, out):
@@ -129,7 +129,7 @@ def test_graph_replay_fused_decode_append(spec, ptok):
     vn[rows] = w.v_new
     k_rows, v_rows = U.to_dev(kn, w.dtype), U.to_dev(vn, w.dtype)
     need = PA.workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim,
-                              w.max_context_len, ptok)
+                              w.max_context_len, ptok, dtype=w.kv_dtype)
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
 
     def call(kp, vp, out):
@@ -218,7 +218,7 @@ def test_graph_replay_reads_per_head_scales_at_replay():
     d = U.device_inputs(w)
     sc = U.scales(w)
     need = PA.workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim,
-                              w.max_context_len, ptok)
+                              w.max_context_len, ptok, dtype=w.kv_dtype)
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
     kp, vp = U.device_pools(w)
     fresh_k, fresh_v = kp.clone(), vp.clone()

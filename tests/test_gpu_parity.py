@@ -112,6 +112,15 @@ SMALL = [
     W.Spec("fp8_heads_bf16_g8_d256", "bf16", 32, 4, 256, [300, 7], seed=121, spare_blocks=1,
            kv_dtype="fp8", k_scale=(0.0125, 0.006, 0.02, 0.01),
            v_scale=(0.0125, 0.03, 0.004, 0.008)),
+    # 16-bit pools above 16 q-heads take the shared-tile kernel: a second chunk with 4
+    # live heads (G = 20), two workgroups per (sequence, kv-head) (G = 128), and
+    # contexts past one partition's 2 x 64 blocks at head_dim 64 with empty ones
+    W.Spec("f16_g20_d64_shared", "f16", 40, 2, 64, [77, 1, 300, 16, 0], seed=122,
+           spare_blocks=1),
+    W.Spec("bf16_g128_d128_shared", "bf16", 128, 1, 128, [500, 33, 1200], seed=123,
+           spare_blocks=1),
+    W.Spec("bf16_g64_d64_shared_long", "bf16", 128, 2, 64, [3000, 5, 2049, 0, 4100], seed=124,
+           spare_blocks=1),
 ]
 
 
@@ -174,7 +183,7 @@ def test_decode_config(i):
     w = config(i)
     say(f"[decode] config {i} {w.spec.name} B={w.num_seqs} Hq={w.num_q_heads} "
         f"Hkv={w.num_kv_heads} d={w.head_dim} max_ctx={w.max_context_len} "
-        f"auto partition={PA.partition_tokens(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.max_context_len)}")
+        f"auto partition={PA.partition_tokens(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.max_context_len, w.kv_dtype)}")
     ref = oracle_decode(w)
     got, _, _ = gpu_step(w)
     check(w, got, ref, f"config {i}")
@@ -196,7 +205,8 @@ def test_decode_config_planned_partitions(i):
     """The partition length pa_decode_plan picks from the host context lengths (config
     5: the long sequences cut into 6 partitions) meets the same bar."""
     w = config(i)
-    ptok = PA.plan_partition_tokens(w.num_q_heads, w.num_kv_heads, w.head_dim, w.context_lens)
+    ptok = PA.plan_partition_tokens(w.num_q_heads, w.num_kv_heads, w.head_dim, w.context_lens,
+                                  w.kv_dtype)
     say(f"[plan] config {i} planned partition_tokens={ptok}")
     ref = oracle_decode(w)
     got, _, _ = gpu_step(w, ptok)
@@ -302,7 +312,8 @@ def test_split_workspace_reuse_and_garbage():
             for ptok in (16, 32, 64):
                 w = W.build(spec)
                 need = PA.workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads,
-                                          w.head_dim, w.max_context_len, ptok)
+                                          w.head_dim, w.max_context_len, ptok,
+                                          dtype=w.kv_dtype)
                 assert 0 < need <= ws.numel()
                 kp, vp = U.device_pools(w)
                 d = U.device_inputs(w)
@@ -326,7 +337,7 @@ def test_binding_grows_a_too_small_workspace():
     w = W.build(SMALL[0])
     ptok = 16
     need = PA.workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim,
-                              w.max_context_len, ptok)
+                              w.max_context_len, ptok, dtype=w.kv_dtype)
     assert need > 64
     small = torch.full((need // 2,), 0xA5, dtype=torch.uint8, device="cuda")
     kp, vp = U.device_pools(w)
@@ -395,7 +406,8 @@ def test_decode_random_batches(i):
         f"{spec.head_dim} {spec.dtype}/{spec.kv_dtype or spec.dtype} B {len(spec.context_lens)}")
     w = W.build(spec)
     ref = oracle_decode(w)
-    plan = PA.plan_partition_tokens(w.num_q_heads, w.num_kv_heads, w.head_dim, w.context_lens)
+    plan = PA.plan_partition_tokens(w.num_q_heads, w.num_kv_heads, w.head_dim, w.context_lens,
+                                  w.kv_dtype)
     for ptok in (plan, 64):
         got, _, _ = gpu_step(w, ptok)
         check(w, got, ref, f"dec_random_{i} p{ptok}")

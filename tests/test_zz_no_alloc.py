@@ -60,7 +60,7 @@ def test_noalloc_equals_decode_twice_second_smaller(lib, pair):
     for spec, ptok in pair:
         w = W.build(spec)
         need = PA.workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim,
-                                  w.max_context_len, ptok)
+                                  w.max_context_len, ptok, dtype=w.kv_dtype)
         say(f"[noalloc] {spec.name} ptok={ptok} partials {need} B")
         assert 0 < need <= PA.NOALLOC_SCRATCH_BYTES
         d = U.device_inputs(w)
