@@ -12,11 +12,12 @@ layers of a real step do, so K/V is not reused from the 256 MB last-level cache.
 
 Printed: ONE JSON line on stdout.
   value      KV GB/s over the whole step (algorithmic K+V bytes / wall time per step)
-  roofline   the decode call, timed over back-to-back launches with HIP events on the
-             launching stream, against the 8 TB/s HBM peak (unique K/V bytes; shared
-             prefix blocks count once) and against the read rate a plain 16-byte-load
-             kernel measures in the same run; traffic from the committed rocprofv3
-             counter passes when they match the current kernel source
+  roofline   the step's launch, timed with HIP events on the launching stream around
+             the K timed steps (also over a longer run of back-to-back launches), against
+             the 8 TB/s HBM peak (unique K/V bytes; shared prefix blocks count once) and
+             against the read rate a plain 16-byte-load kernel measures in the same run
+             before the steps; traffic from the committed rocprofv3 counter passes when
+             they match the current kernel source
   cpu_baseline  the fp64 oracle on the host cores, on the same workload
 Progress goes to stderr.
 """
@@ -65,6 +66,13 @@ def parse():
                     help="step: the decode step (default); copy_blocks: the copy-on-write "
                          "block copy on the workload's pool; prefill: append + paged "
                          "prefill of prompt chunks")
+    ap.add_argument("--sweep", choices=["decode-types", "decode-groups", "prefill-types"],
+                    default=None,
+                    help="instead of the bench line, time one call per shape of a family "
+                         "and print one JSON line of rows: decode pool types and head "
+                         "sizes on the Llama-70B-shaped decode, decode GQA group sizes on "
+                         "32 x 4096 tokens, or prefill pool types and head sizes on the "
+                         "512-token chunked prefill")
     ap.add_argument("--calibrate", action="store_true",
                     help="also run one 256 MiB device copy (a kernel of known traffic for "
                          "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
@@ -457,6 +465,108 @@ def bench_prefill(args, w, PA, U, dev):
     }), flush=True)
 
 
+def sweep_shapes(name, W):
+    """(label, Spec) of one shape family, each derived from a named workload."""
+    import dataclasses
+    fp8 = dict(kv_dtype="fp8", k_scale=0.0117, v_scale=0.0093)
+    if name == "prefill-types":
+        base = W.config_spec(PREFILL_HEADLINE)
+        rows = [("bf16 d128", {}), ("f16 d128", dict(dtype="f16")),
+                ("fp8/bf16 d128", fp8), ("fp8/f16 d128", dict(dtype="f16", **fp8)),
+                ("bf16 d64", dict(head_dim=64)), ("fp8/bf16 d64", dict(head_dim=64, **fp8)),
+                ("bf16 d256", dict(head_dim=256)), ("fp8/bf16 d256", dict(head_dim=256, **fp8))]
+    elif name == "decode-types":
+        base = W.config_spec(HEADLINE)
+        rows = [("bf16 d128", {}), ("f16 d128", dict(dtype="f16")),
+                ("fp8/bf16 d128", fp8), ("bf16 d64", dict(head_dim=64)),
+                ("fp8/bf16 d64", dict(head_dim=64, **fp8)), ("bf16 d256", dict(head_dim=256)),
+                ("fp8/bf16 d256", dict(head_dim=256, **fp8)),
+                ("f32 d64", dict(dtype="f32", head_dim=64))]
+    else:
+        base = W.config_spec(HEADLINE)
+        rows = [("bf16 G8 (64 q / 8 kv)", {}),
+                ("bf16 G16 (64 q / 4 kv)", dict(num_kv_heads=4)),
+                ("bf16 G32 (64 q / 2 kv)", dict(num_kv_heads=2)),
+                ("bf16 G64 MQA (64 q / 1 kv)", dict(num_kv_heads=1)),
+                ("f16 G64 MQA (64 q / 1 kv)", dict(num_kv_heads=1, dtype="f16")),
+                ("bf16 G48 (96 q / 2 kv)", dict(num_q_heads=96, num_kv_heads=2)),
+                ("bf16 G64 (128 q / 2 kv)", dict(num_q_heads=128, num_kv_heads=2)),
+                ("bf16 G32 (128 q / 4 kv)", dict(num_q_heads=128, num_kv_heads=4)),
+                ("fp8/bf16 G32 (64 q / 2 kv)", dict(num_kv_heads=2, **fp8)),
+                ("fp8/bf16 G64 MQA (64 q / 1 kv)", dict(num_kv_heads=1, **fp8))]
+    import re
+    return [(label, dataclasses.replace(base, name=base.name + "_" +
+                                        re.sub(r"[^A-Za-z0-9]+", "_", label).strip("_"), **kw))
+            for label, kw in rows]
+
+
+def bench_sweep(args, PA, W, U, dev):
+    """One timed call per shape (decode: the fused step's launch at the planned
+    partition, cycling four pools; prefill: the prefill call), best of three rounds of
+    back-to-back launches between HIP events on the launching stream."""
+    rows = []
+    for label, spec in sweep_shapes(args.sweep, W):
+        w = W.build(spec)
+        sc = U.scales(w)
+        d = U.device_inputs(w, dev)
+        out = torch.empty_like(d["q"])
+        if w.is_prefill:
+            kp, vp = U.device_pools(w, dev)
+            PA.cache_append(kp, vp, d["k_new"], d["v_new"], d["slot_mapping"], **sc)
+            qs = torch.from_numpy(w.query_start).to(dev)
+
+            def call(i):
+                PA.prefill(d["q"], kp, vp, qs, d["block_tables"], d["context_lens"],
+                           float(w.scale), w.max_context_len, w.max_query_len, out=out, **sc)
+            n_warm, n_launch = 20, 30
+        else:
+            pools = [U.device_pools(w, dev) for _ in range(LAYERS)]
+            ptok = PA.plan_partition_tokens(w.num_q_heads, w.num_kv_heads, w.head_dim,
+                                            w.context_lens, w.kv_dtype)
+            ws = torch.empty(max(PA.workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads,
+                                                    w.head_dim, w.max_context_len, ptok,
+                                                    w.kv_dtype), 1),
+                             dtype=torch.uint8, device=dev)
+            rows_new = np.zeros((w.num_seqs,) + w.k_new.shape[1:], w.k_new.dtype)
+            rows_new[np.flatnonzero(w.context_lens > 0)] = w.k_new
+            kr = U.to_dev(rows_new, w.dtype, dev)
+
+            def call(i):
+                kp, vp = pools[i % LAYERS]
+                PA.decode_append(d["q"], kp, vp, kr, kr, d["block_tables"], d["context_lens"],
+                                 float(w.scale), w.max_context_len, ptok, out=out,
+                                 workspace=ws, **sc)
+            n_warm, n_launch = 200, 100
+        for i in range(n_warm):
+            call(i)
+        torch.cuda.synchronize()
+        s = torch.cuda.current_stream(dev)
+        best = float("inf")
+        for _ in range(3):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(s)
+            for i in range(n_launch):
+                call(i)
+            e1.record(s)
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1) * 1e3 / n_launch)
+        finite = bool(torch.isfinite(out.float()).all().item())
+        row = {"shape": label, "workload": spec.name, "us": round(best, 2), "finite": finite}
+        if w.is_prefill:
+            tf = prefill_flops(w) / best / 1e6
+            row.update(tflops=round(tf, 1), pct_mfma_peak=round(100 * tf / MFMA_BF16_PEAK_TFLOPS, 1))
+        else:
+            by = w.unique_kv_bytes()
+            row.update(partition_tokens=ptok, kv_bytes=int(by), GBps=round(by / best / 1e3, 1),
+                       pct_hbm_peak=round(100 * by / best / 1e3 / HBM_PEAK_GBS, 1))
+        log(f"[sweep] {json.dumps(row)}")
+        rows.append(row)
+        del out, d
+        torch.cuda.empty_cache()
+    print(json.dumps({"sweep": args.sweep, "rows": rows}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -475,6 +585,8 @@ def main():
 
     PA.load()
     dev = torch.device("cuda:0")
+    if args.sweep:
+        return bench_sweep(args, PA, W, U, dev)
     t0 = time.time()
     if args.config is None:
         args.config = PREFILL_HEADLINE if args.op == "prefill" else HEADLINE
@@ -530,20 +642,32 @@ def main():
 
     if args.calibrate:
         calibration_copy(dev)
+    # the HBM read ceiling of this machine, measured before the steps (a plain 16-byte-load
+    # read of 2 GiB, ten times)
+    ceiling = measured_read_ceiling(dev)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
     log(f"[bench] warmup {args.warmup} steps done")
 
+    # the timed steps: wall clock between two synchronisations, and HIP events on the
+    # launching stream around the same launches (the roofline's launch duration)
+    stream = torch.cuda.current_stream(dev)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start = time.perf_counter()
+    ev0.record(stream)
     for i in range(args.steps):
         step(i)
+    ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     ms_per_step = wall * 1e3 / args.steps
-    log(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.1f} us/step")
+    dur = ev0.elapsed_time(ev1) * 1e-3 / args.steps
+    log(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.1f} us/step "
+        f"({dur * 1e6:.1f} us per launch by events)")
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(args.steps):
@@ -552,11 +676,14 @@ def main():
     two_call_ms = (time.perf_counter() - t_start) * 1e3 / args.steps
     log(f"[bench] {args.steps} steps as append + decode: {two_call_ms * 1e3:.1f} us/step")
 
-    # roofline: decode calls launched back to back on one stream, bracketed by HIP
-    # events on that stream, cycling over the layers' pools so each launch's K/V is
-    # out of the caches (1.5 GiB of other pools in between); the pools already hold
-    # the step's appended rows
-    stream = torch.cuda.current_stream(dev)
+    # the least HBM traffic the method must move is each physical K/V row once: shared
+    # prefix blocks count once (the logical rate is reported beside it)
+    achieved = uniq_bytes / dur / 1e9
+    log(f"[bench] decode_append launches of the timed steps: {dur * 1e6:.1f} us each -> "
+        f"{achieved:.0f} GB/s unique, {kv_bytes / dur / 1e9:.0f} logical")
+    # a longer run of the same launches, back to back between HIP events on the stream,
+    # cycling over the layers' pools so each launch's K/V is out of the caches (1.5 GiB
+    # of other pools in between); reported beside the timed steps' figure
     n_l = args.roofline_launches
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
@@ -566,13 +693,8 @@ def main():
         fused(i)
     e1.record(stream)
     torch.cuda.synchronize()
-    dur = e0.elapsed_time(e1) * 1e-3 / n_l
-    # the least HBM traffic the method must move is each physical K/V row once: shared
-    # prefix blocks count once (the logical rate is reported beside it)
-    achieved = uniq_bytes / dur / 1e9
-    log(f"[bench] decode_append call: {dur * 1e6:.1f} us per launch over {n_l} back-to-back "
-        f"launches -> {achieved:.0f} GB/s unique, {kv_bytes / dur / 1e9:.0f} logical")
-    ceiling = measured_read_ceiling(dev)
+    dur_loop = e0.elapsed_time(e1) * 1e-3 / n_l
+    log(f"[bench] {n_l} more back-to-back launches: {dur_loop * 1e6:.1f} us each")
     traffic = recorded_traffic(w.spec.name, ptok)
 
     # the same step captured as one HIP graph per layer pool and replayed (the
@@ -692,8 +814,11 @@ def main():
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "launch_us_mean": round(dur * 1e6, 2),
+                     "launch_us_source": f"HIP events around the {args.steps} timed steps",
                      "bytes_per_launch": uniq_bytes,
                      "achieved_logical": round(kv_bytes / dur / 1e9, 1),
+                     "launch_us_mean_longer_run": round(dur_loop * 1e6, 2),
+                     "longer_run_launches": n_l,
                      "measured_read_ceiling": None if ceiling is None else round(ceiling, 1),
                      "frac_of_measured_read_ceiling":
                          None if ceiling is None else round(achieved / ceiling, 4)},
