@@ -1,0 +1,33 @@
+"""The fp64 oracle (C) and the host block allocator (C++) built with AddressSanitizer and
+UndefinedBehaviorSanitizer (gcc / g++, host code only, any finding aborts) and run over
+tests/sanitize_driver.c's cases (CPU only)."""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SAN = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer",
+       "-g", "-O1"]
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None or shutil.which("g++") is None,
+                    reason="needs gcc and g++")
+def test_oracle_and_allocator_under_asan_ubsan(tmp_path):
+    objs = []
+    for src, cc, std in (("oracle/oracle.c", "gcc", "-std=c11"),
+                         ("tests/sanitize_driver.c", "gcc", "-std=c11"),
+                         ("paged_kv_cache_161_amd/csrc/pa_alloc.cpp", "g++", "-std=c++17")):
+        obj = tmp_path / (os.path.basename(src) + ".o")
+        subprocess.run([cc, std, *SAN, "-pthread", "-c", os.path.join(ROOT, src), "-o", str(obj)],
+                       check=True)
+        objs.append(str(obj))
+    exe = tmp_path / "sanitized"
+    subprocess.run(["g++", *SAN, "-pthread", *objs, "-o", str(exe), "-lm"], check=True)
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=0",
+               UBSAN_OPTIONS="print_stacktrace=1")
+    env.pop("LD_PRELOAD", None)
+    res = subprocess.run([str(exe)], capture_output=True, text=True, env=env, timeout=120)
+    assert res.returncode == 0, res.stdout + res.stderr
+    assert "passed" in res.stdout
