@@ -1381,7 +1381,7 @@ hipError_t launch_decode_t(const DecodeArgs &a, int num_seqs, hipStream_t stream
     const int ch = decode_chunks(DT, D, a.group);
     if (a.wg_heads != 16 * ch)
         return hipErrorInvalidValue;
-    if constexpr (D <= 128) {
+    if constexpr (D <= 128 && (DT == DT_F16 || DT == DT_BF16)) {
         if (ch == 4)
             return launch_shared_t<DT, AT, D, 4>(a, num_seqs, stream);
         if (ch == 2)
