@@ -98,6 +98,8 @@ def test_decode_rejects_bad_arguments(lib):
     assert _decode(lib, _pool(), ptok=32) == wsp
     assert _decode(lib, _pool(), ptok=32, ws=FAKE, ws_bytes=need - 1) == wsp
     assert _decode(lib, _pool(), num_seqs=0) == 0               # nothing to do
+    # one launch holds at most 65,535 sequences (the grid's z extent)
+    assert _decode(lib, _pool(), num_seqs=65536) == unsup
     # block counts of the largest context stay in int32
     assert _decode(lib, _pool(), max_ctx=2 ** 31 - 1) == unsup
     assert lib.pa_decode_workspace_bytes(2, 4, 2, 128, B.PA_BF16, 2 ** 31 - 1, 0) == 2 ** 64 - 1

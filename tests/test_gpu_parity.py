@@ -94,8 +94,9 @@ SMALL = [
     W.Spec("bf16_300_ragged_seqs", "bf16", 8, 2, 128,
            [int(x) for x in np.random.Generator(np.random.PCG64(110)).integers(0, 70, 300)],
            seed=110, spare_blocks=1),
-    # groups above 16 q-heads: one workgroup per 16-head chunk, regrouped so a unit's
-    # chunks share an XCD (whole groups of 8 units) or spread plainly (the last group)
+    # groups above 16 q-heads: fp8 pools run one workgroup per 16-head chunk,
+    # regrouped so a unit's chunks share an XCD (whole groups of 8 units) or spread
+    # plainly (the last group); 16-bit pools stage each tile once for 64 q-heads
     W.Spec("bf16_g48_d128", "bf16", 96, 2, 128, [300, 45, 1, 900, 17], seed=115,
            spare_blocks=1),
     W.Spec("fp8_bf16_g40_d64", "bf16", 80, 2, 64, [77, 200, 3], seed=116, spare_blocks=1,
