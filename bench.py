@@ -73,6 +73,10 @@ def parse():
                          "sizes on the Llama-70B-shaped decode, decode GQA group sizes on "
                          "32 x 4096 tokens, or prefill pool types and head sizes on the "
                          "512-token chunked prefill")
+    ap.add_argument("--sweep-launches", type=int, default=0,
+                    help="with --sweep: launches per timed round and warm-up launches "
+                         "(default 100 and 200 for decode, 30 and 20 for prefill); small "
+                         "values keep a rocprofv3 counter pass over a sweep short")
     ap.add_argument("--calibrate", action="store_true",
                     help="also run one 256 MiB device copy (a kernel of known traffic for "
                          "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
@@ -505,6 +509,8 @@ def bench_sweep(args, PA, W, U, dev):
     partition, cycling four pools; prefill: the prefill call), best of three rounds of
     back-to-back launches between HIP events on the launching stream."""
     rows = []
+    if args.calibrate:
+        calibration_copy(dev)
     for label, spec in sweep_shapes(args.sweep, W):
         w = W.build(spec)
         sc = U.scales(w)
@@ -519,6 +525,8 @@ def bench_sweep(args, PA, W, U, dev):
                 PA.prefill(d["q"], kp, vp, qs, d["block_tables"], d["context_lens"],
                            float(w.scale), w.max_context_len, w.max_query_len, out=out, **sc)
             n_warm, n_launch = 20, 30
+            if args.sweep_launches > 0:
+                n_warm, n_launch = args.sweep_launches, args.sweep_launches
         else:
             pools = [U.device_pools(w, dev) for _ in range(LAYERS)]
             ptok = PA.plan_partition_tokens(w.num_q_heads, w.num_kv_heads, w.head_dim,
@@ -537,6 +545,8 @@ def bench_sweep(args, PA, W, U, dev):
                                  float(w.scale), w.max_context_len, ptok, out=out,
                                  workspace=ws, **sc)
             n_warm, n_launch = 200, 100
+            if args.sweep_launches > 0:
+                n_warm, n_launch = args.sweep_launches, args.sweep_launches
         for i in range(n_warm):
             call(i)
         torch.cuda.synchronize()
