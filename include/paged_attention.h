@@ -285,6 +285,38 @@ pa_status pa_prefill(const pa_kv_pool *pool, const void *q, void *out, int32_t n
 pa_status pa_copy_blocks(const pa_kv_pool *pool, const int32_t *pairs, int32_t num_pairs,
                          void *stream);
 
+/* ---------------------------------------------------------------- host input checks
+ * Host-only checks of a batch's index arrays (HOST int32 arrays, read only) against the
+ * rules the kernels assume: a sequence's logical block i lives in physical block
+ * table[i], token t in block t / 16 at offset t % 16, and an appended row goes to slot
+ * block * 16 + offset (LLM-101-CN "推理优化", section "物理块与逻辑块").  The kernels
+ * never read or write outside the pool whatever the arrays hold (a bad entry gives NaN
+ * rows or a skipped row); these calls name the first offender before anything is
+ * launched.  Each returns PA_OK, or PA_ERR_INVALID_ARG with the offender's index in
+ * *bad_*_out (if not NULL; -1 when the scalars themselves are wrong), and keeps no state. */
+
+/* Every context length in [0, max_context_len] and at most max_blocks_per_seq * 16, and
+ * every table entry a sequence reads (the first ceil(context_lens[b] / 16) of its row of
+ * block_tables [num_seqs][max_blocks_per_seq]) in [0, num_blocks). */
+pa_status pa_validate_decode_tables(int32_t num_seqs, const int32_t *block_tables,
+                                    int32_t max_blocks_per_seq, const int32_t *context_lens,
+                                    int32_t max_context_len, int32_t num_blocks,
+                                    int32_t *bad_seq_out);
+
+/* pa_validate_decode_tables' rules, and query_start [num_seqs + 1] starting at 0, never
+ * decreasing, each range at most max_query_len rows and ending at num_query_tokens. */
+pa_status pa_validate_prefill_batch(int32_t num_seqs, const int32_t *query_start,
+                                    int32_t num_query_tokens, int32_t max_query_len,
+                                    const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                    const int32_t *context_lens, int32_t max_context_len,
+                                    int32_t num_blocks, int32_t *bad_seq_out);
+
+/* Every slot of slot_mapping [num_tokens] negative (a padding row) or in
+ * [0, num_blocks * 16), and no slot named twice (two rows written to one slot land in
+ * an undefined order).  Allocates num_blocks * 16 bytes of host memory while it runs. */
+pa_status pa_validate_slots(const int32_t *slot_mapping, int32_t num_tokens, int32_t num_blocks,
+                            int32_t *bad_token_out);
+
 /* ---------------------------------------------------------------- host block allocator
  * Bookkeeping of which physical blocks are free, with reference counts so that blocks
  * can be shared by several sequences (beam-search prefixes) and copied on first write

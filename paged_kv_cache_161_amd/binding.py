@@ -100,6 +100,12 @@ def load(path: str = LIB_PATH):
     lib.pa_seq_fork.restype = ctypes.c_int
     lib.pa_seq_truncate.argtypes = [P, P, I32, I32, I32]
     lib.pa_seq_truncate.restype = ctypes.c_int
+    lib.pa_validate_decode_tables.argtypes = [I32, P, I32, P, I32, I32, P]
+    lib.pa_validate_decode_tables.restype = ctypes.c_int
+    lib.pa_validate_prefill_batch.argtypes = [I32, P, I32, I32, P, I32, P, I32, I32, P]
+    lib.pa_validate_prefill_batch.restype = ctypes.c_int
+    lib.pa_validate_slots.argtypes = [P, I32, I32, P]
+    lib.pa_validate_slots.restype = ctypes.c_int
     if path == LIB_PATH:
         _lib = lib
     return lib
@@ -391,6 +397,55 @@ def copy_blocks(k_pool, v_pool, pairs: torch.Tensor) -> None:
 
 def _np_ptr(a):
     return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _host_i32(a, name):
+    import numpy as np
+    if isinstance(a, torch.Tensor):
+        a = a.detach().cpu().numpy()
+    a = np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+    return a
+
+
+def validate_decode_tables(block_tables, context_lens, max_context_len: int,
+                           num_blocks: int) -> int:
+    """pa_validate_decode_tables on host copies of the arrays: -1 when every sequence
+    is valid, else the first offending sequence's index."""
+    bt, cl = _host_i32(block_tables, "block_tables"), _host_i32(context_lens, "context_lens")
+    bad = ctypes.c_int32(-1)
+    st = load().pa_validate_decode_tables(int(cl.size), _np_ptr(bt), int(bt.shape[1]),
+                                          _np_ptr(cl), int(max_context_len), int(num_blocks),
+                                          ctypes.byref(bad))
+    if st not in (0, 1) or (st == 1 and bad.value < 0):
+        _raise(st)
+    return -1 if st == 0 else int(bad.value)
+
+
+def validate_prefill_batch(query_start, block_tables, context_lens, num_query_tokens: int,
+                           max_query_len: int, max_context_len: int, num_blocks: int) -> int:
+    """pa_validate_prefill_batch on host copies of the arrays: -1 when the batch is
+    valid, else the first offending sequence's index."""
+    qs = _host_i32(query_start, "query_start")
+    bt, cl = _host_i32(block_tables, "block_tables"), _host_i32(context_lens, "context_lens")
+    bad = ctypes.c_int32(-1)
+    st = load().pa_validate_prefill_batch(int(cl.size), _np_ptr(qs), int(num_query_tokens),
+                                          int(max_query_len), _np_ptr(bt), int(bt.shape[1]),
+                                          _np_ptr(cl), int(max_context_len), int(num_blocks),
+                                          ctypes.byref(bad))
+    if st not in (0, 1) or (st == 1 and bad.value < 0):
+        _raise(st)
+    return -1 if st == 0 else int(bad.value)
+
+
+def validate_slots(slot_mapping, num_blocks: int) -> int:
+    """pa_validate_slots on a host copy: -1 when every slot is padding or a distinct
+    slot of the pool, else the first offending row's index."""
+    sm = _host_i32(slot_mapping, "slot_mapping")
+    bad = ctypes.c_int32(-1)
+    st = load().pa_validate_slots(_np_ptr(sm), int(sm.size), int(num_blocks), ctypes.byref(bad))
+    if st not in (0, 1) or (st == 1 and bad.value < 0):
+        _raise(st)
+    return -1 if st == 0 else int(bad.value)
 
 
 class BlockAllocator:

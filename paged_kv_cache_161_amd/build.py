@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libpa_mi355x.so")
 PROBE_LIB = os.path.join(HERE, "libpa_hbm_probe.so")
-SOURCES = ["pa_api.cpp", "pa_alloc.cpp", "pa_decode.hip", "pa_append.hip", "pa_prefill.hip"]
+SOURCES = ["pa_api.cpp", "pa_alloc.cpp", "pa_validate.cpp", "pa_decode.hip", "pa_append.hip", "pa_prefill.hip"]
 ARCH = "gfx950"
 
 

@@ -1,9 +1,10 @@
-/* Drives the fp64 oracle and the host block allocator through small seeded cases so
- * that an AddressSanitizer / UndefinedBehaviorSanitizer build can watch every path:
- * decode, contiguous decode, prefill, append (with fp8 per-head scales), block copy,
- * widening and the E4M3 encoder; allocator acquire, share, release, reserve with
- * copy-on-write, fork, truncate and rejected calls.  Exits 0 when every call returned
- * what it should (the sanitizers abort the process on a finding). */
+/* Drives the fp64 oracle, the host block allocator and the host input checks through
+ * small seeded cases so that an AddressSanitizer / UndefinedBehaviorSanitizer build can
+ * watch every path: decode, contiguous decode, prefill, append (with fp8 per-head
+ * scales), block copy, widening and the E4M3 encoder; allocator acquire, share,
+ * release, reserve with copy-on-write, fork, truncate and rejected calls; table, query
+ * range and slot checks.  Exits 0 when every call returned what it should (the
+ * sanitizers abort the process on a finding). */
 #include <stdint.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -125,9 +126,28 @@ static int allocator_cases(void)
     return 0;
 }
 
+static int validate_cases(void)
+{
+    int32_t bt[2 * 4] = {5, 7, 2, -1, 1, 99, -3, 0};
+    int32_t cl[2] = {37, 16}, bad = 0;
+    CHECK(pa_validate_decode_tables(2, bt, 4, cl, 64, 8, &bad) == PA_OK && bad == -1);
+    cl[1] = 17;
+    CHECK(pa_validate_decode_tables(2, bt, 4, cl, 64, 8, &bad) == PA_ERR_INVALID_ARG && bad == 1);
+    cl[1] = 16;
+    int32_t qs[3] = {0, 5, 12};
+    CHECK(pa_validate_prefill_batch(2, qs, 12, 8, bt, 4, cl, 64, 8, &bad) == PA_OK);
+    qs[2] = 13;
+    CHECK(pa_validate_prefill_batch(2, qs, 12, 8, bt, 4, cl, 64, 8, &bad) == PA_ERR_INVALID_ARG);
+    int32_t slots[5] = {3, -1, 17, 127, 3};
+    CHECK(pa_validate_slots(slots, 4, 8, &bad) == PA_OK);
+    CHECK(pa_validate_slots(slots, 5, 8, &bad) == PA_ERR_INVALID_ARG && bad == 4);
+    CHECK(pa_validate_slots(slots, 5, 0, NULL) == PA_ERR_INVALID_ARG);
+    return 0;
+}
+
 int main(void)
 {
-    if (oracle_cases() || allocator_cases())
+    if (oracle_cases() || allocator_cases() || validate_cases())
         return 1;
     printf("sanitized oracle and allocator cases passed\n");
     return 0;

@@ -1,4 +1,4 @@
-"""The fp64 oracle (C) and the host block allocator (C++) built with AddressSanitizer and
+"""The fp64 oracle (C), the host block allocator and the host input checks (C++) built with AddressSanitizer and
 UndefinedBehaviorSanitizer (gcc / g++, host code only, any finding aborts) and run over
 tests/sanitize_driver.c's cases (CPU only)."""
 import os
@@ -18,7 +18,8 @@ def test_oracle_and_allocator_under_asan_ubsan(tmp_path):
     objs = []
     for src, cc, std in (("oracle/oracle.c", "gcc", "-std=c11"),
                          ("tests/sanitize_driver.c", "gcc", "-std=c11"),
-                         ("paged_kv_cache_161_amd/csrc/pa_alloc.cpp", "g++", "-std=c++17")):
+                         ("paged_kv_cache_161_amd/csrc/pa_alloc.cpp", "g++", "-std=c++17"),
+                         ("paged_kv_cache_161_amd/csrc/pa_validate.cpp", "g++", "-std=c++17")):
         obj = tmp_path / (os.path.basename(src) + ".o")
         subprocess.run([cc, std, *SAN, "-pthread", "-c", os.path.join(ROOT, src), "-o", str(obj)],
                        check=True)

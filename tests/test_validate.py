@@ -1,0 +1,66 @@
+"""Host input checks of the C ABI (CPU only): each rule of the block table and slot
+numbering, the first offender named, and every workload the tests and bench build
+passing."""
+import numpy as np
+import pytest
+
+from paged_kv_cache_161_amd import binding as B
+from paged_kv_cache_161_amd import workloads as W
+
+
+@pytest.fixture(scope="module", autouse=True)
+def lib():
+    return B.load()
+
+
+def _tables():
+    # two sequences over an 8-block pool: 37 tokens (3 blocks) and 16 tokens (1 block);
+    # entries past a sequence's last block are padding and never checked
+    bt = np.array([[5, 7, 2, -1], [1, 99, -3, 0]], np.int32)
+    cl = np.array([37, 16], np.int32)
+    return bt, cl
+
+
+def test_decode_tables():
+    bt, cl = _tables()
+    assert B.validate_decode_tables(bt, cl, 64, 8) == -1
+    assert B.validate_decode_tables(bt, cl, 36, 8) == 0          # ctx above the bound
+    assert B.validate_decode_tables(bt, np.array([37, 17], np.int32), 64, 8) == 1  # entry 99
+    assert B.validate_decode_tables(bt, np.array([65, 0], np.int32), 100, 8) == 0  # > 4 blocks
+    assert B.validate_decode_tables(bt, np.array([0, -1], np.int32), 64, 8) == 1
+    assert B.validate_decode_tables(bt, cl, 64, 7) == 0          # block 7 outside a 7-block pool
+    assert B.validate_decode_tables(bt, np.array([0, 0], np.int32), 0, 1) == -1   # empty contexts
+    with pytest.raises(B.PaError):
+        B.validate_decode_tables(bt, cl, 64, 0)
+
+
+def test_prefill_batch():
+    bt, cl = _tables()
+    ok = dict(num_query_tokens=12, max_query_len=8, max_context_len=64, num_blocks=8)
+    assert B.validate_prefill_batch([0, 5, 12], bt, cl, **ok) == -1
+    assert B.validate_prefill_batch([0, 5, 12], bt, cl, **{**ok, "max_query_len": 6}) == 1
+    assert B.validate_prefill_batch([1, 5, 12], bt, cl, **ok) == 0        # must start at 0
+    assert B.validate_prefill_batch([0, 6, 5], bt, cl, **ok) == 1         # decreasing
+    assert B.validate_prefill_batch([0, 5, 11], bt, cl, **ok) == 1        # short of T
+    assert B.validate_prefill_batch([0, 5, 13], bt, cl, **ok) == 1        # past T
+    assert B.validate_prefill_batch([0, 0, 12], bt, cl, **{**ok, "max_query_len": 12}) == -1
+
+
+def test_slots():
+    assert B.validate_slots([3, -1, 17, 127, -5], 8) == -1
+    assert B.validate_slots([3, 128], 8) == 1                             # past the pool
+    assert B.validate_slots([3, 40, 3], 8) == 2                           # written twice
+    assert B.validate_slots([], 8) == -1
+
+
+@pytest.mark.parametrize("i", [1, 2, 3, 4, 5, 6, 7, 8])
+def test_configs_are_valid(i):
+    w = W.make_config(i)
+    kp, vp, bt, sl = w.oracle_view()
+    nb = kp.shape[0]
+    assert B.validate_slots(sl, nb) == -1
+    if w.is_prefill:
+        assert B.validate_prefill_batch(w.query_start, bt, w.context_lens, w.num_query_tokens,
+                                        w.max_query_len, w.max_context_len, nb) == -1
+    else:
+        assert B.validate_decode_tables(bt, w.context_lens, w.max_context_len, nb) == -1
