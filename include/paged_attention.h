@@ -20,6 +20,11 @@
  *                    Flash-Decoding: split the KV axis and merge partials with the same
  *                    m, l rescaling rule.)
  *
+ * Around them: pa_decode_append (both in one launch), pa_decode_noalloc (pa_decode with
+ * no workspace argument), pa_prefill (prompt chunks over the same pool), pa_copy_blocks
+ * and the host block allocator (copy-on-write and rollback), the partition planners and
+ * host checks of the index arrays.
+ *
  * Conventions shared by every entry point
  *   - Pointers named *_pool, q, out, k_new, v_new, slot_mapping, block_tables,
  *     context_lens and workspace are DEVICE pointers (hipMalloc'd or torch CUDA
@@ -28,8 +33,11 @@
  *     16-byte boundary (every hipMalloc and torch allocation does; a view that starts
  *     inside one may not); the int32 arrays on a 4-byte boundary.  A misaligned pointer
  *     is PA_ERR_INVALID_ARG.
- *   - The caller owns every buffer.  The library allocates nothing, keeps no state
- *     across calls other than cached device attributes, and never frees caller memory.
+ *   - The caller owns every buffer.  The library allocates no device memory at run time
+ *     and never frees caller memory; the only state it keeps across calls is cached
+ *     device attributes and pa_decode_noalloc's static per-GPU buffer (a 16 MiB device
+ *     array in the library's image).  The host allocator's state lives in the handle
+ *     the caller creates and destroys.
  *   - Calls are asynchronous on `stream` (a hipStream_t passed as void*, NULL = the
  *     default stream): they return once the kernels are enqueued.
  *   - Argument errors are detected on the host before anything is enqueued; nothing is
@@ -189,7 +197,8 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
  *   workspace      device scratch of at least pa_decode_workspace_bytes(...) bytes
  *                  (may be NULL when that is 0); contents need no initialisation
  * num_q_heads must be a multiple of the pool's num_kv_heads; q-head h reads kv-head
- * h / (num_q_heads / num_kv_heads).
+ * h / (num_q_heads / num_kv_heads).  One call takes at most 65,535 sequences (the
+ * launch grid's extent; PA_ERR_UNSUPPORTED above).
  * A sequence with context length 0 gets an all-zero output.  Device-side inconsistency
  * the host cannot see -- a context length < 0, > max_context_len or
  * > max_blocks_per_seq * 16, or a needed table entry outside [0, num_blocks) -- makes
