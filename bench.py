@@ -66,13 +66,15 @@ def parse():
                     help="step: the decode step (default); copy_blocks: the copy-on-write "
                          "block copy on the workload's pool; prefill: append + paged "
                          "prefill of prompt chunks")
-    ap.add_argument("--sweep", choices=["decode-types", "decode-groups", "prefill-types"],
+    ap.add_argument("--sweep", choices=["decode-types", "decode-groups", "prefill-types",
+                                        "prefill-splits"],
                     default=None,
                     help="instead of the bench line, time one call per shape of a family "
                          "and print one JSON line of rows: decode pool types and head "
                          "sizes on the Llama-70B-shaped decode, decode GQA group sizes on "
-                         "32 x 4096 tokens, or prefill pool types and head sizes on the "
-                         "512-token chunked prefill")
+                         "32 x 4096 tokens, prefill pool types and head sizes on the "
+                         "512-token chunked prefill, or prefill launches too small to fill "
+                         "the GPU with and without key splits")
     ap.add_argument("--sweep-launches", type=int, default=0,
                     help="with --sweep: launches per timed round and warm-up launches "
                          "(default 100 and 200 for decode, 30 and 20 for prefill); small "
@@ -470,9 +472,29 @@ def bench_prefill(args, w, PA, U, dev):
 
 
 def sweep_shapes(name, W):
-    """(label, Spec) of one shape family, each derived from a named workload."""
+    """(label, Spec, prefill key splits) of one shape family, each derived from a named
+    workload (key splits 0 = the library's choice)."""
     import dataclasses
+    import re
     fp8 = dict(kv_dtype="fp8", k_scale=0.0117, v_scale=0.0093)
+    if name == "prefill-splits":
+        # one request's chunk over a long context, and a few long decode rows alone:
+        # 64 q / 8 kv heads, d 128, bf16, each without a key split and with the
+        # library's choice
+        base = W.config_spec(PREFILL_HEADLINE)
+        shapes = [("1 x 512-token chunk at 32k", dict(context_lens=[32768], query_lens=[512])),
+                  ("1 x 256-token chunk at 32k", dict(context_lens=[32768], query_lens=[256])),
+                  ("2 x 256-token chunks at 16k", dict(context_lens=[16384] * 2,
+                                                       query_lens=[256] * 2)),
+                  ("4 decode rows at 32k", dict(context_lens=[32768] * 4, query_lens=[1] * 4))]
+        out = []
+        for label, kw in shapes:
+            for ks in (1, 0):
+                tag = f"{label}, {'no split' if ks == 1 else 'auto split'}"
+                spec = dataclasses.replace(base, name=base.name + "_" + re.sub(
+                    r"[^A-Za-z0-9]+", "_", label).strip("_"), spare_blocks=1, **kw)
+                out.append((tag, spec, ks))
+        return out
     if name == "prefill-types":
         base = W.config_spec(PREFILL_HEADLINE)
         rows = [("bf16 d128", {}), ("f16 d128", dict(dtype="f16")),
@@ -498,9 +520,8 @@ def sweep_shapes(name, W):
                 ("bf16 G32 (128 q / 4 kv)", dict(num_q_heads=128, num_kv_heads=4)),
                 ("fp8/bf16 G32 (64 q / 2 kv)", dict(num_kv_heads=2, **fp8)),
                 ("fp8/bf16 G64 MQA (64 q / 1 kv)", dict(num_kv_heads=1, **fp8))]
-    import re
     return [(label, dataclasses.replace(base, name=base.name + "_" +
-                                        re.sub(r"[^A-Za-z0-9]+", "_", label).strip("_"), **kw))
+                                        re.sub(r"[^A-Za-z0-9]+", "_", label).strip("_"), **kw), 0)
             for label, kw in rows]
 
 
@@ -511,7 +532,7 @@ def bench_sweep(args, PA, W, U, dev):
     rows = []
     if args.calibrate:
         calibration_copy(dev)
-    for label, spec in sweep_shapes(args.sweep, W):
+    for label, spec, key_splits in sweep_shapes(args.sweep, W):
         w = W.build(spec)
         sc = U.scales(w)
         d = U.device_inputs(w, dev)
@@ -521,9 +542,18 @@ def bench_sweep(args, PA, W, U, dev):
             PA.cache_append(kp, vp, d["k_new"], d["v_new"], d["slot_mapping"], **sc)
             qs = torch.from_numpy(w.query_start).to(dev)
 
+            ks_used = key_splits or PA.prefill_key_splits(
+                w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.num_query_tokens,
+                w.max_query_len, w.max_context_len, w.kv_dtype)
+            ws_bytes = PA.prefill_workspace_bytes(
+                w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.num_query_tokens,
+                w.max_query_len, w.max_context_len, key_splits, w.kv_dtype)
+            pws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+
             def call(i):
                 PA.prefill(d["q"], kp, vp, qs, d["block_tables"], d["context_lens"],
-                           float(w.scale), w.max_context_len, w.max_query_len, out=out, **sc)
+                           float(w.scale), w.max_context_len, w.max_query_len, out=out,
+                           key_splits=key_splits, workspace=pws, **sc)
             n_warm, n_launch = 20, 30
             if args.sweep_launches > 0:
                 n_warm, n_launch = args.sweep_launches, args.sweep_launches
@@ -565,7 +595,8 @@ def bench_sweep(args, PA, W, U, dev):
         row = {"shape": label, "workload": spec.name, "us": round(best, 2), "finite": finite}
         if w.is_prefill:
             tf = prefill_flops(w) / best / 1e6
-            row.update(tflops=round(tf, 1), pct_mfma_peak=round(100 * tf / MFMA_BF16_PEAK_TFLOPS, 1))
+            row.update(tflops=round(tf, 1), pct_mfma_peak=round(100 * tf / MFMA_BF16_PEAK_TFLOPS, 1),
+                       key_splits=int(ks_used))
         else:
             by = w.unique_kv_bytes()
             row.update(partition_tokens=ptok, kv_bytes=int(by), GBps=round(by / best / 1e3, 1),

@@ -267,6 +267,16 @@ pa_status pa_decode_append(const pa_kv_pool *pool, const void *q, const void *k_
  *   block_tables, max_blocks_per_seq, context_lens, max_context_len: as for pa_decode;
  *                  context_lens[b] counts the chunk, whose K/V rows must already be in
  *                  the pool (pa_cache_append first)
+ *   key_splits     0 = automatic; otherwise 1 .. 8: the keys each (sequence, kv-head,
+ *                  query tile) attends are cut into this many contiguous ranges,
+ *                  computed by separate workgroups and merged by the max/normaliser rule
+ *                  ("Deep dive into vLLM 06", Flash-Decoding: split the KV axis when the
+ *                  grid would leave the GPU's CUs idle, merge the partials exactly).
+ *                  Automatic splits only a launch with fewer units than CUs (a single
+ *                  long prompt's chunk, a few long decode rows), see pa_prefill_key_splits.
+ *   workspace      device scratch of at least pa_prefill_workspace_bytes(...) bytes for
+ *                  the same arguments (may be NULL when that is 0); contents need no
+ *                  initialisation
  * Query i of sequence b is token context_lens[b] - q_len + i and attends to tokens
  * 0 .. context_lens[b] - q_len + i; a query placed before the context (q_len >
  * context_lens[b]) gets a zero row.  A chunk of one query is exactly a decode step.
@@ -276,12 +286,36 @@ pa_status pa_decode_append(const pa_kv_pool *pool, const void *q, const void *k_
  * Device-side inconsistency: a bad context length or a needed table entry outside
  * [0, num_blocks) makes that sequence's rows NaN; a query range that is decreasing,
  * longer than max_query_len or outside [0, num_query_tokens) leaves that sequence's
- * rows unwritten.  Nothing out of bounds is ever read or written.  No workspace. */
+ * rows unwritten.  Nothing out of bounds is ever read or written. */
 pa_status pa_prefill(const pa_kv_pool *pool, const void *q, void *out, int32_t num_seqs,
                      int32_t num_q_heads, float scale, const int32_t *query_start,
                      int32_t num_query_tokens, int32_t max_query_len,
                      const int32_t *block_tables, int32_t max_blocks_per_seq,
-                     const int32_t *context_lens, int32_t max_context_len, void *stream);
+                     const int32_t *context_lens, int32_t max_context_len,
+                     int32_t key_splits, void *workspace, size_t workspace_bytes,
+                     void *stream);
+
+/* The key splits pa_prefill uses when key_splits == 0: as many as bring the launch's
+ * (sequence, kv-head, query tile) units up to one per CU of the MI355X (units estimated
+ * from these host bounds: at most num_query_tokens / q_tile + num_seqs query tiles per
+ * kv-head, q_tile query positions per tile), at most 8, and each split covering at
+ * least 1,024 keys of max_context_len; 1 when the units already fill the CUs (the
+ * pages' Flash-Decoding rule, "Deep dive into vLLM 06": split the KV axis only where
+ * the parallelism is missing).  dtype is the pools' pa_dtype.  Host-only; -1 on bad
+ * input. */
+int32_t pa_prefill_key_splits(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t dtype, int32_t num_query_tokens,
+                              int32_t max_query_len, int32_t max_context_len);
+
+/* Workspace bytes pa_prefill needs for these arguments (key_splits as passed to it):
+ * with S > 1 splits, one unnormalised fp32 output row, its running max and normaliser
+ * per (query row, q-head, split), i.e. num_query_tokens * num_q_heads * S *
+ * (head_dim + 2) * 4 bytes; 0 without a split.  SIZE_MAX on invalid arguments.
+ * Host-only. */
+size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t dtype, int32_t num_query_tokens,
+                                  int32_t max_query_len, int32_t max_context_len,
+                                  int32_t key_splits);
 
 /* Copy whole physical blocks inside the pool: for each pair i, block pairs[2i] (src)
  * is copied to block pairs[2i+1] (dst), every kv-head, in both K and V, bytes

@@ -74,7 +74,11 @@ def load(path: str = LIB_PATH):
                                      ctypes.c_float, P, I32, P, I32, I32, P, ctypes.c_size_t, P]
     lib.pa_decode_append.restype = I32
     lib.pa_prefill.argtypes = [ctypes.POINTER(PaKvPool), P, P, I32, I32, ctypes.c_float, P, I32,
-                               I32, P, I32, P, I32, P]
+                               I32, P, I32, P, I32, I32, P, ctypes.c_size_t, P]
+    lib.pa_prefill_key_splits.argtypes = [I32, I32, I32, I32, I32, I32, I32, I32]
+    lib.pa_prefill_key_splits.restype = I32
+    lib.pa_prefill_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32, I32, I32, I32]
+    lib.pa_prefill_workspace_bytes.restype = ctypes.c_size_t
     lib.pa_prefill.restype = I32
     lib.pa_status_string.argtypes = [I32]
     lib.pa_status_string.restype = ctypes.c_char_p
@@ -353,15 +357,39 @@ def decode_append(q, k_pool, v_pool, k_new, v_new, block_tables, context_lens, s
     return out
 
 
+def prefill_key_splits(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                       num_query_tokens: int, max_query_len: int, max_context_len: int,
+                       dtype=torch.bfloat16) -> int:
+    """pa_prefill_key_splits: the key splits pa_prefill chooses with key_splits=0."""
+    return int(load().pa_prefill_key_splits(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                            dtype_code(dtype), num_query_tokens, max_query_len,
+                                            max_context_len))
+
+
+def prefill_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                            num_query_tokens: int, max_query_len: int, max_context_len: int,
+                            key_splits: int = 0, dtype=torch.bfloat16) -> int:
+    """pa_prefill_workspace_bytes; raises on invalid arguments."""
+    n = load().pa_prefill_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                          dtype_code(dtype), num_query_tokens, max_query_len,
+                                          max_context_len, key_splits)
+    if n == ctypes.c_size_t(-1).value:
+        raise PaError(1, "invalid arguments for pa_prefill_workspace_bytes")
+    return int(n)
+
+
 def prefill(q, k_pool, v_pool, query_start, block_tables, context_lens, scale: float,
             max_context_len: int, max_query_len: int, out: Optional[torch.Tensor] = None,
-            k_scale=1.0, v_scale=1.0) -> torch.Tensor:
+            k_scale=1.0, v_scale=1.0, key_splits: int = 0,
+            workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Causal attention of prompt-chunk queries over the paged cache.
 
     q [T][Hq][d]; query_start [B+1] int32 (rows of sequence b: query_start[b] ..
     query_start[b+1]-1); block_tables [B][max_blocks] int32; context_lens [B] int32
     (chunk included, appended beforehand); max_context_len / max_query_len: host-side
-    bounds.  Returns out [T][Hq][d] in q's dtype.
+    bounds; key_splits: 0 = automatic, else 1 .. 8 key ranges per query tile merged
+    afterwards (workspace: device bytes for their partials; allocated here when None
+    and needed).  Returns out [T][Hq][d] in q's dtype.
     """
     act = q.dtype if k_pool.dtype in FP8_STORAGE else None
     pool = make_pool(k_pool, v_pool, act, k_scale, v_scale)
@@ -374,13 +402,23 @@ def prefill(q, k_pool, v_pool, query_start, block_tables, context_lens, scale: f
     if out is None:
         out = torch.empty_like(q)
     act = _act_dtype(pool)
-    st = load().pa_prefill(ctypes.byref(pool), _dev_ptr(q, "q", act), _dev_ptr(out, "out", act),
-                           B, hq, ctypes.c_float(scale),
-                           _dev_ptr(query_start, "query_start", torch.int32), T, max_query_len,
-                           _dev_ptr(block_tables, "block_tables", torch.int32),
-                           block_tables.shape[1],
-                           _dev_ptr(context_lens, "context_lens", torch.int32),
-                           max_context_len, _stream_handle(q.device))
+    args = (ctypes.byref(pool), _dev_ptr(q, "q", act), _dev_ptr(out, "out", act),
+            B, hq, ctypes.c_float(scale),
+            _dev_ptr(query_start, "query_start", torch.int32), T, max_query_len,
+            _dev_ptr(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+            _dev_ptr(context_lens, "context_lens", torch.int32), max_context_len, key_splits)
+    fn = load().pa_prefill
+    stream = _stream_handle(q.device)
+    if workspace is not None:
+        st = fn(*args, _dev_ptr(workspace, "workspace"),
+                workspace.numel() * workspace.element_size(), stream)
+    else:
+        st = fn(*args, None, 0, stream)              # no split: no workspace needed
+    if st == PA_ERR_WORKSPACE:
+        need = prefill_workspace_bytes(B, hq, pool.num_kv_heads, d, T, max_query_len,
+                                       max_context_len, key_splits, pool.dtype)
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device) if need else None
+        st = fn(*args, ws.data_ptr() if need else None, need, stream)
     _raise(st)
     return out
 

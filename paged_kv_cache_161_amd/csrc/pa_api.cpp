@@ -5,6 +5,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <atomic>
 #include <mutex>
 
@@ -340,6 +341,65 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
 
 namespace {
 
+// Fewest keys of the longest context one prefill key split covers: below that the
+// partials' write and merge outweigh the CUs the split brings in.
+constexpr int64_t kPrefillMinSplitKeys = 1024;
+
+// Scalar checks shared by pa_prefill and its planners; PA_OK when the shapes are ones
+// the prefill kernels take.
+pa_status check_prefill_scalars(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t dtype, int32_t num_query_tokens,
+                                int32_t max_query_len, int32_t max_context_len,
+                                int32_t key_splits)
+{
+    if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+        num_q_heads % num_kv_heads != 0 || num_query_tokens < 0 || max_query_len < 0 ||
+        max_context_len < 0 || key_splits < 0)
+        return PA_ERR_INVALID_ARG;
+    if (!dtype_ok(dtype) || !head_dim_ok(dtype, head_dim))
+        return PA_ERR_UNSUPPORTED;
+    // 16-bit MFMA kernels only (fp8 pools convert to their 16-bit activation type)
+    if (dtype == PA_F32)
+        return PA_ERR_UNSUPPORTED;
+    if (key_splits > pa::kPrefillMaxSplits)
+        return PA_ERR_UNSUPPORTED;
+    const int32_t group = num_q_heads / num_kv_heads;
+    if (group > pa::prefill_rows_per_group(head_dim))
+        return PA_ERR_UNSUPPORTED;
+    if ((int64_t)num_query_tokens * num_q_heads > INT32_MAX)
+        return PA_ERR_UNSUPPORTED;
+    if (max_context_len > INT32_MAX - kBlock)         // block counts stay in int32
+        return PA_ERR_UNSUPPORTED;
+    if ((int64_t)num_kv_heads * kBlock * head_dim > UINT32_MAX)
+        return PA_ERR_UNSUPPORTED;                    // block stride in 32 bits
+    return PA_OK;
+}
+
+// Key splits of a prefill launch: key_splits when given; otherwise as many as bring the
+// launch's (sequence, kv-head, query tile) units up to one per CU, at most
+// kPrefillMaxSplits and at least kPrefillMinSplitKeys keys of the longest context per
+// split.  Units are estimated from host bounds only: per kv-head the tiles of T query
+// rows in chunks of at most max_query_len, i.e. at most T / q_tile + B and B x
+// ceil(max_query_len / q_tile) -- ragged batches are overestimated, so they split less.
+int32_t choose_prefill_splits(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t num_query_tokens, int32_t max_query_len,
+                              int32_t max_context_len, int32_t key_splits)
+{
+    if (key_splits > 0)
+        return key_splits;
+    const int64_t q_tile = pa::prefill_rows_per_group(head_dim) / (num_q_heads / num_kv_heads);
+    const int64_t qtiles = ((int64_t)max_query_len + q_tile - 1) / q_tile;
+    const int64_t tiles = std::min<int64_t>((num_query_tokens + q_tile - 1) / q_tile + num_seqs,
+                                            (int64_t)num_seqs * qtiles);
+    const int64_t units = (int64_t)num_kv_heads * tiles;
+    if (units <= 0 || units * 2 > pa::kTargetGroups)
+        return 1;
+    int64_t sp = pa::kTargetGroups / units;
+    sp = std::min<int64_t>(sp, pa::kPrefillMaxSplits);
+    sp = std::min<int64_t>(sp, max_context_len / kPrefillMinSplitKeys);
+    return (int32_t)std::max<int64_t>(sp, 1);
+}
+
 // pa_decode, and pa_decode_append when k_new / v_new are given.
 pa_status decode_impl(const pa_kv_pool *pool, const void *q, const void *k_new,
                       const void *v_new, void *out, int32_t num_seqs, int32_t num_q_heads,
@@ -500,32 +560,55 @@ pa_status pa_decode_append(const pa_kv_pool *pool, const void *q, const void *k_
                        workspace, workspace_bytes, stream);
 }
 
+int32_t pa_prefill_key_splits(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t dtype, int32_t num_query_tokens,
+                              int32_t max_query_len, int32_t max_context_len)
+{
+    if (check_prefill_scalars(num_seqs, num_q_heads, num_kv_heads, head_dim, dtype,
+                              num_query_tokens, max_query_len, max_context_len, 0) != PA_OK)
+        return -1;
+    return choose_prefill_splits(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                 num_query_tokens, max_query_len, max_context_len, 0);
+}
+
+size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t dtype, int32_t num_query_tokens,
+                                  int32_t max_query_len, int32_t max_context_len,
+                                  int32_t key_splits)
+{
+    if (check_prefill_scalars(num_seqs, num_q_heads, num_kv_heads, head_dim, dtype,
+                              num_query_tokens, max_query_len, max_context_len,
+                              key_splits) != PA_OK)
+        return SIZE_MAX;
+    if (num_seqs == 0 || num_query_tokens == 0 || max_query_len == 0)
+        return 0;
+    const int32_t sp = choose_prefill_splits(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                             num_query_tokens, max_query_len, max_context_len,
+                                             key_splits);
+    if (sp <= 1)
+        return 0;
+    return (size_t)num_query_tokens * num_q_heads * sp * (head_dim + 2) * sizeof(float);
+}
+
 pa_status pa_prefill(const pa_kv_pool *pool, const void *q, void *out, int32_t num_seqs,
                      int32_t num_q_heads, float scale, const int32_t *query_start,
                      int32_t num_query_tokens, int32_t max_query_len,
                      const int32_t *block_tables, int32_t max_blocks_per_seq,
-                     const int32_t *context_lens, int32_t max_context_len, void *stream)
+                     const int32_t *context_lens, int32_t max_context_len,
+                     int32_t key_splits, void *workspace, size_t workspace_bytes, void *stream)
 {
     pa_status st = check_pool(pool);
     if (st != PA_OK)
         return st;
-    if (num_seqs < 0 || num_q_heads <= 0 || num_q_heads % pool->num_kv_heads != 0 ||
-        num_query_tokens < 0 || max_query_len < 0 || max_context_len < 0 ||
-        max_blocks_per_seq < 0 || !isfinite(scale) || !(scale > 0.f))
+    if (max_blocks_per_seq < 0 || !isfinite(scale) || !(scale > 0.f))
         return PA_ERR_INVALID_ARG;
-    // 16-bit MFMA kernels only (fp8 pools convert to their 16-bit activation type)
-    if (pool->dtype == PA_F32)
-        return PA_ERR_UNSUPPORTED;
+    st = check_prefill_scalars(num_seqs, num_q_heads, pool->num_kv_heads, pool->head_dim,
+                               pool->dtype, num_query_tokens, max_query_len, max_context_len,
+                               key_splits);
+    if (st != PA_OK)
+        return st;
     const int32_t group = num_q_heads / pool->num_kv_heads;
     const int32_t rows = pa::prefill_rows_per_group(pool->head_dim);
-    if (group > rows)
-        return PA_ERR_UNSUPPORTED;
-    if ((int64_t)num_query_tokens * num_q_heads > INT32_MAX)
-        return PA_ERR_UNSUPPORTED;
-    if (max_context_len > INT32_MAX - kBlock)         // block counts stay in int32
-        return PA_ERR_UNSUPPORTED;
-    if ((int64_t)pool->num_kv_heads * kBlock * pool->head_dim > UINT32_MAX)
-        return PA_ERR_UNSUPPORTED;                    // block stride in 32 bits
     if (num_seqs == 0 || num_query_tokens == 0 || max_query_len == 0)
         return PA_OK;
     if (!q || !out || !query_start || !block_tables || !context_lens || max_blocks_per_seq == 0)
@@ -538,6 +621,18 @@ pa_status pa_prefill(const pa_kv_pool *pool, const void *q, void *out, int32_t n
     const int64_t pairs = (int64_t)num_seqs * pool->num_kv_heads;
     if (pairs > INT32_MAX || ((pairs + 7) / 8) * 8 * qtiles > INT32_MAX)
         return PA_ERR_UNSUPPORTED;
+    const int32_t splits = choose_prefill_splits(num_seqs, num_q_heads, pool->num_kv_heads,
+                                                 pool->head_dim, num_query_tokens,
+                                                 max_query_len, max_context_len, key_splits);
+    const size_t need = splits > 1 ? pa_prefill_workspace_bytes(
+                                         num_seqs, num_q_heads, pool->num_kv_heads,
+                                         pool->head_dim, pool->dtype, num_query_tokens,
+                                         max_query_len, max_context_len, key_splits)
+                                   : 0;
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return PA_ERR_WORKSPACE;
+    if (need > 0 && !aligned16(workspace))
+        return PA_ERR_INVALID_ARG;
 
     pa::PrefillArgs a;
     a.k_pool = pool->k_pool;
@@ -564,6 +659,11 @@ pa_status pa_prefill(const pa_kv_pool *pool, const void *q, void *out, int32_t n
     a.k_head_scales = k_heads(pool);
     a.v_head_scales = v_heads(pool);
     a.longest_first = (num_seqs > 1 && num_seqs <= pa::kLongestFirstMax) ? 1 : 0;
+    a.splits = splits;
+    const size_t partials = (size_t)num_query_tokens * num_q_heads * splits;
+    a.ws_o = splits > 1 ? static_cast<float *>(workspace) : nullptr;
+    a.ws_m = splits > 1 ? a.ws_o + partials * pool->head_dim : nullptr;
+    a.ws_l = splits > 1 ? a.ws_m + partials : nullptr;
     hipError_t e = pa::launch_prefill(pool->dtype, pool->act_dtype, pool->head_dim, a,
                                       static_cast<hipStream_t>(stream));
     return e == hipSuccess ? PA_OK : PA_ERR_HIP;

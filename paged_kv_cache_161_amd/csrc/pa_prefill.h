@@ -32,7 +32,17 @@ struct PrefillArgs {
     // multiplies scale_log2 for its head, a non-null v_head_scales replaces v_scale.
     const float *k_head_scales;
     const float *v_head_scales;
+    // key splits (launch grid y): each (sequence, kv-head, query tile) is cut into this
+    // many contiguous ranges of its key steps; above 1 the workgroups write partials
+    // (slot = (q-row * hq + head) * splits + split) that pa_prefill_reduce merges
+    int32_t splits;
+    float *ws_o;                      // [T * hq * splits][D] unnormalised outputs
+    float *ws_m;                      // [T * hq * splits] reference max (log2 domain)
+    float *ws_l;                      // [T * hq * splits] normaliser
 };
+
+// Most key splits one prefill launch takes.
+constexpr int kPrefillMaxSplits = 8;
 
 // Prefill workgroup shape: waves and 16-row MFMA column blocks per wave.
 #ifndef PA_PREFILL_WAVES
@@ -58,5 +68,12 @@ int prefill_rows_per_group(int head_dim);
 
 hipError_t launch_prefill(int dtype, int act_dtype, int head_dim, const PrefillArgs &a,
                           hipStream_t stream);
+
+// Token rows one reduce workgroup merges, all q-heads of one kv-head for each: 256
+// threads x 4 items of 4 elements, at least one row.
+constexpr int prefill_reduce_rows(int group, int head_dim)
+{
+    return group * head_dim / 4 >= 1024 ? 1 : 1024 / (group * head_dim / 4);
+}
 
 }  // namespace pa

@@ -145,7 +145,30 @@ __device__ __forceinline__ u32x4 keep_tokens8(u32x4 v, int t0, int valid)
     return v;
 }
 
-template <int DT, int AT, int D, int NW, int C, bool IDLE, bool SMALLQ>
+// One row's partial result of a key split, for the reduce kernel: the unnormalised
+// output (this lane's four elements of each 16-element block, times the V scale), the
+// reference max it is relative to (log2 domain; -inf when the split saw no key) and the
+// normaliser.  A workgroup with bad input writes NaN, which the merge propagates.
+template <int NDB>
+__device__ __forceinline__ void store_partial(const PrefillArgs &a, int orow, int split,
+                                              int nsplit, const f32x4 (&o)[NDB], float m_raw,
+                                              float sl, float l, float vs, bool bad, int g)
+{
+    constexpr int D = NDB * 16;
+    const float qnan = __builtin_nanf("");
+    const size_t slot = (size_t)orow * nsplit + split;
+#pragma unroll
+    for (int n = 0; n < NDB; ++n) {
+        const f32x4 v = bad ? f32x4{qnan, qnan, qnan, qnan} : o[n] * vs;
+        *reinterpret_cast<f32x4 *>(a.ws_o + slot * D + 16 * n + 4 * g) = v;
+    }
+    if (g == 0) {
+        a.ws_m[slot] = bad ? qnan : (m_raw == -INFINITY ? -INFINITY : m_raw * sl);
+        a.ws_l[slot] = bad ? qnan : l;
+    }
+}
+
+template <int DT, int AT, int D, int NW, int C, bool IDLE, bool SMALLQ, bool SPLIT>
 __global__ __launch_bounds__(NW *kWave, C * D <= 256 ? 2 : 1) void pa_prefill_kernel(PrefillArgs a)
 {
     using Elem = typename std::conditional<DT == DT_FP8, uint8_t, uint16_t>::type;
@@ -286,6 +309,19 @@ __global__ __launch_bounds__(NW *kWave, C * D <= 256 ? 2 : 1) void pa_prefill_ke
     const int first = ctx - q_len + p_lo;                // position of the tile's first
     const int key_end = bad_ctx ? 0 : max(0, first + n_here);   // keys [0, key_end)
     const int nsteps = (key_end + 31) / 32;
+    // This workgroup's share of the tile's 32-key steps: all of them, or, in the
+    // instance for launches that split keys (SPLIT, gridDim.y splits: a grid too small
+    // to fill the chip), the split-th of gridDim.y contiguous ranges, whose partial
+    // (m, l, O) the reduce kernel merges with the max/normaliser rule.  Ranges start
+    // on even steps, so every range but the tile's last holds whole pairs of steps and
+    // the staged loop, which runs pairs, never computes a step outside its range; the
+    // last range's padding step lies past every row's position, as without a split.
+    const int nsplit = SPLIT ? (int)gridDim.y : 1;
+    const int split = SPLIT ? (int)blockIdx.y : 0;
+    const int npair_all = (nsteps + 1) / 2;
+    const int s_begin = SPLIT ? 2 * (int)(((int64_t)npair_all * split) / nsplit) : 0;
+    const int s_end =
+        SPLIT ? min(nsteps, 2 * (int)(((int64_t)npair_all * (split + 1)) / nsplit)) : nsteps;
 
     // This kv-head's scales: fp8 pools with per-head arrays read them here (a bad one
     // poisons the head's rows); otherwise the pool's, folded in on the host.
@@ -392,8 +428,8 @@ __global__ __launch_bounds__(NW *kWave, C * D <= 256 ? 2 : 1) void pa_prefill_ke
             const float sl = sl_h;
             const float grow_thr = fminf(kRescaleSlack / sl, 3.0e38f);
             const u32x4 ones = {one_pair<AT>(), one_pair<AT>(), one_pair<AT>(), one_pair<AT>()};
-            const int s_lo = (int)(((int64_t)nsteps * wave) / NW);
-            const int s_hi = (int)(((int64_t)nsteps * (wave + 1)) / NW);
+            const int s_lo = s_begin + (int)(((int64_t)(s_end - s_begin) * wave) / NW);
+            const int s_hi = s_begin + (int)(((int64_t)(s_end - s_begin) * (wave + 1)) / NW);
             // this lane's K row (product row r16) and V^T piece, inside a step
             const int k_blk = r16 >> 3;                                    // 0 or 1
             const int k_tok0 = 8 * ((r16 >> 2) & 1) + (r16 & 3);          // + 4 t
@@ -667,6 +703,15 @@ __global__ __launch_bounds__(NW *kWave, C * D <= 256 ? 2 : 1) void pa_prefill_ke
 #pragma unroll
                         for (int w = 0; w < NW; ++w)
                             l += s_l[c][w][r16];
+                        if constexpr (SPLIT) {
+                            float mx = -INFINITY;
+#pragma unroll
+                            for (int w = 0; w < NW; ++w)
+                                mx = fmaxf(mx, s_m[c][w][r16]);
+                            store_partial(a, orow1[c], split, nsplit, o1[c], mx, sl, l, vs_h,
+                                          any_bad, g);
+                            continue;
+                        }
                         const float fo = l > 0.f ? vs_h / l : 0.f;
 #pragma unroll
                         for (int n = 0; n < NDB; ++n) {
@@ -927,33 +972,35 @@ __global__ __launch_bounds__(NW *kWave, C * D <= 256 ? 2 : 1) void pa_prefill_ke
     // unrolled by two, so the ring slots and the two score sets are fixed registers,
     // and runs whole pairs of passes with no other exit: every pass issues the same
     // loads and waits, so each wait covers exactly the slot it needs.  Loads past the
-    // last step are clamped to it; steps past the last stage zeros, and every key of
-    // theirs lies after every row's position, so they are masked out entirely and
-    // change nothing.  Every LDS buffer is rewritten only after a barrier that follows
-    // all reads of its previous contents.
-    if (nsteps > 0) {
-        const int last = nsteps - 1;
+    // last step are clamped to it; steps past the tile's last stage zeros, and every
+    // key of theirs lies after every row's position, so they are masked out entirely
+    // and change nothing.  Steps are counted from the tile's first key; the workgroup
+    // walks steps s_begin .. s_end-1.  Every LDS buffer is rewritten only after a
+    // barrier that follows all reads of its previous contents.
+    if (s_end > s_begin) {
+        const int sb = s_begin;
+        const int last = s_end - 1;
         int raw[2], ph_a[2], ph_b[2];
-        table(0, raw);
-        resolve(0, raw, ph_a);
-        table(min(1, last), raw);
-        resolve(min(1, last), raw, ph_b);
+        table(sb, raw);
+        resolve(sb, raw, ph_a);
+        table(min(sb + 1, last), raw);
+        resolve(min(sb + 1, last), raw, ph_b);
         fetch_k(ph_a, 0);
         fetch_k(ph_b, 1);
         fetch_v(ph_a, 0);
         stash_k(0, 0);                            // waits for these loads and for q
         stash_k(1, 1);
-        stash_v(0, 0, 0);
-        table(min(2, last), raw);
-        resolve(min(2, last), raw, ph_a);            // step 2
+        stash_v(sb, 0, 0);
+        table(min(sb + 2, last), raw);
+        resolve(min(sb + 2, last), raw, ph_a);       // step sb+2
         fetch_k(ph_a, 0);
-        table(min(3, last), raw);
+        table(min(sb + 3, last), raw);
         int ph_k[2];                                 // block ids of the last K fetch
-        resolve(min(3, last), raw, ph_k);            // step 3
+        resolve(min(sb + 3, last), raw, ph_k);       // step sb+3
         fetch_k(ph_k, 1);
-        fetch_v(ph_b, 1);                            // V of step 1
-        fetch_v(ph_a, 0);                            // V of step 2
-        table(min(4, last), raw);
+        fetch_v(ph_b, 1);                            // V of step sb+1
+        fetch_v(ph_a, 0);                            // V of step sb+2
+        table(min(sb + 4, last), raw);
         __syncthreads();
         // Pass it's staging, first thing after the barrier that ended pass it-1: K of
         // step it+2 and V of step it+1 into the LDS buffers whose contents (steps it and
@@ -962,16 +1009,16 @@ __global__ __launch_bounds__(NW *kWave, C * D <= 256 ? 2 : 1) void pa_prefill_ke
         // have the whole pass to complete before the next barrier waits on them.
         auto stage = [&](int it, int u) {
             stash_k(u, u);
-            stash_v(it + 1, u ^ 1, u ^ 1);
+            stash_v(sb + it + 1, u ^ 1, u ^ 1);
             int ph_n[2];
-            resolve(min(it + 4, last), raw, ph_n);
-            fetch_k(ph_n, u);                        // K of step it+4
-            fetch_v(ph_k, u ^ 1);                    // V of step it+3
+            resolve(min(sb + it + 4, last), raw, ph_n);
+            fetch_k(ph_n, u);                        // K of step sb+it+4
+            fetch_v(ph_k, u ^ 1);                    // V of step sb+it+3
             ph_k[0] = ph_n[0];
             ph_k[1] = ph_n[1];
-            table(min(it + 5, last), raw);
+            table(min(sb + it + 5, last), raw);
         };
-        const int npairs = (nsteps + 1) / 2;
+        const int npairs = (s_end - s_begin + 1) / 2;
         // A wave whose rows are all idle (a short chunk, a decode row in the tile)
         // runs only the staging: the same loads, stores and barriers, no products.
         // Launches where every tile is full (IDLE false) carry no such branch.
@@ -979,7 +1026,7 @@ __global__ __launch_bounds__(NW *kWave, C * D <= 256 ? 2 : 1) void pa_prefill_ke
         f32x4 sc[2][C][2];
         if (!idle) {
             qk(0, sc[0]);
-            mask_max(0, sc[0]);
+            mask_max(sb, sc[0]);
         }
         // Pass 0 restages buffer 0 (K of step 2): every wave's reads of step 0's K
         // must be done first.
@@ -1030,7 +1077,7 @@ __global__ __launch_bounds__(NW *kWave, C * D <= 256 ? 2 : 1) void pa_prefill_ke
                     }
                     __builtin_amdgcn_sched_group_barrier(0x008, NDB * C + C, 0);
                     __syncthreads();
-                    mask_max(it + 1, sc[u ^ 1]);
+                    mask_max(sb + it + 1, sc[u ^ 1]);
                 }
             }
         }
@@ -1043,6 +1090,10 @@ __global__ __launch_bounds__(NW *kWave, C * D <= 256 ? 2 : 1) void pa_prefill_ke
         if (orow[c] < 0)
             continue;
         const float l = lacc[c][0];
+        if constexpr (SPLIT) {
+            store_partial(a, orow[c], split, nsplit, o[c], m_run[c], sl, l, vs_h, any_bad, g);
+            continue;
+        }
         const float f = l > 0.f ? vs_h / l : 0.f;
 #pragma unroll
         for (int n = 0; n < NDB; ++n) {
@@ -1058,24 +1109,117 @@ __global__ __launch_bounds__(NW *kWave, C * D <= 256 ? 2 : 1) void pa_prefill_ke
     }
 }
 
+// ------------------------------------------------------------------ reduce kernel
+
+// Merges the key splits' partials of every query row with the max/normaliser rule of
+// the decode path ("Deep dive into vLLM 06", Flash-Decoding: each split's partial
+// result carries its own max and sum):
+//   M = max_s m_s,   out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s
+// (splits that saw no key have m = -inf and weigh nothing; a query with no key at all
+// gets a zero row; a NaN partial, written by a workgroup with bad input, gives NaN).
+// One workgroup per (row chunk, kv-head, sequence): its rows are validated as the main
+// kernel does, so a malformed query range stays unwritten.  A thread owns 4
+// consecutive elements of one (row, q-head) and issues every split's loads together.
+template <int AT, int D>
+__global__ __launch_bounds__(256) void pa_prefill_reduce(PrefillArgs a)
+{
+    const int b = blockIdx.z;
+    const int kvh = blockIdx.y;
+    const int q0 = a.query_start[b];
+    const int q_len = a.query_start[b + 1] - q0;
+    if (q0 < 0 || q_len < 0 || q_len > a.max_query_len || q0 > a.num_tokens - q_len)
+        return;
+    const int rows = prefill_reduce_rows(a.group, D);
+    const int p0 = blockIdx.x * rows;
+    const int S = a.splits;
+    const int items = min(rows, q_len - p0) * a.group * (D / 4);
+    for (int it = threadIdx.x; it < items; it += blockDim.x) {
+        const int e4 = it % (D / 4);
+        const int hr = it / (D / 4);
+        const int h = hr % a.group;
+        const int p = p0 + hr / a.group;
+        const size_t row = (size_t)(q0 + p) * a.num_q_heads + kvh * a.group + h;
+        float m[kPrefillMaxSplits], l[kPrefillMaxSplits];
+        f32x4 o[kPrefillMaxSplits];
+#pragma unroll
+        for (int sp = 0; sp < kPrefillMaxSplits; ++sp) {
+            if (sp < S) {
+                const size_t slot = row * S + sp;
+                m[sp] = a.ws_m[slot];
+                l[sp] = a.ws_l[slot];
+                o[sp] = *reinterpret_cast<const f32x4 *>(a.ws_o + slot * D + 4 * e4);
+            }
+        }
+        float M = -INFINITY;
+        bool nan = false;
+#pragma unroll
+        for (int sp = 0; sp < kPrefillMaxSplits; ++sp)
+            if (sp < S) {
+                M = fmaxf(M, m[sp]);
+                nan |= m[sp] != m[sp];
+            }
+        f32x4 num = {0.f, 0.f, 0.f, 0.f};
+        float den = 0.f;
+#pragma unroll
+        for (int sp = 0; sp < kPrefillMaxSplits; ++sp)
+            if (sp < S) {
+                const float f = m[sp] == -INFINITY ? 0.f : exp2_fast(m[sp] - M);
+                num += f * o[sp];
+                den += f * l[sp];
+            }
+        f32x4 v = den > 0.f ? num * (1.f / den) : f32x4{0.f, 0.f, 0.f, 0.f};
+        if (nan)
+            v = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""),
+                      __builtin_nanf("")};
+        uint16_t *dst = static_cast<uint16_t *>(a.out) + row * D + 4 * e4;
+        if constexpr (AT == DT_BF16)
+            *reinterpret_cast<bf16x4 *>(dst) = __builtin_convertvector(v, bf16x4);
+        else
+            *reinterpret_cast<f16x4 *>(dst) = __builtin_convertvector(v, f16x4);
+    }
+}
+
 template <int DT, int AT, int D>
 hipError_t launch_prefill_t(const PrefillArgs &a, int grid, bool idle, bool smallq,
                             hipStream_t stream)
 {
     constexpr int C = prefill_cols(D);
+    constexpr int NW = kPrefillWaves;
+    const dim3 g2(grid, a.splits);
+    const dim3 blk(NW * kWave);
+    const bool split = a.splits > 1;
+    bool launched = false;
     if constexpr (D <= 128) {
         if (smallq) {
-            hipLaunchKernelGGL((pa_prefill_kernel<DT, AT, D, kPrefillWaves, C, true, true>),
-                               dim3(grid), dim3(kPrefillWaves * kWave), 0, stream, a);
-            return hipGetLastError();
+            if (split)
+                hipLaunchKernelGGL((pa_prefill_kernel<DT, AT, D, NW, C, true, true, true>), g2,
+                                   blk, 0, stream, a);
+            else
+                hipLaunchKernelGGL((pa_prefill_kernel<DT, AT, D, NW, C, true, true, false>), g2,
+                                   blk, 0, stream, a);
+            launched = true;
         }
     }
-    if (idle)
-        hipLaunchKernelGGL((pa_prefill_kernel<DT, AT, D, kPrefillWaves, C, true, false>),
-                           dim3(grid), dim3(kPrefillWaves * kWave), 0, stream, a);
-    else
-        hipLaunchKernelGGL((pa_prefill_kernel<DT, AT, D, kPrefillWaves, C, false, false>),
-                           dim3(grid), dim3(kPrefillWaves * kWave), 0, stream, a);
+    if (!launched) {
+        if (idle && split)
+            hipLaunchKernelGGL((pa_prefill_kernel<DT, AT, D, NW, C, true, false, true>), g2, blk,
+                               0, stream, a);
+        else if (idle)
+            hipLaunchKernelGGL((pa_prefill_kernel<DT, AT, D, NW, C, true, false, false>), g2, blk,
+                               0, stream, a);
+        else if (split)
+            hipLaunchKernelGGL((pa_prefill_kernel<DT, AT, D, NW, C, false, false, true>), g2, blk,
+                               0, stream, a);
+        else
+            hipLaunchKernelGGL((pa_prefill_kernel<DT, AT, D, NW, C, false, false, false>), g2,
+                               blk, 0, stream, a);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.splits <= 1)
+        return e;
+    const int rows = prefill_reduce_rows(a.group, D);
+    const dim3 rgrid((a.max_query_len + rows - 1) / rows, a.num_kv_heads, a.num_seqs);
+    hipLaunchKernelGGL((pa_prefill_reduce<AT, D>), rgrid, dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

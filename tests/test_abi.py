@@ -109,9 +109,10 @@ def test_decode_rejects_bad_arguments(lib):
 
 
 def _prefill(lib, pool, num_seqs=2, hq=4, scale=0.125, qs=FAKE, T=10, maxq=8, bt=FAKE, maxb=8,
-             cl=FAKE, max_ctx=100, q=FAKE, out=FAKE):
+             cl=FAKE, max_ctx=100, q=FAKE, out=FAKE, splits=0, ws=None, ws_bytes=0):
     return lib.pa_prefill(ctypes.byref(pool) if pool is not None else None, q, out, num_seqs,
-                          hq, ctypes.c_float(scale), qs, T, maxq, bt, maxb, cl, max_ctx, None)
+                          hq, ctypes.c_float(scale), qs, T, maxq, bt, maxb, cl, max_ctx, splits,
+                          ws, ws_bytes, None)
 
 
 def test_prefill_rejects_bad_arguments(lib):
@@ -139,6 +140,42 @@ def test_prefill_rejects_bad_arguments(lib):
     assert _prefill(lib, _pool(), num_seqs=0) == 0
     fp8 = dict(dtype=B.PA_FP8_E4M3, act_dtype=B.PA_BF16, k_scale=0.01, v_scale=0.0)
     assert _prefill(lib, _pool(**fp8)) == inval
+    # key splits: 0 .. 8, and a split launch needs the workspace it asked for
+    wsp = 3
+    assert _prefill(lib, _pool(), splits=-1) == inval
+    assert _prefill(lib, _pool(), splits=9) == unsup
+    need = lib.pa_prefill_workspace_bytes(2, 4, 2, 128, B.PA_BF16, 10, 8, 100, 3)
+    assert need == 10 * 4 * 3 * (128 + 2) * 4
+    assert _prefill(lib, _pool(), splits=3) == wsp
+    assert _prefill(lib, _pool(), splits=3, ws=FAKE, ws_bytes=need - 1) == wsp
+    assert _prefill(lib, _pool(), splits=3, ws=ctypes.c_void_p(0x3008), ws_bytes=need) == inval
+
+
+def test_prefill_key_split_planner(lib):
+    ks = lib.pa_prefill_key_splits
+    wb = lib.pa_prefill_workspace_bytes
+    bf = B.PA_BF16
+    # one 512-token chunk of one sequence over a 32k context, 64 q / 8 kv heads, d 128:
+    # 16 query tiles x 8 kv-heads = 128 units, half the CUs: two splits
+    assert ks(1, 64, 8, 128, bf, 512, 512, 32768) == 2
+    assert wb(1, 64, 8, 128, bf, 512, 512, 32768, 0) == 512 * 64 * 2 * 130 * 4
+    # a 256-token chunk: 64 units, four splits; at d 64 the tiles hold 512 rows
+    assert ks(1, 64, 8, 128, bf, 256, 256, 32768) == 4
+    assert ks(1, 64, 8, 64, bf, 256, 256, 32768) == 8
+    # four long decode rows (one position each): 4 tiles x 8 kv-heads, eight splits
+    assert ks(4, 64, 8, 128, bf, 4, 1, 32768) == 8
+    # ... but never below 1,024 keys of the longest context per split
+    assert ks(4, 64, 8, 128, bf, 4, 1, 3000) == 2
+    assert ks(4, 64, 8, 128, bf, 4, 1, 1000) == 1
+    # the chunked-prefill and mixed-batch workloads fill the CUs: no split, no workspace
+    assert ks(16, 64, 8, 128, bf, 16 * 512, 512, 4096) == 1
+    assert ks(29, 64, 8, 128, bf, 2372, 512, 4096) == 1
+    assert wb(16, 64, 8, 128, bf, 16 * 512, 512, 4096, 0) == 0
+    # forced counts are taken as given; bad input
+    assert wb(16, 64, 8, 128, bf, 16 * 512, 512, 4096, 2) == 16 * 512 * 64 * 2 * 130 * 4
+    assert ks(1, 64, 8, 128, B.PA_F32, 512, 512, 32768) == -1
+    assert ks(1, 63, 8, 128, bf, 512, 512, 32768) == -1
+    assert wb(1, 64, 8, 128, bf, 512, 512, 32768, 9) == 2 ** 64 - 1
 
 
 def test_decode_append_rejects_bad_arguments(lib):

@@ -132,8 +132,9 @@ def oracle_pools(w):
     return kp, vp, bt
 
 
-def gpu_prefill(w, pools=None):
-    """Append the chunks, then prefill, on the GPU; returns (out fp64, k_pool, v_pool)."""
+def gpu_prefill(w, pools=None, key_splits=0):
+    """Append the chunks, then prefill (key_splits as pa_prefill takes it), on the GPU;
+    returns (out fp64, k_pool, v_pool)."""
     kp, vp = pools if pools is not None else U.device_pools(w)
     d = U.device_inputs(w)
     PA.cache_append(kp, vp, d["k_new"], d["v_new"], d["slot_mapping"], **U.scales(w))
@@ -141,7 +142,8 @@ def gpu_prefill(w, pools=None):
     # NaN first: a row the launch fails to write cannot pass for a computed one
     out = torch.full_like(d["q"], float("nan"))
     PA.prefill(d["q"], kp, vp, qs, d["block_tables"], d["context_lens"], float(w.scale),
-               w.max_context_len, w.max_query_len, out=out, **U.scales(w))
+               w.max_context_len, w.max_query_len, out=out, key_splits=key_splits,
+               **U.scales(w))
     torch.cuda.synchronize()
     return U.widen(U.from_dev(out, w.dtype), w.dtype), kp, vp
 
@@ -160,14 +162,17 @@ def oracle_rows(w, kp, vp, bt, rows):
     return out
 
 
+@pytest.mark.parametrize("splits", [0, 3])
 @pytest.mark.parametrize("spec", SMALL, ids=lambda s: s.name)
-def test_prefill_small(spec):
-    say(f"[prefill] {spec.name}")
+def test_prefill_small(spec, splits):
+    """Every row of each small workload, unsplit and with the keys of every query tile
+    cut into three ranges merged by the reduce (empty ranges included)."""
+    say(f"[prefill] {spec.name} key_splits={splits}")
     w = W.build(spec)
     kpo, vpo, bt = oracle_pools(w)
     ref, _ = O.prefill_paged(w.q, kpo, vpo, w.kv_dtype, w.query_start, bt, w.context_lens,
                              w.scale, q_dtype=w.dtype, k_scale=w.k_scale, v_scale=w.v_scale)
-    got, kd, vd = gpu_prefill(w)
+    got, kd, vd = gpu_prefill(w, key_splits=splits)
     # the append went to the same rows (relabelled) bit for bit
     idx = torch.from_numpy(w.live_blocks).cuda()
     assert U.from_dev(kd[idx], w.kv_dtype).tobytes() == kpo[:-1].tobytes()
@@ -265,6 +270,67 @@ def test_prefill_bad_table_entry_and_length_poison_only_their_sequence():
     assert np.isnan(got[qs[0]:qs[1]][pos0 >= 32]).all()
     assert np.isnan(got[qs[2]:qs[3]]).all()
     ok, mx, mean = U.tolerance_ok(got[qs[1]:qs[2]], ref[qs[1]:qs[2]], w.dtype)
+    assert ok, (mx, mean)
+
+
+@pytest.mark.parametrize("splits", [1, 4])
+def test_prefill_bad_entries_under_key_splits(splits):
+    """With the keys split over workgroups: a bad id in one split's range poisons that
+    sequence's rows through the merge, a bad length poisons its sequence, a malformed
+    query range leaves its rows unwritten, and the other sequences match the oracle."""
+    spec = W.Spec("pf_bad_ks", "bf16", 16, 2, 128, [600, 700, 500, 400], seed=49,
+                  spare_blocks=1, query_lens=[40, 1, 30, 20])
+    w = W.build(spec)
+    kpo, vpo, bt = oracle_pools(w)
+    ref, _ = O.prefill_paged(w.q, kpo, vpo, w.kv_dtype, w.query_start, bt, w.context_lens,
+                             w.scale, q_dtype=w.dtype)
+    kd, vd = U.device_pools(w)
+    d = U.device_inputs(w)
+    PA.cache_append(kd, vd, d["k_new"], d["v_new"], d["slot_mapping"])
+    tables = d["block_tables"].clone()
+    tables[0, 3] = w.num_blocks + 5                # early keys of sequence 0 (split 0)
+    ctx = d["context_lens"].clone()
+    ctx[2] = -3                                    # sequence 2: a bad length
+    qs = torch.from_numpy(w.query_start).cuda()
+    qs_bad = qs.clone()
+    qs_bad[4] = qs_bad[3] + w.max_query_len + 1    # sequence 3: range past max_query_len
+    out = torch.full_like(d["q"], float("nan"))
+    PA.prefill(d["q"], kd, vd, qs_bad, tables, ctx, float(w.scale), w.max_context_len,
+               w.max_query_len, out=out, key_splits=splits)
+    torch.cuda.synchronize()
+    got = U.widen(U.from_dev(out, w.dtype), w.dtype)
+    q = w.query_start
+    assert np.isnan(got[q[0]:q[1]]).all()
+    assert np.isnan(got[q[2]:q[3]]).all()
+    assert np.isnan(got[q[3]:q[4]]).all()          # never written (NaN-filled before)
+    ok, mx, mean = U.tolerance_ok(got[q[1]:q[2]], ref[q[1]:q[2]], w.dtype)
+    assert ok, (mx, mean)
+
+
+@pytest.mark.parametrize("kind", ["one_long_chunk", "few_long_decode_rows"])
+def test_prefill_automatic_key_splits(kind):
+    """Launches with fewer (sequence, kv-head, tile) units than CUs split their keys by
+    themselves: one 512-token chunk over a 3,072-token context (16 q / 2 kv heads, 32
+    units, three splits), and four decode rows of 5,000 to 9,000 tokens (64 q / 8 kv,
+    32 units, eight splits).  Every row against the oracle."""
+    if kind == "one_long_chunk":
+        spec = W.Spec("pf_auto_split_chunk", "bf16", 16, 2, 128, [3072], seed=61,
+                      spare_blocks=1, query_lens=[512])
+    else:
+        spec = W.Spec("pf_auto_split_rows", "bf16", 64, 8, 128, [5000, 9000, 7321, 6000],
+                      seed=62, spare_blocks=1, query_lens=[1, 1, 1, 1])
+    w = W.build(spec)
+    splits = PA.prefill_key_splits(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                                   w.num_query_tokens, w.max_query_len, w.max_context_len)
+    say(f"[prefill auto split] {spec.name}: {splits} key splits")
+    assert splits == (3 if kind == "one_long_chunk" else 8)
+    kpo, vpo, bt = oracle_pools(w)
+    ref, _ = O.prefill_paged(w.q, kpo, vpo, w.kv_dtype, w.query_start, bt, w.context_lens,
+                             w.scale, q_dtype=w.dtype)
+    got, _, _ = gpu_prefill(w)
+    ok, mx, mean = U.tolerance_ok(got, ref, w.dtype)
+    say(f"  max {mx:.3e} mean {mean:.3e}")
+    assert np.isfinite(got).all()
     assert ok, (mx, mean)
 
 
@@ -369,9 +435,10 @@ def test_prefill_random_batches(i):
     kpo, vpo, bt = oracle_pools(w)
     ref, _ = O.prefill_paged(w.q, kpo, vpo, w.kv_dtype, w.query_start, bt, w.context_lens,
                              w.scale, q_dtype=w.dtype, k_scale=w.k_scale, v_scale=w.v_scale)
-    got, _, _ = gpu_prefill(w)
+    splits = [0, 2, 5, 8][i % 4]
+    got, _, _ = gpu_prefill(w, key_splits=splits)
     ok, mx, mean = U.tolerance_ok(got, ref, w.dtype)
-    say(f"  rows {got.shape[0]}: max {mx:.3e} mean {mean:.3e}")
+    say(f"  rows {got.shape[0]} key_splits {splits}: max {mx:.3e} mean {mean:.3e}")
     assert np.isfinite(got).all()
     assert ok, (mx, mean)
 
