@@ -160,18 +160,27 @@ def test_graph_replay_fused_decode_append(spec, ptok):
         assert torch.equal(U.int_view(out_e), ref)
 
 
-def test_graph_replay_prefill():
-    """Append of a prompt chunk + pa_prefill captured and replayed."""
+@pytest.mark.parametrize("splits", [1, 3])
+def test_graph_replay_prefill(splits):
+    """Append of a prompt chunk + pa_prefill captured and replayed, without and with
+    key splits (the split launch's reduce kernel and its workspace, allocated before
+    the capture, inside the graph)."""
     spec = W.Spec("graph_prefill", "bf16", 16, 2, 128, [600, 90], seed=203, spare_blocks=1,
                   query_lens=[512, 90])
     w = W.build(spec)
     d = U.device_inputs(w)
     qs = torch.from_numpy(w.query_start).cuda()
+    need = PA.prefill_workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                                      w.num_query_tokens, w.max_query_len, w.max_context_len,
+                                      splits)
+    assert (need > 0) == (splits > 1)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
 
     def step(kp, vp, out):
         PA.cache_append(kp, vp, d["k_new"], d["v_new"], d["slot_mapping"])
         PA.prefill(d["q"], kp, vp, qs, d["block_tables"], d["context_lens"], float(w.scale),
-                   w.max_context_len, w.max_query_len, out=out)
+                   w.max_context_len, w.max_query_len, out=out, key_splits=splits,
+                   workspace=ws)
 
     kp_e, vp_e = U.device_pools(w)
     out_e = torch.empty_like(d["q"])
@@ -192,7 +201,8 @@ def test_graph_replay_prefill():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(U.int_view(out), ref), f"replay {rep} differs from eager"
-        check_against_oracle(w, out, kp, vp, (ko, vo), ref_out, f"prefill replay {rep}")
+        check_against_oracle(w, out, kp, vp, (ko, vo), ref_out,
+                             f"prefill replay {rep} key_splits {splits}")
         step(kp_e, vp_e, out_e)
         torch.cuda.synchronize()
         assert torch.equal(U.int_view(out_e), ref)
