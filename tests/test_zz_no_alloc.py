@@ -52,6 +52,10 @@ PAIRS = [
              v_scale=(0.0093, 0.004, 0.02)), 512),
      (W.Spec("na_fp8_small", "f16", 8, 2, 64, [100, 37], seed=404, spare_blocks=1,
              kv_dtype="fp8", k_scale=0.02, v_scale=0.004), 32)),
+    # groups above 16 q-heads: the shared-tile kernel's partials in the buffer
+    ((W.Spec("na_bf16_g32_big", "bf16", 64, 2, 128, [3000, 1900, 64], seed=405,
+             spare_blocks=1), 512),
+     (W.Spec("na_f16_g64_small", "f16", 64, 1, 64, [700, 5], seed=406, spare_blocks=1), 128)),
 ]
 
 
