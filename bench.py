@@ -66,13 +66,14 @@ def parse():
                     help="step: the decode step (default); copy_blocks: the copy-on-write "
                          "block copy on the workload's pool; prefill: append + paged "
                          "prefill of prompt chunks")
-    ap.add_argument("--sweep", choices=["decode-types", "decode-groups", "prefill-types",
-                                        "prefill-splits"],
+    ap.add_argument("--sweep", choices=["decode-types", "decode-groups", "decode-batch",
+                                        "prefill-types", "prefill-splits"],
                     default=None,
                     help="instead of the bench line, time one call per shape of a family "
                          "and print one JSON line of rows: decode pool types and head "
                          "sizes on the Llama-70B-shaped decode, decode GQA group sizes on "
-                         "32 x 4096 tokens, prefill pool types and head sizes on the "
+                         "32 x 4096 tokens, decode batch sizes (1 .. 64 sequences of 4096 "
+                         "tokens), prefill pool types and head sizes on the "
                          "512-token chunked prefill, or prefill launches too small to fill "
                          "the GPU with and without key splits")
     ap.add_argument("--sweep-launches", type=int, default=0,
@@ -501,6 +502,11 @@ def sweep_shapes(name, W):
                 ("fp8/bf16 d128", fp8), ("fp8/f16 d128", dict(dtype="f16", **fp8)),
                 ("bf16 d64", dict(head_dim=64)), ("fp8/bf16 d64", dict(head_dim=64, **fp8)),
                 ("bf16 d256", dict(head_dim=256)), ("fp8/bf16 d256", dict(head_dim=256, **fp8))]
+    elif name == "decode-batch":
+        base = W.config_spec(HEADLINE)
+        rows = [(f"bf16 B={b} x 4096", dict(context_lens=[4096] * b))
+                for b in (1, 2, 4, 8, 16, 32, 64)]
+        rows += [(f"bf16 B={b} x 32768", dict(context_lens=[32768] * b)) for b in (1, 4)]
     elif name == "decode-types":
         base = W.config_spec(HEADLINE)
         rows = [("bf16 d128", {}), ("f16 d128", dict(dtype="f16")),
