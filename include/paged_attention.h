@@ -274,6 +274,7 @@ pa_status pa_decode_append(const pa_kv_pool *pool, const void *q, const void *k_
  *                  grid would leave the GPU's CUs idle, merge the partials exactly).
  *                  Automatic splits only a launch with fewer units than CUs (a single
  *                  long prompt's chunk, a few long decode rows), see pa_prefill_key_splits.
+ *                  A split launch takes at most 65,535 sequences (PA_ERR_UNSUPPORTED).
  *   workspace      device scratch of at least pa_prefill_workspace_bytes(...) bytes for
  *                  the same arguments (may be NULL when that is 0); contents need no
  *                  initialisation

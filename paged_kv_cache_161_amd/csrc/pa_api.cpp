@@ -629,6 +629,9 @@ pa_status pa_prefill(const pa_kv_pool *pool, const void *q, void *out, int32_t n
                                          pool->head_dim, pool->dtype, num_query_tokens,
                                          max_query_len, max_context_len, key_splits)
                                    : 0;
+    // the reduce of a split launch runs one workgroup column per sequence and kv-head
+    if (splits > 1 && (num_seqs > 65535 || pool->num_kv_heads > 65535))
+        return PA_ERR_UNSUPPORTED;
     if (need > 0 && (!workspace || workspace_bytes < need))
         return PA_ERR_WORKSPACE;
     if (need > 0 && !aligned16(workspace))

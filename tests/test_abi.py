@@ -149,6 +149,7 @@ def test_prefill_rejects_bad_arguments(lib):
     assert _prefill(lib, _pool(), splits=3) == wsp
     assert _prefill(lib, _pool(), splits=3, ws=FAKE, ws_bytes=need - 1) == wsp
     assert _prefill(lib, _pool(), splits=3, ws=ctypes.c_void_p(0x3008), ws_bytes=need) == inval
+    assert _prefill(lib, _pool(), splits=2, num_seqs=65536, T=65536, maxq=1) == unsup
 
 
 def test_prefill_key_split_planner(lib):
