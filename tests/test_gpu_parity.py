@@ -201,6 +201,34 @@ def test_decode_llama70b_gqa_forced_partitions(ptok):
     check(w, got, ref, f"llama70b_gqa_bf16 p{ptok}")
 
 
+_FP8 = dict(kv_dtype="fp8", k_scale=0.0117, v_scale=0.0093)
+
+
+_LARGE_GROUPS = [
+    ("bf16_g32_64q_2kv", dict(num_kv_heads=2)),
+    ("f16_g64_mqa", dict(num_kv_heads=1, dtype="f16")),
+    ("bf16_g64_128q_2kv", dict(num_q_heads=128, num_kv_heads=2)),
+    ("bf16_g48_96q_2kv", dict(num_q_heads=96, num_kv_heads=2)),
+    ("fp8_bf16_g64_mqa", dict(num_kv_heads=1, **_FP8)),
+]
+
+
+@pytest.mark.parametrize("label,kw", _LARGE_GROUPS, ids=[x[0] for x in _LARGE_GROUPS])
+def test_decode_large_groups_full_size(label, kw):
+    """The Llama-70B-shaped decode (32 x 4096 tokens, d 128, shuffled pool) with groups
+    above 16 q-heads per kv-head, at full size and on every output: 16-bit pools take
+    the shared-tile kernel (two or four 16-head chunks per staged tile), fp8 pools one
+    workgroup per 16-head chunk."""
+    import dataclasses
+    spec = dataclasses.replace(W.config_spec(3), name="llama70b_" + label, **kw)
+    w = W.build(spec)
+    say(f"[decode large group] {label}: Hq={w.num_q_heads} Hkv={w.num_kv_heads} "
+        f"kv={w.kv_dtype}")
+    ref = oracle_decode(w)
+    got, _, _ = gpu_step(w)
+    check(w, got, ref, label)
+
+
 @pytest.mark.parametrize("i", [4, 5])
 def test_decode_config_planned_partitions(i):
     """The partition length pa_decode_plan picks from the host context lengths (config

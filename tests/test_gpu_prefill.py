@@ -202,11 +202,15 @@ def sample_rows(w, per_seq=3, seed=0):
     return np.unique(np.asarray(rows))
 
 
+@pytest.mark.parametrize("splits", [0, 4])
 @pytest.mark.parametrize("cfg", [7, 8])
-def test_prefill_full_size_sampled(cfg):
-    say(f"[prefill] config {cfg} (full size, sampled rows)")
+def test_prefill_full_size_sampled(cfg, splits):
+    """The two full-size prefill workloads on sampled rows, with the library's choice of
+    key splits (none: both fill the GPU) and with every tile's keys cut into four ranges
+    merged by the reduce."""
+    say(f"[prefill] config {cfg} (full size, sampled rows) key_splits={splits}")
     w = W.make_config(cfg)
-    got, _, _ = gpu_prefill(w)
+    got, _, _ = gpu_prefill(w, key_splits=splits)
     assert np.isfinite(got).all()
     kpo, vpo, bt = oracle_pools(w)
     rows = sample_rows(w, per_seq=2 if cfg == 8 else 3, seed=cfg)
