@@ -34,6 +34,9 @@ import torch
 HBM_PEAK_GBS = 8000.0
 ROOT = os.path.dirname(os.path.abspath(__file__))
 LAYERS = 4
+# Bytes a decode sweep reads between two uses of one layer pool at least: four times the
+# MI355X's 256 MB last-level cache (MALL), so no step finds its K/V still cached there
+MALL_SPAN_BYTES = 1 << 30
 W_ELEM = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}
 CALIBRATION_BYTES = 256 << 20
 HEADLINE = 3
@@ -212,16 +215,21 @@ def calibration_copy(dev):
 READ_PROBE_BYTES = 2 << 30
 
 
-def measured_read_ceiling(dev, launches=10):
+def measured_read_ceiling(dev, launches=10, step_bytes=0):
     """The practical HBM read rate on this device: the benchmark's plain read kernel
     (16-byte loads, grid-stride, libpa_hbm_probe.so) over 2 GiB, median of `launches`
-    launches timed with HIP events on the launching stream.  None if the probe library
+    launches timed with HIP events on the launching stream.  With step_bytes > 0, also
+    the same kernel reading exactly step_bytes per launch, back to back over disjoint
+    slices of the 2 GiB buffer (2 to 64 of them; for steps of 32 MB or more, every
+    slice is evicted from the 256 MB MALL before its next turn): the time a plain read
+    of one step's K/V takes.
+    Returns (GB/s, µs per same-size read or None), or (None, None) if the probe library
     is not built."""
     import ctypes
     path = os.path.join(ROOT, "paged_kv_cache_161_amd", "libpa_hbm_probe.so")
     if not os.path.exists(path):
         log("[bench] read probe not built; no measured read ceiling")
-        return None
+        return None, None
     lib = ctypes.CDLL(path)
     lib.pa_probe_read.restype = ctypes.c_int32
     lib.pa_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
@@ -243,11 +251,36 @@ def measured_read_ceiling(dev, launches=10):
         torch.cuda.synchronize()
         if r >= 2:
             times.append(e0.elapsed_time(e1) * 1e-3)
-    del buf, sink
     gbs = READ_PROBE_BYTES / statistics.median(times) / 1e9
     log(f"[bench] measured read ceiling: {gbs:.0f} GB/s (2 GiB plain read, median of "
         f"{launches})")
-    return gbs
+    same_us = None
+    size = step_bytes // 16 * 16
+    slices = min(READ_PROBE_BYTES // size, 64) if size > 0 else 0
+    if slices >= 2:
+        def sweep(n):
+            for j in range(n):
+                rc = lib.pa_probe_read(buf.data_ptr() + (j % slices) * size, size,
+                                       sink.data_ptr(), groups,
+                                       ctypes.c_void_p(stream.cuda_stream))
+                if rc != 0:
+                    raise RuntimeError(f"pa_probe_read returned {rc}")
+        n = 10 * slices
+        sweep(n)
+        best = float("inf")
+        for _ in range(3):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            sweep(n)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1) * 1e3 / n)
+        same_us = best
+        log(f"[bench] plain read of {size} bytes per launch ({slices} disjoint slices "
+            f"cycled): {same_us:.2f} us")
+    del buf, sink
+    return gbs, same_us
 
 
 def prefill_flops(w):
@@ -531,10 +564,19 @@ def sweep_shapes(name, W):
             for label, kw in rows]
 
 
+def pool_copies(w):
+    """Layer pools a decode sweep cycles: four, as in the bench step, or more when a
+    step reads so few bytes that four pools would fit in the 256 MB MALL (the copies
+    then span MALL_SPAN_BYTES of K/V reads; at most 64)."""
+    per_step = max(w.unique_kv_bytes(), 1)
+    return int(min(64, max(LAYERS, -(-MALL_SPAN_BYTES // per_step))))
+
+
 def bench_sweep(args, PA, W, U, dev):
     """One timed call per shape (decode: the fused step's launch at the planned
-    partition, cycling four pools; prefill: the prefill call), best of three rounds of
-    back-to-back launches between HIP events on the launching stream."""
+    partition, cycling layer pools whose reads together span 1 GiB, so K/V always comes
+    from HBM; prefill: the prefill call), best of three rounds of back-to-back launches
+    between HIP events on the launching stream."""
     rows = []
     if args.calibrate:
         calibration_copy(dev)
@@ -564,7 +606,8 @@ def bench_sweep(args, PA, W, U, dev):
             if args.sweep_launches > 0:
                 n_warm, n_launch = args.sweep_launches, args.sweep_launches
         else:
-            pools = [U.device_pools(w, dev) for _ in range(LAYERS)]
+            n_pools = pool_copies(w)
+            pools = [U.device_pools(w, dev) for _ in range(n_pools)]
             ptok = PA.plan_partition_tokens(w.num_q_heads, w.num_kv_heads, w.head_dim,
                                             w.context_lens, w.kv_dtype)
             ws = torch.empty(max(PA.workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads,
@@ -576,7 +619,7 @@ def bench_sweep(args, PA, W, U, dev):
             kr = U.to_dev(rows_new, w.dtype, dev)
 
             def call(i):
-                kp, vp = pools[i % LAYERS]
+                kp, vp = pools[i % n_pools]
                 PA.decode_append(d["q"], kp, vp, kr, kr, d["block_tables"], d["context_lens"],
                                  float(w.scale), w.max_context_len, ptok, out=out,
                                  workspace=ws, **sc)
@@ -605,7 +648,8 @@ def bench_sweep(args, PA, W, U, dev):
                        key_splits=int(ks_used))
         else:
             by = w.unique_kv_bytes()
-            row.update(partition_tokens=ptok, kv_bytes=int(by), GBps=round(by / best / 1e3, 1),
+            row.update(partition_tokens=ptok, kv_bytes=int(by), pools_cycled=n_pools,
+                       GBps=round(by / best / 1e3, 1),
                        pct_hbm_peak=round(100 * by / best / 1e3 / HBM_PEAK_GBS, 1))
         log(f"[sweep] {json.dumps(row)}")
         rows.append(row)
@@ -691,7 +735,7 @@ def main():
         calibration_copy(dev)
     # the HBM read ceiling of this machine, measured before the steps (a plain 16-byte-load
     # read of 2 GiB, ten times)
-    ceiling = measured_read_ceiling(dev)
+    ceiling, plain_same_us = measured_read_ceiling(dev, step_bytes=uniq_bytes)
 
     for i in range(args.warmup):
         step(i)
@@ -868,7 +912,11 @@ def main():
                      "longer_run_launches": n_l,
                      "measured_read_ceiling": None if ceiling is None else round(ceiling, 1),
                      "frac_of_measured_read_ceiling":
-                         None if ceiling is None else round(achieved / ceiling, 4)},
+                         None if ceiling is None else round(achieved / ceiling, 4),
+                     "plain_read_same_bytes_us":
+                         None if plain_same_us is None else round(plain_same_us, 2),
+                     "frac_of_plain_read_same_bytes":
+                         None if plain_same_us is None else round(plain_same_us / (dur * 1e6), 4)},
         "cpu_baseline": cpu,
         "parity": parity,
         "context_figures": {"A100_ridge_flop_per_byte": 156, "H100_hbm_TBps": 3.35},
