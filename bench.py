@@ -310,11 +310,12 @@ def time_sub_batch(w, d, pools, k_rows, v_rows, idx, sc, n_launch, warmup, dev):
                      dtype=torch.uint8, device=dev)
     out = torch.empty_like(q)
     layers = len(pools)
+    shared = w.shares_blocks(idx)
 
     def step(i):
         kp, vp = pools[i % layers]
         PA.decode_append(q, kp, vp, kr, vr, bt, cl, float(w.scale), max_ctx, ptok, out=out,
-                         workspace=ws, **sc)
+                         workspace=ws, shared_blocks=shared, **sc)
 
     for i in range(warmup):
         step(i)
@@ -607,6 +608,7 @@ def bench_sweep(args, PA, W, U, dev):
                 n_warm, n_launch = args.sweep_launches, args.sweep_launches
         else:
             n_pools = pool_copies(w)
+            shared = w.shares_blocks()
             pools = [U.device_pools(w, dev) for _ in range(n_pools)]
             ptok = PA.plan_partition_tokens(w.num_q_heads, w.num_kv_heads, w.head_dim,
                                             w.context_lens, w.kv_dtype)
@@ -622,7 +624,7 @@ def bench_sweep(args, PA, W, U, dev):
                 kp, vp = pools[i % n_pools]
                 PA.decode_append(d["q"], kp, vp, kr, kr, d["block_tables"], d["context_lens"],
                                  float(w.scale), w.max_context_len, ptok, out=out,
-                                 workspace=ws, **sc)
+                                 workspace=ws, shared_blocks=shared, **sc)
             n_warm, n_launch = 200, 100
             if args.sweep_launches > 0:
                 n_warm, n_launch = args.sweep_launches, args.sweep_launches
@@ -716,16 +718,20 @@ def main():
     k_rows = U.to_dev(rows_k, w.dtype, dev)
     v_rows = U.to_dev(rows_v, w.dtype, dev)
 
+    # a batch whose tables name a block for several sequences (config 5's beams) says
+    # so, as a serving loop would from its reference counts
+    shared = w.shares_blocks()
+
     def fused(i):
         kp, vp = pools[i % LAYERS]
         PA.decode_append(d["q"], kp, vp, k_rows, v_rows, d["block_tables"], d["context_lens"],
-                         scale, max_ctx, ptok, out=out, workspace=ws, **sc)
+                         scale, max_ctx, ptok, out=out, workspace=ws, shared_blocks=shared, **sc)
 
     def two_calls(i):
         kp, vp = pools[i % LAYERS]
         PA.cache_append(kp, vp, d["k_new"], d["v_new"], d["slot_mapping"], **sc)
         PA.decode(d["q"], kp, vp, d["block_tables"], d["context_lens"], scale, max_ctx, ptok,
-                  out=out, workspace=ws, **sc)
+                  out=out, workspace=ws, shared_blocks=shared, **sc)
 
     # a step is one decode_append launch (the append fused into the attention); the
     # same work as two calls is timed beside it
@@ -888,6 +894,7 @@ def main():
                    "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
                    "head_dim": w.head_dim, "block_size": 16,
                    "partition_tokens": ptok,
+                   "shared_blocks": shared,
                    "parallelism": "none (1 GPU)"},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(tokens_per_s, 1),

@@ -102,7 +102,18 @@ typedef enum pa_dtype {
  *                  and > 0 gets NaN codes on append and NaN outputs from decode and
  *                  prefill; no other head is affected.
  *   k_scale, v_scale  one scale for the whole pool (finite, > 0), used where the
- *                  corresponding per-head array is NULL. */
+ *                  corresponding per-head array is NULL.
+ * flags: 0, or PA_POOL_SHARED_BLOCKS when one call's block tables may name the same
+ *   physical block for several sequences (forked beams, a shared prompt prefix: the
+ *   blocks whose reference count, pa_allocator_ref_count, is above 1; LLM-101-CN
+ *   "推理优化", copy-on-write between sequences).  A performance hint for the decode
+ *   calls, never a correctness one: results are bit for bit the same either way.
+ *   Without it the decode kernels stream K/V with non-temporal loads, which read once
+ *   from HBM at the rate of a plain read but leave nothing in the caches for another
+ *   workgroup; with it they use ordinary loads, so the repeats of a shared block are
+ *   served by the L2 and the last-level cache.  Other bits are invalid. */
+#define PA_POOL_SHARED_BLOCKS 1
+
 typedef struct pa_kv_pool {
     void *k_pool;
     void *v_pool;
@@ -116,6 +127,7 @@ typedef struct pa_kv_pool {
     float v_scale;
     const float *k_head_scales;
     const float *v_head_scales;
+    int32_t flags;
 } pa_kv_pool;
 
 /* Bytes of ONE of the two pools (K or V) for these dimensions; 0 if any argument is

@@ -38,7 +38,11 @@ class PaKvPool(ctypes.Structure):
                 ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("act_dtype", ctypes.c_int32),
                 ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float),
-                ("k_head_scales", ctypes.c_void_p), ("v_head_scales", ctypes.c_void_p)]
+                ("k_head_scales", ctypes.c_void_p), ("v_head_scales", ctypes.c_void_p),
+                ("flags", ctypes.c_int32)]
+
+
+PA_POOL_SHARED_BLOCKS = 1
 
 
 _lib = None
@@ -155,12 +159,14 @@ def _scale_arg(x, name: str, num_kv_heads: int):
 
 
 def make_pool(k_pool, v_pool, act_dtype: Optional[torch.dtype] = None, k_scale=1.0,
-              v_scale=1.0) -> PaKvPool:
+              v_scale=1.0, shared_blocks: bool = False) -> PaKvPool:
     """k_pool [N][Hkv][16][d] and v_pool [N][Hkv][d][16], same dtype.  FP8 pools are
     uint8 (or float8_e4m3fn) tensors of E4M3 codes; act_dtype (f16/bf16) is then the
     type of q, out and the new rows, and K = code * k_scale, V = code * v_scale, each
     scale a number (the whole pool) or a CUDA float32 tensor [Hkv] (one per kv-head,
-    read on the device at every call)."""
+    read on the device at every call).  shared_blocks sets PA_POOL_SHARED_BLOCKS: the
+    call's block tables may name one physical block for several sequences (decode
+    then reads K/V with ordinary instead of non-temporal loads; same results)."""
     if k_pool.dim() != 4 or v_pool.dim() != 4:
         raise ValueError("pools are 4-D: k [N][Hkv][16][d], v [N][Hkv][d][16]")
     n, hkv, bs, d = k_pool.shape
@@ -180,7 +186,8 @@ def make_pool(k_pool, v_pool, act_dtype: Optional[torch.dtype] = None, k_scale=1
     ks, k_heads = _scale_arg(k_scale, "k_scale", hkv)
     vs, v_heads = _scale_arg(v_scale, "v_scale", hkv)
     return PaKvPool(_dev_ptr(k_pool, "k_pool"), _dev_ptr(v_pool, "v_pool"), n, bs, hkv, d,
-                    code, act, ks, vs, k_heads, v_heads)
+                    code, act, ks, vs, k_heads, v_heads,
+                    PA_POOL_SHARED_BLOCKS if shared_blocks else 0)
 
 
 _DTYPE_OF_CODE = {v: k for k, v in DTYPE_CODE.items()}
@@ -277,16 +284,18 @@ def _call_with_workspace(fn, args, workspace, device, dims):
 
 def decode(q, k_pool, v_pool, block_tables, context_lens, scale: float, max_context_len: int,
            partition_tokens: int = 0, out: Optional[torch.Tensor] = None,
-           workspace: Optional[torch.Tensor] = None, k_scale=1.0, v_scale=1.0) -> torch.Tensor:
+           workspace: Optional[torch.Tensor] = None, k_scale=1.0, v_scale=1.0,
+           shared_blocks: bool = False) -> torch.Tensor:
     """softmax(q K^T scale) V per sequence and q-head through the block tables.
 
     q [B][Hq][d]; block_tables [B][max_blocks] int32; context_lens [B] int32;
     max_context_len: host-side bound of context_lens.  Returns out [B][Hq][d] in q's
     dtype.  For an fp8 pool, K = code * k_scale and V = code * v_scale (numbers, or
-    per-kv-head CUDA float32 tensors).
+    per-kv-head CUDA float32 tensors).  shared_blocks: the tables may name one
+    physical block for several sequences (a performance hint, see make_pool).
     """
     act = q.dtype if k_pool.dtype in FP8_STORAGE else None
-    pool = make_pool(k_pool, v_pool, act, k_scale, v_scale)
+    pool = make_pool(k_pool, v_pool, act, k_scale, v_scale, shared_blocks)
     B, hq, d = q.shape
     if d != pool.head_dim:
         raise ValueError("q head_dim differs from the pool's")
@@ -307,12 +316,12 @@ def decode(q, k_pool, v_pool, block_tables, context_lens, scale: float, max_cont
 def decode_noalloc(q, k_pool, v_pool, block_tables, context_lens, scale: float,
                    max_context_len: int, partition_tokens: int = 0,
                    out: Optional[torch.Tensor] = None, k_scale=1.0,
-                   v_scale=1.0) -> torch.Tensor:
+                   v_scale=1.0, shared_blocks: bool = False) -> torch.Tensor:
     """decode() without a workspace and without allocating on the device (out must then
     be given): the split partials live in the library's static per-GPU buffer of
     NOALLOC_SCRATCH_BYTES.  Calls that overlap in time on one GPU race on that buffer."""
     act = q.dtype if k_pool.dtype in FP8_STORAGE else None
-    pool = make_pool(k_pool, v_pool, act, k_scale, v_scale)
+    pool = make_pool(k_pool, v_pool, act, k_scale, v_scale, shared_blocks)
     B, hq, d = q.shape
     if d != pool.head_dim:
         raise ValueError("q head_dim differs from the pool's")
@@ -332,11 +341,11 @@ def decode_noalloc(q, k_pool, v_pool, block_tables, context_lens, scale: float,
 def decode_append(q, k_pool, v_pool, k_new, v_new, block_tables, context_lens, scale: float,
                   max_context_len: int, partition_tokens: int = 0,
                   out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                  k_scale=1.0, v_scale=1.0) -> torch.Tensor:
+                  k_scale=1.0, v_scale=1.0, shared_blocks: bool = False) -> torch.Tensor:
     """One launch for a decode step: each sequence's new row (k_new / v_new [B][Hkv][d])
     becomes token context_lens[b] - 1 in the pool, then decode attention as decode()."""
     act = q.dtype if k_pool.dtype in FP8_STORAGE else None
-    pool = make_pool(k_pool, v_pool, act, k_scale, v_scale)
+    pool = make_pool(k_pool, v_pool, act, k_scale, v_scale, shared_blocks)
     B, hq, d = q.shape
     if d != pool.head_dim:
         raise ValueError("q head_dim differs from the pool's")

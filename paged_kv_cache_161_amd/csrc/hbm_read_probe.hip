@@ -1,6 +1,8 @@
 // Measurement helper, not part of the attention path: a plain HBM read kernel whose
 // rate is the practical ceiling a streaming kernel can reach on this device.  Each
-// thread reads 16 bytes per iteration in a grid-stride loop and folds them with XOR;
+// thread reads 16 bytes per iteration in a grid-stride loop, with the non-temporal
+// hint (on MI355X the faster way to stream data that is read once: 7.2 against
+// 6.4 TB/s over 2 GiB with ordinary loads), and folds them with XOR;
 // the fold result is stored only when it equals a constant no input here produces, so
 // the loads stay (a buffer of repeated bytes, as the benchmark fills it, folds to 0 or
 // to that byte repeated, never to the constant).  Built into its own small library and
@@ -28,7 +30,7 @@ __global__ __launch_bounds__(256) void hbm_read_kernel(const u32x4 *__restrict__
     const size_t stride = (size_t)gridDim.x * blockDim.x;
     uint32_t acc = 0;
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
-        const u32x4 v = p[i];
+        const u32x4 v = __builtin_nontemporal_load(p + i);
         acc ^= v.x ^ v.y ^ v.z ^ v.w;
     }
     if (acc == 0x9E3779B9u)   // data-dependent, so the compiler keeps every load

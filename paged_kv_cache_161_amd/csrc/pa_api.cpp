@@ -76,6 +76,8 @@ pa_status check_pool(const pa_kv_pool *pool)
         return PA_ERR_UNSUPPORTED;
     if ((int64_t)pool->num_blocks * kBlock > INT32_MAX)   // slots are int32
         return PA_ERR_UNSUPPORTED;
+    if ((pool->flags & ~PA_POOL_SHARED_BLOCKS) != 0)
+        return PA_ERR_INVALID_ARG;
     if (pool->dtype == PA_FP8_E4M3) {
         if (pool->act_dtype != PA_F16 && pool->act_dtype != PA_BF16)
             return PA_ERR_UNSUPPORTED;
@@ -476,6 +478,7 @@ pa_status decode_impl(const pa_kv_pool *pool, const void *q, const void *k_new,
     a.k_quant = pool->k_scale;
     a.v_quant = pool->v_scale;
     a.act_bf16 = pool->act_dtype == PA_BF16 ? 1 : 0;
+    a.stream_kv = (pool->flags & PA_POOL_SHARED_BLOCKS) ? 0 : 1;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = pa::launch_decode(pool->dtype, pool->act_dtype, pool->head_dim, a, num_seqs, s);

@@ -97,12 +97,13 @@ struct Tile16 {
     u32x2 v[NPV];                        // V^T[16n + r][4g .. 4g+3]
 
     // ks: elements from one K row to the next (D in the pool; padded rows in LDS)
+    template <bool NT = false>
     __device__ __forceinline__ void load(const uint16_t *kt, const uint16_t *vt, int r, int g,
                                          int ks = D)
     {
 #pragma unroll
         for (int i = 0; i < NQK; ++i)
-            k[i] = *reinterpret_cast<const u32x4 *>(kt + r * ks + 32 * i + 8 * g);
+            k[i] = load_kv<NT, u32x4>(kt + r * ks + 32 * i + 8 * g);
         // V^T as 16-byte half rows (half as many load instructions as 8-byte pieces,
         // which sets how fast one CU streams): lane (r, g) loads tokens 8 (g / 2) .. +7
         // of row 16 (2 i + g % 2) + r into v[2 i] (its first 4 tokens) and v[2 i + 1];
@@ -110,8 +111,8 @@ struct Tile16 {
         // (swapping here would make a prefetched tile wait for its own loads).
 #pragma unroll
         for (int i = 0; i < NPV / 2; ++i) {
-            const u32x4 w = *reinterpret_cast<const u32x4 *>(
-                vt + (16 * (2 * i + (g & 1)) + r) * kBlock + 8 * (g >> 1));
+            const u32x4 w =
+                load_kv<NT, u32x4>(vt + (16 * (2 * i + (g & 1)) + r) * kBlock + 8 * (g >> 1));
             v[2 * i] = u32x2{w[0], w[1]};
             v[2 * i + 1] = u32x2{w[2], w[3]};
         }
@@ -181,15 +182,16 @@ struct Tile32 {
     f32x4 k[NC];                         // K[r][(D/4)g + 4c .. +3]
     f32x4 v[NC];                         // V^T[16n + r][4g .. 4g+3]
 
+    template <bool NT = false>
     __device__ __forceinline__ void load(const float *kt, const float *vt, int r, int g,
                                          int ks = D)
     {
 #pragma unroll
         for (int c = 0; c < NC; ++c)
-            k[c] = *reinterpret_cast<const f32x4 *>(kt + r * ks + (D / 4) * g + 4 * c);
+            k[c] = load_kv<NT, f32x4>(kt + r * ks + (D / 4) * g + 4 * c);
 #pragma unroll
         for (int n = 0; n < NC; ++n)
-            v[n] = *reinterpret_cast<const f32x4 *>(vt + (16 * n + r) * kBlock + 4 * g);
+            v[n] = load_kv<NT, f32x4>(vt + (16 * n + r) * kBlock + 4 * g);
     }
 
     __device__ __forceinline__ void store_row(float *kt, float *vt, int off, int r, int g) const
@@ -251,15 +253,16 @@ struct Tile8 {
     // transpose their 4 x 4 blocks of 4-byte pieces with two rounds of lane swaps
     // (16-lane, then 32-lane), so that v[4 i + j] = V^T[16 (4 i + j) + r][4 g .. 4 g + 3]
     // as the MFMA operand wants: 2 loads per block at d = 128 instead of 8.
+    template <bool NT = false>
     __device__ __forceinline__ void load(const uint8_t *kt, const uint8_t *vt, int r, int g,
                                          int ks = D)
     {
 #pragma unroll
         for (int j = 0; j < NKL; ++j)
-            k[j] = *reinterpret_cast<const u32x4 *>(kt + r * ks + 64 * j + 16 * g);
+            k[j] = load_kv<NT, u32x4>(kt + r * ks + 64 * j + 16 * g);
 #pragma unroll
         for (int i = 0; i < NPV / 4; ++i) {
-            const u32x4 w = *reinterpret_cast<const u32x4 *>(vt + (16 * (g + 4 * i) + r) * kBlock);
+            const u32x4 w = load_kv<NT, u32x4>(vt + (16 * (g + 4 * i) + r) * kBlock);
             // lane g holds e[g][j] = w[j]; afterwards lane g's register j holds e[j][g]
             auto s01 = __builtin_amdgcn_permlane16_swap(w[0], w[1], false, false);
             auto s23 = __builtin_amdgcn_permlane16_swap(w[2], w[3], false, false);
@@ -493,7 +496,9 @@ constexpr int min_waves_per_simd(int dt, int d, int pf)
                       : ((pf + 1) * (dt == DT_FP8 ? 16 : 32) * d / 128 <= 96 ? 2 : 1));
 }
 
-template <int DT, int AT, int D, int NW, int PF, bool FUSE>
+// NT: K/V tiles are read with non-temporal loads (no block is shared between the
+// batch's sequences; never for fp32 pools).
+template <int DT, int AT, int D, int NW, int PF, bool FUSE, bool NT>
 __global__ __launch_bounds__(NW *kWave, min_waves_per_simd(DT, D, PF)) void pa_decode_partition(DecodeArgs a)
 {
     using F = Frags<DT, AT, D>;
@@ -733,7 +738,7 @@ __global__ __launch_bounds__(NW *kWave, min_waves_per_simd(DT, D, PF)) void pa_d
         for (int k = 0; k < PF; ++k) {
             if (k < my_n) {
                 const size_t off = phys_of(k);
-                ring[k].load(kbase + off, vbase + off, r, g);
+                ring[k].template load<NT>(kbase + off, vbase + off, r, g);
             }
         }
     };
@@ -751,7 +756,7 @@ __global__ __launch_bounds__(NW *kWave, min_waves_per_simd(DT, D, PF)) void pa_d
                 if (it < n_loop) {
                     if (it + PF < my_n) {
                         const size_t off = phys_of(it + PF);
-                        ring[(u + PF) % (PF + 1)].load(kbase + off, vbase + off, r, g);
+                        ring[(u + PF) % (PF + 1)].template load<NT>(kbase + off, vbase + off, r, g);
                     }
                     process(NoPatch{}, ring[u], it);
                 }
@@ -791,7 +796,7 @@ __global__ __launch_bounds__(NW *kWave, min_waves_per_simd(DT, D, PF)) void pa_d
 #pragma unroll
         for (int k = 0; k < PF; ++k) {
             const size_t off = my_n > 0 ? phys_of(min(k, my_n - 1)) : 0;
-            ring[k].load(kbase + off, vbase + off, r, g);
+            ring[k].template load<NT>(kbase + off, vbase + off, r, g);
         }
         if (stager) {
             const int ph = __builtin_amdgcn_readlane(bt_lane, (lb_new - lb_begin) / NW);
@@ -912,7 +917,7 @@ struct SharedShape {
     static constexpr int AREA = TILE_AREA > MERGE_AREA ? TILE_AREA : MERGE_AREA;
 };
 
-template <int DT, int AT, int D, int CH, bool FUSE>
+template <int DT, int AT, int D, int CH, bool FUSE, bool NT>
 __global__ __launch_bounds__(kSharedWaves *kWave, 2) void pa_decode_shared(DecodeArgs a)
 {
     using F = Frags<DT, AT, D>;
@@ -1131,7 +1136,7 @@ __global__ __launch_bounds__(kSharedWaves *kWave, 2) void pa_decode_shared(Decod
 #pragma unroll
             for (int i = 0; i < PPL; ++i)
                 ring[slot][k][i] =
-                    *reinterpret_cast<const u32x4 *>((is_k[i] ? kb : vb) + g_off[i]);
+                    load_kv<NT, u32x4>((is_k[i] ? kb : vb) + g_off[i]);
         }
     };
     // Stashes are unconditional too: a tile past the lane's last one lands in a buffer
@@ -1355,8 +1360,10 @@ hipError_t launch_shared_t(const DecodeArgs &a, int num_seqs, hipStream_t stream
 {
     using S = SharedShape<DT, D, CH>;
     const size_t lds = (size_t)S::AREA + (a.longest_first ? sizeof(int) * (num_seqs + 1) : 0);
-    auto kern = a.k_new ? pa_decode_shared<DT, AT, D, CH, true>
-                        : pa_decode_shared<DT, AT, D, CH, false>;
+    auto kern = a.k_new ? (a.stream_kv ? pa_decode_shared<DT, AT, D, CH, true, true>
+                                       : pa_decode_shared<DT, AT, D, CH, true, false>)
+                        : (a.stream_kv ? pa_decode_shared<DT, AT, D, CH, false, true>
+                                       : pa_decode_shared<DT, AT, D, CH, false, false>);
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -1396,8 +1403,13 @@ hipError_t launch_decode_t(const DecodeArgs &a, int num_seqs, hipStream_t stream
     const int gs_max = min(16, a.group);
     const size_t lds = sizeof(float) * (NW * 32 + 16 + (size_t)NW * gs_max * (D + 4)) +
                        (a.longest_first ? sizeof(int) * (num_seqs + 1) : 0);
-    auto kern = a.k_new ? pa_decode_partition<DT, AT, D, NW, PF, true>
-                        : pa_decode_partition<DT, AT, D, NW, PF, false>;
+    // fp32 tiles stream with ordinary loads (the hint measured slower for them)
+    constexpr bool kNt = DT != DT_F32;
+    const bool nt = kNt && a.stream_kv;
+    auto kern = a.k_new ? (nt ? pa_decode_partition<DT, AT, D, NW, PF, true, kNt>
+                              : pa_decode_partition<DT, AT, D, NW, PF, true, false>)
+                        : (nt ? pa_decode_partition<DT, AT, D, NW, PF, false, kNt>
+                              : pa_decode_partition<DT, AT, D, NW, PF, false, false>);
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

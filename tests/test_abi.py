@@ -82,6 +82,10 @@ def test_decode_rejects_bad_arguments(lib):
     assert _decode(lib, _pool(**{**fp8, "v_scale": -1.0})) == inval
     assert _decode(lib, _pool(**fp8), hq=3) == inval
     assert _decode(lib, _pool(num_blocks=0)) == inval
+    # flags: PA_POOL_SHARED_BLOCKS (a hint) or nothing; other bits are invalid
+    assert _decode(lib, _pool(flags=2)) == inval
+    assert _decode(lib, _pool(flags=-1)) == inval
+    assert _decode(lib, _pool(flags=B.PA_POOL_SHARED_BLOCKS), num_seqs=0) == 0
     assert _decode(lib, _pool(), hq=3) == inval                 # 3 % 2 != 0
     assert _decode(lib, _pool(), num_seqs=-1) == inval
     assert _decode(lib, _pool(), max_ctx=-5) == inval

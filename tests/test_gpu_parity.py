@@ -410,6 +410,62 @@ def test_generous_host_bounds_change_nothing(fused):
         assert torch.equal(a, b)
 
 
+_SHARED_HINT = [
+    # fp8 pool (partition kernel), bf16 above 16 heads (shared-tile kernel), a split
+    # partition, and fp32 (ordinary loads either way)
+    W.Spec("hint_fp8_g8", "bf16", 16, 2, 128, [700, 33, 1], seed=131, spare_blocks=1,
+           kv_dtype="fp8", k_scale=0.0117, v_scale=0.0093),
+    W.Spec("hint_bf16_g32", "bf16", 64, 2, 128, [900, 17], seed=132, spare_blocks=1),
+    W.Spec("hint_f16_g4_d256", "f16", 8, 2, 256, [2100, 64], seed=133, spare_blocks=1),
+    W.Spec("hint_f32_g2", "f32", 4, 2, 64, [300, 5], seed=134, spare_blocks=1),
+]
+
+
+@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("spec", _SHARED_HINT, ids=lambda s: s.name)
+def test_shared_blocks_hint_changes_nothing(spec, fused):
+    """PA_POOL_SHARED_BLOCKS only picks ordinary instead of non-temporal K/V loads: both
+    launches give the same bytes (output and appended pool), within the bar of the
+    oracle.  Also with two sequences whose tables name the same blocks."""
+    w = W.build(spec)
+    say(f"[shared-blocks hint] {spec.name} fused={fused}")
+    ref = oracle_decode(w)
+    d = U.device_inputs(w)
+    sc = U.scales(w)
+    kr = U.to_dev(np.ascontiguousarray(w.k_new), w.dtype)
+    vr = U.to_dev(np.ascontiguousarray(w.v_new), w.dtype)
+    got = []
+    for shared in (False, True):
+        kp, vp = U.device_pools(w)
+        if fused:
+            assert (w.context_lens > 0).all()
+            out = PA.decode_append(d["q"], kp, vp, kr, vr, d["block_tables"], d["context_lens"],
+                                   float(w.scale), w.max_context_len, 128,
+                                   shared_blocks=shared, **sc)
+        else:
+            PA.cache_append(kp, vp, d["k_new"], d["v_new"], d["slot_mapping"], **sc)
+            out = PA.decode(d["q"], kp, vp, d["block_tables"], d["context_lens"],
+                            float(w.scale), w.max_context_len, 128, shared_blocks=shared, **sc)
+        torch.cuda.synchronize()
+        got.append((out.clone(), U.int_view(kp).clone(), U.int_view(vp).clone()))
+    assert torch.equal(U.int_view(got[0][0]), U.int_view(got[1][0]))
+    assert torch.equal(got[0][1], got[1][1]) and torch.equal(got[0][2], got[1][2])
+    check(w, U.widen(U.from_dev(got[1][0], w.dtype), w.dtype), ref,
+          f"{spec.name} shared-blocks hint")
+    # the first sequence's table for every sequence: each block is read by all of them
+    bt = d["block_tables"][:1].expand_as(d["block_tables"]).contiguous()
+    cl = d["context_lens"][:1].expand_as(d["context_lens"]).contiguous()
+    outs = []
+    kp, vp = U.device_pools(w)
+    PA.cache_append(kp, vp, d["k_new"], d["v_new"], d["slot_mapping"], **sc)
+    for shared in (False, True):
+        o = PA.decode(d["q"], kp, vp, bt, cl, float(w.scale), int(w.context_lens[0]), 128,
+                      shared_blocks=shared, **sc)
+        torch.cuda.synchronize()
+        outs.append(U.int_view(o).clone())
+    assert torch.equal(outs[0], outs[1])
+
+
 def _random_decode_spec(i):
     """A seeded random decode batch: kv-heads, group (up to 32: two head chunks), head
     size and pool type drawn at random; ragged contexts with empty sequences."""
