@@ -29,7 +29,10 @@
 //   Because the V pool stores each block token-minor ([d][16]), the PV A operand
 //   (4 consecutive tokens of one e) is a plain 8-byte load, and the K operand (8
 //   consecutive e of one token) a 16-byte load; both come straight from HBM into
-//   registers, and every q-head of the group shares them inside the MFMA.
+//   registers, and every q-head of the group shares them inside the MFMA.  Each tile
+//   is read once per launch, so the loads carry the non-temporal hint unless the
+//   call's block tables share blocks between sequences (then the caches serve the
+//   repeats).
 //   The softmax statistics of head h live in the 4 lanes {h, h+16, h+32, h+48}; the
 //   tile max needs two cross-row exchanges, the O rescale none (O^T's head is lane % 16).
 #include <math.h>
