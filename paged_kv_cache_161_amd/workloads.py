@@ -215,6 +215,8 @@ class Workload:
     def compact_index(self, phys: np.ndarray) -> np.ndarray:
         """Physical id -> index in k_live/v_live (the poisoned block maps to n)."""
         phys = np.asarray(phys)
+        if self.live_blocks.size == 0:                  # every context empty
+            return np.zeros(phys.shape, np.int32)
         pos = np.searchsorted(self.live_blocks, phys)
         pos = np.minimum(pos, self.live_blocks.size)
         hit = (pos < self.live_blocks.size) & \

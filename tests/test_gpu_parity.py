@@ -81,6 +81,8 @@ SMALL = [
     W.Spec("f32_g2_d128", "f32", 4, 2, 128, [65, 16], seed=107, spare_blocks=1),
     W.Spec("bf16_g5_d128", "bf16", 10, 2, 128, [190, 3, 0, 512], seed=108, spare_blocks=1),
     W.Spec("bf16_empty_batch_rows", "bf16", 8, 8, 128, [0, 0, 5], seed=109, spare_blocks=1),
+    # every context empty: nothing to stream, every output row zero
+    W.Spec("f16_all_empty_g32", "f16", 64, 2, 128, [0, 0, 0], seed=125, spare_blocks=1),
     # FP8 E4M3 pools with per-tensor scales, bf16 / f16 activations
     W.Spec("fp8_bf16_g8_d128", "bf16", 16, 2, 128, [1, 15, 16, 17, 100, 257], seed=111,
            spare_blocks=3, kv_dtype="fp8", k_scale=0.0117, v_scale=0.0093),
@@ -496,6 +498,48 @@ def test_decode_random_batches(i):
     for ptok in (plan, 64):
         got, _, _ = gpu_step(w, ptok)
         check(w, got, ref, f"dec_random_{i} p{ptok}")
+
+
+@pytest.mark.parametrize("i", range(100, 140))
+def test_decode_random_launch_options(i):
+    """More seeded random batches, each with randomly drawn launch options: partition
+    length (the plan, 16, 64 or 256 tokens), the shared-blocks load hint, and the fused
+    append + decode launch instead of the two calls."""
+    spec = _random_decode_spec(i)
+    w = W.build(spec)
+    ref = oracle_decode(w)
+    r = np.random.Generator(np.random.PCG64(i))
+    plan = PA.plan_partition_tokens(w.num_q_heads, w.num_kv_heads, w.head_dim, w.context_lens,
+                                  w.kv_dtype)
+    ptok = int(r.choice([plan, 16, 64, 256]))
+    shared = bool(r.integers(0, 2))
+    fused = bool(r.integers(0, 2)) and bool((w.context_lens > 0).all())
+    say(f"[decode random options {i}] hq {w.num_q_heads} hkv {w.num_kv_heads} d "
+        f"{w.head_dim} {w.dtype}/{w.kv_dtype} B {w.num_seqs} p{ptok} shared={shared} "
+        f"fused={fused}")
+    d = U.device_inputs(w)
+    sc = U.scales(w)
+    kp, vp = U.device_pools(w)
+    if fused:
+        kr = U.to_dev(np.ascontiguousarray(w.k_new), w.dtype)
+        vr = U.to_dev(np.ascontiguousarray(w.v_new), w.dtype)
+        out = PA.decode_append(d["q"], kp, vp, kr, vr, d["block_tables"], d["context_lens"],
+                               float(w.scale), w.max_context_len, ptok, shared_blocks=shared,
+                               **sc)
+    else:
+        PA.cache_append(kp, vp, d["k_new"], d["v_new"], d["slot_mapping"], **sc)
+        out = PA.decode(d["q"], kp, vp, d["block_tables"], d["context_lens"], float(w.scale),
+                        w.max_context_len, ptok, shared_blocks=shared, **sc)
+    torch.cuda.synchronize()
+    check(w, U.widen(U.from_dev(out, w.dtype), w.dtype), ref, f"dec_random_{i}")
+    # the pool after the append, byte for byte against the oracle's append
+    kpo, vpo, _, sl = w.oracle_view()
+    kpo, vpo = O.cache_append(kpo, vpo, w.k_new, w.v_new, sl, w.kv_dtype, act_dtype=w.dtype,
+                              k_scale=w.k_scale, v_scale=w.v_scale)
+    if w.live_blocks.size:
+        idx = torch.from_numpy(w.live_blocks).cuda()
+        assert U.from_dev(kp[idx], w.kv_dtype).tobytes() == kpo[:-1].tobytes()
+        assert U.from_dev(vp[idx], w.kv_dtype).tobytes() == vpo[:-1].tobytes()
 
 
 BAD_SCALES = [0.0, -0.5, float("inf"), float("nan")]
