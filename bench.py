@@ -64,6 +64,9 @@ def parse():
     ap.add_argument("--no-sub-batches", action="store_true",
                     help="skip the sub-batch timings of a shared-prefix batch (profiler passes "
                          "then see only the whole batch's launches)")
+    ap.add_argument("--ordinary-loads", action="store_true",
+                    help="decode with PA_POOL_SHARED_BLOCKS set whatever the batch (ordinary "
+                         "instead of non-temporal K/V loads), for an A/B of the load hint")
     ap.add_argument("--roofline-launches", type=int, default=100)
     ap.add_argument("--op", choices=["step", "copy_blocks", "prefill"], default="step",
                     help="step: the decode step (default); copy_blocks: the copy-on-write "
@@ -725,7 +728,7 @@ def main():
 
     # a batch whose tables name a block for several sequences (config 5's beams) says
     # so, as a serving loop would from its reference counts
-    shared = w.shares_blocks()
+    shared = w.shares_blocks() or args.ordinary_loads
 
     def fused(i):
         kp, vp = pools[i % LAYERS]
@@ -900,6 +903,7 @@ def main():
                    "head_dim": w.head_dim, "block_size": 16,
                    "partition_tokens": ptok,
                    "shared_blocks": shared,
+                   "ordinary_loads_forced": bool(args.ordinary_loads),
                    "parallelism": "none (1 GPU)"},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(tokens_per_s, 1),
