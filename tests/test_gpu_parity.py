@@ -81,8 +81,6 @@ SMALL = [
     W.Spec("f32_g2_d128", "f32", 4, 2, 128, [65, 16], seed=107, spare_blocks=1),
     W.Spec("bf16_g5_d128", "bf16", 10, 2, 128, [190, 3, 0, 512], seed=108, spare_blocks=1),
     W.Spec("bf16_empty_batch_rows", "bf16", 8, 8, 128, [0, 0, 5], seed=109, spare_blocks=1),
-    # every context empty: nothing to stream, every output row zero
-    W.Spec("f16_all_empty_g32", "f16", 64, 2, 128, [0, 0, 0], seed=125, spare_blocks=1),
     # FP8 E4M3 pools with per-tensor scales, bf16 / f16 activations
     W.Spec("fp8_bf16_g8_d128", "bf16", 16, 2, 128, [1, 15, 16, 17, 100, 257], seed=111,
            spare_blocks=3, kv_dtype="fp8", k_scale=0.0117, v_scale=0.0093),
@@ -124,6 +122,8 @@ SMALL = [
            spare_blocks=1),
     W.Spec("bf16_g64_d64_shared_long", "bf16", 128, 2, 64, [3000, 5, 2049, 0, 4100], seed=124,
            spare_blocks=1),
+    # every context empty: nothing to stream, every output row zero
+    W.Spec("f16_all_empty_g32", "f16", 64, 2, 128, [0, 0, 0], seed=125, spare_blocks=1),
 ]
 
 
@@ -551,7 +551,7 @@ def test_bad_head_scale_poisons_only_that_head(bad):
     case its V scale) makes exactly that head's rows NaN in decode (single pass and
     split), in the fused decode + append and in prefill, and its appended codes the NaN
     code; every other head equals the run with good scales bit for bit."""
-    spec = SMALL[18]                                      # 3 kv-heads, G = 4, d = 64
+    spec = next(s for s in SMALL if s.name == "fp8_heads_f16_g4_d64")   # 3 kv-heads, G 4
     w = W.build(spec)
     G = w.num_q_heads // w.num_kv_heads
     other = np.r_[0:G, 2 * G:w.num_q_heads]
