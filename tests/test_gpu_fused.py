@@ -16,7 +16,7 @@ import oracle as O
 from paged_kv_cache_161_amd import binding as PA
 from paged_kv_cache_161_amd import workloads as W
 from tests import devutil as U
-from tests.test_gpu_parity import SMALL
+from tests.test_gpu_parity import SMALL, small_spec
 
 pytestmark = pytest.mark.gpu
 
@@ -56,8 +56,11 @@ def run_both(w, ptok):
     return out_a, out_b, (ka, va), (kb, vb)
 
 
-CASES = [(s, 0) for s in SMALL] + [(SMALL[0], 16), (SMALL[0], 48), (SMALL[4], 32),
-                                    (SMALL[9], 16), (SMALL[7], 64)]
+CASES = [(s, 0) for s in SMALL] + [(small_spec("bf16_g8_d128"), 16),
+                                    (small_spec("bf16_g8_d128"), 48),
+                                    (small_spec("bf16_g32_d128"), 32),
+                                    (small_spec("fp8_bf16_g8_d128"), 16),
+                                    (small_spec("bf16_g5_d128"), 64)]
 
 
 @pytest.mark.parametrize("spec,ptok", CASES, ids=lambda v: v.name if hasattr(v, "name") else f"p{v}")
@@ -88,7 +91,7 @@ def test_fused_full_size(cfg):
 
 
 def test_fused_bad_table_entry_writes_nothing():
-    w = W.build(SMALL[0])
+    w = W.build(small_spec("bf16_g8_d128"))
     d = U.device_inputs(w)
     kp, vp = U.device_pools(w)
     k0, v0 = kp.clone(), vp.clone()

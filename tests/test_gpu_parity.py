@@ -127,6 +127,11 @@ SMALL = [
 ]
 
 
+def small_spec(name):
+    """The small decode workload of that name."""
+    return next(s for s in SMALL if s.name == name)
+
+
 @pytest.mark.parametrize("spec", SMALL, ids=lambda s: s.name)
 @pytest.mark.parametrize("ptok", [0, 16, 48, 256])
 def test_decode_small(spec, ptok):
@@ -169,7 +174,7 @@ def test_append_bit_exact(i):
 
 
 def test_append_skips_padding_and_out_of_pool_slots():
-    w = W.build(SMALL[0])
+    w = W.build(small_spec("bf16_g8_d128"))
     kp, vp = U.device_pools(w)
     k0, v0 = kp.clone(), vp.clone()
     d = U.device_inputs(w)
@@ -306,7 +311,7 @@ def test_gather_probe(dtype, d, ctx, ptok, kv):
 
 
 def test_bad_table_entry_and_context_give_nan_not_fault():
-    w = W.build(SMALL[0])
+    w = W.build(small_spec("bf16_g8_d128"))
     kp, vp = U.device_pools(w)
     d = U.device_inputs(w)
     bt = d["block_tables"].clone()
@@ -323,7 +328,7 @@ def test_bad_table_entry_and_context_give_nan_not_fault():
 
 
 def test_rejects_unsupported_partition():
-    w = W.build(SMALL[0])
+    w = W.build(small_spec("bf16_g8_d128"))
     kp, vp = U.device_pools(w)
     d = U.device_inputs(w)
     with pytest.raises(PA.PaError):
@@ -336,7 +341,8 @@ def test_split_workspace_reuse_and_garbage():
     differ, gives oracle-correct results: every partial the reduce launch reads is
     written by the partition launch of the same call, so the workspace needs no
     initialisation."""
-    specs = [SMALL[0], SMALL[7], SMALL[4]]
+    specs = [small_spec("bf16_g8_d128"), small_spec("bf16_g5_d128"),
+             small_spec("bf16_g32_d128")]
     ws = torch.full((1 << 22,), 0xA5, dtype=torch.uint8, device="cuda")
     for rep in range(3):
         for spec in specs:
@@ -365,7 +371,7 @@ def test_split_workspace_reuse_and_garbage():
 def test_binding_grows_a_too_small_workspace():
     """A caller's workspace below the split launch's need is reported by the library
     (nothing launched), and the binding then allocates one of the right size."""
-    w = W.build(SMALL[0])
+    w = W.build(small_spec("bf16_g8_d128"))
     ptok = 16
     need = PA.workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim,
                               w.max_context_len, ptok, dtype=w.kv_dtype)
@@ -386,7 +392,7 @@ def test_generous_host_bounds_change_nothing(fused):
     length only adds workgroups with nothing to stream: at the same partition length
     the outputs, and the pool after a fused append, equal the tight-bound call's bit
     for bit."""
-    w = W.build(SMALL[0])
+    w = W.build(small_spec("bf16_g8_d128"))
     d = U.device_inputs(w)
     sc = U.scales(w)
     ptok = 48
