@@ -73,13 +73,15 @@ def parse():
                          "block copy on the workload's pool; prefill: append + paged "
                          "prefill of prompt chunks")
     ap.add_argument("--sweep", choices=["decode-types", "decode-groups", "decode-batch",
-                                        "prefill-types", "prefill-splits"],
+                                        "decode-partitions", "prefill-types",
+                                        "prefill-splits"],
                     default=None,
                     help="instead of the bench line, time one call per shape of a family "
                          "and print one JSON line of rows: decode pool types and head "
                          "sizes on the Llama-70B-shaped decode, decode GQA group sizes on "
                          "32 x 4096 tokens, decode batch sizes (1 .. 64 sequences of 4096 "
-                         "tokens), prefill pool types and head sizes on the "
+                         "tokens), decode partition lengths (the plan against forced ones "
+                         "on small and ragged batches), prefill pool types and head sizes on the "
                          "512-token chunked prefill, or prefill launches too small to fill "
                          "the GPU with and without key splits")
     ap.add_argument("--sweep-launches", type=int, default=0,
@@ -515,11 +517,29 @@ def bench_prefill(args, w, PA, U, dev):
 
 
 def sweep_shapes(name, W):
-    """(label, Spec, prefill key splits) of one shape family, each derived from a named
-    workload (key splits 0 = the library's choice)."""
+    """(label, Spec, knob) of one shape family, each derived from a named workload; the
+    knob is the prefill key splits, or the decode partition length (0 = the library's
+    choice in both)."""
     import dataclasses
     import re
     fp8 = dict(kv_dtype="fp8", k_scale=0.0117, v_scale=0.0093)
+    if name == "decode-partitions":
+        # the partition planner's choice against forced lengths, where the choice is
+        # not one pass per sequence: small batches of 4,096 tokens, one 32k sequence,
+        # the ragged batch and the long + shared-prefix batch
+        base = W.config_spec(HEADLINE)
+        shapes = [(f"bf16 B={b} x 4096", dataclasses.replace(
+                      base, name=f"{base.name}_B{b}", context_lens=[4096] * b))
+                  for b in (1, 4, 16)]
+        shapes.append(("bf16 B=1 x 32768", dataclasses.replace(
+            base, name=f"{base.name}_B1_32k", context_lens=[32768])))
+        shapes += [("ragged bf16 (config 4)", W.config_spec(4)),
+                   ("long + shared prefix (config 5)", W.config_spec(5))]
+        out = []
+        for label, spec in shapes:
+            for ptok in (0, 256, 512, 1024, 2048, 4096):
+                out.append((f"{label}, {'plan' if ptok == 0 else ptok}", spec, ptok))
+        return out
     if name == "prefill-splits":
         # one request's chunk over a long context, and a few long decode rows alone:
         # 64 q / 8 kv heads, d 128, bf16, each without a key split and with the
@@ -618,8 +638,9 @@ def bench_sweep(args, PA, W, U, dev):
             n_pools = pool_copies(w)
             shared = w.shares_blocks()
             pools = [U.device_pools(w, dev) for _ in range(n_pools)]
-            ptok = PA.plan_partition_tokens(w.num_q_heads, w.num_kv_heads, w.head_dim,
+            plan = PA.plan_partition_tokens(w.num_q_heads, w.num_kv_heads, w.head_dim,
                                             w.context_lens, w.kv_dtype)
+            ptok = key_splits or plan          # decode: a forced partition length
             ws = torch.empty(max(PA.workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads,
                                                     w.head_dim, w.max_context_len, ptok,
                                                     w.kv_dtype), 1),
@@ -658,7 +679,8 @@ def bench_sweep(args, PA, W, U, dev):
                        key_splits=int(ks_used))
         else:
             by = w.unique_kv_bytes()
-            row.update(partition_tokens=ptok, kv_bytes=int(by), pools_cycled=n_pools,
+            row.update(partition_tokens=ptok, planned=bool(ptok == plan), kv_bytes=int(by),
+                       pools_cycled=n_pools,
                        GBps=round(by / best / 1e3, 1),
                        pct_hbm_peak=round(100 * by / best / 1e3 / HBM_PEAK_GBS, 1))
         log(f"[sweep] {json.dumps(row)}")
