@@ -320,7 +320,7 @@ def time_sub_batch(w, d, pools, k_rows, v_rows, idx, sc, n_launch, warmup, dev):
                      dtype=torch.uint8, device=dev)
     out = torch.empty_like(q)
     layers = len(pools)
-    shared = w.shares_blocks(idx)
+    shared = PA.tables_share_blocks(w.block_tables[idx], w.context_lens[idx])
 
     def step(i):
         kp, vp = pools[i % layers]
@@ -636,7 +636,7 @@ def bench_sweep(args, PA, W, U, dev):
                 n_warm, n_launch = args.sweep_launches, args.sweep_launches
         else:
             n_pools = pool_copies(w)
-            shared = w.shares_blocks()
+            shared = PA.tables_share_blocks(w.block_tables, w.context_lens)
             pools = [U.device_pools(w, dev) for _ in range(n_pools)]
             plan = PA.plan_partition_tokens(w.num_q_heads, w.num_kv_heads, w.head_dim,
                                             w.context_lens, w.kv_dtype)
@@ -749,8 +749,8 @@ def main():
     v_rows = U.to_dev(rows_v, w.dtype, dev)
 
     # a batch whose tables name a block for several sequences (config 5's beams) says
-    # so, as a serving loop would from its reference counts
-    shared = w.shares_blocks() or args.ordinary_loads
+    # so (the library's host check of the tables, as a serving loop would run it)
+    shared = PA.tables_share_blocks(w.block_tables, w.context_lens) or args.ordinary_loads
 
     def fused(i):
         kp, vp = pools[i % LAYERS]

@@ -373,6 +373,17 @@ pa_status pa_validate_prefill_batch(int32_t num_seqs, const int32_t *query_start
 pa_status pa_validate_slots(const int32_t *slot_mapping, int32_t num_tokens, int32_t num_blocks,
                             int32_t *bad_token_out);
 
+/* Whether a batch's tables share blocks, for the pool's PA_POOL_SHARED_BLOCKS flag: 1 when
+ * some physical block id appears more than once among the entries the sequences read
+ * (the first ceil(context_lens[b] / 16) of each row of block_tables
+ * [num_seqs][max_blocks_per_seq]; negative ids are skipped), as with forked beams or a
+ * shared prompt prefix (LLM-101-CN "推理优化", section "Copy-on-Write 优化"); 0 when
+ * every live entry is distinct; -1 on a negative count, a null array with num_seqs > 0,
+ * or a context length outside [0, max_blocks_per_seq * 16].  HOST arrays; sorts a copy
+ * of the live entries (sum of ceil(context_lens[b] / 16) int32 values). */
+int32_t pa_tables_share_blocks(int32_t num_seqs, const int32_t *block_tables,
+                               int32_t max_blocks_per_seq, const int32_t *context_lens);
+
 /* ---------------------------------------------------------------- host block allocator
  * Bookkeeping of which physical blocks are free, with reference counts so that blocks
  * can be shared by several sequences (beam-search prefixes) and copied on first write

@@ -114,6 +114,8 @@ def load(path: str = LIB_PATH):
     lib.pa_validate_prefill_batch.restype = ctypes.c_int
     lib.pa_validate_slots.argtypes = [P, I32, I32, P]
     lib.pa_validate_slots.restype = ctypes.c_int
+    lib.pa_tables_share_blocks.argtypes = [I32, P, I32, P]
+    lib.pa_tables_share_blocks.restype = I32
     if path == LIB_PATH:
         _lib = lib
     return lib
@@ -493,6 +495,19 @@ def validate_slots(slot_mapping, num_blocks: int) -> int:
     if st not in (0, 1) or (st == 1 and bad.value < 0):
         _raise(st)
     return -1 if st == 0 else int(bad.value)
+
+
+def tables_share_blocks(block_tables, context_lens) -> bool:
+    """pa_tables_share_blocks on host copies: whether some physical block is read by two
+    of the batch's sequences (or twice by one), i.e. whether to pass shared_blocks=True
+    to the decode calls."""
+    bt, cl = _host_i32(block_tables, "block_tables"), _host_i32(context_lens, "context_lens")
+    if bt.ndim != 2 or bt.shape[0] != cl.size:
+        raise ValueError("block_tables must be [num_seqs][max_blocks], context_lens [num_seqs]")
+    r = load().pa_tables_share_blocks(int(cl.size), _np_ptr(bt), int(bt.shape[1]), _np_ptr(cl))
+    if r < 0:
+        raise ValueError("invalid arguments to pa_tables_share_blocks")
+    return bool(r)
 
 
 class BlockAllocator:

@@ -9,6 +9,7 @@
 // offset t % 16) and of the slot numbering slot = block * 16 + offset of the append.
 #include <stdint.h>
 
+#include <algorithm>
 #include <vector>
 
 #include "../../include/paged_attention.h"
@@ -118,6 +119,31 @@ pa_status pa_validate_slots(const int32_t *slot_mapping, int32_t num_tokens, int
         seen[(size_t)s] = 1;
     }
     return PA_OK;
+}
+
+int32_t pa_tables_share_blocks(int32_t num_seqs, const int32_t *block_tables,
+                               int32_t max_blocks_per_seq, const int32_t *context_lens)
+{
+    if (num_seqs < 0 || max_blocks_per_seq < 0)
+        return -1;
+    if (num_seqs > 0 && (!block_tables || !context_lens))
+        return -1;
+    std::vector<int32_t> live;
+    try {
+        for (int32_t b = 0; b < num_seqs; ++b) {
+            const int32_t ctx = context_lens[b];
+            if (ctx < 0 || (int64_t)ctx > (int64_t)max_blocks_per_seq * kBlock)
+                return -1;
+            const int32_t *row = block_tables + (int64_t)b * max_blocks_per_seq;
+            for (int64_t i = 0; i < (ctx + kBlock - 1) / kBlock; ++i)
+                if (row[i] >= 0)            // a negative id names no block
+                    live.push_back(row[i]);
+        }
+    } catch (...) {
+        return -1;
+    }
+    std::sort(live.begin(), live.end());
+    return std::adjacent_find(live.begin(), live.end()) != live.end() ? 1 : 0;
 }
 
 }  // extern "C"

@@ -187,18 +187,6 @@ class Workload:
         rows = sum(seen.values())
         return rows * self.num_kv_heads * 2 * self.head_dim * ELEM_BYTES[self.kv_dtype]
 
-    def shares_blocks(self, seqs=None) -> bool:
-        """Whether one physical block holds live tokens of two of the sequences (all, or
-        the listed ones): what a serving loop knows from its block reference counts."""
-        owner = {}
-        for b in (range(self.num_seqs) if seqs is None else seqs):
-            n = int(self.context_lens[b])
-            for lb in range((n + BLOCK - 1) // BLOCK):
-                p = int(self.block_tables[b, lb])
-                if owner.setdefault(p, b) != b:
-                    return True
-        return False
-
     def pool_shapes(self):
         hkv, d = self.num_kv_heads, self.head_dim
         return (self.num_blocks, hkv, BLOCK, d), (self.num_blocks, hkv, d, BLOCK)

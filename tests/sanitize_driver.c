@@ -142,6 +142,12 @@ static int validate_cases(void)
     CHECK(pa_validate_slots(slots, 4, 8, &bad) == PA_OK);
     CHECK(pa_validate_slots(slots, 5, 8, &bad) == PA_ERR_INVALID_ARG && bad == 4);
     CHECK(pa_validate_slots(slots, 5, 0, NULL) == PA_ERR_INVALID_ARG);
+    /* row 0 reads 5, 7, 2; row 1 reads 1: nothing shared; row 1 reading 2 shares it */
+    CHECK(pa_tables_share_blocks(2, bt, 4, cl) == 0);
+    bt[4] = 2;
+    CHECK(pa_tables_share_blocks(2, bt, 4, cl) == 1);
+    CHECK(pa_tables_share_blocks(0, NULL, 4, NULL) == 0);
+    CHECK(pa_tables_share_blocks(2, NULL, 4, cl) == -1);
     return 0;
 }
 

@@ -64,3 +64,38 @@ def test_configs_are_valid(i):
                                         w.max_query_len, w.max_context_len, nb) == -1
     else:
         assert B.validate_decode_tables(bt, w.context_lens, w.max_context_len, nb) == -1
+
+
+def test_tables_share_blocks():
+    """pa_tables_share_blocks: a block read by two sequences, or twice by one, is shared;
+    entries past a sequence's context are not read and share nothing."""
+    bt, cl = _tables()
+    assert B.tables_share_blocks(bt, cl) is False
+    assert B.tables_share_blocks(bt, np.array([37, 17], np.int32)) is False  # 1, 99: unique
+    shared = bt.copy()
+    shared[1, 0] = 7                                    # row 1 reads row 0's block 7
+    assert B.tables_share_blocks(shared, cl) is True
+    assert B.tables_share_blocks(shared, np.array([37, 0], np.int32)) is False  # row 1 empty
+    twice = bt.copy()
+    twice[0, 2] = 5                                     # row 0 reads block 5 twice
+    assert B.tables_share_blocks(twice, cl) is True
+    assert B.tables_share_blocks(twice, np.array([32, 16], np.int32)) is False  # 2 blocks
+    assert B.tables_share_blocks(np.zeros((0, 4), np.int32), np.zeros(0, np.int32)) is False
+    with pytest.raises(ValueError):
+        B.tables_share_blocks(bt, np.array([37, 65], np.int32))                 # > 4 blocks
+    with pytest.raises(ValueError):
+        B.tables_share_blocks(bt, np.array([-1, 16], np.int32))
+
+
+@pytest.mark.parametrize("i", [2, 3, 4, 5, 6, 7, 8])
+def test_tables_share_blocks_on_workloads(i):
+    """The library's check agrees with a plain Python scan of the live entries: only the
+    long + shared-prefix workload (beams over one prefix) shares blocks."""
+    w = W.make_config(i)
+    owner, plain = {}, False
+    for b in range(w.num_seqs):
+        for p in w.block_tables[b, :(int(w.context_lens[b]) + 15) // 16]:
+            if owner.setdefault(int(p), b) != b:
+                plain = True
+    assert B.tables_share_blocks(w.block_tables, w.context_lens) == plain
+    assert plain == (i == 5)
