@@ -84,6 +84,11 @@ def parse():
                          "on small and ragged batches), prefill pool types and head sizes on the "
                          "512-token chunked prefill, or prefill launches too small to fill "
                          "the GPU with and without key splits")
+    ap.add_argument("--torch-sdpa-reference", action="store_true",
+                    help="instead of the bench line, time PyTorch's own fused attention "
+                         "(flash and memory-efficient backends only) on contiguous dense "
+                         "tensors of the prefill shapes, as a reference rate for the "
+                         "prefill kernel on this GPU; one JSON line of rows")
     ap.add_argument("--sweep-launches", type=int, default=0,
                     help="with --sweep: launches per timed round and warm-up launches "
                          "(default 100 and 200 for decode, 30 and 20 for prefill); small "
@@ -690,6 +695,60 @@ def bench_sweep(args, PA, W, U, dev):
     print(json.dumps({"sweep": args.sweep, "rows": rows}), flush=True)
 
 
+def torch_sdpa_reference(dev):
+    """PyTorch's fused attention on contiguous tensors, the shapes of the prefill
+    workloads without paging: 16 x 512 queries over 4,096 keys unmasked (the chunked
+    prefill's size), and 2 x 4,096 causal, at 64 q-heads over 8 and over 64 kv-heads,
+    d 128, bf16.  Only the flash and memory-efficient backends are allowed (a backend
+    that cannot take a shape is reported unavailable, never replaced by the math
+    path).  Best of three rounds of 20 launches between HIP events."""
+    import torch.nn.functional as F
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    cases = [("512 q x 4096 k, no mask, 64 q / 8 kv heads, B 16", 16, 64, 8, 512, 4096, False),
+             ("512 q x 4096 k, no mask, 64 q / 64 kv heads, B 16", 16, 64, 64, 512, 4096, False),
+             ("4096 x 4096 causal, 64 q / 8 kv heads, B 2", 2, 64, 8, 4096, 4096, True),
+             ("4096 x 4096 causal, 64 q / 64 kv heads, B 2", 2, 64, 64, 4096, 4096, True)]
+    rows = []
+    gen = torch.Generator(device=dev).manual_seed(0)
+    for backend in (SDPBackend.FLASH_ATTENTION, SDPBackend.EFFICIENT_ATTENTION):
+        for label, b, hq, hkv, lq, lk, causal in cases:
+            q = torch.randn(b, hq, lq, 128, device=dev, dtype=torch.bfloat16, generator=gen)
+            k = torch.randn(b, hkv, lk, 128, device=dev, dtype=torch.bfloat16, generator=gen)
+            v = torch.randn(b, hkv, lk, 128, device=dev, dtype=torch.bfloat16, generator=gen)
+            kw = {"enable_gqa": True} if hkv != hq else {}
+            pairs = lq * (lq + 1) // 2 if causal else lq * lk
+            flops = 4 * 128 * b * hq * pairs
+            row = {"backend": backend.name, "shape": label}
+            try:
+                with sdpa_kernel([backend]):
+                    def call():
+                        return F.scaled_dot_product_attention(q, k, v, is_causal=causal, **kw)
+                    for _ in range(3):
+                        call()
+                    torch.cuda.synchronize()
+                    best = float("inf")
+                    s = torch.cuda.current_stream(dev)
+                    for _ in range(3):
+                        e0 = torch.cuda.Event(enable_timing=True)
+                        e1 = torch.cuda.Event(enable_timing=True)
+                        e0.record(s)
+                        for _ in range(20):
+                            call()
+                        e1.record(s)
+                        torch.cuda.synchronize()
+                        best = min(best, e0.elapsed_time(e1) * 1e3 / 20)
+                tf = flops / best / 1e6
+                row.update(us=round(best, 1), tflops=round(tf, 1),
+                           pct_mfma_peak=round(100 * tf / MFMA_BF16_PEAK_TFLOPS, 1))
+            except RuntimeError as exc:
+                row.update(unavailable=str(exc).splitlines()[0][:120])
+            log(f"[sdpa] {json.dumps(row)}")
+            rows.append(row)
+            del q, k, v
+    print(json.dumps({"reference": "torch scaled_dot_product_attention",
+                      "torch": torch.__version__, "rows": rows}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -708,6 +767,8 @@ def main():
 
     PA.load()
     dev = torch.device("cuda:0")
+    if args.torch_sdpa_reference:
+        return torch_sdpa_reference(dev)
     if args.sweep:
         return bench_sweep(args, PA, W, U, dev)
     t0 = time.time()
