@@ -133,26 +133,34 @@ constexpr int kPrefetchMain = PA_PREFETCH;
 constexpr int waves_per_group(int head_dim) { return head_dim <= 128 ? kWavesMain : 4; }
 
 // 16-head chunks of a GQA group one decode workgroup serves.  One for groups up to 16
-// q-heads, at head_dim 256, and for fp8 and fp32 pools: the workgroup's waves walk
-// different blocks, and a larger group runs one workgroup per 16 q-heads, whose K/V
-// reads after the first come from the XCD's L2.  Above 16 q-heads with 16-bit pools
-// at head_dim <= 128, the shared-tile kernel: 2 chunks up to 32 q-heads, else 4, each
-// K/V tile staged once in LDS for all of them (measured faster there, slower for fp8
-// pools, whose half-size tiles the L2 serves to the chunk workgroups cheaply).
+// q-heads, at head_dim 256 and for fp32 pools: the workgroup's waves walk different
+// blocks, and a larger group runs one workgroup per 16 q-heads, whose K/V reads after
+// the first come from the XCD's L2.  Above 16 q-heads at head_dim <= 128: for 16-bit
+// pools the shared-tile kernel, 2 chunks up to 32 q-heads, else 4, each K/V tile
+// staged once in LDS for all of them; for fp8 pools 2 chunks held by every wave of a
+// partition workgroup as two MFMA column blocks over the same tile registers (each
+// choice measured faster than the alternatives for its pool type).
 constexpr int decode_chunks(int dtype, int head_dim, int group)
 {
-    return (head_dim > 128 || group <= 16 || (dtype != DT_F16 && dtype != DT_BF16))
+    return (head_dim > 128 || group <= 16 || dtype == DT_F32)
                ? 1
-               : (group <= 32 ? 2 : 4);
+               : (dtype == DT_FP8 || group <= 32 ? 2 : 4);
 }
 
-// Blocks one decode workgroup walks side by side: its waves (one chunk), or its block
-// lanes (8 waves / chunks, shared-tile kernel).  A partition holds at most 64 blocks per
-// lane (a lane's block ids are one register, one per lane of the wave).
+// Whether those chunks share K/V tiles through LDS (the shared-tile kernel) rather than
+// as the two column blocks of each wave of a partition workgroup.
+constexpr bool decode_shared(int dtype, int head_dim, int group)
+{
+    return decode_chunks(dtype, head_dim, group) > 1 && (dtype == DT_F16 || dtype == DT_BF16);
+}
+
+// Blocks one decode workgroup walks side by side: its waves (partition kernel), or its
+// block lanes (8 waves / chunks, shared-tile kernel).  A partition holds at most 64
+// blocks per lane (a lane's block ids are one register, one per lane of the wave).
 constexpr int decode_lanes(int dtype, int head_dim, int group)
 {
-    return decode_chunks(dtype, head_dim, group) > 1 ? 8 / decode_chunks(dtype, head_dim, group)
-                                                     : waves_per_group(head_dim);
+    return decode_shared(dtype, head_dim, group) ? 8 / decode_chunks(dtype, head_dim, group)
+                                                 : waves_per_group(head_dim);
 }
 
 // Fewest decode workgroups the partition choice aims for: one per CU of the MI355X.

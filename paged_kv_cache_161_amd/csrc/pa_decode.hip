@@ -12,7 +12,10 @@
 //
 // Work decomposition
 //   grid  (P partitions, kv-heads x head-chunks, sequences); a workgroup of NW waves
-//   owns one (sequence, kv-head, <=16 q-heads of its group, partition).  Wave w walks
+//   owns one (sequence, kv-head, <=16 q-heads of its group, partition); with fp8 pools
+//   and a group above 16, <=32 q-heads, as two MFMA column blocks whose products read
+//   the same tile registers (groups above 16 with 16-bit pools take the shared-tile
+//   kernel further below, which stages each tile in LDS for 32 or 64 q-heads).  Wave w walks
 //   the partition's blocks w, w+NW, ...; at the end the NW waves merge their running
 //   (m, l, O) in LDS.  A sequence whose context fits one partition is finished by
 //   that workgroup; longer ones leave unnormalised partials (o, m, l) that
@@ -489,34 +492,38 @@ __device__ __forceinline__ void mask_tail_v(typename Frags<DT, AT, D>::Tile &t, 
 // ------------------------------------------------------------------ partition kernel
 
 // Waves per SIMD the register budget must allow: a tile ring of up to 64 VGPRs (two
-// 16-bit tiles, or four fp8 tiles, at d = 128) fits three waves per SIMD.
-constexpr int min_waves_per_simd(int dt, int d, int pf)
+// 16-bit tiles, or four fp8 tiles, at d = 128) fits three waves per SIMD with one
+// column block of q-heads per wave, two with two.
+constexpr int min_waves_per_simd(int dt, int d, int pf, int cb)
 {
     return (d > 128 || dt == DT_F32)
                ? 1
                : ((pf + 1) * (dt == DT_FP8 ? 16 : 32) * d / 128 <= 64
-                      ? 3
+                      ? (cb > 1 ? 2 : 3)
                       : ((pf + 1) * (dt == DT_FP8 ? 16 : 32) * d / 128 <= 96 ? 2 : 1));
 }
 
 // NT: K/V tiles are read with non-temporal loads (no block is shared between the
-// batch's sequences; never for fp32 pools).
-template <int DT, int AT, int D, int NW, int PF, bool FUSE, bool NT>
-__global__ __launch_bounds__(NW *kWave, min_waves_per_simd(DT, D, PF)) void pa_decode_partition(DecodeArgs a)
+// batch's sequences; never for fp32 pools).  CB: 16-head MFMA column blocks per wave
+// (the workgroup serves 16 CB q-heads of a group); with two, every K/V tile a wave
+// loads feeds both blocks' products from the same registers.
+template <int DT, int AT, int D, int NW, int PF, bool FUSE, bool NT, int CB>
+__global__ __launch_bounds__(NW *kWave, min_waves_per_simd(DT, D, PF, CB)) void pa_decode_partition(DecodeArgs a)
 {
     using F = Frags<DT, AT, D>;
     using Elem = typename F::Elem;        // K/V storage element
     using QElem = typename F::QElem;      // q / out element
     constexpr int DP = D + 4;                       // padded LDS row (floats)
+    constexpr int HS = 16 * CB;                     // q-head slots of the workgroup
 
     extern __shared__ float smem[];
-    float *s_m = smem;                              // [NW][16]
-    float *s_l = smem + NW * 16;                    // [NW][16]
-    int *s_bad = reinterpret_cast<int *>(smem + NW * 32);   // [NW] (16 ints reserved)
-    float *s_o = smem + NW * 32 + 16;               // [NW][GS][DP]
+    float *s_m = smem;                              // [NW][HS]
+    float *s_l = smem + NW * HS;                    // [NW][HS]
+    int *s_bad = reinterpret_cast<int *>(smem + 2 * NW * HS);   // [NW] (16 ints reserved)
+    float *s_o = smem + 2 * NW * HS + 16;           // [NW][GS][DP]
 
-    // (partition, kv-head x head chunk, sequence rank).  A group above 16 q-heads runs
-    // one workgroup per head chunk, each streaming the same K/V: the ids are then
+    // (partition, kv-head x head chunk, sequence rank).  A group above 16 CB q-heads runs
+    // one workgroup per 16 CB heads (a head chunk), each streaming the same K/V: the ids are then
     // regrouped so a (sequence, kv-head, partition) unit's chunks are dispatched back
     // to back on one XCD (ids round-robin over the XCDs, so ids L, L + 8, ... share
     // one L2), where the later chunks find the K/V in that L2.  Units keep the plain
@@ -553,8 +560,8 @@ __global__ __launch_bounds__(NW *kWave, min_waves_per_simd(DT, D, PF)) void pa_d
     const int r = lane & 15;
     const int g = lane >> 4;
 
-    const int gs = min(16, a.group - chunk * 16);   // q-heads handled here
-    const int hq0 = kvh * a.group + chunk * 16;     // first q-head of this workgroup
+    const int gs = min(HS, a.group - chunk * HS);   // q-heads handled here
+    const int hq0 = kvh * a.group + chunk * HS;     // first q-head of this workgroup
 
     // This wave's block ids (one per lane) and the group's q rows, issued before the
     // context length is known so the loads overlap: the table row has max_blocks
@@ -562,14 +569,17 @@ __global__ __launch_bounds__(NW *kWave, min_waves_per_simd(DT, D, PF)) void pa_d
     const int lb_begin = p * a.part_blocks;
     const int lb_cap = min(lb_begin + a.part_blocks, a.max_blocks);
     const int lb_lane = lb_begin + wave + lane * NW;   // this wave's (lane)-th block
-    typename F::Q qf;                                // q rows of the group (0 past gs)
+    typename F::Q qf[CB];                            // q rows of the group (0 past gs)
     int bt_lane;
     auto load_seq = [&](int seq) {
         bt_lane = lb_lane < lb_cap ? a.block_tables[(size_t)seq * a.max_blocks + lb_lane] : 0;
-        const bool hvalid = r < gs;
-        const QElem *qrow = static_cast<const QElem *>(a.q) +
-                           ((size_t)seq * a.num_q_heads + hq0 + (hvalid ? r : 0)) * D;
-        qf.load(qrow, hvalid, g);
+#pragma unroll
+        for (int c = 0; c < CB; ++c) {
+            const bool hvalid = 16 * c + r < gs;
+            const QElem *qrow = static_cast<const QElem *>(a.q) +
+                               ((size_t)seq * a.num_q_heads + hq0 + (hvalid ? 16 * c + r : 0)) * D;
+            qf[c].load(qrow, hvalid, g);
+        }
     };
 
     // Workgroups are dispatched in z order, so with longest_first workgroup z takes the
@@ -606,7 +616,7 @@ __global__ __launch_bounds__(NW *kWave, min_waves_per_simd(DT, D, PF)) void pa_d
     }
     int ctx = -1;
     if (a.longest_first) {
-        int *s_ctx = reinterpret_cast<int *>(smem + NW * 32 + 16 + NW * min(16, a.group) * DP);
+        int *s_ctx = reinterpret_cast<int *>(smem + 2 * NW * HS + 16 + NW * min(HS, a.group) * DP);
         const int nseq = gridDim.z;
         for (int t = tid; t < nseq; t += NW * kWave)
             s_ctx[t] = a.context_lens[t];
@@ -667,12 +677,16 @@ __global__ __launch_bounds__(NW *kWave, min_waves_per_simd(DT, D, PF)) void pa_d
     const Elem *vbase = static_cast<const Elem *>(a.v_pool) + (size_t)kvh * kBlock * D;
     const size_t blk_stride = (size_t)a.num_kv_heads * kBlock * D;
 
-    float m_run = -INFINITY;
-    float l_run = 0.f;
-    f32x4 o[D / 16];
+    float m_run[CB], l_run[CB];
+    f32x4 o[CB][D / 16];
 #pragma unroll
-    for (int n = 0; n < D / 16; ++n)
-        o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < CB; ++c) {
+        m_run[c] = -INFINITY;
+        l_run[c] = 0.f;
+#pragma unroll
+        for (int n = 0; n < D / 16; ++n)
+            o[c][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
     bool tbl_bad = bad_scale;   // (workgroup-uniform)
 
     auto phys_of = [&](int i) -> size_t {
@@ -701,12 +715,16 @@ __global__ __launch_bounds__(NW *kWave, min_waves_per_simd(DT, D, PF)) void pa_d
                 }
             }
         }
-        f32x4 s = scores<DT, AT, D>(t, qf);
-        f32x4 x = s * sl_h;
+        f32x4 x[CB];
+#pragma unroll
+        for (int c = 0; c < CB; ++c)
+            x[c] = scores<DT, AT, D>(t, qf[c]) * sl_h;
         if (valid < kBlock) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                x[j] = (4 * g + j < valid) ? x[j] : -INFINITY;
+            for (int c = 0; c < CB; ++c)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    x[c][j] = (4 * g + j < valid) ? x[c][j] : -INFINITY;
             mask_tail_v<DT, AT, D>(t, valid, g);
         }
         // The running max is only a reference point: O and l are both scaled by
@@ -716,22 +734,34 @@ __global__ __launch_bounds__(NW *kWave, min_waves_per_simd(DT, D, PF)) void pa_d
         // about once per wave instead of whenever a head sees a new maximum.  An empty
         // history (-inf) always takes the first finite max; an all-masked lane never
         // moves it.
-        const float lmx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-        if (__any(lmx - m_run > kRescaleSlack)) {
-            const float m_new = fmaxf(m_run, wave_max_rows(lmx));
-            const float alpha = fast_exp2(m_run - m_new);
+        float lmx[CB];
+        bool grow = false;
 #pragma unroll
-            for (int n = 0; n < D / 16; ++n)
-                o[n] *= alpha;
-            l_run *= alpha;
-            m_run = m_new;
+        for (int c = 0; c < CB; ++c) {
+            lmx[c] = fmaxf(fmaxf(x[c][0], x[c][1]), fmaxf(x[c][2], x[c][3]));
+            grow |= lmx[c] - m_run[c] > kRescaleSlack;
         }
-        f32x4 pw;
+        if (__any(grow)) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            pw[j] = fast_exp2(x[j] - m_run);
-        const f32x4 pu = accumulate_pv<DT, AT, D>(t, pw, o);
-        l_run += (pu[0] + pu[1]) + (pu[2] + pu[3]);
+            for (int c = 0; c < CB; ++c) {
+                const float m_new = fmaxf(m_run[c], wave_max_rows(lmx[c]));
+                const float alpha = fast_exp2(m_run[c] - m_new);
+#pragma unroll
+                for (int n = 0; n < D / 16; ++n)
+                    o[c][n] *= alpha;
+                l_run[c] *= alpha;
+                m_run[c] = m_new;
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < CB; ++c) {
+            f32x4 pw;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                pw[j] = fast_exp2(x[c][j] - m_run[c]);
+            const f32x4 pu = accumulate_pv<DT, AT, D>(t, pw, o[c]);
+            l_run[c] += (pu[0] + pu[1]) + (pu[2] + pu[3]);
+        }
     };
 
     // Ring of PF + 1 tiles: block i + PF is loaded while block i is computed.  The
@@ -828,19 +858,25 @@ __global__ __launch_bounds__(NW *kWave, min_waves_per_simd(DT, D, PF)) void pa_d
         prologue(ring);
         stream_blocks(ring);
     }
-    l_run = wave_sum_rows(l_run);
+#pragma unroll
+    for (int c = 0; c < CB; ++c)
+        l_run[c] = wave_sum_rows(l_run[c]);
 
     // ---- merge the NW waves' (m, l, O) in LDS
     if (lane == 0)
         s_bad[wave] = tbl_bad ? 1 : 0;
-    if (g == 0) {
-        s_m[wave * 16 + r] = m_run;
-        s_l[wave * 16 + r] = l_run;
-    }
-    if (r < gs) {
 #pragma unroll
-        for (int n = 0; n < D / 16; ++n)
-            *reinterpret_cast<f32x4 *>(s_o + (wave * gs + r) * DP + 16 * n + 4 * g) = o[n];
+    for (int c = 0; c < CB; ++c) {
+        const int h = 16 * c + r;
+        if (g == 0) {
+            s_m[wave * HS + h] = m_run[c];
+            s_l[wave * HS + h] = l_run[c];
+        }
+        if (h < gs) {
+#pragma unroll
+            for (int n = 0; n < D / 16; ++n)
+                *reinterpret_cast<f32x4 *>(s_o + (wave * gs + h) * DP + 16 * n + 4 * g) = o[c][n];
+        }
     }
     __syncthreads();
 
@@ -858,14 +894,14 @@ __global__ __launch_bounds__(NW *kWave, min_waves_per_simd(DT, D, PF)) void pa_d
         float M = -INFINITY;
 #pragma unroll
         for (int w = 0; w < NW; ++w)
-            M = fmaxf(M, s_m[w * 16 + h]);
+            M = fmaxf(M, s_m[w * HS + h]);
         float num = 0.f, den = 0.f;
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
-            const float mw = s_m[w * 16 + h];
+            const float mw = s_m[w * HS + h];
             const float f = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
             num += f * s_o[(w * gs + h) * DP + e];
-            den += f * s_l[w * 16 + h];
+            den += f * s_l[w * HS + h];
         }
         const size_t row = (size_t)b * a.num_q_heads + hq0 + h;
         if (!partial) {
@@ -884,7 +920,7 @@ __global__ __launch_bounds__(NW *kWave, min_waves_per_simd(DT, D, PF)) void pa_d
 
 // ------------------------------------------------------------------ shared-tile kernel
 
-// Groups above 16 q-heads (head_dim <= 128).  One 8-wave workgroup owns (sequence,
+// Groups above 16 q-heads with 16-bit pools (head_dim <= 128).  One 8-wave workgroup owns (sequence,
 // kv-head, up to 16 CH q-heads of its group, partition).  Wave w computes head chunk
 // c = w % CH over the blocks of block lane j = w / CH (blocks j, j + NB, ... of the
 // partition, NB = 8 / CH).  Each K/V tile is read from HBM once per workgroup: the CH
@@ -1385,38 +1421,26 @@ hipError_t launch_shared_t(const DecodeArgs &a, int num_seqs, hipStream_t stream
     return hipGetLastError();
 }
 
-template <int DT, int AT, int D>
-hipError_t launch_decode_t(const DecodeArgs &a, int num_seqs, hipStream_t stream)
+template <int DT, int AT, int D, int CB>
+hipError_t launch_partition_t(const DecodeArgs &a, int num_seqs, hipStream_t stream)
 {
-    // the host sized the grid and the partitions for decode_chunks(D, group) chunks per
-    // workgroup; the launch must hold exactly that many
-    const int ch = decode_chunks(DT, D, a.group);
-    if (a.wg_heads != 16 * ch)
-        return hipErrorInvalidValue;
-    if constexpr (D <= 128 && (DT == DT_F16 || DT == DT_BF16)) {
-        if (ch == 4)
-            return launch_shared_t<DT, AT, D, 4>(a, num_seqs, stream);
-        if (ch == 2)
-            return launch_shared_t<DT, AT, D, 2>(a, num_seqs, stream);
-    }
-    if (ch != 1)
-        return hipErrorInvalidValue;
     constexpr int NW = waves_per_group(D);
     // Blocks in flight per wave.  With ordinary loads fp8 tiles (half the bytes) keep
     // the 16-bit tiles' bytes in flight with a deeper ring; with non-temporal loads the
     // 2-tile ring is fastest for them too (4 tiles measured 3-6 % slower).
     constexpr int PF = (D > 128 || DT == DT_F32) ? 1 : kPrefetchMain;
     constexpr int PF_PLAIN = DT == DT_FP8 && D <= 128 ? 2 * kPrefetchMain + 1 : PF;
-    const int gs_max = min(16, a.group);
-    const size_t lds = sizeof(float) * (NW * 32 + 16 + (size_t)NW * gs_max * (D + 4)) +
+    constexpr int HS = 16 * CB;
+    const int gs_max = min(HS, a.group);
+    const size_t lds = sizeof(float) * (2 * NW * HS + 16 + (size_t)NW * gs_max * (D + 4)) +
                        (a.longest_first ? sizeof(int) * (num_seqs + 1) : 0);
     // fp32 tiles stream with ordinary loads (the hint measured slower for them)
     constexpr bool kNt = DT != DT_F32;
     const bool nt = kNt && a.stream_kv;
-    auto kern = a.k_new ? (nt ? pa_decode_partition<DT, AT, D, NW, PF, true, kNt>
-                              : pa_decode_partition<DT, AT, D, NW, PF_PLAIN, true, false>)
-                        : (nt ? pa_decode_partition<DT, AT, D, NW, PF, false, kNt>
-                              : pa_decode_partition<DT, AT, D, NW, PF_PLAIN, false, false>);
+    auto kern = a.k_new ? (nt ? pa_decode_partition<DT, AT, D, NW, PF, true, kNt, CB>
+                              : pa_decode_partition<DT, AT, D, NW, PF_PLAIN, true, false, CB>)
+                        : (nt ? pa_decode_partition<DT, AT, D, NW, PF, false, kNt, CB>
+                              : pa_decode_partition<DT, AT, D, NW, PF_PLAIN, false, false, CB>);
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -1431,6 +1455,32 @@ hipError_t launch_decode_t(const DecodeArgs &a, int num_seqs, hipStream_t stream
     dim3 rgrid(a.num_kv_heads * a.head_chunks, num_seqs);
     hipLaunchKernelGGL((pa_decode_reduce<AT, D>), rgrid, dim3(256), 0, stream, a);
     return hipGetLastError();
+}
+
+template <int DT, int AT, int D>
+hipError_t launch_decode_t(const DecodeArgs &a, int num_seqs, hipStream_t stream)
+{
+    // the host sized the grid and the partitions for decode_chunks(D, group) chunks per
+    // workgroup; the launch must hold exactly that many
+    const int ch = decode_chunks(DT, D, a.group);
+    if (a.wg_heads != 16 * ch)
+        return hipErrorInvalidValue;
+    if constexpr (D <= 128 && (DT == DT_F16 || DT == DT_BF16)) {
+        if (decode_shared(DT, D, a.group)) {
+            if (ch == 4)
+                return launch_shared_t<DT, AT, D, 4>(a, num_seqs, stream);
+            if (ch == 2)
+                return launch_shared_t<DT, AT, D, 2>(a, num_seqs, stream);
+            return hipErrorInvalidValue;
+        }
+    }
+    if constexpr (D <= 128 && DT != DT_F32) {
+        if (ch == 2)
+            return launch_partition_t<DT, AT, D, 2>(a, num_seqs, stream);
+    }
+    if (ch != 1)
+        return hipErrorInvalidValue;
+    return launch_partition_t<DT, AT, D, 1>(a, num_seqs, stream);
 }
 
 }  // namespace

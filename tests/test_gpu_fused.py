@@ -60,7 +60,10 @@ CASES = [(s, 0) for s in SMALL] + [(small_spec("bf16_g8_d128"), 16),
                                     (small_spec("bf16_g8_d128"), 48),
                                     (small_spec("bf16_g32_d128"), 32),
                                     (small_spec("fp8_bf16_g8_d128"), 16),
-                                    (small_spec("bf16_g5_d128"), 64)]
+                                    (small_spec("bf16_g5_d128"), 64),
+                                    # fp8 groups above 16: two column blocks per wave
+                                    (small_spec("fp8_heads_bf16_g32_d128"), 32),
+                                    (small_spec("fp8_bf16_g40_d64"), 48)]
 
 
 @pytest.mark.parametrize("spec,ptok", CASES, ids=lambda v: v.name if hasattr(v, "name") else f"p{v}")
