@@ -312,15 +312,19 @@ def test_misaligned_pointers_are_rejected(lib):
 
 def test_planner_follows_the_decode_kernel_of_the_pool_type(lib):
     """Above 16 q-heads per kv-head, 16-bit pools run the shared-tile kernel (up to 64
-    q-heads per workgroup, 8 / chunks block lanes of at most 64 blocks each), fp8 and
-    fp32 pools one workgroup per 16 q-heads (8 waves of at most 64 blocks each): the
-    planner, the partition bound and the workspace follow the pool type."""
+    q-heads per workgroup, 8 / chunks block lanes of at most 64 blocks each), fp8 pools
+    one workgroup per 32 q-heads (two column blocks per wave) and fp32 pools one per 16
+    q-heads (8 waves of at most 64 blocks each): the planner, the partition bound and
+    the workspace follow the pool type."""
     pt = lambda dt, n, hq, hkv, mx: lib.pa_decode_partition_tokens(n, hq, hkv, 128, dt, mx)
-    # 32 x 4096 at 64 q-heads over one kv-head: bf16 has 32 units of work, fp8 128
+    # 32 x 4096 at 64 q-heads over one kv-head: bf16 has 32 units of work, fp8 64, fp32 128
     bf, f8 = pt(B.PA_BF16, 32, 64, 1, 4096), pt(B.PA_FP8_E4M3, 32, 64, 1, 4096)
+    f32 = pt(B.PA_F32, 32, 64, 1, 4096)
     assert bf % 16 == 0 and f8 % 16 == 0
-    assert 32 * -(-4096 // bf) >= 256 and 32 * 4 * -(-4096 // f8) >= 256
+    assert 32 * -(-4096 // bf) >= 256 and 32 * 2 * -(-4096 // f8) >= 256
     assert bf < f8
+    # the fewest partitions that give 256 workgroups: 4 for fp8 (64 units), 2 for fp32
+    assert (f8, f32) == (1024, 2048)
     # the longest partition: 2 block lanes x 64 blocks (bf16, G = 64) against 8 x 64
     ws = lambda dt, ptok: lib.pa_decode_workspace_bytes(2, 64, 1, 128, dt, 8192, ptok)
     assert ws(B.PA_BF16, 128 * 16) > 0 and ws(B.PA_BF16, 129 * 16) == 2 ** 64 - 1
