@@ -94,9 +94,10 @@ SMALL = [
     W.Spec("bf16_300_ragged_seqs", "bf16", 8, 2, 128,
            [int(x) for x in np.random.Generator(np.random.PCG64(110)).integers(0, 70, 300)],
            seed=110, spare_blocks=1),
-    # groups above 16 q-heads: fp8 pools run one workgroup per 16-head chunk,
-    # regrouped so a unit's chunks share an XCD (whole groups of 8 units) or spread
-    # plainly (the last group); 16-bit pools stage each tile once for 64 q-heads
+    # groups above 16 q-heads: fp8 pools hold two 16-head column blocks per wave, one
+    # workgroup per 32 q-heads, regrouped so a unit's workgroups share an XCD (whole
+    # groups of 8 units) or spread plainly (the last group); 16-bit pools stage each
+    # tile once for 64 q-heads
     W.Spec("bf16_g48_d128", "bf16", 96, 2, 128, [300, 45, 1, 900, 17], seed=115,
            spare_blocks=1),
     W.Spec("fp8_bf16_g40_d64", "bf16", 80, 2, 64, [77, 200, 3], seed=116, spare_blocks=1,
@@ -325,6 +326,41 @@ def test_bad_table_entry_and_context_give_nan_not_fault():
     got = U.widen(U.from_dev(out, w.dtype), w.dtype)
     assert np.isnan(got[[0, 4, 5]]).all()
     assert np.isfinite(got[[1, 2, 3]]).all()
+
+
+@pytest.mark.parametrize("ptok", [0, 64])
+def test_bad_inputs_poison_only_their_rows_two_column_blocks(ptok):
+    """fp8 pools with 32 q-heads per kv-head run two column blocks per wave: a bad table
+    entry or context length makes exactly that sequence NaN, a bad per-head K scale
+    exactly that kv-head's 32 q-heads, single pass and split; every other output equals
+    the clean run bit for bit."""
+    w = W.build(small_spec("fp8_heads_bf16_g32_d128"))      # 2 kv-heads, G 32, 3 sequences
+    G = w.num_q_heads // w.num_kv_heads
+    d = U.device_inputs(w)
+    say(f"[bad inputs, two column blocks] ptok={ptok}")
+
+    def run(bt, cl, sc):
+        kp, vp = U.device_pools(w)
+        PA.cache_append(kp, vp, d["k_new"], d["v_new"], d["slot_mapping"], **sc)
+        o = PA.decode(d["q"], kp, vp, bt, cl, float(w.scale), w.max_context_len, ptok, **sc)
+        torch.cuda.synchronize()
+        return U.int_view(o).cpu().numpy(), U.widen(U.from_dev(o, w.dtype), w.dtype)
+
+    good_i, good_f = run(d["block_tables"], d["context_lens"], U.scales(w))
+    assert np.isfinite(good_f).all()
+    bt = d["block_tables"].clone()
+    bt[2, 3] = w.num_blocks + 7                  # sequence 2 (700 tokens) reads block 3
+    cl = d["context_lens"].clone()
+    cl[0] = -1
+    bi, bf = run(bt, cl, U.scales(w))
+    assert np.isnan(bf[[0, 2]]).all()
+    assert np.array_equal(good_i[1], bi[1])
+    sc = U.scales(w)
+    sc["k_scale"] = sc["k_scale"].clone()
+    sc["k_scale"][1] = float("nan")
+    hi, hf = run(d["block_tables"], d["context_lens"], sc)
+    assert np.isnan(hf[:, G:]).all()
+    assert np.array_equal(good_i[:, :G], hi[:, :G])
 
 
 def test_rejects_unsupported_partition():
