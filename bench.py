@@ -81,9 +81,9 @@ def parse():
                          "sizes on the Llama-70B-shaped decode, decode GQA group sizes on "
                          "32 x 4096 tokens, decode batch sizes (1 .. 64 sequences of 4096 "
                          "tokens), decode partition lengths (the plan against forced ones "
-                         "on small and ragged batches), prefill pool types and head sizes on the "
-                         "512-token chunked prefill, or prefill launches too small to fill "
-                         "the GPU with and without key splits")
+                         "on small, ragged and wide-group batches), prefill pool types and "
+                         "head sizes on the 512-token chunked prefill, or prefill launches "
+                         "too small to fill the GPU with and without key splits")
     ap.add_argument("--torch-sdpa-reference", action="store_true",
                     help="instead of the bench line, time PyTorch's own fused attention "
                          "(flash and memory-efficient backends only) on contiguous dense "
@@ -540,6 +540,14 @@ def sweep_shapes(name, W):
             base, name=f"{base.name}_B1_32k", context_lens=[32768])))
         shapes += [("ragged bf16 (config 4)", W.config_spec(4)),
                    ("long + shared prefix (config 5)", W.config_spec(5))]
+        # groups above 16 q-heads on 32 x 4,096 tokens, where few kv-heads leave the
+        # plan short partitions and a reduce
+        for label, kw in (("bf16 G32 (64 q / 2 kv)", dict(num_kv_heads=2)),
+                          ("bf16 G64 MQA (64 q / 1 kv)", dict(num_kv_heads=1)),
+                          ("fp8/bf16 G32 (64 q / 2 kv)", dict(num_kv_heads=2, **fp8))):
+            shapes.append((label, dataclasses.replace(
+                base, name=base.name + "_" + re.sub(r"[^A-Za-z0-9]+", "_", label).strip("_"),
+                **kw)))
         out = []
         for label, spec in shapes:
             for ptok in (0, 256, 512, 1024, 2048, 4096):
@@ -646,10 +654,19 @@ def bench_sweep(args, PA, W, U, dev):
             plan = PA.plan_partition_tokens(w.num_q_heads, w.num_kv_heads, w.head_dim,
                                             w.context_lens, w.kv_dtype)
             ptok = key_splits or plan          # decode: a forced partition length
-            ws = torch.empty(max(PA.workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads,
-                                                    w.head_dim, w.max_context_len, ptok,
-                                                    w.kv_dtype), 1),
-                             dtype=torch.uint8, device=dev)
+            try:
+                ws_bytes = PA.workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads,
+                                              w.head_dim, w.max_context_len, ptok, w.kv_dtype)
+            except PA.PaError:
+                if not key_splits:
+                    raise
+                # a forced length longer than this kernel's partitions may be
+                row = {"shape": label, "workload": spec.name, "partition_tokens": ptok,
+                       "unsupported": True}
+                log(f"[sweep] {json.dumps(row)}")
+                rows.append(row)
+                continue
+            ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
             rows_new = np.zeros((w.num_seqs,) + w.k_new.shape[1:], w.k_new.dtype)
             rows_new[np.flatnonzero(w.context_lens > 0)] = w.k_new
             kr = U.to_dev(rows_new, w.dtype, dev)
